@@ -1,0 +1,383 @@
+#!/usr/bin/env python3
+"""Benchmark of the KDA recurrent-state hot path on one MI355X.
+
+Headline (`value`): decode state-updates per second (tokens x heads / s) for
+B = 64 sequences, H = 32 heads, dk = dv = 128, bf16 q/k/v, fp32 state.  One
+step is one decode token through L_LAYERS independent layer states (1 GiB in
+total, four times the Infinity Cache), i.e. L_LAYERS kda_decode_step launches,
+so every launch streams its state from HBM as a multi-layer model would.
+
+`rows` reports the other parts of the path, each against its own roofline:
+the decode batch sweep B = 1..64, speculative verify (T = 4) and commit,
+snapshot/restore, the prompt prefill with checkpoints (B = 8, L = 8192), and a
+measured device-to-device copy for reference.  `roofline` is the decode
+kernel's: algorithmic bytes per launch / measured average launch time.
+`cpu_baseline` times the fp64 oracle on a bounded sample of the headline
+workload on the host.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--quick] [--no-cpu]
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+B_HEAD, H, DK, DV = 64, 32, 128, 128
+L_LAYERS = 8                   # 8 x 128 MiB of state per step
+N_TOKENS_IN = 16               # distinct seeded input tokens cycled through the timed steps
+SCALE = DK ** -0.5
+
+# Algorithmic bytes per unit (bf16 q/k/v, fp32 alpha/beta/o/state; dk = dv = 128).
+STATE_BYTES = DK * DV * 4
+DECODE_BYTES = 2 * STATE_BYTES + 3 * 128 * 2 + 128 * 4 + 4 + 128 * 4        # 132,868 per state-update
+TOKEN_IN_BYTES = 3 * 128 * 2 + 128 * 4 + 4                                    # 1,284: q, k, v, alpha, beta
+LOG_BYTES = 128 * 2 * 2 + 128 * 4 + 4                                         # 1,028: k, v, alpha, beta copy
+PREFILL_BYTES_PER_TOKEN_HEAD = TOKEN_IN_BYTES + 128 * 4                       # + o; state and ckpts added per run
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_sha() -> str:
+    h = hashlib.sha256()
+    for f in ("kda_common.h", "kda_state.hip"):
+        with open(os.path.join(ROOT, "recurrent_state_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def counted_traffic():
+    """HBM bytes per decode launch from the committed rocprofv3 counter summary,
+    or None when the decode kernel's source changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", "decode_b64_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("kernel_src_sha") != kernel_sha():
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+class Timer:
+    """HIP events on the current stream (the stream the library launches on)."""
+
+    def __init__(self, torch):
+        self.torch = torch
+        self.a = torch.cuda.Event(enable_timing=True)
+        self.b = torch.cuda.Event(enable_timing=True)
+
+    def __enter__(self):
+        self.torch.cuda.synchronize()
+        self.a.record()
+        return self
+
+    def __exit__(self, *exc):
+        self.b.record()
+        self.torch.cuda.synchronize()
+        self.ms = self.a.elapsed_time(self.b)
+
+
+def dev_tensor(torch, x, device):
+    if x.dtype == np.uint16:
+        return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).to(device).view(torch.bfloat16)
+    return torch.from_numpy(np.ascontiguousarray(x)).to(device)
+
+
+def decode_inputs(torch, kda_synth, B, n, device):
+    """n seeded tokens in [n][B][H][d] layout (token t is a contiguous slice)."""
+    spec = kda_synth.CONFIGS["batched_decode"]
+    inp = kda_synth.token_inputs(spec, B, n)
+    return {k: dev_tensor(torch, v, device).transpose(0, 1).contiguous() for k, v in inp.items()}
+
+
+def capture(torch, fns):
+    """A HIP graph of the given launches (no kernel runs during capture)."""
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for f in fns:
+            f()
+    return g
+
+
+def bench_decode(torch, kda, synth, B, layers, steps, warmup, device, use_graph=True):
+    """Decode through `layers` independent states per step; returns timing dict.
+
+    Step s uses seeded input token s mod 16 for every layer.  With use_graph,
+    each step's launches are replayed from a captured HIP graph (how a serving
+    loop drives per-step work); otherwise they are issued eagerly from plans.
+    """
+    spec = synth.CONFIGS["batched_decode"]
+    inp = decode_inputs(torch, synth, B, N_TOKENS_IN, device)
+    S0 = dev_tensor(torch, synth.initial_state(spec, B), device)
+    states = [S0.clone() for _ in range(layers)]
+    pos = torch.zeros(B, dtype=torch.int64, device=device)
+    o = torch.empty((B, H, DV), dtype=torch.float32, device=device)
+    plans = [[kda.DecodePlan(S, pos, inp["q"][t], inp["k"][t], inp["v"][t], inp["alpha"][t], inp["beta"][t], o)
+              for S in states] for t in range(N_TOKENS_IN)]
+    if use_graph:
+        graphs = [capture(torch, ps) for ps in plans]
+        step = lambda s: graphs[s % N_TOKENS_IN].replay()  # noqa: E731
+    else:
+        def step(s):
+            for p in plans[s % N_TOKENS_IN]:
+                p()
+    for s in range(warmup):
+        step(s)
+    with Timer(torch) as tm:
+        for s in range(steps):
+            step(s)
+    launches = steps * layers
+    launch_us = tm.ms * 1e3 / launches
+    bytes_per_launch = DECODE_BYTES * B * H
+    return {
+        "B": B, "layers": layers, "steps": steps, "graph": use_graph, "ms_per_step": tm.ms / steps,
+        "launch_us": launch_us, "updates_per_s": B * H * launches / (tm.ms / 1e3),
+        "achieved_GBs": bytes_per_launch / (launch_us * 1e-6) / 1e9,
+        "hbm_frac": bytes_per_launch / (launch_us * 1e-6) / 1e9 / HBM_PEAK_GBS,
+        "state_bytes_total": layers * B * H * STATE_BYTES,
+    }
+
+
+def bench_verify_commit(torch, kda, synth, B, T, rounds, layers, device):
+    """Speculative rounds (verify T drafts, commit the accepted prefix) over
+    `layers` independent states; verify and commit are captured as separate
+    graphs per round and timed with events recorded between replays."""
+    spec = synth.CONFIGS["spec_verify"]
+    inp = synth.token_inputs(spec, B, 4 * T)
+    d = {}
+    for k, v in inp.items():
+        t = dev_tensor(torch, v, device)
+        d[k] = t.view(B, 4, T, *t.shape[2:]).transpose(0, 1).contiguous()   # [4][B][T][H][d]
+    acc_np = synth.accepted_counts(spec, B, rounds, T)
+    acc = torch.from_numpy(acc_np).to(device)
+    S0 = dev_tensor(torch, synth.initial_state(spec, B), device)
+    states = [S0.clone() for _ in range(layers)]
+    logs = [kda.InputLog(S0, T_max=T) for _ in range(layers)]
+    pos = torch.zeros(B, dtype=torch.int64, device=device)
+    err = torch.zeros(1, dtype=torch.int32, device=device)
+    o = torch.empty((B, T, H, DV), dtype=torch.float32, device=device)
+    vg, cg = [], []
+    for r in range(rounds):
+        j = r % 4
+        vg.append(capture(torch, [kda.VerifyPlan(S, d["q"][j], d["k"][j], d["v"][j], d["alpha"][j], d["beta"][j],
+                                                 o, lg) for S, lg in zip(states, logs)]))
+        cg.append(capture(torch, [kda.CommitPlan(S, pos, lg, acc[r], err) for S, lg in zip(states, logs)]))
+    for r in range(rounds):          # warm-up pass
+        vg[r].replay()
+        cg[r].replay()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * rounds + 1)]
+    torch.cuda.synchronize()
+    ev[0].record()
+    for r in range(rounds):
+        vg[r].replay()
+        ev[2 * r + 1].record()
+        cg[r].replay()
+        ev[2 * r + 2].record()
+    torch.cuda.synchronize()
+    ver_ms = sum(ev[2 * r].elapsed_time(ev[2 * r + 1]) for r in range(rounds))
+    com_ms = sum(ev[2 * r + 1].elapsed_time(ev[2 * r + 2]) for r in range(rounds))
+    tot_ms = ev[0].elapsed_time(ev[-1])
+    n_launch = rounds * layers
+    ver_bytes = B * H * (STATE_BYTES + T * (TOKEN_IN_BYTES + 128 * 4 + LOG_BYTES))
+    com_bytes = float((int((acc_np > 0).sum()) * 2 * STATE_BYTES + int(acc_np.sum()) * LOG_BYTES) * H) * layers
+    return {
+        "B": B, "T": T, "rounds": rounds, "layers": layers, "mean_accepted": float(acc_np.mean()),
+        "verify_us": ver_ms * 1e3 / n_launch, "commit_us": com_ms * 1e3 / n_launch,
+        "round_us": tot_ms * 1e3 / n_launch,
+        "verify_hbm_frac": ver_bytes * n_launch / (ver_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+        "commit_hbm_frac": com_bytes / (com_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+        "round_hbm_frac": (ver_bytes * n_launch + com_bytes) / (tot_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+        "verified_token_heads_per_s": B * H * n_launch * T / (tot_ms / 1e3),
+        "committed_token_heads_per_s": float(acc_np.sum()) * H * layers / (tot_ms / 1e3),
+    }
+
+
+def bench_prefill(torch, kda, synth, device, variant, reps=2):
+    spec = synth.CONFIGS["prefill"]
+    B, L = spec.B[0], spec.steps
+    every = spec.extra["ckpt_every"]
+    # Timing only: the first 1024 seeded tokens tiled 8x along the prompt (the
+    # parity tests use the full 8192-token draw).
+    base = synth.token_inputs(spec, B, 1024)
+    d = {k: dev_tensor(torch, np.concatenate([v] * (L // 1024), axis=1), device) for k, v in base.items()}
+    S0 = dev_tensor(torch, synth.initial_state(spec, B), device)
+    S = S0.clone()
+    pos = torch.zeros(B, dtype=torch.int64, device=device)
+    n_ck = L // every
+    pool = kda.SlotPool(B * n_ck, H, DK, DV, device)
+    slots = torch.arange(B * n_ck, dtype=torch.int32, device=device).view(B, n_ck)
+    err = torch.zeros(1, dtype=torch.int32, device=device)
+    o = torch.empty((B, L, H, DV), dtype=torch.float32, device=device)
+    fn = kda.prefill_chunked if variant == "chunked" else kda.prefill_recurrent
+    kw = dict(ckpt_every=every, ckpt_slots=slots, pool=pool, dev_err=err)
+    if variant == "chunked":
+        kw["chunk"] = spec.extra["chunk"]
+
+    def run():
+        S.copy_(S0)
+        fn(S, pos, d["q"], d["k"], d["v"], d["alpha"], d["beta"], o, **kw)
+
+    run()
+    best = None
+    for _ in range(reps):
+        S.copy_(S0)
+        with Timer(torch) as tm:
+            fn(S, pos, d["q"], d["k"], d["v"], d["alpha"], d["beta"], o, **kw)
+        best = tm.ms if best is None else min(best, tm.ms)
+    th = B * L * H
+    total_bytes = th * PREFILL_BYTES_PER_TOKEN_HEAD + B * H * STATE_BYTES * (2 + n_ck)
+    return {"variant": variant, "B": B, "L": L, "ms": best, "token_heads_per_s": th / (best / 1e3),
+            "hbm_frac": total_bytes / (best * 1e-3) / 1e9 / HBM_PEAK_GBS, "algorithmic_bytes": total_bytes}
+
+
+def bench_snapshot_restore(torch, kda, synth, device, reps=20):
+    B, n_slots = 64, 64
+    S = torch.randn((B, H, DK, DV), device=device)
+    pos = torch.arange(B, dtype=torch.int64, device=device)
+    pool = kda.SlotPool(n_slots, H, DK, DV, device)
+    ids = list(range(B))
+    kda.snapshot(S, pos, ids, ids, pool)
+    with Timer(torch) as ts:
+        for _ in range(reps):
+            kda.snapshot(S, pos, ids, ids, pool)
+    with Timer(torch) as tr:
+        for _ in range(reps):
+            kda.restore(S, pos, ids, ids, pool)
+    nbytes = 2 * B * H * STATE_BYTES
+    return {"pairs": B, "snapshot_us": ts.ms * 1e3 / reps, "restore_us": tr.ms * 1e3 / reps,
+            "snapshot_hbm_frac": nbytes / (ts.ms * 1e-3 / reps) / 1e9 / HBM_PEAK_GBS,
+            "restore_hbm_frac": nbytes / (tr.ms * 1e-3 / reps) / 1e9 / HBM_PEAK_GBS}
+
+
+def bench_copy(torch, device, reps=20):
+    n = 1 << 28  # 1 GiB of fp32
+    a = torch.empty(n, dtype=torch.float32, device=device).fill_(1.0)
+    b = torch.empty_like(a)
+    b.copy_(a)
+    with Timer(torch) as tm:
+        for _ in range(reps):
+            b.copy_(a)
+    return {"bytes_per_copy": 2 * 4 * n, "GBs": 2 * 4 * n * reps / (tm.ms * 1e-3) / 1e9}
+
+
+def cpu_baseline(synth, budget_s=12.0):
+    """The fp64 oracle (as it stands) on a bounded sample of the headline
+    workload: B = 64, H = 32 decode steps, on one host core."""
+    from threadpoolctl import threadpool_limits
+
+    from oracle import kda_oracle as ko
+    spec = synth.CONFIGS["batched_decode"]
+    B = B_HEAD
+    S0 = synth.initial_state(spec, B)
+    inp = synth.token_inputs(spec, B, N_TOKENS_IN)
+    S = ko.widen(S0)
+    done = 0
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        while True:
+            t = done % N_TOKENS_IN
+            tok = [ko.widen(inp[n][:, t]) for n in ("q", "k", "v", "alpha", "beta")]
+            S, _ = ko.step(S, *tok, SCALE)
+            done += 1
+            el = time.perf_counter() - t0
+            if el >= budget_s:
+                break
+    return {"value": done * B * H / el, "unit": "state-updates/s", "cores": 1, "kind": "oracle",
+            "sample": f"{done} decode steps of B=64 x H=32 (dk=dv=128) in fp64, one core, {el:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--quick", action="store_true", help="headline only")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this library's path has no multi-GPU part "
+              "(sequences and heads shard with no exchange); run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import recurrent_state_amd as kda
+    import synth
+
+    kda.lib()  # fails loudly if libkda.so is missing
+    device = torch.device("cuda:0")
+    torch.cuda.set_device(device)
+    props = torch.cuda.get_device_properties(device)
+    log(f"device: {props.name}, {props.multi_processor_count} CUs")
+
+    log("headline: decode B=64 x 8 layers")
+    head = bench_decode(torch, kda, synth, B_HEAD, L_LAYERS, args.steps, args.warmup, device)
+    rows = {}
+    if not args.quick:
+        log("headline workload launched eagerly (no graph)")
+        rows["decode_b64_eager"] = bench_decode(torch, kda, synth, B_HEAD, L_LAYERS, 100, 10, device,
+                                                use_graph=False)
+        log("copy reference")
+        rows["d2d_copy_1GiB"] = bench_copy(torch, device)
+        log("hot (cache-resident) decode B=64, one layer")
+        rows["decode_b64_one_layer_hot"] = bench_decode(torch, kda, synth, 64, 1, 400, 40, device)
+        sweep = []
+        for B in (1, 2, 4, 8, 16, 32, 64):
+            layers = max(L_LAYERS, (1 << 30) // (B * H * STATE_BYTES))
+            steps = max(10, min(200, int(2e4 // layers)))
+            log(f"sweep B={B} layers={layers} steps={steps}")
+            sweep.append(bench_decode(torch, kda, synth, B, layers, steps, 3, device))
+        rows["decode_sweep"] = sweep
+        log("verify/commit")
+        rows["verify_commit_b16"] = bench_verify_commit(torch, kda, synth, 16, 4, 32, 32, device)
+        rows["verify_commit_b64"] = bench_verify_commit(torch, kda, synth, 64, 4, 32, 8, device)
+        log("snapshot/restore")
+        rows["snapshot_restore"] = bench_snapshot_restore(torch, kda, synth, device)
+        log("prefill")
+        for variant in ("recurrent",):
+            rows[f"prefill_{variant}"] = bench_prefill(torch, kda, synth, device, variant)
+
+    cpu = None if args.no_cpu else cpu_baseline(synth)
+    bytes_per_launch = DECODE_BYTES * B_HEAD * H
+    line = {
+        "metric": "KDA state-updates/s (tokens*heads/s) and % HBM roofline, B=1..64, 1 GPU",
+        "value": head["updates_per_s"],
+        "unit": "state-updates/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": head["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (seeded generator: unit-norm Gaussian q/k, N(0,1) v, exp(-softplus(N(-4,1))) gates, "
+                "sigmoid(N(0,1)) beta, N(0,0.02) initial state)",
+        "config": {"workload": "batched decode, B=64, H=32, dk=dv=128, bf16 q/k/v, fp32 state; one step = one "
+                               "token through 8 independent layer states (1 GiB)",
+                   "B": B_HEAD, "H": H, "dk": DK, "dv": DV, "layers": L_LAYERS, "in_dtype": "bf16"},
+        "roofline": {"bound": "hbm", "kernel": "decode_kernel<128,128,bf16>",
+                     "achieved": head["achieved_GBs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": head["achieved_GBs"] / HBM_PEAK_GBS, "traffic": counted_traffic(),
+                     "algorithmic_bytes_per_launch": bytes_per_launch, "launch_us": head["launch_us"]},
+        "cpu_baseline": cpu,
+        "rows": rows,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

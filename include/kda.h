@@ -1,0 +1,245 @@
+/*
+ * kda.h - C ABI of libkda, the MI355X (gfx950) KDA recurrent-state library.
+ *
+ * Kimi Delta Attention keeps, per sequence and head, a fixed-size recurrent
+ * state that every token updates ("Kimi K3: From Day-0 Availability to
+ * Optimized Inference", nebius webinar summary, opening paragraph).  The
+ * pages do not print the update; this library implements the
+ * per-channel-gated delta rule.  Per sequence b and head h the state S is a
+ * dk x dv fp32 matrix (row i = key channel, column j = value channel), and a
+ * token with q, k (dk), v (dv), per-key-channel gate alpha (dk) and scalar
+ * beta does
+ *
+ *     S <- Diag(alpha) S
+ *     S <- S - beta k (k^T S) + beta k v^T
+ *     o  = scale * S^T q              (read after the update)
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Layouts (all dense, row-major, device memory unless stated otherwise):
+ *   state   f32 [B][H][dk][dv]        updated in place
+ *   q, k    in_dtype [B][T][H][dk]    (T = 1 for a decode step)
+ *   v       in_dtype [B][T][H][dv]
+ *   alpha   f32 [B][T][H][dk]         gates in (0, 1]
+ *   beta    f32 [B][T][H]
+ *   o       f32 [B][T][H][dv]         must not alias any input
+ *   pos     i64 [B]                   token position of each sequence
+ * in_dtype is KDA_BF16 (bfloat16 bit patterns) or KDA_F32.
+ *
+ * Ownership: the caller allocates every buffer (state, inputs, outputs, log,
+ * slot pool, positions, counters).  The library never allocates or frees
+ * device memory and never synchronizes; each call validates its arguments on
+ * the host and then only enqueues kernels on `stream` (a hipStream_t; NULL
+ * is the null stream).  Results are available when the stream reaches them.
+ *
+ * Alignment: every device pointer must be 16-byte aligned; the log buffer
+ * 256-byte aligned.
+ *
+ * Errors: argument errors are detected on the host before anything is
+ * enqueued and return a status without side effects.  Values the host
+ * cannot see (accepted counts, checkpoint slot ids in device memory) are
+ * checked on the device: a bad value sets bits in the caller's sticky
+ * `dev_err` word and leaves the affected sequence untouched.  Launch
+ * failures return KDA_ERR_HIP.  No call prints, throws or aborts.  Values
+ * are not checked: NaN and Inf propagate.
+ *
+ * Threading: calls are reentrant; calls on different streams with disjoint
+ * buffers may run concurrently.  Calls that share a buffer must be ordered
+ * by the caller (same stream or events).
+ *
+ * Supported sizes: dk, dv in {64, 128}; B >= 0 (B = 0 is a no-op); H >= 1;
+ * verify 1 <= T <= T_max <= 16; prefill chunk in {16, 32, 64}.
+ */
+#ifndef KDA_H
+#define KDA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define KDA_ABI_VERSION 1
+
+typedef enum kda_status {
+  KDA_OK = 0,
+  KDA_ERR_NULL = 1,   /* a required pointer is NULL */
+  KDA_ERR_SHAPE = 2,  /* unsupported or inconsistent size */
+  KDA_ERR_DTYPE = 3,  /* unknown in_dtype code */
+  KDA_ERR_ALIGN = 4,  /* a pointer is not aligned as required */
+  KDA_ERR_ORDER = 5,  /* commit without a pending verify, or verify while one is pending */
+  KDA_ERR_SLOT = 6,   /* a sequence or slot index is out of range */
+  KDA_ERR_HIP = 7     /* the HIP runtime rejected a launch */
+} kda_status;
+
+typedef enum kda_dtype { KDA_BF16 = 0, KDA_F32 = 1 } kda_dtype;
+
+/* Bits set in the device error word. */
+#define KDA_DEV_ERR_ACCEPTED 1 /* an accepted count was outside [0, T] */
+#define KDA_DEV_ERR_CKPT_SLOT 2 /* a checkpoint slot id was outside [0, n_slots) */
+
+/* Kernel variants reported by kda_last_variant(). */
+#define KDA_VARIANT_NONE 0
+#define KDA_VARIANT_DECODE 1
+#define KDA_VARIANT_VERIFY 2
+#define KDA_VARIANT_COMMIT 3
+#define KDA_VARIANT_SNAPSHOT 4
+#define KDA_VARIANT_RESTORE 5
+#define KDA_VARIANT_PREFILL_RECURRENT 6
+#define KDA_VARIANT_PREFILL_CHUNKED 7
+
+typedef struct kda_shape {
+  int32_t B;        /* sequences in the batch */
+  int32_t H;        /* heads */
+  int32_t dk;       /* key/query width: 64 or 128 */
+  int32_t dv;       /* value width: 64 or 128 */
+  int32_t in_dtype; /* kda_dtype of q, k, v */
+  float scale;      /* output scale, normally 1/sqrt(dk) */
+} kda_shape;
+
+/*
+ * Speculative-decoding input log ("Kimi K3: From Day-0 Availability to
+ * Optimized Inference", paragraph on rejected draft tokens: the recurrent
+ * inputs are stored and the accepted part is replayed from the last
+ * committed state).  `dev` is a caller-owned device buffer of
+ * kda_log_bytes(shape, T_max) bytes.  It holds four regions, each starting
+ * at a 256-byte boundary, in this order, sized for T_max and filled for the
+ * T of the pending verify:
+ *   k      in_dtype [B][T][H][dk]
+ *   v      in_dtype [B][T][H][dv]
+ *   alpha  f32 [B][T][H][dk]
+ *   beta   f32 [B][T][H]
+ * `pending_T` is host-side bookkeeping: kda_verify sets it to T, kda_commit
+ * consumes it and resets it to 0.  Initialise it to 0.
+ */
+typedef struct kda_log {
+  void* dev;
+  size_t bytes;
+  int32_t T_max;
+  int32_t pending_T;
+} kda_log;
+
+/*
+ * Slot pool for recurrent-state checkpoints (same webinar summary, paragraph
+ * on prefix caching: the checkpoint sits at a token boundary shared with the
+ * attention cache).  Caller-owned device memory:
+ *   states  f32 [n_slots][H][dk][dv]
+ *   pos     i64 [n_slots]   token position at which the slot's state was taken
+ */
+typedef struct kda_slots {
+  float* states;
+  int64_t* pos;
+  int32_t n_slots;
+} kda_slots;
+
+/* Bytes needed for a log of up to T_max draft tokens; 0 for an invalid shape. */
+size_t kda_log_bytes(const kda_shape* shape, int32_t T_max);
+
+/* Bytes of one slot's state (H * dk * dv * 4); 0 for an invalid shape. */
+size_t kda_slot_bytes(const kda_shape* shape);
+
+/*
+ * One decode token for every (sequence, head): the update above applied in
+ * place to `state`, o = scale * S^T q written to `o` (f32 [B][H][dv]), and
+ * pos[b] += 1.  Inputs use the layouts above with T = 1.
+ * ("Hyper-optimizing Kimi K3 in vLLM", Part 1, section 1: a dedicated KDA
+ * decode kernel scheduled for the batch size and heads per GPU.)
+ */
+kda_status kda_decode_step(const kda_shape* shape, float* state, int64_t* pos, const void* q,
+                           const void* k, const void* v, const float* alpha, const float* beta,
+                           float* o, void* stream);
+
+/*
+ * Speculative verify of T draft tokens per sequence from the committed
+ * state: runs the T tokens on a private copy of each (b, h) state, writes
+ * every output o_t (f32 [B][T][H][dv]) and copies k, v, alpha, beta of all T
+ * tokens into the log.  `state` is read, never written.  Fails with
+ * KDA_ERR_ORDER if `log` already has a pending verify.  Output o_t for
+ * t <= a equals, bit for bit, what a decode steps would have produced.
+ * (Webinar summary, paragraph on rejected draft tokens.)
+ */
+kda_status kda_verify(const kda_shape* shape, int32_t T, const float* state, const void* q,
+                      const void* k, const void* v, const float* alpha, const float* beta,
+                      float* o, kda_log* log, void* stream);
+
+/*
+ * Commit: for each sequence b, replays the first accepted[b] logged tokens
+ * onto the committed state in place and adds accepted[b] to pos[b].
+ * `accepted` is a device int32 [B].  A count of 0 leaves the state bytes
+ * untouched; a count outside [0, pending_T] sets KDA_DEV_ERR_ACCEPTED in
+ * *dev_err (device int32, sticky, never cleared by the library) and leaves
+ * that sequence untouched.  The resulting state is bit-identical to
+ * accepted[b] kda_decode_step calls on the same tokens.  Fails with
+ * KDA_ERR_ORDER when no verify is pending; on success the log is released.
+ * (Webinar summary, paragraph on rejected draft tokens.)
+ */
+kda_status kda_commit(const kda_shape* shape, float* state, int64_t* pos, kda_log* log,
+                      const int32_t* accepted, int32_t* dev_err, void* stream);
+
+/*
+ * Snapshot: copies the whole state of sequence seq_ids[i] (all H heads) and
+ * its position into slot slot_ids[i], for i < n.  seq_ids and slot_ids are
+ * HOST int32 arrays; every id is range-checked before anything is enqueued
+ * (KDA_ERR_SLOT).  Slots written twice in one call get the later pair.
+ * The copy is bitwise.  (Webinar summary, paragraph on prefix caching.)
+ */
+kda_status kda_snapshot(const kda_shape* shape, const float* state, const int64_t* pos,
+                        const int32_t* seq_ids, const int32_t* slot_ids, int32_t n,
+                        const kda_slots* slots, void* stream);
+
+/*
+ * Restore: copies slot slot_ids[i]'s state and position into sequence
+ * seq_ids[i], for i < n (host arrays, range-checked as above).  Bitwise.
+ * A sequence named twice gets the later pair.
+ */
+kda_status kda_restore(const kda_shape* shape, float* state, int64_t* pos, const int32_t* seq_ids,
+                       const int32_t* slot_ids, int32_t n, const kda_slots* slots, void* stream);
+
+/*
+ * Prompt processing of L tokens per sequence into the state (in place), in
+ * the chunked (WY / UT-transform) form with `chunk` tokens per chunk; the last
+ * chunk may be partial.  Writes o for every token (f32 [B][L][H][dv]) and
+ * adds L to pos.  Inputs use the layouts above with T = L.
+ * When ckpt_every > 0 (a multiple of chunk) the state after every
+ * ckpt_every tokens is also written to slot ckpt_slots[b * n_ckpt + m]
+ * (m = 0 .. n_ckpt - 1, n_ckpt = L / ckpt_every), with slot position
+ * pos[b] + (m + 1) * ckpt_every.  ckpt_slots is a DEVICE int32 array; an id
+ * outside [0, slots->n_slots) sets KDA_DEV_ERR_CKPT_SLOT and that checkpoint
+ * is skipped.  `dev_err` may be NULL only when ckpt_every == 0.
+ * (Webinar summary: prompt processing that prefix caching avoids, and the
+ * recurrent-state checkpoint at a token boundary.)
+ */
+kda_status kda_prefill_chunked(const kda_shape* shape, int32_t L, int32_t chunk, float* state,
+                               int64_t* pos, const void* q, const void* k, const void* v,
+                               const float* alpha, const float* beta, float* o, int32_t ckpt_every,
+                               const int32_t* ckpt_slots, const kda_slots* slots, int32_t* dev_err,
+                               void* stream);
+
+/*
+ * The same prompt processing as kda_prefill_chunked, computed token by token
+ * with the decode update while each (sequence, head) state stays in
+ * registers for the whole prompt.  Arguments as for kda_prefill_chunked
+ * without `chunk`; any ckpt_every > 0 is allowed.  It is the cross-check for
+ * the chunked form and the cheaper choice for very short prompts.
+ */
+kda_status kda_prefill_recurrent(const kda_shape* shape, int32_t L, float* state, int64_t* pos,
+                                 const void* q, const void* k, const void* v, const float* alpha,
+                                 const float* beta, float* o, int32_t ckpt_every,
+                                 const int32_t* ckpt_slots, const kda_slots* slots, int32_t* dev_err,
+                                 void* stream);
+
+/* Human-readable name of a status code (static string). */
+const char* kda_status_str(kda_status status);
+
+/* Variant launched by the last successful call on this thread (KDA_VARIANT_*). */
+int32_t kda_last_variant(void);
+
+/* KDA_ABI_VERSION of the loaded library. */
+int32_t kda_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KDA_H */

@@ -1,0 +1,32 @@
+"""MI355X (gfx950) KDA recurrent-state library: Python binding of libkda.
+
+The hot path (decode step, speculative verify and commit, snapshot/restore,
+chunked prefill) runs in hand-written HIP kernels inside libkda.so; this
+package only marshals torch tensors (device memory and streams) into the C ABI
+of include/kda.h.
+"""
+
+from ._lib import (  # noqa: F401
+    DEV_ERR_ACCEPTED,
+    DEV_ERR_CKPT_SLOT,
+    CommitPlan,
+    DecodePlan,
+    LIB_PATH,
+    InputLog,
+    KdaError,
+    VerifyPlan,
+    Shape,
+    SlotPool,
+    commit,
+    decode_step,
+    exported_symbols,
+    last_variant,
+    lib,
+    log_bytes,
+    prefill_chunked,
+    prefill_recurrent,
+    restore,
+    slot_bytes,
+    snapshot,
+    verify,
+)

@@ -1,0 +1,192 @@
+// Shared device helpers for the KDA recurrent-state kernels (gfx950, wave64).
+//
+// Thread mapping used by every state-resident kernel (decode, verify, commit,
+// recurrent prefill).  One wave owns a 32-column slice of one (sequence, head)
+// state S [dk][dv]; lane = 8 * rg + cg with
+//   cg in [0, 8): the lane's 4 value columns  col0 = 32 * slice + 4 * cg
+//   rg in [0, 8): the lane's R = dk / 8 consecutive key rows  row0 = R * rg
+// so each lane keeps R x 4 fp32 state values in registers.  A load of one
+// row index by the whole wave touches 8 full 128-byte lines (one per row
+// group).  Reductions over the key axis run inside the wave (xor over lane
+// bits 3..5), so waves never synchronise with each other and no LDS is used.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kda {
+
+constexpr int kWave = 64;
+constexpr int kSliceCols = 32;  // value columns per wave
+constexpr int kRowGroups = 8;   // lanes sharing a column group, each with R rows
+
+typedef uint16_t bf16_t;  // bfloat16 bit pattern
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Raw storage of N consecutive input values (bit-exact copy source for the log).
+template <typename TIn, int N>
+struct Raw;
+template <int N>
+struct Raw<bf16_t, N> {
+  static_assert(N % 8 == 0, "bf16 rows are moved 16 bytes at a time");
+  typedef uint4 vec;
+  vec w[N / 8];
+};
+template <int N>
+struct Raw<float, N> {
+  static_assert(N % 4 == 0, "f32 rows are moved 16 bytes at a time");
+  typedef float4 vec;
+  vec w[N / 4];
+};
+
+template <typename TIn, int N>
+__device__ __forceinline__ void load_raw(const TIn* p, Raw<TIn, N>& r) {
+  typedef typename Raw<TIn, N>::vec vec;
+  constexpr int V = sizeof(r.w) / 16;
+#pragma unroll
+  for (int i = 0; i < V; ++i) r.w[i] = reinterpret_cast<const vec*>(p)[i];
+}
+
+template <typename TIn, int N>
+__device__ __forceinline__ void store_raw(TIn* p, const Raw<TIn, N>& r) {
+  typedef typename Raw<TIn, N>::vec vec;
+  constexpr int V = sizeof(r.w) / 16;
+#pragma unroll
+  for (int i = 0; i < V; ++i) reinterpret_cast<vec*>(p)[i] = r.w[i];
+}
+
+template <int N>
+__device__ __forceinline__ void widen(const Raw<bf16_t, N>& r, float (&x)[N]) {
+#pragma unroll
+  for (int i = 0; i < N / 8; ++i) {
+    const uint32_t a[4] = {r.w[i].x, r.w[i].y, r.w[i].z, r.w[i].w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      x[8 * i + 2 * j] = bf16_lo(a[j]);
+      x[8 * i + 2 * j + 1] = bf16_hi(a[j]);
+    }
+  }
+}
+
+template <int N>
+__device__ __forceinline__ void widen(const Raw<float, N>& r, float (&x)[N]) {
+#pragma unroll
+  for (int i = 0; i < N / 4; ++i) {
+    x[4 * i] = r.w[i].x;
+    x[4 * i + 1] = r.w[i].y;
+    x[4 * i + 2] = r.w[i].z;
+    x[4 * i + 3] = r.w[i].w;
+  }
+}
+
+// Four consecutive value entries (the lane's columns).
+template <typename TIn>
+struct Raw4;
+template <>
+struct Raw4<bf16_t> {
+  typedef uint2 vec;
+  vec w;
+};
+template <>
+struct Raw4<float> {
+  typedef float4 vec;
+  vec w;
+};
+
+template <typename TIn>
+__device__ __forceinline__ void load4(const TIn* p, Raw4<TIn>& r) {
+  r.w = *reinterpret_cast<const typename Raw4<TIn>::vec*>(p);
+}
+template <typename TIn>
+__device__ __forceinline__ void store4(TIn* p, const Raw4<TIn>& r) {
+  *reinterpret_cast<typename Raw4<TIn>::vec*>(p) = r.w;
+}
+__device__ __forceinline__ void widen4(const Raw4<bf16_t>& r, float (&x)[4]) {
+  x[0] = bf16_lo(r.w.x);
+  x[1] = bf16_hi(r.w.x);
+  x[2] = bf16_lo(r.w.y);
+  x[3] = bf16_hi(r.w.y);
+}
+__device__ __forceinline__ void widen4(const Raw4<float>& r, float (&x)[4]) {
+  x[0] = r.w.x;
+  x[1] = r.w.y;
+  x[2] = r.w.z;
+  x[3] = r.w.w;
+}
+
+// Sum over the 8 row groups of a wave (lane bits 3, 4, 5).  Every lane ends
+// with the same value for its column group: each butterfly stage adds the
+// same two operands on both partner lanes, and IEEE addition is commutative.
+__device__ __forceinline__ float rowgroup_sum(float x) {
+  x += __shfl_xor(x, 8);
+  x += __shfl_xor(x, 16);
+  x += __shfl_xor(x, 32);
+  return x;
+}
+
+// One token of the gated delta rule on a lane's R x 4 register tile:
+//   S1 = Diag(alpha) S;  u = S1^T k;  e = beta (v - u);  S = S1 + k e^T
+// and, when WITH_OUT, o = scale (S1^T q + e (k . q)), which equals
+// scale * S^T q of the updated state.  Decode, verify, commit and the
+// recurrent prefill all call this one function with the same lane mapping,
+// so their states and outputs agree bit for bit.
+template <int R, bool WITH_OUT>
+__device__ __forceinline__ void token_update(float (&S)[R][4], const float (&kr)[R], const float (&ar)[R],
+                                             const float (&qr)[R], const float (&vc)[4], float beta,
+                                             float scale, float (&o)[4]) {
+  float u[4] = {0.f, 0.f, 0.f, 0.f};
+  float w[4] = {0.f, 0.f, 0.f, 0.f};
+  float kq = 0.f;
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const float s1 = ar[r] * S[r][c];
+      S[r][c] = s1;
+      u[c] = __builtin_fmaf(kr[r], s1, u[c]);
+      if (WITH_OUT) w[c] = __builtin_fmaf(qr[r], s1, w[c]);
+    }
+    if (WITH_OUT) kq = __builtin_fmaf(kr[r], qr[r], kq);
+  }
+#pragma unroll
+  for (int c = 0; c < 4; ++c) u[c] = rowgroup_sum(u[c]);
+  if (WITH_OUT) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) w[c] = rowgroup_sum(w[c]);
+    kq = rowgroup_sum(kq);
+  }
+  float e[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) e[c] = beta * (vc[c] - u[c]);
+  if (WITH_OUT) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) o[c] = scale * __builtin_fmaf(e[c], kq, w[c]);
+  }
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) S[r][c] = __builtin_fmaf(kr[r], e[c], S[r][c]);
+}
+
+template <int R, int DV>
+__device__ __forceinline__ void load_tile(const float* p, float (&S)[R][4]) {
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const float4 x = *reinterpret_cast<const float4*>(p + (size_t)r * DV);
+    S[r][0] = x.x;
+    S[r][1] = x.y;
+    S[r][2] = x.z;
+    S[r][3] = x.w;
+  }
+}
+
+template <int R, int DV>
+__device__ __forceinline__ void store_tile(float* p, const float (&S)[R][4]) {
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+    *reinterpret_cast<float4*>(p + (size_t)r * DV) = make_float4(S[r][0], S[r][1], S[r][2], S[r][3]);
+}
+
+}  // namespace kda

@@ -1,0 +1,73 @@
+// Internal launch interface between the C ABI layer (kda_api.cpp) and the
+// kernel translation units.  Host-only types; no torch, no allocation.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "kda.h"
+
+namespace kda {
+
+// Byte offsets of the four log regions for a log sized for T_max tokens.
+struct LogLayout {
+  size_t k, v, alpha, beta, total;
+};
+
+inline size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+inline LogLayout log_layout(const kda_shape& s, int32_t T_max) {
+  const size_t es = s.in_dtype == KDA_BF16 ? 2 : 4;
+  const size_t tok = (size_t)s.B * (size_t)T_max * (size_t)s.H;
+  LogLayout L;
+  L.k = 0;
+  L.v = round_up(L.k + tok * s.dk * es, 256);
+  L.alpha = round_up(L.v + tok * s.dv * es, 256);
+  L.beta = round_up(L.alpha + tok * s.dk * 4, 256);
+  L.total = round_up(L.beta + tok * 4, 256);
+  return L;
+}
+
+struct TokenInputs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* alpha;
+  const float* beta;
+};
+
+struct LogPtrs {
+  void* k;
+  void* v;
+  float* alpha;
+  float* beta;
+};
+
+hipError_t launch_decode(const kda_shape& s, float* state, int64_t* pos, TokenInputs in, float* o,
+                         hipStream_t st);
+hipError_t launch_verify(const kda_shape& s, int32_t T, const float* state, TokenInputs in, float* o,
+                         LogPtrs log, hipStream_t st);
+hipError_t launch_commit(const kda_shape& s, int32_t T, float* state, int64_t* pos, LogPtrs log,
+                         const int32_t* accepted, int32_t* dev_err, hipStream_t st);
+hipError_t launch_prefill_recurrent(const kda_shape& s, int32_t L, float* state, int64_t* pos,
+                                    TokenInputs in, float* o, int32_t ckpt_every, const int32_t* ckpt_slots,
+                                    float* slot_states, int64_t* slot_pos, int32_t n_slots,
+                                    int32_t* dev_err, hipStream_t st);
+hipError_t launch_prefill_chunked(const kda_shape& s, int32_t L, int32_t chunk, float* state, int64_t* pos,
+                                  TokenInputs in, float* o, int32_t ckpt_every, const int32_t* ckpt_slots,
+                                  float* slot_states, int64_t* slot_pos, int32_t n_slots, int32_t* dev_err,
+                                  hipStream_t st);
+
+// Copies whole per-sequence states (n_floats each) and positions for up to
+// kMaxPairs (src, dst) index pairs per launch.
+constexpr int kMaxPairs = 64;
+struct CopyPairs {
+  int32_t n;
+  int32_t src[kMaxPairs];
+  int32_t dst[kMaxPairs];
+};
+hipError_t launch_copy_states(const float* src, const int64_t* src_pos, float* dst, int64_t* dst_pos,
+                              size_t n_floats, const CopyPairs& pairs, hipStream_t st);
+
+}  // namespace kda

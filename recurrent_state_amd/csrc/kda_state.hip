@@ -1,0 +1,343 @@
+// State-resident KDA kernels for gfx950: decode step, speculative verify,
+// commit (replay of the accepted prefix) and the token-by-token prefill.
+//
+// Every kernel runs one 64-lane wave per 32-column slice of one
+// (sequence, head) state and keeps that slice in registers for as long as it
+// needs it (one token for decode, T tokens for verify, the accepted count for
+// commit, the whole prompt for the recurrent prefill).  All of them call
+// kda::token_update with the same lane mapping, which is what makes commit
+// bit-identical to repeated decode steps.
+//
+// The decode step streams the fp32 state (read + write, 98.6% of its bytes at
+// dk = dv = 128 with bf16 inputs), so it is bound by HBM bandwidth; the loads
+// of one wave-wide instruction cover eight full 128-byte lines.
+// ("Hyper-optimizing Kimi K3 in vLLM", Part 1, section 4: small-batch decode
+// is memory-bound.)
+
+#include <hip/hip_runtime.h>
+
+#include "kda_common.h"
+#include "kda_internal.h"
+
+namespace kda {
+namespace {
+
+template <typename TIn>
+struct StepArgs {
+  float* state;
+  int64_t* pos;
+  const TIn* q;
+  const TIn* k;
+  const TIn* v;
+  const float* alpha;
+  const float* beta;
+  float* o;
+  int32_t H;
+  float scale;
+};
+
+template <typename TIn>
+struct VerifyArgs {
+  const float* state;
+  const TIn* q;
+  const TIn* k;
+  const TIn* v;
+  const float* alpha;
+  const float* beta;
+  float* o;
+  TIn* log_k;
+  TIn* log_v;
+  float* log_alpha;
+  float* log_beta;
+  int32_t H;
+  int32_t T;
+  float scale;
+};
+
+template <typename TIn>
+struct CommitArgs {
+  float* state;
+  int64_t* pos;
+  const TIn* log_k;
+  const TIn* log_v;
+  const float* log_alpha;
+  const float* log_beta;
+  const int32_t* accepted;
+  int32_t* dev_err;
+  int32_t H;
+  int32_t T;
+};
+
+template <typename TIn>
+struct PrefillArgs {
+  float* state;
+  int64_t* pos;
+  const TIn* q;
+  const TIn* k;
+  const TIn* v;
+  const float* alpha;
+  const float* beta;
+  float* o;
+  const int32_t* ckpt_slots;
+  float* slot_states;
+  int64_t* slot_pos;
+  int32_t* dev_err;
+  int32_t H;
+  int32_t L;
+  int32_t ckpt_every;
+  int32_t n_slots;
+  float scale;
+};
+
+// Where a wave sits: its (sequence, head) index and its lane's rows/columns.
+template <int DK, int DV>
+struct Place {
+  static constexpr int R = DK / kRowGroups;
+  static constexpr int SLICES = DV / kSliceCols;
+  int bh, b, h, slice, rg, cg, row0, col0, lane;
+  __device__ __forceinline__ Place(int H) {
+    lane = threadIdx.x;
+    slice = blockIdx.x % SLICES;
+    bh = blockIdx.x / SLICES;
+    b = bh / H;
+    h = bh - b * H;
+    rg = lane >> 3;
+    cg = lane & 7;
+    row0 = rg * R;
+    col0 = slice * kSliceCols + cg * 4;
+  }
+  // Offset of this lane's first state element inside a [dk][dv] state.
+  __device__ __forceinline__ size_t tile_off() const { return (size_t)row0 * DV + col0; }
+};
+
+// The per-token inputs one lane needs, as stored (raw) and widened.
+template <typename TIn, int R, bool WITH_Q>
+struct TokenIn {
+  Raw<TIn, R> k, q;
+  Raw<float, R> a;
+  Raw4<TIn> v;
+  float beta;
+  __device__ __forceinline__ void load(const TIn* kp, const TIn* qp, const float* ap, const TIn* vp,
+                                       const float* bp) {
+    load_raw(kp, k);
+    if (WITH_Q) load_raw(qp, q);
+    load_raw(ap, a);
+    load4(vp, v);
+    beta = *bp;
+  }
+  __device__ __forceinline__ void widen_all(float (&kr)[R], float (&qr)[R], float (&ar)[R], float (&vc)[4]) const {
+    widen(k, kr);
+    if (WITH_Q) widen(q, qr);
+    widen(a, ar);
+    widen4(v, vc);
+  }
+};
+
+template <int DK, int DV, typename TIn>
+__global__ void __launch_bounds__(kWave) decode_kernel(StepArgs<TIn> a) {
+  typedef Place<DK, DV> P;
+  constexpr int R = P::R;
+  const P p(a.H);
+  float* sp = a.state + (size_t)p.bh * DK * DV + p.tile_off();
+  float S[R][4];
+  load_tile<R, DV>(sp, S);
+  TokenIn<TIn, R, true> in;
+  in.load(a.k + (size_t)p.bh * DK + p.row0, a.q + (size_t)p.bh * DK + p.row0,
+          a.alpha + (size_t)p.bh * DK + p.row0, a.v + (size_t)p.bh * DV + p.col0, a.beta + p.bh);
+  float kr[R], qr[R], ar[R], vc[4], o[4];
+  in.widen_all(kr, qr, ar, vc);
+  token_update<R, true>(S, kr, ar, qr, vc, in.beta, a.scale, o);
+  store_tile<R, DV>(sp, S);
+  if (p.rg == 0) *reinterpret_cast<float4*>(a.o + (size_t)p.bh * DV + p.col0) = make_float4(o[0], o[1], o[2], o[3]);
+  if (p.h == 0 && p.slice == 0 && p.lane == 0) a.pos[p.b] += 1;
+}
+
+template <int DK, int DV, typename TIn>
+__global__ void __launch_bounds__(kWave) verify_kernel(VerifyArgs<TIn> a) {
+  typedef Place<DK, DV> P;
+  constexpr int R = P::R;
+  const P p(a.H);
+  float S[R][4];
+  load_tile<R, DV>(a.state + (size_t)p.bh * DK * DV + p.tile_off(), S);
+  TokenIn<TIn, R, true> cur, nxt;
+  size_t tok = (size_t)p.b * a.T * a.H + p.h;  // [B][T][H] index of token 0
+  cur.load(a.k + tok * DK + p.row0, a.q + tok * DK + p.row0, a.alpha + tok * DK + p.row0,
+           a.v + tok * DV + p.col0, a.beta + tok);
+  for (int t = 0; t < a.T; ++t) {
+    const size_t tn = tok + a.H;
+    if (t + 1 < a.T)
+      nxt.load(a.k + tn * DK + p.row0, a.q + tn * DK + p.row0, a.alpha + tn * DK + p.row0,
+               a.v + tn * DV + p.col0, a.beta + tn);
+    float kr[R], qr[R], ar[R], vc[4], o[4];
+    cur.widen_all(kr, qr, ar, vc);
+    token_update<R, true>(S, kr, ar, qr, vc, cur.beta, a.scale, o);
+    if (p.rg == 0) {
+      *reinterpret_cast<float4*>(a.o + tok * DV + p.col0) = make_float4(o[0], o[1], o[2], o[3]);
+      store4(a.log_v + tok * DV + p.col0, cur.v);
+    }
+    if (p.slice == 0 && p.cg == 0) {
+      store_raw(a.log_k + tok * DK + p.row0, cur.k);
+      store_raw(a.log_alpha + tok * DK + p.row0, cur.a);
+      if (p.rg == 0) a.log_beta[tok] = cur.beta;
+    }
+    cur = nxt;
+    tok = tn;
+  }
+}
+
+template <int DK, int DV, typename TIn>
+__global__ void __launch_bounds__(kWave) commit_kernel(CommitArgs<TIn> a) {
+  typedef Place<DK, DV> P;
+  constexpr int R = P::R;
+  const P p(a.H);
+  const int n = a.accepted[p.b];
+  if (n < 0 || n > a.T) {
+    if (p.h == 0 && p.slice == 0 && p.lane == 0) atomicOr(a.dev_err, KDA_DEV_ERR_ACCEPTED);
+    return;
+  }
+  if (n == 0) return;
+  float* sp = a.state + (size_t)p.bh * DK * DV + p.tile_off();
+  float S[R][4];
+  load_tile<R, DV>(sp, S);
+  TokenIn<TIn, R, false> cur, nxt;
+  size_t tok = (size_t)p.b * a.T * a.H + p.h;
+  cur.load(a.log_k + tok * DK + p.row0, nullptr, a.log_alpha + tok * DK + p.row0, a.log_v + tok * DV + p.col0,
+           a.log_beta + tok);
+  for (int t = 0; t < n; ++t) {
+    const size_t tn = tok + a.H;
+    if (t + 1 < n)
+      nxt.load(a.log_k + tn * DK + p.row0, nullptr, a.log_alpha + tn * DK + p.row0, a.log_v + tn * DV + p.col0,
+               a.log_beta + tn);
+    float kr[R], qr[R], ar[R], vc[4], o[4];
+    cur.widen_all(kr, qr, ar, vc);
+    token_update<R, false>(S, kr, ar, qr, vc, cur.beta, 0.f, o);
+    cur = nxt;
+    tok = tn;
+  }
+  store_tile<R, DV>(sp, S);
+  if (p.h == 0 && p.slice == 0 && p.lane == 0) a.pos[p.b] += n;
+}
+
+template <int DK, int DV, typename TIn>
+__global__ void __launch_bounds__(kWave) prefill_recurrent_kernel(PrefillArgs<TIn> a) {
+  typedef Place<DK, DV> P;
+  constexpr int R = P::R;
+  const P p(a.H);
+  const bool owner = p.h == 0 && p.slice == 0 && p.lane == 0;  // the one writer of positions
+  const int64_t pos0 = owner ? a.pos[p.b] : 0;
+  const int n_ckpt = a.ckpt_every > 0 ? a.L / a.ckpt_every : 0;
+  float* sp = a.state + (size_t)p.bh * DK * DV + p.tile_off();
+  float S[R][4];
+  load_tile<R, DV>(sp, S);
+  TokenIn<TIn, R, true> cur, nxt;
+  size_t tok = (size_t)p.b * a.L * a.H + p.h;
+  if (a.L > 0)
+    cur.load(a.k + tok * DK + p.row0, a.q + tok * DK + p.row0, a.alpha + tok * DK + p.row0,
+             a.v + tok * DV + p.col0, a.beta + tok);
+  for (int t = 0; t < a.L; ++t) {
+    const size_t tn = tok + a.H;
+    if (t + 1 < a.L)
+      nxt.load(a.k + tn * DK + p.row0, a.q + tn * DK + p.row0, a.alpha + tn * DK + p.row0,
+               a.v + tn * DV + p.col0, a.beta + tn);
+    float kr[R], qr[R], ar[R], vc[4], o[4];
+    cur.widen_all(kr, qr, ar, vc);
+    token_update<R, true>(S, kr, ar, qr, vc, cur.beta, a.scale, o);
+    if (p.rg == 0) *reinterpret_cast<float4*>(a.o + tok * DV + p.col0) = make_float4(o[0], o[1], o[2], o[3]);
+    if (n_ckpt > 0 && (t + 1) % a.ckpt_every == 0) {
+      const int m = (t + 1) / a.ckpt_every - 1;
+      const int slot = a.ckpt_slots[(size_t)p.b * n_ckpt + m];
+      if (slot >= 0 && slot < a.n_slots) {
+        store_tile<R, DV>(a.slot_states + ((size_t)slot * a.H + p.h) * DK * DV + p.tile_off(), S);
+        if (owner) a.slot_pos[slot] = pos0 + t + 1;
+      } else if (p.slice == 0 && p.lane == 0) {
+        atomicOr(a.dev_err, KDA_DEV_ERR_CKPT_SLOT);
+      }
+    }
+    cur = nxt;
+    tok = tn;
+  }
+  store_tile<R, DV>(sp, S);
+  if (owner) a.pos[p.b] = pos0 + a.L;
+}
+
+template <int DK, int DV>
+dim3 grid_of(const kda_shape& s) {
+  return dim3((unsigned)((size_t)s.B * s.H * (DV / kSliceCols)));
+}
+
+template <int DK_, int DV_, typename TIn_>
+struct Cfg {
+  static constexpr int DK = DK_, DV = DV_;
+  typedef TIn_ TIn;
+};
+
+// Calls f(Cfg<dk, dv, input type>{}) for the shape's instantiation.
+template <typename TIn, typename F>
+void dispatch_d(const kda_shape& s, F&& f) {
+  if (s.dk == 128 && s.dv == 128) f(Cfg<128, 128, TIn>{});
+  else if (s.dk == 128 && s.dv == 64) f(Cfg<128, 64, TIn>{});
+  else if (s.dk == 64 && s.dv == 128) f(Cfg<64, 128, TIn>{});
+  else f(Cfg<64, 64, TIn>{});
+}
+template <typename F>
+void dispatch(const kda_shape& s, F&& f) {
+  if (s.in_dtype == KDA_BF16) dispatch_d<bf16_t>(s, f);
+  else dispatch_d<float>(s, f);
+}
+
+}  // namespace
+
+hipError_t launch_decode(const kda_shape& s, float* state, int64_t* pos, TokenInputs in, float* o,
+                         hipStream_t st) {
+  dispatch(s, [&](auto c) {
+    typedef decltype(c) C;
+    typedef typename C::TIn TIn;
+    constexpr int DK = C::DK, DV = C::DV;
+    StepArgs<TIn> a{state, pos, (const TIn*)in.q, (const TIn*)in.k, (const TIn*)in.v, in.alpha, in.beta, o,
+                    s.H, s.scale};
+    decode_kernel<DK, DV, TIn><<<grid_of<DK, DV>(s), kWave, 0, st>>>(a);
+  });
+  return hipGetLastError();
+}
+
+hipError_t launch_verify(const kda_shape& s, int32_t T, const float* state, TokenInputs in, float* o,
+                         LogPtrs log, hipStream_t st) {
+  dispatch(s, [&](auto c) {
+    typedef decltype(c) C;
+    typedef typename C::TIn TIn;
+    constexpr int DK = C::DK, DV = C::DV;
+    VerifyArgs<TIn> a{state, (const TIn*)in.q, (const TIn*)in.k, (const TIn*)in.v, in.alpha, in.beta, o,
+                      (TIn*)log.k, (TIn*)log.v, log.alpha, log.beta, s.H, T, s.scale};
+    verify_kernel<DK, DV, TIn><<<grid_of<DK, DV>(s), kWave, 0, st>>>(a);
+  });
+  return hipGetLastError();
+}
+
+hipError_t launch_commit(const kda_shape& s, int32_t T, float* state, int64_t* pos, LogPtrs log,
+                         const int32_t* accepted, int32_t* dev_err, hipStream_t st) {
+  dispatch(s, [&](auto c) {
+    typedef decltype(c) C;
+    typedef typename C::TIn TIn;
+    constexpr int DK = C::DK, DV = C::DV;
+    CommitArgs<TIn> a{state, pos, (const TIn*)log.k, (const TIn*)log.v, log.alpha, log.beta, accepted, dev_err,
+                      s.H, T};
+    commit_kernel<DK, DV, TIn><<<grid_of<DK, DV>(s), kWave, 0, st>>>(a);
+  });
+  return hipGetLastError();
+}
+
+hipError_t launch_prefill_recurrent(const kda_shape& s, int32_t L, float* state, int64_t* pos, TokenInputs in,
+                                    float* o, int32_t ckpt_every, const int32_t* ckpt_slots, float* slot_states,
+                                    int64_t* slot_pos, int32_t n_slots, int32_t* dev_err, hipStream_t st) {
+  dispatch(s, [&](auto c) {
+    typedef decltype(c) C;
+    typedef typename C::TIn TIn;
+    constexpr int DK = C::DK, DV = C::DV;
+    PrefillArgs<TIn> a{state, pos, (const TIn*)in.q, (const TIn*)in.k, (const TIn*)in.v, in.alpha, in.beta, o,
+                       ckpt_slots, slot_states, slot_pos, dev_err, s.H, L, ckpt_every, n_slots, s.scale};
+    prefill_recurrent_kernel<DK, DV, TIn><<<grid_of<DK, DV>(s), kWave, 0, st>>>(a);
+  });
+  return hipGetLastError();
+}
+
+}  // namespace kda

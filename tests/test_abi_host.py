@@ -1,0 +1,167 @@
+"""The C ABI on the host: the library loads, exports every function that
+include/kda.h declares, and rejects invalid arguments before enqueuing
+anything.
+
+Every call here is built to fail host-side validation (or to be a pure size
+query), so no kernel is ever launched: the pointers passed are fake but never
+reach a device.  Safe with or without a GPU.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kda.h")
+
+OK, NULL, SHAPE, DTYPE, ALIGN, ORDER, SLOT, HIP = range(8)
+
+
+@pytest.fixture(scope="module")
+def k():
+    import recurrent_state_amd as kda
+    if not os.path.exists(kda.LIB_PATH):
+        from recurrent_state_amd import build
+        build.build()
+    return kda
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kda_\w+)\s*\(", text)))
+
+
+def test_exports_every_declared_function(k):
+    names = declared_functions()
+    assert len(names) >= 12
+    lib = ctypes.CDLL(k.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in kda.h but not exported"
+    assert set(names) == set(k.exported_symbols()), "binding and header disagree"
+    assert k.lib().kda_abi_version() == 1
+
+
+def shape(k, B=2, H=3, dk=128, dv=128, dt=0, scale=0.1):
+    return k.Shape(B, H, dk, dv, dt, scale)
+
+
+P = ctypes.c_void_p
+GOOD = P(0x10000)      # 16-byte aligned fake pointer: only ever paired with an invalid argument
+MIS = P(0x10004)       # misaligned
+
+
+def test_sizes(k):
+    s = shape(k, B=16, H=32)
+    assert k.slot_bytes(s) == 32 * 128 * 128 * 4
+    nb = k.log_bytes(s, 4)
+    tok = 16 * 4 * 32
+    assert nb >= tok * (128 * 2 * 2 + 128 * 4 + 4) and nb % 256 == 0
+    assert k.log_bytes(s, 0) == 0 and k.log_bytes(s, 17) == 0
+    assert k.log_bytes(shape(k, dk=96), 4) == 0 and k.slot_bytes(shape(k, dt=5)) == 0
+    f32 = shape(k, B=16, H=32, dt=1)
+    assert k.log_bytes(f32, 4) > nb
+
+
+def test_decode_validation(k):
+    L = k.lib()
+    dec = lambda s, state=GOOD, pos=GOOD, q=GOOD, o=GOOD: L.kda_decode_step(  # noqa: E731
+        ctypes.byref(s) if s is not None else None, state, pos, q, GOOD, GOOD, GOOD, GOOD, o, None)
+    assert dec(None) == NULL
+    assert dec(shape(k, dk=96)) == SHAPE
+    assert dec(shape(k, dv=256)) == SHAPE
+    assert dec(shape(k, H=0)) == SHAPE
+    assert dec(shape(k, B=-1)) == SHAPE
+    assert dec(shape(k, dt=2)) == DTYPE
+    assert dec(shape(k), state=None) == NULL
+    assert dec(shape(k), q=None) == NULL
+    assert dec(shape(k), pos=None) == NULL
+    assert dec(shape(k), o=MIS) == ALIGN
+    assert dec(shape(k), state=MIS) == ALIGN
+    # An empty batch is a no-op that needs no buffers.
+    assert dec(shape(k, B=0), state=None, pos=None, q=None, o=None) == OK
+
+
+def test_verify_commit_validation(k):
+    L = k.lib()
+    s = shape(k)
+    need = k.log_bytes(s, 4)
+    log = k._lib._Log(0x100000, need, 4, 0)
+    ver = lambda T, lg, st=GOOD: L.kda_verify(ctypes.byref(s), T, st, GOOD, GOOD, GOOD, GOOD, GOOD, GOOD,  # noqa
+                                              ctypes.byref(lg) if lg is not None else None, None)
+    assert ver(1, None) == NULL
+    assert ver(0, log) == SHAPE
+    assert ver(5, log) == SHAPE                                   # T > T_max
+    assert ver(1, k._lib._Log(0x100000, need - 256, 4, 0)) == SHAPE  # buffer too small
+    assert ver(1, k._lib._Log(0x100080, need, 4, 0)) == ALIGN        # log not 256-byte aligned
+    assert ver(1, k._lib._Log(0x100000, need, 4, 2)) == ORDER        # a verify is already pending
+    assert ver(2, log, st=None) == NULL
+    com = lambda lg, acc=GOOD, err=GOOD: L.kda_commit(ctypes.byref(s), GOOD, GOOD, ctypes.byref(lg), acc,  # noqa
+                                                      err, None)
+    assert com(log) == ORDER                                      # nothing pending
+    pend = k._lib._Log(0x100000, need, 4, 3)
+    assert com(pend, acc=None) == NULL
+    assert com(pend, err=None) == NULL
+    assert com(pend, acc=P(0x10002)) == ALIGN
+    assert pend.pending_T == 3, "a rejected commit must not consume the pending verify"
+
+
+def test_snapshot_restore_validation(k):
+    L = k.lib()
+    s = shape(k, B=4)
+    slots = k._lib._Slots(0x200000, 0x300000, 8)
+    ids = lambda *v: (ctypes.c_int32 * len(v))(*v)  # noqa: E731
+    for fn in (L.kda_snapshot, L.kda_restore):
+        assert fn(ctypes.byref(s), GOOD, GOOD, ids(0), ids(8), 1, ctypes.byref(slots), None) == SLOT
+        assert fn(ctypes.byref(s), GOOD, GOOD, ids(4), ids(0), 1, ctypes.byref(slots), None) == SLOT
+        assert fn(ctypes.byref(s), GOOD, GOOD, ids(-1), ids(0), 1, ctypes.byref(slots), None) == SLOT
+        assert fn(ctypes.byref(s), GOOD, GOOD, ids(0, 1), ids(0, -3), 2, ctypes.byref(slots), None) == SLOT
+        assert fn(ctypes.byref(s), GOOD, GOOD, None, ids(0), 1, ctypes.byref(slots), None) == NULL
+        assert fn(ctypes.byref(s), GOOD, GOOD, ids(0), ids(0), -1, ctypes.byref(slots), None) == SHAPE
+        assert fn(ctypes.byref(s), GOOD, GOOD, ids(0), ids(0), 1, None, None) == NULL
+        assert fn(ctypes.byref(s), MIS, GOOD, ids(0), ids(0), 1, ctypes.byref(slots), None) == ALIGN
+        assert fn(ctypes.byref(s), GOOD, GOOD, ids(), ids(), 0, ctypes.byref(slots), None) == OK
+
+
+def test_prefill_validation(k):
+    L = k.lib()
+    s = shape(k)
+    slots = k._lib._Slots(0x200000, 0x300000, 8)
+
+    def pre(Lt=64, chunk=64, every=0, ck=GOOD, sl=slots, err=GOOD, q=GOOD):
+        return L.kda_prefill_chunked(ctypes.byref(s), Lt, chunk, GOOD, GOOD, q, GOOD, GOOD, GOOD, GOOD, GOOD,
+                                     every, ck, ctypes.byref(sl) if sl is not None else None, err, None)
+
+    assert pre(chunk=48) == SHAPE
+    assert pre(Lt=-1) == SHAPE
+    assert pre(every=100) == SHAPE             # not a multiple of the chunk
+    assert pre(every=-64) == SHAPE
+    assert pre(every=64, ck=None) == NULL
+    assert pre(every=64, sl=None) == NULL
+    assert pre(every=64, err=None) == NULL
+    assert pre(q=None) == NULL
+    assert pre(q=MIS) == ALIGN
+    rec = L.kda_prefill_recurrent
+    assert rec(ctypes.byref(s), -2, GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, 0, None, None, None,
+               None) == SHAPE
+    assert rec(ctypes.byref(s), 8, GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, 4, None, None, None,
+               None) == NULL
+
+
+def test_status_strings(k):
+    L = k.lib()
+    names = [L.kda_status_str(i).decode() for i in range(8)]
+    assert names[0] == "ok" and len(set(names)) == 8
+    assert L.kda_status_str(99).decode() == "unknown status"
+
+
+def test_binding_refuses_missing_library(tmp_path, monkeypatch):
+    import recurrent_state_amd._lib as binding
+    monkeypatch.setattr(binding, "LIB_PATH", str(tmp_path / "absent.so"))
+    monkeypatch.setattr(binding, "_lib", None)
+    with pytest.raises(RuntimeError, match="missing"):
+        binding.lib()

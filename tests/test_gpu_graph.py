@@ -1,0 +1,102 @@
+"""The library's launches captured in HIP graphs (as a serving loop replays its
+per-step work) give the same bits as eager launches.
+
+Each graph is replayed several times with unrelated eager work and host
+synchronisation between replays, and every replay is compared with the eager
+result of the same step.
+"""
+
+from __future__ import annotations
+
+import pytest
+import torch
+
+import recurrent_state_amd as kda
+import synth
+from tests.kda_testutil import bits, dev_tensor, say
+
+pytestmark = pytest.mark.gpu
+
+SPEC = synth.ConfigSpec("graph", 110, (4,), 8, 128, 128, "bf16", "softplus", "normal", 0)
+
+
+def steps_major(inp):
+    return {k: dev_tensor(v).transpose(0, 1).contiguous() for k, v in inp.items()}
+
+
+def test_decode_graph_replays_match_eager():
+    B, layers, n = 4, 3, 6
+    say("graph: decode")
+    S0 = dev_tensor(synth.initial_state(SPEC, B))
+    d = steps_major(synth.token_inputs(SPEC, B, n))
+    o_e = torch.empty((B, SPEC.H, 128), device="cuda")
+    SA = [S0.clone() for _ in range(layers)]
+    posA = torch.zeros(B, dtype=torch.int64, device="cuda")
+    ref = []
+    for t in range(n):
+        for S in SA:
+            kda.decode_step(S, posA, d["q"][t], d["k"][t], d["v"][t], d["alpha"][t], d["beta"][t], o_e)
+        ref.append(([bits(S).clone() for S in SA], bits(o_e).clone(), posA.clone()))
+    SB = [S0.clone() for _ in range(layers)]
+    posB = torch.zeros(B, dtype=torch.int64, device="cuda")
+    o_g = torch.empty_like(o_e)
+    graphs = []
+    for t in range(n):
+        plans = [kda.DecodePlan(S, posB, d["q"][t], d["k"][t], d["v"][t], d["alpha"][t], d["beta"][t], o_g)
+                 for S in SB]
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for p in plans:
+                p()
+        graphs.append(g)
+    torch.cuda.synchronize()
+    assert posB.sum().item() == 0, "capture must not run the kernels"
+    for t in range(n):
+        graphs[t].replay()
+        junk = torch.randn(1000, device="cuda").cumsum(0)  # unrelated eager work between replays
+        torch.cuda.synchronize()
+        assert junk.numel() == 1000
+        states, o_ref, pos_ref = ref[t]
+        for l in range(layers):
+            assert torch.equal(bits(SB[l]), states[l]), f"replay {t} layer {l}"
+        assert torch.equal(bits(o_g), o_ref) and torch.equal(posB, pos_ref)
+
+
+def test_verify_commit_graph_replays_match_eager():
+    B, T, rounds = 4, 3, 4
+    say("graph: verify + commit")
+    S0 = dev_tensor(synth.initial_state(SPEC, B))
+    d = {k: dev_tensor(v) for k, v in synth.token_inputs(SPEC, B, T).items()}
+    counts = [[3, 0, 1, 2], [0, 0, 0, 0], [2, 3, 3, 1], [1, 2, 0, 3]]
+    # Eager reference.
+    SA = S0.clone()
+    posA = torch.zeros(B, dtype=torch.int64, device="cuda")
+    logA = kda.InputLog(SA, T_max=T)
+    errA = torch.zeros(1, dtype=torch.int32, device="cuda")
+    oA = torch.empty((B, T, SPEC.H, 128), device="cuda")
+    ref = []
+    for r in range(rounds):
+        kda.verify(SA, d["q"], d["k"], d["v"], d["alpha"], d["beta"], oA, logA)
+        kda.commit(SA, posA, logA, torch.tensor(counts[r], dtype=torch.int32, device="cuda"), errA)
+        ref.append((bits(SA).clone(), bits(oA).clone(), posA.clone()))
+    # One captured round, replayed with new accepted counts written in between.
+    SB = S0.clone()
+    posB = torch.zeros(B, dtype=torch.int64, device="cuda")
+    logB = kda.InputLog(SB, T_max=T)
+    errB = torch.zeros(1, dtype=torch.int32, device="cuda")
+    oB = torch.empty_like(oA)
+    acc = torch.zeros(B, dtype=torch.int32, device="cuda")
+    vp = kda.VerifyPlan(SB, d["q"], d["k"], d["v"], d["alpha"], d["beta"], oB, logB)
+    cp = kda.CommitPlan(SB, posB, logB, acc, errB)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        vp()
+        cp()
+    assert logB.pending_T == 0
+    for r in range(rounds):
+        acc.copy_(torch.tensor(counts[r], dtype=torch.int32))
+        g.replay()
+        torch.cuda.synchronize()
+        S_ref, o_ref, pos_ref = ref[r]
+        assert torch.equal(bits(SB), S_ref) and torch.equal(bits(oB), o_ref) and torch.equal(posB, pos_ref), r
+    assert errA.item() == 0 and errB.item() == 0

@@ -1,0 +1,242 @@
+"""GPU parity and bookkeeping on small shapes (every dk/dv/dtype combination).
+
+Parity: the HIP path against the fp64 oracle at the tolerance bar.  Bit-exact
+bookkeeping: commit(a) equals a decode steps, verify outputs equal decode
+outputs, a = 0 leaves the state untouched, snapshot/restore round-trips, and
+positions add up; these compare GPU results with each other.  Every test also
+checks that the kernel variant it meant to exercise is the one that ran.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import recurrent_state_amd as kda
+import synth
+from oracle import kda_oracle as ko
+from tests.kda_testutil import assert_parity, bits, dev_inputs, dev_tensor, say, token_slice
+
+pytestmark = pytest.mark.gpu
+
+SHAPES = [(64, 64, "f32"), (64, 128, "bf16"), (128, 64, "f32"), (128, 128, "bf16"), (128, 128, "f32"),
+          (64, 64, "bf16")]
+
+
+def spec_for(dk, dv, dt, gate="softplus", tag=100):
+    return synth.ConfigSpec(f"s{dk}x{dv}{dt}", tag, (3,), 5, dk, dv, dt, gate, "normal", 0)
+
+
+def decode_run(S, pos, inp_dev, scale=None):
+    B, H, _, dv = S.shape
+    n = inp_dev["k"].shape[1]
+    outs = []
+    for t in range(n):
+        o = torch.empty((B, 1, H, dv), dtype=torch.float32, device=S.device)
+        tok = token_slice(inp_dev, t, t + 1)
+        kda.decode_step(S, pos, tok["q"].contiguous(), tok["k"].contiguous(), tok["v"].contiguous(),
+                        tok["alpha"].contiguous(), tok["beta"].contiguous(), o, scale=scale)
+        outs.append(o)
+    if not outs:
+        return torch.empty((B, 0, H, dv), dtype=torch.float32, device=S.device)
+    return torch.cat(outs, dim=1)
+
+
+@pytest.mark.parametrize("dk,dv,dt", SHAPES)
+def test_decode_matches_oracle(dk, dv, dt):
+    spec = spec_for(dk, dv, dt)
+    B, n = 3, 40
+    say(f"decode dk={dk} dv={dv} {dt} B={B} steps={n}")
+    S0 = synth.initial_state(spec, B)
+    inp = synth.token_inputs(spec, B, n)
+    S = dev_tensor(S0)
+    pos = torch.zeros(B, dtype=torch.int64, device="cuda")
+    o = decode_run(S, pos, dev_inputs(inp))
+    assert kda.last_variant() == "decode"
+    S_ref, o_ref = ko.decode(S0, inp, spec.scale)
+    assert_parity(o.cpu().numpy(), o_ref, S.cpu().numpy(), S_ref, f"decode {dk}x{dv} {dt}")
+    assert pos.cpu().tolist() == [n] * B
+
+
+@pytest.mark.parametrize("dk,dv,dt", SHAPES)
+@pytest.mark.parametrize("T", [1, 3, 8])
+def test_verify_commit_matches_oracle_and_decode(dk, dv, dt, T):
+    spec = spec_for(dk, dv, dt, tag=101)
+    B = 3
+    say(f"verify/commit dk={dk} dv={dv} {dt} T={T}")
+    S0 = synth.initial_state(spec, B)
+    inp = synth.token_inputs(spec, B, T)
+    d = dev_inputs(inp)
+    S = dev_tensor(S0)
+    S_keep = S.clone()
+    pos = torch.tensor([7, 0, 3], dtype=torch.int64, device="cuda")
+    log = kda.InputLog(S, T_max=8, in_dtype=d["q"].dtype)
+    o = torch.empty((B, T, spec.H, dv), dtype=torch.float32, device="cuda")
+    kda.verify(S, d["q"], d["k"], d["v"], d["alpha"], d["beta"], o, log)
+    assert kda.last_variant() == "verify" and log.pending_T == T
+    assert torch.equal(bits(S), bits(S_keep)), "verify must not write the committed state"
+    _, o_ref = ko.decode(S0, inp, spec.scale)
+    assert_parity(o.cpu().numpy(), o_ref, what=f"verify T={T}")
+    # Bit-exact: verify outputs equal decode outputs token by token.
+    S_dec = S.clone()
+    pos_dec = pos.clone()
+    o_dec = decode_run(S_dec, pos_dec, d)
+    assert torch.equal(bits(o), bits(o_dec))
+    # Commit a different count per sequence; compare with that many decode steps.
+    acc = [T, 0, min(1, T)] if T > 1 else [1, 0, 1]
+    accepted = torch.tensor(acc, dtype=torch.int32, device="cuda")
+    dev_err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    kda.commit(S, pos, log, accepted, dev_err)
+    assert kda.last_variant() == "commit" and log.pending_T == 0
+    assert dev_err.item() == 0
+    for b, a in enumerate(acc):
+        Sb = S_keep[b:b + 1].clone()
+        pb = torch.zeros(1, dtype=torch.int64, device="cuda")
+        decode_run(Sb, pb, {k_: v_[b:b + 1, :a] for k_, v_ in d.items()})
+        assert torch.equal(bits(S[b:b + 1]), bits(Sb)), f"commit({a}) != {a} decode steps (seq {b})"
+    assert pos.cpu().tolist() == [7 + acc[0], 0 + acc[1], 3 + acc[2]]
+
+
+def test_commit_rejects_out_of_range_counts():
+    spec = spec_for(128, 128, "bf16", tag=102)
+    B, T = 3, 4
+    S0 = synth.initial_state(spec, B)
+    d = dev_inputs(synth.token_inputs(spec, B, T))
+    S = dev_tensor(S0)
+    S_keep = S.clone()
+    pos = torch.zeros(B, dtype=torch.int64, device="cuda")
+    log = kda.InputLog(S, T_max=4)
+    o = torch.empty((B, T, spec.H, 128), dtype=torch.float32, device="cuda")
+    kda.verify(S, d["q"], d["k"], d["v"], d["alpha"], d["beta"], o, log)
+    dev_err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    kda.commit(S, pos, log, torch.tensor([-1, 5, 2], dtype=torch.int32, device="cuda"), dev_err)
+    assert dev_err.item() == kda.DEV_ERR_ACCEPTED
+    assert torch.equal(bits(S[:2]), bits(S_keep[:2])) and not torch.equal(bits(S[2]), bits(S_keep[2]))
+    assert pos.cpu().tolist() == [0, 0, 2]
+
+
+def test_order_errors():
+    spec = spec_for(64, 64, "f32", tag=103)
+    S = dev_tensor(synth.initial_state(spec, 3))
+    pos = torch.zeros(3, dtype=torch.int64, device="cuda")
+    d = dev_inputs(synth.token_inputs(spec, 3, 2))
+    log = kda.InputLog(S, T_max=2, in_dtype=torch.float32)
+    acc = torch.zeros(3, dtype=torch.int32, device="cuda")
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    with pytest.raises(kda.KdaError) as ei:
+        kda.commit(S, pos, log, acc, err)
+    assert ei.value.status == 5
+    o = torch.empty((3, 2, spec.H, 64), dtype=torch.float32, device="cuda")
+    kda.verify(S, d["q"], d["k"], d["v"], d["alpha"], d["beta"], o, log)
+    with pytest.raises(kda.KdaError) as ei:
+        kda.verify(S, d["q"], d["k"], d["v"], d["alpha"], d["beta"], o, log)
+    assert ei.value.status == 5
+    kda.commit(S, pos, log, acc, err)
+    torch.cuda.synchronize()
+
+
+def test_snapshot_restore_bitwise():
+    spec = spec_for(128, 128, "bf16", tag=104)
+    B = 4
+    S = dev_tensor(synth.initial_state(spec, B))
+    pos = torch.tensor([11, 22, 33, 44], dtype=torch.int64, device="cuda")
+    pool = kda.SlotPool(6, spec.H, 128, 128, "cuda")
+    kda.snapshot(S, pos, [2, 0, 3], [5, 1, 1], pool)   # slot 1 written twice: the later pair wins
+    assert kda.last_variant() == "snapshot"
+    assert torch.equal(bits(pool.states[5]), bits(S[2])) and torch.equal(bits(pool.states[1]), bits(S[3]))
+    assert pool.pos.cpu().tolist() == [-1, 44, -1, -1, -1, 33]
+    live = torch.zeros_like(S)
+    lpos = torch.zeros(B, dtype=torch.int64, device="cuda")
+    kda.restore(live, lpos, [0, 3], [5, 1], pool)
+    assert kda.last_variant() == "restore"
+    assert torch.equal(bits(live[0]), bits(S[2])) and torch.equal(bits(live[3]), bits(S[3]))
+    assert not live[1].any() and lpos.cpu().tolist() == [33, 0, 0, 44]
+    with pytest.raises(kda.KdaError):
+        kda.snapshot(S, pos, [4], [0], pool)
+    with pytest.raises(kda.KdaError):
+        kda.restore(live, lpos, [0], [6], pool)
+
+
+def test_snapshot_many_pairs_batches():
+    # More pairs than one launch carries: exercises the host-side batching.
+    spec = spec_for(64, 64, "f32", tag=105)
+    B = 70
+    S = torch.randn((B, 2, 64, 64), device="cuda")
+    pos = torch.arange(B, dtype=torch.int64, device="cuda")
+    pool = kda.SlotPool(B, 2, 64, 64, "cuda")
+    kda.snapshot(S, pos, list(range(B)), list(reversed(range(B))), pool)
+    assert torch.equal(bits(pool.states), bits(S.flip(0)))
+    assert torch.equal(pool.pos, pos.flip(0))
+
+
+@pytest.mark.parametrize("dk,dv,dt", [(128, 128, "bf16"), (64, 64, "f32"), (64, 128, "bf16")])
+@pytest.mark.parametrize("L", [1, 37, 96])
+def test_prefill_recurrent_matches_oracle_and_decode(dk, dv, dt, L):
+    spec = spec_for(dk, dv, dt, tag=106)
+    B = 2
+    every = 32
+    say(f"prefill_recurrent dk={dk} dv={dv} {dt} L={L}")
+    S0 = synth.initial_state(spec, B)
+    inp = synth.token_inputs(spec, B, L)
+    d = dev_inputs(inp)
+    S = dev_tensor(S0)
+    pos = torch.tensor([5, 0], dtype=torch.int64, device="cuda")
+    n_ck = L // every
+    pool = kda.SlotPool(max(1, 2 * n_ck), spec.H, dk, dv, "cuda")
+    slots = torch.arange(2 * n_ck, dtype=torch.int32, device="cuda").view(2, n_ck) if n_ck else None
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    o = torch.empty((B, L, spec.H, dv), dtype=torch.float32, device="cuda")
+    kda.prefill_recurrent(S, pos, d["q"], d["k"], d["v"], d["alpha"], d["beta"], o, ckpt_every=every,
+                          ckpt_slots=slots, pool=pool, dev_err=err)
+    assert kda.last_variant() == "prefill_recurrent"
+    S_ref, pos_ref, o_ref, ck = ko.prefill(S0, np.array([5, 0]), inp, spec.scale, every)
+    assert_parity(o.cpu().numpy(), o_ref, S.cpu().numpy(), S_ref, f"prefill_recurrent L={L}")
+    assert pos.cpu().tolist() == pos_ref.tolist() and err.item() == 0
+    for m, (Sm, pm) in enumerate(ck):
+        for b in range(B):
+            slot = b * n_ck + m
+            assert_parity(o.cpu().numpy(), o_ref, pool.states[slot:slot + 1].cpu().numpy(), Sm[b:b + 1],
+                          f"checkpoint {m} seq {b}")
+            assert pool.pos[slot].item() == pm[b]
+    # Bit-exact with L decode steps from the same state.
+    S2 = dev_tensor(S0)
+    decode_run(S2, torch.zeros(B, dtype=torch.int64, device="cuda"), d)
+    assert torch.equal(bits(S), bits(S2))
+
+
+def test_prefill_bad_checkpoint_slot_flags_error():
+    spec = spec_for(64, 64, "f32", tag=107)
+    B, L = 2, 8
+    d = dev_inputs(synth.token_inputs(spec, B, L))
+    S = dev_tensor(synth.initial_state(spec, B))
+    pos = torch.zeros(B, dtype=torch.int64, device="cuda")
+    pool = kda.SlotPool(2, spec.H, 64, 64, "cuda")
+    slots = torch.tensor([[0], [9]], dtype=torch.int32, device="cuda")
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    o = torch.empty((B, L, spec.H, 64), dtype=torch.float32, device="cuda")
+    kda.prefill_recurrent(S, pos, d["q"], d["k"], d["v"], d["alpha"], d["beta"], o, ckpt_every=8,
+                          ckpt_slots=slots, pool=pool, dev_err=err)
+    assert err.item() == kda.DEV_ERR_CKPT_SLOT
+    assert pool.pos.cpu().tolist() == [8, -1]
+
+
+def test_empty_batch_is_noop():
+    S = torch.zeros((0, 2, 64, 64), device="cuda")
+    pos = torch.zeros(0, dtype=torch.int64, device="cuda")
+    z = lambda *s, dt=torch.float32: torch.zeros(s, dtype=dt, device="cuda")  # noqa: E731
+    kda.decode_step(S, pos, z(0, 1, 2, 64), z(0, 1, 2, 64), z(0, 1, 2, 64), z(0, 1, 2, 64), z(0, 1, 2),
+                    z(0, 1, 2, 64))
+
+
+def test_decode_is_deterministic():
+    spec = spec_for(128, 128, "bf16", tag=108)
+    B = 4
+    S0 = dev_tensor(synth.initial_state(spec, B))
+    d = dev_inputs(synth.token_inputs(spec, B, 3))
+    outs = []
+    for _ in range(2):
+        S = S0.clone()
+        o = decode_run(S, torch.zeros(B, dtype=torch.int64, device="cuda"), d)
+        outs.append((bits(S).clone(), bits(o).clone()))
+    assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
