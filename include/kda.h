@@ -32,8 +32,10 @@
  * the host and then only enqueues kernels on `stream` (a hipStream_t; NULL
  * is the null stream).  Results are available when the stream reaches them.
  *
- * Alignment: every device pointer must be 16-byte aligned; the log buffer
- * 256-byte aligned.
+ * Alignment: state, q, k, v, alpha, o and the slot states must be 16-byte
+ * aligned; beta, accepted, dev_err and checkpoint slot ids 4-byte; pos and
+ * slot positions 8-byte; the log buffer 256-byte.  (Any row-aligned slice of
+ * a dense tensor along B, T or H satisfies these.)
  *
  * Errors: argument errors are detected on the host before anything is
  * enqueued and return a status without side effects.  Values the host

@@ -40,6 +40,17 @@ kda_status check_ptrs(std::initializer_list<const void*> ps) {
   return KDA_OK;
 }
 
+// Per-token inputs and outputs: q, k, v, alpha, o are read/written with
+// 16-byte vector accesses; beta is read one float at a time.
+kda_status check_tokens(const void* q, const void* k, const void* v, const float* alpha, const float* beta,
+                        const float* o) {
+  kda_status r = check_ptrs({q, k, v, alpha, o});
+  if (r != KDA_OK) return r;
+  if (!beta) return KDA_ERR_NULL;
+  if (!aligned(beta, 4)) return KDA_ERR_ALIGN;
+  return KDA_OK;
+}
+
 kda_status launched(hipError_t e, int32_t variant) {
   if (e != hipSuccess) return KDA_ERR_HIP;
   g_last_variant = variant;
@@ -118,7 +129,7 @@ kda_status check_prefill(const kda_shape* shape, int32_t L, int32_t chunk, float
   if ((int64_t)shape->B * L * shape->H > (int64_t)1 << 40) return KDA_ERR_SHAPE;
   if (shape->B == 0) return KDA_OK;
   if (!state || !pos) return KDA_ERR_NULL;
-  if (L > 0 && (r = check_ptrs({q, k, v, alpha, beta, o})) != KDA_OK) return r;
+  if (L > 0 && (r = check_tokens(q, k, v, alpha, beta, o)) != KDA_OK) return r;
   if ((r = check_ptrs({state})) != KDA_OK) return r;
   if (!aligned(pos, 8)) return KDA_ERR_ALIGN;
   if (ckpt_every > 0 && L >= ckpt_every) {
@@ -148,7 +159,8 @@ kda_status kda_decode_step(const kda_shape* shape, float* state, int64_t* pos, c
   kda_status r = check_shape(shape);
   if (r != KDA_OK) return r;
   if (shape->B == 0) return KDA_OK;
-  if ((r = check_ptrs({state, q, k, v, alpha, beta, o})) != KDA_OK) return r;
+  if ((r = check_ptrs({state})) != KDA_OK) return r;
+  if ((r = check_tokens(q, k, v, alpha, beta, o)) != KDA_OK) return r;
   if (!pos) return KDA_ERR_NULL;
   if (!aligned(pos, 8)) return KDA_ERR_ALIGN;
   return launched(kda::launch_decode(*shape, state, pos, kda::TokenInputs{q, k, v, alpha, beta}, o,
@@ -164,7 +176,8 @@ kda_status kda_verify(const kda_shape* shape, int32_t T, const float* state, con
   if (T < 1 || T > log->T_max) return KDA_ERR_SHAPE;
   if (log->pending_T != 0) return KDA_ERR_ORDER;
   if (shape->B > 0) {
-    if ((r = check_ptrs({state, q, k, v, alpha, beta, o})) != KDA_OK) return r;
+    if ((r = check_ptrs({state})) != KDA_OK) return r;
+    if ((r = check_tokens(q, k, v, alpha, beta, o)) != KDA_OK) return r;
     r = launched(kda::launch_verify(*shape, T, state, kda::TokenInputs{q, k, v, alpha, beta}, o,
                                     log_ptrs(*shape, log), static_cast<hipStream_t>(stream)),
                  KDA_VARIANT_VERIFY);
