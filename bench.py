@@ -306,6 +306,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--quick", action="store_true", help="headline only")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--with-copy-ref", action="store_true",
+                    help="also run one 256 MiB device copy (known bytes) to scale profiler byte counters")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: this library's path has no multi-GPU part "
@@ -322,6 +324,14 @@ def main():
     torch.cuda.set_device(device)
     props = torch.cuda.get_device_properties(device)
     log(f"device: {props.name}, {props.multi_processor_count} CUs")
+
+    if args.with_copy_ref:
+        ref_a = torch.ones(1 << 26, dtype=torch.float32, device=device)   # 256 MiB
+        ref_b = torch.empty_like(ref_a)
+        ref_b.copy_(ref_a)
+        torch.cuda.synchronize()
+        log("copy reference: 268435456 bytes read, 268435456 bytes written")
+        del ref_a, ref_b
 
     log("headline: decode B=64 x 8 layers")
     head = bench_decode(torch, kda, synth, B_HEAD, L_LAYERS, args.steps, args.warmup, device)

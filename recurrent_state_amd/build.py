@@ -40,9 +40,9 @@ def hipcc() -> str:
     return "hipcc"
 
 
-def build(verbose: bool = False, extra_flags=()) -> str:
-    """Compile every HIP/C++ source into libkda.so; returns its path."""
-    tmp = LIB + ".tmp"
+def build(verbose: bool = False, extra_flags=(), out: str = LIB) -> str:
+    """Compile every HIP/C++ source into libkda.so (or `out`); returns its path."""
+    tmp = out + ".tmp"
     cmd = [hipcc(), *HIPCC_FLAGS, *extra_flags, "-I", os.path.join(ROOT, "include"), "-I", CSRC,
            *[os.path.join(CSRC, s) for s in SOURCES], "-o", tmp]
     if verbose:
@@ -52,8 +52,8 @@ def build(verbose: bool = False, extra_flags=()) -> str:
         raise RuntimeError(f"hipcc failed ({res.returncode}):\n{res.stderr[-8000:]}")
     if verbose and res.stderr.strip():
         print(res.stderr[-4000:], file=sys.stderr)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":

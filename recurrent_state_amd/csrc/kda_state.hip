@@ -89,16 +89,28 @@ struct PrefillArgs {
   float scale;
 };
 
+// Waves per workgroup: the column slices of one (sequence, head) are either
+// spread over independent one-wave workgroups (1) or kept together in one
+// workgroup on one CU (all slices).  The waves never synchronise either way.
+#ifndef KDA_STATE_WAVES
+#define KDA_STATE_WAVES 1
+#endif
+template <int DV>
+constexpr int waves_per_group() {
+  return KDA_STATE_WAVES < DV / kSliceCols ? KDA_STATE_WAVES : DV / kSliceCols;
+}
+
 // Where a wave sits: its (sequence, head) index and its lane's rows/columns.
 template <int DK, int DV>
 struct Place {
   static constexpr int R = DK / kRowGroups;
   static constexpr int SLICES = DV / kSliceCols;
+  static constexpr int WPG = waves_per_group<DV>();
   int bh, b, h, slice, rg, cg, row0, col0, lane;
   __device__ __forceinline__ Place(int H) {
-    lane = threadIdx.x;
-    slice = blockIdx.x % SLICES;
-    bh = blockIdx.x / SLICES;
+    lane = threadIdx.x & (kWave - 1);
+    slice = (blockIdx.x % (SLICES / WPG)) * WPG + (threadIdx.x >> 6);
+    bh = blockIdx.x / (SLICES / WPG);
     b = bh / H;
     h = bh - b * H;
     rg = lane >> 3;
@@ -134,7 +146,7 @@ struct TokenIn {
 };
 
 template <int DK, int DV, typename TIn>
-__global__ void __launch_bounds__(kWave) decode_kernel(StepArgs<TIn> a) {
+__global__ void __launch_bounds__(kWave * waves_per_group<DV>()) decode_kernel(StepArgs<TIn> a) {
   typedef Place<DK, DV> P;
   constexpr int R = P::R;
   const P p(a.H);
@@ -153,7 +165,7 @@ __global__ void __launch_bounds__(kWave) decode_kernel(StepArgs<TIn> a) {
 }
 
 template <int DK, int DV, typename TIn>
-__global__ void __launch_bounds__(kWave) verify_kernel(VerifyArgs<TIn> a) {
+__global__ void __launch_bounds__(kWave * waves_per_group<DV>()) verify_kernel(VerifyArgs<TIn> a) {
   typedef Place<DK, DV> P;
   constexpr int R = P::R;
   const P p(a.H);
@@ -186,7 +198,7 @@ __global__ void __launch_bounds__(kWave) verify_kernel(VerifyArgs<TIn> a) {
 }
 
 template <int DK, int DV, typename TIn>
-__global__ void __launch_bounds__(kWave) commit_kernel(CommitArgs<TIn> a) {
+__global__ void __launch_bounds__(kWave * waves_per_group<DV>()) commit_kernel(CommitArgs<TIn> a) {
   typedef Place<DK, DV> P;
   constexpr int R = P::R;
   const P p(a.H);
@@ -219,7 +231,7 @@ __global__ void __launch_bounds__(kWave) commit_kernel(CommitArgs<TIn> a) {
 }
 
 template <int DK, int DV, typename TIn>
-__global__ void __launch_bounds__(kWave) prefill_recurrent_kernel(PrefillArgs<TIn> a) {
+__global__ void __launch_bounds__(kWave * waves_per_group<DV>()) prefill_recurrent_kernel(PrefillArgs<TIn> a) {
   typedef Place<DK, DV> P;
   constexpr int R = P::R;
   const P p(a.H);
@@ -262,7 +274,7 @@ __global__ void __launch_bounds__(kWave) prefill_recurrent_kernel(PrefillArgs<TI
 
 template <int DK, int DV>
 dim3 grid_of(const kda_shape& s) {
-  return dim3((unsigned)((size_t)s.B * s.H * (DV / kSliceCols)));
+  return dim3((unsigned)((size_t)s.B * s.H * (DV / kSliceCols) / waves_per_group<DV>()));
 }
 
 template <int DK_, int DV_, typename TIn_>
@@ -295,7 +307,7 @@ hipError_t launch_decode(const kda_shape& s, float* state, int64_t* pos, TokenIn
     constexpr int DK = C::DK, DV = C::DV;
     StepArgs<TIn> a{state, pos, (const TIn*)in.q, (const TIn*)in.k, (const TIn*)in.v, in.alpha, in.beta, o,
                     s.H, s.scale};
-    decode_kernel<DK, DV, TIn><<<grid_of<DK, DV>(s), kWave, 0, st>>>(a);
+    decode_kernel<DK, DV, TIn><<<grid_of<DK, DV>(s), kWave * waves_per_group<DV>(), 0, st>>>(a);
   });
   return hipGetLastError();
 }
@@ -308,7 +320,7 @@ hipError_t launch_verify(const kda_shape& s, int32_t T, const float* state, Toke
     constexpr int DK = C::DK, DV = C::DV;
     VerifyArgs<TIn> a{state, (const TIn*)in.q, (const TIn*)in.k, (const TIn*)in.v, in.alpha, in.beta, o,
                       (TIn*)log.k, (TIn*)log.v, log.alpha, log.beta, s.H, T, s.scale};
-    verify_kernel<DK, DV, TIn><<<grid_of<DK, DV>(s), kWave, 0, st>>>(a);
+    verify_kernel<DK, DV, TIn><<<grid_of<DK, DV>(s), kWave * waves_per_group<DV>(), 0, st>>>(a);
   });
   return hipGetLastError();
 }
@@ -321,7 +333,7 @@ hipError_t launch_commit(const kda_shape& s, int32_t T, float* state, int64_t* p
     constexpr int DK = C::DK, DV = C::DV;
     CommitArgs<TIn> a{state, pos, (const TIn*)log.k, (const TIn*)log.v, log.alpha, log.beta, accepted, dev_err,
                       s.H, T};
-    commit_kernel<DK, DV, TIn><<<grid_of<DK, DV>(s), kWave, 0, st>>>(a);
+    commit_kernel<DK, DV, TIn><<<grid_of<DK, DV>(s), kWave * waves_per_group<DV>(), 0, st>>>(a);
   });
   return hipGetLastError();
 }
@@ -335,7 +347,7 @@ hipError_t launch_prefill_recurrent(const kda_shape& s, int32_t L, float* state,
     constexpr int DK = C::DK, DV = C::DV;
     PrefillArgs<TIn> a{state, pos, (const TIn*)in.q, (const TIn*)in.k, (const TIn*)in.v, in.alpha, in.beta, o,
                        ckpt_slots, slot_states, slot_pos, dev_err, s.H, L, ckpt_every, n_slots, s.scale};
-    prefill_recurrent_kernel<DK, DV, TIn><<<grid_of<DK, DV>(s), kWave, 0, st>>>(a);
+    prefill_recurrent_kernel<DK, DV, TIn><<<grid_of<DK, DV>(s), kWave * waves_per_group<DV>(), 0, st>>>(a);
   });
   return hipGetLastError();
 }
