@@ -357,7 +357,7 @@ def main():
         log("snapshot/restore")
         rows["snapshot_restore"] = bench_snapshot_restore(torch, kda, synth, device)
         log("prefill")
-        for variant in ("recurrent",):
+        for variant in ("chunked", "recurrent"):
             rows[f"prefill_{variant}"] = bench_prefill(torch, kda, synth, device, variant)
 
     cpu = None if args.no_cpu else cpu_baseline(synth)

@@ -50,7 +50,7 @@
  * by the caller (same stream or events).
  *
  * Supported sizes: dk, dv in {64, 128}; B >= 0 (B = 0 is a no-op); H >= 1;
- * verify 1 <= T <= T_max <= 16; prefill chunk in {16, 32, 64}.
+ * verify 1 <= T <= T_max <= 16; prefill chunk in {32, 64}.
  */
 #ifndef KDA_H
 #define KDA_H

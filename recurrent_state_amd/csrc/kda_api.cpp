@@ -124,7 +124,7 @@ kda_status check_prefill(const kda_shape* shape, int32_t L, int32_t chunk, float
                          int32_t* dev_err) {
   kda_status r = check_shape(shape);
   if (r != KDA_OK) return r;
-  if (L < 0 || !(chunk == 16 || chunk == 32 || chunk == 64)) return KDA_ERR_SHAPE;
+  if (L < 0 || !(chunk == 32 || chunk == 64)) return KDA_ERR_SHAPE;
   if (ckpt_every < 0 || (ckpt_every > 0 && ckpt_every % chunk != 0)) return KDA_ERR_SHAPE;
   if ((int64_t)shape->B * L * shape->H > (int64_t)1 << 40) return KDA_ERR_SHAPE;
   if (shape->B == 0) return KDA_OK;
@@ -259,10 +259,9 @@ kda_status kda_prefill_recurrent(const kda_shape* shape, int32_t L, float* state
                                  const void* k, const void* v, const float* alpha, const float* beta, float* o,
                                  int32_t ckpt_every, const int32_t* ckpt_slots, const kda_slots* slots,
                                  int32_t* dev_err, void* stream) {
-  // Same checks as the chunked form; the chunk size does not apply, so any
-  // positive checkpoint interval is allowed (validated with chunk = 16 after
-  // rounding the interval check out).
-  kda_status r = check_prefill(shape, L, 16, state, pos, q, k, v, alpha, beta, o, 0, nullptr, nullptr, dev_err);
+  // Same checks as the chunked form except the chunk size, which does not
+  // apply here, so any positive checkpoint interval is allowed.
+  kda_status r = check_prefill(shape, L, 32, state, pos, q, k, v, alpha, beta, o, 0, nullptr, nullptr, dev_err);
   if (r != KDA_OK || shape->B == 0) return r;
   if (ckpt_every < 0) return KDA_ERR_SHAPE;
   const bool ck = ckpt_every > 0 && L >= ckpt_every;

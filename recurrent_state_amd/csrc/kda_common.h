@@ -81,6 +81,20 @@ __device__ __forceinline__ void widen(const Raw<float, N>& r, float (&x)[N]) {
   }
 }
 
+// Element r of a raw row run, widened to fp32 (r is a compile-time constant
+// after unrolling, so this is one shift/mask or a register read).
+template <int N>
+__device__ __forceinline__ float elem(const Raw<bf16_t, N>& r, int i) {
+  const uint4 w = r.w[i / 8];
+  const uint32_t x = (i % 8) < 2 ? w.x : (i % 8) < 4 ? w.y : (i % 8) < 6 ? w.z : w.w;
+  return (i & 1) ? bf16_hi(x) : bf16_lo(x);
+}
+template <int N>
+__device__ __forceinline__ float elem(const Raw<float, N>& r, int i) {
+  const float4 w = r.w[i / 4];
+  return (i % 4) == 0 ? w.x : (i % 4) == 1 ? w.y : (i % 4) == 2 ? w.z : w.w;
+}
+
 // Four consecutive value entries (the lane's columns).
 template <typename TIn>
 struct Raw4;
@@ -116,39 +130,62 @@ __device__ __forceinline__ void widen4(const Raw4<float>& r, float (&x)[4]) {
   x[3] = r.w.w;
 }
 
-// Sum over the 8 row groups of a wave (lane bits 3, 4, 5).  Every lane ends
-// with the same value for its column group: each butterfly stage adds the
-// same two operands on both partner lanes, and IEEE addition is commutative.
+// Cross-lane pair exchange on gfx950.  After the swap, a holds the value of
+// the lower partner (even 16-lane row, resp. lower 32 lanes) and b the upper
+// one, on both partners.  Written as inline assembly because hipcc folds the
+// two results of __builtin_amdgcn_permlane{16,32}_swap(x, x) into one (it
+// adds the first result to itself).  "s_nop 1" gives the two wait states a
+// permlane read needs after a VALU write of its operands.
+__device__ __forceinline__ float pair_sum16(float x) {
+  float a = x, b = x;
+  asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+  return a + b;
+}
+__device__ __forceinline__ float pair_sum32(float x) {
+  float a = x, b = x;
+  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+  return a + b;
+}
+
+// Sum over the 8 row groups of a wave (lane bits 3, 4, 5), without LDS:
+//   bit 3: DPP rotate of each 16-lane row by 8 (lane i reads lane i ^ 8),
+//   bit 4: v_permlane16_swap (odd 16-lane rows exchanged with even rows),
+//   bit 5: v_permlane32_swap (upper 32 lanes exchanged with lower 32).
+// Every lane ends with the same value for its column group: each stage adds
+// the same two operands on both partner lanes (the swaps return the pair in
+// a fixed (lower, upper) order), and IEEE addition is commutative.
 __device__ __forceinline__ float rowgroup_sum(float x) {
-  x += __shfl_xor(x, 8);
-  x += __shfl_xor(x, 16);
-  x += __shfl_xor(x, 32);
-  return x;
+  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x128 /* row_ror:8 */,
+                                                             0xf, 0xf, false));
+  return pair_sum32(pair_sum16(x));
 }
 
 // One token of the gated delta rule on a lane's R x 4 register tile:
 //   S1 = Diag(alpha) S;  u = S1^T k;  e = beta (v - u);  S = S1 + k e^T
 // and, when WITH_OUT, o = scale (S1^T q + e (k . q)), which equals
-// scale * S^T q of the updated state.  Decode, verify, commit and the
-// recurrent prefill all call this one function with the same lane mapping,
-// so their states and outputs agree bit for bit.
-template <int R, bool WITH_OUT>
-__device__ __forceinline__ void token_update(float (&S)[R][4], const float (&kr)[R], const float (&ar)[R],
-                                             const float (&qr)[R], const float (&vc)[4], float beta,
+// scale * S^T q of the updated state.  k, q and alpha stay in their loaded
+// (raw) form and are widened row by row, so no fp32 copy of them is kept
+// live next to the state.  Decode, verify, commit and the recurrent prefill
+// all call this one function with the same lane mapping, so their states and
+// outputs agree bit for bit.
+template <int R, bool WITH_OUT, typename TIn>
+__device__ __forceinline__ void token_update(float (&S)[R][4], const Raw<TIn, R>& kraw, const Raw<float, R>& araw,
+                                             const Raw<TIn, R>& qraw, const float (&vc)[4], float beta,
                                              float scale, float (&o)[4]) {
   float u[4] = {0.f, 0.f, 0.f, 0.f};
   float w[4] = {0.f, 0.f, 0.f, 0.f};
   float kq = 0.f;
 #pragma unroll
   for (int r = 0; r < R; ++r) {
+    const float kr = elem(kraw, r), ar = elem(araw, r);
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-      const float s1 = ar[r] * S[r][c];
+      const float s1 = ar * S[r][c];
       S[r][c] = s1;
-      u[c] = __builtin_fmaf(kr[r], s1, u[c]);
-      if (WITH_OUT) w[c] = __builtin_fmaf(qr[r], s1, w[c]);
+      u[c] = __builtin_fmaf(kr, s1, u[c]);
+      if (WITH_OUT) w[c] = __builtin_fmaf(elem(qraw, r), s1, w[c]);
     }
-    if (WITH_OUT) kq = __builtin_fmaf(kr[r], qr[r], kq);
+    if (WITH_OUT) kq = __builtin_fmaf(kr, elem(qraw, r), kq);
   }
 #pragma unroll
   for (int c = 0; c < 4; ++c) u[c] = rowgroup_sum(u[c]);
@@ -165,9 +202,11 @@ __device__ __forceinline__ void token_update(float (&S)[R][4], const float (&kr)
     for (int c = 0; c < 4; ++c) o[c] = scale * __builtin_fmaf(e[c], kq, w[c]);
   }
 #pragma unroll
-  for (int r = 0; r < R; ++r)
+  for (int r = 0; r < R; ++r) {
+    const float kr = elem(kraw, r);
 #pragma unroll
-    for (int c = 0; c < 4; ++c) S[r][c] = __builtin_fmaf(kr[r], e[c], S[r][c]);
+    for (int c = 0; c < 4; ++c) S[r][c] = __builtin_fmaf(kr, e[c], S[r][c]);
+  }
 }
 
 template <int R, int DV>

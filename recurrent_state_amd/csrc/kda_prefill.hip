@@ -1,16 +1,689 @@
-// Chunked (WY / UT-transform) prefill for gfx950.  Placeholder until the MFMA
-// kernel lands: reports "not supported" so that no caller mistakes another
-// kernel for it.
+// Chunked (WY / UT-transform) prompt processing for gfx950 on MFMA.
+//
+// The pages leave the prefill math to the method; this kernel computes the
+// same result as running the gated delta rule token by token (up to
+// rounding), chunk by chunk.  For a chunk of n <= CH tokens starting from
+// state S (rows = key channels, columns = value channels):
+//
+//   g_r  = sum_{s <= r} log alpha_s                 per key channel (log2 domain here)
+//   Kt   = k * 2^g,  Qt = q * 2^g,  Kh = k * 2^-g,  Kb = k * 2^(g_n - g)
+//   A    = strictly-lower(Diag(beta) Kt Kh^T)       (CH x CH)
+//   P    = lower-with-diagonal(Qt Kh^T)             (CH x CH)
+//   T    = (I + A)^-1 Diag(beta)
+//   E    = T (V - Kt S)                             (CH x dv)
+//   O    = scale (Qt S + P E)
+//   S'   = Diag(2^g_n) S + Kb^T E
+//
+// One workgroup owns one (sequence, head) for the whole prompt and walks
+// its chunks in order; wave w of the workgroup owns value columns
+// [32 w, 32 w + 32) of the state, which stays in registers in the MFMA
+// accumulator layout across chunks.  The key-side products (Kt, Qt, Kh, Kb,
+// A, P, T) are shared by the waves through LDS.
+//
+// Precision: every contraction runs on v_mfma_f32_16x16x32_bf16 with fp32
+// operands split as x = hi + lo (two bf16), and x*y ~ hi*hi + hi*lo + lo*hi
+// accumulated in fp32 (the three-product bf16 scheme of Henry, Tang and
+// Heinecke, "Leveraging the bfloat16 Artificial Intelligence Datatype For
+// Higher-Precision Computations", ARITH 2019): about 2^-16 relative error
+// per product instead of bf16's 2^-9.  The triangular inverse is fp32 VALU.
+//
+// Operand layouts (16x16x32 bf16, verified on gfx950): lane l holds
+//   A[m = l & 15][k = 8 (l >> 4) + e],  B[k = 8 (l >> 4) + e][n = l & 15],
+//   D[m = 4 (l >> 4) + r][n = l & 15],  e < 8, r < 4.
+// The contraction index k may be permuted consistently in A and B; this
+// kernel uses k-slot e of lane group g = l >> 4 for index
+//   pi(g, e) = 4 g + e (e < 4),  16 + 4 g + (e - 4) (e >= 4)
+// inside each 32-wide k block, which turns two stacked D tiles (rows 0..15
+// and 16..31 of the block) directly into a B operand, and makes the A
+// operand two 8-byte LDS reads per plane.
 
 #include <hip/hip_runtime.h>
 
+#include "kda_common.h"
 #include "kda_internal.h"
 
 namespace kda {
+namespace {
 
-hipError_t launch_prefill_chunked(const kda_shape&, int32_t, int32_t, float*, int64_t*, TokenInputs, float*, int32_t,
-                                  const int32_t*, float*, int64_t*, int32_t, int32_t*, hipStream_t) {
-  return hipErrorNotSupported;
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
+typedef __attribute__((ext_vector_type(4))) float f32x4_t;
+typedef __attribute__((ext_vector_type(4))) unsigned u32x4_t;
+
+struct Op {  // one MFMA operand as hi and lo bf16 parts
+  bf16x8_t hi, lo;
+};
+
+__device__ __forceinline__ f32x4_t mfma(bf16x8_t a, bf16x8_t b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// c += a * b with both operands split: hi*hi + hi*lo + lo*hi.
+__device__ __forceinline__ f32x4_t mfma3(const Op& a, const Op& b, f32x4_t c) {
+  c = mfma(a.lo, b.hi, c);
+  c = mfma(a.hi, b.lo, c);
+  return mfma(a.hi, b.hi, c);
+}
+
+__device__ __forceinline__ uint32_t bf16_bits(__bf16 h) { return (uint32_t)__builtin_bit_cast(uint16_t, h); }
+
+// fp32 pair -> packed hi and lo bf16 pairs (round to nearest even both times).
+__device__ __forceinline__ void split2(float a, float b, uint32_t& hi, uint32_t& lo) {
+  const __bf16 ha = (__bf16)a, hb = (__bf16)b;
+  const __bf16 la = (__bf16)(a - (float)ha), lb = (__bf16)(b - (float)hb);
+  hi = bf16_bits(ha) | (bf16_bits(hb) << 16);
+  lo = bf16_bits(la) | (bf16_bits(lb) << 16);
+}
+
+__device__ __forceinline__ __bf16 split_hi(float x, __bf16& lo) {
+  const __bf16 h = (__bf16)x;
+  lo = (__bf16)(x - (float)h);
+  return h;
+}
+
+// B operand from two stacked D tiles (rows 0..15 and 16..31 of a k block).
+__device__ __forceinline__ Op op_from_tiles(const f32x4_t& t0, const f32x4_t& t1) {
+  Op o;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    __bf16 l0, l1;
+    o.hi[e] = split_hi(t0[e], l0);
+    o.hi[4 + e] = split_hi(t1[e], l1);
+    o.lo[e] = l0;
+    o.lo[4 + e] = l1;
+  }
+  return o;
+}
+
+// A (or B) operand read from a row-major bf16 plane: row `row`, k block
+// starting at column c0 = 32 kb + 4 g: columns c0..c0+3 and c0+16..c0+19.
+__device__ __forceinline__ bf16x8_t plane_op(const bf16_t* plane, int row, int rs, int c0) {
+  const uint2 a = *reinterpret_cast<const uint2*>(plane + row * rs + c0);
+  const uint2 b = *reinterpret_cast<const uint2*>(plane + row * rs + c0 + 16);
+  const u32x4_t v = {a.x, a.y, b.x, b.y};
+  return __builtin_bit_cast(bf16x8_t, v);
+}
+
+__device__ __forceinline__ Op plane_op2(const bf16_t* hi, const bf16_t* lo, int row, int rs, int c0) {
+  return Op{plane_op(hi, row, rs, c0), plane_op(lo, row, rs, c0)};
+}
+
+// Buffer resources: the base address and byte range of a window live in
+// SGPRs, each lane supplies one VGPR offset, and per-access constants go in
+// the SGPR offset operand, so a 64-element register tile spread over many
+// rows costs one address VGPR.  The hardware range check covers only the
+// VGPR (+ instruction) offset, not the SGPR offset, so every access below is
+// kept inside its window by explicit guards; the window size is a backstop.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr int kRsrcWord3 = 0x00020000;  // raw 32-bit data format
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kRsrcWord3);
+}
+__device__ __forceinline__ float ld_f32(rsrc_t r, int voff, int soff) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0));
+}
+__device__ __forceinline__ void st_f32(rsrc_t r, float v, int voff, int soff) {
+  __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, v), r, voff, soff, 0);
+}
+// One input element (bf16 widened, or f32).
+__device__ __forceinline__ float ld_in(rsrc_t r, int voff, int soff, const bf16_t*) {
+  return bf16_lo((uint32_t)__builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, 0));
+}
+__device__ __forceinline__ float ld_in(rsrc_t r, int voff, int soff, const float*) { return ld_f32(r, voff, soff); }
+// Two consecutive input elements.
+__device__ __forceinline__ void ld_in2(rsrc_t r, int voff, int soff, float& a, float& b, const bf16_t*) {
+  const uint32_t w = __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0);
+  a = bf16_lo(w);
+  b = bf16_hi(w);
+}
+// (Two 32-bit loads: hipcc lowers __builtin_amdgcn_raw_buffer_load_b64 to a
+// single-dword load, leaving the upper half undefined.)
+__device__ __forceinline__ void ld_in2(rsrc_t r, int voff, int soff, float& a, float& b, const float*) {
+  a = ld_f32(r, voff, soff);
+  b = ld_f32(r, voff + 4, soff);
+}
+
+template <typename TIn>
+struct PrefillArgs {
+  float* state;
+  int64_t* pos;
+  const TIn* q;
+  const TIn* k;
+  const TIn* v;
+  const float* alpha;
+  const float* beta;
+  float* o;
+  const int32_t* ckpt_slots;
+  float* slot_states;
+  int64_t* slot_pos;
+  int32_t* dev_err;
+  int32_t H;
+  int32_t L;
+  int32_t ckpt_every;
+  int32_t n_slots;
+  float scale;
+};
+
+// LDS layout of one workgroup (bytes).  Regions are reused across phases:
+// R2 holds Kh during the A/P products and then A (fp32) and P (hi/lo); R3
+// holds the off-diagonal inverse blocks and per-wave scratch during the
+// triangular solve and then T (hi/lo).
+template <int DK, int CH, int NW>
+struct Smem {
+  static constexpr int RS_K = DK + 4;  // row stride (elements) of channel-indexed planes
+  static constexpr int RS_C = CH + 4;  // row stride of token-indexed planes
+  static constexpr int NB = CH / 16;   // 16-token blocks per chunk
+  static constexpr int NG = (64 * NW) / (DK / 2);  // token groups in the preparation phase
+  static constexpr int KQ_PLANE = 2 * CH * RS_K;   // elements per KQ plane
+  static constexpr int KH_PLANE = CH * RS_K;
+  static constexpr int KB_PLANE = DK * RS_C;
+  static constexpr int CC_PLANE = CH * RS_C;
+  static constexpr int off_kq = 0;
+  static constexpr int off_kb = off_kq + 2 * KQ_PLANE * 2;
+  static constexpr int off_r2 = off_kb + 2 * KB_PLANE * 2;
+  static constexpr int r2_a = 2 * KH_PLANE * 2;
+  static constexpr int r2_b = CH * CH * 4 + 2 * CC_PLANE * 2;
+  static constexpr int off_r3 = off_r2 + (r2_a > r2_b ? r2_a : r2_b);
+  static constexpr int r3_a = 2 * CC_PLANE * 2;
+  static constexpr int r3_b = (NB * (NB - 1) / 2 + NW) * 16 * 16 * 4;
+  static constexpr int off_misc = off_r3 + (r3_a > r3_b ? r3_a : r3_b);
+  static constexpr int off_beta = off_misc;
+  static constexpr int off_gn = off_beta + CH * 4;
+  static constexpr int off_tot = off_gn + DK * 4;
+  static constexpr int total = off_tot + NG * DK * 4;
+  static_assert(total <= 163840, "LDS budget exceeded");
+  static_assert(r2_a % 16 == 0 && off_r3 % 16 == 0 && off_misc % 16 == 0, "alignment");
+};
+
+// Index of off-diagonal block (i, j), i > j, inside the inverse scratch.
+__device__ __forceinline__ int off_block(int i, int j) { return i * (i - 1) / 2 + j; }
+
+template <int DK, int DV, int CH, typename TIn>
+__global__ void __launch_bounds__(DV * 2) prefill_chunked_kernel(PrefillArgs<TIn> a) {
+  constexpr int NW = DV / 32;        // waves; wave w owns value columns [32 w, 32 w + 32)
+  constexpr int NT = 64 * NW;        // threads
+  constexpr int NB = CH / 16;        // 16-token blocks
+  constexpr int KB = DK / 32;        // 32-channel k blocks
+  constexpr int MT = DK / 16;        // channel tiles of the state
+  constexpr int CP = DK / 2;         // channel pairs
+  typedef Smem<DK, CH, NW> L;
+  constexpr int NG = L::NG;
+  constexpr int TPG = CH / NG;       // tokens per preparation group
+  static_assert(NT % CP == 0 && CH % NG == 0 && TPG % 4 == 0, "preparation mapping");
+  static_assert(CH == 32 || CH == 64, "chunk");
+
+  __shared__ __align__(16) char smem[L::total];
+  bf16_t* kq_hi = reinterpret_cast<bf16_t*>(smem + L::off_kq);
+  bf16_t* kq_lo = kq_hi + L::KQ_PLANE;
+  bf16_t* kb_hi = reinterpret_cast<bf16_t*>(smem + L::off_kb);
+  bf16_t* kb_lo = kb_hi + L::KB_PLANE;
+  bf16_t* kh_hi = reinterpret_cast<bf16_t*>(smem + L::off_r2);
+  bf16_t* kh_lo = kh_hi + L::KH_PLANE;
+  float* abuf = reinterpret_cast<float*>(smem + L::off_r2);
+  bf16_t* p_hi = reinterpret_cast<bf16_t*>(smem + L::off_r2 + CH * CH * 4);
+  bf16_t* p_lo = p_hi + L::CC_PLANE;
+  bf16_t* t_hi = reinterpret_cast<bf16_t*>(smem + L::off_r3);
+  bf16_t* t_lo = t_hi + L::CC_PLANE;
+  float* xoff = reinterpret_cast<float*>(smem + L::off_r3);
+  float* sbeta = reinterpret_cast<float*>(smem + L::off_beta);
+  float* sgn = reinterpret_cast<float*>(smem + L::off_gn);
+  float* stot = reinterpret_cast<float*>(smem + L::off_tot);
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int l16 = lane & 15, g = lane >> 4;
+  const int bh = blockIdx.x;
+  const int b = bh / a.H, h = bh - b * a.H;
+  const bool owner = h == 0 && tid == 0;  // the one writer of positions
+  const int64_t pos0 = owner ? a.pos[b] : 0;
+  const int n_ckpt = a.ckpt_every > 0 ? a.L / a.ckpt_every : 0;
+  const size_t tok0 = (size_t)b * a.L;             // first token row of this sequence
+
+  // State slice of this wave in the accumulator layout:
+  // st[mt][nt][r] = S[16 mt + 4 g + r][32 wave + 16 nt + l16].
+  f32x4_t st[MT][2];
+  // Tile element (mt, nt, r) of a [DK][DV] fp32 state lies at byte
+  // tile_voff + tile_soff(mt, nt, r).
+  const int tile_voff = ((4 * g) * DV + 32 * wave + l16) * 4;
+#define KDA_TILE_SOFF(mt, nt, r) (((16 * (mt) + (r)) * DV + 16 * (nt)) * 4)
+  const rsrc_t rs_state = make_rsrc(a.state + (size_t)bh * DK * DV, DK * DV * 4);
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) st[mt][nt][r] = ld_f32(rs_state, tile_voff, KDA_TILE_SOFF(mt, nt, r));
+
+  const int n_chunks = (a.L + CH - 1) / CH;
+  for (int c = 0; c < n_chunks; ++c) {
+    const int t_base = c * CH;
+    const int n = min(CH, a.L - t_base);  // valid tokens in this chunk
+    // Windows over this chunk's valid token rows of this head.  Rows at and
+    // past n are padding: they are never loaded (their values are zero) and
+    // never stored.
+    const size_t row0 = (tok0 + t_base) * a.H + h;  // [B][L][H] row index of the chunk's first token
+    const int rowk = a.H * DK, rowv = a.H * DV;       // elements between consecutive tokens
+    const rsrc_t rs_k = make_rsrc(a.k + row0 * DK, ((n - 1) * rowk + DK) * sizeof(TIn));
+    const rsrc_t rs_q = make_rsrc(a.q + row0 * DK, ((n - 1) * rowk + DK) * sizeof(TIn));
+    const rsrc_t rs_a = make_rsrc(a.alpha + row0 * DK, ((n - 1) * rowk + DK) * 4);
+    const rsrc_t rs_b = make_rsrc(a.beta + row0, ((n - 1) * a.H + 1) * 4);
+    const rsrc_t rs_v = make_rsrc(a.v + row0 * DV, ((n - 1) * rowv + DV) * sizeof(TIn));
+    const rsrc_t rs_o = make_rsrc(a.o + row0 * DV, ((n - 1) * rowv + DV) * 4);
+
+    // ---- Phase 1: decay cumsum and the decayed key/query planes ---------
+    // Pass A: per-channel prefix sums of log2(alpha) within each token group,
+    // then the group totals are combined through LDS.  Pass B reads k and q
+    // (an L2 hit) and writes the decayed planes.
+    {
+      const int cp = tid % CP, tg = tid / CP;
+      const int c0 = 2 * cp;
+      float g0[TPG], g1[TPG];
+      float s0 = 0.f, s1 = 0.f;
+#pragma unroll
+      for (int i = 0; i < TPG; ++i) {
+        const int tr = tg * TPG + i;
+        float al0 = 1.f, al1 = 1.f;  // padding tokens do not decay
+        if (tr < n) ld_in2(rs_a, (tg * TPG * rowk + c0) * 4, i * rowk * 4, al0, al1, (const float*)nullptr);
+        s0 += __log2f(al0);
+        s1 += __log2f(al1);
+        g0[i] = s0;
+        g1[i] = s1;
+      }
+      stot[tg * DK + c0] = s0;
+      stot[tg * DK + c0 + 1] = s1;
+      if (cp == 0) {
+#pragma unroll
+        for (int i = 0; i < TPG; ++i) {
+          const int tr = tg * TPG + i;
+          float bv = 0.f;
+          if (tr < n) bv = ld_f32(rs_b, tg * TPG * a.H * 4, i * a.H * 4);
+          sbeta[tr] = bv;
+        }
+      }
+      __syncthreads();
+      float off0 = 0.f, off1 = 0.f, gn0 = 0.f, gn1 = 0.f;
+#pragma unroll
+      for (int j = 0; j < NG; ++j) {
+        const float t0 = stot[j * DK + c0], t1 = stot[j * DK + c0 + 1];
+        if (j < tg) {
+          off0 += t0;
+          off1 += t1;
+        }
+        gn0 += t0;
+        gn1 += t1;
+      }
+      if (tg == 0) {
+        sgn[c0] = exp2f(gn0);
+        sgn[c0 + 1] = exp2f(gn1);
+      }
+      uint32_t kbh0[2], kbl0[2], kbh1[2], kbl1[2];
+#pragma unroll
+      for (int i = 0; i < TPG; ++i) {
+        const int tr = tg * TPG + i;
+        float k0 = 0.f, k1 = 0.f, q0 = 0.f, q1 = 0.f;
+        if (tr < n) {
+          const int vo = (tg * TPG * rowk + c0) * (int)sizeof(TIn), so = i * rowk * (int)sizeof(TIn);
+          ld_in2(rs_k, vo, so, k0, k1, (const TIn*)nullptr);
+          ld_in2(rs_q, vo, so, q0, q1, (const TIn*)nullptr);
+        }
+        const float x0 = off0 + g0[i], x1 = off1 + g1[i];
+        const float e0 = exp2f(x0), e1 = exp2f(x1);
+        const float ie0 = exp2f(-x0), ie1 = exp2f(-x1);
+        uint32_t hi, lo;
+        split2(k0 * e0, k1 * e1, hi, lo);  // Kt
+        *reinterpret_cast<uint32_t*>(kq_hi + tr * L::RS_K + c0) = hi;
+        *reinterpret_cast<uint32_t*>(kq_lo + tr * L::RS_K + c0) = lo;
+        split2(q0 * e0, q1 * e1, hi, lo);  // Qt
+        *reinterpret_cast<uint32_t*>(kq_hi + (CH + tr) * L::RS_K + c0) = hi;
+        *reinterpret_cast<uint32_t*>(kq_lo + (CH + tr) * L::RS_K + c0) = lo;
+        split2(k0 * ie0, k1 * ie1, hi, lo);  // Kh
+        *reinterpret_cast<uint32_t*>(kh_hi + tr * L::RS_K + c0) = hi;
+        *reinterpret_cast<uint32_t*>(kh_lo + tr * L::RS_K + c0) = lo;
+        // Kb = k 2^(g_n - g): the transposed planes are written 4 tokens at a time.
+        __bf16 l0, l1;
+        const __bf16 h0 = split_hi(k0 * exp2f(gn0 - x0), l0), h1 = split_hi(k1 * exp2f(gn1 - x1), l1);
+        const int w = (i >> 1) & 1, sh = (i & 1) * 16;
+        if ((i & 1) == 0) kbh0[w] = kbl0[w] = kbh1[w] = kbl1[w] = 0;
+        kbh0[w] |= bf16_bits(h0) << sh;
+        kbl0[w] |= bf16_bits(l0) << sh;
+        kbh1[w] |= bf16_bits(h1) << sh;
+        kbl1[w] |= bf16_bits(l1) << sh;
+        if ((i & 3) == 3) {
+          const int t4 = tr - 3;
+          *reinterpret_cast<uint2*>(kb_hi + c0 * L::RS_C + t4) = make_uint2(kbh0[0], kbh0[1]);
+          *reinterpret_cast<uint2*>(kb_lo + c0 * L::RS_C + t4) = make_uint2(kbl0[0], kbl0[1]);
+          *reinterpret_cast<uint2*>(kb_hi + (c0 + 1) * L::RS_C + t4) = make_uint2(kbh1[0], kbh1[1]);
+          *reinterpret_cast<uint2*>(kb_lo + (c0 + 1) * L::RS_C + t4) = make_uint2(kbl1[0], kbl1[1]);
+        }
+      }
+    }
+    __syncthreads();
+
+    // Value tiles this wave needs in phase 4, loaded now so the latency
+    // overlaps the key-side products: vv[mt][nt][r] = V[16 mt + 4 g + r][32 wave + 16 nt + l16].
+    // Value / output element (mt, nt, r) of this wave lies at
+    // io_voff + io_soff(mt, nt, r) elements inside the chunk window.
+    const int io_voff = (4 * g) * rowv + 32 * wave + l16;
+#define KDA_IO_SOFF(mt, nt, r) ((16 * (mt) + (r)) * rowv + 16 * (nt))
+    float vv[NB][2][4];
+#pragma unroll
+    for (int mt = 0; mt < NB; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          vv[mt][nt][r] = 0.f;
+          if (16 * mt + 4 * g + r < n)
+            vv[mt][nt][r] = ld_in(rs_v, io_voff * (int)sizeof(TIn), KDA_IO_SOFF(mt, nt, r) * (int)sizeof(TIn),
+                                  (const TIn*)nullptr);
+        }
+
+    // ---- Phase 2: A = Diag(beta) Kt Kh^T and P = Qt Kh^T (lower tiles) ---
+    // Tile list: index i < NA are A tiles (mt, nt), nt <= mt < NB; the next
+    // NA are P tiles (NB + mt, nt).  Waves take tiles round-robin.
+    constexpr int NA = NB * (NB + 1) / 2;
+    constexpr int MAXT = (2 * NA + NW - 1) / NW;
+    f32x4_t at[MAXT];
+#pragma unroll
+    for (int s = 0; s < MAXT; ++s) {
+      const int i = wave + s * NW;
+      at[s] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      if (i < 2 * NA) {
+        const int ii = i < NA ? i : i - NA;
+        int mt = 0;
+        while ((mt + 1) * (mt + 2) / 2 <= ii) ++mt;
+        const int nt = ii - mt * (mt + 1) / 2;
+        const int row = (i < NA ? 0 : CH) + 16 * mt + l16;
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+          const int c0 = 32 * kb + 4 * g;
+          at[s] = mfma3(plane_op2(kq_hi, kq_lo, row, L::RS_K, c0), plane_op2(kh_hi, kh_lo, 16 * nt + l16, L::RS_K, c0),
+                        at[s]);
+        }
+      }
+    }
+    __syncthreads();  // Kh is dead from here on; A and P take its place
+#pragma unroll
+    for (int s = 0; s < MAXT; ++s) {
+      const int i = wave + s * NW;
+      if (i < 2 * NA) {
+        const int ii = i < NA ? i : i - NA;
+        int mt = 0;
+        while ((mt + 1) * (mt + 2) / 2 <= ii) ++mt;
+        const int nt = ii - mt * (mt + 1) / 2;
+        const int col = 16 * nt + l16;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int row = 16 * mt + 4 * g + r;
+          if (i < NA) {
+            abuf[row * CH + col] = col < row ? at[s][r] * sbeta[row] : 0.f;
+          } else {
+            __bf16 lo;
+            const __bf16 hi = split_hi(col <= row ? at[s][r] : 0.f, lo);
+            p_hi[row * L::RS_C + col] = __builtin_bit_cast(bf16_t, hi);
+            p_lo[row * L::RS_C + col] = __builtin_bit_cast(bf16_t, lo);
+          }
+        }
+      }
+    }
+    // P tiles above the diagonal inside a 32-token k block are read by the
+    // P E product: make them zero.
+    for (int i = wave; i < NB / 2; i += NW) {
+      const int mt = 2 * i, nt = 2 * i + 1;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = 16 * mt + 4 * g + r, col = 16 * nt + l16;
+        p_hi[row * L::RS_C + col] = 0;
+        p_lo[row * L::RS_C + col] = 0;
+      }
+    }
+    __syncthreads();
+
+    // ---- Phase 3: T = (I + A)^-1 Diag(beta) by 16 x 16 blocks (fp32) -----
+    // 3a: diagonal blocks X_jj = (I + A_jj)^-1; lane c < 16 solves column c.
+    // The strictly lower part of X_jj replaces A_jj (its diagonal is 1).
+    for (int j = wave; j < NB; j += NW) {
+      if (lane < 16) {
+        const int cc = lane;
+        float x[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          float acc = 0.f;
+#pragma unroll
+          for (int i = 0; i < 16; ++i)
+            if (i < r) acc = __builtin_fmaf(abuf[(16 * j + r) * CH + 16 * j + i], x[i], acc);
+          x[r] = r == cc ? 1.f : (r < cc ? 0.f : -acc);
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (r > cc) abuf[(16 * j + r) * CH + 16 * j + cc] = x[r];
+      }
+    }
+    __syncthreads();
+    // 3b: off-diagonal blocks by distance d = i - j:
+    //   X_ij = -X_ii sum_{k=j}^{i-1} A_ik X_kj.
+    // Lane l computes row m = l >> 2, columns 4 (l & 3) .. + 3 of a block.
+    {
+      float* yscr = xoff + (NB * (NB - 1) / 2 + wave) * 256;
+      const int m = lane >> 2, n0 = 4 * (lane & 3);
+      for (int d = 1; d < NB; ++d) {
+        for (int j = wave; j + d < NB; j += NW) {
+          const int i = j + d;
+          float y[4] = {0.f, 0.f, 0.f, 0.f};
+          for (int kk = j; kk < i; ++kk) {
+#pragma unroll
+            for (int q = 0; q < 16; ++q) {
+              const float aik = abuf[(16 * i + m) * CH + 16 * kk + q];
+              float xq[4];
+              if (kk == j) {
+#pragma unroll
+                for (int u = 0; u < 4; ++u)
+                  xq[u] = abuf[(16 * j + q) * CH + 16 * j + n0 + u] + (q == n0 + u ? 1.f : 0.f);
+              } else {
+#pragma unroll
+                for (int u = 0; u < 4; ++u) xq[u] = xoff[off_block(kk, j) * 256 + q * 16 + n0 + u];
+              }
+#pragma unroll
+              for (int u = 0; u < 4; ++u) y[u] = __builtin_fmaf(aik, xq[u], y[u]);
+            }
+          }
+#pragma unroll
+          for (int u = 0; u < 4; ++u) yscr[m * 16 + n0 + u] = y[u];
+          float z[4] = {y[0], y[1], y[2], y[3]};
+#pragma unroll
+          for (int q = 0; q < 16; ++q) {
+            const float xiq = abuf[(16 * i + m) * CH + 16 * i + q];  // strictly lower part of X_ii
+#pragma unroll
+            for (int u = 0; u < 4; ++u) z[u] = __builtin_fmaf(xiq, yscr[q * 16 + n0 + u], z[u]);
+          }
+#pragma unroll
+          for (int u = 0; u < 4; ++u) xoff[off_block(i, j) * 256 + m * 16 + n0 + u] = -z[u];
+        }
+        __syncthreads();
+      }
+    }
+    // 3c: T = X Diag(beta), split into hi/lo planes (T overwrites the scratch).
+    {
+      constexpr int PER = CH * CH / NT;  // elements per thread, one row segment
+      const int row = tid / (CH / PER), col0 = (tid % (CH / PER)) * PER;
+      float tv[PER];
+#pragma unroll
+      for (int u = 0; u < PER; ++u) {
+        const int col = col0 + u, bi = row >> 4, bj = col >> 4;
+        float xv;
+        if (bi == bj)
+          xv = abuf[row * CH + col] + (row == col ? 1.f : 0.f);
+        else if (bi > bj)
+          xv = xoff[off_block(bi, bj) * 256 + (row & 15) * 16 + (col & 15)];
+        else
+          xv = 0.f;
+        tv[u] = xv * sbeta[col];
+      }
+      __syncthreads();
+#pragma unroll
+      for (int u = 0; u < PER; u += 2) {
+        uint32_t hi, lo;
+        split2(tv[u], tv[u + 1], hi, lo);
+        *reinterpret_cast<uint32_t*>(t_hi + row * L::RS_C + col0 + u) = hi;
+        *reinterpret_cast<uint32_t*>(t_lo + row * L::RS_C + col0 + u) = lo;
+      }
+    }
+    __syncthreads();
+
+    // ---- Phase 4: value side for this wave's 32 columns ------------------
+    // 4b: X = [Kt; Qt] S, rows 0..CH-1 = Kt S, rows CH..2CH-1 = Qt S.
+    f32x4_t xs[2 * NB][2];
+#pragma unroll
+    for (int mt = 0; mt < 2 * NB; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) xs[mt][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+      const Op s0 = op_from_tiles(st[2 * kb][0], st[2 * kb + 1][0]);
+      const Op s1 = op_from_tiles(st[2 * kb][1], st[2 * kb + 1][1]);
+      const int c0 = 32 * kb + 4 * g;
+#pragma unroll
+      for (int mt = 0; mt < 2 * NB; ++mt) {
+        const Op ak = plane_op2(kq_hi, kq_lo, 16 * mt + l16, L::RS_K, c0);
+        xs[mt][0] = mfma3(ak, s0, xs[mt][0]);
+        xs[mt][1] = mfma3(ak, s1, xs[mt][1]);
+      }
+    }
+    // 4c: R = V - Kt S (padding tokens give 0 - 0).
+#pragma unroll
+    for (int mt = 0; mt < NB; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) xs[mt][nt][r] = vv[mt][nt][r] - xs[mt][nt][r];
+    // 4d: E = T R (T lower triangular: token tile mt needs k blocks <= mt / 2).
+    Op rop[NB / 2][2];
+#pragma unroll
+    for (int kb = 0; kb < NB / 2; ++kb)
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) rop[kb][nt] = op_from_tiles(xs[2 * kb][nt], xs[2 * kb + 1][nt]);
+    f32x4_t et[NB][2];
+#pragma unroll
+    for (int mt = 0; mt < NB; ++mt) {
+      et[mt][0] = et[mt][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kb = 0; kb <= mt / 2; ++kb) {
+        const Op at_ = plane_op2(t_hi, t_lo, 16 * mt + l16, L::RS_C, 32 * kb + 4 * g);
+        et[mt][0] = mfma3(at_, rop[kb][0], et[mt][0]);
+        et[mt][1] = mfma3(at_, rop[kb][1], et[mt][1]);
+      }
+    }
+    Op eop[NB / 2][2];
+#pragma unroll
+    for (int kb = 0; kb < NB / 2; ++kb)
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) eop[kb][nt] = op_from_tiles(et[2 * kb][nt], et[2 * kb + 1][nt]);
+    // 4e: O = scale (Qt S + P E), stored for the valid tokens.
+#pragma unroll
+    for (int mt = 0; mt < NB; ++mt) {
+#pragma unroll
+      for (int kb = 0; kb <= mt / 2; ++kb) {
+        const Op ap = plane_op2(p_hi, p_lo, 16 * mt + l16, L::RS_C, 32 * kb + 4 * g);
+        xs[NB + mt][0] = mfma3(ap, eop[kb][0], xs[NB + mt][0]);
+        xs[NB + mt][1] = mfma3(ap, eop[kb][1], xs[NB + mt][1]);
+      }
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (16 * mt + 4 * g + r < n) st_f32(rs_o, a.scale * xs[NB + mt][nt][r], io_voff * 4, KDA_IO_SOFF(mt, nt, r) * 4);
+    }
+    // 4f: S = Diag(2^g_n) S + Kb^T E.
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float gm = sgn[16 * mt + 4 * g + r];
+        st[mt][0][r] *= gm;
+        st[mt][1][r] *= gm;
+      }
+#pragma unroll
+      for (int kb = 0; kb < NB / 2; ++kb) {
+        const Op ak = plane_op2(kb_hi, kb_lo, 16 * mt + l16, L::RS_C, 32 * kb + 4 * g);
+        st[mt][0] = mfma3(ak, eop[kb][0], st[mt][0]);
+        st[mt][1] = mfma3(ak, eop[kb][1], st[mt][1]);
+      }
+    }
+    // Checkpoint at the end of this chunk when one is due.
+    const int t_end = t_base + n;
+    if (n_ckpt > 0 && n == CH && t_end % a.ckpt_every == 0) {
+      const int m = t_end / a.ckpt_every - 1;
+      const int slot = a.ckpt_slots[(size_t)b * n_ckpt + m];
+      if (slot >= 0 && slot < a.n_slots) {
+        const rsrc_t rs_slot = make_rsrc(a.slot_states + ((size_t)slot * a.H + h) * DK * DV, DK * DV * 4);
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+          for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) st_f32(rs_slot, st[mt][nt][r], tile_voff, KDA_TILE_SOFF(mt, nt, r));
+        if (owner) a.slot_pos[slot] = pos0 + t_end;
+      } else if (tid == 0) {
+        atomicOr(a.dev_err, KDA_DEV_ERR_CKPT_SLOT);
+      }
+    }
+    __syncthreads();  // the next chunk rewrites every LDS region
+  }
+
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) st_f32(rs_state, st[mt][nt][r], tile_voff, KDA_TILE_SOFF(mt, nt, r));
+#undef KDA_TILE_SOFF
+#undef KDA_IO_SOFF
+  if (owner) a.pos[b] = pos0 + a.L;
+}
+
+template <int DK, int DV, typename TIn>
+hipError_t launch_cfg(const kda_shape& s, int32_t L, int32_t chunk, float* state, int64_t* pos, TokenInputs in,
+                      float* o, int32_t ckpt_every, const int32_t* ckpt_slots, float* slot_states, int64_t* slot_pos,
+                      int32_t n_slots, int32_t* dev_err, hipStream_t st) {
+  PrefillArgs<TIn> a{state, pos, (const TIn*)in.q, (const TIn*)in.k, (const TIn*)in.v, in.alpha, in.beta, o,
+                     ckpt_slots, slot_states, slot_pos, dev_err, s.H, L, ckpt_every, n_slots, s.scale};
+  const dim3 grid((unsigned)((size_t)s.B * s.H));
+  if (chunk == 64)
+    prefill_chunked_kernel<DK, DV, 64, TIn><<<grid, 2 * DV, 0, st>>>(a);
+  else
+    prefill_chunked_kernel<DK, DV, 32, TIn><<<grid, 2 * DV, 0, st>>>(a);
+  return hipGetLastError();
+}
+
+template <typename TIn>
+hipError_t launch_dtype(const kda_shape& s, int32_t L, int32_t chunk, float* state, int64_t* pos, TokenInputs in,
+                        float* o, int32_t ckpt_every, const int32_t* ckpt_slots, float* slot_states, int64_t* slot_pos,
+                        int32_t n_slots, int32_t* dev_err, hipStream_t st) {
+  if (s.dk == 128 && s.dv == 128)
+    return launch_cfg<128, 128, TIn>(s, L, chunk, state, pos, in, o, ckpt_every, ckpt_slots, slot_states, slot_pos,
+                                     n_slots, dev_err, st);
+  if (s.dk == 128 && s.dv == 64)
+    return launch_cfg<128, 64, TIn>(s, L, chunk, state, pos, in, o, ckpt_every, ckpt_slots, slot_states, slot_pos,
+                                    n_slots, dev_err, st);
+  if (s.dk == 64 && s.dv == 128)
+    return launch_cfg<64, 128, TIn>(s, L, chunk, state, pos, in, o, ckpt_every, ckpt_slots, slot_states, slot_pos,
+                                    n_slots, dev_err, st);
+  return launch_cfg<64, 64, TIn>(s, L, chunk, state, pos, in, o, ckpt_every, ckpt_slots, slot_states, slot_pos,
+                                 n_slots, dev_err, st);
+}
+
+}  // namespace
+
+hipError_t launch_prefill_chunked(const kda_shape& s, int32_t L, int32_t chunk, float* state, int64_t* pos,
+                                  TokenInputs in, float* o, int32_t ckpt_every, const int32_t* ckpt_slots,
+                                  float* slot_states, int64_t* slot_pos, int32_t n_slots, int32_t* dev_err,
+                                  hipStream_t st) {
+  if (chunk != 32 && chunk != 64) return hipErrorInvalidValue;
+  if (s.in_dtype == KDA_BF16)
+    return launch_dtype<bf16_t>(s, L, chunk, state, pos, in, o, ckpt_every, ckpt_slots, slot_states, slot_pos,
+                                n_slots, dev_err, st);
+  return launch_dtype<float>(s, L, chunk, state, pos, in, o, ckpt_every, ckpt_slots, slot_states, slot_pos, n_slots,
+                             dev_err, st);
 }
 
 }  // namespace kda

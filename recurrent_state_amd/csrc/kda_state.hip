@@ -95,6 +95,24 @@ struct PrefillArgs {
 #ifndef KDA_STATE_WAVES
 #define KDA_STATE_WAVES 1
 #endif
+// Token-loop kernels load token t+1's inputs while token t computes (1), or
+// load each token's inputs when it starts (0: fewer live registers).
+#ifndef KDA_PREFETCH_NEXT
+#define KDA_PREFETCH_NEXT 0
+#endif
+
+// Minimum waves per SIMD the register allocator must allow (0: no request).
+#ifndef KDA_MIN_WAVES
+#define KDA_MIN_WAVES 0
+#endif
+#if KDA_MIN_WAVES > 0
+#define KDA_OCCUPANCY __attribute__((amdgpu_waves_per_eu(KDA_MIN_WAVES)))
+#else
+#define KDA_OCCUPANCY
+#endif
+
+constexpr int kXcds = 8;  // accelerator complex dies on MI355X, each with its own L2
+
 template <int DV>
 constexpr int waves_per_group() {
   return KDA_STATE_WAVES < DV / kSliceCols ? KDA_STATE_WAVES : DV / kSliceCols;
@@ -109,8 +127,19 @@ struct Place {
   int bh, b, h, slice, rg, cg, row0, col0, lane;
   __device__ __forceinline__ Place(int H) {
     lane = threadIdx.x & (kWave - 1);
-    slice = (blockIdx.x % (SLICES / WPG)) * WPG + (threadIdx.x >> 6);
-    bh = blockIdx.x / (SLICES / WPG);
+    constexpr int G = SLICES / WPG;  // workgroups per (sequence, head)
+    const int x = blockIdx.x;
+    if (G > 1 && (gridDim.x % (kXcds * G)) == 0) {
+      // Workgroups are handed to the 8 XCDs round-robin by id.  Give the G
+      // workgroups of one (sequence, head) ids that are equal mod 8 so they
+      // run on one XCD and share its L2 for the per-token inputs.
+      const int xcd = x % kXcds, j = x / kXcds;
+      slice = (j % G) * WPG + (threadIdx.x >> 6);
+      bh = (j / G) * kXcds + xcd;
+    } else {
+      slice = (x % G) * WPG + (threadIdx.x >> 6);
+      bh = x / G;
+    }
     b = bh / H;
     h = bh - b * H;
     rg = lane >> 3;
@@ -137,16 +166,15 @@ struct TokenIn {
     load4(vp, v);
     beta = *bp;
   }
-  __device__ __forceinline__ void widen_all(float (&kr)[R], float (&qr)[R], float (&ar)[R], float (&vc)[4]) const {
-    widen(k, kr);
-    if (WITH_Q) widen(q, qr);
-    widen(a, ar);
+  __device__ __forceinline__ void update(float (&S)[R][4], float scale, float (&o)[4]) const {
+    float vc[4];
     widen4(v, vc);
+    token_update<R, WITH_Q>(S, k, a, q, vc, beta, scale, o);
   }
 };
 
 template <int DK, int DV, typename TIn>
-__global__ void __launch_bounds__(kWave * waves_per_group<DV>()) decode_kernel(StepArgs<TIn> a) {
+__global__ void KDA_OCCUPANCY __launch_bounds__(kWave * waves_per_group<DV>()) decode_kernel(StepArgs<TIn> a) {
   typedef Place<DK, DV> P;
   constexpr int R = P::R;
   const P p(a.H);
@@ -156,16 +184,15 @@ __global__ void __launch_bounds__(kWave * waves_per_group<DV>()) decode_kernel(S
   TokenIn<TIn, R, true> in;
   in.load(a.k + (size_t)p.bh * DK + p.row0, a.q + (size_t)p.bh * DK + p.row0,
           a.alpha + (size_t)p.bh * DK + p.row0, a.v + (size_t)p.bh * DV + p.col0, a.beta + p.bh);
-  float kr[R], qr[R], ar[R], vc[4], o[4];
-  in.widen_all(kr, qr, ar, vc);
-  token_update<R, true>(S, kr, ar, qr, vc, in.beta, a.scale, o);
+  float o[4];
+  in.update(S, a.scale, o);
   store_tile<R, DV>(sp, S);
   if (p.rg == 0) *reinterpret_cast<float4*>(a.o + (size_t)p.bh * DV + p.col0) = make_float4(o[0], o[1], o[2], o[3]);
   if (p.h == 0 && p.slice == 0 && p.lane == 0) a.pos[p.b] += 1;
 }
 
 template <int DK, int DV, typename TIn>
-__global__ void __launch_bounds__(kWave * waves_per_group<DV>()) verify_kernel(VerifyArgs<TIn> a) {
+__global__ void KDA_OCCUPANCY __launch_bounds__(kWave * waves_per_group<DV>()) verify_kernel(VerifyArgs<TIn> a) {
   typedef Place<DK, DV> P;
   constexpr int R = P::R;
   const P p(a.H);
@@ -177,12 +204,11 @@ __global__ void __launch_bounds__(kWave * waves_per_group<DV>()) verify_kernel(V
            a.v + tok * DV + p.col0, a.beta + tok);
   for (int t = 0; t < a.T; ++t) {
     const size_t tn = tok + a.H;
-    if (t + 1 < a.T)
+    if (KDA_PREFETCH_NEXT && t + 1 < a.T)
       nxt.load(a.k + tn * DK + p.row0, a.q + tn * DK + p.row0, a.alpha + tn * DK + p.row0,
                a.v + tn * DV + p.col0, a.beta + tn);
-    float kr[R], qr[R], ar[R], vc[4], o[4];
-    cur.widen_all(kr, qr, ar, vc);
-    token_update<R, true>(S, kr, ar, qr, vc, cur.beta, a.scale, o);
+    float o[4];
+    cur.update(S, a.scale, o);
     if (p.rg == 0) {
       *reinterpret_cast<float4*>(a.o + tok * DV + p.col0) = make_float4(o[0], o[1], o[2], o[3]);
       store4(a.log_v + tok * DV + p.col0, cur.v);
@@ -192,13 +218,17 @@ __global__ void __launch_bounds__(kWave * waves_per_group<DV>()) verify_kernel(V
       store_raw(a.log_alpha + tok * DK + p.row0, cur.a);
       if (p.rg == 0) a.log_beta[tok] = cur.beta;
     }
-    cur = nxt;
+    if (KDA_PREFETCH_NEXT)
+      cur = nxt;
+    else if (t + 1 < a.T)
+      cur.load(a.k + tn * DK + p.row0, a.q + tn * DK + p.row0, a.alpha + tn * DK + p.row0,
+               a.v + tn * DV + p.col0, a.beta + tn);
     tok = tn;
   }
 }
 
 template <int DK, int DV, typename TIn>
-__global__ void __launch_bounds__(kWave * waves_per_group<DV>()) commit_kernel(CommitArgs<TIn> a) {
+__global__ void KDA_OCCUPANCY __launch_bounds__(kWave * waves_per_group<DV>()) commit_kernel(CommitArgs<TIn> a) {
   typedef Place<DK, DV> P;
   constexpr int R = P::R;
   const P p(a.H);
@@ -217,13 +247,16 @@ __global__ void __launch_bounds__(kWave * waves_per_group<DV>()) commit_kernel(C
            a.log_beta + tok);
   for (int t = 0; t < n; ++t) {
     const size_t tn = tok + a.H;
-    if (t + 1 < n)
+    if (KDA_PREFETCH_NEXT && t + 1 < n)
       nxt.load(a.log_k + tn * DK + p.row0, nullptr, a.log_alpha + tn * DK + p.row0, a.log_v + tn * DV + p.col0,
                a.log_beta + tn);
-    float kr[R], qr[R], ar[R], vc[4], o[4];
-    cur.widen_all(kr, qr, ar, vc);
-    token_update<R, false>(S, kr, ar, qr, vc, cur.beta, 0.f, o);
-    cur = nxt;
+    float o[4];
+    cur.update(S, 0.f, o);
+    if (KDA_PREFETCH_NEXT)
+      cur = nxt;
+    else if (t + 1 < n)
+      cur.load(a.log_k + tn * DK + p.row0, nullptr, a.log_alpha + tn * DK + p.row0, a.log_v + tn * DV + p.col0,
+               a.log_beta + tn);
     tok = tn;
   }
   store_tile<R, DV>(sp, S);
@@ -231,7 +264,7 @@ __global__ void __launch_bounds__(kWave * waves_per_group<DV>()) commit_kernel(C
 }
 
 template <int DK, int DV, typename TIn>
-__global__ void __launch_bounds__(kWave * waves_per_group<DV>()) prefill_recurrent_kernel(PrefillArgs<TIn> a) {
+__global__ void KDA_OCCUPANCY __launch_bounds__(kWave * waves_per_group<DV>()) prefill_recurrent_kernel(PrefillArgs<TIn> a) {
   typedef Place<DK, DV> P;
   constexpr int R = P::R;
   const P p(a.H);
@@ -251,9 +284,8 @@ __global__ void __launch_bounds__(kWave * waves_per_group<DV>()) prefill_recurre
     if (t + 1 < a.L)
       nxt.load(a.k + tn * DK + p.row0, a.q + tn * DK + p.row0, a.alpha + tn * DK + p.row0,
                a.v + tn * DV + p.col0, a.beta + tn);
-    float kr[R], qr[R], ar[R], vc[4], o[4];
-    cur.widen_all(kr, qr, ar, vc);
-    token_update<R, true>(S, kr, ar, qr, vc, cur.beta, a.scale, o);
+    float o[4];
+    cur.update(S, a.scale, o);
     if (p.rg == 0) *reinterpret_cast<float4*>(a.o + tok * DV + p.col0) = make_float4(o[0], o[1], o[2], o[3]);
     if (n_ckpt > 0 && (t + 1) % a.ckpt_every == 0) {
       const int m = (t + 1) / a.ckpt_every - 1;

@@ -137,6 +137,7 @@ def test_prefill_validation(k):
                                      every, ck, ctypes.byref(sl) if sl is not None else None, err, None)
 
     assert pre(chunk=48) == SHAPE
+    assert pre(chunk=16) == SHAPE
     assert pre(Lt=-1) == SHAPE
     assert pre(every=100) == SHAPE             # not a multiple of the chunk
     assert pre(every=-64) == SHAPE

@@ -153,7 +153,8 @@ def test_spec_verify_rounds():
     assert_parity(o_gpu, np.stack(o_ref), S[:, heads].cpu().numpy(), Sr, "spec_verify 512 rounds")
 
 
-def test_prefill_checkpoints_and_resume():
+@pytest.mark.parametrize("variant", ["chunked", "recurrent"])
+def test_prefill_checkpoints_and_resume(variant):
     spec = CFG["prefill"]
     B, L, H = spec.B[0], spec.steps, spec.H
     every, rpos, rsteps = spec.extra["ckpt_every"], spec.extra["resume_pos"], spec.extra["resume_steps"]
@@ -169,10 +170,15 @@ def test_prefill_checkpoints_and_resume():
     slots = torch.arange(B * n_ck, dtype=torch.int32, device="cuda").view(B, n_ck)
     err = torch.zeros(1, dtype=torch.int32, device="cuda")
     o = torch.empty((B, L, H, spec.dv), dtype=torch.float32, device="cuda")
-    say("prefill: GPU")
-    kda.prefill_recurrent(S, pos, d["q"], d["k"], d["v"], d["alpha"], d["beta"], o, ckpt_every=every,
-                          ckpt_slots=slots, pool=pool, dev_err=err)
+    say(f"prefill ({variant}): GPU")
+    if variant == "chunked":
+        kda.prefill_chunked(S, pos, d["q"], d["k"], d["v"], d["alpha"], d["beta"], o, chunk=spec.extra["chunk"],
+                            ckpt_every=every, ckpt_slots=slots, pool=pool, dev_err=err)
+    else:
+        kda.prefill_recurrent(S, pos, d["q"], d["k"], d["v"], d["alpha"], d["beta"], o, ckpt_every=every,
+                              ckpt_slots=slots, pool=pool, dev_err=err)
     torch.cuda.synchronize()
+    assert kda.last_variant() == f"prefill_{variant}"
     assert err.item() == 0 and pos.cpu().tolist() == [L] * B
     m_res = rpos // every - 1
     kda.restore(S, pos, list(range(B)), [b * n_ck + m_res for b in range(B)], pool)

@@ -16,7 +16,7 @@ import torch
 import recurrent_state_amd as kda
 import synth
 from oracle import kda_oracle as ko
-from tests.kda_testutil import assert_parity, bits, dev_inputs, dev_tensor, say, token_slice
+from tests.kda_testutil import assert_parity, bits, dev_inputs, dev_tensor, say, state_err, token_slice
 
 pytestmark = pytest.mark.gpu
 
@@ -240,3 +240,74 @@ def test_decode_is_deterministic():
         o = decode_run(S, torch.zeros(B, dtype=torch.int64, device="cuda"), d)
         outs.append((bits(S).clone(), bits(o).clone()))
     assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
+
+
+@pytest.mark.parametrize("dk,dv,dt", [(128, 128, "bf16"), (64, 64, "f32"), (64, 128, "bf16"), (128, 64, "f32")])
+@pytest.mark.parametrize("chunk", [32, 64])
+@pytest.mark.parametrize("L", [1, 37, 64, 200])
+def test_prefill_chunked_matches_oracle(dk, dv, dt, chunk, L):
+    spec = spec_for(dk, dv, dt, tag=109)
+    B = 2
+    every = 2 * chunk
+    say(f"prefill_chunked dk={dk} dv={dv} {dt} chunk={chunk} L={L}")
+    S0 = synth.initial_state(spec, B)
+    inp = synth.token_inputs(spec, B, L)
+    d = dev_inputs(inp)
+    S = dev_tensor(S0)
+    pos = torch.tensor([3, 0], dtype=torch.int64, device="cuda")
+    n_ck = L // every
+    pool = kda.SlotPool(max(1, 2 * n_ck), spec.H, dk, dv, "cuda")
+    slots = torch.arange(2 * n_ck, dtype=torch.int32, device="cuda").view(2, n_ck) if n_ck else None
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    o = torch.full((B, L, spec.H, dv), float("nan"), dtype=torch.float32, device="cuda")
+    kda.prefill_chunked(S, pos, d["q"], d["k"], d["v"], d["alpha"], d["beta"], o, chunk=chunk, ckpt_every=every,
+                        ckpt_slots=slots, pool=pool, dev_err=err)
+    assert kda.last_variant() == "prefill_chunked"
+    S_ref, pos_ref, o_ref, ck = ko.prefill(S0, np.array([3, 0]), inp, spec.scale, every)
+    assert_parity(o.cpu().numpy(), o_ref, S.cpu().numpy(), S_ref, f"prefill_chunked L={L} chunk={chunk}")
+    assert pos.cpu().tolist() == pos_ref.tolist() and err.item() == 0
+    for m, (Sm, pm) in enumerate(ck):
+        for b in range(B):
+            slot = b * n_ck + m
+            se = state_err(pool.states[slot:slot + 1].cpu().numpy(), Sm[b:b + 1])
+            assert se <= 1e-3, f"checkpoint {m} seq {b}: {se:.3e}"
+            assert pool.pos[slot].item() == pm[b]
+
+
+@pytest.mark.parametrize("gate", ["sigmoid", "softplus"])
+def test_prefill_chunked_gate_ranges_and_zero_state(gate):
+    # Stronger decay (the tiny workload's gates) and a zero initial state.
+    spec = synth.ConfigSpec("gates", 111, (2,), 4, 128, 128, "bf16", gate, "zero", 0)
+    B, L = 2, 300
+    S0 = synth.initial_state(spec, B)
+    inp = synth.token_inputs(spec, B, L)
+    d = dev_inputs(inp)
+    S = dev_tensor(S0)
+    pos = torch.zeros(B, dtype=torch.int64, device="cuda")
+    o = torch.empty((B, L, spec.H, 128), dtype=torch.float32, device="cuda")
+    kda.prefill_chunked(S, pos, d["q"], d["k"], d["v"], d["alpha"], d["beta"], o, chunk=64)
+    S_ref, _, o_ref, _ = ko.prefill(S0, np.zeros(B, np.int64), inp, spec.scale, 0)
+    assert_parity(o.cpu().numpy(), o_ref, S.cpu().numpy(), S_ref, f"prefill_chunked gate={gate}")
+
+
+def test_prefill_chunked_then_decode_continues():
+    # A prompt processed in two chunked calls equals one call (positions and
+    # state carry over), and decode continues from it.
+    spec = spec_for(128, 128, "bf16", tag=112)
+    B, L1, L2 = 2, 96, 70
+    S0 = synth.initial_state(spec, B)
+    inp = synth.token_inputs(spec, B, L1 + L2 + 3)
+    d = dev_inputs(inp)
+    S = dev_tensor(S0)
+    pos = torch.zeros(B, dtype=torch.int64, device="cuda")
+    part = lambda t0, t1: {k_: v_[:, t0:t1].contiguous() for k_, v_ in d.items()}  # noqa: E731
+    o1 = torch.empty((B, L1, spec.H, 128), device="cuda")
+    o2 = torch.empty((B, L2, spec.H, 128), device="cuda")
+    p1, p2 = part(0, L1), part(L1, L1 + L2)
+    kda.prefill_chunked(S, pos, p1["q"], p1["k"], p1["v"], p1["alpha"], p1["beta"], o1, chunk=32)
+    kda.prefill_chunked(S, pos, p2["q"], p2["k"], p2["v"], p2["alpha"], p2["beta"], o2, chunk=64)
+    o3 = decode_run(S, pos, part(L1 + L2, L1 + L2 + 3))
+    assert pos.cpu().tolist() == [L1 + L2 + 3] * B
+    S_ref, o_ref = ko.decode(S0, inp, spec.scale)
+    assert_parity(torch.cat([o1, o2, o3], dim=1).cpu().numpy(), o_ref, S.cpu().numpy(), S_ref,
+                  "two chunked prefills + decode")
