@@ -15,9 +15,10 @@
 //   S'   = Diag(2^g_n) S + Kb^T E
 //
 // One workgroup owns one (sequence, head) for the whole prompt and walks
-// its chunks in order; wave w of the workgroup owns value columns
-// [32 w, 32 w + 32) of the state, which stays in registers in the MFMA
-// accumulator layout across chunks.  The key-side products (Kt, Qt, Kh, Kb,
+// its chunks in order; wave w of the workgroup (dv / 16 waves) owns value
+// columns [16 w, 16 w + 16) of the state, which stays in registers in the
+// MFMA accumulator layout across chunks.  With two waves per SIMD, one
+// wave's MFMA and LDS latency hides behind the other's work.  The key-side products (Kt, Qt, Kh, Kb,
 // A, P, T) are shared by the waves through LDS.
 //
 // Precision: every contraction runs on v_mfma_f32_16x16x32_bf16 with fp32
@@ -164,10 +165,10 @@ struct PrefillArgs {
   float scale;
 };
 
-// LDS layout of one workgroup (bytes).  Regions are reused across phases:
-// R2 holds Kh during the A/P products and then A (fp32) and P (hi/lo); R3
-// holds the off-diagonal inverse blocks and per-wave scratch during the
-// triangular solve and then T (hi/lo).
+// LDS layout of one workgroup (bytes).  Region R2 holds Kh during the A/P
+// products and then P (hi/lo) plus the fp32 diagonal 16 x 16 blocks of A;
+// R3 holds M (hi/lo): the strictly lower off-diagonal blocks of A and, on
+// the diagonal, the inverses (I + A_jj)^-1.
 template <int DK, int CH, int NW>
 struct Smem {
   static constexpr int RS_K = DK + 4;  // row stride (elements) of channel-indexed planes
@@ -182,11 +183,11 @@ struct Smem {
   static constexpr int off_kb = off_kq + 2 * KQ_PLANE * 2;
   static constexpr int off_r2 = off_kb + 2 * KB_PLANE * 2;
   static constexpr int r2_a = 2 * KH_PLANE * 2;
-  static constexpr int r2_b = CH * CH * 4 + 2 * CC_PLANE * 2;
+  static constexpr int RS_D = 17;      // fp32 row stride of a diagonal block: odd, conflict-free columns
+  static constexpr int DIAG = NB * 16 * RS_D;  // floats of the diagonal blocks
+  static constexpr int r2_b = 2 * CC_PLANE * 2 + DIAG * 4;
   static constexpr int off_r3 = off_r2 + (r2_a > r2_b ? r2_a : r2_b);
-  static constexpr int r3_a = 2 * CC_PLANE * 2;
-  static constexpr int r3_b = (NB * (NB - 1) / 2 + NW) * 16 * 16 * 4;
-  static constexpr int off_misc = off_r3 + (r3_a > r3_b ? r3_a : r3_b);
+  static constexpr int off_misc = off_r3 + 2 * CC_PLANE * 2;
   static constexpr int off_beta = off_misc;
   static constexpr int off_gn = off_beta + CH * 4;
   static constexpr int off_tot = off_gn + DK * 4;
@@ -195,12 +196,15 @@ struct Smem {
   static_assert(r2_a % 16 == 0 && off_r3 % 16 == 0 && off_misc % 16 == 0, "alignment");
 };
 
-// Index of off-diagonal block (i, j), i > j, inside the inverse scratch.
-__device__ __forceinline__ int off_block(int i, int j) { return i * (i - 1) / 2 + j; }
+// Lower-triangular tile (mt, nt), nt <= mt < 4, of triangular index ii.
+__device__ __forceinline__ void tri_tile(int ii, int& mt, int& nt) {
+  mt = ii >= 6 ? 3 : ii >= 3 ? 2 : ii >= 1 ? 1 : 0;
+  nt = ii - mt * (mt + 1) / 2;
+}
 
 template <int DK, int DV, int CH, typename TIn>
-__global__ void __launch_bounds__(DV * 2) prefill_chunked_kernel(PrefillArgs<TIn> a) {
-  constexpr int NW = DV / 32;        // waves; wave w owns value columns [32 w, 32 w + 32)
+__global__ void __launch_bounds__(DV * 4) prefill_chunked_kernel(PrefillArgs<TIn> a) {
+  constexpr int NW = DV / 16;        // waves; wave w owns value columns [16 w, 16 w + 16)
   constexpr int NT = 64 * NW;        // threads
   constexpr int NB = CH / 16;        // 16-token blocks
   constexpr int KB = DK / 32;        // 32-channel k blocks
@@ -209,7 +213,7 @@ __global__ void __launch_bounds__(DV * 2) prefill_chunked_kernel(PrefillArgs<TIn
   typedef Smem<DK, CH, NW> L;
   constexpr int NG = L::NG;
   constexpr int TPG = CH / NG;       // tokens per preparation group
-  static_assert(NT % CP == 0 && CH % NG == 0 && TPG % 4 == 0, "preparation mapping");
+  static_assert(NT % CP == 0 && CH % NG == 0 && TPG % 2 == 0, "preparation mapping");
   static_assert(CH == 32 || CH == 64, "chunk");
 
   __shared__ __align__(16) char smem[L::total];
@@ -219,48 +223,46 @@ __global__ void __launch_bounds__(DV * 2) prefill_chunked_kernel(PrefillArgs<TIn
   bf16_t* kb_lo = kb_hi + L::KB_PLANE;
   bf16_t* kh_hi = reinterpret_cast<bf16_t*>(smem + L::off_r2);
   bf16_t* kh_lo = kh_hi + L::KH_PLANE;
-  float* abuf = reinterpret_cast<float*>(smem + L::off_r2);
-  bf16_t* p_hi = reinterpret_cast<bf16_t*>(smem + L::off_r2 + CH * CH * 4);
+  bf16_t* p_hi = reinterpret_cast<bf16_t*>(smem + L::off_r2);
   bf16_t* p_lo = p_hi + L::CC_PLANE;
-  bf16_t* t_hi = reinterpret_cast<bf16_t*>(smem + L::off_r3);
-  bf16_t* t_lo = t_hi + L::CC_PLANE;
-  float* xoff = reinterpret_cast<float*>(smem + L::off_r3);
+  float* adiag = reinterpret_cast<float*>(smem + L::off_r2 + 2 * L::CC_PLANE * 2);
+  bf16_t* m_hi = reinterpret_cast<bf16_t*>(smem + L::off_r3);
+  bf16_t* m_lo = m_hi + L::CC_PLANE;
   float* sbeta = reinterpret_cast<float*>(smem + L::off_beta);
   float* sgn = reinterpret_cast<float*>(smem + L::off_gn);
   float* stot = reinterpret_cast<float*>(smem + L::off_tot);
 
-  const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
-  const int l16 = lane & 15, g = lane >> 4;
   const int bh = blockIdx.x;
   const int b = bh / a.H, h = bh - b * a.H;
-  const bool owner = h == 0 && tid == 0;  // the one writer of positions
+  const bool owner = h == 0 && threadIdx.x == 0;  // the one writer of positions
   const int64_t pos0 = owner ? a.pos[b] : 0;
   const int n_ckpt = a.ckpt_every > 0 ? a.L / a.ckpt_every : 0;
-  const size_t tok0 = (size_t)b * a.L;             // first token row of this sequence
+  const size_t tok0 = (size_t)b * a.L;  // first token row of this sequence
+  const f32x4_t zero4 = {0.f, 0.f, 0.f, 0.f};
 
-  // State slice of this wave in the accumulator layout:
-  // st[mt][nt][r] = S[16 mt + 4 g + r][32 wave + 16 nt + l16].
-  f32x4_t st[MT][2];
-  // Tile element (mt, nt, r) of a [DK][DV] fp32 state lies at byte
-  // tile_voff + tile_soff(mt, nt, r).
-  const int tile_voff = ((4 * g) * DV + 32 * wave + l16) * 4;
-#define KDA_TILE_SOFF(mt, nt, r) (((16 * (mt) + (r)) * DV + 16 * (nt)) * 4)
+  // State columns of this wave in the accumulator layout:
+  // st[mt][r] = S[16 mt + 4 g + r][col], at byte tile_voff + (16 mt + r) DV 4.
+  f32x4_t st[MT];
+  const int tile_voff = ((4 * ((threadIdx.x & 63) >> 4)) * DV + 16 * (threadIdx.x >> 6) + (threadIdx.x & 15)) * 4;
   const rsrc_t rs_state = make_rsrc(a.state + (size_t)bh * DK * DV, DK * DV * 4);
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) st[mt][nt][r] = ld_f32(rs_state, tile_voff, KDA_TILE_SOFF(mt, nt, r));
+    for (int r = 0; r < 4; ++r) st[mt][r] = ld_f32(rs_state, tile_voff, (16 * mt + r) * DV * 4);
 
   const int n_chunks = (a.L + CH - 1) / CH;
   for (int c = 0; c < n_chunks; ++c) {
+    // Lane coordinates are re-derived from an opaque copy of the thread id
+    // in every chunk: otherwise the compiler hoists every LDS address of the
+    // loop body out of the chunk loop and keeps them all live in registers.
+    int tid = threadIdx.x;
+    asm volatile("" : "+v"(tid));
+    const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int l16 = lane & 15, g = lane >> 4;
+    const int col = 16 * wave + l16;  // this lane's value column in the accumulator layout
     const int t_base = c * CH;
-    const int n = min(CH, a.L - t_base);  // valid tokens in this chunk
-    // Windows over this chunk's valid token rows of this head.  Rows at and
-    // past n are padding: they are never loaded (their values are zero) and
-    // never stored.
+    const int n = min(CH, a.L - t_base);  // valid tokens in this chunk; rows n.. are padding
+    // Windows over this chunk's valid token rows of this head.
     const size_t row0 = (tok0 + t_base) * a.H + h;  // [B][L][H] row index of the chunk's first token
     const int rowk = a.H * DK, rowv = a.H * DV;       // elements between consecutive tokens
     const rsrc_t rs_k = make_rsrc(a.k + row0 * DK, ((n - 1) * rowk + DK) * sizeof(TIn));
@@ -271,21 +273,58 @@ __global__ void __launch_bounds__(DV * 2) prefill_chunked_kernel(PrefillArgs<TIn
     const rsrc_t rs_o = make_rsrc(a.o + row0 * DV, ((n - 1) * rowv + DV) * 4);
 
     // ---- Phase 1: decay cumsum and the decayed key/query planes ---------
-    // Pass A: per-channel prefix sums of log2(alpha) within each token group,
-    // then the group totals are combined through LDS.  Pass B reads k and q
-    // (an L2 hit) and writes the decayed planes.
+    // Thread (cp, tg) owns key channels 2 cp, 2 cp + 1 for tokens
+    // [tg TPG, tg TPG + TPG).  Every global load of the chunk (alpha, k, q,
+    // beta and this wave's value tiles) is issued here, before any use, and
+    // unconditionally, so the compiler issues them back to back and the
+    // chunk pays one memory latency: a padding row reads the last valid row
+    // (always inside the window) and its value is then replaced (alpha by 1,
+    // the others by 0).
+    const int cp = tid % CP, tg = tid / CP;
+    const int c0 = 2 * cp;
+    float al0[TPG], al1[TPG], k0[TPG], k1[TPG], q0[TPG], q1[TPG], bt[TPG];
+#pragma unroll
+    for (int i = 0; i < TPG; ++i) {
+      const int rc = min(tg * TPG + i, n - 1);
+      const int vo = rc * rowk + c0;
+      ld_in2(rs_a, vo * 4, 0, al0[i], al1[i], (const float*)nullptr);
+      ld_in2(rs_k, vo * (int)sizeof(TIn), 0, k0[i], k1[i], (const TIn*)nullptr);
+      ld_in2(rs_q, vo * (int)sizeof(TIn), 0, q0[i], q1[i], (const TIn*)nullptr);
+      bt[i] = ld_f32(rs_b, rc * a.H * 4, 0);
+    }
+    // Value tile of this wave: vv[mt][r] = V[16 mt + 4 g + r][col].
+    float vv[NB][4];
+#pragma unroll
+    for (int mt = 0; mt < NB; ++mt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int rc = min(16 * mt + 4 * g + r, n - 1);
+        vv[mt][r] = ld_in(rs_v, (rc * rowv + col) * (int)sizeof(TIn), 0, (const TIn*)nullptr);
+      }
+#pragma unroll
+    for (int i = 0; i < TPG; ++i) {
+      const bool pad = tg * TPG + i >= n;
+      al0[i] = pad ? 1.f : al0[i];  // padding tokens do not decay
+      al1[i] = pad ? 1.f : al1[i];
+      k0[i] = pad ? 0.f : k0[i];
+      k1[i] = pad ? 0.f : k1[i];
+      q0[i] = pad ? 0.f : q0[i];
+      q1[i] = pad ? 0.f : q1[i];
+      bt[i] = pad ? 0.f : bt[i];
+    }
+#pragma unroll
+    for (int mt = 0; mt < NB; ++mt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) vv[mt][r] = 16 * mt + 4 * g + r < n ? vv[mt][r] : 0.f;
     {
-      const int cp = tid % CP, tg = tid / CP;
-      const int c0 = 2 * cp;
+      // Pass A: per-channel prefix sums of log2(alpha) within the token
+      // group; the group totals are combined through LDS.
       float g0[TPG], g1[TPG];
       float s0 = 0.f, s1 = 0.f;
 #pragma unroll
       for (int i = 0; i < TPG; ++i) {
-        const int tr = tg * TPG + i;
-        float al0 = 1.f, al1 = 1.f;  // padding tokens do not decay
-        if (tr < n) ld_in2(rs_a, (tg * TPG * rowk + c0) * 4, i * rowk * 4, al0, al1, (const float*)nullptr);
-        s0 += __log2f(al0);
-        s1 += __log2f(al1);
+        s0 += __log2f(al0[i]);
+        s1 += __log2f(al1[i]);
         g0[i] = s0;
         g1[i] = s1;
       }
@@ -293,12 +332,7 @@ __global__ void __launch_bounds__(DV * 2) prefill_chunked_kernel(PrefillArgs<TIn
       stot[tg * DK + c0 + 1] = s1;
       if (cp == 0) {
 #pragma unroll
-        for (int i = 0; i < TPG; ++i) {
-          const int tr = tg * TPG + i;
-          float bv = 0.f;
-          if (tr < n) bv = ld_f32(rs_b, tg * TPG * a.H * 4, i * a.H * 4);
-          sbeta[tr] = bv;
-        }
+        for (int i = 0; i < TPG; ++i) sbeta[tg * TPG + i] = bt[i];
       }
       __syncthreads();
       float off0 = 0.f, off1 = 0.f, gn0 = 0.f, gn1 = 0.f;
@@ -316,132 +350,113 @@ __global__ void __launch_bounds__(DV * 2) prefill_chunked_kernel(PrefillArgs<TIn
         sgn[c0] = exp2f(gn0);
         sgn[c0 + 1] = exp2f(gn1);
       }
-      uint32_t kbh0[2], kbl0[2], kbh1[2], kbl1[2];
+      // Pass B: the decayed planes; Kb goes to transposed planes two tokens at a time.
+      uint32_t kbh0 = 0, kbl0 = 0, kbh1 = 0, kbl1 = 0;
 #pragma unroll
       for (int i = 0; i < TPG; ++i) {
         const int tr = tg * TPG + i;
-        float k0 = 0.f, k1 = 0.f, q0 = 0.f, q1 = 0.f;
-        if (tr < n) {
-          const int vo = (tg * TPG * rowk + c0) * (int)sizeof(TIn), so = i * rowk * (int)sizeof(TIn);
-          ld_in2(rs_k, vo, so, k0, k1, (const TIn*)nullptr);
-          ld_in2(rs_q, vo, so, q0, q1, (const TIn*)nullptr);
-        }
         const float x0 = off0 + g0[i], x1 = off1 + g1[i];
         const float e0 = exp2f(x0), e1 = exp2f(x1);
         const float ie0 = exp2f(-x0), ie1 = exp2f(-x1);
         uint32_t hi, lo;
-        split2(k0 * e0, k1 * e1, hi, lo);  // Kt
+        split2(k0[i] * e0, k1[i] * e1, hi, lo);  // Kt
         *reinterpret_cast<uint32_t*>(kq_hi + tr * L::RS_K + c0) = hi;
         *reinterpret_cast<uint32_t*>(kq_lo + tr * L::RS_K + c0) = lo;
-        split2(q0 * e0, q1 * e1, hi, lo);  // Qt
+        split2(q0[i] * e0, q1[i] * e1, hi, lo);  // Qt
         *reinterpret_cast<uint32_t*>(kq_hi + (CH + tr) * L::RS_K + c0) = hi;
         *reinterpret_cast<uint32_t*>(kq_lo + (CH + tr) * L::RS_K + c0) = lo;
-        split2(k0 * ie0, k1 * ie1, hi, lo);  // Kh
+        split2(k0[i] * ie0, k1[i] * ie1, hi, lo);  // Kh
         *reinterpret_cast<uint32_t*>(kh_hi + tr * L::RS_K + c0) = hi;
         *reinterpret_cast<uint32_t*>(kh_lo + tr * L::RS_K + c0) = lo;
-        // Kb = k 2^(g_n - g): the transposed planes are written 4 tokens at a time.
         __bf16 l0, l1;
-        const __bf16 h0 = split_hi(k0 * exp2f(gn0 - x0), l0), h1 = split_hi(k1 * exp2f(gn1 - x1), l1);
-        const int w = (i >> 1) & 1, sh = (i & 1) * 16;
-        if ((i & 1) == 0) kbh0[w] = kbl0[w] = kbh1[w] = kbl1[w] = 0;
-        kbh0[w] |= bf16_bits(h0) << sh;
-        kbl0[w] |= bf16_bits(l0) << sh;
-        kbh1[w] |= bf16_bits(h1) << sh;
-        kbl1[w] |= bf16_bits(l1) << sh;
-        if ((i & 3) == 3) {
-          const int t4 = tr - 3;
-          *reinterpret_cast<uint2*>(kb_hi + c0 * L::RS_C + t4) = make_uint2(kbh0[0], kbh0[1]);
-          *reinterpret_cast<uint2*>(kb_lo + c0 * L::RS_C + t4) = make_uint2(kbl0[0], kbl0[1]);
-          *reinterpret_cast<uint2*>(kb_hi + (c0 + 1) * L::RS_C + t4) = make_uint2(kbh1[0], kbh1[1]);
-          *reinterpret_cast<uint2*>(kb_lo + (c0 + 1) * L::RS_C + t4) = make_uint2(kbl1[0], kbl1[1]);
+        const __bf16 h0 = split_hi(k0[i] * exp2f(gn0 - x0), l0), h1 = split_hi(k1[i] * exp2f(gn1 - x1), l1);
+        const int sh = (i & 1) * 16;
+        kbh0 |= bf16_bits(h0) << sh;
+        kbl0 |= bf16_bits(l0) << sh;
+        kbh1 |= bf16_bits(h1) << sh;
+        kbl1 |= bf16_bits(l1) << sh;
+        if (i & 1) {
+          *reinterpret_cast<uint32_t*>(kb_hi + c0 * L::RS_C + tr - 1) = kbh0;
+          *reinterpret_cast<uint32_t*>(kb_lo + c0 * L::RS_C + tr - 1) = kbl0;
+          *reinterpret_cast<uint32_t*>(kb_hi + (c0 + 1) * L::RS_C + tr - 1) = kbh1;
+          *reinterpret_cast<uint32_t*>(kb_lo + (c0 + 1) * L::RS_C + tr - 1) = kbl1;
+          kbh0 = kbl0 = kbh1 = kbl1 = 0;
         }
       }
     }
     __syncthreads();
-
-    // Value tiles this wave needs in phase 4, loaded now so the latency
-    // overlaps the key-side products: vv[mt][nt][r] = V[16 mt + 4 g + r][32 wave + 16 nt + l16].
-    // Value / output element (mt, nt, r) of this wave lies at
-    // io_voff + io_soff(mt, nt, r) elements inside the chunk window.
-    const int io_voff = (4 * g) * rowv + 32 * wave + l16;
-#define KDA_IO_SOFF(mt, nt, r) ((16 * (mt) + (r)) * rowv + 16 * (nt))
-    float vv[NB][2][4];
-#pragma unroll
-    for (int mt = 0; mt < NB; ++mt)
-#pragma unroll
-      for (int nt = 0; nt < 2; ++nt)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          vv[mt][nt][r] = 0.f;
-          if (16 * mt + 4 * g + r < n)
-            vv[mt][nt][r] = ld_in(rs_v, io_voff * (int)sizeof(TIn), KDA_IO_SOFF(mt, nt, r) * (int)sizeof(TIn),
-                                  (const TIn*)nullptr);
-        }
 
     // ---- Phase 2: A = Diag(beta) Kt Kh^T and P = Qt Kh^T (lower tiles) ---
     // Tile list: index i < NA are A tiles (mt, nt), nt <= mt < NB; the next
     // NA are P tiles (NB + mt, nt).  Waves take tiles round-robin.
     constexpr int NA = NB * (NB + 1) / 2;
     constexpr int MAXT = (2 * NA + NW - 1) / NW;
+    constexpr bool EVEN = (2 * NA) % NW == 0;  // every wave has MAXT tiles
     f32x4_t at[MAXT];
 #pragma unroll
-    for (int s = 0; s < MAXT; ++s) {
-      const int i = wave + s * NW;
-      at[s] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-      if (i < 2 * NA) {
-        const int ii = i < NA ? i : i - NA;
-        int mt = 0;
-        while ((mt + 1) * (mt + 2) / 2 <= ii) ++mt;
-        const int nt = ii - mt * (mt + 1) / 2;
+    for (int s_ = 0; s_ < MAXT; ++s_) {
+      const int i = wave + s_ * NW;
+      at[s_] = zero4;
+      if (EVEN || i < 2 * NA) {
+        int mt, nt;
+        tri_tile(i < NA ? i : i - NA, mt, nt);
         const int row = (i < NA ? 0 : CH) + 16 * mt + l16;
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) {
-          const int c0 = 32 * kb + 4 * g;
-          at[s] = mfma3(plane_op2(kq_hi, kq_lo, row, L::RS_K, c0), plane_op2(kh_hi, kh_lo, 16 * nt + l16, L::RS_K, c0),
-                        at[s]);
+          const int k0_ = 32 * kb + 4 * g;
+          at[s_] = mfma3(plane_op2(kq_hi, kq_lo, row, L::RS_K, k0_), plane_op2(kh_hi, kh_lo, 16 * nt + l16, L::RS_K, k0_),
+                         at[s_]);
         }
       }
     }
-    __syncthreads();  // Kh is dead from here on; A and P take its place
+    __syncthreads();  // Kh is dead from here on; P and the diagonal blocks of A take its place
 #pragma unroll
-    for (int s = 0; s < MAXT; ++s) {
-      const int i = wave + s * NW;
-      if (i < 2 * NA) {
-        const int ii = i < NA ? i : i - NA;
-        int mt = 0;
-        while ((mt + 1) * (mt + 2) / 2 <= ii) ++mt;
-        const int nt = ii - mt * (mt + 1) / 2;
-        const int col = 16 * nt + l16;
+    for (int s_ = 0; s_ < MAXT; ++s_) {
+      const int i = wave + s_ * NW;
+      if (EVEN || i < 2 * NA) {
+        int mt, nt;
+        tri_tile(i < NA ? i : i - NA, mt, nt);
+        const int tc = 16 * nt + l16;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const int row = 16 * mt + 4 * g + r;
+          const int tr = 16 * mt + 4 * g + r;
           if (i < NA) {
-            abuf[row * CH + col] = col < row ? at[s][r] * sbeta[row] : 0.f;
+            const float av = tc < tr ? at[s_][r] * sbeta[tr] : 0.f;
+            if (mt == nt) {
+              adiag[(mt * 16 + 4 * g + r) * L::RS_D + l16] = av;
+            } else {
+              __bf16 lo;
+              const __bf16 hi = split_hi(av, lo);
+              m_hi[tr * L::RS_C + tc] = __builtin_bit_cast(bf16_t, hi);
+              m_lo[tr * L::RS_C + tc] = __builtin_bit_cast(bf16_t, lo);
+            }
           } else {
             __bf16 lo;
-            const __bf16 hi = split_hi(col <= row ? at[s][r] : 0.f, lo);
-            p_hi[row * L::RS_C + col] = __builtin_bit_cast(bf16_t, hi);
-            p_lo[row * L::RS_C + col] = __builtin_bit_cast(bf16_t, lo);
+            const __bf16 hi = split_hi(tc <= tr ? at[s_][r] : 0.f, lo);
+            p_hi[tr * L::RS_C + tc] = __builtin_bit_cast(bf16_t, hi);
+            p_lo[tr * L::RS_C + tc] = __builtin_bit_cast(bf16_t, lo);
           }
         }
       }
     }
-    // P tiles above the diagonal inside a 32-token k block are read by the
-    // P E product: make them zero.
+    // Upper tiles inside a 32-token k block are read (against zero operands)
+    // by the P E product and the block solve: make them zero in P and M.
     for (int i = wave; i < NB / 2; i += NW) {
-      const int mt = 2 * i, nt = 2 * i + 1;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int row = 16 * mt + 4 * g + r, col = 16 * nt + l16;
-        p_hi[row * L::RS_C + col] = 0;
-        p_lo[row * L::RS_C + col] = 0;
+        const int tr = 32 * i + 4 * g + r, tc = 32 * i + 16 + l16;
+        p_hi[tr * L::RS_C + tc] = 0;
+        p_lo[tr * L::RS_C + tc] = 0;
+        m_hi[tr * L::RS_C + tc] = 0;
+        m_lo[tr * L::RS_C + tc] = 0;
       }
     }
     __syncthreads();
 
-    // ---- Phase 3: T = (I + A)^-1 Diag(beta) by 16 x 16 blocks (fp32) -----
-    // 3a: diagonal blocks X_jj = (I + A_jj)^-1; lane c < 16 solves column c.
-    // The strictly lower part of X_jj replaces A_jj (its diagonal is 1).
+    // ---- Phase 3: diagonal blocks X_jj = (I + A_jj)^-1 into M ------------
+    // Lane c < 16 of wave j solves column c of block j by forward
+    // substitution in fp32, then writes the block (1 on the diagonal, 0
+    // above) as hi/lo.
     for (int j = wave; j < NB; j += NW) {
       if (lane < 16) {
         const int cc = lane;
@@ -451,163 +466,75 @@ __global__ void __launch_bounds__(DV * 2) prefill_chunked_kernel(PrefillArgs<TIn
           float acc = 0.f;
 #pragma unroll
           for (int i = 0; i < 16; ++i)
-            if (i < r) acc = __builtin_fmaf(abuf[(16 * j + r) * CH + 16 * j + i], x[i], acc);
+            if (i < r) acc = __builtin_fmaf(adiag[(j * 16 + r) * L::RS_D + i], x[i], acc);
           x[r] = r == cc ? 1.f : (r < cc ? 0.f : -acc);
         }
 #pragma unroll
-        for (int r = 0; r < 16; ++r)
-          if (r > cc) abuf[(16 * j + r) * CH + 16 * j + cc] = x[r];
-      }
-    }
-    __syncthreads();
-    // 3b: off-diagonal blocks by distance d = i - j:
-    //   X_ij = -X_ii sum_{k=j}^{i-1} A_ik X_kj.
-    // Lane l computes row m = l >> 2, columns 4 (l & 3) .. + 3 of a block.
-    {
-      float* yscr = xoff + (NB * (NB - 1) / 2 + wave) * 256;
-      const int m = lane >> 2, n0 = 4 * (lane & 3);
-      for (int d = 1; d < NB; ++d) {
-        for (int j = wave; j + d < NB; j += NW) {
-          const int i = j + d;
-          float y[4] = {0.f, 0.f, 0.f, 0.f};
-          for (int kk = j; kk < i; ++kk) {
-#pragma unroll
-            for (int q = 0; q < 16; ++q) {
-              const float aik = abuf[(16 * i + m) * CH + 16 * kk + q];
-              float xq[4];
-              if (kk == j) {
-#pragma unroll
-                for (int u = 0; u < 4; ++u)
-                  xq[u] = abuf[(16 * j + q) * CH + 16 * j + n0 + u] + (q == n0 + u ? 1.f : 0.f);
-              } else {
-#pragma unroll
-                for (int u = 0; u < 4; ++u) xq[u] = xoff[off_block(kk, j) * 256 + q * 16 + n0 + u];
-              }
-#pragma unroll
-              for (int u = 0; u < 4; ++u) y[u] = __builtin_fmaf(aik, xq[u], y[u]);
-            }
-          }
-#pragma unroll
-          for (int u = 0; u < 4; ++u) yscr[m * 16 + n0 + u] = y[u];
-          float z[4] = {y[0], y[1], y[2], y[3]};
-#pragma unroll
-          for (int q = 0; q < 16; ++q) {
-            const float xiq = abuf[(16 * i + m) * CH + 16 * i + q];  // strictly lower part of X_ii
-#pragma unroll
-            for (int u = 0; u < 4; ++u) z[u] = __builtin_fmaf(xiq, yscr[q * 16 + n0 + u], z[u]);
-          }
-#pragma unroll
-          for (int u = 0; u < 4; ++u) xoff[off_block(i, j) * 256 + m * 16 + n0 + u] = -z[u];
+        for (int r = 0; r < 16; ++r) {
+          __bf16 lo;
+          const __bf16 hi = split_hi(x[r], lo);
+          m_hi[(16 * j + r) * L::RS_C + 16 * j + cc] = __builtin_bit_cast(bf16_t, hi);
+          m_lo[(16 * j + r) * L::RS_C + 16 * j + cc] = __builtin_bit_cast(bf16_t, lo);
         }
-        __syncthreads();
-      }
-    }
-    // 3c: T = X Diag(beta), split into hi/lo planes (T overwrites the scratch).
-    {
-      constexpr int PER = CH * CH / NT;  // elements per thread, one row segment
-      const int row = tid / (CH / PER), col0 = (tid % (CH / PER)) * PER;
-      float tv[PER];
-#pragma unroll
-      for (int u = 0; u < PER; ++u) {
-        const int col = col0 + u, bi = row >> 4, bj = col >> 4;
-        float xv;
-        if (bi == bj)
-          xv = abuf[row * CH + col] + (row == col ? 1.f : 0.f);
-        else if (bi > bj)
-          xv = xoff[off_block(bi, bj) * 256 + (row & 15) * 16 + (col & 15)];
-        else
-          xv = 0.f;
-        tv[u] = xv * sbeta[col];
-      }
-      __syncthreads();
-#pragma unroll
-      for (int u = 0; u < PER; u += 2) {
-        uint32_t hi, lo;
-        split2(tv[u], tv[u + 1], hi, lo);
-        *reinterpret_cast<uint32_t*>(t_hi + row * L::RS_C + col0 + u) = hi;
-        *reinterpret_cast<uint32_t*>(t_lo + row * L::RS_C + col0 + u) = lo;
       }
     }
     __syncthreads();
 
-    // ---- Phase 4: value side for this wave's 32 columns ------------------
+    // ---- Phase 4: value side for this wave's 16 columns ------------------
     // 4b: X = [Kt; Qt] S, rows 0..CH-1 = Kt S, rows CH..2CH-1 = Qt S.
-    f32x4_t xs[2 * NB][2];
+    f32x4_t xs[2 * NB];
 #pragma unroll
-    for (int mt = 0; mt < 2 * NB; ++mt)
-#pragma unroll
-      for (int nt = 0; nt < 2; ++nt) xs[mt][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int mt = 0; mt < 2 * NB; ++mt) xs[mt] = zero4;
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
-      const Op s0 = op_from_tiles(st[2 * kb][0], st[2 * kb + 1][0]);
-      const Op s1 = op_from_tiles(st[2 * kb][1], st[2 * kb + 1][1]);
-      const int c0 = 32 * kb + 4 * g;
+      const Op sop = op_from_tiles(st[2 * kb], st[2 * kb + 1]);
+      const int k0_ = 32 * kb + 4 * g;
 #pragma unroll
-      for (int mt = 0; mt < 2 * NB; ++mt) {
-        const Op ak = plane_op2(kq_hi, kq_lo, 16 * mt + l16, L::RS_K, c0);
-        xs[mt][0] = mfma3(ak, s0, xs[mt][0]);
-        xs[mt][1] = mfma3(ak, s1, xs[mt][1]);
-      }
+      for (int mt = 0; mt < 2 * NB; ++mt) xs[mt] = mfma3(plane_op2(kq_hi, kq_lo, 16 * mt + l16, L::RS_K, k0_), sop, xs[mt]);
     }
-    // 4c: R = V - Kt S (padding tokens give 0 - 0).
+    // 4c/4d: R = V - Kt S, then E = (I + A)^-1 Diag(beta) R by 16-token blocks:
+    //   E_i = X_ii (beta_i R_i - sum_{j<i} A_ij E_j).
+    // E is kept only as MFMA B operands eop[kb] (32-token k blocks); while
+    // block 2 kb + 1 is pending, eop[kb] holds E_{2kb} and zeros.  The sum
+    // runs over whole k blocks of M: the zero half adds nothing.
+    Op eop[NB / 2];
 #pragma unroll
-    for (int mt = 0; mt < NB; ++mt)
+    for (int i = 0; i < NB; ++i) {
+      f32x4_t z;
 #pragma unroll
-      for (int nt = 0; nt < 2; ++nt)
+      for (int r = 0; r < 4; ++r) z[r] = sbeta[16 * i + 4 * g + r] * (vv[i][r] - xs[i][r]);
+      if (i > 0) {
+        f32x4_t cs = zero4;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) xs[mt][nt][r] = vv[mt][nt][r] - xs[mt][nt][r];
-    // 4d: E = T R (T lower triangular: token tile mt needs k blocks <= mt / 2).
-    Op rop[NB / 2][2];
-#pragma unroll
-    for (int kb = 0; kb < NB / 2; ++kb)
-#pragma unroll
-      for (int nt = 0; nt < 2; ++nt) rop[kb][nt] = op_from_tiles(xs[2 * kb][nt], xs[2 * kb + 1][nt]);
-    f32x4_t et[NB][2];
-#pragma unroll
-    for (int mt = 0; mt < NB; ++mt) {
-      et[mt][0] = et[mt][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int kb = 0; kb <= mt / 2; ++kb) {
-        const Op at_ = plane_op2(t_hi, t_lo, 16 * mt + l16, L::RS_C, 32 * kb + 4 * g);
-        et[mt][0] = mfma3(at_, rop[kb][0], et[mt][0]);
-        et[mt][1] = mfma3(at_, rop[kb][1], et[mt][1]);
+        for (int kb = 0; kb <= (i - 1) / 2; ++kb)
+          cs = mfma3(plane_op2(m_hi, m_lo, 16 * i + l16, L::RS_C, 32 * kb + 4 * g), eop[kb], cs);
+        z -= cs;
       }
+      const Op ax = plane_op2(m_hi, m_lo, 16 * i + l16, L::RS_C, 32 * (i / 2) + 4 * g);
+      const f32x4_t e = mfma3(ax, (i & 1) ? op_from_tiles(zero4, z) : op_from_tiles(z, zero4), zero4);
+      xs[i] = e;  // R_i is dead: keep E_i until its k block is complete
+      eop[i / 2] = (i & 1) ? op_from_tiles(xs[i - 1], e) : op_from_tiles(e, zero4);
     }
-    Op eop[NB / 2][2];
-#pragma unroll
-    for (int kb = 0; kb < NB / 2; ++kb)
-#pragma unroll
-      for (int nt = 0; nt < 2; ++nt) eop[kb][nt] = op_from_tiles(et[2 * kb][nt], et[2 * kb + 1][nt]);
     // 4e: O = scale (Qt S + P E), stored for the valid tokens.
 #pragma unroll
     for (int mt = 0; mt < NB; ++mt) {
 #pragma unroll
-      for (int kb = 0; kb <= mt / 2; ++kb) {
-        const Op ap = plane_op2(p_hi, p_lo, 16 * mt + l16, L::RS_C, 32 * kb + 4 * g);
-        xs[NB + mt][0] = mfma3(ap, eop[kb][0], xs[NB + mt][0]);
-        xs[NB + mt][1] = mfma3(ap, eop[kb][1], xs[NB + mt][1]);
+      for (int kb = 0; kb <= mt / 2; ++kb)
+        xs[NB + mt] = mfma3(plane_op2(p_hi, p_lo, 16 * mt + l16, L::RS_C, 32 * kb + 4 * g), eop[kb], xs[NB + mt]);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int tr = 16 * mt + 4 * g + r;
+        if (tr < n) st_f32(rs_o, a.scale * xs[NB + mt][r], (tr * rowv + col) * 4, 0);
       }
-#pragma unroll
-      for (int nt = 0; nt < 2; ++nt)
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-          if (16 * mt + 4 * g + r < n) st_f32(rs_o, a.scale * xs[NB + mt][nt][r], io_voff * 4, KDA_IO_SOFF(mt, nt, r) * 4);
     }
     // 4f: S = Diag(2^g_n) S + Kb^T E.
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float gm = sgn[16 * mt + 4 * g + r];
-        st[mt][0][r] *= gm;
-        st[mt][1][r] *= gm;
-      }
+      for (int r = 0; r < 4; ++r) st[mt][r] *= sgn[16 * mt + 4 * g + r];
 #pragma unroll
-      for (int kb = 0; kb < NB / 2; ++kb) {
-        const Op ak = plane_op2(kb_hi, kb_lo, 16 * mt + l16, L::RS_C, 32 * kb + 4 * g);
-        st[mt][0] = mfma3(ak, eop[kb][0], st[mt][0]);
-        st[mt][1] = mfma3(ak, eop[kb][1], st[mt][1]);
-      }
+      for (int kb = 0; kb < NB / 2; ++kb)
+        st[mt] = mfma3(plane_op2(kb_hi, kb_lo, 16 * mt + l16, L::RS_C, 32 * kb + 4 * g), eop[kb], st[mt]);
     }
     // Checkpoint at the end of this chunk when one is due.
     const int t_end = t_base + n;
@@ -619,9 +546,7 @@ __global__ void __launch_bounds__(DV * 2) prefill_chunked_kernel(PrefillArgs<TIn
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-          for (int nt = 0; nt < 2; ++nt)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) st_f32(rs_slot, st[mt][nt][r], tile_voff, KDA_TILE_SOFF(mt, nt, r));
+          for (int r = 0; r < 4; ++r) st_f32(rs_slot, st[mt][r], tile_voff, (16 * mt + r) * DV * 4);
         if (owner) a.slot_pos[slot] = pos0 + t_end;
       } else if (tid == 0) {
         atomicOr(a.dev_err, KDA_DEV_ERR_CKPT_SLOT);
@@ -633,11 +558,7 @@ __global__ void __launch_bounds__(DV * 2) prefill_chunked_kernel(PrefillArgs<TIn
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) st_f32(rs_state, st[mt][nt][r], tile_voff, KDA_TILE_SOFF(mt, nt, r));
-#undef KDA_TILE_SOFF
-#undef KDA_IO_SOFF
+    for (int r = 0; r < 4; ++r) st_f32(rs_state, st[mt][r], tile_voff, (16 * mt + r) * DV * 4);
   if (owner) a.pos[b] = pos0 + a.L;
 }
 
@@ -649,9 +570,9 @@ hipError_t launch_cfg(const kda_shape& s, int32_t L, int32_t chunk, float* state
                      ckpt_slots, slot_states, slot_pos, dev_err, s.H, L, ckpt_every, n_slots, s.scale};
   const dim3 grid((unsigned)((size_t)s.B * s.H));
   if (chunk == 64)
-    prefill_chunked_kernel<DK, DV, 64, TIn><<<grid, 2 * DV, 0, st>>>(a);
+    prefill_chunked_kernel<DK, DV, 64, TIn><<<grid, 4 * DV, 0, st>>>(a);
   else
-    prefill_chunked_kernel<DK, DV, 32, TIn><<<grid, 2 * DV, 0, st>>>(a);
+    prefill_chunked_kernel<DK, DV, 32, TIn><<<grid, 4 * DV, 0, st>>>(a);
   return hipGetLastError();
 }
 
