@@ -205,6 +205,32 @@ def bench_verify_commit(torch, kda, synth, B, T, rounds, layers, device):
     }
 
 
+def bench_verify_only(torch, kda, synth, B, T, layers, reps, device):
+    """Verify alone: T drafts through `layers` independent states per round,
+    replayed back to back from one captured graph (each layer has its own log;
+    nothing is committed, so the states are only read)."""
+    spec = synth.CONFIGS["spec_verify"]
+    inp = synth.token_inputs(spec, B, T)
+    d = {k: dev_tensor(torch, v, device) for k, v in inp.items()}
+    S0 = dev_tensor(torch, synth.initial_state(spec, B), device)
+    states = [S0.clone() for _ in range(layers)]
+    logs = [kda.InputLog(S0, T_max=T) for _ in range(layers)]
+    o = torch.empty((B, T, H, DV), dtype=torch.float32, device=device)
+    g = capture(torch, [kda.VerifyPlan(S, d["q"], d["k"], d["v"], d["alpha"], d["beta"], o, lg)
+                        for S, lg in zip(states, logs)])
+    for _ in range(3):
+        g.replay()
+    with Timer(torch) as tm:
+        for _ in range(reps):
+            g.replay()
+    launches = reps * layers
+    us = tm.ms * 1e3 / launches
+    ver_bytes = B * H * (STATE_BYTES + T * (TOKEN_IN_BYTES + 128 * 4 + LOG_BYTES))
+    return {"B": B, "T": T, "layers": layers, "launch_us": us,
+            "verified_token_heads_per_s": B * H * T / (us * 1e-6),
+            "hbm_frac": ver_bytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS}
+
+
 def bench_prefill(torch, kda, synth, device, variant, reps=2):
     spec = synth.CONFIGS["prefill"]
     B, L = spec.B[0], spec.steps
@@ -354,6 +380,9 @@ def main():
         log("verify/commit")
         rows["verify_commit_b16"] = bench_verify_commit(torch, kda, synth, 16, 4, 32, 32, device)
         rows["verify_commit_b64"] = bench_verify_commit(torch, kda, synth, 64, 4, 32, 8, device)
+        log("verify alone")
+        rows["verify_only_b16"] = bench_verify_only(torch, kda, synth, 16, 4, 32, 20, device)
+        rows["verify_only_b64"] = bench_verify_only(torch, kda, synth, 64, 4, 8, 50, device)
         log("snapshot/restore")
         rows["snapshot_restore"] = bench_snapshot_restore(torch, kda, synth, device)
         log("prefill")

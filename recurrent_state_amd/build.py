@@ -15,10 +15,10 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libkda.so")
 
-SOURCES = ["kda_api.cpp", "kda_state.hip", "kda_slots.hip", "kda_prefill.hip"]
+SOURCES = ["kda_api.cpp", "kda_state.hip", "kda_verify.hip", "kda_slots.hip", "kda_prefill.hip"]
 
 # -ffp-contract=off: every fused multiply-add in the kernels is written out,
-#   so decode, verify and commit round identically.
+#   so decode and commit round identically.
 # -packed-fp32-ops off: no packed fp32 VALU instructions are generated.
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",

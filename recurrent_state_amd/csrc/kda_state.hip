@@ -1,12 +1,12 @@
-// State-resident KDA kernels for gfx950: decode step, speculative verify,
-// commit (replay of the accepted prefix) and the token-by-token prefill.
+// State-resident KDA kernels for gfx950: decode step, commit (replay of the
+// accepted prefix of a verify) and the token-by-token prefill.
 //
 // Every kernel runs one 64-lane wave per 32-column slice of one
 // (sequence, head) state and keeps that slice in registers for as long as it
-// needs it (one token for decode, T tokens for verify, the accepted count for
-// commit, the whole prompt for the recurrent prefill).  All of them call
-// kda::token_update with the same lane mapping, which is what makes commit
-// bit-identical to repeated decode steps.
+// needs it (one token for decode, the accepted count for commit, the whole
+// prompt for the recurrent prefill).  All of them call kda::token_update with
+// the same lane mapping, which is what makes commit bit-identical to repeated
+// decode steps.
 //
 // The decode step streams the fp32 state (read + write, 98.6% of its bytes at
 // dk = dv = 128 with bf16 inputs), so it is bound by HBM bandwidth; the loads
@@ -33,24 +33,6 @@ struct StepArgs {
   const float* beta;
   float* o;
   int32_t H;
-  float scale;
-};
-
-template <typename TIn>
-struct VerifyArgs {
-  const float* state;
-  const TIn* q;
-  const TIn* k;
-  const TIn* v;
-  const float* alpha;
-  const float* beta;
-  float* o;
-  TIn* log_k;
-  TIn* log_v;
-  float* log_alpha;
-  float* log_beta;
-  int32_t H;
-  int32_t T;
   float scale;
 };
 
@@ -192,42 +174,6 @@ __global__ void KDA_OCCUPANCY __launch_bounds__(kWave * waves_per_group<DV>()) d
 }
 
 template <int DK, int DV, typename TIn>
-__global__ void KDA_OCCUPANCY __launch_bounds__(kWave * waves_per_group<DV>()) verify_kernel(VerifyArgs<TIn> a) {
-  typedef Place<DK, DV> P;
-  constexpr int R = P::R;
-  const P p(a.H);
-  float S[R][4];
-  load_tile<R, DV>(a.state + (size_t)p.bh * DK * DV + p.tile_off(), S);
-  TokenIn<TIn, R, true> cur, nxt;
-  size_t tok = (size_t)p.b * a.T * a.H + p.h;  // [B][T][H] index of token 0
-  cur.load(a.k + tok * DK + p.row0, a.q + tok * DK + p.row0, a.alpha + tok * DK + p.row0,
-           a.v + tok * DV + p.col0, a.beta + tok);
-  for (int t = 0; t < a.T; ++t) {
-    const size_t tn = tok + a.H;
-    if (KDA_PREFETCH_NEXT && t + 1 < a.T)
-      nxt.load(a.k + tn * DK + p.row0, a.q + tn * DK + p.row0, a.alpha + tn * DK + p.row0,
-               a.v + tn * DV + p.col0, a.beta + tn);
-    float o[4];
-    cur.update(S, a.scale, o);
-    if (p.rg == 0) {
-      *reinterpret_cast<float4*>(a.o + tok * DV + p.col0) = make_float4(o[0], o[1], o[2], o[3]);
-      store4(a.log_v + tok * DV + p.col0, cur.v);
-    }
-    if (p.slice == 0 && p.cg == 0) {
-      store_raw(a.log_k + tok * DK + p.row0, cur.k);
-      store_raw(a.log_alpha + tok * DK + p.row0, cur.a);
-      if (p.rg == 0) a.log_beta[tok] = cur.beta;
-    }
-    if (KDA_PREFETCH_NEXT)
-      cur = nxt;
-    else if (t + 1 < a.T)
-      cur.load(a.k + tn * DK + p.row0, a.q + tn * DK + p.row0, a.alpha + tn * DK + p.row0,
-               a.v + tn * DV + p.col0, a.beta + tn);
-    tok = tn;
-  }
-}
-
-template <int DK, int DV, typename TIn>
 __global__ void KDA_OCCUPANCY __launch_bounds__(kWave * waves_per_group<DV>()) commit_kernel(CommitArgs<TIn> a) {
   typedef Place<DK, DV> P;
   constexpr int R = P::R;
@@ -340,19 +286,6 @@ hipError_t launch_decode(const kda_shape& s, float* state, int64_t* pos, TokenIn
     StepArgs<TIn> a{state, pos, (const TIn*)in.q, (const TIn*)in.k, (const TIn*)in.v, in.alpha, in.beta, o,
                     s.H, s.scale};
     decode_kernel<DK, DV, TIn><<<grid_of<DK, DV>(s), kWave * waves_per_group<DV>(), 0, st>>>(a);
-  });
-  return hipGetLastError();
-}
-
-hipError_t launch_verify(const kda_shape& s, int32_t T, const float* state, TokenInputs in, float* o,
-                         LogPtrs log, hipStream_t st) {
-  dispatch(s, [&](auto c) {
-    typedef decltype(c) C;
-    typedef typename C::TIn TIn;
-    constexpr int DK = C::DK, DV = C::DV;
-    VerifyArgs<TIn> a{state, (const TIn*)in.q, (const TIn*)in.k, (const TIn*)in.v, in.alpha, in.beta, o,
-                      (TIn*)log.k, (TIn*)log.v, log.alpha, log.beta, s.H, T, s.scale};
-    verify_kernel<DK, DV, TIn><<<grid_of<DK, DV>(s), kWave * waves_per_group<DV>(), 0, st>>>(a);
   });
   return hipGetLastError();
 }

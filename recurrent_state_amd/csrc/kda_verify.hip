@@ -1,0 +1,493 @@
+// Speculative verify for gfx950: T draft tokens from a committed state that
+// is read once and never written, in the chunk (WY) form of the same gated
+// delta rule, on the vector units.
+//
+// Unrolling the recurrence over a group of G tokens from the group's start
+// state S0 (gamma_t = prod_{r<=t} alpha_r per key channel, products over the
+// group only):
+//   u_t = S0^T (gamma_t k_t) + sum_{s<t} A_ts e_s,   e_t = beta_t (v_t - u_t)
+//   o_t = scale (S0^T (gamma_t q_t) + sum_{s<=t} P_ts e_s)
+//   A_ts = sum_i k_s,i k_t,i prod_{s<r<=t} alpha_r,i      (s < t)
+//   P_ts = sum_i k_s,i q_t,i prod_{s<r<=t} alpha_r,i      (s <= t)
+// and the state after the group is
+//   S_G = Diag(gamma_{G-1}) S0 + sum_s Diag(prod_{s<r<G} alpha_r) k_s e_s^T.
+// (Chunked form of the per-channel-gated delta rule, written out in the
+// appendix on the chunked WY/UT form; the per-token rule is the one the
+// "Hyper-optimizing Kimi K3 in vLLM" pages call KDA.)
+//
+// Only 2 G multiply-adds per state element are needed for a group (the two
+// projections S0^T (gamma k) and S0^T (gamma q)), against 4 G for the token
+// loop (decay, k projection, q projection, rank-1 update).  Without packed
+// fp32 a wave64 FMA costs four cycles, so at T = 4 the token loop's vector
+// work is as long as the state's HBM read; this form halves it.  The decay
+// products are formed as products of alphas (no division by a cumulative
+// product), so gates of 0 are exact.
+//
+// One workgroup per (sequence, head), dv / 32 waves; wave w owns value
+// columns [32 w, 32 w + 32) with the state lane mapping of the other state
+// kernels (lane = 8 rg + cg: rows [R rg, R rg + R), columns 4 cg .. 4 cg + 3).
+// Per group of up to four tokens:
+//   1. preparation (all waves): gamma_t k_t, gamma_t q_t, the update
+//      coefficients and the A / P entries into LDS; wave w takes the tokens
+//      t = w (mod waves) and lane l key channels [CPL l, CPL l + CPL);
+//   2. projections: each lane multiplies its R x 4 state tile into 2 G
+//      accumulators per column, then sums over the 8 row groups in-wave
+//      (DPP row rotate, v_permlane16_swap, v_permlane32_swap);
+//   3. per column: forward substitution for e_t, then o_t;
+//   4. when tokens remain: S <- S_G in registers.
+// The verify outputs therefore differ from decode-step outputs by rounding
+// only; the committed state is always advanced by the commit kernel's token
+// loop, which is the decode step's arithmetic.
+
+#include <hip/hip_runtime.h>
+
+#include "kda_common.h"
+#include "kda_internal.h"
+
+namespace kda {
+namespace {
+
+constexpr int kGroup = 4;  // tokens per group
+
+template <typename TIn>
+struct VerifyArgs {
+  const float* state;
+  const TIn* q;
+  const TIn* k;
+  const TIn* v;
+  const float* alpha;
+  const float* beta;
+  float* o;
+  TIn* log_k;
+  TIn* log_v;
+  float* log_alpha;
+  float* log_beta;
+  int32_t H;
+  int32_t T;
+  float scale;
+};
+
+// Per-group LDS.  Key-channel vectors are stored by row group with a padded
+// stride (RP = R + 4 floats): the eight distinct row groups a wave reads in
+// one 16-byte load then fall on disjoint banks.
+template <int DK>
+struct VerifyLds {
+  static constexpr int R = DK / kRowGroups;
+  static constexpr int RP = R + 4;
+  static constexpr int VEC = kRowGroups * RP;
+  float kap[kGroup][VEC];  // gamma_t k_t
+  float rho[kGroup][VEC];  // gamma_t q_t
+  float cof[kGroup][VEC];  // k_s prod_{s<r<G} alpha_r
+  float gend[VEC];         // prod_{r<G} alpha_r
+  float A[kGroup][kGroup];
+  float P[kGroup][kGroup];
+  static __device__ __forceinline__ int at(int ch) { return (ch / R) * RP + ch % R; }
+};
+
+// Sum over all 64 lanes: rotations by 8, 4, 2, 1 inside each 16-lane row,
+// then the two permlane swaps across rows.
+__device__ __forceinline__ float wave_sum(float x) {
+  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x128, 0xf, 0xf, false));
+  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x124, 0xf, 0xf, false));
+  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x122, 0xf, 0xf, false));
+  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x121, 0xf, 0xf, false));
+  return pair_sum32(pair_sum16(x));
+}
+
+// Buffer-resource access: one SGPR base + range per tensor window, a 32-bit
+// lane offset in a VGPR and uniform offsets in SGPRs, so no 64-bit address
+// is kept per load.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+constexpr int kRsrcWord3 = 0x00020000;  // raw 32-bit data format
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kRsrcWord3);
+}
+
+// N consecutive key channels as stored (N = 1 or 2).
+template <typename TIn, int N>
+struct Chan;
+template <>
+struct Chan<bf16_t, 1> {
+  uint32_t w;
+  __device__ __forceinline__ float operator[](int) const { return bf16_lo(w); }
+  __device__ __forceinline__ void load(rsrc_t r, int vo, int so) {
+    w = __builtin_amdgcn_raw_buffer_load_b16(r, vo, so, 0);
+  }
+  __device__ __forceinline__ void store(rsrc_t r, int vo, int so) const {
+    __builtin_amdgcn_raw_buffer_store_b16((unsigned short)w, r, vo, so, 0);
+  }
+};
+template <>
+struct Chan<bf16_t, 2> {
+  uint32_t w;
+  __device__ __forceinline__ float operator[](int i) const { return i ? bf16_hi(w) : bf16_lo(w); }
+  __device__ __forceinline__ void load(rsrc_t r, int vo, int so) { w = __builtin_amdgcn_raw_buffer_load_b32(r, vo, so, 0); }
+  __device__ __forceinline__ void store(rsrc_t r, int vo, int so) const {
+    __builtin_amdgcn_raw_buffer_store_b32(w, r, vo, so, 0);
+  }
+};
+template <>
+struct Chan<float, 1> {
+  uint32_t w;
+  __device__ __forceinline__ float operator[](int) const { return __uint_as_float(w); }
+  __device__ __forceinline__ void load(rsrc_t r, int vo, int so) { w = __builtin_amdgcn_raw_buffer_load_b32(r, vo, so, 0); }
+  __device__ __forceinline__ void store(rsrc_t r, int vo, int so) const {
+    __builtin_amdgcn_raw_buffer_store_b32(w, r, vo, so, 0);
+  }
+};
+template <>
+struct Chan<float, 2> {
+  u32x2 w;
+  __device__ __forceinline__ float operator[](int i) const { return __uint_as_float(i ? w.y : w.x); }
+  __device__ __forceinline__ void load(rsrc_t r, int vo, int so) { w = __builtin_amdgcn_raw_buffer_load_b64(r, vo, so, 0); }
+  __device__ __forceinline__ void store(rsrc_t r, int vo, int so) const {
+    __builtin_amdgcn_raw_buffer_store_b64(w, r, vo, so, 0);
+  }
+};
+
+// Four consecutive value columns as stored.
+template <typename TIn>
+struct Val4;
+template <>
+struct Val4<bf16_t> {
+  u32x2 w;
+  __device__ __forceinline__ void load(rsrc_t r, int vo, int so) { w = __builtin_amdgcn_raw_buffer_load_b64(r, vo, so, 0); }
+  __device__ __forceinline__ void store(rsrc_t r, int vo, int so) const {
+    __builtin_amdgcn_raw_buffer_store_b64(w, r, vo, so, 0);
+  }
+  __device__ __forceinline__ void widen(float (&x)[4]) const {
+    x[0] = bf16_lo(w.x);
+    x[1] = bf16_hi(w.x);
+    x[2] = bf16_lo(w.y);
+    x[3] = bf16_hi(w.y);
+  }
+};
+template <>
+struct Val4<float> {
+  u32x4 w;
+  __device__ __forceinline__ void load(rsrc_t r, int vo, int so) { w = __builtin_amdgcn_raw_buffer_load_b128(r, vo, so, 0); }
+  __device__ __forceinline__ void store(rsrc_t r, int vo, int so) const {
+    __builtin_amdgcn_raw_buffer_store_b128(w, r, vo, so, 0);
+  }
+  __device__ __forceinline__ void widen(float (&x)[4]) const {
+    x[0] = __uint_as_float(w.x);
+    x[1] = __uint_as_float(w.y);
+    x[2] = __uint_as_float(w.z);
+    x[3] = __uint_as_float(w.w);
+  }
+};
+
+// Windows over one (sequence, head)'s T tokens: consecutive tokens are H
+// rows apart in every [B][T][H][d] tensor.
+template <typename TIn, int DK, int DV>
+struct Streams {
+  rsrc_t k, q, alpha, v, o, log_k, log_v, log_alpha;
+  int sk_in, sk_f32, sv_in, sv_f32;  // bytes between consecutive tokens
+  __device__ __forceinline__ Streams(const VerifyArgs<TIn>& a, size_t tok0, int T) {
+    const size_t span = (size_t)(T - 1) * a.H;  // rows from the first to the last token
+    const size_t es = sizeof(TIn);
+    k = make_rsrc(a.k + tok0 * DK, (uint32_t)((span * DK + DK) * es));
+    q = make_rsrc(a.q + tok0 * DK, (uint32_t)((span * DK + DK) * es));
+    alpha = make_rsrc(a.alpha + tok0 * DK, (uint32_t)((span * DK + DK) * 4));
+    v = make_rsrc(a.v + tok0 * DV, (uint32_t)((span * DV + DV) * es));
+    o = make_rsrc(a.o + tok0 * DV, (uint32_t)((span * DV + DV) * 4));
+    log_k = make_rsrc(a.log_k + tok0 * DK, (uint32_t)((span * DK + DK) * es));
+    log_v = make_rsrc(a.log_v + tok0 * DV, (uint32_t)((span * DV + DV) * es));
+    log_alpha = make_rsrc(a.log_alpha + tok0 * DK, (uint32_t)((span * DK + DK) * 4));
+    sk_in = a.H * DK * (int)es;
+    sk_f32 = a.H * DK * 4;
+    sv_in = a.H * DV * (int)es;
+    sv_f32 = a.H * DV * 4;
+  }
+};
+
+// One group of G <= kGroup tokens starting at token t0, from the state tile S
+// (rows [R rg, R rg + R) of this lane, columns col0 .. col0 + 3).  MULTI:
+// advance S to the state after the group.
+template <int DK, int DV, typename TIn, bool MULTI, typename LoadState>
+__device__ __forceinline__ void verify_group(const VerifyArgs<TIn>& a, const Streams<TIn, DK, DV>& st,
+                                             VerifyLds<DK>& L, float (&S)[DK / kRowGroups][4], int t0, int G,
+                                             size_t tok0, int lane, int wave, bool first,
+                                             const LoadState& load_state) {
+  constexpr int NW = DV / kSliceCols;
+  constexpr int R = DK / kRowGroups;
+  constexpr int CPL = DK / kWave;  // key channels per lane in the preparation
+  constexpr int RP = VerifyLds<DK>::RP;
+  const int rg = lane >> 3, cg = lane & 7;
+  const int col0 = wave * kSliceCols + cg * 4;
+  const int ch0 = lane * CPL;
+  const int kvo_in = ch0 * (int)sizeof(TIn), kvo_f32 = ch0 * 4;
+  const int vvo_in = col0 * (int)sizeof(TIn), vvo_f32 = col0 * 4;
+
+  // ---- 1. preparation ---------------------------------------------------
+  // Every input load of the group is issued before any use; padding tokens
+  // (r >= G) re-read the group's last token and are never used.
+  Chan<float, CPL> al[kGroup];
+  Chan<TIn, CPL> kk[kGroup];
+  Val4<TIn> vv[kGroup];
+  Chan<TIn, CPL> qq[kGroup / NW];  // q of this wave's tokens wave, wave + NW, ...
+  float bt[kGroup];
+#pragma unroll
+  for (int r = 0; r < kGroup; ++r) {
+    const int tr = t0 + min(r, G - 1);
+    al[r].load(st.alpha, kvo_f32, tr * st.sk_f32);
+    kk[r].load(st.k, kvo_in, tr * st.sk_in);
+    vv[r].load(st.v, vvo_in, tr * st.sv_in);
+    bt[r] = a.beta[tok0 + (size_t)tr * a.H];
+  }
+#pragma unroll
+  for (int j = 0; j < kGroup / NW; ++j) qq[j].load(st.q, kvo_in, (t0 + min(wave + j * NW, G - 1)) * st.sk_in);
+  // The state tile goes last: loads retire in order, so the preparation
+  // below waits only for the small input loads while the tile streams in,
+  // and the projections consume its rows as they land.
+  if (first) {
+    __builtin_amdgcn_sched_barrier(0);  // keep the issue order: inputs, then the tile
+    load_state(S);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  if (MULTI && !first) __syncthreads();  // the previous group's LDS reads are done
+#pragma unroll
+  for (int j = 0; j < kGroup / NW; ++j) {
+    const int t = wave + j * NW;
+    if (t >= G) break;
+    const int tt = t0 + t;
+    const Chan<TIn, CPL> qt = qq[j];
+    // Pick k_t and alpha_t out of the unrolled arrays without dynamic indexing.
+    Chan<TIn, CPL> kt = kk[0];
+    Chan<float, CPL> at = al[0];
+#pragma unroll
+    for (int r = 1; r < kGroup; ++r)
+      if (r == t) {
+        kt = kk[r];
+        at = al[r];
+      }
+    kt.store(st.log_k, kvo_in, tt * st.sk_in);
+    at.store(st.log_alpha, kvo_f32, tt * st.sk_f32);
+    float pA[kGroup], pP[kGroup];
+#pragma unroll
+    for (int s = 0; s < kGroup; ++s) pA[s] = pP[s] = 0.f;
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) {
+      const float kv = kt[c], qv = qt[c];
+      float gam = al[0][c];
+#pragma unroll
+      for (int r = 1; r < kGroup; ++r)
+        if (r <= t) gam *= al[r][c];
+      const int ix = VerifyLds<DK>::at(ch0 + c);
+      L.kap[t][ix] = kv * gam;
+      L.rho[t][ix] = qv * gam;
+      if (MULTI) {
+        float cof = kv;
+#pragma unroll
+        for (int r = 1; r < kGroup; ++r)
+          if (r > t && r < G) cof *= al[r][c];
+        L.cof[t][ix] = cof;
+      }
+      // Backward over s = t .. 0 with bb = prod_{s<r<=t} alpha_r.
+      float bb = 1.f;
+#pragma unroll
+      for (int s = kGroup - 1; s >= 0; --s) {
+        if (s <= t) {
+          const float ks = kk[s][c];
+          pP[s] = __builtin_fmaf(qv * ks, bb, pP[s]);
+          if (s < t) pA[s] = __builtin_fmaf(kv * ks, bb, pA[s]);
+          bb *= al[s][c];
+        }
+      }
+    }
+#pragma unroll
+    for (int s = 0; s < kGroup; ++s) {
+      if (s <= t) {
+        const float ps = wave_sum(pP[s]);
+        const float as = s < t ? wave_sum(pA[s]) : 0.f;
+        if (lane == 0) {
+          L.P[t][s] = ps;
+          L.A[t][s] = as;
+        }
+      }
+    }
+  }
+  if (MULTI && wave == 0) {
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) {
+      float gam = al[0][c];
+#pragma unroll
+      for (int r = 1; r < kGroup; ++r)
+        if (r < G) gam *= al[r][c];
+      L.gend[VerifyLds<DK>::at(ch0 + c)] = gam;
+    }
+  }
+  // Log of v (this wave's columns; row group r writes token r) and beta.
+#pragma unroll
+  for (int r = 0; r < kGroup; ++r)
+    if (r < G && rg == r) vv[r].store(st.log_v, vvo_in, (t0 + r) * st.sv_in);
+  if (wave == 0 && lane < G) {
+    float bl = bt[0];
+#pragma unroll
+    for (int r = 1; r < kGroup; ++r)
+      if (lane == r) bl = bt[r];
+    a.log_beta[tok0 + (size_t)(t0 + lane) * a.H] = bl;
+  }
+  __syncthreads();
+
+  // ---- 2. projections x_t = S0^T kap_t, y_t = S0^T rho_t -----------------
+  // Row blocks outermost: each block of four state rows is used by every
+  // token of the group and is then dead (single-group case).
+  float x[kGroup][4], y[kGroup][4];
+#pragma unroll
+  for (int t = 0; t < kGroup; ++t)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) x[t][c] = y[t][c] = 0.f;
+#pragma unroll
+  for (int r4 = 0; r4 < R / 4; ++r4) {
+#pragma unroll
+    for (int t = 0; t < kGroup; ++t) {
+      if (t < G) {
+        const float4 kp = *reinterpret_cast<const float4*>(&L.kap[t][rg * RP + 4 * r4]);
+        const float4 rp = *reinterpret_cast<const float4*>(&L.rho[t][rg * RP + 4 * r4]);
+        const float kq[4] = {kp.x, kp.y, kp.z, kp.w}, rq[4] = {rp.x, rp.y, rp.z, rp.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            x[t][c] = __builtin_fmaf(kq[i], S[4 * r4 + i][c], x[t][c]);
+            y[t][c] = __builtin_fmaf(rq[i], S[4 * r4 + i][c], y[t][c]);
+          }
+      }
+    }
+  }
+#pragma unroll
+  for (int t = 0; t < kGroup; ++t) {
+    if (t < G) {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        x[t][c] = rowgroup_sum(x[t][c]);
+        y[t][c] = rowgroup_sum(y[t][c]);
+      }
+    }
+  }
+
+  // ---- 3. forward substitution and outputs, per column ------------------
+  float e[kGroup][4];
+#pragma unroll
+  for (int t = 0; t < kGroup; ++t) {
+    if (t < G) {
+      float vc[4];
+      vv[t].widen(vc);
+      float o[4];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        float u = x[t][c];
+#pragma unroll
+        for (int s = 0; s < t; ++s) u = __builtin_fmaf(L.A[t][s], e[s][c], u);
+        e[t][c] = bt[t] * (vc[c] - u);
+        float w = y[t][c];
+#pragma unroll
+        for (int s = 0; s <= t; ++s) w = __builtin_fmaf(L.P[t][s], e[s][c], w);
+        o[c] = a.scale * w;
+      }
+      if (rg == t) {
+        const u32x4 ov = {__float_as_uint(o[0]), __float_as_uint(o[1]), __float_as_uint(o[2]), __float_as_uint(o[3])};
+        __builtin_amdgcn_raw_buffer_store_b128(ov, st.o, vvo_f32, (t0 + t) * st.sv_f32, 0);
+      }
+    }
+  }
+
+  // ---- 4. advance the in-register state --------------------------------
+  if (MULTI) {
+#pragma unroll
+    for (int r4 = 0; r4 < R / 4; ++r4) {
+      const float4 g4 = *reinterpret_cast<const float4*>(&L.gend[rg * RP + 4 * r4]);
+      const float gq[4] = {g4.x, g4.y, g4.z, g4.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) S[4 * r4 + i][c] *= gq[i];
+#pragma unroll
+      for (int s = 0; s < kGroup; ++s) {
+        if (s < G) {
+          const float4 c4 = *reinterpret_cast<const float4*>(&L.cof[s][rg * RP + 4 * r4]);
+          const float cq[4] = {c4.x, c4.y, c4.z, c4.w};
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int c = 0; c < 4; ++c) S[4 * r4 + i][c] = __builtin_fmaf(cq[i], e[s][c], S[4 * r4 + i][c]);
+        }
+      }
+    }
+  }
+}
+
+// MULTI: T may exceed one group (the state is advanced in registers between
+// groups); otherwise T <= kGroup and the state dies after the projections.
+template <int DK, int DV, typename TIn, bool MULTI>
+__global__ void __launch_bounds__(kWave * (DV / kSliceCols)) verify_chunk_kernel(VerifyArgs<TIn> a) {
+  constexpr int R = DK / kRowGroups;
+  __shared__ __align__(16) VerifyLds<DK> L;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int rg = lane >> 3, cg = lane & 7;
+  const int bh = blockIdx.x;
+  const int b = bh / a.H, h = bh - b * a.H;
+  const int T = a.T;
+  const size_t tok0 = (size_t)b * T * a.H + h;  // [B][T][H] row of token 0
+  const Streams<TIn, DK, DV> st(a, tok0, T);
+
+  // The lane's state tile, loaded once (inside the first group).
+  float S[R][4];
+  const rsrc_t rs = make_rsrc(a.state + (size_t)bh * DK * DV, DK * DV * 4);
+  const int svo = ((rg * R) * DV + wave * kSliceCols + cg * 4) * 4;
+  auto load_state = [&](float (&St)[R][4]) {
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const u32x4 w = __builtin_amdgcn_raw_buffer_load_b128(rs, svo, r * DV * 4, 0);
+      St[r][0] = __uint_as_float(w.x);
+      St[r][1] = __uint_as_float(w.y);
+      St[r][2] = __uint_as_float(w.z);
+      St[r][3] = __uint_as_float(w.w);
+    }
+  };
+  if (MULTI) {
+    for (int t0 = 0; t0 < T; t0 += kGroup)
+      verify_group<DK, DV, TIn, true>(a, st, L, S, t0, min(kGroup, T - t0), tok0, lane, wave, t0 == 0, load_state);
+  } else {
+    verify_group<DK, DV, TIn, false>(a, st, L, S, 0, T, tok0, lane, wave, true, load_state);
+  }
+}
+
+template <int DK, int DV, typename TIn>
+void launch_cfg(const kda_shape& s, int32_t T, const float* state, TokenInputs in, float* o, LogPtrs log,
+                hipStream_t st) {
+  VerifyArgs<TIn> a{state, (const TIn*)in.q, (const TIn*)in.k, (const TIn*)in.v, in.alpha, in.beta, o,
+                    (TIn*)log.k, (TIn*)log.v, log.alpha, log.beta, s.H, T, s.scale};
+  const dim3 grid(s.B * s.H), block(kWave * (DV / kSliceCols));
+  if (T <= kGroup)
+    verify_chunk_kernel<DK, DV, TIn, false><<<grid, block, 0, st>>>(a);
+  else
+    verify_chunk_kernel<DK, DV, TIn, true><<<grid, block, 0, st>>>(a);
+}
+
+template <typename TIn>
+void launch_dtype(const kda_shape& s, int32_t T, const float* state, TokenInputs in, float* o, LogPtrs log,
+                  hipStream_t st) {
+  if (s.dk == 128 && s.dv == 128) launch_cfg<128, 128, TIn>(s, T, state, in, o, log, st);
+  else if (s.dk == 128) launch_cfg<128, 64, TIn>(s, T, state, in, o, log, st);
+  else if (s.dv == 128) launch_cfg<64, 128, TIn>(s, T, state, in, o, log, st);
+  else launch_cfg<64, 64, TIn>(s, T, state, in, o, log, st);
+}
+
+}  // namespace
+
+hipError_t launch_verify(const kda_shape& s, int32_t T, const float* state, TokenInputs in, float* o, LogPtrs log,
+                         hipStream_t st) {
+  if (s.in_dtype == KDA_BF16)
+    launch_dtype<bf16_t>(s, T, state, in, o, log, st);
+  else
+    launch_dtype<float>(s, T, state, in, o, log, st);
+  return hipGetLastError();
+}
+
+}  // namespace kda

@@ -1,9 +1,11 @@
 """GPU parity and bookkeeping on small shapes (every dk/dv/dtype combination).
 
 Parity: the HIP path against the fp64 oracle at the tolerance bar.  Bit-exact
-bookkeeping: commit(a) equals a decode steps, verify outputs equal decode
-outputs, a = 0 leaves the state untouched, snapshot/restore round-trips, and
-positions add up; these compare GPU results with each other.  Every test also
+bookkeeping: commit(a) equals a decode steps, a = 0 leaves the state
+untouched, snapshot/restore round-trips, and positions add up; these compare
+GPU results with each other.  Verify computes its outputs in the chunk form of
+the rule (a different rounding order from the token loop), so its outputs are
+held to the tolerance bar, against the oracle and against decode steps.  Every test also
 checks that the kernel variant it meant to exercise is the one that ran.
 """
 
@@ -60,7 +62,7 @@ def test_decode_matches_oracle(dk, dv, dt):
 
 
 @pytest.mark.parametrize("dk,dv,dt", SHAPES)
-@pytest.mark.parametrize("T", [1, 3, 8])
+@pytest.mark.parametrize("T", [1, 3, 4, 5, 8, 16])
 def test_verify_commit_matches_oracle_and_decode(dk, dv, dt, T):
     spec = spec_for(dk, dv, dt, tag=101)
     B = 3
@@ -71,18 +73,18 @@ def test_verify_commit_matches_oracle_and_decode(dk, dv, dt, T):
     S = dev_tensor(S0)
     S_keep = S.clone()
     pos = torch.tensor([7, 0, 3], dtype=torch.int64, device="cuda")
-    log = kda.InputLog(S, T_max=8, in_dtype=d["q"].dtype)
+    log = kda.InputLog(S, T_max=16, in_dtype=d["q"].dtype)
     o = torch.empty((B, T, spec.H, dv), dtype=torch.float32, device="cuda")
     kda.verify(S, d["q"], d["k"], d["v"], d["alpha"], d["beta"], o, log)
     assert kda.last_variant() == "verify" and log.pending_T == T
     assert torch.equal(bits(S), bits(S_keep)), "verify must not write the committed state"
     _, o_ref = ko.decode(S0, inp, spec.scale)
     assert_parity(o.cpu().numpy(), o_ref, what=f"verify T={T}")
-    # Bit-exact: verify outputs equal decode outputs token by token.
+    # Verify outputs agree with decode steps from the same state to the bar.
     S_dec = S.clone()
     pos_dec = pos.clone()
     o_dec = decode_run(S_dec, pos_dec, d)
-    assert torch.equal(bits(o), bits(o_dec))
+    assert_parity(o.cpu().numpy(), o_dec.cpu().numpy().astype(np.float64), what=f"verify vs decode T={T}")
     # Commit a different count per sequence; compare with that many decode steps.
     acc = [T, 0, min(1, T)] if T > 1 else [1, 0, 1]
     accepted = torch.tensor(acc, dtype=torch.int32, device="cuda")
@@ -96,6 +98,42 @@ def test_verify_commit_matches_oracle_and_decode(dk, dv, dt, T):
         decode_run(Sb, pb, {k_: v_[b:b + 1, :a] for k_, v_ in d.items()})
         assert torch.equal(bits(S[b:b + 1]), bits(Sb)), f"commit({a}) != {a} decode steps (seq {b})"
     assert pos.cpu().tolist() == [7 + acc[0], 0 + acc[1], 3 + acc[2]]
+
+
+@pytest.mark.parametrize("T", [4, 7])
+def test_verify_extreme_gates(T):
+    # Gates of exactly 0 (a full reset of a key channel), exactly 1, and beta
+    # of 0 and 1: the verify's decay products never divide by a cumulative
+    # decay, so these stay finite and match the oracle; commit still equals
+    # the decode steps bit for bit.
+    spec = spec_for(128, 128, "bf16", tag=113)
+    B = 2
+    inp = synth.token_inputs(spec, B, T)
+    rng = np.random.default_rng(5)
+    a = inp["alpha"]
+    a[rng.random(a.shape) < 0.2] = 0.0
+    a[rng.random(a.shape) < 0.2] = 1.0
+    bt = inp["beta"]
+    bt[:, 0] = 1.0
+    bt[:, -1] = 0.0
+    S0 = synth.initial_state(spec, B)
+    d = dev_inputs(inp)
+    S = dev_tensor(S0)
+    S_keep = S.clone()
+    pos = torch.zeros(B, dtype=torch.int64, device="cuda")
+    log = kda.InputLog(S, T_max=T)
+    o = torch.empty((B, T, spec.H, 128), dtype=torch.float32, device="cuda")
+    kda.verify(S, d["q"], d["k"], d["v"], d["alpha"], d["beta"], o, log)
+    assert torch.isfinite(o).all()
+    _, o_ref = ko.decode(S0, inp, spec.scale)
+    assert_parity(o.cpu().numpy(), o_ref, what=f"verify extreme gates T={T}")
+    accepted = torch.tensor([T, T - 1], dtype=torch.int32, device="cuda")
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    kda.commit(S, pos, log, accepted, err)
+    for b, n in enumerate([T, T - 1]):
+        Sb = S_keep[b:b + 1].clone()
+        decode_run(Sb, torch.zeros(1, dtype=torch.int64, device="cuda"), {k_: v_[b:b + 1, :n] for k_, v_ in d.items()})
+        assert torch.equal(bits(S[b:b + 1]), bits(Sb))
 
 
 def test_commit_rejects_out_of_range_counts():
