@@ -35,8 +35,9 @@
 // kernel uses k-slot e of lane group g = l >> 4 for index
 //   pi(g, e) = 4 g + e (e < 4),  16 + 4 g + (e - 4) (e >= 4)
 // inside each 32-wide k block, which turns two stacked D tiles (rows 0..15
-// and 16..31 of the block) directly into a B operand, and makes the A
-// operand two 8-byte LDS reads per plane.
+// and 16..31 of the block) directly into a B operand.  The LDS planes store
+// every k block in that slot order (column c at kpos(c)), so an operand is
+// one aligned 16-byte LDS read per plane.
 
 #include <hip/hip_runtime.h>
 
@@ -95,13 +96,16 @@ __device__ __forceinline__ Op op_from_tiles(const f32x4_t& t0, const f32x4_t& t1
   return o;
 }
 
-// A (or B) operand read from a row-major bf16 plane: row `row`, k block
-// starting at column c0 = 32 kb + 4 g: columns c0..c0+3 and c0+16..c0+19.
+// Storage position of column c in a plane row: inside each 32-wide k block,
+// slot e of lane group g (logical column pi(g, e)) sits at 8 g + e.
+__device__ __forceinline__ int kpos(int c) { return (c & ~31) + 8 * ((c & 15) >> 2) + 4 * ((c & 31) >> 4) + (c & 3); }
+
+// A (or B) operand read from a row-major bf16 plane: row `row`, lane group
+// g's eight slots of the k block starting at logical column c0 = 32 kb + 4 g
+// (logical columns c0..c0+3 and c0+16..c0+19), stored contiguously at
+// 32 kb + 8 g.
 __device__ __forceinline__ bf16x8_t plane_op(const bf16_t* plane, int row, int rs, int c0) {
-  const uint2 a = *reinterpret_cast<const uint2*>(plane + row * rs + c0);
-  const uint2 b = *reinterpret_cast<const uint2*>(plane + row * rs + c0 + 16);
-  const u32x4_t v = {a.x, a.y, b.x, b.y};
-  return __builtin_bit_cast(bf16x8_t, v);
+  return *reinterpret_cast<const bf16x8_t*>(plane + row * rs + c0 + (c0 & 31));
 }
 
 __device__ __forceinline__ Op plane_op2(const bf16_t* hi, const bf16_t* lo, int row, int rs, int c0) {
@@ -126,23 +130,42 @@ __device__ __forceinline__ float ld_f32(rsrc_t r, int voff, int soff) {
 __device__ __forceinline__ void st_f32(rsrc_t r, float v, int voff, int soff) {
   __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, v), r, voff, soff, 0);
 }
-// One input element (bf16 widened, or f32).
-__device__ __forceinline__ float ld_in(rsrc_t r, int voff, int soff, const bf16_t*) {
-  return bf16_lo((uint32_t)__builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, 0));
-}
-__device__ __forceinline__ float ld_in(rsrc_t r, int voff, int soff, const float*) { return ld_f32(r, voff, soff); }
-// Two consecutive input elements.
-__device__ __forceinline__ void ld_in2(rsrc_t r, int voff, int soff, float& a, float& b, const bf16_t*) {
-  const uint32_t w = __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0);
-  a = bf16_lo(w);
-  b = bf16_hi(w);
-}
-// (Two 32-bit loads: hipcc lowers __builtin_amdgcn_raw_buffer_load_b64 to a
-// single-dword load, leaving the upper half undefined.)
-__device__ __forceinline__ void ld_in2(rsrc_t r, int voff, int soff, float& a, float& b, const float*) {
-  a = ld_f32(r, voff, soff);
-  b = ld_f32(r, voff + 4, soff);
-}
+// Two consecutive input elements as loaded (bf16: one packed dword; f32: two
+// dwords), widened when used.
+template <typename TIn>
+struct Pair2;
+template <>
+struct Pair2<bf16_t> {
+  uint32_t w;
+  __device__ __forceinline__ void load(rsrc_t r, int voff) { w = __builtin_amdgcn_raw_buffer_load_b32(r, voff, 0, 0); }
+  __device__ __forceinline__ float lo() const { return bf16_lo(w); }
+  __device__ __forceinline__ float hi() const { return bf16_hi(w); }
+};
+template <>
+struct Pair2<float> {
+  float a, b;
+  __device__ __forceinline__ void load(rsrc_t r, int voff) {
+    a = ld_f32(r, voff, 0);
+    b = ld_f32(r, voff + 4, 0);
+  }
+  __device__ __forceinline__ float lo() const { return a; }
+  __device__ __forceinline__ float hi() const { return b; }
+};
+// One input element as loaded.
+template <typename TIn>
+struct One;
+template <>
+struct One<bf16_t> {
+  uint32_t w;
+  __device__ __forceinline__ void load(rsrc_t r, int voff) { w = __builtin_amdgcn_raw_buffer_load_b16(r, voff, 0, 0); }
+  __device__ __forceinline__ float get() const { return bf16_lo(w); }
+};
+template <>
+struct One<float> {
+  float w;
+  __device__ __forceinline__ void load(rsrc_t r, int voff) { w = ld_f32(r, voff, 0); }
+  __device__ __forceinline__ float get() const { return w; }
+};
 
 template <typename TIn>
 struct PrefillArgs {
@@ -171,11 +194,18 @@ struct PrefillArgs {
 // the diagonal, the inverses (I + A_jj)^-1.
 template <int DK, int CH, int NW>
 struct Smem {
-  static constexpr int RS_K = DK + 4;  // row stride (elements) of channel-indexed planes
-  static constexpr int RS_C = CH + 4;  // row stride of token-indexed planes
+  // Row strides (elements) of 16-byte aligned rows.  A wave reads an
+  // operand as rows l & 15 at 16-byte column group l >> 4; on gfx950 that is
+  // free of bank conflicts when the row stride is 8 mod 16 dwords, and
+  // 2-way conflicted at 4 mod 8 dwords (measured).  The Kt/Qt planes, the
+  // most-read operand, get the conflict-free stride; the others the 8-element
+  // pad that fits the 160 KiB budget.
+  static constexpr int RS_Q = DK + 16;  // Kt / Qt planes
+  static constexpr int RS_K = DK + 8;   // Kh planes
+  static constexpr int RS_C = CH + 8;   // token-indexed planes (Kb^T, M, P)
   static constexpr int NB = CH / 16;   // 16-token blocks per chunk
   static constexpr int NG = (64 * NW) / (DK / 2);  // token groups in the preparation phase
-  static constexpr int KQ_PLANE = 2 * CH * RS_K;   // elements per KQ plane
+  static constexpr int KQ_PLANE = 2 * CH * RS_Q;   // elements per KQ plane
   static constexpr int KH_PLANE = CH * RS_K;
   static constexpr int KB_PLANE = DK * RS_C;
   static constexpr int CC_PLANE = CH * RS_C;
@@ -183,17 +213,23 @@ struct Smem {
   static constexpr int off_kb = off_kq + 2 * KQ_PLANE * 2;
   static constexpr int off_r2 = off_kb + 2 * KB_PLANE * 2;
   static constexpr int r2_a = 2 * KH_PLANE * 2;
-  static constexpr int RS_D = 17;      // fp32 row stride of a diagonal block: odd, conflict-free columns
+  static constexpr int RS_D = 20;      // fp32 row stride of a diagonal block: 16-byte rows, conflict-free writes
   static constexpr int DIAG = NB * 16 * RS_D;  // floats of the diagonal blocks
   static constexpr int r2_b = 2 * CC_PLANE * 2 + DIAG * 4;
   static constexpr int off_r3 = off_r2 + (r2_a > r2_b ? r2_a : r2_b);
-  static constexpr int off_misc = off_r3 + 2 * CC_PLANE * 2;
-  static constexpr int off_beta = off_misc;
-  static constexpr int off_gn = off_beta + CH * 4;
-  static constexpr int off_tot = off_gn + DK * 4;
-  static constexpr int total = off_tot + NG * DK * 4;
+  static constexpr int total = off_r3 + 2 * CC_PLANE * 2;
+  // beta (CH floats) and 2^g_n (DK floats) live in the 16 unused bytes at
+  // the end of each row of the Kb^T hi plane (4 floats per row).
+  static_assert(CH + DK <= 4 * DK && (RS_C - CH) * 2 == 16, "beta and 2^g_n must fit the Kb row padding");
+  // Token-group totals of the decay cumsum, only live between the two passes
+  // of the preparation: they borrow the M region, which is written later.
+  static constexpr int off_tot = off_r3;
+  static_assert(NG * DK * 4 <= 2 * CC_PLANE * 2, "cumsum scratch must fit the M region");
   static_assert(total <= 163840, "LDS budget exceeded");
-  static_assert(r2_a % 16 == 0 && off_r3 % 16 == 0 && off_misc % 16 == 0, "alignment");
+  static_assert(off_kb % 16 == 0 && r2_a % 16 == 0 && off_r3 % 16 == 0 && (RS_Q * 2) % 16 == 0 &&
+                    (KQ_PLANE * 2) % 16 == 0 && (KB_PLANE * 2) % 16 == 0 && (KH_PLANE * 2) % 16 == 0 &&
+                    (CC_PLANE * 2) % 16 == 0 && (RS_K * 2) % 16 == 0 && (RS_C * 2) % 16 == 0,
+                "16-byte aligned planes and rows");
 };
 
 // Lower-triangular tile (mt, nt), nt <= mt < 4, of triangular index ii.
@@ -228,8 +264,10 @@ __global__ void __launch_bounds__(DV * 4) prefill_chunked_kernel(PrefillArgs<TIn
   float* adiag = reinterpret_cast<float*>(smem + L::off_r2 + 2 * L::CC_PLANE * 2);
   bf16_t* m_hi = reinterpret_cast<bf16_t*>(smem + L::off_r3);
   bf16_t* m_lo = m_hi + L::CC_PLANE;
-  float* sbeta = reinterpret_cast<float*>(smem + L::off_beta);
-  float* sgn = reinterpret_cast<float*>(smem + L::off_gn);
+  // beta_t at misc(t), 2^g_n of channel c at misc(CH + c): the Kb^T row padding.
+  auto misc = [&](int v) -> float& {
+    return *reinterpret_cast<float*>(smem + L::off_kb + (v >> 2) * (L::RS_C * 2) + CH * 2 + (v & 3) * 4);
+  };
   float* stot = reinterpret_cast<float*>(smem + L::off_tot);
 
   const int bh = blockIdx.x;
@@ -251,6 +289,47 @@ __global__ void __launch_bounds__(DV * 4) prefill_chunked_kernel(PrefillArgs<TIn
     for (int r = 0; r < 4; ++r) st[mt][r] = ld_f32(rs_state, tile_voff, (16 * mt + r) * DV * 4);
 
   const int n_chunks = (a.L + CH - 1) / CH;
+  const int rowk = a.H * DK, rowv = a.H * DV;  // elements between consecutive tokens
+
+  // Every global input load of a chunk (alpha, k, q, beta and this wave's
+  // value tile) is issued one chunk ahead, before the previous chunk's value
+  // phase, so its memory latency hides behind that phase.  Thread (cp, tg)
+  // owns key channels 2 cp, 2 cp + 1 for tokens [tg TPG, tg TPG + TPG); a
+  // padding row reads the chunk's last valid row (always inside the window)
+  // and is replaced when used (alpha by 1, the others by 0).
+  Pair2<float> ra[TPG];
+  Pair2<TIn> rk[TPG], rq[TPG];
+  float rb;  // beta of token tg TPG + (cp mod TPG): one load per lane instead of TPG identical ones
+  One<TIn> rv[NB][4];
+  auto issue_loads = [&](int cc, int tid_) {
+    const int t_b = cc * CH, nn = min(CH, a.L - t_b);
+    const size_t r0 = (tok0 + t_b) * a.H + h;
+    const rsrc_t wk = make_rsrc(a.k + r0 * DK, ((nn - 1) * rowk + DK) * sizeof(TIn));
+    const rsrc_t wq = make_rsrc(a.q + r0 * DK, ((nn - 1) * rowk + DK) * sizeof(TIn));
+    const rsrc_t wa = make_rsrc(a.alpha + r0 * DK, ((nn - 1) * rowk + DK) * 4);
+    const rsrc_t wb = make_rsrc(a.beta + r0, ((nn - 1) * a.H + 1) * 4);
+    const rsrc_t wv = make_rsrc(a.v + r0 * DV, ((nn - 1) * rowv + DV) * sizeof(TIn));
+    const int cp_ = tid_ % CP, tg_ = tid_ / CP;
+    const int g_ = (tid_ & 63) >> 4, col_ = 16 * (tid_ >> 6) + (tid_ & 15);
+#pragma unroll
+    for (int i = 0; i < TPG; ++i) {
+      const int rc = min(tg_ * TPG + i, nn - 1);
+      const int vo = rc * rowk + 2 * cp_;
+      ra[i].load(wa, vo * 4);
+      rk[i].load(wk, vo * (int)sizeof(TIn));
+      rq[i].load(wq, vo * (int)sizeof(TIn));
+    }
+    rb = ld_f32(wb, min(tg_ * TPG + cp_ % TPG, nn - 1) * a.H * 4, 0);
+#pragma unroll
+    for (int mt = 0; mt < NB; ++mt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int rc = min(16 * mt + 4 * g_ + r, nn - 1);
+        rv[mt][r].load(wv, (rc * rowv + col_) * (int)sizeof(TIn));
+      }
+  };
+  issue_loads(0, threadIdx.x);
+
   for (int c = 0; c < n_chunks; ++c) {
     // Lane coordinates are re-derived from an opaque copy of the thread id
     // in every chunk: otherwise the compiler hoists every LDS address of the
@@ -262,60 +341,28 @@ __global__ void __launch_bounds__(DV * 4) prefill_chunked_kernel(PrefillArgs<TIn
     const int col = 16 * wave + l16;  // this lane's value column in the accumulator layout
     const int t_base = c * CH;
     const int n = min(CH, a.L - t_base);  // valid tokens in this chunk; rows n.. are padding
-    // Windows over this chunk's valid token rows of this head.
     const size_t row0 = (tok0 + t_base) * a.H + h;  // [B][L][H] row index of the chunk's first token
-    const int rowk = a.H * DK, rowv = a.H * DV;       // elements between consecutive tokens
-    const rsrc_t rs_k = make_rsrc(a.k + row0 * DK, ((n - 1) * rowk + DK) * sizeof(TIn));
-    const rsrc_t rs_q = make_rsrc(a.q + row0 * DK, ((n - 1) * rowk + DK) * sizeof(TIn));
-    const rsrc_t rs_a = make_rsrc(a.alpha + row0 * DK, ((n - 1) * rowk + DK) * 4);
-    const rsrc_t rs_b = make_rsrc(a.beta + row0, ((n - 1) * a.H + 1) * 4);
-    const rsrc_t rs_v = make_rsrc(a.v + row0 * DV, ((n - 1) * rowv + DV) * sizeof(TIn));
     const rsrc_t rs_o = make_rsrc(a.o + row0 * DV, ((n - 1) * rowv + DV) * 4);
 
     // ---- Phase 1: decay cumsum and the decayed key/query planes ---------
-    // Thread (cp, tg) owns key channels 2 cp, 2 cp + 1 for tokens
-    // [tg TPG, tg TPG + TPG).  Every global load of the chunk (alpha, k, q,
-    // beta and this wave's value tiles) is issued here, before any use, and
-    // unconditionally, so the compiler issues them back to back and the
-    // chunk pays one memory latency: a padding row reads the last valid row
-    // (always inside the window) and its value is then replaced (alpha by 1,
-    // the others by 0).
     const int cp = tid % CP, tg = tid / CP;
     const int c0 = 2 * cp;
-    float al0[TPG], al1[TPG], k0[TPG], k1[TPG], q0[TPG], q1[TPG], bt[TPG];
-#pragma unroll
-    for (int i = 0; i < TPG; ++i) {
-      const int rc = min(tg * TPG + i, n - 1);
-      const int vo = rc * rowk + c0;
-      ld_in2(rs_a, vo * 4, 0, al0[i], al1[i], (const float*)nullptr);
-      ld_in2(rs_k, vo * (int)sizeof(TIn), 0, k0[i], k1[i], (const TIn*)nullptr);
-      ld_in2(rs_q, vo * (int)sizeof(TIn), 0, q0[i], q1[i], (const TIn*)nullptr);
-      bt[i] = ld_f32(rs_b, rc * a.H * 4, 0);
-    }
-    // Value tile of this wave: vv[mt][r] = V[16 mt + 4 g + r][col].
+    float al0[TPG], al1[TPG], k0[TPG], k1[TPG], q0[TPG], q1[TPG];
     float vv[NB][4];
-#pragma unroll
-    for (int mt = 0; mt < NB; ++mt)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int rc = min(16 * mt + 4 * g + r, n - 1);
-        vv[mt][r] = ld_in(rs_v, (rc * rowv + col) * (int)sizeof(TIn), 0, (const TIn*)nullptr);
-      }
 #pragma unroll
     for (int i = 0; i < TPG; ++i) {
       const bool pad = tg * TPG + i >= n;
-      al0[i] = pad ? 1.f : al0[i];  // padding tokens do not decay
-      al1[i] = pad ? 1.f : al1[i];
-      k0[i] = pad ? 0.f : k0[i];
-      k1[i] = pad ? 0.f : k1[i];
-      q0[i] = pad ? 0.f : q0[i];
-      q1[i] = pad ? 0.f : q1[i];
-      bt[i] = pad ? 0.f : bt[i];
+      al0[i] = pad ? 1.f : ra[i].lo();  // padding tokens do not decay
+      al1[i] = pad ? 1.f : ra[i].hi();
+      k0[i] = pad ? 0.f : rk[i].lo();
+      k1[i] = pad ? 0.f : rk[i].hi();
+      q0[i] = pad ? 0.f : rq[i].lo();
+      q1[i] = pad ? 0.f : rq[i].hi();
     }
 #pragma unroll
     for (int mt = 0; mt < NB; ++mt)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) vv[mt][r] = 16 * mt + 4 * g + r < n ? vv[mt][r] : 0.f;
+      for (int r = 0; r < 4; ++r) vv[mt][r] = 16 * mt + 4 * g + r < n ? rv[mt][r].get() : 0.f;
     {
       // Pass A: per-channel prefix sums of log2(alpha) within the token
       // group; the group totals are combined through LDS.
@@ -330,10 +377,7 @@ __global__ void __launch_bounds__(DV * 4) prefill_chunked_kernel(PrefillArgs<TIn
       }
       stot[tg * DK + c0] = s0;
       stot[tg * DK + c0 + 1] = s1;
-      if (cp == 0) {
-#pragma unroll
-        for (int i = 0; i < TPG; ++i) sbeta[tg * TPG + i] = bt[i];
-      }
+      if (cp < TPG) misc(tg * TPG + cp) = tg * TPG + cp < n ? rb : 0.f;  // padding tokens get beta 0
       __syncthreads();
       float off0 = 0.f, off1 = 0.f, gn0 = 0.f, gn1 = 0.f;
 #pragma unroll
@@ -347,39 +391,44 @@ __global__ void __launch_bounds__(DV * 4) prefill_chunked_kernel(PrefillArgs<TIn
         gn1 += t1;
       }
       if (tg == 0) {
-        sgn[c0] = exp2f(gn0);
-        sgn[c0 + 1] = exp2f(gn1);
+        misc(CH + c0) = __builtin_amdgcn_exp2f(gn0);
+        misc(CH + c0 + 1) = __builtin_amdgcn_exp2f(gn1);
       }
       // Pass B: the decayed planes; Kb goes to transposed planes two tokens at a time.
+      // Kb = Kh 2^(g_n) (no third exponential per element).
+      const float egn0 = __builtin_amdgcn_exp2f(gn0), egn1 = __builtin_amdgcn_exp2f(gn1);
+      const int pc = kpos(c0);  // storage column of the channel pair (c0, c0 + 1)
       uint32_t kbh0 = 0, kbl0 = 0, kbh1 = 0, kbl1 = 0;
 #pragma unroll
       for (int i = 0; i < TPG; ++i) {
         const int tr = tg * TPG + i;
         const float x0 = off0 + g0[i], x1 = off1 + g1[i];
-        const float e0 = exp2f(x0), e1 = exp2f(x1);
-        const float ie0 = exp2f(-x0), ie1 = exp2f(-x1);
+        const float e0 = __builtin_amdgcn_exp2f(x0), e1 = __builtin_amdgcn_exp2f(x1);
+        const float ie0 = __builtin_amdgcn_exp2f(-x0), ie1 = __builtin_amdgcn_exp2f(-x1);
         uint32_t hi, lo;
         split2(k0[i] * e0, k1[i] * e1, hi, lo);  // Kt
-        *reinterpret_cast<uint32_t*>(kq_hi + tr * L::RS_K + c0) = hi;
-        *reinterpret_cast<uint32_t*>(kq_lo + tr * L::RS_K + c0) = lo;
+        *reinterpret_cast<uint32_t*>(kq_hi + tr * L::RS_Q + pc) = hi;
+        *reinterpret_cast<uint32_t*>(kq_lo + tr * L::RS_Q + pc) = lo;
         split2(q0[i] * e0, q1[i] * e1, hi, lo);  // Qt
-        *reinterpret_cast<uint32_t*>(kq_hi + (CH + tr) * L::RS_K + c0) = hi;
-        *reinterpret_cast<uint32_t*>(kq_lo + (CH + tr) * L::RS_K + c0) = lo;
-        split2(k0[i] * ie0, k1[i] * ie1, hi, lo);  // Kh
-        *reinterpret_cast<uint32_t*>(kh_hi + tr * L::RS_K + c0) = hi;
-        *reinterpret_cast<uint32_t*>(kh_lo + tr * L::RS_K + c0) = lo;
+        *reinterpret_cast<uint32_t*>(kq_hi + (CH + tr) * L::RS_Q + pc) = hi;
+        *reinterpret_cast<uint32_t*>(kq_lo + (CH + tr) * L::RS_Q + pc) = lo;
+        const float kh0 = k0[i] * ie0, kh1 = k1[i] * ie1;
+        split2(kh0, kh1, hi, lo);  // Kh
+        *reinterpret_cast<uint32_t*>(kh_hi + tr * L::RS_K + pc) = hi;
+        *reinterpret_cast<uint32_t*>(kh_lo + tr * L::RS_K + pc) = lo;
         __bf16 l0, l1;
-        const __bf16 h0 = split_hi(k0[i] * exp2f(gn0 - x0), l0), h1 = split_hi(k1[i] * exp2f(gn1 - x1), l1);
+        const __bf16 h0 = split_hi(kh0 * egn0, l0), h1 = split_hi(kh1 * egn1, l1);
         const int sh = (i & 1) * 16;
         kbh0 |= bf16_bits(h0) << sh;
         kbl0 |= bf16_bits(l0) << sh;
         kbh1 |= bf16_bits(h1) << sh;
         kbl1 |= bf16_bits(l1) << sh;
         if (i & 1) {
-          *reinterpret_cast<uint32_t*>(kb_hi + c0 * L::RS_C + tr - 1) = kbh0;
-          *reinterpret_cast<uint32_t*>(kb_lo + c0 * L::RS_C + tr - 1) = kbl0;
-          *reinterpret_cast<uint32_t*>(kb_hi + (c0 + 1) * L::RS_C + tr - 1) = kbh1;
-          *reinterpret_cast<uint32_t*>(kb_lo + (c0 + 1) * L::RS_C + tr - 1) = kbl1;
+          const int pt = kpos(tr - 1);  // storage column of the token pair (tr - 1, tr)
+          *reinterpret_cast<uint32_t*>(kb_hi + c0 * L::RS_C + pt) = kbh0;
+          *reinterpret_cast<uint32_t*>(kb_lo + c0 * L::RS_C + pt) = kbl0;
+          *reinterpret_cast<uint32_t*>(kb_hi + (c0 + 1) * L::RS_C + pt) = kbh1;
+          *reinterpret_cast<uint32_t*>(kb_lo + (c0 + 1) * L::RS_C + pt) = kbl1;
           kbh0 = kbl0 = kbh1 = kbl1 = 0;
         }
       }
@@ -404,7 +453,7 @@ __global__ void __launch_bounds__(DV * 4) prefill_chunked_kernel(PrefillArgs<TIn
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) {
           const int k0_ = 32 * kb + 4 * g;
-          at[s_] = mfma3(plane_op2(kq_hi, kq_lo, row, L::RS_K, k0_), plane_op2(kh_hi, kh_lo, 16 * nt + l16, L::RS_K, k0_),
+          at[s_] = mfma3(plane_op2(kq_hi, kq_lo, row, L::RS_Q, k0_), plane_op2(kh_hi, kh_lo, 16 * nt + l16, L::RS_K, k0_),
                          at[s_]);
         }
       }
@@ -421,20 +470,21 @@ __global__ void __launch_bounds__(DV * 4) prefill_chunked_kernel(PrefillArgs<TIn
         for (int r = 0; r < 4; ++r) {
           const int tr = 16 * mt + 4 * g + r;
           if (i < NA) {
-            const float av = tc < tr ? at[s_][r] * sbeta[tr] : 0.f;
+            const float bta = misc(tr);  // read on every lane: no divergent LDS access
+            const float av = tc < tr ? at[s_][r] * bta : 0.f;
             if (mt == nt) {
               adiag[(mt * 16 + 4 * g + r) * L::RS_D + l16] = av;
             } else {
               __bf16 lo;
               const __bf16 hi = split_hi(av, lo);
-              m_hi[tr * L::RS_C + tc] = __builtin_bit_cast(bf16_t, hi);
-              m_lo[tr * L::RS_C + tc] = __builtin_bit_cast(bf16_t, lo);
+              m_hi[tr * L::RS_C + kpos(tc)] = __builtin_bit_cast(bf16_t, hi);
+              m_lo[tr * L::RS_C + kpos(tc)] = __builtin_bit_cast(bf16_t, lo);
             }
           } else {
             __bf16 lo;
             const __bf16 hi = split_hi(tc <= tr ? at[s_][r] : 0.f, lo);
-            p_hi[tr * L::RS_C + tc] = __builtin_bit_cast(bf16_t, hi);
-            p_lo[tr * L::RS_C + tc] = __builtin_bit_cast(bf16_t, lo);
+            p_hi[tr * L::RS_C + kpos(tc)] = __builtin_bit_cast(bf16_t, hi);
+            p_lo[tr * L::RS_C + kpos(tc)] = __builtin_bit_cast(bf16_t, lo);
           }
         }
       }
@@ -445,10 +495,10 @@ __global__ void __launch_bounds__(DV * 4) prefill_chunked_kernel(PrefillArgs<TIn
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int tr = 32 * i + 4 * g + r, tc = 32 * i + 16 + l16;
-        p_hi[tr * L::RS_C + tc] = 0;
-        p_lo[tr * L::RS_C + tc] = 0;
-        m_hi[tr * L::RS_C + tc] = 0;
-        m_lo[tr * L::RS_C + tc] = 0;
+        p_hi[tr * L::RS_C + kpos(tc)] = 0;
+        p_lo[tr * L::RS_C + kpos(tc)] = 0;
+        m_hi[tr * L::RS_C + kpos(tc)] = 0;
+        m_lo[tr * L::RS_C + kpos(tc)] = 0;
       }
     }
     __syncthreads();
@@ -463,22 +513,31 @@ __global__ void __launch_bounds__(DV * 4) prefill_chunked_kernel(PrefillArgs<TIn
         float x[16];
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
+          // Row r of the block, read four entries at a time (same address on
+          // every lane: a broadcast).
           float acc = 0.f;
 #pragma unroll
-          for (int i = 0; i < 16; ++i)
-            if (i < r) acc = __builtin_fmaf(adiag[(j * 16 + r) * L::RS_D + i], x[i], acc);
+          for (int i4 = 0; i4 < (r + 3) / 4; ++i4) {
+            const float4 a4 = *reinterpret_cast<const float4*>(&adiag[(j * 16 + r) * L::RS_D + 4 * i4]);
+            const float av[4] = {a4.x, a4.y, a4.z, a4.w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              if (4 * i4 + i < r) acc = __builtin_fmaf(av[i], x[4 * i4 + i], acc);
+          }
           x[r] = r == cc ? 1.f : (r < cc ? 0.f : -acc);
         }
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           __bf16 lo;
           const __bf16 hi = split_hi(x[r], lo);
-          m_hi[(16 * j + r) * L::RS_C + 16 * j + cc] = __builtin_bit_cast(bf16_t, hi);
-          m_lo[(16 * j + r) * L::RS_C + 16 * j + cc] = __builtin_bit_cast(bf16_t, lo);
+          m_hi[(16 * j + r) * L::RS_C + kpos(16 * j + cc)] = __builtin_bit_cast(bf16_t, hi);
+          m_lo[(16 * j + r) * L::RS_C + kpos(16 * j + cc)] = __builtin_bit_cast(bf16_t, lo);
         }
       }
     }
     __syncthreads();
+
+    if (c + 1 < n_chunks) issue_loads(c + 1, tid);
 
     // ---- Phase 4: value side for this wave's 16 columns ------------------
     // 4b: X = [Kt; Qt] S, rows 0..CH-1 = Kt S, rows CH..2CH-1 = Qt S.
@@ -490,7 +549,7 @@ __global__ void __launch_bounds__(DV * 4) prefill_chunked_kernel(PrefillArgs<TIn
       const Op sop = op_from_tiles(st[2 * kb], st[2 * kb + 1]);
       const int k0_ = 32 * kb + 4 * g;
 #pragma unroll
-      for (int mt = 0; mt < 2 * NB; ++mt) xs[mt] = mfma3(plane_op2(kq_hi, kq_lo, 16 * mt + l16, L::RS_K, k0_), sop, xs[mt]);
+      for (int mt = 0; mt < 2 * NB; ++mt) xs[mt] = mfma3(plane_op2(kq_hi, kq_lo, 16 * mt + l16, L::RS_Q, k0_), sop, xs[mt]);
     }
     // 4c/4d: R = V - Kt S, then E = (I + A)^-1 Diag(beta) R by 16-token blocks:
     //   E_i = X_ii (beta_i R_i - sum_{j<i} A_ij E_j).
@@ -502,7 +561,7 @@ __global__ void __launch_bounds__(DV * 4) prefill_chunked_kernel(PrefillArgs<TIn
     for (int i = 0; i < NB; ++i) {
       f32x4_t z;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) z[r] = sbeta[16 * i + 4 * g + r] * (vv[i][r] - xs[i][r]);
+      for (int r = 0; r < 4; ++r) z[r] = misc(16 * i + 4 * g + r) * (vv[i][r] - xs[i][r]);
       if (i > 0) {
         f32x4_t cs = zero4;
 #pragma unroll
@@ -531,7 +590,7 @@ __global__ void __launch_bounds__(DV * 4) prefill_chunked_kernel(PrefillArgs<TIn
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) st[mt][r] *= sgn[16 * mt + 4 * g + r];
+      for (int r = 0; r < 4; ++r) st[mt][r] *= misc(CH + 16 * mt + 4 * g + r);
 #pragma unroll
       for (int kb = 0; kb < NB / 2; ++kb)
         st[mt] = mfma3(plane_op2(kb_hi, kb_lo, 16 * mt + l16, L::RS_C, 32 * kb + 4 * g), eop[kb], st[mt]);
