@@ -205,6 +205,49 @@ def bench_verify_commit(torch, kda, synth, B, T, rounds, layers, device):
     }
 
 
+def bench_spec_fused(torch, kda, synth, B, T, rounds, layers, device):
+    """Speculative rounds through the fused entry point: each round is one
+    launch per layer that commits the previous round's accepted prefix and
+    verifies T new drafts (the first round is a plain verify)."""
+    spec = synth.CONFIGS["spec_verify"]
+    inp = synth.token_inputs(spec, B, 4 * T)
+    d = {}
+    for k, v in inp.items():
+        t = dev_tensor(torch, v, device)
+        d[k] = t.view(B, 4, T, *t.shape[2:]).transpose(0, 1).contiguous()   # [4][B][T][H][d]
+    acc_np = synth.accepted_counts(spec, B, rounds + 1, T)
+    acc = torch.from_numpy(acc_np).to(device)
+    S0 = dev_tensor(torch, synth.initial_state(spec, B), device)
+    states = [S0.clone() for _ in range(layers)]
+    logs = [kda.InputLog(S0, T_max=T) for _ in range(layers)]
+    pos = torch.zeros(B, dtype=torch.int64, device=device)
+    err = torch.zeros(1, dtype=torch.int32, device=device)
+    o = torch.empty((B, T, H, DV), dtype=torch.float32, device=device)
+    for S, lg in zip(states, logs):     # round 0: nothing pending yet
+        kda.commit_verify(S, pos, d["q"][0], d["k"][0], d["v"][0], d["alpha"][0], d["beta"][0], o, lg)
+    graphs = []
+    for r in range(rounds):
+        j = (r + 1) % 4
+        graphs.append(capture(torch, [kda.CommitVerifyPlan(S, pos, d["q"][j], d["k"][j], d["v"][j], d["alpha"][j],
+                                                           d["beta"][j], o, lg, acc[r], err)
+                                      for S, lg in zip(states, logs)]))
+    for g in graphs:
+        g.replay()
+    with Timer(torch) as tm:
+        for g in graphs:
+            g.replay()
+    n_launch = rounds * layers
+    us = tm.ms * 1e3 / n_launch
+    a = acc_np[:rounds]
+    per_bh = (STATE_BYTES + T * (TOKEN_IN_BYTES + 128 * 4 + LOG_BYTES)) * a.size
+    per_bh += int((a > 0).sum()) * STATE_BYTES + int(a.sum()) * LOG_BYTES
+    bytes_total = float(per_bh) * H * layers
+    return {"B": B, "T": T, "rounds": rounds, "layers": layers, "mean_accepted": float(a.mean()),
+            "round_us": us, "hbm_frac": bytes_total / (tm.ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "verified_token_heads_per_s": B * H * T / (us * 1e-6),
+            "committed_token_heads_per_s": float(a.sum()) * H * layers / (tm.ms * 1e-3)}
+
+
 def bench_verify_only(torch, kda, synth, B, T, layers, reps, device):
     """Verify alone: T drafts through `layers` independent states per round,
     replayed back to back from one captured graph (each layer has its own log;
@@ -380,6 +423,9 @@ def main():
         log("verify/commit")
         rows["verify_commit_b16"] = bench_verify_commit(torch, kda, synth, 16, 4, 32, 32, device)
         rows["verify_commit_b64"] = bench_verify_commit(torch, kda, synth, 64, 4, 32, 8, device)
+        log("fused commit + verify rounds")
+        rows["spec_fused_b16"] = bench_spec_fused(torch, kda, synth, 16, 4, 32, 32, device)
+        rows["spec_fused_b64"] = bench_spec_fused(torch, kda, synth, 64, 4, 32, 8, device)
         log("verify alone")
         rows["verify_only_b16"] = bench_verify_only(torch, kda, synth, 16, 4, 32, 20, device)
         rows["verify_only_b64"] = bench_verify_only(torch, kda, synth, 64, 4, 8, 50, device)

@@ -90,6 +90,7 @@ typedef enum kda_dtype { KDA_BF16 = 0, KDA_F32 = 1 } kda_dtype;
 #define KDA_VARIANT_RESTORE 5
 #define KDA_VARIANT_PREFILL_RECURRENT 6
 #define KDA_VARIANT_PREFILL_CHUNKED 7
+#define KDA_VARIANT_COMMIT_VERIFY 8
 
 typedef struct kda_shape {
   int32_t B;        /* sequences in the batch */
@@ -106,14 +107,14 @@ typedef struct kda_shape {
  * inputs are stored and the accepted part is replayed from the last
  * committed state).  `dev` is a caller-owned device buffer of
  * kda_log_bytes(shape, T_max) bytes.  It holds four regions, each starting
- * at a 256-byte boundary, in this order, sized for T_max and filled for the
- * T of the pending verify:
- *   k      in_dtype [B][T][H][dk]
- *   v      in_dtype [B][T][H][dv]
- *   alpha  f32 [B][T][H][dk]
- *   beta   f32 [B][T][H]
- * `pending_T` is host-side bookkeeping: kda_verify sets it to T, kda_commit
- * consumes it and resets it to 0.  Initialise it to 0.
+ * at a 256-byte boundary, in this order, with T_max token rows per sequence
+ * of which the first T (of the pending verify) are filled:
+ *   k      in_dtype [B][T_max][H][dk]
+ *   v      in_dtype [B][T_max][H][dv]
+ *   alpha  f32 [B][T_max][H][dk]
+ *   beta   f32 [B][T_max][H]
+ * `pending_T` is host-side bookkeeping: kda_verify and kda_commit_verify set
+ * it to T, kda_commit consumes it and resets it to 0.  Initialise it to 0.
  */
 typedef struct kda_log {
   void* dev;
@@ -157,8 +158,10 @@ kda_status kda_decode_step(const kda_shape* shape, float* state, int64_t* pos, c
  * state: runs the T tokens on a private copy of each (b, h) state, writes
  * every output o_t (f32 [B][T][H][dv]) and copies k, v, alpha, beta of all T
  * tokens into the log.  `state` is read, never written.  Fails with
- * KDA_ERR_ORDER if `log` already has a pending verify.  Output o_t for
- * t <= a equals, bit for bit, what a decode steps would have produced.
+ * KDA_ERR_ORDER if `log` already has a pending verify.  The outputs are
+ * computed in the chunk form of the rule (groups of up to four tokens from
+ * the group's start state), so o_t agrees with what t decode steps would
+ * produce to rounding, not bit for bit.
  * (Webinar summary, paragraph on rejected draft tokens.)
  */
 kda_status kda_verify(const kda_shape* shape, int32_t T, const float* state, const void* q,
@@ -178,6 +181,25 @@ kda_status kda_verify(const kda_shape* shape, int32_t T, const float* state, con
  */
 kda_status kda_commit(const kda_shape* shape, float* state, int64_t* pos, kda_log* log,
                       const int32_t* accepted, int32_t* dev_err, void* stream);
+
+/*
+ * Commit of the pending verify fused with the next verify, in one launch:
+ * for each sequence b, replays the first accepted[b] tokens of the pending
+ * verify onto the state (exactly as kda_commit: bit-identical to that many
+ * decode steps, pos[b] += accepted[b], KDA_DEV_ERR_ACCEPTED and no change
+ * for a count outside [0, pending_T]), then verifies T new draft tokens from
+ * the committed state (exactly as kda_verify: outputs o and the log of the
+ * new tokens).  With no verify pending (pending_T == 0) it is a verify.
+ * The committed state is written once and not read back: one state read per
+ * speculative round instead of two.  accepted and dev_err may be NULL only
+ * when nothing is pending.  On success pending_T = T.
+ * (Webinar summary, paragraph on rejected draft tokens: the accepted part is
+ * replayed from the last committed state; here the replay happens at the
+ * start of the next round's verify.)
+ */
+kda_status kda_commit_verify(const kda_shape* shape, int32_t T, float* state, int64_t* pos, const void* q,
+                             const void* k, const void* v, const float* alpha, const float* beta, float* o,
+                             kda_log* log, const int32_t* accepted, int32_t* dev_err, void* stream);
 
 /*
  * Snapshot: copies the whole state of sequence seq_ids[i] (all H heads) and

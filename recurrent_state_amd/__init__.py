@@ -10,6 +10,7 @@ from ._lib import (  # noqa: F401
     DEV_ERR_ACCEPTED,
     DEV_ERR_CKPT_SLOT,
     CommitPlan,
+    CommitVerifyPlan,
     DecodePlan,
     LIB_PATH,
     InputLog,
@@ -18,6 +19,7 @@ from ._lib import (  # noqa: F401
     Shape,
     SlotPool,
     commit,
+    commit_verify,
     decode_step,
     exported_symbols,
     last_variant,

@@ -19,7 +19,7 @@ LIB_PATH = os.path.join(_HERE, "libkda.so")
 
 KDA_BF16, KDA_F32 = 0, 1
 VARIANTS = {0: "none", 1: "decode", 2: "verify", 3: "commit", 4: "snapshot", 5: "restore",
-            6: "prefill_recurrent", 7: "prefill_chunked"}
+            6: "prefill_recurrent", 7: "prefill_chunked", 8: "commit_verify"}
 DEV_ERR_ACCEPTED, DEV_ERR_CKPT_SLOT = 1, 2
 
 
@@ -53,6 +53,8 @@ _SIGS = {
     "kda_decode_step": (_I, [ctypes.POINTER(Shape), _P, _P, _P, _P, _P, _P, _P, _P, _P]),
     "kda_verify": (_I, [ctypes.POINTER(Shape), _I, _P, _P, _P, _P, _P, _P, _P, ctypes.POINTER(_Log), _P]),
     "kda_commit": (_I, [ctypes.POINTER(Shape), _P, _P, ctypes.POINTER(_Log), _P, _P, _P]),
+    "kda_commit_verify": (_I, [ctypes.POINTER(Shape), _I, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.POINTER(_Log), _P,
+                               _P, _P]),
     "kda_snapshot": (_I, [ctypes.POINTER(Shape), _P, _P, _P, _P, _I, ctypes.POINTER(_Slots), _P]),
     "kda_restore": (_I, [ctypes.POINTER(Shape), _P, _P, _P, _P, _I, ctypes.POINTER(_Slots), _P]),
     "kda_prefill_chunked": (_I, [ctypes.POINTER(Shape), _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _I, _P,
@@ -212,6 +214,30 @@ def commit(state, pos, log: InputLog, accepted, dev_err):
                             _ptr(accepted), _ptr(dev_err), _stream()))
 
 
+def _commit_verify_args(state, pos, q, k, v, alpha, beta, o, log: InputLog, accepted, dev_err, scale):
+    B, H, dk, dv = state.shape
+    T = q.shape[1]
+    _need(state, "state", (B, H, dk, dv), torch.float32, state.device)
+    _need(pos, "pos", (B,), torch.int64, state.device)
+    _check_tokens(state, T, q, k, v, alpha, beta, o)
+    if accepted is not None:
+        _need(accepted, "accepted", (B,), torch.int32, state.device)
+    if dev_err is not None:
+        _need(dev_err, "dev_err", (1,), torch.int32, state.device)
+    sh = _shape(state, q.dtype, scale)
+    if (B, H, dk, dv, sh.in_dtype) != (log.shape.B, log.shape.H, log.shape.dk, log.shape.dv, log.shape.in_dtype):
+        raise ValueError("log was sized for a different shape")
+    ptrs = tuple(_ptr(t) for t in (state, pos, q, k, v, alpha, beta, o))
+    extra = (_ptr(accepted) if accepted is not None else None, _ptr(dev_err) if dev_err is not None else None)
+    return sh, T, ptrs, extra
+
+
+def commit_verify(state, pos, q, k, v, alpha, beta, o, log: InputLog, accepted=None, dev_err=None, scale=None):
+    """Commit the pending verify's accepted prefix, then verify T new drafts, in one launch."""
+    sh, T, ptrs, extra = _commit_verify_args(state, pos, q, k, v, alpha, beta, o, log, accepted, dev_err, scale)
+    _check(lib().kda_commit_verify(ctypes.byref(sh), T, *ptrs, ctypes.byref(log.c), *extra, _stream()))
+
+
 def _pairs(seq_ids, slot_ids):
     s = (ctypes.c_int32 * len(seq_ids))(*[int(x) for x in seq_ids])
     t = (ctypes.c_int32 * len(slot_ids))(*[int(x) for x in slot_ids])
@@ -339,6 +365,21 @@ class CommitPlan:
         self._args = (ctypes.byref(log.shape), _ptr(state), _ptr(pos), ctypes.byref(log.c), _ptr(accepted),
                       _ptr(dev_err))
         self._fn = lib().kda_commit
+
+    def __call__(self):
+        _check(self._fn(*self._args, _stream()))
+
+
+class CommitVerifyPlan:
+    """A commit_verify call validated once (see DecodePlan).  The pending
+    count of the log when the plan is called is the one committed."""
+
+    def __init__(self, state, pos, q, k, v, alpha, beta, o, log: InputLog, accepted=None, dev_err=None, scale=None):
+        self._shape, T, ptrs, extra = _commit_verify_args(state, pos, q, k, v, alpha, beta, o, log, accepted,
+                                                          dev_err, scale)
+        self._keep = (state, pos, q, k, v, alpha, beta, o, log, accepted, dev_err)
+        self._args = (ctypes.byref(self._shape), T) + ptrs + (ctypes.byref(log.c),) + extra
+        self._fn = lib().kda_commit_verify
 
     def __call__(self):
         _check(self._fn(*self._args, _stream()))

@@ -69,7 +69,7 @@ kda::LogPtrs log_ptrs(const kda_shape& s, const kda_log* log) {
   const kda::LogLayout L = kda::log_layout(s, log->T_max);
   char* base = static_cast<char*>(log->dev);
   return kda::LogPtrs{base + L.k, base + L.v, reinterpret_cast<float*>(base + L.alpha),
-                      reinterpret_cast<float*>(base + L.beta)};
+                      reinterpret_cast<float*>(base + L.beta), log->T_max};
 }
 
 kda_status check_slots(const kda_slots* slots) {
@@ -203,6 +203,34 @@ kda_status kda_commit(const kda_shape* shape, float* state, int64_t* pos, kda_lo
     if (r != KDA_OK) return r;
   }
   log->pending_T = 0;
+  return KDA_OK;
+}
+
+kda_status kda_commit_verify(const kda_shape* shape, int32_t T, float* state, int64_t* pos, const void* q,
+                             const void* k, const void* v, const float* alpha, const float* beta, float* o,
+                             kda_log* log, const int32_t* accepted, int32_t* dev_err, void* stream) {
+  kda_status r = check_shape(shape);
+  if (r != KDA_OK) return r;
+  if ((r = check_log(*shape, log)) != KDA_OK) return r;
+  if (T < 1 || T > log->T_max) return KDA_ERR_SHAPE;
+  const int32_t pend = log->pending_T;
+  if (pend < 0 || pend > log->T_max) return KDA_ERR_ORDER;
+  if (shape->B > 0) {
+    if ((r = check_ptrs({state})) != KDA_OK) return r;
+    if ((r = check_tokens(q, k, v, alpha, beta, o)) != KDA_OK) return r;
+    if (!pos) return KDA_ERR_NULL;
+    if (!aligned(pos, 8)) return KDA_ERR_ALIGN;
+    if (pend > 0) {
+      if (!accepted || !dev_err) return KDA_ERR_NULL;
+      if (!aligned(accepted, 4) || !aligned(dev_err, 4)) return KDA_ERR_ALIGN;
+    }
+    r = launched(kda::launch_commit_verify(*shape, pend, T, state, pos, accepted, dev_err,
+                                           kda::TokenInputs{q, k, v, alpha, beta}, o, log_ptrs(*shape, log),
+                                           static_cast<hipStream_t>(stream)),
+                 KDA_VARIANT_COMMIT_VERIFY);
+    if (r != KDA_OK) return r;
+  }
+  log->pending_T = T;
   return KDA_OK;
 }
 

@@ -228,4 +228,44 @@ __device__ __forceinline__ void store_tile(float* p, const float (&S)[R][4]) {
     *reinterpret_cast<float4*>(p + (size_t)r * DV) = make_float4(S[r][0], S[r][1], S[r][2], S[r][3]);
 }
 
+// The per-token inputs one lane needs, as stored (raw) and widened.
+template <typename TIn, int R, bool WITH_Q>
+struct TokenIn {
+  Raw<TIn, R> k, q;
+  Raw<float, R> a;
+  Raw4<TIn> v;
+  float beta;
+  __device__ __forceinline__ void load(const TIn* kp, const TIn* qp, const float* ap, const TIn* vp,
+                                       const float* bp) {
+    load_raw(kp, k);
+    if (WITH_Q) load_raw(qp, q);
+    load_raw(ap, a);
+    load4(vp, v);
+    beta = *bp;
+  }
+  __device__ __forceinline__ void update(float (&S)[R][4], float scale, float (&o)[4]) const {
+    float vc[4];
+    widen4(v, vc);
+    token_update<R, WITH_Q>(S, k, a, q, vc, beta, scale, o);
+  }
+};
+
+// Replays n logged tokens onto a lane's R x 4 state tile (rows row0..,
+// columns col0..): the commit step.  Logged token t of this (sequence, head)
+// sits at row tok0 + t * H of the [B][T_max][H] log regions.  Commit and the
+// fused commit + verify both call this, so their states are bit-identical to
+// n decode steps.
+template <int DK, int DV, typename TIn, int R>
+__device__ __forceinline__ void replay_log(float (&S)[R][4], const TIn* log_k, const TIn* log_v,
+                                           const float* log_alpha, const float* log_beta, size_t tok0, int H,
+                                           int n, int row0, int col0) {
+  TokenIn<TIn, R, false> cur;
+  for (int t = 0; t < n; ++t) {
+    const size_t tk = tok0 + (size_t)t * H;
+    cur.load(log_k + tk * DK + row0, nullptr, log_alpha + tk * DK + row0, log_v + tk * DV + col0, log_beta + tk);
+    float o[4];
+    cur.update(S, 0.f, o);
+  }
+}
+
 }  // namespace kda

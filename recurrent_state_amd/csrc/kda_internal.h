@@ -17,6 +17,8 @@ struct LogLayout {
 
 inline size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
+// Regions hold [B][T_max][H] token rows, so every (sequence, head) owns the
+// same rows whatever T a call uses.
 inline LogLayout log_layout(const kda_shape& s, int32_t T_max) {
   const size_t es = s.in_dtype == KDA_BF16 ? 2 : 4;
   const size_t tok = (size_t)s.B * (size_t)T_max * (size_t)s.H;
@@ -37,11 +39,13 @@ struct TokenInputs {
   const float* beta;
 };
 
+// The four log regions; token t of (b, h) is row (b * T_max + t) * H + h.
 struct LogPtrs {
   void* k;
   void* v;
   float* alpha;
   float* beta;
+  int32_t T_max;
 };
 
 hipError_t launch_decode(const kda_shape& s, float* state, int64_t* pos, TokenInputs in, float* o,
@@ -50,6 +54,11 @@ hipError_t launch_verify(const kda_shape& s, int32_t T, const float* state, Toke
                          LogPtrs log, hipStream_t st);
 hipError_t launch_commit(const kda_shape& s, int32_t T, float* state, int64_t* pos, LogPtrs log,
                          const int32_t* accepted, int32_t* dev_err, hipStream_t st);
+// Commit of the pending T_pend logged tokens (T_pend = 0: none) followed by
+// the verify of T new tokens from the committed state, in one launch.
+hipError_t launch_commit_verify(const kda_shape& s, int32_t T_pend, int32_t T, float* state, int64_t* pos,
+                                const int32_t* accepted, int32_t* dev_err, TokenInputs in, float* o, LogPtrs log,
+                                hipStream_t st);
 hipError_t launch_prefill_recurrent(const kda_shape& s, int32_t L, float* state, int64_t* pos,
                                     TokenInputs in, float* o, int32_t ckpt_every, const int32_t* ckpt_slots,
                                     float* slot_states, int64_t* slot_pos, int32_t n_slots,

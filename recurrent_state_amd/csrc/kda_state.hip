@@ -47,7 +47,8 @@ struct CommitArgs {
   const int32_t* accepted;
   int32_t* dev_err;
   int32_t H;
-  int32_t T;
+  int32_t T;     // tokens of the pending verify
+  int32_t Tmax;  // token rows per sequence in the log
 };
 
 template <typename TIn>
@@ -77,8 +78,8 @@ struct PrefillArgs {
 #ifndef KDA_STATE_WAVES
 #define KDA_STATE_WAVES 1
 #endif
-// Token-loop kernels load token t+1's inputs while token t computes (1), or
-// load each token's inputs when it starts (0: fewer live registers).
+// The recurrent prefill loads token t+1's inputs while token t computes (1),
+// or loads each token's inputs when it starts (0: fewer live registers).
 #ifndef KDA_PREFETCH_NEXT
 #define KDA_PREFETCH_NEXT 0
 #endif
@@ -133,28 +134,6 @@ struct Place {
   __device__ __forceinline__ size_t tile_off() const { return (size_t)row0 * DV + col0; }
 };
 
-// The per-token inputs one lane needs, as stored (raw) and widened.
-template <typename TIn, int R, bool WITH_Q>
-struct TokenIn {
-  Raw<TIn, R> k, q;
-  Raw<float, R> a;
-  Raw4<TIn> v;
-  float beta;
-  __device__ __forceinline__ void load(const TIn* kp, const TIn* qp, const float* ap, const TIn* vp,
-                                       const float* bp) {
-    load_raw(kp, k);
-    if (WITH_Q) load_raw(qp, q);
-    load_raw(ap, a);
-    load4(vp, v);
-    beta = *bp;
-  }
-  __device__ __forceinline__ void update(float (&S)[R][4], float scale, float (&o)[4]) const {
-    float vc[4];
-    widen4(v, vc);
-    token_update<R, WITH_Q>(S, k, a, q, vc, beta, scale, o);
-  }
-};
-
 template <int DK, int DV, typename TIn>
 __global__ void KDA_OCCUPANCY __launch_bounds__(kWave * waves_per_group<DV>()) decode_kernel(StepArgs<TIn> a) {
   typedef Place<DK, DV> P;
@@ -187,24 +166,8 @@ __global__ void KDA_OCCUPANCY __launch_bounds__(kWave * waves_per_group<DV>()) c
   float* sp = a.state + (size_t)p.bh * DK * DV + p.tile_off();
   float S[R][4];
   load_tile<R, DV>(sp, S);
-  TokenIn<TIn, R, false> cur, nxt;
-  size_t tok = (size_t)p.b * a.T * a.H + p.h;
-  cur.load(a.log_k + tok * DK + p.row0, nullptr, a.log_alpha + tok * DK + p.row0, a.log_v + tok * DV + p.col0,
-           a.log_beta + tok);
-  for (int t = 0; t < n; ++t) {
-    const size_t tn = tok + a.H;
-    if (KDA_PREFETCH_NEXT && t + 1 < n)
-      nxt.load(a.log_k + tn * DK + p.row0, nullptr, a.log_alpha + tn * DK + p.row0, a.log_v + tn * DV + p.col0,
-               a.log_beta + tn);
-    float o[4];
-    cur.update(S, 0.f, o);
-    if (KDA_PREFETCH_NEXT)
-      cur = nxt;
-    else if (t + 1 < n)
-      cur.load(a.log_k + tn * DK + p.row0, nullptr, a.log_alpha + tn * DK + p.row0, a.log_v + tn * DV + p.col0,
-               a.log_beta + tn);
-    tok = tn;
-  }
+  replay_log<DK, DV, TIn, R>(S, a.log_k, a.log_v, a.log_alpha, a.log_beta, (size_t)p.b * a.Tmax * a.H + p.h, a.H, n,
+                             p.row0, p.col0);
   store_tile<R, DV>(sp, S);
   if (p.h == 0 && p.slice == 0 && p.lane == 0) a.pos[p.b] += n;
 }
@@ -297,7 +260,7 @@ hipError_t launch_commit(const kda_shape& s, int32_t T, float* state, int64_t* p
     typedef typename C::TIn TIn;
     constexpr int DK = C::DK, DV = C::DV;
     CommitArgs<TIn> a{state, pos, (const TIn*)log.k, (const TIn*)log.v, log.alpha, log.beta, accepted, dev_err,
-                      s.H, T};
+                      s.H, T, log.T_max};
     commit_kernel<DK, DV, TIn><<<grid_of<DK, DV>(s), kWave * waves_per_group<DV>(), 0, st>>>(a);
   });
   return hipGetLastError();

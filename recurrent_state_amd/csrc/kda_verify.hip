@@ -51,7 +51,7 @@ constexpr int kGroup = 4;  // tokens per group
 
 template <typename TIn>
 struct VerifyArgs {
-  const float* state;
+  float* state;  // written only by the fused commit + verify
   const TIn* q;
   const TIn* k;
   const TIn* v;
@@ -63,8 +63,14 @@ struct VerifyArgs {
   float* log_alpha;
   float* log_beta;
   int32_t H;
-  int32_t T;
+  int32_t T;      // tokens verified by this call
+  int32_t Tmax;   // token rows per sequence in the log
   float scale;
+  // Fused commit + verify only: commit of the pending T_pend logged tokens.
+  int64_t* pos;
+  const int32_t* accepted;
+  int32_t* dev_err;
+  int32_t T_pend;
 };
 
 // Per-group LDS.  Key-channel vectors are stored by row group with a padded
@@ -186,7 +192,7 @@ template <typename TIn, int DK, int DV>
 struct Streams {
   rsrc_t k, q, alpha, v, o, log_k, log_v, log_alpha;
   int sk_in, sk_f32, sv_in, sv_f32;  // bytes between consecutive tokens
-  __device__ __forceinline__ Streams(const VerifyArgs<TIn>& a, size_t tok0, int T) {
+  __device__ __forceinline__ Streams(const VerifyArgs<TIn>& a, size_t tok0, size_t tok0_log, int T) {
     const size_t span = (size_t)(T - 1) * a.H;  // rows from the first to the last token
     const size_t es = sizeof(TIn);
     k = make_rsrc(a.k + tok0 * DK, (uint32_t)((span * DK + DK) * es));
@@ -194,9 +200,9 @@ struct Streams {
     alpha = make_rsrc(a.alpha + tok0 * DK, (uint32_t)((span * DK + DK) * 4));
     v = make_rsrc(a.v + tok0 * DV, (uint32_t)((span * DV + DV) * es));
     o = make_rsrc(a.o + tok0 * DV, (uint32_t)((span * DV + DV) * 4));
-    log_k = make_rsrc(a.log_k + tok0 * DK, (uint32_t)((span * DK + DK) * es));
-    log_v = make_rsrc(a.log_v + tok0 * DV, (uint32_t)((span * DV + DV) * es));
-    log_alpha = make_rsrc(a.log_alpha + tok0 * DK, (uint32_t)((span * DK + DK) * 4));
+    log_k = make_rsrc(a.log_k + tok0_log * DK, (uint32_t)((span * DK + DK) * es));
+    log_v = make_rsrc(a.log_v + tok0_log * DV, (uint32_t)((span * DV + DV) * es));
+    log_alpha = make_rsrc(a.log_alpha + tok0_log * DK, (uint32_t)((span * DK + DK) * 4));
     sk_in = a.H * DK * (int)es;
     sk_f32 = a.H * DK * 4;
     sv_in = a.H * DV * (int)es;
@@ -210,7 +216,7 @@ struct Streams {
 template <int DK, int DV, typename TIn, bool MULTI, typename LoadState>
 __device__ __forceinline__ void verify_group(const VerifyArgs<TIn>& a, const Streams<TIn, DK, DV>& st,
                                              VerifyLds<DK>& L, float (&S)[DK / kRowGroups][4], int t0, int G,
-                                             size_t tok0, int lane, int wave, bool first,
+                                             size_t tok0, size_t tok0_log, int lane, int wave, bool first,
                                              const LoadState& load_state) {
   constexpr int NW = DV / kSliceCols;
   constexpr int R = DK / kRowGroups;
@@ -329,7 +335,7 @@ __device__ __forceinline__ void verify_group(const VerifyArgs<TIn>& a, const Str
 #pragma unroll
     for (int r = 1; r < kGroup; ++r)
       if (lane == r) bl = bt[r];
-    a.log_beta[tok0 + (size_t)(t0 + lane) * a.H] = bl;
+    a.log_beta[tok0_log + (size_t)(t0 + lane) * a.H] = bl;
   }
   __syncthreads();
 
@@ -423,7 +429,10 @@ __device__ __forceinline__ void verify_group(const VerifyArgs<TIn>& a, const Str
 
 // MULTI: T may exceed one group (the state is advanced in registers between
 // groups); otherwise T <= kGroup and the state dies after the projections.
-template <int DK, int DV, typename TIn, bool MULTI>
+// COMMIT: first replay the accepted prefix of the pending verify (the commit
+// step, with the decode step's token loop), write the committed state and
+// position, then verify the new tokens from the state still in registers.
+template <int DK, int DV, typename TIn, bool MULTI, bool COMMIT>
 __global__ void __launch_bounds__(kWave * (DV / kSliceCols)) verify_chunk_kernel(VerifyArgs<TIn> a) {
   constexpr int R = DK / kRowGroups;
   __shared__ __align__(16) VerifyLds<DK> L;
@@ -433,13 +442,15 @@ __global__ void __launch_bounds__(kWave * (DV / kSliceCols)) verify_chunk_kernel
   const int bh = blockIdx.x;
   const int b = bh / a.H, h = bh - b * a.H;
   const int T = a.T;
-  const size_t tok0 = (size_t)b * T * a.H + h;  // [B][T][H] row of token 0
-  const Streams<TIn, DK, DV> st(a, tok0, T);
+  const size_t tok0 = (size_t)b * T * a.H + h;         // [B][T][H] row of input token 0
+  const size_t tok0_log = (size_t)b * a.Tmax * a.H + h;  // [B][T_max][H] row of log token 0
+  const Streams<TIn, DK, DV> st(a, tok0, tok0_log, T);
 
-  // The lane's state tile, loaded once (inside the first group).
+  // The lane's state tile, loaded once.
   float S[R][4];
   const rsrc_t rs = make_rsrc(a.state + (size_t)bh * DK * DV, DK * DV * 4);
-  const int svo = ((rg * R) * DV + wave * kSliceCols + cg * 4) * 4;
+  const int row0 = rg * R, col0 = wave * kSliceCols + cg * 4;
+  const int svo = (row0 * DV + col0) * 4;
   auto load_state = [&](float (&St)[R][4]) {
 #pragma unroll
     for (int r = 0; r < R; ++r) {
@@ -450,43 +461,87 @@ __global__ void __launch_bounds__(kWave * (DV / kSliceCols)) verify_chunk_kernel
       St[r][3] = __uint_as_float(w.w);
     }
   };
-  if (MULTI) {
+  auto no_load = [](float (&)[R][4]) {};
+  if (COMMIT) {
+    load_state(S);
+    if (a.T_pend > 0) {
+      const int n = a.accepted[b];
+      if (n < 0 || n > a.T_pend) {
+        if (h == 0 && wave == 0 && lane == 0) atomicOr(a.dev_err, KDA_DEV_ERR_ACCEPTED);
+      } else if (n > 0) {
+        replay_log<DK, DV, TIn, R>(S, a.log_k, a.log_v, a.log_alpha, a.log_beta, tok0_log, a.H, n, row0, col0);
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+          const u32x4 w = {__float_as_uint(S[r][0]), __float_as_uint(S[r][1]), __float_as_uint(S[r][2]),
+                           __float_as_uint(S[r][3])};
+          __builtin_amdgcn_raw_buffer_store_b128(w, rs, svo, r * DV * 4, 0);
+        }
+        if (h == 0 && wave == 0 && lane == 0) a.pos[b] += n;
+      }
+      __syncthreads();  // every wave has read the pending log rows before the verify rewrites them
+    }
+    if (MULTI) {
+      for (int t0 = 0; t0 < T; t0 += kGroup)
+        verify_group<DK, DV, TIn, true>(a, st, L, S, t0, min(kGroup, T - t0), tok0, tok0_log, lane, wave, t0 == 0,
+                                        no_load);
+    } else {
+      verify_group<DK, DV, TIn, false>(a, st, L, S, 0, T, tok0, tok0_log, lane, wave, true, no_load);
+    }
+  } else if (MULTI) {
     for (int t0 = 0; t0 < T; t0 += kGroup)
-      verify_group<DK, DV, TIn, true>(a, st, L, S, t0, min(kGroup, T - t0), tok0, lane, wave, t0 == 0, load_state);
+      verify_group<DK, DV, TIn, true>(a, st, L, S, t0, min(kGroup, T - t0), tok0, tok0_log, lane, wave, t0 == 0,
+                                      load_state);
   } else {
-    verify_group<DK, DV, TIn, false>(a, st, L, S, 0, T, tok0, lane, wave, true, load_state);
+    verify_group<DK, DV, TIn, false>(a, st, L, S, 0, T, tok0, tok0_log, lane, wave, true, load_state);
   }
 }
 
-template <int DK, int DV, typename TIn>
-void launch_cfg(const kda_shape& s, int32_t T, const float* state, TokenInputs in, float* o, LogPtrs log,
-                hipStream_t st) {
-  VerifyArgs<TIn> a{state, (const TIn*)in.q, (const TIn*)in.k, (const TIn*)in.v, in.alpha, in.beta, o,
-                    (TIn*)log.k, (TIn*)log.v, log.alpha, log.beta, s.H, T, s.scale};
-  const dim3 grid(s.B * s.H), block(kWave * (DV / kSliceCols));
-  if (T <= kGroup)
-    verify_chunk_kernel<DK, DV, TIn, false><<<grid, block, 0, st>>>(a);
+template <int DK, int DV, typename TIn, bool COMMIT>
+void launch_cfg(const VerifyArgs<TIn>& a, int32_t B, hipStream_t st) {
+  const dim3 grid(B * a.H), block(kWave * (DV / kSliceCols));
+  if (a.T <= kGroup)
+    verify_chunk_kernel<DK, DV, TIn, false, COMMIT><<<grid, block, 0, st>>>(a);
   else
-    verify_chunk_kernel<DK, DV, TIn, true><<<grid, block, 0, st>>>(a);
+    verify_chunk_kernel<DK, DV, TIn, true, COMMIT><<<grid, block, 0, st>>>(a);
 }
 
-template <typename TIn>
-void launch_dtype(const kda_shape& s, int32_t T, const float* state, TokenInputs in, float* o, LogPtrs log,
-                  hipStream_t st) {
-  if (s.dk == 128 && s.dv == 128) launch_cfg<128, 128, TIn>(s, T, state, in, o, log, st);
-  else if (s.dk == 128) launch_cfg<128, 64, TIn>(s, T, state, in, o, log, st);
-  else if (s.dv == 128) launch_cfg<64, 128, TIn>(s, T, state, in, o, log, st);
-  else launch_cfg<64, 64, TIn>(s, T, state, in, o, log, st);
+template <typename TIn, bool COMMIT>
+void launch_shape(const kda_shape& s, const VerifyArgs<TIn>& a, hipStream_t st) {
+  if (s.dk == 128 && s.dv == 128) launch_cfg<128, 128, TIn, COMMIT>(a, s.B, st);
+  else if (s.dk == 128) launch_cfg<128, 64, TIn, COMMIT>(a, s.B, st);
+  else if (s.dv == 128) launch_cfg<64, 128, TIn, COMMIT>(a, s.B, st);
+  else launch_cfg<64, 64, TIn, COMMIT>(a, s.B, st);
+}
+
+template <typename TIn, bool COMMIT>
+void launch_any(const kda_shape& s, int32_t T_pend, int32_t T, float* state, int64_t* pos, const int32_t* accepted,
+                int32_t* dev_err, TokenInputs in, float* o, LogPtrs log, hipStream_t st) {
+  const VerifyArgs<TIn> a{state,   (const TIn*)in.q, (const TIn*)in.k, (const TIn*)in.v, in.alpha, in.beta, o,
+                          (TIn*)log.k, (TIn*)log.v, log.alpha, log.beta, s.H, T, log.T_max, s.scale, pos, accepted,
+                          dev_err, T_pend};
+  launch_shape<TIn, COMMIT>(s, a, st);
 }
 
 }  // namespace
 
 hipError_t launch_verify(const kda_shape& s, int32_t T, const float* state, TokenInputs in, float* o, LogPtrs log,
                          hipStream_t st) {
+  // The verify-only kernel never writes through `state`.
+  float* sp = const_cast<float*>(state);
   if (s.in_dtype == KDA_BF16)
-    launch_dtype<bf16_t>(s, T, state, in, o, log, st);
+    launch_any<bf16_t, false>(s, 0, T, sp, nullptr, nullptr, nullptr, in, o, log, st);
   else
-    launch_dtype<float>(s, T, state, in, o, log, st);
+    launch_any<float, false>(s, 0, T, sp, nullptr, nullptr, nullptr, in, o, log, st);
+  return hipGetLastError();
+}
+
+hipError_t launch_commit_verify(const kda_shape& s, int32_t T_pend, int32_t T, float* state, int64_t* pos,
+                                const int32_t* accepted, int32_t* dev_err, TokenInputs in, float* o, LogPtrs log,
+                                hipStream_t st) {
+  if (s.in_dtype == KDA_BF16)
+    launch_any<bf16_t, true>(s, T_pend, T, state, pos, accepted, dev_err, in, o, log, st);
+  else
+    launch_any<float, true>(s, T_pend, T, state, pos, accepted, dev_err, in, o, log, st);
   return hipGetLastError();
 }
 

@@ -38,7 +38,7 @@ def declared_functions():
 
 def test_exports_every_declared_function(k):
     names = declared_functions()
-    assert len(names) >= 12
+    assert len(names) >= 13
     lib = ctypes.CDLL(k.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), f"{n} declared in kda.h but not exported"
@@ -108,6 +108,35 @@ def test_verify_commit_validation(k):
     assert com(pend, err=None) == NULL
     assert com(pend, acc=P(0x10002)) == ALIGN
     assert pend.pending_T == 3, "a rejected commit must not consume the pending verify"
+
+
+def test_commit_verify_validation(k):
+    L = k.lib()
+    s = shape(k)
+    need = k.log_bytes(s, 4)
+
+    def cv(T, lg, pos=GOOD, acc=GOOD, err=GOOD, st=GOOD):
+        return L.kda_commit_verify(ctypes.byref(s), T, st, pos, GOOD, GOOD, GOOD, GOOD, GOOD, GOOD,
+                                   ctypes.byref(lg) if lg is not None else None, acc, err, None)
+
+    log = k._lib._Log(0x100000, need, 4, 2)
+    assert cv(1, None) == NULL
+    assert cv(0, log) == SHAPE
+    assert cv(5, log) == SHAPE                                    # T > T_max
+    assert cv(2, log, pos=None) == NULL
+    assert cv(2, log, pos=P(0x10004)) == ALIGN
+    assert cv(2, log, acc=None) == NULL                           # a verify is pending: counts needed
+    assert cv(2, log, err=None) == NULL
+    assert cv(2, log, acc=P(0x10002)) == ALIGN
+    assert cv(2, log, st=None) == NULL
+    assert log.pending_T == 2, "a rejected call must not touch the pending count"
+    assert cv(2, k._lib._Log(0x100000, need - 256, 4, 0)) == SHAPE
+    # An empty batch needs no buffers and moves the log to the new pending count.
+    empty = shape(k, B=0)
+    lg0 = k._lib._Log(0x100000, k.log_bytes(empty, 4) or 256, 4, 3)
+    assert L.kda_commit_verify(ctypes.byref(empty), 4, None, None, None, None, None, None, None, None,
+                               ctypes.byref(lg0), None, None, None) == OK
+    assert lg0.pending_T == 4
 
 
 def test_snapshot_restore_validation(k):

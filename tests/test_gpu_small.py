@@ -349,3 +349,107 @@ def test_prefill_chunked_then_decode_continues():
     S_ref, o_ref = ko.decode(S0, inp, spec.scale)
     assert_parity(torch.cat([o1, o2, o3], dim=1).cpu().numpy(), o_ref, S.cpu().numpy(), S_ref,
                   "two chunked prefills + decode")
+
+
+def _log_rows(log, B, T, H, dk, dv, es):
+    """The filled rows (t < T) of the four log regions as int tensors, for bitwise comparison."""
+    n = log.buf.numel()
+    Tm = log.c.T_max
+    r = lambda x: (x + 255) // 256 * 256  # noqa: E731
+    tok = B * Tm * H
+    offs = [0]
+    offs.append(r(offs[0] + tok * dk * es))
+    offs.append(r(offs[1] + tok * dv * es))
+    offs.append(r(offs[2] + tok * dk * 4))
+    assert r(offs[3] + tok * 4) <= n
+    out = []
+    for off, width, e in ((offs[0], dk, es), (offs[1], dv, es), (offs[2], dk, 4), (offs[3], 1, 4)):
+        reg = log.buf[off:off + tok * width * e].view(B, Tm, H, width * e)[:, :T]
+        out.append(reg.clone())
+    return out
+
+
+@pytest.mark.parametrize("dk,dv,dt", SHAPES)
+@pytest.mark.parametrize("T1,T2", [(3, 3), (4, 2), (2, 5), (8, 4)])
+def test_commit_verify_equals_commit_then_verify(dk, dv, dt, T1, T2):
+    spec = spec_for(dk, dv, dt, tag=114)
+    B = 3
+    say(f"commit_verify dk={dk} dv={dv} {dt} T1={T1} T2={T2}")
+    S0 = synth.initial_state(spec, B)
+    inp = synth.token_inputs(spec, B, T1 + T2)
+    d = dev_inputs(inp)
+    r1 = token_slice(d, 0, T1)
+    r2 = {k_: v_.contiguous() for k_, v_ in token_slice(d, T1, T1 + T2).items()}
+    r1 = {k_: v_.contiguous() for k_, v_ in r1.items()}
+    acc = torch.tensor([T1, 0, min(2, T1)], dtype=torch.int32, device="cuda")
+    outs = {}
+    for path in ("separate", "fused"):
+        S = dev_tensor(S0)
+        pos = torch.tensor([5, 0, 2], dtype=torch.int64, device="cuda")
+        log = kda.InputLog(S, T_max=8, in_dtype=d["q"].dtype)
+        err = torch.zeros(1, dtype=torch.int32, device="cuda")
+        o1 = torch.empty((B, T1, spec.H, dv), dtype=torch.float32, device="cuda")
+        o2 = torch.empty((B, T2, spec.H, dv), dtype=torch.float32, device="cuda")
+        kda.verify(S, r1["q"], r1["k"], r1["v"], r1["alpha"], r1["beta"], o1, log)
+        if path == "separate":
+            kda.commit(S, pos, log, acc, err)
+            kda.verify(S, r2["q"], r2["k"], r2["v"], r2["alpha"], r2["beta"], o2, log)
+        else:
+            kda.commit_verify(S, pos, r2["q"], r2["k"], r2["v"], r2["alpha"], r2["beta"], o2, log, acc, err)
+            assert kda.last_variant() == "commit_verify" and log.pending_T == T2
+        S_mid = S.clone()
+        rows = _log_rows(log, B, T2, spec.H, dk, dv, 2 if dt == "bf16" else 4)
+        # Commit the second round too (a different count per sequence).
+        acc2 = torch.tensor([1, T2, 0], dtype=torch.int32, device="cuda")
+        kda.commit(S, pos, log, acc2, err)
+        torch.cuda.synchronize()
+        assert err.item() == 0
+        outs[path] = (bits(S_mid), bits(o2), rows, bits(S), pos.clone())
+    a, b_ = outs["separate"], outs["fused"]
+    assert torch.equal(a[0], b_[0]), "committed state differs"
+    assert torch.equal(a[1], b_[1]), "verify outputs differ"
+    for x, y in zip(a[2], b_[2]):
+        assert torch.equal(x, y), "log rows differ"
+    assert torch.equal(a[3], b_[3]) and torch.equal(a[4], b_[4])
+    # And against the oracle: the second verify's outputs follow the accepted prefix of round 1.
+    for bi in range(B):
+        a1 = int(acc[bi])
+        tok = {k_: np.concatenate([v_[bi:bi + 1, :a1], v_[bi:bi + 1, T1:T1 + T2]], axis=1) for k_, v_ in inp.items()}
+        _, o_ref = ko.decode(S0[bi:bi + 1], tok, spec.scale)
+        o_gpu = b_[1].view(torch.float32)[bi:bi + 1].cpu().numpy()
+        assert_parity(o_gpu, o_ref[:, a1:], what=f"commit_verify seq {bi}")
+
+
+def test_commit_verify_bad_count_and_nothing_pending():
+    spec = spec_for(128, 128, "bf16", tag=115)
+    B, T = 2, 4
+    S0 = synth.initial_state(spec, B)
+    inp = synth.token_inputs(spec, B, 2 * T)
+    d = dev_inputs(inp)
+    r1 = {k_: v_.contiguous() for k_, v_ in token_slice(d, 0, T).items()}
+    r2 = {k_: v_.contiguous() for k_, v_ in token_slice(d, T, 2 * T).items()}
+    S = dev_tensor(S0)
+    S_keep = S.clone()
+    pos = torch.zeros(B, dtype=torch.int64, device="cuda")
+    log = kda.InputLog(S, T_max=T)
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    o1 = torch.empty((B, T, spec.H, 128), dtype=torch.float32, device="cuda")
+    o_ref = torch.empty_like(o1)
+    # Nothing pending: a plain verify (no accepted / dev_err needed).
+    kda.commit_verify(S, pos, r1["q"], r1["k"], r1["v"], r1["alpha"], r1["beta"], o1, log)
+    log2 = kda.InputLog(S, T_max=T)
+    kda.verify(S, r1["q"], r1["k"], r1["v"], r1["alpha"], r1["beta"], o_ref, log2)
+    assert torch.equal(bits(o1), bits(o_ref)) and torch.equal(bits(S), bits(S_keep))
+    assert pos.cpu().tolist() == [0, 0]
+    # Count out of range for sequence 1: flagged, sequence 1 untouched, verify still runs from it.
+    acc = torch.tensor([2, T + 1], dtype=torch.int32, device="cuda")
+    o2 = torch.empty_like(o1)
+    kda.commit_verify(S, pos, r2["q"], r2["k"], r2["v"], r2["alpha"], r2["beta"], o2, log, acc, err)
+    torch.cuda.synchronize()
+    assert err.item() & kda.DEV_ERR_ACCEPTED
+    assert torch.equal(bits(S[1]), bits(S_keep[1])) and not torch.equal(bits(S[0]), bits(S_keep[0]))
+    assert pos.cpu().tolist() == [2, 0]
+    o3 = torch.empty_like(o1)
+    log3 = kda.InputLog(S, T_max=T)
+    kda.verify(S, r2["q"], r2["k"], r2["v"], r2["alpha"], r2["beta"], o3, log3)
+    assert torch.equal(bits(o2), bits(o3))
