@@ -100,3 +100,45 @@ def test_verify_commit_graph_replays_match_eager():
         S_ref, o_ref, pos_ref = ref[r]
         assert torch.equal(bits(SB), S_ref) and torch.equal(bits(oB), o_ref) and torch.equal(posB, pos_ref), r
     assert errA.item() == 0 and errB.item() == 0
+
+
+def test_commit_verify_graph_replays_match_eager():
+    # Round r commits counts[r - 1] of the previous round and verifies new drafts;
+    # one captured fused round is replayed with new counts written in between.
+    B, T, rounds = 4, 3, 4
+    say("graph: fused commit + verify")
+    S0 = dev_tensor(synth.initial_state(SPEC, B))
+    d = {k: dev_tensor(v) for k, v in synth.token_inputs(SPEC, B, T).items()}
+    counts = [[3, 0, 1, 2], [0, 0, 0, 0], [2, 3, 3, 1], [1, 2, 0, 3]]
+    SA = S0.clone()
+    posA = torch.zeros(B, dtype=torch.int64, device="cuda")
+    logA = kda.InputLog(SA, T_max=T)
+    errA = torch.zeros(1, dtype=torch.int32, device="cuda")
+    oA = torch.empty((B, T, SPEC.H, 128), device="cuda")
+    kda.commit_verify(SA, posA, d["q"], d["k"], d["v"], d["alpha"], d["beta"], oA, logA)
+    ref = []
+    for r in range(rounds):
+        kda.commit_verify(SA, posA, d["q"], d["k"], d["v"], d["alpha"], d["beta"], oA, logA,
+                          torch.tensor(counts[r], dtype=torch.int32, device="cuda"), errA)
+        ref.append((bits(SA).clone(), bits(oA).clone(), posA.clone()))
+    SB = S0.clone()
+    posB = torch.zeros(B, dtype=torch.int64, device="cuda")
+    logB = kda.InputLog(SB, T_max=T)
+    errB = torch.zeros(1, dtype=torch.int32, device="cuda")
+    oB = torch.empty_like(oA)
+    acc = torch.zeros(B, dtype=torch.int32, device="cuda")
+    kda.commit_verify(SB, posB, d["q"], d["k"], d["v"], d["alpha"], d["beta"], oB, logB)   # round 0, eager
+    plan = kda.CommitVerifyPlan(SB, posB, d["q"], d["k"], d["v"], d["alpha"], d["beta"], oB, logB, acc, errB)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        plan()
+    assert logB.pending_T == T
+    for r in range(rounds):
+        acc.copy_(torch.tensor(counts[r], dtype=torch.int32))
+        g.replay()
+        junk = torch.randn(1000, device="cuda").cumsum(0)
+        torch.cuda.synchronize()
+        assert junk.numel() == 1000
+        S_ref, o_ref, pos_ref = ref[r]
+        assert torch.equal(bits(SB), S_ref) and torch.equal(bits(oB), o_ref) and torch.equal(posB, pos_ref), r
+    assert errA.item() == 0 and errB.item() == 0
