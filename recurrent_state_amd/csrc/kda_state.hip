@@ -72,12 +72,17 @@ struct PrefillArgs {
   float scale;
 };
 
-// Waves per workgroup: the column slices of one (sequence, head) are either
-// spread over independent one-wave workgroups (1) or kept together in one
-// workgroup on one CU (all slices).  The waves never synchronise either way.
-#ifndef KDA_STATE_WAVES
-#define KDA_STATE_WAVES 1
+// Waves per workgroup (WPG): the column slices of one (sequence, head) are
+// either spread over independent one-wave workgroups (1) or kept together in
+// one workgroup on one CU (all slices).  The waves never synchronise either
+// way.  Decode and commit pick WPG from the batch: one-wave workgroups start
+// faster when there are few of them; whole-state workgroups keep a state's
+// reads and writes on one CU, which measured 3.5 % faster at B = 64 and 2 %
+// at B = 16 (H = 32).
+#ifndef KDA_WIDE_WAVES
+#define KDA_WIDE_WAVES 2048
 #endif
+constexpr size_t kWideWaves = KDA_WIDE_WAVES;  // total slices from which whole-state workgroups are used
 // The recurrent prefill loads token t+1's inputs while token t computes (1),
 // or loads each token's inputs when it starts (0: fewer live registers).
 #ifndef KDA_PREFETCH_NEXT
@@ -96,17 +101,17 @@ struct PrefillArgs {
 
 constexpr int kXcds = 8;  // accelerator complex dies on MI355X, each with its own L2
 
-template <int DV>
+template <int DV, int WPG>
 constexpr int waves_per_group() {
-  return KDA_STATE_WAVES < DV / kSliceCols ? KDA_STATE_WAVES : DV / kSliceCols;
+  return WPG < DV / kSliceCols ? WPG : DV / kSliceCols;
 }
 
 // Where a wave sits: its (sequence, head) index and its lane's rows/columns.
-template <int DK, int DV>
+template <int DK, int DV, int WPG_ = 1>
 struct Place {
   static constexpr int R = DK / kRowGroups;
   static constexpr int SLICES = DV / kSliceCols;
-  static constexpr int WPG = waves_per_group<DV>();
+  static constexpr int WPG = waves_per_group<DV, WPG_>();
   int bh, b, h, slice, rg, cg, row0, col0, lane;
   __device__ __forceinline__ Place(int H) {
     lane = threadIdx.x & (kWave - 1);
@@ -134,9 +139,9 @@ struct Place {
   __device__ __forceinline__ size_t tile_off() const { return (size_t)row0 * DV + col0; }
 };
 
-template <int DK, int DV, typename TIn>
-__global__ void KDA_OCCUPANCY __launch_bounds__(kWave * waves_per_group<DV>()) decode_kernel(StepArgs<TIn> a) {
-  typedef Place<DK, DV> P;
+template <int DK, int DV, typename TIn, int WPG>
+__global__ void KDA_OCCUPANCY __launch_bounds__((kWave * waves_per_group<DV, WPG>())) decode_kernel(StepArgs<TIn> a) {
+  typedef Place<DK, DV, WPG> P;
   constexpr int R = P::R;
   const P p(a.H);
   float* sp = a.state + (size_t)p.bh * DK * DV + p.tile_off();
@@ -152,9 +157,9 @@ __global__ void KDA_OCCUPANCY __launch_bounds__(kWave * waves_per_group<DV>()) d
   if (p.h == 0 && p.slice == 0 && p.lane == 0) a.pos[p.b] += 1;
 }
 
-template <int DK, int DV, typename TIn>
-__global__ void KDA_OCCUPANCY __launch_bounds__(kWave * waves_per_group<DV>()) commit_kernel(CommitArgs<TIn> a) {
-  typedef Place<DK, DV> P;
+template <int DK, int DV, typename TIn, int WPG>
+__global__ void KDA_OCCUPANCY __launch_bounds__((kWave * waves_per_group<DV, WPG>())) commit_kernel(CommitArgs<TIn> a) {
+  typedef Place<DK, DV, WPG> P;
   constexpr int R = P::R;
   const P p(a.H);
   const int n = a.accepted[p.b];
@@ -173,8 +178,8 @@ __global__ void KDA_OCCUPANCY __launch_bounds__(kWave * waves_per_group<DV>()) c
 }
 
 template <int DK, int DV, typename TIn>
-__global__ void KDA_OCCUPANCY __launch_bounds__(kWave * waves_per_group<DV>()) prefill_recurrent_kernel(PrefillArgs<TIn> a) {
-  typedef Place<DK, DV> P;
+__global__ void KDA_OCCUPANCY __launch_bounds__(kWave) prefill_recurrent_kernel(PrefillArgs<TIn> a) {
+  typedef Place<DK, DV, 1> P;
   constexpr int R = P::R;
   const P p(a.H);
   const bool owner = p.h == 0 && p.slice == 0 && p.lane == 0;  // the one writer of positions
@@ -213,9 +218,15 @@ __global__ void KDA_OCCUPANCY __launch_bounds__(kWave * waves_per_group<DV>()) p
   if (owner) a.pos[p.b] = pos0 + a.L;
 }
 
-template <int DK, int DV>
+template <int DK, int DV, int WPG>
 dim3 grid_of(const kda_shape& s) {
-  return dim3((unsigned)((size_t)s.B * s.H * (DV / kSliceCols) / waves_per_group<DV>()));
+  return dim3((unsigned)((size_t)s.B * s.H * (DV / kSliceCols) / waves_per_group<DV, WPG>()));
+}
+
+// Total one-wave slices of a launch (one per 32 value columns of every state).
+template <int DV>
+size_t slice_waves(const kda_shape& s) {
+  return (size_t)s.B * s.H * (DV / kSliceCols);
 }
 
 template <int DK_, int DV_, typename TIn_>
@@ -248,7 +259,10 @@ hipError_t launch_decode(const kda_shape& s, float* state, int64_t* pos, TokenIn
     constexpr int DK = C::DK, DV = C::DV;
     StepArgs<TIn> a{state, pos, (const TIn*)in.q, (const TIn*)in.k, (const TIn*)in.v, in.alpha, in.beta, o,
                     s.H, s.scale};
-    decode_kernel<DK, DV, TIn><<<grid_of<DK, DV>(s), kWave * waves_per_group<DV>(), 0, st>>>(a);
+    if (slice_waves<DV>(s) >= kWideWaves)
+      decode_kernel<DK, DV, TIn, 4><<<grid_of<DK, DV, 4>(s), kWave * waves_per_group<DV, 4>(), 0, st>>>(a);
+    else
+      decode_kernel<DK, DV, TIn, 1><<<grid_of<DK, DV, 1>(s), kWave, 0, st>>>(a);
   });
   return hipGetLastError();
 }
@@ -261,7 +275,10 @@ hipError_t launch_commit(const kda_shape& s, int32_t T, float* state, int64_t* p
     constexpr int DK = C::DK, DV = C::DV;
     CommitArgs<TIn> a{state, pos, (const TIn*)log.k, (const TIn*)log.v, log.alpha, log.beta, accepted, dev_err,
                       s.H, T, log.T_max};
-    commit_kernel<DK, DV, TIn><<<grid_of<DK, DV>(s), kWave * waves_per_group<DV>(), 0, st>>>(a);
+    if (slice_waves<DV>(s) >= kWideWaves)
+      commit_kernel<DK, DV, TIn, 4><<<grid_of<DK, DV, 4>(s), kWave * waves_per_group<DV, 4>(), 0, st>>>(a);
+    else
+      commit_kernel<DK, DV, TIn, 1><<<grid_of<DK, DV, 1>(s), kWave, 0, st>>>(a);
   });
   return hipGetLastError();
 }
@@ -275,7 +292,7 @@ hipError_t launch_prefill_recurrent(const kda_shape& s, int32_t L, float* state,
     constexpr int DK = C::DK, DV = C::DV;
     PrefillArgs<TIn> a{state, pos, (const TIn*)in.q, (const TIn*)in.k, (const TIn*)in.v, in.alpha, in.beta, o,
                        ckpt_slots, slot_states, slot_pos, dev_err, s.H, L, ckpt_every, n_slots, s.scale};
-    prefill_recurrent_kernel<DK, DV, TIn><<<grid_of<DK, DV>(s), kWave * waves_per_group<DV>(), 0, st>>>(a);
+    prefill_recurrent_kernel<DK, DV, TIn><<<grid_of<DK, DV, 1>(s), kWave, 0, st>>>(a);
   });
   return hipGetLastError();
 }

@@ -453,3 +453,32 @@ def test_commit_verify_bad_count_and_nothing_pending():
     log3 = kda.InputLog(S, T_max=T)
     kda.verify(S, r2["q"], r2["k"], r2["v"], r2["alpha"], r2["beta"], o3, log3)
     assert torch.equal(bits(o2), bits(o3))
+
+
+def test_workgroup_shapes_bit_identical():
+    # Large batches run decode and commit with whole-state workgroups, small
+    # ones with one-wave workgroups; the lane arithmetic is the same, so a
+    # sequence's results do not depend on the batch it ran in, and commit(a)
+    # equals a decode steps in both shapes.
+    spec = synth.ConfigSpec("wg", 117, (16,), 32, 128, 128, "bf16", "softplus", "normal", 0)
+    Bbig, T = 16, 3                      # 16 x 32 x 4 = 2,048 slices: whole-state workgroups
+    S0 = synth.initial_state(spec, Bbig)
+    inp = synth.token_inputs(spec, Bbig, T)
+    d = dev_inputs(inp)
+    res = {}
+    for B in (Bbig, 2):
+        dd = {k_: v_[:B].contiguous() for k_, v_ in d.items()}
+        S = dev_tensor(S0[:B])
+        pos = torch.zeros(B, dtype=torch.int64, device="cuda")
+        o_dec = decode_run(S, pos, dd)
+        Sc = dev_tensor(S0[:B])
+        posc = torch.zeros(B, dtype=torch.int64, device="cuda")
+        log = kda.InputLog(Sc, T_max=T)
+        o_v = torch.empty((B, T, spec.H, 128), dtype=torch.float32, device="cuda")
+        kda.verify(Sc, dd["q"], dd["k"], dd["v"], dd["alpha"], dd["beta"], o_v, log)
+        err = torch.zeros(1, dtype=torch.int32, device="cuda")
+        kda.commit(Sc, posc, log, torch.full((B,), T, dtype=torch.int32, device="cuda"), err)
+        assert err.item() == 0
+        assert torch.equal(bits(Sc), bits(S)), f"commit({T}) != {T} decode steps at B={B}"
+        res[B] = (bits(S[:2]).clone(), bits(o_dec[:2]).clone())
+    assert torch.equal(res[2][0], res[Bbig][0]) and torch.equal(res[2][1], res[Bbig][1])
