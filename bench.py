@@ -46,6 +46,9 @@ LOG_BYTES = 128 * 2 * 2 + 128 * 4 + 4                                         # 
 PREFILL_BYTES_PER_TOKEN_HEAD = TOKEN_IN_BYTES + 128 * 4                       # + o; state and ckpts added per run
 
 
+MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 matrix peak
+
+
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
@@ -308,8 +311,38 @@ def bench_prefill(torch, kda, synth, device, variant, reps=2):
         best = tm.ms if best is None else min(best, tm.ms)
     th = B * L * H
     total_bytes = th * PREFILL_BYTES_PER_TOKEN_HEAD + B * H * STATE_BYTES * (2 + n_ck)
-    return {"variant": variant, "B": B, "L": L, "ms": best, "token_heads_per_s": th / (best / 1e3),
-            "hbm_frac": total_bytes / (best * 1e-3) / 1e9 / HBM_PEAK_GBS, "algorithmic_bytes": total_bytes}
+    row = {"variant": variant, "B": B, "L": L, "ms": best, "token_heads_per_s": th / (best / 1e3),
+           "hbm_frac": total_bytes / (best * 1e-3) / 1e9 / HBM_PEAK_GBS, "algorithmic_bytes": total_bytes}
+    if variant == "chunked":
+        C = spec.extra["chunk"]
+        chunks = B * H * (L // C)
+        alg, exe = prefill_flops_per_chunk(C, DK, DV)
+        row.update({"algorithmic_tflops": alg * chunks / (best * 1e-3) / 1e12,
+                    "mfma_executed_tflops": exe * chunks / (best * 1e-3) / 1e12,
+                    "mfma_executed_frac": exe * chunks / (best * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
+                    "mfma_algorithmic_frac": alg * chunks / (best * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS})
+    return row
+
+
+def prefill_flops_per_chunk(C, K, V):
+    """(algorithmic, executed) flops of one chunk of one (sequence, head).
+
+    Algorithmic: the chunk form's products counted once, triangular parts
+    halved -- A = Diag(beta) Kt Kh^T and P = Qt Kh^T (C^2/2 K each), the two
+    triangular applications of (I + A)^-1 (C^2/2 K and C^2/2 V), the inverse
+    (C^3/6), Kt S, Qt S and Kb^T E (C K V each) and P E (C^2/2 V); 2 flops per
+    multiply-add.  Executed: the v_mfma_f32_16x16x32_bf16 instructions the
+    chunked kernel issues (three per fp32-accurate product), 16,384 flops each.
+    """
+    alg = 2 * (3 * (C * C / 2) * K + (C * C / 2) * V + C ** 3 / 6 + 3 * C * K * V + (C * C / 2) * V)
+    NB, KB, MT = C // 16, K // 32, K // 16
+    NA = NB * (NB + 1) // 2
+    per_wave = 3 * (2 * NB * KB                                                     # X = [Kt; Qt] S
+                    + sum(1 + (i > 0) * ((i - 1) // 2 + 1) for i in range(NB))     # block solve
+                    + sum(mt // 2 + 1 for mt in range(NB))                         # P E
+                    + MT * (NB // 2))                                              # Kb^T E
+    mfmas = 3 * 2 * NA * KB + (V // 16) * per_wave                                 # + A and P tiles
+    return alg, mfmas * 16384
 
 
 def bench_snapshot_restore(torch, kda, synth, device, reps=20):
