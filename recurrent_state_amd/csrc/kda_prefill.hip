@@ -268,6 +268,10 @@ __global__ void __launch_bounds__(DV * 4) prefill_chunked_kernel(PrefillArgs<TIn
   auto misc = [&](int v) -> float& {
     return *reinterpret_cast<float*>(smem + L::off_kb + (v >> 2) * (L::RS_C * 2) + CH * 2 + (v & 3) * 4);
   };
+  // misc(v) .. misc(v + 3) for v = 0 mod 4: one 16-byte read (one row's padding).
+  auto misc4 = [&](int v) -> float4 {
+    return *reinterpret_cast<const float4*>(smem + L::off_kb + (v >> 2) * (L::RS_C * 2) + CH * 2);
+  };
   float* stot = reinterpret_cast<float*>(smem + L::off_tot);
 
   const int bh = blockIdx.x;
@@ -466,11 +470,14 @@ __global__ void __launch_bounds__(DV * 4) prefill_chunked_kernel(PrefillArgs<TIn
         int mt, nt;
         tri_tile(i < NA ? i : i - NA, mt, nt);
         const int tc = 16 * nt + l16;
+        float4 b4 = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (i < NA) b4 = misc4(16 * mt + 4 * g);  // wave-uniform branch
+        const float bt4[4] = {b4.x, b4.y, b4.z, b4.w};
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int tr = 16 * mt + 4 * g + r;
           if (i < NA) {
-            const float bta = misc(tr);  // read on every lane: no divergent LDS access
+            const float bta = bt4[r];
             const float av = tc < tr ? at[s_][r] * bta : 0.f;
             if (mt == nt) {
               adiag[(mt * 16 + 4 * g + r) * L::RS_D + l16] = av;
@@ -560,8 +567,10 @@ __global__ void __launch_bounds__(DV * 4) prefill_chunked_kernel(PrefillArgs<TIn
 #pragma unroll
     for (int i = 0; i < NB; ++i) {
       f32x4_t z;
+      const float4 b4 = misc4(16 * i + 4 * g);
+      const float bt4[4] = {b4.x, b4.y, b4.z, b4.w};
 #pragma unroll
-      for (int r = 0; r < 4; ++r) z[r] = misc(16 * i + 4 * g + r) * (vv[i][r] - xs[i][r]);
+      for (int r = 0; r < 4; ++r) z[r] = bt4[r] * (vv[i][r] - xs[i][r]);
       if (i > 0) {
         f32x4_t cs = zero4;
 #pragma unroll
@@ -589,8 +598,10 @@ __global__ void __launch_bounds__(DV * 4) prefill_chunked_kernel(PrefillArgs<TIn
     // 4f: S = Diag(2^g_n) S + Kb^T E.
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
+      const float4 g4 = misc4(CH + 16 * mt + 4 * g);
+      const float gn4[4] = {g4.x, g4.y, g4.z, g4.w};
 #pragma unroll
-      for (int r = 0; r < 4; ++r) st[mt][r] *= misc(CH + 16 * mt + 4 * g + r);
+      for (int r = 0; r < 4; ++r) st[mt][r] *= gn4[r];
 #pragma unroll
       for (int kb = 0; kb < NB / 2; ++kb)
         st[mt] = mfma3(plane_op2(kb_hi, kb_lo, 16 * mt + l16, L::RS_C, 32 * kb + 4 * g), eop[kb], st[mt]);
