@@ -95,16 +95,35 @@ def decode(S0, inp: dict, scale: float):
     return S, np.ascontiguousarray(o.transpose(0, 2, 1, 3))
 
 
-def verify(S_c, inp: dict, scale: float):
-    """Speculative verify of T draft tokens from the committed state.
+def verify(S_c, inp: dict, scale: float, draft_len=None):
+    """Speculative verify of draft tokens from the committed state.
 
     Runs the T tokens from ``S_c`` and returns (outputs [B][T][H][dv], log);
     ``S_c`` is not changed.  The log holds copies of the recurrent inputs the
     commit needs to replay the state (k, v, alpha, beta); q only shapes the
     outputs and is not logged.
+
+    ``draft_len`` (int [B], optional) gives sequence b only its first
+    ``draft_len[b]`` tokens (the rest of its T rows are padding): its outputs
+    from there on are NaN (not produced), and its logged length
+    (``log["len"]``) is that count.  A length outside [0, T] produces nothing,
+    logs length 0 and is reported in ``log["err"]``.  Outputs of the tokens a
+    sequence does verify are those of the full run, as token t's output depends
+    only on tokens up to t.
     """
     _, o = decode(S_c, inp, scale)
+    B, T = inp["k"].shape[:2]
     log = {name: np.array(inp[name], copy=True) for name in ("k", "v", "alpha", "beta")}
+    if draft_len is None:
+        log["len"] = np.full(B, T, np.int64)
+        log["err"] = np.zeros(B, bool)
+        return o, log
+    d = np.asarray(draft_len, dtype=np.int64)
+    err = (d < 0) | (d > T)
+    d = np.where(err, 0, d)
+    for b in range(B):
+        o[b, d[b]:] = np.nan
+    log["len"], log["err"] = d, err
     return o, log
 
 
@@ -113,15 +132,17 @@ def commit(S_c, pos, log: dict, accepted):
 
     For each sequence b, applies the first ``accepted[b]`` logged tokens to
     ``S_c[b]`` and advances ``pos[b]`` by that count.  A count outside
-    [0, T] leaves that sequence's state and position unchanged and is
-    reported in the returned error flags.
+    [0, n_b], with n_b the sequence's logged draft length (T when the log has
+    none), leaves that sequence's state and position unchanged and is reported
+    in the returned error flags.
     Returns (state f64, pos int64, err bool [B]).
     """
     S = widen(S_c).copy()
     pos = np.array(pos, dtype=np.int64, copy=True)
-    T = log["k"].shape[1]
+    B, T = log["k"].shape[:2]
+    n = np.asarray(log["len"]) if "len" in log else np.full(B, T)
     acc = np.asarray(accepted)
-    err = (acc < 0) | (acc > T)
+    err = (acc < 0) | (acc > n)
     for b in range(S.shape[0]):
         if err[b]:
             continue

@@ -65,6 +65,53 @@ def test_commit_rejects_out_of_range_count():
     assert np.array_equal(S[:2], ko.widen(S0[:2])) and pos.tolist() == [0, 0, 1]
 
 
+def test_varlen_verify_equals_verify_of_each_shorter_draft():
+    # Sequence b verifies only its first d_b tokens: its outputs there are those
+    # of a verify of exactly those tokens, and nothing is produced after them.
+    spec = SPEC
+    B, T = spec.B[0], 5
+    S0 = synth.initial_state(spec, B)
+    inp = synth.token_inputs(spec, B, T)
+    d = np.array([0, 5, 2], np.int32)
+    o, log = ko.verify(S0, inp, spec.scale, draft_len=d)
+    assert log["len"].tolist() == [0, 5, 2] and not log["err"].any()
+    for b in range(B):
+        if d[b]:
+            sub = {n: x[b:b + 1, :d[b]] for n, x in inp.items()}
+            o_b, _ = ko.verify(S0[b:b + 1], sub, spec.scale)
+            assert np.array_equal(o[b, :d[b]], o_b[0])
+        assert np.isnan(o[b, d[b]:]).all()
+
+
+def test_varlen_commit_is_bounded_by_each_draft_length():
+    spec = SPEC
+    B, T = spec.B[0], 4
+    S0 = synth.initial_state(spec, B)
+    inp = synth.token_inputs(spec, B, T)
+    _, log = ko.verify(S0, inp, spec.scale, draft_len=np.array([1, 3, 0], np.int32))
+    S, pos, err = ko.commit(S0, np.zeros(B, np.int64), log, np.array([2, 3, 1], np.int32))
+    assert err.tolist() == [True, False, True]
+    assert pos.tolist() == [0, 3, 0]
+    assert np.array_equal(S[0], ko.widen(S0[0])) and np.array_equal(S[2], ko.widen(S0[2]))
+    sub = {n: x[1:2, :3] for n, x in inp.items()}
+    S_ref, _ = ko.decode(S0[1:2], sub, spec.scale)
+    assert np.array_equal(S[1], S_ref[0])
+    _, pos, err = ko.commit(S0, np.zeros(B, np.int64), log, np.array([1, 0, 0], np.int32))
+    assert not err.any() and pos.tolist() == [1, 0, 0]
+
+
+def test_varlen_verify_rejects_out_of_range_length():
+    spec = SPEC
+    B, T = spec.B[0], 3
+    S0 = synth.initial_state(spec, B)
+    inp = synth.token_inputs(spec, B, T)
+    o, log = ko.verify(S0, inp, spec.scale, draft_len=np.array([-1, 4, 3], np.int32))
+    assert log["err"].tolist() == [True, True, False] and log["len"].tolist() == [0, 0, 3]
+    assert np.isnan(o[:2]).all() and not np.isnan(o[2]).any()
+    _, _, err = ko.commit(S0, np.zeros(B, np.int64), log, np.array([0, 1, 3], np.int32))
+    assert err.tolist() == [False, True, False]
+
+
 def test_snapshot_restore_roundtrip():
     r = np.random.default_rng(0)
     state = r.standard_normal((4, 2, 3, 5)).astype(np.float32)
