@@ -80,6 +80,7 @@ typedef enum kda_dtype { KDA_BF16 = 0, KDA_F32 = 1 } kda_dtype;
 /* Bits set in the device error word. */
 #define KDA_DEV_ERR_ACCEPTED 1 /* an accepted count was outside [0, T] */
 #define KDA_DEV_ERR_CKPT_SLOT 2 /* a checkpoint slot id was outside [0, n_slots) */
+#define KDA_DEV_ERR_DRAFT_LEN 4 /* a per-sequence draft length was outside [0, T] */
 
 /* Kernel variants reported by kda_last_variant(). */
 #define KDA_VARIANT_NONE 0
@@ -91,6 +92,8 @@ typedef enum kda_dtype { KDA_BF16 = 0, KDA_F32 = 1 } kda_dtype;
 #define KDA_VARIANT_PREFILL_RECURRENT 6
 #define KDA_VARIANT_PREFILL_CHUNKED 7
 #define KDA_VARIANT_COMMIT_VERIFY 8
+#define KDA_VARIANT_VERIFY_VARLEN 9
+#define KDA_VARIANT_COMMIT_VERIFY_VARLEN 10
 
 typedef struct kda_shape {
   int32_t B;        /* sequences in the batch */
@@ -106,13 +109,16 @@ typedef struct kda_shape {
  * Optimized Inference", paragraph on rejected draft tokens: the recurrent
  * inputs are stored and the accepted part is replayed from the last
  * committed state).  `dev` is a caller-owned device buffer of
- * kda_log_bytes(shape, T_max) bytes.  It holds four regions, each starting
+ * kda_log_bytes(shape, T_max) bytes.  It holds five regions, each starting
  * at a 256-byte boundary, in this order, with T_max token rows per sequence
- * of which the first T (of the pending verify) are filled:
+ * of which the first n_bh (of the pending verify) are filled:
  *   k      in_dtype [B][T_max][H][dk]
  *   v      in_dtype [B][T_max][H][dv]
  *   alpha  f32 [B][T_max][H][dk]
  *   beta   f32 [B][T_max][H]
+ *   n      i32 [B][H]   rows the pending verify filled for (b, h): T, or the
+ *                       sequence's draft length under the _varlen calls
+ * The device writes n; a commit accepts at most n_bh tokens of (b, h).
  * `pending_T` is host-side bookkeeping: kda_verify and kda_commit_verify set
  * it to T, kda_commit consumes it and resets it to 0.  Initialise it to 0.
  */
@@ -172,7 +178,8 @@ kda_status kda_verify(const kda_shape* shape, int32_t T, const float* state, con
  * Commit: for each sequence b, replays the first accepted[b] logged tokens
  * onto the committed state in place and adds accepted[b] to pos[b].
  * `accepted` is a device int32 [B].  A count of 0 leaves the state bytes
- * untouched; a count outside [0, pending_T] sets KDA_DEV_ERR_ACCEPTED in
+ * untouched; a count outside [0, n_bh] (the rows the pending verify logged
+ * for the sequence: pending_T, or its draft length) sets KDA_DEV_ERR_ACCEPTED in
  * *dev_err (device int32, sticky, never cleared by the library) and leaves
  * that sequence untouched.  The resulting state is bit-identical to
  * accepted[b] kda_decode_step calls on the same tokens.  Fails with
@@ -200,6 +207,32 @@ kda_status kda_commit(const kda_shape* shape, float* state, int64_t* pos, kda_lo
 kda_status kda_commit_verify(const kda_shape* shape, int32_t T, float* state, int64_t* pos, const void* q,
                              const void* k, const void* v, const float* alpha, const float* beta, float* o,
                              kda_log* log, const int32_t* accepted, int32_t* dev_err, void* stream);
+
+/*
+ * kda_verify with a draft length per sequence ("Hyper-optimizing Kimi K3 in
+ * vLLM", section 2 on bounding the scope: speculative decoding is validated
+ * over various draft lengths).  Inputs keep the [B][T][H][d] layout with T
+ * the longest draft; sequence b verifies only its first draft_len[b] tokens
+ * (device int32 [B], each in [0, T]; 0 = the sequence sits this round out).
+ * For t >= draft_len[b] nothing is read, o is not written and no log row is
+ * filled; the log records draft_len[b] so that a later commit accepts at most
+ * that many tokens of b (KDA_DEV_ERR_ACCEPTED above it).  A length outside
+ * [0, T] sets KDA_DEV_ERR_DRAFT_LEN in *dev_err and counts as 0.  draft_len
+ * and dev_err must not be NULL when B > 0.  Otherwise as kda_verify.
+ */
+kda_status kda_verify_varlen(const kda_shape* shape, int32_t T, const int32_t* draft_len, const float* state,
+                             const void* q, const void* k, const void* v, const float* alpha, const float* beta,
+                             float* o, kda_log* log, int32_t* dev_err, void* stream);
+
+/*
+ * kda_commit_verify whose new drafts have a length per sequence, as in
+ * kda_verify_varlen.  The commit half accepts at most the length logged by
+ * the pending verify; dev_err must not be NULL when B > 0.
+ */
+kda_status kda_commit_verify_varlen(const kda_shape* shape, int32_t T, const int32_t* draft_len, float* state,
+                                    int64_t* pos, const void* q, const void* k, const void* v, const float* alpha,
+                                    const float* beta, float* o, kda_log* log, const int32_t* accepted,
+                                    int32_t* dev_err, void* stream);
 
 /*
  * Snapshot: copies the whole state of sequence seq_ids[i] (all H heads) and

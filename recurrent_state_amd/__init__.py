@@ -9,6 +9,7 @@ of include/kda.h.
 from ._lib import (  # noqa: F401
     DEV_ERR_ACCEPTED,
     DEV_ERR_CKPT_SLOT,
+    DEV_ERR_DRAFT_LEN,
     CommitPlan,
     CommitVerifyPlan,
     DecodePlan,
@@ -20,6 +21,7 @@ from ._lib import (  # noqa: F401
     SlotPool,
     commit,
     commit_verify,
+    commit_verify_varlen,
     decode_step,
     exported_symbols,
     last_variant,
@@ -31,4 +33,5 @@ from ._lib import (  # noqa: F401
     slot_bytes,
     snapshot,
     verify,
+    verify_varlen,
 )

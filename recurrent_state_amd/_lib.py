@@ -19,8 +19,9 @@ LIB_PATH = os.path.join(_HERE, "libkda.so")
 
 KDA_BF16, KDA_F32 = 0, 1
 VARIANTS = {0: "none", 1: "decode", 2: "verify", 3: "commit", 4: "snapshot", 5: "restore",
-            6: "prefill_recurrent", 7: "prefill_chunked", 8: "commit_verify"}
-DEV_ERR_ACCEPTED, DEV_ERR_CKPT_SLOT = 1, 2
+            6: "prefill_recurrent", 7: "prefill_chunked", 8: "commit_verify", 9: "verify_varlen",
+            10: "commit_verify_varlen"}
+DEV_ERR_ACCEPTED, DEV_ERR_CKPT_SLOT, DEV_ERR_DRAFT_LEN = 1, 2, 4
 
 
 class KdaError(RuntimeError):
@@ -55,6 +56,10 @@ _SIGS = {
     "kda_commit": (_I, [ctypes.POINTER(Shape), _P, _P, ctypes.POINTER(_Log), _P, _P, _P]),
     "kda_commit_verify": (_I, [ctypes.POINTER(Shape), _I, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.POINTER(_Log), _P,
                                _P, _P]),
+    "kda_verify_varlen": (_I, [ctypes.POINTER(Shape), _I, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.POINTER(_Log), _P,
+                               _P]),
+    "kda_commit_verify_varlen": (_I, [ctypes.POINTER(Shape), _I, _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                                      ctypes.POINTER(_Log), _P, _P, _P]),
     "kda_snapshot": (_I, [ctypes.POINTER(Shape), _P, _P, _P, _P, _I, ctypes.POINTER(_Slots), _P]),
     "kda_restore": (_I, [ctypes.POINTER(Shape), _P, _P, _P, _P, _I, ctypes.POINTER(_Slots), _P]),
     "kda_prefill_chunked": (_I, [ctypes.POINTER(Shape), _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _I, _P,
@@ -187,8 +192,7 @@ def decode_step(state, pos, q, k, v, alpha, beta, o, scale=None):
                                  _ptr(alpha), _ptr(beta), _ptr(o), _stream()))
 
 
-def verify(state, q, k, v, alpha, beta, o, log: InputLog, scale=None):
-    """Verify T draft tokens (inputs [B][T][H][d]) from the committed state; fills the log."""
+def _verify_args(state, q, k, v, alpha, beta, o, log: InputLog, scale):
     B, H, dk, dv = state.shape
     T = q.shape[1]
     _need(state, "state", (B, H, dk, dv), torch.float32, state.device)
@@ -197,8 +201,22 @@ def verify(state, q, k, v, alpha, beta, o, log: InputLog, scale=None):
     if sh.in_dtype != log.shape.in_dtype or (B, H, dk, dv) != (log.shape.B, log.shape.H, log.shape.dk,
                                                                log.shape.dv):
         raise ValueError("log was sized for a different shape")
-    _check(lib().kda_verify(ctypes.byref(sh), T, _ptr(state), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha),
-                            _ptr(beta), _ptr(o), ctypes.byref(log.c), _stream()))
+    return sh, T, tuple(_ptr(t) for t in (state, q, k, v, alpha, beta, o))
+
+
+def verify(state, q, k, v, alpha, beta, o, log: InputLog, scale=None):
+    """Verify T draft tokens (inputs [B][T][H][d]) from the committed state; fills the log."""
+    sh, T, ptrs = _verify_args(state, q, k, v, alpha, beta, o, log, scale)
+    _check(lib().kda_verify(ctypes.byref(sh), T, *ptrs, ctypes.byref(log.c), _stream()))
+
+
+def verify_varlen(state, q, k, v, alpha, beta, o, log: InputLog, draft_len, dev_err, scale=None):
+    """verify where sequence b has only its first draft_len[b] tokens (device int32 [B], each in [0, T])."""
+    sh, T, ptrs = _verify_args(state, q, k, v, alpha, beta, o, log, scale)
+    _need(draft_len, "draft_len", (state.shape[0],), torch.int32, state.device)
+    _need(dev_err, "dev_err", (1,), torch.int32, state.device)
+    _check(lib().kda_verify_varlen(ctypes.byref(sh), T, _ptr(draft_len), *ptrs, ctypes.byref(log.c), _ptr(dev_err),
+                                   _stream()))
 
 
 def commit(state, pos, log: InputLog, accepted, dev_err):
@@ -236,6 +254,15 @@ def commit_verify(state, pos, q, k, v, alpha, beta, o, log: InputLog, accepted=N
     """Commit the pending verify's accepted prefix, then verify T new drafts, in one launch."""
     sh, T, ptrs, extra = _commit_verify_args(state, pos, q, k, v, alpha, beta, o, log, accepted, dev_err, scale)
     _check(lib().kda_commit_verify(ctypes.byref(sh), T, *ptrs, ctypes.byref(log.c), *extra, _stream()))
+
+
+def commit_verify_varlen(state, pos, q, k, v, alpha, beta, o, log: InputLog, draft_len, accepted=None, dev_err=None,
+                         scale=None):
+    """commit_verify whose new drafts have a length per sequence (draft_len: device int32 [B])."""
+    sh, T, ptrs, extra = _commit_verify_args(state, pos, q, k, v, alpha, beta, o, log, accepted, dev_err, scale)
+    _need(draft_len, "draft_len", (state.shape[0],), torch.int32, state.device)
+    _check(lib().kda_commit_verify_varlen(ctypes.byref(sh), T, _ptr(draft_len), *ptrs, ctypes.byref(log.c), *extra,
+                                          _stream()))
 
 
 def _pairs(seq_ids, slot_ids):
@@ -330,21 +357,21 @@ class DecodePlan:
 
 
 class VerifyPlan:
-    """A verify call validated once (see DecodePlan)."""
+    """A verify call validated once (see DecodePlan); with draft_len (and
+    dev_err) it is a verify_varlen call."""
 
-    def __init__(self, state, q, k, v, alpha, beta, o, log: InputLog, scale=None):
-        B, H, dk, dv = state.shape
-        T = q.shape[1]
-        _need(state, "state", (B, H, dk, dv), torch.float32, state.device)
-        _check_tokens(state, T, q, k, v, alpha, beta, o)
-        self._shape = _shape(state, q.dtype, scale)
-        if (B, H, dk, dv, self._shape.in_dtype) != (log.shape.B, log.shape.H, log.shape.dk, log.shape.dv,
-                                                   log.shape.in_dtype):
-            raise ValueError("log was sized for a different shape")
-        self._keep = (state, q, k, v, alpha, beta, o, log)
-        self._args = (ctypes.byref(self._shape), T) + tuple(_ptr(t) for t in (state, q, k, v, alpha, beta, o)) + (
-            ctypes.byref(log.c),)
-        self._fn = lib().kda_verify
+    def __init__(self, state, q, k, v, alpha, beta, o, log: InputLog, scale=None, draft_len=None, dev_err=None):
+        self._shape, T, ptrs = _verify_args(state, q, k, v, alpha, beta, o, log, scale)
+        self._keep = (state, q, k, v, alpha, beta, o, log, draft_len, dev_err)
+        if draft_len is None:
+            self._args = (ctypes.byref(self._shape), T) + ptrs + (ctypes.byref(log.c),)
+            self._fn = lib().kda_verify
+        else:
+            _need(draft_len, "draft_len", (state.shape[0],), torch.int32, state.device)
+            _need(dev_err, "dev_err", (1,), torch.int32, state.device)
+            self._args = (ctypes.byref(self._shape), T, _ptr(draft_len)) + ptrs + (ctypes.byref(log.c),
+                                                                                   _ptr(dev_err))
+            self._fn = lib().kda_verify_varlen
 
     def __call__(self):
         _check(self._fn(*self._args, _stream()))
@@ -374,12 +401,18 @@ class CommitVerifyPlan:
     """A commit_verify call validated once (see DecodePlan).  The pending
     count of the log when the plan is called is the one committed."""
 
-    def __init__(self, state, pos, q, k, v, alpha, beta, o, log: InputLog, accepted=None, dev_err=None, scale=None):
+    def __init__(self, state, pos, q, k, v, alpha, beta, o, log: InputLog, accepted=None, dev_err=None, scale=None,
+                 draft_len=None):
         self._shape, T, ptrs, extra = _commit_verify_args(state, pos, q, k, v, alpha, beta, o, log, accepted,
                                                           dev_err, scale)
-        self._keep = (state, pos, q, k, v, alpha, beta, o, log, accepted, dev_err)
-        self._args = (ctypes.byref(self._shape), T) + ptrs + (ctypes.byref(log.c),) + extra
-        self._fn = lib().kda_commit_verify
+        self._keep = (state, pos, q, k, v, alpha, beta, o, log, accepted, dev_err, draft_len)
+        if draft_len is None:
+            self._args = (ctypes.byref(self._shape), T) + ptrs + (ctypes.byref(log.c),) + extra
+            self._fn = lib().kda_commit_verify
+        else:
+            _need(draft_len, "draft_len", (state.shape[0],), torch.int32, state.device)
+            self._args = (ctypes.byref(self._shape), T, _ptr(draft_len)) + ptrs + (ctypes.byref(log.c),) + extra
+            self._fn = lib().kda_commit_verify_varlen
 
     def __call__(self):
         _check(self._fn(*self._args, _stream()))

@@ -69,7 +69,8 @@ kda::LogPtrs log_ptrs(const kda_shape& s, const kda_log* log) {
   const kda::LogLayout L = kda::log_layout(s, log->T_max);
   char* base = static_cast<char*>(log->dev);
   return kda::LogPtrs{base + L.k, base + L.v, reinterpret_cast<float*>(base + L.alpha),
-                      reinterpret_cast<float*>(base + L.beta), log->T_max};
+                      reinterpret_cast<float*>(base + L.beta), reinterpret_cast<int32_t*>(base + L.len),
+                      log->T_max};
 }
 
 kda_status check_slots(const kda_slots* slots) {
@@ -168,8 +169,11 @@ kda_status kda_decode_step(const kda_shape* shape, float* state, int64_t* pos, c
                   KDA_VARIANT_DECODE);
 }
 
-kda_status kda_verify(const kda_shape* shape, int32_t T, const float* state, const void* q, const void* k,
-                      const void* v, const float* alpha, const float* beta, float* o, kda_log* log, void* stream) {
+namespace {
+
+kda_status verify_impl(const kda_shape* shape, int32_t T, const int32_t* draft_len, const float* state, const void* q,
+                       const void* k, const void* v, const float* alpha, const float* beta, float* o, kda_log* log,
+                       int32_t* dev_err, bool varlen, void* stream) {
   kda_status r = check_shape(shape);
   if (r != KDA_OK) return r;
   if ((r = check_log(*shape, log)) != KDA_OK) return r;
@@ -178,13 +182,67 @@ kda_status kda_verify(const kda_shape* shape, int32_t T, const float* state, con
   if (shape->B > 0) {
     if ((r = check_ptrs({state})) != KDA_OK) return r;
     if ((r = check_tokens(q, k, v, alpha, beta, o)) != KDA_OK) return r;
-    r = launched(kda::launch_verify(*shape, T, state, kda::TokenInputs{q, k, v, alpha, beta}, o,
-                                    log_ptrs(*shape, log), static_cast<hipStream_t>(stream)),
-                 KDA_VARIANT_VERIFY);
+    if (varlen) {
+      if (!draft_len || !dev_err) return KDA_ERR_NULL;
+      if (!aligned(draft_len, 4) || !aligned(dev_err, 4)) return KDA_ERR_ALIGN;
+    }
+    r = launched(kda::launch_verify(*shape, T, draft_len, state, kda::TokenInputs{q, k, v, alpha, beta}, o,
+                                    log_ptrs(*shape, log), dev_err, static_cast<hipStream_t>(stream)),
+                 varlen ? KDA_VARIANT_VERIFY_VARLEN : KDA_VARIANT_VERIFY);
     if (r != KDA_OK) return r;
   }
   log->pending_T = T;
   return KDA_OK;
+}
+
+kda_status commit_verify_impl(const kda_shape* shape, int32_t T, const int32_t* draft_len, float* state,
+                              int64_t* pos, const void* q, const void* k, const void* v, const float* alpha,
+                              const float* beta, float* o, kda_log* log, const int32_t* accepted, int32_t* dev_err,
+                              bool varlen, void* stream) {
+  kda_status r = check_shape(shape);
+  if (r != KDA_OK) return r;
+  if ((r = check_log(*shape, log)) != KDA_OK) return r;
+  if (T < 1 || T > log->T_max) return KDA_ERR_SHAPE;
+  const int32_t pend = log->pending_T;
+  if (pend < 0 || pend > log->T_max) return KDA_ERR_ORDER;
+  if (shape->B > 0) {
+    if ((r = check_ptrs({state})) != KDA_OK) return r;
+    if ((r = check_tokens(q, k, v, alpha, beta, o)) != KDA_OK) return r;
+    if (!pos) return KDA_ERR_NULL;
+    if (!aligned(pos, 8)) return KDA_ERR_ALIGN;
+    if (pend > 0) {
+      if (!accepted) return KDA_ERR_NULL;
+      if (!aligned(accepted, 4)) return KDA_ERR_ALIGN;
+    }
+    if (varlen) {
+      if (!draft_len) return KDA_ERR_NULL;
+      if (!aligned(draft_len, 4)) return KDA_ERR_ALIGN;
+    }
+    if (pend > 0 || varlen) {
+      if (!dev_err) return KDA_ERR_NULL;
+      if (!aligned(dev_err, 4)) return KDA_ERR_ALIGN;
+    }
+    r = launched(kda::launch_commit_verify(*shape, pend, T, draft_len, state, pos, accepted, dev_err,
+                                           kda::TokenInputs{q, k, v, alpha, beta}, o, log_ptrs(*shape, log),
+                                           static_cast<hipStream_t>(stream)),
+                 varlen ? KDA_VARIANT_COMMIT_VERIFY_VARLEN : KDA_VARIANT_COMMIT_VERIFY);
+    if (r != KDA_OK) return r;
+  }
+  log->pending_T = T;
+  return KDA_OK;
+}
+
+}  // namespace
+
+kda_status kda_verify(const kda_shape* shape, int32_t T, const float* state, const void* q, const void* k,
+                      const void* v, const float* alpha, const float* beta, float* o, kda_log* log, void* stream) {
+  return verify_impl(shape, T, nullptr, state, q, k, v, alpha, beta, o, log, nullptr, false, stream);
+}
+
+kda_status kda_verify_varlen(const kda_shape* shape, int32_t T, const int32_t* draft_len, const float* state,
+                             const void* q, const void* k, const void* v, const float* alpha, const float* beta,
+                             float* o, kda_log* log, int32_t* dev_err, void* stream) {
+  return verify_impl(shape, T, draft_len, state, q, k, v, alpha, beta, o, log, dev_err, true, stream);
 }
 
 kda_status kda_commit(const kda_shape* shape, float* state, int64_t* pos, kda_log* log, const int32_t* accepted,
@@ -209,29 +267,16 @@ kda_status kda_commit(const kda_shape* shape, float* state, int64_t* pos, kda_lo
 kda_status kda_commit_verify(const kda_shape* shape, int32_t T, float* state, int64_t* pos, const void* q,
                              const void* k, const void* v, const float* alpha, const float* beta, float* o,
                              kda_log* log, const int32_t* accepted, int32_t* dev_err, void* stream) {
-  kda_status r = check_shape(shape);
-  if (r != KDA_OK) return r;
-  if ((r = check_log(*shape, log)) != KDA_OK) return r;
-  if (T < 1 || T > log->T_max) return KDA_ERR_SHAPE;
-  const int32_t pend = log->pending_T;
-  if (pend < 0 || pend > log->T_max) return KDA_ERR_ORDER;
-  if (shape->B > 0) {
-    if ((r = check_ptrs({state})) != KDA_OK) return r;
-    if ((r = check_tokens(q, k, v, alpha, beta, o)) != KDA_OK) return r;
-    if (!pos) return KDA_ERR_NULL;
-    if (!aligned(pos, 8)) return KDA_ERR_ALIGN;
-    if (pend > 0) {
-      if (!accepted || !dev_err) return KDA_ERR_NULL;
-      if (!aligned(accepted, 4) || !aligned(dev_err, 4)) return KDA_ERR_ALIGN;
-    }
-    r = launched(kda::launch_commit_verify(*shape, pend, T, state, pos, accepted, dev_err,
-                                           kda::TokenInputs{q, k, v, alpha, beta}, o, log_ptrs(*shape, log),
-                                           static_cast<hipStream_t>(stream)),
-                 KDA_VARIANT_COMMIT_VERIFY);
-    if (r != KDA_OK) return r;
-  }
-  log->pending_T = T;
-  return KDA_OK;
+  return commit_verify_impl(shape, T, nullptr, state, pos, q, k, v, alpha, beta, o, log, accepted, dev_err, false,
+                            stream);
+}
+
+kda_status kda_commit_verify_varlen(const kda_shape* shape, int32_t T, const int32_t* draft_len, float* state,
+                                    int64_t* pos, const void* q, const void* k, const void* v, const float* alpha,
+                                    const float* beta, float* o, kda_log* log, const int32_t* accepted,
+                                    int32_t* dev_err, void* stream) {
+  return commit_verify_impl(shape, T, draft_len, state, pos, q, k, v, alpha, beta, o, log, accepted, dev_err, true,
+                            stream);
 }
 
 kda_status kda_snapshot(const kda_shape* shape, const float* state, const int64_t* pos, const int32_t* seq_ids,

@@ -12,7 +12,7 @@ namespace kda {
 
 // Byte offsets of the four log regions for a log sized for T_max tokens.
 struct LogLayout {
-  size_t k, v, alpha, beta, total;
+  size_t k, v, alpha, beta, len, total;
 };
 
 inline size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
@@ -27,7 +27,8 @@ inline LogLayout log_layout(const kda_shape& s, int32_t T_max) {
   L.v = round_up(L.k + tok * s.dk * es, 256);
   L.alpha = round_up(L.v + tok * s.dv * es, 256);
   L.beta = round_up(L.alpha + tok * s.dk * 4, 256);
-  L.total = round_up(L.beta + tok * 4, 256);
+  L.len = round_up(L.beta + tok * 4, 256);
+  L.total = round_up(L.len + (size_t)s.B * s.H * 4, 256);
   return L;
 }
 
@@ -39,26 +40,31 @@ struct TokenInputs {
   const float* beta;
 };
 
-// The four log regions; token t of (b, h) is row (b * T_max + t) * H + h.
+// The log regions; token t of (b, h) is row (b * T_max + t) * H + h, and
+// len[b * H + h] is the number of rows the last verify of (b, h) wrote.
 struct LogPtrs {
   void* k;
   void* v;
   float* alpha;
   float* beta;
+  int32_t* len;
   int32_t T_max;
 };
 
 hipError_t launch_decode(const kda_shape& s, float* state, int64_t* pos, TokenInputs in, float* o,
                          hipStream_t st);
-hipError_t launch_verify(const kda_shape& s, int32_t T, const float* state, TokenInputs in, float* o,
-                         LogPtrs log, hipStream_t st);
+// draft_len (device [B], may be null: every sequence has T tokens) limits
+// sequence b to its first draft_len[b] tokens; a length outside [0, T] sets
+// KDA_DEV_ERR_DRAFT_LEN in *dev_err and counts as 0.
+hipError_t launch_verify(const kda_shape& s, int32_t T, const int32_t* draft_len, const float* state, TokenInputs in,
+                         float* o, LogPtrs log, int32_t* dev_err, hipStream_t st);
 hipError_t launch_commit(const kda_shape& s, int32_t T, float* state, int64_t* pos, LogPtrs log,
                          const int32_t* accepted, int32_t* dev_err, hipStream_t st);
 // Commit of the pending T_pend logged tokens (T_pend = 0: none) followed by
 // the verify of T new tokens from the committed state, in one launch.
-hipError_t launch_commit_verify(const kda_shape& s, int32_t T_pend, int32_t T, float* state, int64_t* pos,
-                                const int32_t* accepted, int32_t* dev_err, TokenInputs in, float* o, LogPtrs log,
-                                hipStream_t st);
+hipError_t launch_commit_verify(const kda_shape& s, int32_t T_pend, int32_t T, const int32_t* draft_len, float* state,
+                                int64_t* pos, const int32_t* accepted, int32_t* dev_err, TokenInputs in, float* o,
+                                LogPtrs log, hipStream_t st);
 hipError_t launch_prefill_recurrent(const kda_shape& s, int32_t L, float* state, int64_t* pos,
                                     TokenInputs in, float* o, int32_t ckpt_every, const int32_t* ckpt_slots,
                                     float* slot_states, int64_t* slot_pos, int32_t n_slots,

@@ -46,6 +46,7 @@ struct CommitArgs {
   const float* log_beta;
   const int32_t* accepted;
   int32_t* dev_err;
+  const int32_t* log_len;  // rows the pending verify wrote, per (b, h)
   int32_t H;
   int32_t T;     // tokens of the pending verify
   int32_t Tmax;  // token rows per sequence in the log
@@ -163,7 +164,7 @@ __global__ void KDA_OCCUPANCY __launch_bounds__((kWave * waves_per_group<DV, WPG
   constexpr int R = P::R;
   const P p(a.H);
   const int n = a.accepted[p.b];
-  if (n < 0 || n > a.T) {
+  if (n < 0 || n > min(a.T, a.log_len[p.bh])) {
     if (p.h == 0 && p.slice == 0 && p.lane == 0) atomicOr(a.dev_err, KDA_DEV_ERR_ACCEPTED);
     return;
   }
@@ -274,7 +275,7 @@ hipError_t launch_commit(const kda_shape& s, int32_t T, float* state, int64_t* p
     typedef typename C::TIn TIn;
     constexpr int DK = C::DK, DV = C::DV;
     CommitArgs<TIn> a{state, pos, (const TIn*)log.k, (const TIn*)log.v, log.alpha, log.beta, accepted, dev_err,
-                      s.H, T, log.T_max};
+                      log.len, s.H, T, log.T_max};
     if (slice_waves<DV>(s) >= kWideWaves)
       commit_kernel<DK, DV, TIn, 4><<<grid_of<DK, DV, 4>(s), kWave * waves_per_group<DV, 4>(), 0, st>>>(a);
     else

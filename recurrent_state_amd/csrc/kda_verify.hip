@@ -71,6 +71,10 @@ struct VerifyArgs {
   const int32_t* accepted;
   int32_t* dev_err;
   int32_t T_pend;
+  // Per-sequence draft lengths (null: all T) and the log's per-(b, h) count
+  // of verified rows, which bounds the next commit.
+  const int32_t* draft_len;
+  int32_t* log_len;
 };
 
 // Per-group LDS.  Key-channel vectors are stored by row group with a padded
@@ -462,11 +466,22 @@ __global__ void __launch_bounds__(kWave * (DV / kSliceCols)) verify_chunk_kernel
     }
   };
   auto no_load = [](float (&)[R][4]) {};
+  // Tokens this sequence verifies.
+  int Tv = T;
+  if (a.draft_len) {
+    const int d = a.draft_len[b];
+    if (d < 0 || d > T) {
+      if (h == 0 && wave == 0 && lane == 0) atomicOr(a.dev_err, KDA_DEV_ERR_DRAFT_LEN);
+      Tv = 0;
+    } else {
+      Tv = d;
+    }
+  }
   if (COMMIT) {
     load_state(S);
     if (a.T_pend > 0) {
       const int n = a.accepted[b];
-      if (n < 0 || n > a.T_pend) {
+      if (n < 0 || n > min(a.T_pend, a.log_len[bh])) {
         if (h == 0 && wave == 0 && lane == 0) atomicOr(a.dev_err, KDA_DEV_ERR_ACCEPTED);
       } else if (n > 0) {
         replay_log<DK, DV, TIn, R>(S, a.log_k, a.log_v, a.log_alpha, a.log_beta, tok0_log, a.H, n, row0, col0);
@@ -478,21 +493,25 @@ __global__ void __launch_bounds__(kWave * (DV / kSliceCols)) verify_chunk_kernel
         }
         if (h == 0 && wave == 0 && lane == 0) a.pos[b] += n;
       }
-      __syncthreads();  // every wave has read the pending log rows before the verify rewrites them
+      __syncthreads();  // every wave has read the pending log rows and count before the verify rewrites them
     }
+  }
+  if (threadIdx.x == 0) a.log_len[bh] = Tv;
+  if (Tv == 0) return;
+  if (COMMIT) {
     if (MULTI) {
-      for (int t0 = 0; t0 < T; t0 += kGroup)
-        verify_group<DK, DV, TIn, true>(a, st, L, S, t0, min(kGroup, T - t0), tok0, tok0_log, lane, wave, t0 == 0,
+      for (int t0 = 0; t0 < Tv; t0 += kGroup)
+        verify_group<DK, DV, TIn, true>(a, st, L, S, t0, min(kGroup, Tv - t0), tok0, tok0_log, lane, wave, t0 == 0,
                                         no_load);
     } else {
-      verify_group<DK, DV, TIn, false>(a, st, L, S, 0, T, tok0, tok0_log, lane, wave, true, no_load);
+      verify_group<DK, DV, TIn, false>(a, st, L, S, 0, Tv, tok0, tok0_log, lane, wave, true, no_load);
     }
   } else if (MULTI) {
-    for (int t0 = 0; t0 < T; t0 += kGroup)
-      verify_group<DK, DV, TIn, true>(a, st, L, S, t0, min(kGroup, T - t0), tok0, tok0_log, lane, wave, t0 == 0,
+    for (int t0 = 0; t0 < Tv; t0 += kGroup)
+      verify_group<DK, DV, TIn, true>(a, st, L, S, t0, min(kGroup, Tv - t0), tok0, tok0_log, lane, wave, t0 == 0,
                                       load_state);
   } else {
-    verify_group<DK, DV, TIn, false>(a, st, L, S, 0, T, tok0, tok0_log, lane, wave, true, load_state);
+    verify_group<DK, DV, TIn, false>(a, st, L, S, 0, Tv, tok0, tok0_log, lane, wave, true, load_state);
   }
 }
 
@@ -514,34 +533,34 @@ void launch_shape(const kda_shape& s, const VerifyArgs<TIn>& a, hipStream_t st) 
 }
 
 template <typename TIn, bool COMMIT>
-void launch_any(const kda_shape& s, int32_t T_pend, int32_t T, float* state, int64_t* pos, const int32_t* accepted,
-                int32_t* dev_err, TokenInputs in, float* o, LogPtrs log, hipStream_t st) {
+void launch_any(const kda_shape& s, int32_t T_pend, int32_t T, const int32_t* draft_len, float* state, int64_t* pos,
+                const int32_t* accepted, int32_t* dev_err, TokenInputs in, float* o, LogPtrs log, hipStream_t st) {
   const VerifyArgs<TIn> a{state,   (const TIn*)in.q, (const TIn*)in.k, (const TIn*)in.v, in.alpha, in.beta, o,
                           (TIn*)log.k, (TIn*)log.v, log.alpha, log.beta, s.H, T, log.T_max, s.scale, pos, accepted,
-                          dev_err, T_pend};
+                          dev_err, T_pend, draft_len, log.len};
   launch_shape<TIn, COMMIT>(s, a, st);
 }
 
 }  // namespace
 
-hipError_t launch_verify(const kda_shape& s, int32_t T, const float* state, TokenInputs in, float* o, LogPtrs log,
-                         hipStream_t st) {
+hipError_t launch_verify(const kda_shape& s, int32_t T, const int32_t* draft_len, const float* state, TokenInputs in,
+                         float* o, LogPtrs log, int32_t* dev_err, hipStream_t st) {
   // The verify-only kernel never writes through `state`.
   float* sp = const_cast<float*>(state);
   if (s.in_dtype == KDA_BF16)
-    launch_any<bf16_t, false>(s, 0, T, sp, nullptr, nullptr, nullptr, in, o, log, st);
+    launch_any<bf16_t, false>(s, 0, T, draft_len, sp, nullptr, nullptr, dev_err, in, o, log, st);
   else
-    launch_any<float, false>(s, 0, T, sp, nullptr, nullptr, nullptr, in, o, log, st);
+    launch_any<float, false>(s, 0, T, draft_len, sp, nullptr, nullptr, dev_err, in, o, log, st);
   return hipGetLastError();
 }
 
-hipError_t launch_commit_verify(const kda_shape& s, int32_t T_pend, int32_t T, float* state, int64_t* pos,
-                                const int32_t* accepted, int32_t* dev_err, TokenInputs in, float* o, LogPtrs log,
-                                hipStream_t st) {
+hipError_t launch_commit_verify(const kda_shape& s, int32_t T_pend, int32_t T, const int32_t* draft_len, float* state,
+                                int64_t* pos, const int32_t* accepted, int32_t* dev_err, TokenInputs in, float* o,
+                                LogPtrs log, hipStream_t st) {
   if (s.in_dtype == KDA_BF16)
-    launch_any<bf16_t, true>(s, T_pend, T, state, pos, accepted, dev_err, in, o, log, st);
+    launch_any<bf16_t, true>(s, T_pend, T, draft_len, state, pos, accepted, dev_err, in, o, log, st);
   else
-    launch_any<float, true>(s, T_pend, T, state, pos, accepted, dev_err, in, o, log, st);
+    launch_any<float, true>(s, T_pend, T, draft_len, state, pos, accepted, dev_err, in, o, log, st);
   return hipGetLastError();
 }
 

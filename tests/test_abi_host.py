@@ -60,7 +60,7 @@ def test_sizes(k):
     assert k.slot_bytes(s) == 32 * 128 * 128 * 4
     nb = k.log_bytes(s, 4)
     tok = 16 * 4 * 32
-    assert nb >= tok * (128 * 2 * 2 + 128 * 4 + 4) and nb % 256 == 0
+    assert nb >= tok * (128 * 2 * 2 + 128 * 4 + 4) + 16 * 32 * 4 and nb % 256 == 0   # + per-(b, h) counts
     assert k.log_bytes(s, 0) == 0 and k.log_bytes(s, 17) == 0
     assert k.log_bytes(shape(k, dk=96), 4) == 0 and k.slot_bytes(shape(k, dt=5)) == 0
     f32 = shape(k, B=16, H=32, dt=1)
@@ -137,6 +137,45 @@ def test_commit_verify_validation(k):
     assert L.kda_commit_verify(ctypes.byref(empty), 4, None, None, None, None, None, None, None, None,
                                ctypes.byref(lg0), None, None, None) == OK
     assert lg0.pending_T == 4
+
+
+def test_varlen_validation(k):
+    L = k.lib()
+    s = shape(k)
+    need = k.log_bytes(s, 4)
+    MIS4 = P(0x10002)
+
+    def ver(T, lg, dl=GOOD, err=GOOD):
+        return L.kda_verify_varlen(ctypes.byref(s), T, dl, GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, GOOD,
+                                   ctypes.byref(lg), err, None)
+
+    log = k._lib._Log(0x100000, need, 4, 0)
+    assert ver(2, log, dl=None) == NULL
+    assert ver(2, log, err=None) == NULL
+    assert ver(2, log, dl=MIS4) == ALIGN
+    assert ver(2, log, err=MIS4) == ALIGN
+    assert ver(0, log) == SHAPE and ver(5, log) == SHAPE
+    assert ver(2, k._lib._Log(0x100000, need, 4, 3)) == ORDER
+    assert log.pending_T == 0
+
+    def cv(lg, dl=GOOD, acc=GOOD, err=GOOD):
+        return L.kda_commit_verify_varlen(ctypes.byref(s), 3, dl, GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, GOOD,
+                                          ctypes.byref(lg), acc, err, None)
+
+    idle = k._lib._Log(0x100000, need, 4, 0)
+    assert cv(idle, dl=None) == NULL
+    assert cv(idle, err=None) == NULL          # nothing pending, but draft lengths can be rejected
+    assert cv(idle, dl=MIS4) == ALIGN
+    pend = k._lib._Log(0x100000, need, 4, 2)
+    assert cv(pend, acc=None) == NULL
+    assert cv(pend, acc=MIS4) == ALIGN
+    assert idle.pending_T == 0 and pend.pending_T == 2
+    # An empty batch needs no buffers.
+    empty = shape(k, B=0)
+    lg0 = k._lib._Log(0x100000, k.log_bytes(empty, 4) or 256, 4, 0)
+    assert L.kda_verify_varlen(ctypes.byref(empty), 3, None, None, None, None, None, None, None, None,
+                               ctypes.byref(lg0), None, None) == OK
+    assert lg0.pending_T == 3
 
 
 def test_snapshot_restore_validation(k):

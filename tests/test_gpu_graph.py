@@ -142,3 +142,49 @@ def test_commit_verify_graph_replays_match_eager():
         S_ref, o_ref, pos_ref = ref[r]
         assert torch.equal(bits(SB), S_ref) and torch.equal(bits(oB), o_ref) and torch.equal(posB, pos_ref), r
     assert errA.item() == 0 and errB.item() == 0
+
+
+def test_commit_verify_varlen_graph_replays_match_eager():
+    # As above with a draft length per sequence that changes every round.
+    B, T, rounds = 4, 4, 4
+    say("graph: fused commit + verify, per-sequence draft lengths")
+    S0 = dev_tensor(synth.initial_state(SPEC, B))
+    d = {k: dev_tensor(v) for k, v in synth.token_inputs(SPEC, B, T).items()}
+    lens = [[4, 0, 2, 3], [1, 4, 4, 0], [0, 0, 0, 0], [3, 2, 1, 4]]
+    counts = [[4, 0, 1, 3], [1, 2, 4, 0], [0, 0, 0, 0], [2, 2, 0, 4]]   # round r commits within lens[r - 1]
+    SA = S0.clone()
+    posA = torch.zeros(B, dtype=torch.int64, device="cuda")
+    logA = kda.InputLog(SA, T_max=T)
+    errA = torch.zeros(1, dtype=torch.int32, device="cuda")
+    oA = torch.zeros((B, T, SPEC.H, 128), device="cuda")
+    kda.commit_verify_varlen(SA, posA, d["q"], d["k"], d["v"], d["alpha"], d["beta"], oA, logA,
+                             torch.tensor(lens[0], dtype=torch.int32, device="cuda"), None, errA)
+    ref = []
+    for r in range(1, rounds):
+        kda.commit_verify_varlen(SA, posA, d["q"], d["k"], d["v"], d["alpha"], d["beta"], oA, logA,
+                                 torch.tensor(lens[r], dtype=torch.int32, device="cuda"),
+                                 torch.tensor(counts[r - 1], dtype=torch.int32, device="cuda"), errA)
+        ref.append((bits(SA).clone(), bits(oA).clone(), posA.clone()))
+    SB = S0.clone()
+    posB = torch.zeros(B, dtype=torch.int64, device="cuda")
+    logB = kda.InputLog(SB, T_max=T)
+    errB = torch.zeros(1, dtype=torch.int32, device="cuda")
+    oB = torch.zeros_like(oA)
+    dl = torch.tensor(lens[0], dtype=torch.int32, device="cuda")
+    acc = torch.zeros(B, dtype=torch.int32, device="cuda")
+    kda.commit_verify_varlen(SB, posB, d["q"], d["k"], d["v"], d["alpha"], d["beta"], oB, logB, dl, None, errB)
+    plan = kda.CommitVerifyPlan(SB, posB, d["q"], d["k"], d["v"], d["alpha"], d["beta"], oB, logB, acc, errB,
+                                draft_len=dl)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        plan()
+    for r in range(1, rounds):
+        dl.copy_(torch.tensor(lens[r], dtype=torch.int32))
+        acc.copy_(torch.tensor(counts[r - 1], dtype=torch.int32))
+        g.replay()
+        junk = torch.randn(1000, device="cuda").cumsum(0)
+        torch.cuda.synchronize()
+        assert junk.numel() == 1000
+        S_ref, o_ref, pos_ref = ref[r - 1]
+        assert torch.equal(bits(SB), S_ref) and torch.equal(bits(oB), o_ref) and torch.equal(posB, pos_ref), r
+    assert errA.item() == 0 and errB.item() == 0
