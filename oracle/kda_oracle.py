@@ -187,3 +187,60 @@ def prefill(S0, pos0, inp: dict, scale: float, ckpt_every: int = 0):
         if ckpt_every and (t + 1) % ckpt_every == 0:
             ckpts.append((S.copy(), pos0 + (t + 1)))
     return S, pos0 + L, np.ascontiguousarray(o.transpose(0, 2, 1, 3)), ckpts
+
+
+# ---------------------------------------------------------------------------
+# Input preparation from raw projections.
+#
+# The webinar summary lists removing needless copies and type conversions
+# among its optimisations (paragraph on profiling the token path); fusing the
+# preparation of the recurrent inputs into the decode kernel is that step for
+# this path.  The pages do not print the preparation itself; it follows the
+# input recipe the workloads are defined by: q and k are L2-normalised over the
+# key channels, the per-channel decay is either exp(-softplus(x)) or
+# sigmoid(x) of its logit x, and beta is sigmoid of its logit.  A zero q or k
+# vector (no direction) is taken to normalise to zero.
+
+GATE_EXP_NEG_SOFTPLUS = 0
+GATE_SIGMOID = 1
+
+
+def l2_normalize(x):
+    """x / ||x||_2 over the last axis, in float64; a zero vector stays zero."""
+    x = np.asarray(x, dtype=np.float64)
+    n = np.sqrt(np.sum(x * x, axis=-1, keepdims=True))
+    return np.divide(x, n, out=np.zeros_like(x), where=n > 0)
+
+
+def sigmoid(x):
+    """1 / (1 + e^-x); saturates to exactly 0 or 1 far out."""
+    with np.errstate(over="ignore"):
+        return 1.0 / (1.0 + np.exp(-np.asarray(x, dtype=np.float64)))
+
+
+def softplus(x):
+    """log(1 + e^x), evaluated without overflow."""
+    return np.logaddexp(0.0, np.asarray(x, dtype=np.float64))
+
+
+def decay_gate(x, kind: int):
+    """Per-channel decay from its logit: exp(-softplus(x)) or sigmoid(x)."""
+    if kind == GATE_EXP_NEG_SOFTPLUS:
+        return np.exp(-softplus(x))
+    if kind == GATE_SIGMOID:
+        return sigmoid(x)
+    raise ValueError(f"unknown gate kind {kind}")
+
+
+def prep(raw: dict, kind: int) -> dict:
+    """Prepared token inputs (float64) from raw ones.
+
+    raw: q, k, v as stored ([..][dk] / [..][dv]), alpha_logit [..][dk] and
+    beta_logit [..].  Returns q, k (unit vectors), v, alpha and beta in the
+    layouts ``decode`` takes.
+    """
+    out = {"k": l2_normalize(widen(raw["k"])), "v": widen(raw["v"]),
+           "alpha": decay_gate(widen(raw["alpha_logit"]), kind), "beta": sigmoid(widen(raw["beta_logit"]))}
+    if "q" in raw:
+        out["q"] = l2_normalize(widen(raw["q"]))
+    return out

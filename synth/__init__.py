@@ -13,5 +13,6 @@ from .kda_inputs import (  # noqa: F401
     bf16_bits_to_f32,
     f32_to_bf16_bits,
     initial_state,
+    raw_token_inputs,
     token_inputs,
 )

@@ -114,9 +114,31 @@ def _draw_bh(args):
             _gate(xa, gate).astype(np.float32), (1.0 / (1.0 + np.exp(-xb))).astype(np.float32))
 
 
+def _draw_raw_bh(args):
+    # The same streams as _draw_bh, before any transform: q, k un-normalised,
+    # the gate and beta draws as logits.
+    seed, tag, phase, b, h, n, dk, dv, in_dtype, gate = args
+    q = _rng(seed, tag, phase, _T_Q, b, h).standard_normal((n, dk))
+    k = _rng(seed, tag, phase, _T_K, b, h).standard_normal((n, dk))
+    v = _rng(seed, tag, phase, _T_V, b, h).standard_normal((n, dv))
+    mu = 3.0 if gate == "sigmoid" else -4.0
+    xa = mu + _rng(seed, tag, phase, _T_ALPHA, b, h).standard_normal((n, dk))
+    xb = _rng(seed, tag, phase, _T_BETA, b, h).standard_normal((n,))
+    return (b, h, _store(q, in_dtype), _store(k, in_dtype), _store(v, in_dtype), xa.astype(np.float32),
+            xb.astype(np.float32))
+
+
 def default_workers() -> int:
     """Worker processes for large draws: the host cores available, at most 16."""
     return max(1, min(16, len(os.sched_getaffinity(0))))
+
+
+def raw_token_inputs(spec: ConfigSpec, B: int, n_tokens: int, *, seqs=None, heads=None, phase: int = 0,
+                     seed: int = 0) -> dict:
+    """The draws behind ``token_inputs`` before their transforms, same layout:
+    q, k (un-normalised Gaussians rounded to the storage type), v, alpha_logit
+    (the gate's f32 argument x) and beta_logit (f32 [B][n][H])."""
+    return _collect(spec, B, n_tokens, seqs, heads, phase, seed, 1, _draw_raw_bh, ("alpha_logit", "beta_logit"))
 
 
 def token_inputs(spec: ConfigSpec, B: int, n_tokens: int, *, seqs=None, heads=None, phase: int = 0,
@@ -132,6 +154,10 @@ def token_inputs(spec: ConfigSpec, B: int, n_tokens: int, *, seqs=None, heads=No
     Returns a dict with q, k, v (uint16 bf16 bits or float32), alpha (float32)
     and beta (float32, [B][n][H]).
     """
+    return _collect(spec, B, n_tokens, seqs, heads, phase, seed, workers, _draw_bh, ("alpha", "beta"))
+
+
+def _collect(spec, B, n_tokens, seqs, heads, phase, seed, workers, draw, gate_names) -> dict:
     seqs = list(range(B)) if seqs is None else [int(s) for s in seqs]
     heads = list(range(spec.H)) if heads is None else [int(h) for h in heads]
     dk, dv = spec.dk, spec.dv
@@ -141,8 +167,8 @@ def token_inputs(spec: ConfigSpec, B: int, n_tokens: int, *, seqs=None, heads=No
         "q": np.empty((nb, n_tokens, nh, dk), sdt),
         "k": np.empty((nb, n_tokens, nh, dk), sdt),
         "v": np.empty((nb, n_tokens, nh, dv), sdt),
-        "alpha": np.empty((nb, n_tokens, nh, dk), np.float32),
-        "beta": np.empty((nb, n_tokens, nh), np.float32),
+        gate_names[0]: np.empty((nb, n_tokens, nh, dk), np.float32),
+        gate_names[1]: np.empty((nb, n_tokens, nh), np.float32),
     }
     bpos = {b: i for i, b in enumerate(seqs)}
     hpos = {h: i for i, h in enumerate(heads)}
@@ -155,19 +181,19 @@ def token_inputs(spec: ConfigSpec, B: int, n_tokens: int, *, seqs=None, heads=No
         out["q"][i, :, j] = q
         out["k"][i, :, j] = k
         out["v"][i, :, j] = v
-        out["alpha"][i, :, j] = a
-        out["beta"][i, :, j] = be
+        out[gate_names[0]][i, :, j] = a
+        out[gate_names[1]][i, :, j] = be
 
     if workers is None:
         big = len(tasks) * n_tokens * (3 * dk + dv) > (32 << 20)
         workers = default_workers() if big else 1
     if workers > 1 and len(tasks) > 1:
         with ProcessPoolExecutor(max_workers=workers, mp_context=get_context("spawn")) as ex:
-            for res in ex.map(_draw_bh, tasks, chunksize=max(1, len(tasks) // (4 * workers))):
+            for res in ex.map(draw, tasks, chunksize=max(1, len(tasks) // (4 * workers))):
                 scatter(res)
     else:
         for t in tasks:
-            scatter(_draw_bh(t))
+            scatter(draw(t))
     return out
 
 
