@@ -99,10 +99,16 @@ def dev_tensor(torch, x, device):
     return torch.from_numpy(np.ascontiguousarray(x)).to(device)
 
 
-def decode_inputs(torch, kda_synth, B, n, device):
-    """n seeded tokens in [n][B][H][d] layout (token t is a contiguous slice)."""
+def decode_inputs(torch, kda_synth, B, n, device, raw=False):
+    """n seeded tokens in [n][B][H][d] layout (token t is a contiguous slice);
+    with raw, the un-prepared projections and logits of the same draws, under
+    the names of the prepared inputs."""
     spec = kda_synth.CONFIGS["batched_decode"]
-    inp = kda_synth.token_inputs(spec, B, n)
+    if raw:
+        r = kda_synth.raw_token_inputs(spec, B, n)
+        inp = {"q": r["q"], "k": r["k"], "v": r["v"], "alpha": r["alpha_logit"], "beta": r["beta_logit"]}
+    else:
+        inp = kda_synth.token_inputs(spec, B, n)
     return {k: dev_tensor(torch, v, device).transpose(0, 1).contiguous() for k, v in inp.items()}
 
 
@@ -115,20 +121,24 @@ def capture(torch, fns):
     return g
 
 
-def bench_decode(torch, kda, synth, B, layers, steps, warmup, device, use_graph=True):
+def bench_decode(torch, kda, synth, B, layers, steps, warmup, device, use_graph=True, prep=False):
     """Decode through `layers` independent states per step; returns timing dict.
 
     Step s uses seeded input token s mod 16 for every layer.  With use_graph,
     each step's launches are replayed from a captured HIP graph (how a serving
     loop drives per-step work); otherwise they are issued eagerly from plans.
+    With prep, the launches take raw projections and logits and prepare them
+    in the kernel (decode_step_prep); the bytes moved are the same.
     """
     spec = synth.CONFIGS["batched_decode"]
-    inp = decode_inputs(torch, synth, B, N_TOKENS_IN, device)
+    inp = decode_inputs(torch, synth, B, N_TOKENS_IN, device, raw=prep)
+    gate = kda.GATE_EXP_NEG_SOFTPLUS if prep else None
     S0 = dev_tensor(torch, synth.initial_state(spec, B), device)
     states = [S0.clone() for _ in range(layers)]
     pos = torch.zeros(B, dtype=torch.int64, device=device)
     o = torch.empty((B, H, DV), dtype=torch.float32, device=device)
-    plans = [[kda.DecodePlan(S, pos, inp["q"][t], inp["k"][t], inp["v"][t], inp["alpha"][t], inp["beta"][t], o)
+    plans = [[kda.DecodePlan(S, pos, inp["q"][t], inp["k"][t], inp["v"][t], inp["alpha"][t], inp["beta"][t], o,
+                             prep_gate=gate)
               for S in states] for t in range(N_TOKENS_IN)]
     if use_graph:
         graphs = [capture(torch, ps) for ps in plans]
@@ -208,17 +218,21 @@ def bench_verify_commit(torch, kda, synth, B, T, rounds, layers, device):
     }
 
 
-def bench_spec_fused(torch, kda, synth, B, T, rounds, layers, device):
+def bench_spec_fused(torch, kda, synth, B, T, rounds, layers, device, fixed_accept=None):
     """Speculative rounds through the fused entry point: each round is one
     launch per layer that commits the previous round's accepted prefix and
-    verifies T new drafts (the first round is a plain verify)."""
+    verifies T new drafts (the first round is a plain verify).  Accepted
+    counts are the seeded uniform draws, or `fixed_accept` every round."""
     spec = synth.CONFIGS["spec_verify"]
     inp = synth.token_inputs(spec, B, 4 * T)
     d = {}
     for k, v in inp.items():
         t = dev_tensor(torch, v, device)
         d[k] = t.view(B, 4, T, *t.shape[2:]).transpose(0, 1).contiguous()   # [4][B][T][H][d]
-    acc_np = synth.accepted_counts(spec, B, rounds + 1, T)
+    if fixed_accept is None:
+        acc_np = synth.accepted_counts(spec, B, rounds + 1, T)
+    else:
+        acc_np = np.full((rounds + 1, B), fixed_accept, dtype=np.int32)
     acc = torch.from_numpy(acc_np).to(device)
     S0 = dev_tensor(torch, synth.initial_state(spec, B), device)
     states = [S0.clone() for _ in range(layers)]
@@ -442,6 +456,8 @@ def main():
         log("headline workload launched eagerly (no graph)")
         rows["decode_b64_eager"] = bench_decode(torch, kda, synth, B_HEAD, L_LAYERS, 100, 10, device,
                                                 use_graph=False)
+        log("headline workload from raw projections (input preparation in the kernel)")
+        rows["decode_prep_b64"] = bench_decode(torch, kda, synth, B_HEAD, L_LAYERS, 100, 10, device, prep=True)
         log("copy reference")
         rows["d2d_copy_1GiB"] = bench_copy(torch, device)
         log("hot (cache-resident) decode B=64, one layer")
@@ -459,6 +475,9 @@ def main():
         log("fused commit + verify rounds")
         rows["spec_fused_b16"] = bench_spec_fused(torch, kda, synth, 16, 4, 32, 32, device)
         rows["spec_fused_b64"] = bench_spec_fused(torch, kda, synth, 64, 4, 32, 8, device)
+        log("fused rounds, seven drafts with six accepted")
+        rows["spec_fused_dl7_al6_b1"] = bench_spec_fused(torch, kda, synth, 1, 7, 8, 512, device, fixed_accept=6)
+        rows["spec_fused_dl7_al6_b64"] = bench_spec_fused(torch, kda, synth, 64, 7, 16, 8, device, fixed_accept=6)
         log("verify alone")
         rows["verify_only_b16"] = bench_verify_only(torch, kda, synth, 16, 4, 32, 20, device)
         rows["verify_only_b64"] = bench_verify_only(torch, kda, synth, 64, 4, 8, 50, device)

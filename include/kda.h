@@ -94,6 +94,11 @@ typedef enum kda_dtype { KDA_BF16 = 0, KDA_F32 = 1 } kda_dtype;
 #define KDA_VARIANT_COMMIT_VERIFY 8
 #define KDA_VARIANT_VERIFY_VARLEN 9
 #define KDA_VARIANT_COMMIT_VERIFY_VARLEN 10
+#define KDA_VARIANT_DECODE_PREP 11
+
+/* Decay gate of kda_decode_step_prep: alpha = f(x) of the logit x. */
+#define KDA_GATE_EXP_NEG_SOFTPLUS 0 /* alpha = exp(-softplus(x)) = 1 / (1 + e^x) */
+#define KDA_GATE_SIGMOID 1          /* alpha = sigmoid(x) = 1 / (1 + e^-x) */
 
 typedef struct kda_shape {
   int32_t B;        /* sequences in the batch */
@@ -158,6 +163,21 @@ size_t kda_slot_bytes(const kda_shape* shape);
 kda_status kda_decode_step(const kda_shape* shape, float* state, int64_t* pos, const void* q,
                            const void* k, const void* v, const float* alpha, const float* beta,
                            float* o, void* stream);
+
+/*
+ * kda_decode_step from raw projections, with the input preparation done in
+ * the kernel ("Kimi K3: From Day-0 Availability to Optimized Inference",
+ * paragraph on profiling the token path: needless copies and type
+ * conversions removed).  q and k (in_dtype [B][H][dk]) are taken
+ * un-normalised and divided by their L2 norm over dk in fp32 (a zero vector
+ * stays zero); alpha_logit (f32 [B][H][dk]) gives the decay through `gate`
+ * (KDA_GATE_*); beta_logit (f32 [B][H]) gives beta = sigmoid(beta_logit).
+ * v, state, o and pos as kda_decode_step.  Fails with KDA_ERR_SHAPE for an
+ * unknown gate.
+ */
+kda_status kda_decode_step_prep(const kda_shape* shape, int32_t gate, float* state, int64_t* pos,
+                                const void* q, const void* k, const void* v, const float* alpha_logit,
+                                const float* beta_logit, float* o, void* stream);
 
 /*
  * Speculative verify of T draft tokens per sequence from the committed

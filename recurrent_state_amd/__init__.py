@@ -10,6 +10,8 @@ from ._lib import (  # noqa: F401
     DEV_ERR_ACCEPTED,
     DEV_ERR_CKPT_SLOT,
     DEV_ERR_DRAFT_LEN,
+    GATE_EXP_NEG_SOFTPLUS,
+    GATE_SIGMOID,
     CommitPlan,
     CommitVerifyPlan,
     DecodePlan,
@@ -23,6 +25,7 @@ from ._lib import (  # noqa: F401
     commit_verify,
     commit_verify_varlen,
     decode_step,
+    decode_step_prep,
     exported_symbols,
     last_variant,
     lib,

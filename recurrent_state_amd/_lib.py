@@ -20,7 +20,8 @@ LIB_PATH = os.path.join(_HERE, "libkda.so")
 KDA_BF16, KDA_F32 = 0, 1
 VARIANTS = {0: "none", 1: "decode", 2: "verify", 3: "commit", 4: "snapshot", 5: "restore",
             6: "prefill_recurrent", 7: "prefill_chunked", 8: "commit_verify", 9: "verify_varlen",
-            10: "commit_verify_varlen"}
+            10: "commit_verify_varlen", 11: "decode_prep"}
+GATE_EXP_NEG_SOFTPLUS, GATE_SIGMOID = 0, 1
 DEV_ERR_ACCEPTED, DEV_ERR_CKPT_SLOT, DEV_ERR_DRAFT_LEN = 1, 2, 4
 
 
@@ -52,6 +53,7 @@ _SIGS = {
     "kda_log_bytes": (ctypes.c_size_t, [ctypes.POINTER(Shape), _I]),
     "kda_slot_bytes": (ctypes.c_size_t, [ctypes.POINTER(Shape)]),
     "kda_decode_step": (_I, [ctypes.POINTER(Shape), _P, _P, _P, _P, _P, _P, _P, _P, _P]),
+    "kda_decode_step_prep": (_I, [ctypes.POINTER(Shape), _I, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
     "kda_verify": (_I, [ctypes.POINTER(Shape), _I, _P, _P, _P, _P, _P, _P, _P, ctypes.POINTER(_Log), _P]),
     "kda_commit": (_I, [ctypes.POINTER(Shape), _P, _P, ctypes.POINTER(_Log), _P, _P, _P]),
     "kda_commit_verify": (_I, [ctypes.POINTER(Shape), _I, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.POINTER(_Log), _P,
@@ -190,6 +192,20 @@ def decode_step(state, pos, q, k, v, alpha, beta, o, scale=None):
     sh = _shape(state, q.dtype, scale)
     _check(lib().kda_decode_step(ctypes.byref(sh), _ptr(state), _ptr(pos), _ptr(q), _ptr(k), _ptr(v),
                                  _ptr(alpha), _ptr(beta), _ptr(o), _stream()))
+
+
+def decode_step_prep(state, pos, q, k, v, alpha_logit, beta_logit, o, gate=GATE_EXP_NEG_SOFTPLUS, scale=None):
+    """decode_step from raw projections: q, k un-normalised, the decay and beta as logits
+    (decay = exp(-softplus(x)) for GATE_EXP_NEG_SOFTPLUS, sigmoid(x) for GATE_SIGMOID)."""
+    B, H, dk, dv = state.shape
+    if beta_logit.dim() == 2:
+        q, k, v, alpha_logit, beta_logit, o = (x.unsqueeze(1) for x in (q, k, v, alpha_logit, beta_logit, o))
+    _need(state, "state", (B, H, dk, dv), torch.float32, state.device)
+    _need(pos, "pos", (B,), torch.int64, state.device)
+    _check_tokens(state, 1, q, k, v, alpha_logit, beta_logit, o)
+    sh = _shape(state, q.dtype, scale)
+    _check(lib().kda_decode_step_prep(ctypes.byref(sh), int(gate), _ptr(state), _ptr(pos), _ptr(q), _ptr(k),
+                                      _ptr(v), _ptr(alpha_logit), _ptr(beta_logit), _ptr(o), _stream()))
 
 
 def _verify_args(state, q, k, v, alpha, beta, o, log: InputLog, scale):
@@ -340,7 +356,7 @@ class DecodePlan:
     capture: calling the plan only passes the stored pointers and the current
     stream to the library."""
 
-    def __init__(self, state, pos, q, k, v, alpha, beta, o, scale=None):
+    def __init__(self, state, pos, q, k, v, alpha, beta, o, scale=None, prep_gate=None):
         B, H, dk, dv = state.shape
         if beta.dim() == 2:
             q, k, v, alpha, beta, o = (x.unsqueeze(1) for x in (q, k, v, alpha, beta, o))
@@ -349,8 +365,12 @@ class DecodePlan:
         _check_tokens(state, 1, q, k, v, alpha, beta, o)
         self._keep = (state, pos, q, k, v, alpha, beta, o)
         self._shape = _shape(state, q.dtype, scale)
-        self._args = (ctypes.byref(self._shape),) + tuple(_ptr(t) for t in self._keep)
-        self._fn = lib().kda_decode_step
+        if prep_gate is None:      # prepared inputs
+            self._args = (ctypes.byref(self._shape),) + tuple(_ptr(t) for t in self._keep)
+            self._fn = lib().kda_decode_step
+        else:                      # raw projections and logits (decode_step_prep)
+            self._args = (ctypes.byref(self._shape), int(prep_gate)) + tuple(_ptr(t) for t in self._keep)
+            self._fn = lib().kda_decode_step_prep
 
     def __call__(self):
         _check(self._fn(*self._args, _stream()))

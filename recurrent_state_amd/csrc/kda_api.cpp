@@ -169,6 +169,23 @@ kda_status kda_decode_step(const kda_shape* shape, float* state, int64_t* pos, c
                   KDA_VARIANT_DECODE);
 }
 
+kda_status kda_decode_step_prep(const kda_shape* shape, int32_t gate, float* state, int64_t* pos, const void* q,
+                                const void* k, const void* v, const float* alpha_logit, const float* beta_logit,
+                                float* o, void* stream) {
+  kda_status r = check_shape(shape);
+  if (r != KDA_OK) return r;
+  if (gate != KDA_GATE_EXP_NEG_SOFTPLUS && gate != KDA_GATE_SIGMOID) return KDA_ERR_SHAPE;
+  if (shape->B == 0) return KDA_OK;
+  if ((r = check_ptrs({state})) != KDA_OK) return r;
+  if ((r = check_tokens(q, k, v, alpha_logit, beta_logit, o)) != KDA_OK) return r;
+  if (!pos) return KDA_ERR_NULL;
+  if (!aligned(pos, 8)) return KDA_ERR_ALIGN;
+  const float gate_sign = gate == KDA_GATE_SIGMOID ? 1.f : -1.f;
+  return launched(kda::launch_decode_prep(*shape, state, pos, kda::TokenInputs{q, k, v, alpha_logit, beta_logit}, o,
+                                          gate_sign, static_cast<hipStream_t>(stream)),
+                  KDA_VARIANT_DECODE_PREP);
+}
+
 namespace {
 
 kda_status verify_impl(const kda_shape* shape, int32_t T, const int32_t* draft_len, const float* state, const void* q,

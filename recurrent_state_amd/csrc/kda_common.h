@@ -209,6 +209,74 @@ __device__ __forceinline__ void token_update(float (&S)[R][4], const Raw<TIn, R>
   }
 }
 
+// 1 / (1 + e^-x): exactly 0 for x = -inf (or far below zero) and exactly 1
+// for x = +inf (or far above).
+__device__ __forceinline__ float sigmoid_f32(float x) { return __builtin_amdgcn_rcpf(1.f + __expf(-x)); }
+
+// 1 / |x| from the squared norm; a zero vector keeps norm factor 0, so it
+// stays zero.  IEEE square root and division: scaling the vector by 2^p
+// scales the factor by exactly 2^-p.
+__device__ __forceinline__ float inv_norm(float sq) { return sq > 0.f ? 1.f / sqrtf(sq) : 0.f; }
+
+// token_update from raw projections (the input preparation fused into the
+// step).  q and k arrive un-normalised, the decay as its logit x (per key
+// channel) and beta as its logit.  The step uses
+//   k^ = k / |k|, q^ = q / |q|  (L2 norms over the key channels),
+//   alpha = sigmoid(gsign * x)  (gsign = -1: exp(-softplus(x)) = 1 / (1 + e^x);
+//                                gsign = +1: sigmoid(x)),
+//   beta = sigmoid(beta logit),
+// and otherwise the same update and output as token_update.  The squared
+// norms are reduced in the same pass as S1^T k and S1^T q, and the unit
+// vectors enter as factors: u = (S1^T k) / |k|, S = S1 + (k / |k|) e^T,
+// o = scale (S1^T q / |q| + e (k . q) / (|k| |q|)).
+template <int R, typename TIn>
+__device__ __forceinline__ void token_update_prep(float (&S)[R][4], const Raw<TIn, R>& kraw,
+                                                  const Raw<float, R>& xraw, const Raw<TIn, R>& qraw,
+                                                  const float (&vc)[4], float beta_logit, float gsign, float scale,
+                                                  float (&o)[4]) {
+  float u[4] = {0.f, 0.f, 0.f, 0.f};
+  float w[4] = {0.f, 0.f, 0.f, 0.f};
+  float kq = 0.f, kk = 0.f, qq = 0.f;
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const float kr = elem(kraw, r), qr = elem(qraw, r);
+    const float ar = sigmoid_f32(gsign * elem(xraw, r));
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const float s1 = ar * S[r][c];
+      S[r][c] = s1;
+      u[c] = __builtin_fmaf(kr, s1, u[c]);
+      w[c] = __builtin_fmaf(qr, s1, w[c]);
+    }
+    kq = __builtin_fmaf(kr, qr, kq);
+    kk = __builtin_fmaf(kr, kr, kk);
+    qq = __builtin_fmaf(qr, qr, qq);
+  }
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    u[c] = rowgroup_sum(u[c]);
+    w[c] = rowgroup_sum(w[c]);
+  }
+  kq = rowgroup_sum(kq);
+  kk = rowgroup_sum(kk);
+  qq = rowgroup_sum(qq);
+  const float rk = inv_norm(kk), rq = inv_norm(qq);
+  const float beta = sigmoid_f32(beta_logit);
+  const float kqn = kq * rk * rq;
+  float e[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    e[c] = beta * (vc[c] - u[c] * rk);
+    o[c] = scale * __builtin_fmaf(e[c], kqn, w[c] * rq);
+  }
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const float kn = elem(kraw, r) * rk;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) S[r][c] = __builtin_fmaf(kn, e[c], S[r][c]);
+  }
+}
+
 template <int R, int DV>
 __device__ __forceinline__ void load_tile(const float* p, float (&S)[R][4]) {
 #pragma unroll
@@ -247,6 +315,12 @@ struct TokenIn {
     float vc[4];
     widen4(v, vc);
     token_update<R, WITH_Q>(S, k, a, q, vc, beta, scale, o);
+  }
+  // Raw projections: `a` holds the decay logits and `beta` the beta logit.
+  __device__ __forceinline__ void update_prep(float (&S)[R][4], float gsign, float scale, float (&o)[4]) const {
+    float vc[4];
+    widen4(v, vc);
+    token_update_prep<R>(S, k, a, q, vc, beta, gsign, scale, o);
   }
 };
 

@@ -58,6 +58,10 @@ hipError_t launch_decode(const kda_shape& s, float* state, int64_t* pos, TokenIn
 // KDA_DEV_ERR_DRAFT_LEN in *dev_err and counts as 0.
 hipError_t launch_verify(const kda_shape& s, int32_t T, const int32_t* draft_len, const float* state, TokenInputs in,
                          float* o, LogPtrs log, int32_t* dev_err, hipStream_t st);
+// Decode from raw projections: q, k un-normalised, `alpha` / `beta` hold the
+// decay and beta logits; decay = sigmoid(gate_sign * logit).
+hipError_t launch_decode_prep(const kda_shape& s, float* state, int64_t* pos, TokenInputs raw, float* o,
+                              float gate_sign, hipStream_t st);
 hipError_t launch_commit(const kda_shape& s, int32_t T, float* state, int64_t* pos, LogPtrs log,
                          const int32_t* accepted, int32_t* dev_err, hipStream_t st);
 // Commit of the pending T_pend logged tokens (T_pend = 0: none) followed by

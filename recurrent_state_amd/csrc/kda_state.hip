@@ -29,11 +29,12 @@ struct StepArgs {
   const TIn* q;
   const TIn* k;
   const TIn* v;
-  const float* alpha;
-  const float* beta;
+  const float* alpha;  // decay logits when the inputs are raw projections
+  const float* beta;   // beta logits when the inputs are raw projections
   float* o;
   int32_t H;
   float scale;
+  float gate_sign;     // raw projections: decay = sigmoid(gate_sign * logit)
 };
 
 template <typename TIn>
@@ -140,7 +141,9 @@ struct Place {
   __device__ __forceinline__ size_t tile_off() const { return (size_t)row0 * DV + col0; }
 };
 
-template <int DK, int DV, typename TIn, int WPG>
+// PREP: the inputs are raw projections and logits, prepared in the step
+// (token_update_prep).
+template <int DK, int DV, typename TIn, int WPG, bool PREP>
 __global__ void KDA_OCCUPANCY __launch_bounds__((kWave * waves_per_group<DV, WPG>())) decode_kernel(StepArgs<TIn> a) {
   typedef Place<DK, DV, WPG> P;
   constexpr int R = P::R;
@@ -152,7 +155,10 @@ __global__ void KDA_OCCUPANCY __launch_bounds__((kWave * waves_per_group<DV, WPG
   in.load(a.k + (size_t)p.bh * DK + p.row0, a.q + (size_t)p.bh * DK + p.row0,
           a.alpha + (size_t)p.bh * DK + p.row0, a.v + (size_t)p.bh * DV + p.col0, a.beta + p.bh);
   float o[4];
-  in.update(S, a.scale, o);
+  if constexpr (PREP)
+    in.update_prep(S, a.gate_sign, a.scale, o);
+  else
+    in.update(S, a.scale, o);
   store_tile<R, DV>(sp, S);
   if (p.rg == 0) *reinterpret_cast<float4*>(a.o + (size_t)p.bh * DV + p.col0) = make_float4(o[0], o[1], o[2], o[3]);
   if (p.h == 0 && p.slice == 0 && p.lane == 0) a.pos[p.b] += 1;
@@ -252,20 +258,35 @@ void dispatch(const kda_shape& s, F&& f) {
 
 }  // namespace
 
-hipError_t launch_decode(const kda_shape& s, float* state, int64_t* pos, TokenInputs in, float* o,
-                         hipStream_t st) {
+namespace {
+
+template <bool PREP>
+hipError_t launch_decode_any(const kda_shape& s, float* state, int64_t* pos, TokenInputs in, float* o,
+                             float gate_sign, hipStream_t st) {
   dispatch(s, [&](auto c) {
     typedef decltype(c) C;
     typedef typename C::TIn TIn;
     constexpr int DK = C::DK, DV = C::DV;
     StepArgs<TIn> a{state, pos, (const TIn*)in.q, (const TIn*)in.k, (const TIn*)in.v, in.alpha, in.beta, o,
-                    s.H, s.scale};
+                    s.H, s.scale, gate_sign};
     if (slice_waves<DV>(s) >= kWideWaves)
-      decode_kernel<DK, DV, TIn, 4><<<grid_of<DK, DV, 4>(s), kWave * waves_per_group<DV, 4>(), 0, st>>>(a);
+      decode_kernel<DK, DV, TIn, 4, PREP><<<grid_of<DK, DV, 4>(s), kWave * waves_per_group<DV, 4>(), 0, st>>>(a);
     else
-      decode_kernel<DK, DV, TIn, 1><<<grid_of<DK, DV, 1>(s), kWave, 0, st>>>(a);
+      decode_kernel<DK, DV, TIn, 1, PREP><<<grid_of<DK, DV, 1>(s), kWave, 0, st>>>(a);
   });
   return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_decode(const kda_shape& s, float* state, int64_t* pos, TokenInputs in, float* o,
+                         hipStream_t st) {
+  return launch_decode_any<false>(s, state, pos, in, o, 0.f, st);
+}
+
+hipError_t launch_decode_prep(const kda_shape& s, float* state, int64_t* pos, TokenInputs raw, float* o,
+                              float gate_sign, hipStream_t st) {
+  return launch_decode_any<true>(s, state, pos, raw, o, gate_sign, st);
 }
 
 hipError_t launch_commit(const kda_shape& s, int32_t T, float* state, int64_t* pos, LogPtrs log,

@@ -86,6 +86,22 @@ def test_decode_validation(k):
     assert dec(shape(k, B=0), state=None, pos=None, q=None, o=None) == OK
 
 
+def test_decode_prep_validation(k):
+    L = k.lib()
+    dec = lambda s, gate=0, state=GOOD, pos=GOOD, q=GOOD, a=GOOD, o=GOOD: L.kda_decode_step_prep(  # noqa: E731
+        ctypes.byref(s) if s is not None else None, gate, state, pos, q, GOOD, GOOD, a, GOOD, o, None)
+    assert dec(None) == NULL
+    assert dec(shape(k, dk=96)) == SHAPE
+    assert dec(shape(k), gate=2) == SHAPE and dec(shape(k), gate=-1) == SHAPE
+    assert dec(shape(k, B=0), gate=7) == SHAPE, "the gate is checked before the empty-batch shortcut"
+    assert dec(shape(k), state=None) == NULL
+    assert dec(shape(k), q=None) == NULL
+    assert dec(shape(k), a=None) == NULL
+    assert dec(shape(k), pos=None) == NULL
+    assert dec(shape(k), o=MIS) == ALIGN
+    assert dec(shape(k, B=0), gate=1, state=None, pos=None, q=None, a=None, o=None) == OK
+
+
 def test_verify_commit_validation(k):
     L = k.lib()
     s = shape(k)

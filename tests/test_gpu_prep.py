@@ -1,0 +1,124 @@
+"""Decode from raw projections (kda_decode_step_prep): the input preparation
+(L2 norms of q and k, the decay gate and beta from their logits) runs inside
+the decode kernel.
+
+Parity: against the fp64 oracle's preparation followed by its recurrence, at
+the tolerance bar, for every shape and both gate forms.  Exact properties:
+scaling the raw q or k by a power of two leaves every output and state bit
+unchanged (the kernel's norms use IEEE square root and division), saturated
+gates (a closed decay gate, beta 0) leave the state unchanged, and a zero key
+writes nothing.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import recurrent_state_amd as kda
+import synth
+from oracle import kda_oracle as ko
+from tests.kda_testutil import assert_parity, bits, dev_tensor, say
+from tests.test_gpu_small import SHAPES, spec_for
+
+pytestmark = pytest.mark.gpu
+
+GATES = {"softplus": kda.GATE_EXP_NEG_SOFTPLUS, "sigmoid": kda.GATE_SIGMOID}
+
+
+def run_prep(S, pos, raw, gate, scale=None):
+    """Token-by-token decode_step_prep over raw inputs [B][n][H][d] (host arrays)."""
+    B, H, _, dv = S.shape
+    n = raw["k"].shape[1]
+    d = {name: dev_tensor(np.ascontiguousarray(x)) for name, x in raw.items()}
+    outs = []
+    for t in range(n):
+        o = torch.empty((B, 1, H, dv), dtype=torch.float32, device=S.device)
+        kda.decode_step_prep(S, pos, d["q"][:, t:t + 1].contiguous(), d["k"][:, t:t + 1].contiguous(),
+                             d["v"][:, t:t + 1].contiguous(), d["alpha_logit"][:, t:t + 1].contiguous(),
+                             d["beta_logit"][:, t:t + 1].contiguous(), o, gate=gate, scale=scale)
+        outs.append(o)
+    return torch.cat(outs, dim=1)
+
+
+@pytest.mark.parametrize("gate", ["softplus", "sigmoid"])
+@pytest.mark.parametrize("dk,dv,dt", SHAPES)
+def test_decode_prep_matches_oracle(dk, dv, dt, gate):
+    spec = spec_for(dk, dv, dt, gate=gate, tag=130)
+    B, n = 3, 40
+    say(f"decode_prep dk={dk} dv={dv} {dt} gate={gate}")
+    S0 = synth.initial_state(spec, B)
+    raw = synth.raw_token_inputs(spec, B, n)
+    S = dev_tensor(S0)
+    pos = torch.zeros(B, dtype=torch.int64, device="cuda")
+    o = run_prep(S, pos, raw, GATES[gate])
+    assert kda.last_variant() == "decode_prep"
+    S_ref, o_ref = ko.decode(S0, ko.prep(raw, GATES[gate]), spec.scale)
+    assert_parity(o.cpu().numpy(), o_ref, S.cpu().numpy(), S_ref, f"decode_prep {dk}x{dv} {dt} {gate}")
+    assert pos.cpu().tolist() == [n] * B
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_decode_prep_power_of_two_scaling_is_exact(dt):
+    spec = spec_for(128, 128, dt, tag=131)
+    B, n = 2, 6
+    say(f"decode_prep scaling {dt}")
+    S0 = synth.initial_state(spec, B)
+    raw = synth.raw_token_inputs(spec, B, n)
+    scaled = dict(raw)
+    if dt == "bf16":
+        # bf16 bit patterns: add to the exponent field (no value here is near under- or overflow).
+        scaled["q"] = (raw["q"].astype(np.int32) + (5 << 7)).astype(np.uint16)    # x 2^5
+        scaled["k"] = (raw["k"].astype(np.int32) - (3 << 7)).astype(np.uint16)    # x 2^-3
+        nz = (raw["q"] & 0x7FFF) != 0
+        assert nz.all() and ((raw["k"] & 0x7FFF) != 0).all()
+    else:
+        scaled["q"] = raw["q"] * np.float32(32.0)
+        scaled["k"] = raw["k"] * np.float32(0.125)
+    res = []
+    for r in (raw, scaled):
+        S = dev_tensor(S0)
+        pos = torch.zeros(B, dtype=torch.int64, device="cuda")
+        o = run_prep(S, pos, r, kda.GATE_EXP_NEG_SOFTPLUS)
+        res.append((bits(S).clone(), bits(o).clone()))
+    assert torch.equal(res[0][0], res[1][0]) and torch.equal(res[0][1], res[1][1])
+
+
+def test_decode_prep_saturated_gates_and_zero_vectors():
+    spec = spec_for(128, 128, "f32", tag=132)
+    B, n = 3, 3
+    say("decode_prep edge cases")
+    S0 = synth.initial_state(spec, B)
+    raw = synth.raw_token_inputs(spec, B, n)
+    raw = {k_: v_.copy() for k_, v_ in raw.items()}
+    # seq 0, token 0: decay gate fully open (alpha = 1) and beta = 0: the state must not change.
+    raw["alpha_logit"][0, 0] = -np.inf
+    raw["beta_logit"][0, 0] = -np.inf
+    # seq 1, token 1: zero key (no direction, nothing written) and zero query (output 0).
+    raw["k"][1, 1] = 0.0
+    raw["q"][1, 1] = 0.0
+    # seq 2: saturated logits of both signs, large but finite.
+    raw["alpha_logit"][2, 0, :, ::2] = 1e4
+    raw["alpha_logit"][2, 0, :, 1::2] = -1e4
+    raw["beta_logit"][2, 1] = 1e4
+    S = dev_tensor(S0)
+    pos = torch.zeros(B, dtype=torch.int64, device="cuda")
+    d = {name: dev_tensor(np.ascontiguousarray(x)) for name, x in raw.items()}
+    o = torch.empty((B, 1, spec.H, 128), dtype=torch.float32, device="cuda")
+    tok = lambda t: [d[x][:, t:t + 1].contiguous() for x in ("q", "k", "v", "alpha_logit", "beta_logit")]  # noqa: E731
+    kda.decode_step_prep(S, pos, *tok(0), o, gate=kda.GATE_EXP_NEG_SOFTPLUS)
+    torch.cuda.synchronize()
+    assert torch.equal(S[0], dev_tensor(S0)[0]), "alpha = 1 and beta = 0 must leave the state unchanged"
+    S_after0 = S.clone()
+    kda.decode_step_prep(S, pos, *tok(1), o, gate=kda.GATE_EXP_NEG_SOFTPLUS)
+    # Zero key: only the decay applies (S1 = Diag(alpha) S, computed on the host from the
+    # oracle's gate in fp64, rounded once: the kernel forms each product once in fp32).
+    alpha1 = ko.decay_gate(raw["alpha_logit"][1, 1].astype(np.float64), ko.GATE_EXP_NEG_SOFTPLUS)
+    S1 = S_after0[1].cpu().numpy().astype(np.float64) * alpha1[:, :, None]
+    assert np.max(np.abs(S[1].cpu().numpy() - S1)) <= 4e-7 * np.max(np.abs(S1))
+    assert torch.count_nonzero(o[1, 0]).item() == 0, "zero query: zero output"
+    kda.decode_step_prep(S, pos, *tok(2), o, gate=kda.GATE_EXP_NEG_SOFTPLUS)
+    S_ref, o_ref = ko.decode(S0, ko.prep(raw, ko.GATE_EXP_NEG_SOFTPLUS), spec.scale)
+    assert_parity(o[:, 0].cpu().numpy(), o_ref[:, 2], S.cpu().numpy(), S_ref, "saturated gates, zero vectors")
+    assert pos.cpu().tolist() == [3, 3, 3]
