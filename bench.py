@@ -424,7 +424,13 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--with-copy-ref", action="store_true",
                     help="also run one 256 MiB device copy (known bytes) to scale profiler byte counters")
+    ap.add_argument("--rows", default="all",
+                    help="comma-separated row groups after the headline: decode, spec, slots, prefill (default all)")
     args = ap.parse_args()
+    groups = {"decode", "spec", "slots", "prefill"}
+    picked = groups if args.rows == "all" else set(args.rows.split(","))
+    if not picked <= groups:
+        ap.error(f"--rows: unknown group(s) {sorted(picked - groups)}")
     if args.gpus != 1:
         print("bench.py measures one GPU: this library's path has no multi-GPU part "
               "(sequences and heads shard with no exchange); run with --gpus 1.", file=sys.stderr)
@@ -452,7 +458,7 @@ def main():
     log("headline: decode B=64 x 8 layers")
     head = bench_decode(torch, kda, synth, B_HEAD, L_LAYERS, args.steps, args.warmup, device)
     rows = {}
-    if not args.quick:
+    if not args.quick and "decode" in picked:
         log("headline workload launched eagerly (no graph)")
         rows["decode_b64_eager"] = bench_decode(torch, kda, synth, B_HEAD, L_LAYERS, 100, 10, device,
                                                 use_graph=False)
@@ -469,6 +475,7 @@ def main():
             log(f"sweep B={B} layers={layers} steps={steps}")
             sweep.append(bench_decode(torch, kda, synth, B, layers, steps, 3, device))
         rows["decode_sweep"] = sweep
+    if not args.quick and "spec" in picked:
         log("verify/commit")
         rows["verify_commit_b16"] = bench_verify_commit(torch, kda, synth, 16, 4, 32, 32, device)
         rows["verify_commit_b64"] = bench_verify_commit(torch, kda, synth, 64, 4, 32, 8, device)
@@ -481,8 +488,10 @@ def main():
         log("verify alone")
         rows["verify_only_b16"] = bench_verify_only(torch, kda, synth, 16, 4, 32, 20, device)
         rows["verify_only_b64"] = bench_verify_only(torch, kda, synth, 64, 4, 8, 50, device)
+    if not args.quick and "slots" in picked:
         log("snapshot/restore")
         rows["snapshot_restore"] = bench_snapshot_restore(torch, kda, synth, device)
+    if not args.quick and "prefill" in picked:
         log("prefill")
         for variant in ("chunked", "recurrent"):
             rows[f"prefill_{variant}"] = bench_prefill(torch, kda, synth, device, variant)

@@ -95,6 +95,8 @@ typedef enum kda_dtype { KDA_BF16 = 0, KDA_F32 = 1 } kda_dtype;
 #define KDA_VARIANT_VERIFY_VARLEN 9
 #define KDA_VARIANT_COMMIT_VERIFY_VARLEN 10
 #define KDA_VARIANT_DECODE_PREP 11
+#define KDA_VARIANT_VERIFY_PREP 12
+#define KDA_VARIANT_COMMIT_VERIFY_PREP 13
 
 /* Decay gate of kda_decode_step_prep: alpha = f(x) of the logit x. */
 #define KDA_GATE_EXP_NEG_SOFTPLUS 0 /* alpha = exp(-softplus(x)) = 1 / (1 + e^x) */
@@ -121,17 +123,24 @@ typedef struct kda_shape {
  *   v      in_dtype [B][T_max][H][dv]
  *   alpha  f32 [B][T_max][H][dk]
  *   beta   f32 [B][T_max][H]
- *   n      i32 [B][H]   rows the pending verify filled for (b, h): T, or the
- *                       sequence's draft length under the _varlen calls
- * The device writes n; a commit accepts at most n_bh tokens of (b, h).
- * `pending_T` is host-side bookkeeping: kda_verify and kda_commit_verify set
- * it to T, kda_commit consumes it and resets it to 0.  Initialise it to 0.
+ *   n      i32 [B][H]   per (b, h): bits 0-15 the rows the pending verify
+ *                       filled (T, or the sequence's draft length under the
+ *                       _varlen calls); bits 16 and up the form of the logged
+ *                       inputs: 0 prepared, 1 + gate for raw projections
+ *                       (the _prep calls, which log their inputs raw)
+ * The device writes n; a commit accepts at most n_bh tokens of (b, h) and
+ * replays them with the update of their form.
+ * `pending_T` and `pending_form` are host-side bookkeeping: the verify calls
+ * set pending_T to T and pending_form to the form they logged (0 prepared
+ * inputs, 1 + gate for the _prep calls), kda_commit consumes them and resets
+ * pending_T to 0.  Initialise both to 0.
  */
 typedef struct kda_log {
   void* dev;
   size_t bytes;
   int32_t T_max;
   int32_t pending_T;
+  int32_t pending_form;
 } kda_log;
 
 /*
@@ -253,6 +262,32 @@ kda_status kda_commit_verify_varlen(const kda_shape* shape, int32_t T, const int
                                     int64_t* pos, const void* q, const void* k, const void* v, const float* alpha,
                                     const float* beta, float* o, kda_log* log, const int32_t* accepted,
                                     int32_t* dev_err, void* stream);
+
+/*
+ * kda_verify from raw projections: q, k, alpha_logit, beta_logit as in
+ * kda_decode_step_prep, with the [B][T][H][d] token layout.  The kernel
+ * prepares them (unit q and k, decay and beta from their logits) and logs
+ * them raw (k, v, alpha_logit, beta_logit), marking the log's records as raw
+ * with this gate; kda_commit then replays them through the same preparation,
+ * so the committed state is bit-identical to that many
+ * kda_decode_step_prep calls.  Fails with KDA_ERR_SHAPE for an unknown gate.
+ * (Webinar summary: rejected draft tokens, and needless conversions removed.)
+ */
+kda_status kda_verify_prep(const kda_shape* shape, int32_t gate, int32_t T, const float* state, const void* q,
+                           const void* k, const void* v, const float* alpha_logit, const float* beta_logit,
+                           float* o, kda_log* log, void* stream);
+
+/*
+ * kda_commit_verify whose new drafts are raw projections (as kda_verify_prep).
+ * The pending verify, if any, must have logged raw projections too (any gate:
+ * it is replayed with its own); after a verify of prepared inputs commit with
+ * kda_commit first (KDA_ERR_ORDER otherwise).  Likewise kda_commit_verify and
+ * kda_commit_verify_varlen need a pending verify of prepared inputs.
+ */
+kda_status kda_commit_verify_prep(const kda_shape* shape, int32_t gate, int32_t T, float* state, int64_t* pos,
+                                  const void* q, const void* k, const void* v, const float* alpha_logit,
+                                  const float* beta_logit, float* o, kda_log* log, const int32_t* accepted,
+                                  int32_t* dev_err, void* stream);
 
 /*
  * Snapshot: copies the whole state of sequence seq_ids[i] (all H heads) and

@@ -23,6 +23,7 @@ from ._lib import (  # noqa: F401
     SlotPool,
     commit,
     commit_verify,
+    commit_verify_prep,
     commit_verify_varlen,
     decode_step,
     decode_step_prep,
@@ -36,5 +37,6 @@ from ._lib import (  # noqa: F401
     slot_bytes,
     snapshot,
     verify,
+    verify_prep,
     verify_varlen,
 )

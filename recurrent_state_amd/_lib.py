@@ -20,7 +20,7 @@ LIB_PATH = os.path.join(_HERE, "libkda.so")
 KDA_BF16, KDA_F32 = 0, 1
 VARIANTS = {0: "none", 1: "decode", 2: "verify", 3: "commit", 4: "snapshot", 5: "restore",
             6: "prefill_recurrent", 7: "prefill_chunked", 8: "commit_verify", 9: "verify_varlen",
-            10: "commit_verify_varlen", 11: "decode_prep"}
+            10: "commit_verify_varlen", 11: "decode_prep", 12: "verify_prep", 13: "commit_verify_prep"}
 GATE_EXP_NEG_SOFTPLUS, GATE_SIGMOID = 0, 1
 DEV_ERR_ACCEPTED, DEV_ERR_CKPT_SLOT, DEV_ERR_DRAFT_LEN = 1, 2, 4
 
@@ -38,7 +38,7 @@ class Shape(ctypes.Structure):
 
 class _Log(ctypes.Structure):
     _fields_ = [("dev", ctypes.c_void_p), ("bytes", ctypes.c_size_t), ("T_max", ctypes.c_int32),
-                ("pending_T", ctypes.c_int32)]
+                ("pending_T", ctypes.c_int32), ("pending_form", ctypes.c_int32)]
 
 
 class _Slots(ctypes.Structure):
@@ -54,6 +54,9 @@ _SIGS = {
     "kda_slot_bytes": (ctypes.c_size_t, [ctypes.POINTER(Shape)]),
     "kda_decode_step": (_I, [ctypes.POINTER(Shape), _P, _P, _P, _P, _P, _P, _P, _P, _P]),
     "kda_decode_step_prep": (_I, [ctypes.POINTER(Shape), _I, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
+    "kda_verify_prep": (_I, [ctypes.POINTER(Shape), _I, _I, _P, _P, _P, _P, _P, _P, _P, ctypes.POINTER(_Log), _P]),
+    "kda_commit_verify_prep": (_I, [ctypes.POINTER(Shape), _I, _I, _P, _P, _P, _P, _P, _P, _P, _P,
+                                    ctypes.POINTER(_Log), _P, _P, _P]),
     "kda_verify": (_I, [ctypes.POINTER(Shape), _I, _P, _P, _P, _P, _P, _P, _P, ctypes.POINTER(_Log), _P]),
     "kda_commit": (_I, [ctypes.POINTER(Shape), _P, _P, ctypes.POINTER(_Log), _P, _P, _P]),
     "kda_commit_verify": (_I, [ctypes.POINTER(Shape), _I, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.POINTER(_Log), _P,
@@ -226,6 +229,12 @@ def verify(state, q, k, v, alpha, beta, o, log: InputLog, scale=None):
     _check(lib().kda_verify(ctypes.byref(sh), T, *ptrs, ctypes.byref(log.c), _stream()))
 
 
+def verify_prep(state, q, k, v, alpha_logit, beta_logit, o, log: InputLog, gate=GATE_EXP_NEG_SOFTPLUS, scale=None):
+    """verify from raw projections and logits (prepared in the kernel, logged raw)."""
+    sh, T, ptrs = _verify_args(state, q, k, v, alpha_logit, beta_logit, o, log, scale)
+    _check(lib().kda_verify_prep(ctypes.byref(sh), int(gate), T, *ptrs, ctypes.byref(log.c), _stream()))
+
+
 def verify_varlen(state, q, k, v, alpha, beta, o, log: InputLog, draft_len, dev_err, scale=None):
     """verify where sequence b has only its first draft_len[b] tokens (device int32 [B], each in [0, T])."""
     sh, T, ptrs = _verify_args(state, q, k, v, alpha, beta, o, log, scale)
@@ -270,6 +279,15 @@ def commit_verify(state, pos, q, k, v, alpha, beta, o, log: InputLog, accepted=N
     """Commit the pending verify's accepted prefix, then verify T new drafts, in one launch."""
     sh, T, ptrs, extra = _commit_verify_args(state, pos, q, k, v, alpha, beta, o, log, accepted, dev_err, scale)
     _check(lib().kda_commit_verify(ctypes.byref(sh), T, *ptrs, ctypes.byref(log.c), *extra, _stream()))
+
+
+def commit_verify_prep(state, pos, q, k, v, alpha_logit, beta_logit, o, log: InputLog, accepted=None, dev_err=None,
+                       gate=GATE_EXP_NEG_SOFTPLUS, scale=None):
+    """commit_verify whose new drafts are raw projections and logits (as verify_prep)."""
+    sh, T, ptrs, extra = _commit_verify_args(state, pos, q, k, v, alpha_logit, beta_logit, o, log, accepted, dev_err,
+                                             scale)
+    _check(lib().kda_commit_verify_prep(ctypes.byref(sh), int(gate), T, *ptrs, ctypes.byref(log.c), *extra,
+                                        _stream()))
 
 
 def commit_verify_varlen(state, pos, q, k, v, alpha, beta, o, log: InputLog, draft_len, accepted=None, dev_err=None,
@@ -380,10 +398,16 @@ class VerifyPlan:
     """A verify call validated once (see DecodePlan); with draft_len (and
     dev_err) it is a verify_varlen call."""
 
-    def __init__(self, state, q, k, v, alpha, beta, o, log: InputLog, scale=None, draft_len=None, dev_err=None):
+    def __init__(self, state, q, k, v, alpha, beta, o, log: InputLog, scale=None, draft_len=None, dev_err=None,
+                 prep_gate=None):
         self._shape, T, ptrs = _verify_args(state, q, k, v, alpha, beta, o, log, scale)
         self._keep = (state, q, k, v, alpha, beta, o, log, draft_len, dev_err)
-        if draft_len is None:
+        if prep_gate is not None:
+            if draft_len is not None:
+                raise ValueError("draft lengths and raw projections do not combine")
+            self._args = (ctypes.byref(self._shape), int(prep_gate), T) + ptrs + (ctypes.byref(log.c),)
+            self._fn = lib().kda_verify_prep
+        elif draft_len is None:
             self._args = (ctypes.byref(self._shape), T) + ptrs + (ctypes.byref(log.c),)
             self._fn = lib().kda_verify
         else:
@@ -422,11 +446,16 @@ class CommitVerifyPlan:
     count of the log when the plan is called is the one committed."""
 
     def __init__(self, state, pos, q, k, v, alpha, beta, o, log: InputLog, accepted=None, dev_err=None, scale=None,
-                 draft_len=None):
+                 draft_len=None, prep_gate=None):
         self._shape, T, ptrs, extra = _commit_verify_args(state, pos, q, k, v, alpha, beta, o, log, accepted,
                                                           dev_err, scale)
         self._keep = (state, pos, q, k, v, alpha, beta, o, log, accepted, dev_err, draft_len)
-        if draft_len is None:
+        if prep_gate is not None:
+            if draft_len is not None:
+                raise ValueError("draft lengths and raw projections do not combine")
+            self._args = (ctypes.byref(self._shape), int(prep_gate), T) + ptrs + (ctypes.byref(log.c),) + extra
+            self._fn = lib().kda_commit_verify_prep
+        elif draft_len is None:
             self._args = (ctypes.byref(self._shape), T) + ptrs + (ctypes.byref(log.c),) + extra
             self._fn = lib().kda_commit_verify
         else:

@@ -61,6 +61,7 @@ kda_status check_log(const kda_shape& s, const kda_log* log) {
   if (!log || !log->dev) return KDA_ERR_NULL;
   if (!aligned(log->dev, 256)) return KDA_ERR_ALIGN;
   if (log->T_max < 1 || log->T_max > kMaxT) return KDA_ERR_SHAPE;
+  if (log->pending_form < 0 || log->pending_form > 2) return KDA_ERR_SHAPE;
   if (log->bytes < kda::log_layout(s, log->T_max).total) return KDA_ERR_SHAPE;
   return KDA_OK;
 }
@@ -188,9 +189,12 @@ kda_status kda_decode_step_prep(const kda_shape* shape, int32_t gate, float* sta
 
 namespace {
 
+bool valid_gate(int32_t gate) { return gate == KDA_GATE_EXP_NEG_SOFTPLUS || gate == KDA_GATE_SIGMOID; }
+
+// gate < 0: prepared inputs; otherwise raw projections and logits.
 kda_status verify_impl(const kda_shape* shape, int32_t T, const int32_t* draft_len, const float* state, const void* q,
                        const void* k, const void* v, const float* alpha, const float* beta, float* o, kda_log* log,
-                       int32_t* dev_err, bool varlen, void* stream) {
+                       int32_t* dev_err, bool varlen, int32_t gate, void* stream) {
   kda_status r = check_shape(shape);
   if (r != KDA_OK) return r;
   if ((r = check_log(*shape, log)) != KDA_OK) return r;
@@ -204,24 +208,27 @@ kda_status verify_impl(const kda_shape* shape, int32_t T, const int32_t* draft_l
       if (!aligned(draft_len, 4) || !aligned(dev_err, 4)) return KDA_ERR_ALIGN;
     }
     r = launched(kda::launch_verify(*shape, T, draft_len, state, kda::TokenInputs{q, k, v, alpha, beta}, o,
-                                    log_ptrs(*shape, log), dev_err, static_cast<hipStream_t>(stream)),
-                 varlen ? KDA_VARIANT_VERIFY_VARLEN : KDA_VARIANT_VERIFY);
+                                    log_ptrs(*shape, log), dev_err, gate, static_cast<hipStream_t>(stream)),
+                 gate >= 0 ? KDA_VARIANT_VERIFY_PREP : varlen ? KDA_VARIANT_VERIFY_VARLEN : KDA_VARIANT_VERIFY);
     if (r != KDA_OK) return r;
   }
   log->pending_T = T;
+  log->pending_form = gate < 0 ? 0 : 1 + gate;
   return KDA_OK;
 }
 
 kda_status commit_verify_impl(const kda_shape* shape, int32_t T, const int32_t* draft_len, float* state,
                               int64_t* pos, const void* q, const void* k, const void* v, const float* alpha,
                               const float* beta, float* o, kda_log* log, const int32_t* accepted, int32_t* dev_err,
-                              bool varlen, void* stream) {
+                              bool varlen, int32_t gate, void* stream) {
   kda_status r = check_shape(shape);
   if (r != KDA_OK) return r;
   if ((r = check_log(*shape, log)) != KDA_OK) return r;
   if (T < 1 || T > log->T_max) return KDA_ERR_SHAPE;
   const int32_t pend = log->pending_T;
   if (pend < 0 || pend > log->T_max) return KDA_ERR_ORDER;
+  // One fused launch replays one logged form: raw after the _prep verify only.
+  if (pend > 0 && (log->pending_form != 0) != (gate >= 0)) return KDA_ERR_ORDER;
   if (shape->B > 0) {
     if ((r = check_ptrs({state})) != KDA_OK) return r;
     if ((r = check_tokens(q, k, v, alpha, beta, o)) != KDA_OK) return r;
@@ -240,12 +247,14 @@ kda_status commit_verify_impl(const kda_shape* shape, int32_t T, const int32_t* 
       if (!aligned(dev_err, 4)) return KDA_ERR_ALIGN;
     }
     r = launched(kda::launch_commit_verify(*shape, pend, T, draft_len, state, pos, accepted, dev_err,
-                                           kda::TokenInputs{q, k, v, alpha, beta}, o, log_ptrs(*shape, log),
-                                           static_cast<hipStream_t>(stream)),
-                 varlen ? KDA_VARIANT_COMMIT_VERIFY_VARLEN : KDA_VARIANT_COMMIT_VERIFY);
+                                           kda::TokenInputs{q, k, v, alpha, beta}, o, log_ptrs(*shape, log), gate,
+                                           log->pending_form - 1, static_cast<hipStream_t>(stream)),
+                 gate >= 0 ? KDA_VARIANT_COMMIT_VERIFY_PREP
+                           : varlen ? KDA_VARIANT_COMMIT_VERIFY_VARLEN : KDA_VARIANT_COMMIT_VERIFY);
     if (r != KDA_OK) return r;
   }
   log->pending_T = T;
+  log->pending_form = gate < 0 ? 0 : 1 + gate;
   return KDA_OK;
 }
 
@@ -253,13 +262,20 @@ kda_status commit_verify_impl(const kda_shape* shape, int32_t T, const int32_t* 
 
 kda_status kda_verify(const kda_shape* shape, int32_t T, const float* state, const void* q, const void* k,
                       const void* v, const float* alpha, const float* beta, float* o, kda_log* log, void* stream) {
-  return verify_impl(shape, T, nullptr, state, q, k, v, alpha, beta, o, log, nullptr, false, stream);
+  return verify_impl(shape, T, nullptr, state, q, k, v, alpha, beta, o, log, nullptr, false, -1, stream);
+}
+
+kda_status kda_verify_prep(const kda_shape* shape, int32_t gate, int32_t T, const float* state, const void* q,
+                           const void* k, const void* v, const float* alpha_logit, const float* beta_logit, float* o,
+                           kda_log* log, void* stream) {
+  if (!valid_gate(gate)) return KDA_ERR_SHAPE;
+  return verify_impl(shape, T, nullptr, state, q, k, v, alpha_logit, beta_logit, o, log, nullptr, false, gate, stream);
 }
 
 kda_status kda_verify_varlen(const kda_shape* shape, int32_t T, const int32_t* draft_len, const float* state,
                              const void* q, const void* k, const void* v, const float* alpha, const float* beta,
                              float* o, kda_log* log, int32_t* dev_err, void* stream) {
-  return verify_impl(shape, T, draft_len, state, q, k, v, alpha, beta, o, log, dev_err, true, stream);
+  return verify_impl(shape, T, draft_len, state, q, k, v, alpha, beta, o, log, dev_err, true, -1, stream);
 }
 
 kda_status kda_commit(const kda_shape* shape, float* state, int64_t* pos, kda_log* log, const int32_t* accepted,
@@ -273,7 +289,7 @@ kda_status kda_commit(const kda_shape* shape, float* state, int64_t* pos, kda_lo
     if (!pos || !accepted || !dev_err) return KDA_ERR_NULL;
     if (!aligned(pos, 8) || !aligned(accepted, 4) || !aligned(dev_err, 4)) return KDA_ERR_ALIGN;
     r = launched(kda::launch_commit(*shape, log->pending_T, state, pos, log_ptrs(*shape, log), accepted, dev_err,
-                                    static_cast<hipStream_t>(stream)),
+                                    log->pending_form, static_cast<hipStream_t>(stream)),
                  KDA_VARIANT_COMMIT);
     if (r != KDA_OK) return r;
   }
@@ -285,7 +301,16 @@ kda_status kda_commit_verify(const kda_shape* shape, int32_t T, float* state, in
                              const void* k, const void* v, const float* alpha, const float* beta, float* o,
                              kda_log* log, const int32_t* accepted, int32_t* dev_err, void* stream) {
   return commit_verify_impl(shape, T, nullptr, state, pos, q, k, v, alpha, beta, o, log, accepted, dev_err, false,
-                            stream);
+                            -1, stream);
+}
+
+kda_status kda_commit_verify_prep(const kda_shape* shape, int32_t gate, int32_t T, float* state, int64_t* pos,
+                                  const void* q, const void* k, const void* v, const float* alpha_logit,
+                                  const float* beta_logit, float* o, kda_log* log, const int32_t* accepted,
+                                  int32_t* dev_err, void* stream) {
+  if (!valid_gate(gate)) return KDA_ERR_SHAPE;
+  return commit_verify_impl(shape, T, nullptr, state, pos, q, k, v, alpha_logit, beta_logit, o, log, accepted,
+                            dev_err, false, gate, stream);
 }
 
 kda_status kda_commit_verify_varlen(const kda_shape* shape, int32_t T, const int32_t* draft_len, float* state,
@@ -293,7 +318,7 @@ kda_status kda_commit_verify_varlen(const kda_shape* shape, int32_t T, const int
                                     const float* beta, float* o, kda_log* log, const int32_t* accepted,
                                     int32_t* dev_err, void* stream) {
   return commit_verify_impl(shape, T, draft_len, state, pos, q, k, v, alpha, beta, o, log, accepted, dev_err, true,
-                            stream);
+                            -1, stream);
 }
 
 kda_status kda_snapshot(const kda_shape* shape, const float* state, const int64_t* pos, const int32_t* seq_ids,

@@ -14,6 +14,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "kda.h"
+
 namespace kda {
 
 constexpr int kWave = 64;
@@ -228,8 +230,9 @@ __device__ __forceinline__ float inv_norm(float sq) { return sq > 0.f ? 1.f / sq
 // and otherwise the same update and output as token_update.  The squared
 // norms are reduced in the same pass as S1^T k and S1^T q, and the unit
 // vectors enter as factors: u = (S1^T k) / |k|, S = S1 + (k / |k|) e^T,
-// o = scale (S1^T q / |q| + e (k . q) / (|k| |q|)).
-template <int R, typename TIn>
+// o = scale (S1^T q / |q| + e (k . q) / (|k| |q|)).  Without WITH_OUT (the
+// replay of logged tokens) q is not touched and the state is the same.
+template <int R, bool WITH_OUT, typename TIn>
 __device__ __forceinline__ void token_update_prep(float (&S)[R][4], const Raw<TIn, R>& kraw,
                                                   const Raw<float, R>& xraw, const Raw<TIn, R>& qraw,
                                                   const float (&vc)[4], float beta_logit, float gsign, float scale,
@@ -239,35 +242,42 @@ __device__ __forceinline__ void token_update_prep(float (&S)[R][4], const Raw<TI
   float kq = 0.f, kk = 0.f, qq = 0.f;
 #pragma unroll
   for (int r = 0; r < R; ++r) {
-    const float kr = elem(kraw, r), qr = elem(qraw, r);
+    const float kr = elem(kraw, r);
     const float ar = sigmoid_f32(gsign * elem(xraw, r));
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       const float s1 = ar * S[r][c];
       S[r][c] = s1;
       u[c] = __builtin_fmaf(kr, s1, u[c]);
-      w[c] = __builtin_fmaf(qr, s1, w[c]);
+      if (WITH_OUT) w[c] = __builtin_fmaf(elem(qraw, r), s1, w[c]);
     }
-    kq = __builtin_fmaf(kr, qr, kq);
     kk = __builtin_fmaf(kr, kr, kk);
-    qq = __builtin_fmaf(qr, qr, qq);
+    if (WITH_OUT) {
+      const float qr = elem(qraw, r);
+      kq = __builtin_fmaf(kr, qr, kq);
+      qq = __builtin_fmaf(qr, qr, qq);
+    }
   }
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
     u[c] = rowgroup_sum(u[c]);
-    w[c] = rowgroup_sum(w[c]);
+    if (WITH_OUT) w[c] = rowgroup_sum(w[c]);
   }
-  kq = rowgroup_sum(kq);
   kk = rowgroup_sum(kk);
-  qq = rowgroup_sum(qq);
-  const float rk = inv_norm(kk), rq = inv_norm(qq);
+  if (WITH_OUT) {
+    kq = rowgroup_sum(kq);
+    qq = rowgroup_sum(qq);
+  }
+  const float rk = inv_norm(kk);
   const float beta = sigmoid_f32(beta_logit);
-  const float kqn = kq * rk * rq;
   float e[4];
 #pragma unroll
-  for (int c = 0; c < 4; ++c) {
-    e[c] = beta * (vc[c] - u[c] * rk);
-    o[c] = scale * __builtin_fmaf(e[c], kqn, w[c] * rq);
+  for (int c = 0; c < 4; ++c) e[c] = beta * (vc[c] - u[c] * rk);
+  if (WITH_OUT) {
+    const float rq = inv_norm(qq);
+    const float kqn = kq * rk * rq;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) o[c] = scale * __builtin_fmaf(e[c], kqn, w[c] * rq);
   }
 #pragma unroll
   for (int r = 0; r < R; ++r) {
@@ -320,26 +330,42 @@ struct TokenIn {
   __device__ __forceinline__ void update_prep(float (&S)[R][4], float gsign, float scale, float (&o)[4]) const {
     float vc[4];
     widen4(v, vc);
-    token_update_prep<R>(S, k, a, q, vc, beta, gsign, scale, o);
+    token_update_prep<R, WITH_Q>(S, k, a, q, vc, beta, gsign, scale, o);
   }
 };
 
 // Replays n logged tokens onto a lane's R x 4 state tile (rows row0..,
 // columns col0..): the commit step.  Logged token t of this (sequence, head)
-// sits at row tok0 + t * H of the [B][T_max][H] log regions.  Commit and the
-// fused commit + verify both call this, so their states are bit-identical to
-// n decode steps.
-template <int DK, int DV, typename TIn, int R>
+// sits at row tok0 + t * H of the [B][T_max][H] log regions.  RAW = false:
+// the log holds prepared inputs (the decode step's update); RAW = true: raw
+// projections and logits with decay sigmoid(gsign * logit) (the update of the
+// decode step from raw projections).  Commit and the fused commit + verify
+// both call this, so their states are bit-identical to n decode steps of the
+// matching kind.  Callers pick RAW from the log record before loading any
+// state, so each form runs as its own code path.
+template <int DK, int DV, typename TIn, int R, bool RAW>
 __device__ __forceinline__ void replay_log(float (&S)[R][4], const TIn* log_k, const TIn* log_v,
                                            const float* log_alpha, const float* log_beta, size_t tok0, int H,
-                                           int n, int row0, int col0) {
+                                           int n, int row0, int col0, float gsign) {
   TokenIn<TIn, R, false> cur;
   for (int t = 0; t < n; ++t) {
     const size_t tk = tok0 + (size_t)t * H;
     cur.load(log_k + tk * DK + row0, nullptr, log_alpha + tk * DK + row0, log_v + tk * DV + col0, log_beta + tk);
     float o[4];
-    cur.update(S, 0.f, o);
+    if constexpr (RAW)
+      cur.update_prep(S, gsign, 0.f, o);
+    else
+      cur.update(S, 0.f, o);
   }
 }
+
+// The per-(sequence, head) record of the log: the rows the last verify
+// filled (low 16 bits) and the form of the logged inputs (high bits:
+// kLogPrepared, or kLogRaw + gate for raw projections; the host keeps the
+// same form in kda_log.pending_form to pick the replay kernel).
+constexpr int kLogPrepared = 0;
+constexpr int kLogRaw = 1;
+__host__ __device__ constexpr int log_record(int rows, int form) { return rows | (form << 16); }
+__device__ __forceinline__ int log_rows(int rec) { return rec & 0xffff; }
 
 }  // namespace kda

@@ -56,19 +56,24 @@ hipError_t launch_decode(const kda_shape& s, float* state, int64_t* pos, TokenIn
 // draft_len (device [B], may be null: every sequence has T tokens) limits
 // sequence b to its first draft_len[b] tokens; a length outside [0, T] sets
 // KDA_DEV_ERR_DRAFT_LEN in *dev_err and counts as 0.
+// gate < 0: prepared inputs; otherwise raw projections and logits with that
+// KDA_GATE_* (prepared in the kernel, logged raw).
 hipError_t launch_verify(const kda_shape& s, int32_t T, const int32_t* draft_len, const float* state, TokenInputs in,
-                         float* o, LogPtrs log, int32_t* dev_err, hipStream_t st);
+                         float* o, LogPtrs log, int32_t* dev_err, int32_t gate, hipStream_t st);
 // Decode from raw projections: q, k un-normalised, `alpha` / `beta` hold the
 // decay and beta logits; decay = sigmoid(gate_sign * logit).
 hipError_t launch_decode_prep(const kda_shape& s, float* state, int64_t* pos, TokenInputs raw, float* o,
                               float gate_sign, hipStream_t st);
+// form: the logged inputs' form (0 prepared, 1 + KDA_GATE_* raw projections).
 hipError_t launch_commit(const kda_shape& s, int32_t T, float* state, int64_t* pos, LogPtrs log,
-                         const int32_t* accepted, int32_t* dev_err, hipStream_t st);
+                         const int32_t* accepted, int32_t* dev_err, int32_t form, hipStream_t st);
 // Commit of the pending T_pend logged tokens (T_pend = 0: none) followed by
 // the verify of T new tokens from the committed state, in one launch.
+// The pending log must be prepared when gate < 0 and raw when gate >= 0;
+// pend_gate is the gate of a raw pending log.
 hipError_t launch_commit_verify(const kda_shape& s, int32_t T_pend, int32_t T, const int32_t* draft_len, float* state,
                                 int64_t* pos, const int32_t* accepted, int32_t* dev_err, TokenInputs in, float* o,
-                                LogPtrs log, hipStream_t st);
+                                LogPtrs log, int32_t gate, int32_t pend_gate, hipStream_t st);
 hipError_t launch_prefill_recurrent(const kda_shape& s, int32_t L, float* state, int64_t* pos,
                                     TokenInputs in, float* o, int32_t ckpt_every, const int32_t* ckpt_slots,
                                     float* slot_states, int64_t* slot_pos, int32_t n_slots,

@@ -16,6 +16,8 @@
 
 #include <hip/hip_runtime.h>
 
+#include <type_traits>
+
 #include "kda_common.h"
 #include "kda_internal.h"
 
@@ -47,10 +49,11 @@ struct CommitArgs {
   const float* log_beta;
   const int32_t* accepted;
   int32_t* dev_err;
-  const int32_t* log_len;  // rows the pending verify wrote, per (b, h)
+  const int32_t* log_len;  // per (b, h): rows the pending verify wrote and their form (log_record)
   int32_t H;
   int32_t T;     // tokens of the pending verify
   int32_t Tmax;  // token rows per sequence in the log
+  float gate_sign;  // raw logs: decay = sigmoid(gate_sign * logit)
 };
 
 template <typename TIn>
@@ -164,13 +167,14 @@ __global__ void KDA_OCCUPANCY __launch_bounds__((kWave * waves_per_group<DV, WPG
   if (p.h == 0 && p.slice == 0 && p.lane == 0) a.pos[p.b] += 1;
 }
 
-template <int DK, int DV, typename TIn, int WPG>
+// RAW: the log holds raw projections and logits (decay sigmoid(gate_sign * x)).
+template <int DK, int DV, typename TIn, int WPG, bool RAW>
 __global__ void KDA_OCCUPANCY __launch_bounds__((kWave * waves_per_group<DV, WPG>())) commit_kernel(CommitArgs<TIn> a) {
   typedef Place<DK, DV, WPG> P;
   constexpr int R = P::R;
   const P p(a.H);
   const int n = a.accepted[p.b];
-  if (n < 0 || n > min(a.T, a.log_len[p.bh])) {
+  if (n < 0 || n > min(a.T, log_rows(a.log_len[p.bh]))) {
     if (p.h == 0 && p.slice == 0 && p.lane == 0) atomicOr(a.dev_err, KDA_DEV_ERR_ACCEPTED);
     return;
   }
@@ -178,8 +182,8 @@ __global__ void KDA_OCCUPANCY __launch_bounds__((kWave * waves_per_group<DV, WPG
   float* sp = a.state + (size_t)p.bh * DK * DV + p.tile_off();
   float S[R][4];
   load_tile<R, DV>(sp, S);
-  replay_log<DK, DV, TIn, R>(S, a.log_k, a.log_v, a.log_alpha, a.log_beta, (size_t)p.b * a.Tmax * a.H + p.h, a.H, n,
-                             p.row0, p.col0);
+  replay_log<DK, DV, TIn, R, RAW>(S, a.log_k, a.log_v, a.log_alpha, a.log_beta, (size_t)p.b * a.Tmax * a.H + p.h,
+                                  a.H, n, p.row0, p.col0, a.gate_sign);
   store_tile<R, DV>(sp, S);
   if (p.h == 0 && p.slice == 0 && p.lane == 0) a.pos[p.b] += n;
 }
@@ -290,17 +294,25 @@ hipError_t launch_decode_prep(const kda_shape& s, float* state, int64_t* pos, To
 }
 
 hipError_t launch_commit(const kda_shape& s, int32_t T, float* state, int64_t* pos, LogPtrs log,
-                         const int32_t* accepted, int32_t* dev_err, hipStream_t st) {
+                         const int32_t* accepted, int32_t* dev_err, int32_t form, hipStream_t st) {
   dispatch(s, [&](auto c) {
     typedef decltype(c) C;
     typedef typename C::TIn TIn;
     constexpr int DK = C::DK, DV = C::DV;
+    const float gsign = form == kLogPrepared ? 0.f : (form - kLogRaw == KDA_GATE_SIGMOID ? 1.f : -1.f);
     CommitArgs<TIn> a{state, pos, (const TIn*)log.k, (const TIn*)log.v, log.alpha, log.beta, accepted, dev_err,
-                      log.len, s.H, T, log.T_max};
-    if (slice_waves<DV>(s) >= kWideWaves)
-      commit_kernel<DK, DV, TIn, 4><<<grid_of<DK, DV, 4>(s), kWave * waves_per_group<DV, 4>(), 0, st>>>(a);
+                      log.len, s.H, T, log.T_max, gsign};
+    auto go = [&](auto raw) {
+      constexpr bool RAW = decltype(raw)::value;
+      if (slice_waves<DV>(s) >= kWideWaves)
+        commit_kernel<DK, DV, TIn, 4, RAW><<<grid_of<DK, DV, 4>(s), kWave * waves_per_group<DV, 4>(), 0, st>>>(a);
+      else
+        commit_kernel<DK, DV, TIn, 1, RAW><<<grid_of<DK, DV, 1>(s), kWave, 0, st>>>(a);
+    };
+    if (form == kLogPrepared)
+      go(std::false_type{});
     else
-      commit_kernel<DK, DV, TIn, 1><<<grid_of<DK, DV, 1>(s), kWave, 0, st>>>(a);
+      go(std::true_type{});
   });
   return hipGetLastError();
 }

@@ -75,6 +75,11 @@ struct VerifyArgs {
   // of verified rows, which bounds the next commit.
   const int32_t* draft_len;
   int32_t* log_len;
+  // Raw projections (verify from raw inputs only): KDA_GATE_* of the decay
+  // logits and its sign (decay = sigmoid(gate_sign * logit)).
+  int32_t gate;
+  float gate_sign;
+  float pend_gate_sign;  // fused commit of a raw pending log (PREP): its decay sign
 };
 
 // Per-group LDS.  Key-channel vectors are stored by row group with a padded
@@ -216,8 +221,11 @@ struct Streams {
 
 // One group of G <= kGroup tokens starting at token t0, from the state tile S
 // (rows [R rg, R rg + R) of this lane, columns col0 .. col0 + 3).  MULTI:
-// advance S to the state after the group.
-template <int DK, int DV, typename TIn, bool MULTI, typename LoadState>
+// advance S to the state after the group.  PREP: the inputs are raw
+// projections and logits; they are prepared here (unit q and k, decay and
+// beta from their logits, as the decode step from raw projections does) and
+// logged raw.
+template <int DK, int DV, typename TIn, bool MULTI, bool PREP, typename LoadState>
 __device__ __forceinline__ void verify_group(const VerifyArgs<TIn>& a, const Streams<TIn, DK, DV>& st,
                                              VerifyLds<DK>& L, float (&S)[DK / kRowGroups][4], int t0, int G,
                                              size_t tok0, size_t tok0_log, int lane, int wave, bool first,
@@ -258,6 +266,29 @@ __device__ __forceinline__ void verify_group(const VerifyArgs<TIn>& a, const Str
     load_state(S);
     __builtin_amdgcn_sched_barrier(0);
   }
+  // The group's decays, key norm factors and betas as the recurrence uses
+  // them (the loaded values themselves unless PREP).
+  float av[kGroup][CPL], kn[kGroup], bp[kGroup];
+#pragma unroll
+  for (int r = 0; r < kGroup; ++r) {
+    float k2 = 0.f;
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) {
+      if constexpr (PREP) {
+        av[r][c] = sigmoid_f32(a.gate_sign * al[r][c]);
+        k2 = __builtin_fmaf(kk[r][c], kk[r][c], k2);
+      } else {
+        av[r][c] = al[r][c];
+      }
+    }
+    if constexpr (PREP) {
+      kn[r] = inv_norm(wave_sum(k2));
+      bp[r] = sigmoid_f32(bt[r]);
+    } else {
+      kn[r] = 1.f;
+      bp[r] = bt[r];
+    }
+  }
   if (MULTI && !first) __syncthreads();  // the previous group's LDS reads are done
 #pragma unroll
   for (int j = 0; j < kGroup / NW; ++j) {
@@ -268,12 +299,21 @@ __device__ __forceinline__ void verify_group(const VerifyArgs<TIn>& a, const Str
     // Pick k_t and alpha_t out of the unrolled arrays without dynamic indexing.
     Chan<TIn, CPL> kt = kk[0];
     Chan<float, CPL> at = al[0];
+    float knt = kn[0];
 #pragma unroll
     for (int r = 1; r < kGroup; ++r)
       if (r == t) {
         kt = kk[r];
         at = al[r];
+        knt = kn[r];
       }
+    float qnt = 1.f;
+    if constexpr (PREP) {
+      float q2 = 0.f;
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) q2 = __builtin_fmaf(qt[c], qt[c], q2);
+      qnt = inv_norm(wave_sum(q2));
+    }
     kt.store(st.log_k, kvo_in, tt * st.sk_in);
     at.store(st.log_alpha, kvo_f32, tt * st.sk_f32);
     float pA[kGroup], pP[kGroup];
@@ -281,11 +321,11 @@ __device__ __forceinline__ void verify_group(const VerifyArgs<TIn>& a, const Str
     for (int s = 0; s < kGroup; ++s) pA[s] = pP[s] = 0.f;
 #pragma unroll
     for (int c = 0; c < CPL; ++c) {
-      const float kv = kt[c], qv = qt[c];
-      float gam = al[0][c];
+      const float kv = PREP ? kt[c] * knt : kt[c], qv = PREP ? qt[c] * qnt : qt[c];
+      float gam = av[0][c];
 #pragma unroll
       for (int r = 1; r < kGroup; ++r)
-        if (r <= t) gam *= al[r][c];
+        if (r <= t) gam *= av[r][c];
       const int ix = VerifyLds<DK>::at(ch0 + c);
       L.kap[t][ix] = kv * gam;
       L.rho[t][ix] = qv * gam;
@@ -293,7 +333,7 @@ __device__ __forceinline__ void verify_group(const VerifyArgs<TIn>& a, const Str
         float cof = kv;
 #pragma unroll
         for (int r = 1; r < kGroup; ++r)
-          if (r > t && r < G) cof *= al[r][c];
+          if (r > t && r < G) cof *= av[r][c];
         L.cof[t][ix] = cof;
       }
       // Backward over s = t .. 0 with bb = prod_{s<r<=t} alpha_r.
@@ -301,10 +341,10 @@ __device__ __forceinline__ void verify_group(const VerifyArgs<TIn>& a, const Str
 #pragma unroll
       for (int s = kGroup - 1; s >= 0; --s) {
         if (s <= t) {
-          const float ks = kk[s][c];
+          const float ks = PREP ? kk[s][c] * kn[s] : kk[s][c];
           pP[s] = __builtin_fmaf(qv * ks, bb, pP[s]);
           if (s < t) pA[s] = __builtin_fmaf(kv * ks, bb, pA[s]);
-          bb *= al[s][c];
+          bb *= av[s][c];
         }
       }
     }
@@ -323,10 +363,10 @@ __device__ __forceinline__ void verify_group(const VerifyArgs<TIn>& a, const Str
   if (MULTI && wave == 0) {
 #pragma unroll
     for (int c = 0; c < CPL; ++c) {
-      float gam = al[0][c];
+      float gam = av[0][c];
 #pragma unroll
       for (int r = 1; r < kGroup; ++r)
-        if (r < G) gam *= al[r][c];
+        if (r < G) gam *= av[r][c];
       L.gend[VerifyLds<DK>::at(ch0 + c)] = gam;
     }
   }
@@ -393,7 +433,7 @@ __device__ __forceinline__ void verify_group(const VerifyArgs<TIn>& a, const Str
         float u = x[t][c];
 #pragma unroll
         for (int s = 0; s < t; ++s) u = __builtin_fmaf(L.A[t][s], e[s][c], u);
-        e[t][c] = bt[t] * (vc[c] - u);
+        e[t][c] = bp[t] * (vc[c] - u);
         float w = y[t][c];
 #pragma unroll
         for (int s = 0; s <= t; ++s) w = __builtin_fmaf(L.P[t][s], e[s][c], w);
@@ -436,7 +476,7 @@ __device__ __forceinline__ void verify_group(const VerifyArgs<TIn>& a, const Str
 // COMMIT: first replay the accepted prefix of the pending verify (the commit
 // step, with the decode step's token loop), write the committed state and
 // position, then verify the new tokens from the state still in registers.
-template <int DK, int DV, typename TIn, bool MULTI, bool COMMIT>
+template <int DK, int DV, typename TIn, bool MULTI, bool COMMIT, bool PREP>
 __global__ void __launch_bounds__(kWave * (DV / kSliceCols)) verify_chunk_kernel(VerifyArgs<TIn> a) {
   constexpr int R = DK / kRowGroups;
   __shared__ __align__(16) VerifyLds<DK> L;
@@ -481,10 +521,12 @@ __global__ void __launch_bounds__(kWave * (DV / kSliceCols)) verify_chunk_kernel
     load_state(S);
     if (a.T_pend > 0) {
       const int n = a.accepted[b];
-      if (n < 0 || n > min(a.T_pend, a.log_len[bh])) {
+      const int rec = a.log_len[bh];
+      if (n < 0 || n > min(a.T_pend, log_rows(rec))) {
         if (h == 0 && wave == 0 && lane == 0) atomicOr(a.dev_err, KDA_DEV_ERR_ACCEPTED);
       } else if (n > 0) {
-        replay_log<DK, DV, TIn, R>(S, a.log_k, a.log_v, a.log_alpha, a.log_beta, tok0_log, a.H, n, row0, col0);
+        replay_log<DK, DV, TIn, R, PREP>(S, a.log_k, a.log_v, a.log_alpha, a.log_beta, tok0_log, a.H, n, row0,
+                                         col0, a.pend_gate_sign);
 #pragma unroll
         for (int r = 0; r < R; ++r) {
           const u32x4 w = {__float_as_uint(S[r][0]), __float_as_uint(S[r][1]), __float_as_uint(S[r][2]),
@@ -496,71 +538,77 @@ __global__ void __launch_bounds__(kWave * (DV / kSliceCols)) verify_chunk_kernel
       __syncthreads();  // every wave has read the pending log rows and count before the verify rewrites them
     }
   }
-  if (threadIdx.x == 0) a.log_len[bh] = Tv;
+  if (threadIdx.x == 0) a.log_len[bh] = log_record(Tv, PREP ? kLogRaw + a.gate : kLogPrepared);
   if (Tv == 0) return;
   if (COMMIT) {
     if (MULTI) {
       for (int t0 = 0; t0 < Tv; t0 += kGroup)
-        verify_group<DK, DV, TIn, true>(a, st, L, S, t0, min(kGroup, Tv - t0), tok0, tok0_log, lane, wave, t0 == 0,
+        verify_group<DK, DV, TIn, true, PREP>(a, st, L, S, t0, min(kGroup, Tv - t0), tok0, tok0_log, lane, wave, t0 == 0,
                                         no_load);
     } else {
-      verify_group<DK, DV, TIn, false>(a, st, L, S, 0, Tv, tok0, tok0_log, lane, wave, true, no_load);
+      verify_group<DK, DV, TIn, false, PREP>(a, st, L, S, 0, Tv, tok0, tok0_log, lane, wave, true, no_load);
     }
   } else if (MULTI) {
     for (int t0 = 0; t0 < Tv; t0 += kGroup)
-      verify_group<DK, DV, TIn, true>(a, st, L, S, t0, min(kGroup, Tv - t0), tok0, tok0_log, lane, wave, t0 == 0,
+      verify_group<DK, DV, TIn, true, PREP>(a, st, L, S, t0, min(kGroup, Tv - t0), tok0, tok0_log, lane, wave, t0 == 0,
                                       load_state);
   } else {
-    verify_group<DK, DV, TIn, false>(a, st, L, S, 0, Tv, tok0, tok0_log, lane, wave, true, load_state);
+    verify_group<DK, DV, TIn, false, PREP>(a, st, L, S, 0, Tv, tok0, tok0_log, lane, wave, true, load_state);
   }
 }
 
-template <int DK, int DV, typename TIn, bool COMMIT>
+template <int DK, int DV, typename TIn, bool COMMIT, bool PREP>
 void launch_cfg(const VerifyArgs<TIn>& a, int32_t B, hipStream_t st) {
   const dim3 grid(B * a.H), block(kWave * (DV / kSliceCols));
   if (a.T <= kGroup)
-    verify_chunk_kernel<DK, DV, TIn, false, COMMIT><<<grid, block, 0, st>>>(a);
+    verify_chunk_kernel<DK, DV, TIn, false, COMMIT, PREP><<<grid, block, 0, st>>>(a);
   else
-    verify_chunk_kernel<DK, DV, TIn, true, COMMIT><<<grid, block, 0, st>>>(a);
+    verify_chunk_kernel<DK, DV, TIn, true, COMMIT, PREP><<<grid, block, 0, st>>>(a);
 }
 
-template <typename TIn, bool COMMIT>
+template <typename TIn, bool COMMIT, bool PREP>
 void launch_shape(const kda_shape& s, const VerifyArgs<TIn>& a, hipStream_t st) {
-  if (s.dk == 128 && s.dv == 128) launch_cfg<128, 128, TIn, COMMIT>(a, s.B, st);
-  else if (s.dk == 128) launch_cfg<128, 64, TIn, COMMIT>(a, s.B, st);
-  else if (s.dv == 128) launch_cfg<64, 128, TIn, COMMIT>(a, s.B, st);
-  else launch_cfg<64, 64, TIn, COMMIT>(a, s.B, st);
+  if (s.dk == 128 && s.dv == 128) launch_cfg<128, 128, TIn, COMMIT, PREP>(a, s.B, st);
+  else if (s.dk == 128) launch_cfg<128, 64, TIn, COMMIT, PREP>(a, s.B, st);
+  else if (s.dv == 128) launch_cfg<64, 128, TIn, COMMIT, PREP>(a, s.B, st);
+  else launch_cfg<64, 64, TIn, COMMIT, PREP>(a, s.B, st);
 }
 
+// gate < 0: prepared inputs; otherwise raw projections with that KDA_GATE_*.
 template <typename TIn, bool COMMIT>
 void launch_any(const kda_shape& s, int32_t T_pend, int32_t T, const int32_t* draft_len, float* state, int64_t* pos,
-                const int32_t* accepted, int32_t* dev_err, TokenInputs in, float* o, LogPtrs log, hipStream_t st) {
+                const int32_t* accepted, int32_t* dev_err, TokenInputs in, float* o, LogPtrs log, int32_t gate,
+                int32_t pend_gate, hipStream_t st) {
   const VerifyArgs<TIn> a{state,   (const TIn*)in.q, (const TIn*)in.k, (const TIn*)in.v, in.alpha, in.beta, o,
                           (TIn*)log.k, (TIn*)log.v, log.alpha, log.beta, s.H, T, log.T_max, s.scale, pos, accepted,
-                          dev_err, T_pend, draft_len, log.len};
-  launch_shape<TIn, COMMIT>(s, a, st);
+                          dev_err, T_pend, draft_len, log.len, gate < 0 ? 0 : gate,
+                          gate == KDA_GATE_SIGMOID ? 1.f : -1.f, pend_gate == KDA_GATE_SIGMOID ? 1.f : -1.f};
+  if (gate < 0)
+    launch_shape<TIn, COMMIT, false>(s, a, st);
+  else
+    launch_shape<TIn, COMMIT, true>(s, a, st);
 }
 
 }  // namespace
 
 hipError_t launch_verify(const kda_shape& s, int32_t T, const int32_t* draft_len, const float* state, TokenInputs in,
-                         float* o, LogPtrs log, int32_t* dev_err, hipStream_t st) {
+                         float* o, LogPtrs log, int32_t* dev_err, int32_t gate, hipStream_t st) {
   // The verify-only kernel never writes through `state`.
   float* sp = const_cast<float*>(state);
   if (s.in_dtype == KDA_BF16)
-    launch_any<bf16_t, false>(s, 0, T, draft_len, sp, nullptr, nullptr, dev_err, in, o, log, st);
+    launch_any<bf16_t, false>(s, 0, T, draft_len, sp, nullptr, nullptr, dev_err, in, o, log, gate, -1, st);
   else
-    launch_any<float, false>(s, 0, T, draft_len, sp, nullptr, nullptr, dev_err, in, o, log, st);
+    launch_any<float, false>(s, 0, T, draft_len, sp, nullptr, nullptr, dev_err, in, o, log, gate, -1, st);
   return hipGetLastError();
 }
 
 hipError_t launch_commit_verify(const kda_shape& s, int32_t T_pend, int32_t T, const int32_t* draft_len, float* state,
                                 int64_t* pos, const int32_t* accepted, int32_t* dev_err, TokenInputs in, float* o,
-                                LogPtrs log, hipStream_t st) {
+                                LogPtrs log, int32_t gate, int32_t pend_gate, hipStream_t st) {
   if (s.in_dtype == KDA_BF16)
-    launch_any<bf16_t, true>(s, T_pend, T, draft_len, state, pos, accepted, dev_err, in, o, log, st);
+    launch_any<bf16_t, true>(s, T_pend, T, draft_len, state, pos, accepted, dev_err, in, o, log, gate, pend_gate, st);
   else
-    launch_any<float, true>(s, T_pend, T, draft_len, state, pos, accepted, dev_err, in, o, log, st);
+    launch_any<float, true>(s, T_pend, T, draft_len, state, pos, accepted, dev_err, in, o, log, gate, pend_gate, st);
   return hipGetLastError();
 }
 

@@ -102,6 +102,28 @@ def test_decode_prep_validation(k):
     assert dec(shape(k, B=0), gate=1, state=None, pos=None, q=None, a=None, o=None) == OK
 
 
+def test_prep_verify_validation(k):
+    L = k.lib()
+    s = shape(k)
+    need = k.log_bytes(s, 4)
+    log = k._lib._Log(0x100000, need, 4, 0, 0)
+    ver = lambda gate, T=2, lg=log: L.kda_verify_prep(  # noqa: E731
+        ctypes.byref(s), gate, T, GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, None, ctypes.byref(lg), None)
+    assert ver(3) == SHAPE and ver(-1) == SHAPE
+    assert ver(0) == NULL                                  # o is NULL: rejected before any launch
+    assert ver(0, lg=k._lib._Log(0x100000, need, 4, 0, 7)) == SHAPE   # unknown pending form
+    # The fused calls need the pending verify's form: raw after verify_prep, prepared otherwise.
+    raw_pend = k._lib._Log(0x100000, need, 4, 2, 1)
+    prep_pend = k._lib._Log(0x100000, need, 4, 2, 0)
+    assert L.kda_commit_verify(ctypes.byref(s), 2, GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, GOOD,
+                               ctypes.byref(raw_pend), GOOD, GOOD, None) == ORDER
+    assert L.kda_commit_verify_prep(ctypes.byref(s), 0, 2, GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, GOOD,
+                                    ctypes.byref(prep_pend), GOOD, GOOD, None) == ORDER
+    assert L.kda_commit_verify_prep(ctypes.byref(s), 9, 2, GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, GOOD,
+                                    ctypes.byref(raw_pend), GOOD, GOOD, None) == SHAPE
+    assert raw_pend.pending_T == 2 and raw_pend.pending_form == 1 and prep_pend.pending_form == 0
+
+
 def test_verify_commit_validation(k):
     L = k.lib()
     s = shape(k)

@@ -39,6 +39,8 @@ def run_prep(S, pos, raw, gate, scale=None):
                              d["v"][:, t:t + 1].contiguous(), d["alpha_logit"][:, t:t + 1].contiguous(),
                              d["beta_logit"][:, t:t + 1].contiguous(), o, gate=gate, scale=scale)
         outs.append(o)
+    if not outs:
+        return torch.empty((B, 0, H, dv), dtype=torch.float32, device=S.device)
     return torch.cat(outs, dim=1)
 
 
@@ -122,3 +124,117 @@ def test_decode_prep_saturated_gates_and_zero_vectors():
     S_ref, o_ref = ko.decode(S0, ko.prep(raw, ko.GATE_EXP_NEG_SOFTPLUS), spec.scale)
     assert_parity(o[:, 0].cpu().numpy(), o_ref[:, 2], S.cpu().numpy(), S_ref, "saturated gates, zero vectors")
     assert pos.cpu().tolist() == [3, 3, 3]
+
+
+def _raw_dev(raw):
+    return {name: dev_tensor(np.ascontiguousarray(x)) for name, x in raw.items()}
+
+
+@pytest.mark.parametrize("gate", ["softplus", "sigmoid"])
+@pytest.mark.parametrize("T", [1, 4, 6])
+@pytest.mark.parametrize("dk,dv,dt", [(128, 128, "bf16"), (64, 64, "f32"), (128, 64, "bf16"), (64, 128, "f32")])
+def test_verify_prep_matches_oracle_and_commit_equals_decode_prep(dk, dv, dt, T, gate):
+    spec = spec_for(dk, dv, dt, gate=gate, tag=133)
+    B = 3
+    say(f"verify_prep dk={dk} dv={dv} {dt} T={T} gate={gate}")
+    S0 = synth.initial_state(spec, B)
+    raw = synth.raw_token_inputs(spec, B, T)
+    d = _raw_dev(raw)
+    S = dev_tensor(S0)
+    S_keep = S.clone()
+    log = kda.InputLog(S, T_max=8, in_dtype=d["q"].dtype)
+    o = torch.empty((B, T, spec.H, dv), dtype=torch.float32, device="cuda")
+    kda.verify_prep(S, d["q"], d["k"], d["v"], d["alpha_logit"], d["beta_logit"], o, log, gate=GATES[gate])
+    assert kda.last_variant() == "verify_prep" and log.pending_T == T and log.c.pending_form == 1 + GATES[gate]
+    assert torch.equal(bits(S), bits(S_keep))
+    _, o_ref = ko.decode(S0, ko.prep(raw, GATES[gate]), spec.scale)
+    assert_parity(o.cpu().numpy(), o_ref, what=f"verify_prep T={T}")
+    # The log keeps the raw inputs.
+    es = 2 if dt == "bf16" else 4
+    rows = _log_rows_raw(log, B, T, spec.H, dk, dv, es)
+    for name, reg in zip(("k", "v", "alpha_logit", "beta_logit"), rows):
+        want = d[name].contiguous().view(torch.uint8).view(B, T, spec.H, -1)
+        assert torch.equal(reg, want), name
+    # Commit: bit-identical to that many decode steps from raw projections.
+    acc = [T, 0, min(2, T)]
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    pos = torch.zeros(B, dtype=torch.int64, device="cuda")
+    kda.commit(S, pos, log, torch.tensor(acc, dtype=torch.int32, device="cuda"), err)
+    torch.cuda.synchronize()
+    assert err.item() == 0 and pos.cpu().tolist() == acc
+    for b, a in enumerate(acc):
+        Sb = S_keep[b:b + 1].clone()
+        run_prep(Sb, torch.zeros(1, dtype=torch.int64, device="cuda"),
+                 {k_: v_[b:b + 1, :a] for k_, v_ in raw.items()}, GATES[gate])
+        assert torch.equal(bits(S[b:b + 1]), bits(Sb)), f"commit({a}) != {a} raw decode steps (seq {b})"
+
+
+def _log_rows_raw(log, B, T, H, dk, dv, es):
+    Tm = log.c.T_max
+    r = lambda x: (x + 255) // 256 * 256  # noqa: E731
+    tok = B * Tm * H
+    offs = [0]
+    offs.append(r(offs[0] + tok * dk * es))
+    offs.append(r(offs[1] + tok * dv * es))
+    offs.append(r(offs[2] + tok * dk * 4))
+    out = []
+    for off, width in ((offs[0], dk * es), (offs[1], dv * es), (offs[2], dk * 4), (offs[3], 4)):
+        out.append(log.buf[off:off + tok * width].view(B, Tm, H, width)[:, :T].clone())
+    return out
+
+
+@pytest.mark.parametrize("T1,T2", [(4, 4), (3, 6)])
+def test_commit_verify_prep_equals_separate_calls(T1, T2):
+    spec = spec_for(128, 128, "bf16", tag=134)
+    B = 3
+    say(f"commit_verify_prep T1={T1} T2={T2}")
+    S0 = synth.initial_state(spec, B)
+    raw = synth.raw_token_inputs(spec, B, T1 + T2)
+    d = _raw_dev(raw)
+    r1 = {k_: v_[:, :T1].contiguous() for k_, v_ in d.items()}
+    r2 = {k_: v_[:, T1:].contiguous() for k_, v_ in d.items()}
+    acc = torch.tensor([T1, 0, 1], dtype=torch.int32, device="cuda")
+    outs = {}
+    for path in ("separate", "fused"):
+        S = dev_tensor(S0)
+        pos = torch.zeros(B, dtype=torch.int64, device="cuda")
+        log = kda.InputLog(S, T_max=8)
+        err = torch.zeros(1, dtype=torch.int32, device="cuda")
+        o1 = torch.empty((B, T1, spec.H, 128), device="cuda")
+        o2 = torch.empty((B, T2, spec.H, 128), device="cuda")
+        kda.verify_prep(S, r1["q"], r1["k"], r1["v"], r1["alpha_logit"], r1["beta_logit"], o1, log)
+        if path == "separate":
+            kda.commit(S, pos, log, acc, err)
+            kda.verify_prep(S, r2["q"], r2["k"], r2["v"], r2["alpha_logit"], r2["beta_logit"], o2, log)
+        else:
+            kda.commit_verify_prep(S, pos, r2["q"], r2["k"], r2["v"], r2["alpha_logit"], r2["beta_logit"], o2, log,
+                                   acc, err)
+            assert kda.last_variant() == "commit_verify_prep"
+        S_mid = S.clone()
+        kda.commit(S, pos, log, torch.tensor([1, T2, 0], dtype=torch.int32, device="cuda"), err)
+        torch.cuda.synchronize()
+        assert err.item() == 0
+        outs[path] = (bits(S_mid), bits(o2), bits(S), pos.clone())
+    for x, y in zip(outs["separate"], outs["fused"]):
+        assert torch.equal(x, y)
+
+
+def test_fused_call_needs_the_pending_form():
+    spec = spec_for(128, 128, "bf16", tag=135)
+    B, T = 2, 3
+    S0 = synth.initial_state(spec, B)
+    raw = _raw_dev(synth.raw_token_inputs(spec, B, T))
+    S = dev_tensor(S0)
+    pos = torch.zeros(B, dtype=torch.int64, device="cuda")
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    acc = torch.ones(B, dtype=torch.int32, device="cuda")
+    o = torch.empty((B, T, spec.H, 128), device="cuda")
+    log = kda.InputLog(S, T_max=T)
+    kda.verify_prep(S, raw["q"], raw["k"], raw["v"], raw["alpha_logit"], raw["beta_logit"], o, log)
+    with pytest.raises(kda.KdaError):   # a fused call of prepared inputs cannot replay a raw log
+        kda.commit_verify(S, pos, raw["q"], raw["k"], raw["v"], raw["alpha_logit"], raw["beta_logit"], o, log,
+                          acc, err)
+    assert log.pending_T == T
+    kda.commit(S, pos, log, acc, err)   # the plain commit replays either form
+    torch.cuda.synchronize()
+    assert err.item() == 0 and pos.cpu().tolist() == [1, 1]
