@@ -164,6 +164,37 @@ def bench_decode(torch, kda, synth, B, layers, steps, warmup, device, use_graph=
     }
 
 
+def bench_decode_slots(torch, kda, synth, B, layers, steps, warmup, device):
+    """Decode on states kept in one slot pool (B * layers slots): layer l of
+    step s updates the slots of its own id set, a seeded permutation of the
+    pool, so consecutive sequences read scattered 2 MiB slots."""
+    spec = synth.CONFIGS["batched_decode"]
+    inp = decode_inputs(torch, synth, B, N_TOKENS_IN, device)
+    pool = kda.SlotPool(B * layers, H, DK, DV, device)
+    S0 = dev_tensor(torch, synth.initial_state(spec, B), device)
+    perm = np.random.default_rng(7).permutation(B * layers).astype(np.int32)
+    ids = [torch.from_numpy(perm[l * B:(l + 1) * B].copy()).to(device) for l in range(layers)]
+    for l in range(layers):
+        pool.states[ids[l].long()] = S0
+    err = torch.zeros(1, dtype=torch.int32, device=device)
+    o = torch.empty((B, H, DV), dtype=torch.float32, device=device)
+    graphs = [capture(torch, [kda.DecodeSlotsPlan(ids[l], pool, inp["q"][t], inp["k"][t], inp["v"][t],
+                                                  inp["alpha"][t], inp["beta"][t], o, err) for l in range(layers)])
+              for t in range(N_TOKENS_IN)]
+    for s in range(warmup):
+        graphs[s % N_TOKENS_IN].replay()
+    with Timer(torch) as tm:
+        for s in range(steps):
+            graphs[s % N_TOKENS_IN].replay()
+    launches = steps * layers
+    launch_us = tm.ms * 1e3 / launches
+    bytes_per_launch = DECODE_BYTES * B * H
+    assert err.item() == 0
+    return {"B": B, "layers": layers, "steps": steps, "launch_us": launch_us,
+            "updates_per_s": B * H * launches / (tm.ms / 1e3),
+            "hbm_frac": bytes_per_launch / (launch_us * 1e-6) / 1e9 / HBM_PEAK_GBS}
+
+
 def bench_verify_commit(torch, kda, synth, B, T, rounds, layers, device):
     """Speculative rounds (verify T drafts, commit the accepted prefix) over
     `layers` independent states; verify and commit are captured as separate
@@ -464,6 +495,8 @@ def main():
                                                 use_graph=False)
         log("headline workload from raw projections (input preparation in the kernel)")
         rows["decode_prep_b64"] = bench_decode(torch, kda, synth, B_HEAD, L_LAYERS, 100, 10, device, prep=True)
+        log("headline workload on states in a slot pool (scattered slot ids)")
+        rows["decode_slots_b64"] = bench_decode_slots(torch, kda, synth, B_HEAD, L_LAYERS, 100, 10, device)
         log("copy reference")
         rows["d2d_copy_1GiB"] = bench_copy(torch, device)
         log("hot (cache-resident) decode B=64, one layer")

@@ -81,6 +81,7 @@ typedef enum kda_dtype { KDA_BF16 = 0, KDA_F32 = 1 } kda_dtype;
 #define KDA_DEV_ERR_ACCEPTED 1 /* an accepted count was outside [0, T] */
 #define KDA_DEV_ERR_CKPT_SLOT 2 /* a checkpoint slot id was outside [0, n_slots) */
 #define KDA_DEV_ERR_DRAFT_LEN 4 /* a per-sequence draft length was outside [0, T] */
+#define KDA_DEV_ERR_SLOT_ID 8   /* a device-side state slot id was outside [0, n_slots) */
 
 /* Kernel variants reported by kda_last_variant(). */
 #define KDA_VARIANT_NONE 0
@@ -97,6 +98,8 @@ typedef enum kda_dtype { KDA_BF16 = 0, KDA_F32 = 1 } kda_dtype;
 #define KDA_VARIANT_DECODE_PREP 11
 #define KDA_VARIANT_VERIFY_PREP 12
 #define KDA_VARIANT_COMMIT_VERIFY_PREP 13
+#define KDA_VARIANT_DECODE_SLOTS 14
+#define KDA_VARIANT_SLOT_COPY 15
 
 /* Decay gate of kda_decode_step_prep: alpha = f(x) of the logit x. */
 #define KDA_GATE_EXP_NEG_SOFTPLUS 0 /* alpha = exp(-softplus(x)) = 1 / (1 + e^x) */
@@ -288,6 +291,33 @@ kda_status kda_commit_verify_prep(const kda_shape* shape, int32_t gate, int32_t 
                                   const void* q, const void* k, const void* v, const float* alpha_logit,
                                   const float* beta_logit, float* o, kda_log* log, const int32_t* accepted,
                                   int32_t* dev_err, void* stream);
+
+/*
+ * kda_decode_step on states that live in a slot pool, for serving loops that
+ * keep every request's recurrent state in one pool and reuse cached prefixes
+ * without copying states in and out (webinar summary, paragraph on the two
+ * state systems and their allocation and reuse).  Sequence b of the batch
+ * (inputs and o as kda_decode_step, batch B = shape->B) updates
+ * slots->states[slot_ids[b]] in place and adds 1 to slots->pos[slot_ids[b]].
+ * slot_ids is a DEVICE int32 [B]; the ids must be distinct (two sequences
+ * naming one slot race).  An id outside [0, n_slots) sets KDA_DEV_ERR_SLOT_ID
+ * in *dev_err and that sequence is skipped (its o rows are not written).
+ * The arithmetic is kda_decode_step's, so the states are bit-identical.
+ */
+kda_status kda_decode_step_slots(const kda_shape* shape, const int32_t* slot_ids, const kda_slots* slots,
+                                 const void* q, const void* k, const void* v, const float* alpha,
+                                 const float* beta, float* o, int32_t* dev_err, void* stream);
+
+/*
+ * Slot-to-slot copy of whole states (all H heads) and positions:
+ * slot dst_slots[i] <- slot src_slots[i], i < n (HOST int32 arrays,
+ * range-checked before anything is enqueued: KDA_ERR_SLOT).  Forks a cached
+ * prefix into the slot of a new request.  A destination named twice gets the
+ * later pair; a slot that is both a source and a destination of one call is
+ * rejected (KDA_ERR_SLOT), as the copies run concurrently.  Bitwise.
+ */
+kda_status kda_slot_copy(const kda_shape* shape, const int32_t* src_slots, const int32_t* dst_slots, int32_t n,
+                         const kda_slots* slots, void* stream);
 
 /*
  * Snapshot: copies the whole state of sequence seq_ids[i] (all H heads) and

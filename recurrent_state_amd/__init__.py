@@ -10,11 +10,13 @@ from ._lib import (  # noqa: F401
     DEV_ERR_ACCEPTED,
     DEV_ERR_CKPT_SLOT,
     DEV_ERR_DRAFT_LEN,
+    DEV_ERR_SLOT_ID,
     GATE_EXP_NEG_SOFTPLUS,
     GATE_SIGMOID,
     CommitPlan,
     CommitVerifyPlan,
     DecodePlan,
+    DecodeSlotsPlan,
     LIB_PATH,
     InputLog,
     KdaError,
@@ -27,6 +29,7 @@ from ._lib import (  # noqa: F401
     commit_verify_varlen,
     decode_step,
     decode_step_prep,
+    decode_step_slots,
     exported_symbols,
     last_variant,
     lib,
@@ -35,6 +38,7 @@ from ._lib import (  # noqa: F401
     prefill_recurrent,
     restore,
     slot_bytes,
+    slot_copy,
     snapshot,
     verify,
     verify_prep,

@@ -20,9 +20,10 @@ LIB_PATH = os.path.join(_HERE, "libkda.so")
 KDA_BF16, KDA_F32 = 0, 1
 VARIANTS = {0: "none", 1: "decode", 2: "verify", 3: "commit", 4: "snapshot", 5: "restore",
             6: "prefill_recurrent", 7: "prefill_chunked", 8: "commit_verify", 9: "verify_varlen",
-            10: "commit_verify_varlen", 11: "decode_prep", 12: "verify_prep", 13: "commit_verify_prep"}
+            10: "commit_verify_varlen", 11: "decode_prep", 12: "verify_prep", 13: "commit_verify_prep",
+            14: "decode_slots", 15: "slot_copy"}
 GATE_EXP_NEG_SOFTPLUS, GATE_SIGMOID = 0, 1
-DEV_ERR_ACCEPTED, DEV_ERR_CKPT_SLOT, DEV_ERR_DRAFT_LEN = 1, 2, 4
+DEV_ERR_ACCEPTED, DEV_ERR_CKPT_SLOT, DEV_ERR_DRAFT_LEN, DEV_ERR_SLOT_ID = 1, 2, 4, 8
 
 
 class KdaError(RuntimeError):
@@ -65,6 +66,9 @@ _SIGS = {
                                _P]),
     "kda_commit_verify_varlen": (_I, [ctypes.POINTER(Shape), _I, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                       ctypes.POINTER(_Log), _P, _P, _P]),
+    "kda_decode_step_slots": (_I, [ctypes.POINTER(Shape), _P, ctypes.POINTER(_Slots), _P, _P, _P, _P, _P, _P, _P,
+                                   _P]),
+    "kda_slot_copy": (_I, [ctypes.POINTER(Shape), _P, _P, _I, ctypes.POINTER(_Slots), _P]),
     "kda_snapshot": (_I, [ctypes.POINTER(Shape), _P, _P, _P, _P, _I, ctypes.POINTER(_Slots), _P]),
     "kda_restore": (_I, [ctypes.POINTER(Shape), _P, _P, _P, _P, _I, ctypes.POINTER(_Slots), _P]),
     "kda_prefill_chunked": (_I, [ctypes.POINTER(Shape), _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _I, _P,
@@ -305,6 +309,58 @@ def _pairs(seq_ids, slot_ids):
     if len(seq_ids) != len(slot_ids):
         raise ValueError("seq_ids and slot_ids differ in length")
     return s, t
+
+
+class _Batch:
+    """Stands in for a [B][H][dk][dv] state tensor where only its shape and device matter."""
+
+    def __init__(self, B, pool: SlotPool):
+        _, H, dk, dv = pool.states.shape
+        self.shape = (B, H, dk, dv)
+        self.device = pool.states.device
+
+
+def _decode_slots_args(slot_ids, pool: SlotPool, q, k, v, alpha, beta, o, dev_err, scale):
+    B = slot_ids.shape[0]
+    _need(slot_ids, "slot_ids", (B,), torch.int32, pool.states.device)
+    _need(dev_err, "dev_err", (1,), torch.int32, pool.states.device)
+    if beta.dim() == 2:
+        q, k, v, alpha, beta, o = (x.unsqueeze(1) for x in (q, k, v, alpha, beta, o))
+    batch = _Batch(B, pool)
+    _check_tokens(batch, 1, q, k, v, alpha, beta, o)
+    sh = _shape(batch, q.dtype, scale)
+    return sh, (slot_ids, q, k, v, alpha, beta, o, dev_err)
+
+
+def decode_step_slots(slot_ids, pool: SlotPool, q, k, v, alpha, beta, o, dev_err, scale=None):
+    """decode_step on states in a slot pool: sequence b updates pool slot slot_ids[b] (device int32 [B])."""
+    sh, t = _decode_slots_args(slot_ids, pool, q, k, v, alpha, beta, o, dev_err, scale)
+    slot_ids, q, k, v, alpha, beta, o, dev_err = t
+    _check(lib().kda_decode_step_slots(ctypes.byref(sh), _ptr(slot_ids), ctypes.byref(pool.c), _ptr(q), _ptr(k),
+                                       _ptr(v), _ptr(alpha), _ptr(beta), _ptr(o), _ptr(dev_err), _stream()))
+
+
+class DecodeSlotsPlan:
+    """A decode_step_slots call validated once (see DecodePlan)."""
+
+    def __init__(self, slot_ids, pool: SlotPool, q, k, v, alpha, beta, o, dev_err, scale=None):
+        self._shape, t = _decode_slots_args(slot_ids, pool, q, k, v, alpha, beta, o, dev_err, scale)
+        self._keep = (pool,) + t
+        slot_ids, q, k, v, alpha, beta, o, dev_err = t
+        self._args = (ctypes.byref(self._shape), _ptr(slot_ids), ctypes.byref(pool.c)) + tuple(
+            _ptr(x) for x in (q, k, v, alpha, beta, o, dev_err))
+        self._fn = lib().kda_decode_step_slots
+
+    def __call__(self):
+        _check(self._fn(*self._args, _stream()))
+
+
+def slot_copy(src_slots, dst_slots, pool: SlotPool):
+    """Copy whole states and positions between pool slots: dst_slots[i] <- src_slots[i] (host ids)."""
+    s, t = _pairs(src_slots, dst_slots)
+    _, H, dk, dv = pool.states.shape
+    sh = Shape(0, H, dk, dv, KDA_BF16, 1.0)
+    _check(lib().kda_slot_copy(ctypes.byref(sh), s, t, len(src_slots), ctypes.byref(pool.c), _stream()))
 
 
 def snapshot(state, pos, seq_ids, slot_ids, pool: SlotPool):

@@ -321,6 +321,44 @@ kda_status kda_commit_verify_varlen(const kda_shape* shape, int32_t T, const int
                             -1, stream);
 }
 
+kda_status kda_decode_step_slots(const kda_shape* shape, const int32_t* slot_ids, const kda_slots* slots,
+                                 const void* q, const void* k, const void* v, const float* alpha, const float* beta,
+                                 float* o, int32_t* dev_err, void* stream) {
+  kda_status r = check_shape(shape);
+  if (r != KDA_OK) return r;
+  if ((r = check_slots(slots)) != KDA_OK) return r;
+  if (shape->B == 0) return KDA_OK;
+  if ((r = check_tokens(q, k, v, alpha, beta, o)) != KDA_OK) return r;
+  if (!slot_ids || !dev_err) return KDA_ERR_NULL;
+  if (!aligned(slot_ids, 4) || !aligned(dev_err, 4)) return KDA_ERR_ALIGN;
+  return launched(kda::launch_decode_slots(*shape, slot_ids, slots->states, slots->pos, slots->n_slots,
+                                           kda::TokenInputs{q, k, v, alpha, beta}, o, dev_err,
+                                           static_cast<hipStream_t>(stream)),
+                  KDA_VARIANT_DECODE_SLOTS);
+}
+
+kda_status kda_slot_copy(const kda_shape* shape, const int32_t* src_slots, const int32_t* dst_slots, int32_t n,
+                         const kda_slots* slots, void* stream) {
+  kda_status r = check_shape(shape);
+  if (r != KDA_OK) return r;
+  if ((r = check_slots(slots)) != KDA_OK) return r;
+  if (n < 0) return KDA_ERR_SHAPE;
+  if (n == 0) return KDA_OK;
+  if (!src_slots || !dst_slots) return KDA_ERR_NULL;
+  for (int32_t i = 0; i < n; ++i) {
+    if (src_slots[i] < 0 || src_slots[i] >= slots->n_slots) return KDA_ERR_SLOT;
+    if (dst_slots[i] < 0 || dst_slots[i] >= slots->n_slots) return KDA_ERR_SLOT;
+  }
+  for (int32_t i = 0; i < n; ++i)
+    for (int32_t j = 0; j < n; ++j)
+      if (src_slots[i] == dst_slots[j]) return KDA_ERR_SLOT;  // copies of one call run concurrently
+  const size_t n_floats = (size_t)shape->H * shape->dk * shape->dv;
+  r = copy_pairs(std::vector<int32_t>(src_slots, src_slots + n), std::vector<int32_t>(dst_slots, dst_slots + n),
+                 slots->states, slots->pos, slots->states, slots->pos, n_floats, static_cast<hipStream_t>(stream));
+  if (r == KDA_OK) g_last_variant = KDA_VARIANT_SLOT_COPY;
+  return r;
+}
+
 kda_status kda_snapshot(const kda_shape* shape, const float* state, const int64_t* pos, const int32_t* seq_ids,
                         const int32_t* slot_ids, int32_t n, const kda_slots* slots, void* stream) {
   kda_status r = check_shape(shape);

@@ -65,6 +65,11 @@ hipError_t launch_verify(const kda_shape& s, int32_t T, const int32_t* draft_len
 hipError_t launch_decode_prep(const kda_shape& s, float* state, int64_t* pos, TokenInputs raw, float* o,
                               float gate_sign, hipStream_t st);
 // form: the logged inputs' form (0 prepared, 1 + KDA_GATE_* raw projections).
+// Decode on states in a slot pool: sequence b updates pool_states[slot_ids[b]]
+// and pool_pos[slot_ids[b]]; an id outside [0, n_slots) sets
+// KDA_DEV_ERR_SLOT_ID and that sequence is skipped.
+hipError_t launch_decode_slots(const kda_shape& s, const int32_t* slot_ids, float* pool_states, int64_t* pool_pos,
+                               int32_t n_slots, TokenInputs in, float* o, int32_t* dev_err, hipStream_t st);
 hipError_t launch_commit(const kda_shape& s, int32_t T, float* state, int64_t* pos, LogPtrs log,
                          const int32_t* accepted, int32_t* dev_err, int32_t form, hipStream_t st);
 // Commit of the pending T_pend logged tokens (T_pend = 0: none) followed by

@@ -37,6 +37,10 @@ struct StepArgs {
   int32_t H;
   float scale;
   float gate_sign;     // raw projections: decay = sigmoid(gate_sign * logit)
+  // States in a slot pool: sequence b uses state[slot_ids[b]] and pos[slot_ids[b]].
+  const int32_t* slot_ids;
+  int32_t n_slots;
+  int32_t* dev_err;
 };
 
 template <typename TIn>
@@ -145,13 +149,22 @@ struct Place {
 };
 
 // PREP: the inputs are raw projections and logits, prepared in the step
-// (token_update_prep).
-template <int DK, int DV, typename TIn, int WPG, bool PREP>
+// (token_update_prep).  SLOTS: the states and positions live in a slot pool,
+// addressed through slot_ids (an id out of range is flagged and skipped).
+template <int DK, int DV, typename TIn, int WPG, bool PREP, bool SLOTS>
 __global__ void KDA_OCCUPANCY __launch_bounds__((kWave * waves_per_group<DV, WPG>())) decode_kernel(StepArgs<TIn> a) {
   typedef Place<DK, DV, WPG> P;
   constexpr int R = P::R;
   const P p(a.H);
-  float* sp = a.state + (size_t)p.bh * DK * DV + p.tile_off();
+  int sb = p.b;  // index of the state (and position) this sequence uses
+  if constexpr (SLOTS) {
+    sb = a.slot_ids[p.b];
+    if (sb < 0 || sb >= a.n_slots) {
+      if (p.h == 0 && p.slice == 0 && p.lane == 0) atomicOr(a.dev_err, KDA_DEV_ERR_SLOT_ID);
+      return;
+    }
+  }
+  float* sp = a.state + ((size_t)sb * a.H + p.h) * DK * DV + p.tile_off();
   float S[R][4];
   load_tile<R, DV>(sp, S);
   TokenIn<TIn, R, true> in;
@@ -164,7 +177,7 @@ __global__ void KDA_OCCUPANCY __launch_bounds__((kWave * waves_per_group<DV, WPG
     in.update(S, a.scale, o);
   store_tile<R, DV>(sp, S);
   if (p.rg == 0) *reinterpret_cast<float4*>(a.o + (size_t)p.bh * DV + p.col0) = make_float4(o[0], o[1], o[2], o[3]);
-  if (p.h == 0 && p.slice == 0 && p.lane == 0) a.pos[p.b] += 1;
+  if (p.h == 0 && p.slice == 0 && p.lane == 0) a.pos[sb] += 1;
 }
 
 // RAW: the log holds raw projections and logits (decay sigmoid(gate_sign * x)).
@@ -264,19 +277,21 @@ void dispatch(const kda_shape& s, F&& f) {
 
 namespace {
 
-template <bool PREP>
+template <bool PREP, bool SLOTS>
 hipError_t launch_decode_any(const kda_shape& s, float* state, int64_t* pos, TokenInputs in, float* o,
-                             float gate_sign, hipStream_t st) {
+                             float gate_sign, const int32_t* slot_ids, int32_t n_slots, int32_t* dev_err,
+                             hipStream_t st) {
   dispatch(s, [&](auto c) {
     typedef decltype(c) C;
     typedef typename C::TIn TIn;
     constexpr int DK = C::DK, DV = C::DV;
-    StepArgs<TIn> a{state, pos, (const TIn*)in.q, (const TIn*)in.k, (const TIn*)in.v, in.alpha, in.beta, o,
-                    s.H, s.scale, gate_sign};
+    StepArgs<TIn> a{state, pos,   (const TIn*)in.q, (const TIn*)in.k, (const TIn*)in.v, in.alpha, in.beta, o,
+                    s.H,   s.scale, gate_sign,       slot_ids,         n_slots,          dev_err};
     if (slice_waves<DV>(s) >= kWideWaves)
-      decode_kernel<DK, DV, TIn, 4, PREP><<<grid_of<DK, DV, 4>(s), kWave * waves_per_group<DV, 4>(), 0, st>>>(a);
+      decode_kernel<DK, DV, TIn, 4, PREP, SLOTS>
+          <<<grid_of<DK, DV, 4>(s), kWave * waves_per_group<DV, 4>(), 0, st>>>(a);
     else
-      decode_kernel<DK, DV, TIn, 1, PREP><<<grid_of<DK, DV, 1>(s), kWave, 0, st>>>(a);
+      decode_kernel<DK, DV, TIn, 1, PREP, SLOTS><<<grid_of<DK, DV, 1>(s), kWave, 0, st>>>(a);
   });
   return hipGetLastError();
 }
@@ -285,12 +300,17 @@ hipError_t launch_decode_any(const kda_shape& s, float* state, int64_t* pos, Tok
 
 hipError_t launch_decode(const kda_shape& s, float* state, int64_t* pos, TokenInputs in, float* o,
                          hipStream_t st) {
-  return launch_decode_any<false>(s, state, pos, in, o, 0.f, st);
+  return launch_decode_any<false, false>(s, state, pos, in, o, 0.f, nullptr, 0, nullptr, st);
 }
 
 hipError_t launch_decode_prep(const kda_shape& s, float* state, int64_t* pos, TokenInputs raw, float* o,
                               float gate_sign, hipStream_t st) {
-  return launch_decode_any<true>(s, state, pos, raw, o, gate_sign, st);
+  return launch_decode_any<true, false>(s, state, pos, raw, o, gate_sign, nullptr, 0, nullptr, st);
+}
+
+hipError_t launch_decode_slots(const kda_shape& s, const int32_t* slot_ids, float* pool_states, int64_t* pool_pos,
+                               int32_t n_slots, TokenInputs in, float* o, int32_t* dev_err, hipStream_t st) {
+  return launch_decode_any<false, true>(s, pool_states, pool_pos, in, o, 0.f, slot_ids, n_slots, dev_err, st);
 }
 
 hipError_t launch_commit(const kda_shape& s, int32_t T, float* state, int64_t* pos, LogPtrs log,

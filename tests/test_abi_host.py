@@ -216,6 +216,29 @@ def test_varlen_validation(k):
     assert lg0.pending_T == 3
 
 
+def test_slot_decode_and_copy_validation(k):
+    L = k.lib()
+    s = shape(k, B=4)
+    slots = k._lib._Slots(0x200000, 0x300000, 8)
+    dec = lambda sl=slots, ids=GOOD, err=GOOD, q=GOOD, shp=s: L.kda_decode_step_slots(  # noqa: E731
+        ctypes.byref(shp), ids, ctypes.byref(sl) if sl is not None else None, q, GOOD, GOOD, GOOD, GOOD, GOOD, err,
+        None)
+    assert dec(sl=None) == NULL
+    assert dec(ids=None) == NULL and dec(err=None) == NULL and dec(q=None) == NULL
+    assert dec(ids=P(0x10002)) == ALIGN
+    assert dec(sl=k._lib._Slots(0x200000, 0x300000, -1)) == SHAPE
+    assert dec(shp=shape(k, B=0), ids=None, err=None, q=None) == OK
+    ids = lambda *v: (ctypes.c_int32 * len(v))(*v)  # noqa: E731
+    cp = lambda a, b, n=None: L.kda_slot_copy(ctypes.byref(s), a, b, len(a) if n is None else n,  # noqa: E731
+                                              ctypes.byref(slots), None)
+    assert cp(ids(0), ids(8)) == SLOT and cp(ids(-1), ids(0)) == SLOT
+    assert cp(ids(1, 2), ids(2, 3)) == SLOT, "a slot that is both a source and a destination"
+    assert cp(ids(1), ids(1)) == SLOT
+    assert cp(ids(), ids(), 0) == OK
+    assert cp(ids(0), ids(1), -1) == SHAPE
+    assert L.kda_slot_copy(ctypes.byref(s), None, None, 1, ctypes.byref(slots), None) == NULL
+
+
 def test_snapshot_restore_validation(k):
     L = k.lib()
     s = shape(k, B=4)

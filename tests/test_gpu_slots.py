@@ -1,0 +1,110 @@
+"""Decode on states that live in a slot pool (kda_decode_step_slots) and
+slot-to-slot copies (kda_slot_copy).
+
+Bit for bit: decoding through slot ids equals decoding the same states in a
+dense batch (outputs, states, positions), slots no sequence names are not
+touched, ids out of range are flagged and skipped, and a copied slot decodes
+exactly like its source.  Both workgroup shapes of the decode kernel are
+covered (one-wave workgroups at small batches, whole-state workgroups at
+large ones).
+"""
+
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import recurrent_state_amd as kda
+import synth
+from tests.kda_testutil import bits, dev_tensor, say
+from tests.test_gpu_small import spec_for
+
+pytestmark = pytest.mark.gpu
+
+SENTINEL = 0x7FC0BEEF
+
+
+def _pool(spec, n_slots, seed):
+    pool = kda.SlotPool(n_slots, spec.H, spec.dk, spec.dv, "cuda")
+    g = torch.Generator(device="cuda").manual_seed(seed)
+    pool.states.copy_(torch.randn(pool.states.shape, generator=g, device="cuda") * 0.02)
+    pool.pos.copy_(torch.arange(n_slots, device="cuda") * 10)
+    return pool
+
+
+@pytest.mark.parametrize("dk,dv,dt,B", [(128, 128, "bf16", 4), (64, 64, "f32", 5), (128, 128, "bf16", 128)])
+def test_decode_slots_equals_dense_decode(dk, dv, dt, B):
+    spec = spec_for(dk, dv, dt, tag=150)
+    n_slots = 2 * B + 3
+    say(f"decode_slots dk={dk} dv={dv} {dt} B={B}")
+    pool = _pool(spec, n_slots, 1)
+    ids = np.random.default_rng(2).permutation(n_slots)[:B].astype(np.int32)
+    slot_ids = torch.from_numpy(ids).cuda()
+    S = pool.states[slot_ids.long()].clone()          # the same states as a dense batch
+    pos = pool.pos[slot_ids.long()].clone()
+    untouched = [i for i in range(n_slots) if i not in set(ids.tolist())]
+    keep = bits(pool.states[untouched]).clone()
+    keep_pos = pool.pos[untouched].clone()
+    inp = {name: dev_tensor(x) for name, x in synth.token_inputs(spec, B, 4).items()}
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    for t in range(4):
+        tok = {name: x[:, t:t + 1].contiguous() for name, x in inp.items()}
+        o_s = torch.empty((B, 1, spec.H, dv), device="cuda")
+        o_d = torch.empty_like(o_s)
+        kda.decode_step_slots(slot_ids, pool, tok["q"], tok["k"], tok["v"], tok["alpha"], tok["beta"], o_s, err)
+        assert kda.last_variant() == "decode_slots"
+        kda.decode_step(S, pos, tok["q"], tok["k"], tok["v"], tok["alpha"], tok["beta"], o_d)
+        assert torch.equal(bits(o_s), bits(o_d)), f"token {t}"
+    torch.cuda.synchronize()
+    assert err.item() == 0
+    assert torch.equal(bits(pool.states[slot_ids.long()]), bits(S))
+    assert torch.equal(pool.pos[slot_ids.long()], pos)
+    assert torch.equal(bits(pool.states[untouched]), keep) and torch.equal(pool.pos[untouched], keep_pos)
+
+
+def test_decode_slots_out_of_range_ids_are_flagged_and_skipped():
+    spec = spec_for(128, 128, "bf16", tag=151)
+    B, n_slots = 4, 6
+    pool = _pool(spec, n_slots, 3)
+    before = bits(pool.states).clone()
+    pos_before = pool.pos.clone()
+    slot_ids = torch.tensor([3, n_slots, -1, 0], dtype=torch.int32, device="cuda")
+    inp = {name: dev_tensor(x) for name, x in synth.token_inputs(spec, B, 1).items()}
+    o = torch.full((B, 1, spec.H, 128), SENTINEL, dtype=torch.int32, device="cuda").view(torch.float32)
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    kda.decode_step_slots(slot_ids, pool, inp["q"], inp["k"], inp["v"], inp["alpha"], inp["beta"], o, err)
+    torch.cuda.synchronize()
+    assert err.item() == kda.DEV_ERR_SLOT_ID
+    ob = bits(o)
+    assert (ob[1:3] == SENTINEL).all() and not (ob[0] == SENTINEL).any() and not (ob[3] == SENTINEL).any()
+    changed = [i for i in range(n_slots) if not torch.equal(bits(pool.states[i]), before[i])]
+    assert changed == [0, 3]
+    assert (pool.pos - pos_before).tolist() == [1, 0, 0, 1, 0, 0]
+
+
+def test_slot_copy_forks_a_prefix():
+    spec = spec_for(128, 128, "bf16", tag=152)
+    n_slots = 6
+    say("slot_copy")
+    pool = _pool(spec, n_slots, 4)
+    kda.slot_copy([2, 4], [5, 1], pool)
+    assert kda.last_variant() == "slot_copy"
+    torch.cuda.synchronize()
+    assert torch.equal(bits(pool.states[5]), bits(pool.states[2])) and torch.equal(bits(pool.states[1]),
+                                                                                bits(pool.states[4]))
+    assert pool.pos[5].item() == 20 and pool.pos[1].item() == 40
+    # The fork and its source continue identically on the same tokens.
+    inp = {name: dev_tensor(x) for name, x in synth.token_inputs(spec, 1, 3).items()}
+    both = {name: torch.cat([x, x], dim=0).contiguous() for name, x in inp.items()}
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    slot_ids = torch.tensor([2, 5], dtype=torch.int32, device="cuda")
+    for t in range(3):
+        tok = {name: x[:, t:t + 1].contiguous() for name, x in both.items()}
+        o = torch.empty((2, 1, spec.H, 128), device="cuda")
+        kda.decode_step_slots(slot_ids, pool, tok["q"], tok["k"], tok["v"], tok["alpha"], tok["beta"], o, err)
+        assert torch.equal(bits(o[0]), bits(o[1]))
+    torch.cuda.synchronize()
+    assert torch.equal(bits(pool.states[5]), bits(pool.states[2])) and pool.pos[5].item() == 23
+    with pytest.raises(kda.KdaError):
+        kda.slot_copy([1, 2], [2, 3], pool)    # slot 2 both read and written
