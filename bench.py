@@ -328,7 +328,11 @@ def bench_prefill(torch, kda, synth, device, variant, reps=2):
     every = spec.extra["ckpt_every"]
     # Timing only: the first 1024 seeded tokens tiled 8x along the prompt (the
     # parity tests use the full 8192-token draw).
-    base = synth.token_inputs(spec, B, 1024)
+    if variant == "chunked_prep":   # raw projections and logits, prepared in the kernel
+        r = synth.raw_token_inputs(spec, B, 1024)
+        base = {"q": r["q"], "k": r["k"], "v": r["v"], "alpha": r["alpha_logit"], "beta": r["beta_logit"]}
+    else:
+        base = synth.token_inputs(spec, B, 1024)
     d = {k: dev_tensor(torch, np.concatenate([v] * (L // 1024), axis=1), device) for k, v in base.items()}
     S0 = dev_tensor(torch, synth.initial_state(spec, B), device)
     S = S0.clone()
@@ -338,9 +342,10 @@ def bench_prefill(torch, kda, synth, device, variant, reps=2):
     slots = torch.arange(B * n_ck, dtype=torch.int32, device=device).view(B, n_ck)
     err = torch.zeros(1, dtype=torch.int32, device=device)
     o = torch.empty((B, L, H, DV), dtype=torch.float32, device=device)
-    fn = kda.prefill_chunked if variant == "chunked" else kda.prefill_recurrent
+    fn = {"chunked": kda.prefill_chunked, "chunked_prep": kda.prefill_chunked_prep,
+          "recurrent": kda.prefill_recurrent}[variant]
     kw = dict(ckpt_every=every, ckpt_slots=slots, pool=pool, dev_err=err)
-    if variant == "chunked":
+    if variant != "recurrent":
         kw["chunk"] = spec.extra["chunk"]
 
     def run():
@@ -526,7 +531,7 @@ def main():
         rows["snapshot_restore"] = bench_snapshot_restore(torch, kda, synth, device)
     if not args.quick and "prefill" in picked:
         log("prefill")
-        for variant in ("chunked", "recurrent"):
+        for variant in ("chunked", "chunked_prep", "recurrent"):
             rows[f"prefill_{variant}"] = bench_prefill(torch, kda, synth, device, variant)
 
     cpu = None if args.no_cpu else cpu_baseline(synth)

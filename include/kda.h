@@ -100,6 +100,8 @@ typedef enum kda_dtype { KDA_BF16 = 0, KDA_F32 = 1 } kda_dtype;
 #define KDA_VARIANT_COMMIT_VERIFY_PREP 13
 #define KDA_VARIANT_DECODE_SLOTS 14
 #define KDA_VARIANT_SLOT_COPY 15
+#define KDA_VARIANT_PREFILL_CHUNKED_PREP 16
+#define KDA_VARIANT_PREFILL_RECURRENT_PREP 17
 
 /* Decay gate of kda_decode_step_prep: alpha = f(x) of the logit x. */
 #define KDA_GATE_EXP_NEG_SOFTPLUS 0 /* alpha = exp(-softplus(x)) = 1 / (1 + e^x) */
@@ -370,6 +372,24 @@ kda_status kda_prefill_recurrent(const kda_shape* shape, int32_t L, float* state
                                  const float* beta, float* o, int32_t ckpt_every,
                                  const int32_t* ckpt_slots, const kda_slots* slots, int32_t* dev_err,
                                  void* stream);
+
+/*
+ * The two prefills from raw projections (q, k, alpha_logit, beta_logit as in
+ * kda_decode_step_prep, with the [B][L][H][d] token layout), the inputs
+ * prepared inside the kernels (webinar summary: needless conversions removed).
+ * The token-by-token form is bit-identical to L kda_decode_step_prep calls.
+ * Fails with KDA_ERR_SHAPE for an unknown gate; otherwise as above.
+ */
+kda_status kda_prefill_chunked_prep(const kda_shape* shape, int32_t gate, int32_t L, int32_t chunk, float* state,
+                                    int64_t* pos, const void* q, const void* k, const void* v,
+                                    const float* alpha_logit, const float* beta_logit, float* o, int32_t ckpt_every,
+                                    const int32_t* ckpt_slots, const kda_slots* slots, int32_t* dev_err,
+                                    void* stream);
+kda_status kda_prefill_recurrent_prep(const kda_shape* shape, int32_t gate, int32_t L, float* state, int64_t* pos,
+                                      const void* q, const void* k, const void* v, const float* alpha_logit,
+                                      const float* beta_logit, float* o, int32_t ckpt_every,
+                                      const int32_t* ckpt_slots, const kda_slots* slots, int32_t* dev_err,
+                                      void* stream);
 
 /* Human-readable name of a status code (static string). */
 const char* kda_status_str(kda_status status);

@@ -35,7 +35,9 @@ from ._lib import (  # noqa: F401
     lib,
     log_bytes,
     prefill_chunked,
+    prefill_chunked_prep,
     prefill_recurrent,
+    prefill_recurrent_prep,
     restore,
     slot_bytes,
     slot_copy,

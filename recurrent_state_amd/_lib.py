@@ -21,7 +21,7 @@ KDA_BF16, KDA_F32 = 0, 1
 VARIANTS = {0: "none", 1: "decode", 2: "verify", 3: "commit", 4: "snapshot", 5: "restore",
             6: "prefill_recurrent", 7: "prefill_chunked", 8: "commit_verify", 9: "verify_varlen",
             10: "commit_verify_varlen", 11: "decode_prep", 12: "verify_prep", 13: "commit_verify_prep",
-            14: "decode_slots", 15: "slot_copy"}
+            14: "decode_slots", 15: "slot_copy", 16: "prefill_chunked_prep", 17: "prefill_recurrent_prep"}
 GATE_EXP_NEG_SOFTPLUS, GATE_SIGMOID = 0, 1
 DEV_ERR_ACCEPTED, DEV_ERR_CKPT_SLOT, DEV_ERR_DRAFT_LEN, DEV_ERR_SLOT_ID = 1, 2, 4, 8
 
@@ -75,6 +75,10 @@ _SIGS = {
                                  ctypes.POINTER(_Slots), _P, _P]),
     "kda_prefill_recurrent": (_I, [ctypes.POINTER(Shape), _I, _P, _P, _P, _P, _P, _P, _P, _P, _I, _P,
                                    ctypes.POINTER(_Slots), _P, _P]),
+    "kda_prefill_chunked_prep": (_I, [ctypes.POINTER(Shape), _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _I, _P,
+                                      ctypes.POINTER(_Slots), _P, _P]),
+    "kda_prefill_recurrent_prep": (_I, [ctypes.POINTER(Shape), _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _I, _P,
+                                        ctypes.POINTER(_Slots), _P, _P]),
     "kda_status_str": (ctypes.c_char_p, [_I]),
     "kda_last_variant": (_I, []),
     "kda_abi_version": (_I, []),
@@ -423,6 +427,30 @@ def prefill_recurrent(state, pos, q, k, v, alpha, beta, o, *, ckpt_every=0, ckpt
                                        _ptr(ckpt_slots) if n_ckpt else None,
                                        ctypes.byref(pool.c) if pool is not None else None,
                                        _ptr(dev_err), _stream()))
+
+
+def prefill_chunked_prep(state, pos, q, k, v, alpha_logit, beta_logit, o, *, gate=GATE_EXP_NEG_SOFTPLUS, chunk=64,
+                         ckpt_every=0, ckpt_slots=None, pool: SlotPool | None = None, dev_err=None, scale=None):
+    """prefill_chunked from raw projections and logits (prepared in the kernel)."""
+    L, n_ckpt = _prefill_args(state, pos, q, k, v, alpha_logit, beta_logit, o, ckpt_every, ckpt_slots, pool, dev_err)
+    sh = _shape(state, q.dtype, scale)
+    _check(lib().kda_prefill_chunked_prep(ctypes.byref(sh), int(gate), L, chunk, _ptr(state), _ptr(pos), _ptr(q),
+                                          _ptr(k), _ptr(v), _ptr(alpha_logit), _ptr(beta_logit), _ptr(o), ckpt_every,
+                                          _ptr(ckpt_slots) if n_ckpt else None,
+                                          ctypes.byref(pool.c) if pool is not None else None,
+                                          _ptr(dev_err), _stream()))
+
+
+def prefill_recurrent_prep(state, pos, q, k, v, alpha_logit, beta_logit, o, *, gate=GATE_EXP_NEG_SOFTPLUS,
+                           ckpt_every=0, ckpt_slots=None, pool: SlotPool | None = None, dev_err=None, scale=None):
+    """prefill_recurrent from raw projections and logits (bit-identical to decode_step_prep token by token)."""
+    L, n_ckpt = _prefill_args(state, pos, q, k, v, alpha_logit, beta_logit, o, ckpt_every, ckpt_slots, pool, dev_err)
+    sh = _shape(state, q.dtype, scale)
+    _check(lib().kda_prefill_recurrent_prep(ctypes.byref(sh), int(gate), L, _ptr(state), _ptr(pos), _ptr(q),
+                                            _ptr(k), _ptr(v), _ptr(alpha_logit), _ptr(beta_logit), _ptr(o),
+                                            ckpt_every, _ptr(ckpt_slots) if n_ckpt else None,
+                                            ctypes.byref(pool.c) if pool is not None else None,
+                                            _ptr(dev_err), _stream()))
 
 
 class DecodePlan:

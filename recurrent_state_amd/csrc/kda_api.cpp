@@ -393,10 +393,12 @@ kda_status kda_restore(const kda_shape* shape, float* state, int64_t* pos, const
   return r;
 }
 
-kda_status kda_prefill_chunked(const kda_shape* shape, int32_t L, int32_t chunk, float* state, int64_t* pos,
-                               const void* q, const void* k, const void* v, const float* alpha, const float* beta,
-                               float* o, int32_t ckpt_every, const int32_t* ckpt_slots, const kda_slots* slots,
-                               int32_t* dev_err, void* stream) {
+namespace {
+
+kda_status prefill_chunked_impl(const kda_shape* shape, int32_t L, int32_t chunk, float* state, int64_t* pos,
+                                const void* q, const void* k, const void* v, const float* alpha, const float* beta,
+                                float* o, int32_t ckpt_every, const int32_t* ckpt_slots, const kda_slots* slots,
+                                int32_t* dev_err, int32_t gate, void* stream) {
   kda_status r = check_prefill(shape, L, chunk, state, pos, q, k, v, alpha, beta, o, ckpt_every, ckpt_slots, slots,
                                dev_err);
   if (r != KDA_OK || shape->B == 0) return r;
@@ -404,14 +406,15 @@ kda_status kda_prefill_chunked(const kda_shape* shape, int32_t L, int32_t chunk,
   return launched(kda::launch_prefill_chunked(*shape, L, chunk, state, pos, kda::TokenInputs{q, k, v, alpha, beta},
                                               o, ck ? ckpt_every : 0, ck ? ckpt_slots : nullptr,
                                               ck ? slots->states : nullptr, ck ? slots->pos : nullptr,
-                                              ck ? slots->n_slots : 0, dev_err, static_cast<hipStream_t>(stream)),
-                  KDA_VARIANT_PREFILL_CHUNKED);
+                                              ck ? slots->n_slots : 0, dev_err, gate,
+                                              static_cast<hipStream_t>(stream)),
+                  gate < 0 ? KDA_VARIANT_PREFILL_CHUNKED : KDA_VARIANT_PREFILL_CHUNKED_PREP);
 }
 
-kda_status kda_prefill_recurrent(const kda_shape* shape, int32_t L, float* state, int64_t* pos, const void* q,
-                                 const void* k, const void* v, const float* alpha, const float* beta, float* o,
-                                 int32_t ckpt_every, const int32_t* ckpt_slots, const kda_slots* slots,
-                                 int32_t* dev_err, void* stream) {
+kda_status prefill_recurrent_impl(const kda_shape* shape, int32_t L, float* state, int64_t* pos, const void* q,
+                                  const void* k, const void* v, const float* alpha, const float* beta, float* o,
+                                  int32_t ckpt_every, const int32_t* ckpt_slots, const kda_slots* slots,
+                                  int32_t* dev_err, int32_t gate, void* stream) {
   // Same checks as the chunked form except the chunk size, which does not
   // apply here, so any positive checkpoint interval is allowed.
   kda_status r = check_prefill(shape, L, 32, state, pos, q, k, v, alpha, beta, o, 0, nullptr, nullptr, dev_err);
@@ -426,8 +429,47 @@ kda_status kda_prefill_recurrent(const kda_shape* shape, int32_t L, float* state
   return launched(kda::launch_prefill_recurrent(*shape, L, state, pos, kda::TokenInputs{q, k, v, alpha, beta}, o,
                                                 ck ? ckpt_every : 0, ck ? ckpt_slots : nullptr,
                                                 ck ? slots->states : nullptr, ck ? slots->pos : nullptr,
-                                                ck ? slots->n_slots : 0, dev_err, static_cast<hipStream_t>(stream)),
-                  KDA_VARIANT_PREFILL_RECURRENT);
+                                                ck ? slots->n_slots : 0, dev_err, gate,
+                                                static_cast<hipStream_t>(stream)),
+                  gate < 0 ? KDA_VARIANT_PREFILL_RECURRENT : KDA_VARIANT_PREFILL_RECURRENT_PREP);
+}
+
+}  // namespace
+
+kda_status kda_prefill_chunked(const kda_shape* shape, int32_t L, int32_t chunk, float* state, int64_t* pos,
+                               const void* q, const void* k, const void* v, const float* alpha, const float* beta,
+                               float* o, int32_t ckpt_every, const int32_t* ckpt_slots, const kda_slots* slots,
+                               int32_t* dev_err, void* stream) {
+  return prefill_chunked_impl(shape, L, chunk, state, pos, q, k, v, alpha, beta, o, ckpt_every, ckpt_slots, slots,
+                              dev_err, -1, stream);
+}
+
+kda_status kda_prefill_chunked_prep(const kda_shape* shape, int32_t gate, int32_t L, int32_t chunk, float* state,
+                                    int64_t* pos, const void* q, const void* k, const void* v,
+                                    const float* alpha_logit, const float* beta_logit, float* o, int32_t ckpt_every,
+                                    const int32_t* ckpt_slots, const kda_slots* slots, int32_t* dev_err,
+                                    void* stream) {
+  if (!valid_gate(gate)) return KDA_ERR_SHAPE;
+  return prefill_chunked_impl(shape, L, chunk, state, pos, q, k, v, alpha_logit, beta_logit, o, ckpt_every,
+                              ckpt_slots, slots, dev_err, gate, stream);
+}
+
+kda_status kda_prefill_recurrent(const kda_shape* shape, int32_t L, float* state, int64_t* pos, const void* q,
+                                 const void* k, const void* v, const float* alpha, const float* beta, float* o,
+                                 int32_t ckpt_every, const int32_t* ckpt_slots, const kda_slots* slots,
+                                 int32_t* dev_err, void* stream) {
+  return prefill_recurrent_impl(shape, L, state, pos, q, k, v, alpha, beta, o, ckpt_every, ckpt_slots, slots, dev_err,
+                                -1, stream);
+}
+
+kda_status kda_prefill_recurrent_prep(const kda_shape* shape, int32_t gate, int32_t L, float* state, int64_t* pos,
+                                      const void* q, const void* k, const void* v, const float* alpha_logit,
+                                      const float* beta_logit, float* o, int32_t ckpt_every,
+                                      const int32_t* ckpt_slots, const kda_slots* slots, int32_t* dev_err,
+                                      void* stream) {
+  if (!valid_gate(gate)) return KDA_ERR_SHAPE;
+  return prefill_recurrent_impl(shape, L, state, pos, q, k, v, alpha_logit, beta_logit, o, ckpt_every, ckpt_slots,
+                                slots, dev_err, gate, stream);
 }
 
 const char* kda_status_str(kda_status status) {

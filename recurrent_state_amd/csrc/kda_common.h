@@ -162,6 +162,28 @@ __device__ __forceinline__ float rowgroup_sum(float x) {
   return pair_sum32(pair_sum16(x));
 }
 
+// Sum over all 64 lanes: rotations by 8, 4, 2, 1 inside each 16-lane row,
+// then the two permlane swaps across rows.
+__device__ __forceinline__ float wave_sum(float x) {
+  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x128, 0xf, 0xf, false));
+  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x124, 0xf, 0xf, false));
+  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x122, 0xf, 0xf, false));
+  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x121, 0xf, 0xf, false));
+  return pair_sum32(pair_sum16(x));
+}
+
+// Sum over aligned groups of N = 32 or 64 lanes (N = 64: wave_sum).
+template <int N>
+__device__ __forceinline__ float lane_group_sum(float x) {
+  static_assert(N == 32 || N == 64, "lane group");
+  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x128, 0xf, 0xf, false));
+  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x124, 0xf, 0xf, false));
+  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x122, 0xf, 0xf, false));
+  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x121, 0xf, 0xf, false));
+  x = pair_sum16(x);
+  return N == 64 ? pair_sum32(x) : x;
+}
+
 // One token of the gated delta rule on a lane's R x 4 register tile:
 //   S1 = Diag(alpha) S;  u = S1^T k;  e = beta (v - u);  S = S1 + k e^T
 // and, when WITH_OUT, o = scale (S1^T q + e (k . q)), which equals

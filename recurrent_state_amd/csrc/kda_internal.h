@@ -79,14 +79,15 @@ hipError_t launch_commit(const kda_shape& s, int32_t T, float* state, int64_t* p
 hipError_t launch_commit_verify(const kda_shape& s, int32_t T_pend, int32_t T, const int32_t* draft_len, float* state,
                                 int64_t* pos, const int32_t* accepted, int32_t* dev_err, TokenInputs in, float* o,
                                 LogPtrs log, int32_t gate, int32_t pend_gate, hipStream_t st);
+// Prefills: gate < 0 prepared inputs, otherwise raw projections and logits.
 hipError_t launch_prefill_recurrent(const kda_shape& s, int32_t L, float* state, int64_t* pos,
                                     TokenInputs in, float* o, int32_t ckpt_every, const int32_t* ckpt_slots,
                                     float* slot_states, int64_t* slot_pos, int32_t n_slots,
-                                    int32_t* dev_err, hipStream_t st);
+                                    int32_t* dev_err, int32_t gate, hipStream_t st);
 hipError_t launch_prefill_chunked(const kda_shape& s, int32_t L, int32_t chunk, float* state, int64_t* pos,
                                   TokenInputs in, float* o, int32_t ckpt_every, const int32_t* ckpt_slots,
                                   float* slot_states, int64_t* slot_pos, int32_t n_slots, int32_t* dev_err,
-                                  hipStream_t st);
+                                  int32_t gate, hipStream_t st);
 
 // Copies whole per-sequence states (n_floats each) and positions for up to
 // kMaxPairs (src, dst) index pairs per launch.

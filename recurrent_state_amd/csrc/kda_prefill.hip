@@ -41,6 +41,8 @@
 
 #include <hip/hip_runtime.h>
 
+#include <type_traits>
+
 #include "kda_common.h"
 #include "kda_internal.h"
 
@@ -186,6 +188,7 @@ struct PrefillArgs {
   int32_t ckpt_every;
   int32_t n_slots;
   float scale;
+  float gate_sign;  // raw projections: decay = sigmoid(gate_sign * logit)
 };
 
 // LDS layout of one workgroup (bytes).  Region R2 holds Kh during the A/P
@@ -238,7 +241,11 @@ __device__ __forceinline__ void tri_tile(int ii, int& mt, int& nt) {
   nt = ii - mt * (mt + 1) / 2;
 }
 
-template <int DK, int DV, int CH, typename TIn>
+// PREP: q, k arrive un-normalised and the decay and beta as logits; the
+// preparation phase normalises q and k (one full-wave sum per token: a wave
+// holds every key channel of its tokens) and applies the gates, and the rest
+// of the chunk is the prepared kernel's.
+template <int DK, int DV, int CH, typename TIn, bool PREP>
 __global__ void __launch_bounds__(DV * 4) prefill_chunked_kernel(PrefillArgs<TIn> a) {
   constexpr int NW = DV / 16;        // waves; wave w owns value columns [16 w, 16 w + 16)
   constexpr int NT = 64 * NW;        // threads
@@ -356,12 +363,27 @@ __global__ void __launch_bounds__(DV * 4) prefill_chunked_kernel(PrefillArgs<TIn
 #pragma unroll
     for (int i = 0; i < TPG; ++i) {
       const bool pad = tg * TPG + i >= n;
-      al0[i] = pad ? 1.f : ra[i].lo();  // padding tokens do not decay
-      al1[i] = pad ? 1.f : ra[i].hi();
+      float x0 = ra[i].lo(), x1 = ra[i].hi();
+      if constexpr (PREP) {
+        x0 = sigmoid_f32(a.gate_sign * x0);
+        x1 = sigmoid_f32(a.gate_sign * x1);
+      }
+      al0[i] = pad ? 1.f : x0;  // padding tokens do not decay
+      al1[i] = pad ? 1.f : x1;
       k0[i] = pad ? 0.f : rk[i].lo();
       k1[i] = pad ? 0.f : rk[i].hi();
       q0[i] = pad ? 0.f : rq[i].lo();
       q1[i] = pad ? 0.f : rq[i].hi();
+      if constexpr (PREP) {
+        // The CP lanes of token group tg (an aligned group of 32 or 64 lanes)
+        // hold all DK key channels of token tg TPG + i, two per lane.
+        const float rk_ = inv_norm(lane_group_sum<CP>(__builtin_fmaf(k0[i], k0[i], k1[i] * k1[i])));
+        const float rq_ = inv_norm(lane_group_sum<CP>(__builtin_fmaf(q0[i], q0[i], q1[i] * q1[i])));
+        k0[i] *= rk_;
+        k1[i] *= rk_;
+        q0[i] *= rq_;
+        q1[i] *= rq_;
+      }
     }
 #pragma unroll
     for (int mt = 0; mt < NB; ++mt)
@@ -381,7 +403,7 @@ __global__ void __launch_bounds__(DV * 4) prefill_chunked_kernel(PrefillArgs<TIn
       }
       stot[tg * DK + c0] = s0;
       stot[tg * DK + c0 + 1] = s1;
-      if (cp < TPG) misc(tg * TPG + cp) = tg * TPG + cp < n ? rb : 0.f;  // padding tokens get beta 0
+      if (cp < TPG) misc(tg * TPG + cp) = tg * TPG + cp < n ? (PREP ? sigmoid_f32(rb) : rb) : 0.f;  // padding: beta 0
       __syncthreads();
       float off0 = 0.f, off1 = 0.f, gn0 = 0.f, gn1 = 0.f;
 #pragma unroll
@@ -635,32 +657,40 @@ __global__ void __launch_bounds__(DV * 4) prefill_chunked_kernel(PrefillArgs<TIn
 template <int DK, int DV, typename TIn>
 hipError_t launch_cfg(const kda_shape& s, int32_t L, int32_t chunk, float* state, int64_t* pos, TokenInputs in,
                       float* o, int32_t ckpt_every, const int32_t* ckpt_slots, float* slot_states, int64_t* slot_pos,
-                      int32_t n_slots, int32_t* dev_err, hipStream_t st) {
-  PrefillArgs<TIn> a{state, pos, (const TIn*)in.q, (const TIn*)in.k, (const TIn*)in.v, in.alpha, in.beta, o,
-                     ckpt_slots, slot_states, slot_pos, dev_err, s.H, L, ckpt_every, n_slots, s.scale};
+                      int32_t n_slots, int32_t* dev_err, int32_t gate, hipStream_t st) {
+  PrefillArgs<TIn> a{state,      pos,     (const TIn*)in.q, (const TIn*)in.k, (const TIn*)in.v, in.alpha, in.beta,
+                     o,          ckpt_slots, slot_states,  slot_pos,         dev_err,          s.H,      L,
+                     ckpt_every, n_slots, s.scale,         gate == KDA_GATE_SIGMOID ? 1.f : -1.f};
   const dim3 grid((unsigned)((size_t)s.B * s.H));
-  if (chunk == 64)
-    prefill_chunked_kernel<DK, DV, 64, TIn><<<grid, 4 * DV, 0, st>>>(a);
+  auto go = [&](auto prep) {
+    constexpr bool PREP = decltype(prep)::value;
+    if (chunk == 64)
+      prefill_chunked_kernel<DK, DV, 64, TIn, PREP><<<grid, 4 * DV, 0, st>>>(a);
+    else
+      prefill_chunked_kernel<DK, DV, 32, TIn, PREP><<<grid, 4 * DV, 0, st>>>(a);
+  };
+  if (gate < 0)
+    go(std::false_type{});
   else
-    prefill_chunked_kernel<DK, DV, 32, TIn><<<grid, 4 * DV, 0, st>>>(a);
+    go(std::true_type{});
   return hipGetLastError();
 }
 
 template <typename TIn>
 hipError_t launch_dtype(const kda_shape& s, int32_t L, int32_t chunk, float* state, int64_t* pos, TokenInputs in,
                         float* o, int32_t ckpt_every, const int32_t* ckpt_slots, float* slot_states, int64_t* slot_pos,
-                        int32_t n_slots, int32_t* dev_err, hipStream_t st) {
+                        int32_t n_slots, int32_t* dev_err, int32_t gate, hipStream_t st) {
   if (s.dk == 128 && s.dv == 128)
     return launch_cfg<128, 128, TIn>(s, L, chunk, state, pos, in, o, ckpt_every, ckpt_slots, slot_states, slot_pos,
-                                     n_slots, dev_err, st);
+                                     n_slots, dev_err, gate, st);
   if (s.dk == 128 && s.dv == 64)
     return launch_cfg<128, 64, TIn>(s, L, chunk, state, pos, in, o, ckpt_every, ckpt_slots, slot_states, slot_pos,
-                                    n_slots, dev_err, st);
+                                    n_slots, dev_err, gate, st);
   if (s.dk == 64 && s.dv == 128)
     return launch_cfg<64, 128, TIn>(s, L, chunk, state, pos, in, o, ckpt_every, ckpt_slots, slot_states, slot_pos,
-                                    n_slots, dev_err, st);
+                                    n_slots, dev_err, gate, st);
   return launch_cfg<64, 64, TIn>(s, L, chunk, state, pos, in, o, ckpt_every, ckpt_slots, slot_states, slot_pos,
-                                 n_slots, dev_err, st);
+                                 n_slots, dev_err, gate, st);
 }
 
 }  // namespace
@@ -668,13 +698,13 @@ hipError_t launch_dtype(const kda_shape& s, int32_t L, int32_t chunk, float* sta
 hipError_t launch_prefill_chunked(const kda_shape& s, int32_t L, int32_t chunk, float* state, int64_t* pos,
                                   TokenInputs in, float* o, int32_t ckpt_every, const int32_t* ckpt_slots,
                                   float* slot_states, int64_t* slot_pos, int32_t n_slots, int32_t* dev_err,
-                                  hipStream_t st) {
+                                  int32_t gate, hipStream_t st) {
   if (chunk != 32 && chunk != 64) return hipErrorInvalidValue;
   if (s.in_dtype == KDA_BF16)
     return launch_dtype<bf16_t>(s, L, chunk, state, pos, in, o, ckpt_every, ckpt_slots, slot_states, slot_pos,
-                                n_slots, dev_err, st);
+                                n_slots, dev_err, gate, st);
   return launch_dtype<float>(s, L, chunk, state, pos, in, o, ckpt_every, ckpt_slots, slot_states, slot_pos, n_slots,
-                             dev_err, st);
+                             dev_err, gate, st);
 }
 
 }  // namespace kda

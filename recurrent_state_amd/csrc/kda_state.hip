@@ -79,6 +79,7 @@ struct PrefillArgs {
   int32_t ckpt_every;
   int32_t n_slots;
   float scale;
+  float gate_sign;  // raw projections: decay = sigmoid(gate_sign * logit)
 };
 
 // Waves per workgroup (WPG): the column slices of one (sequence, head) are
@@ -201,7 +202,9 @@ __global__ void KDA_OCCUPANCY __launch_bounds__((kWave * waves_per_group<DV, WPG
   if (p.h == 0 && p.slice == 0 && p.lane == 0) a.pos[p.b] += n;
 }
 
-template <int DK, int DV, typename TIn>
+// PREP: raw projections and logits, prepared in every step (the decode step
+// from raw projections, token by token).
+template <int DK, int DV, typename TIn, bool PREP>
 __global__ void KDA_OCCUPANCY __launch_bounds__(kWave) prefill_recurrent_kernel(PrefillArgs<TIn> a) {
   typedef Place<DK, DV, 1> P;
   constexpr int R = P::R;
@@ -223,7 +226,10 @@ __global__ void KDA_OCCUPANCY __launch_bounds__(kWave) prefill_recurrent_kernel(
       nxt.load(a.k + tn * DK + p.row0, a.q + tn * DK + p.row0, a.alpha + tn * DK + p.row0,
                a.v + tn * DV + p.col0, a.beta + tn);
     float o[4];
-    cur.update(S, a.scale, o);
+    if constexpr (PREP)
+      cur.update_prep(S, a.gate_sign, a.scale, o);
+    else
+      cur.update(S, a.scale, o);
     if (p.rg == 0) *reinterpret_cast<float4*>(a.o + tok * DV + p.col0) = make_float4(o[0], o[1], o[2], o[3]);
     if (n_ckpt > 0 && (t + 1) % a.ckpt_every == 0) {
       const int m = (t + 1) / a.ckpt_every - 1;
@@ -339,14 +345,19 @@ hipError_t launch_commit(const kda_shape& s, int32_t T, float* state, int64_t* p
 
 hipError_t launch_prefill_recurrent(const kda_shape& s, int32_t L, float* state, int64_t* pos, TokenInputs in,
                                     float* o, int32_t ckpt_every, const int32_t* ckpt_slots, float* slot_states,
-                                    int64_t* slot_pos, int32_t n_slots, int32_t* dev_err, hipStream_t st) {
+                                    int64_t* slot_pos, int32_t n_slots, int32_t* dev_err, int32_t gate,
+                                    hipStream_t st) {
   dispatch(s, [&](auto c) {
     typedef decltype(c) C;
     typedef typename C::TIn TIn;
     constexpr int DK = C::DK, DV = C::DV;
-    PrefillArgs<TIn> a{state, pos, (const TIn*)in.q, (const TIn*)in.k, (const TIn*)in.v, in.alpha, in.beta, o,
-                       ckpt_slots, slot_states, slot_pos, dev_err, s.H, L, ckpt_every, n_slots, s.scale};
-    prefill_recurrent_kernel<DK, DV, TIn><<<grid_of<DK, DV, 1>(s), kWave, 0, st>>>(a);
+    PrefillArgs<TIn> a{state,    pos,     (const TIn*)in.q, (const TIn*)in.k, (const TIn*)in.v, in.alpha, in.beta,
+                       o,        ckpt_slots, slot_states,  slot_pos,         dev_err,          s.H,      L,
+                       ckpt_every, n_slots, s.scale,       gate == KDA_GATE_SIGMOID ? 1.f : -1.f};
+    if (gate < 0)
+      prefill_recurrent_kernel<DK, DV, TIn, false><<<grid_of<DK, DV, 1>(s), kWave, 0, st>>>(a);
+    else
+      prefill_recurrent_kernel<DK, DV, TIn, true><<<grid_of<DK, DV, 1>(s), kWave, 0, st>>>(a);
   });
   return hipGetLastError();
 }

@@ -99,16 +99,6 @@ struct VerifyLds {
   static __device__ __forceinline__ int at(int ch) { return (ch / R) * RP + ch % R; }
 };
 
-// Sum over all 64 lanes: rotations by 8, 4, 2, 1 inside each 16-lane row,
-// then the two permlane swaps across rows.
-__device__ __forceinline__ float wave_sum(float x) {
-  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x128, 0xf, 0xf, false));
-  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x124, 0xf, 0xf, false));
-  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x122, 0xf, 0xf, false));
-  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x121, 0xf, 0xf, false));
-  return pair_sum32(pair_sum16(x));
-}
-
 // Buffer-resource access: one SGPR base + range per tensor window, a 32-bit
 // lane offset in a VGPR and uniform offsets in SGPRs, so no 64-bit address
 // is kept per load.

@@ -122,6 +122,13 @@ def test_prep_verify_validation(k):
     assert L.kda_commit_verify_prep(ctypes.byref(s), 9, 2, GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, GOOD,
                                     ctypes.byref(raw_pend), GOOD, GOOD, None) == SHAPE
     assert raw_pend.pending_T == 2 and raw_pend.pending_form == 1 and prep_pend.pending_form == 0
+    slots = k._lib._Slots(0x200000, 0x300000, 8)
+    assert L.kda_prefill_chunked_prep(ctypes.byref(s), 2, 64, 64, GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, 0,
+                                      None, ctypes.byref(slots), None, None) == SHAPE
+    assert L.kda_prefill_recurrent_prep(ctypes.byref(s), -1, 64, GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, 0,
+                                        None, ctypes.byref(slots), None, None) == SHAPE
+    assert L.kda_prefill_chunked_prep(ctypes.byref(s), 1, 64, 48, GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, 0,
+                                      None, ctypes.byref(slots), None, None) == SHAPE   # chunk 48
 
 
 def test_verify_commit_validation(k):

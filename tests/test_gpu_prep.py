@@ -19,7 +19,7 @@ import torch
 import recurrent_state_amd as kda
 import synth
 from oracle import kda_oracle as ko
-from tests.kda_testutil import assert_parity, bits, dev_tensor, say
+from tests.kda_testutil import assert_parity, bits, dev_tensor, say, state_err
 from tests.test_gpu_small import SHAPES, spec_for
 
 pytestmark = pytest.mark.gpu
@@ -238,3 +238,56 @@ def test_fused_call_needs_the_pending_form():
     kda.commit(S, pos, log, acc, err)   # the plain commit replays either form
     torch.cuda.synchronize()
     assert err.item() == 0 and pos.cpu().tolist() == [1, 1]
+
+
+@pytest.mark.parametrize("gate", ["softplus", "sigmoid"])
+@pytest.mark.parametrize("dk,dv,dt", [(128, 128, "bf16"), (64, 64, "f32"), (128, 64, "bf16")])
+def test_prefill_recurrent_prep_equals_decode_prep_steps(dk, dv, dt, gate):
+    spec = spec_for(dk, dv, dt, gate=gate, tag=136)
+    B, L = 2, 37
+    say(f"prefill_recurrent_prep dk={dk} dv={dv} {dt} {gate}")
+    S0 = synth.initial_state(spec, B)
+    raw = synth.raw_token_inputs(spec, B, L)
+    d = _raw_dev(raw)
+    S = dev_tensor(S0)
+    pos = torch.zeros(B, dtype=torch.int64, device="cuda")
+    o = torch.empty((B, L, spec.H, dv), device="cuda")
+    kda.prefill_recurrent_prep(S, pos, d["q"], d["k"], d["v"], d["alpha_logit"], d["beta_logit"], o,
+                               gate=GATES[gate])
+    assert kda.last_variant() == "prefill_recurrent_prep"
+    S2 = dev_tensor(S0)
+    pos2 = torch.zeros(B, dtype=torch.int64, device="cuda")
+    o2 = run_prep(S2, pos2, raw, GATES[gate])
+    assert torch.equal(bits(S), bits(S2)) and torch.equal(bits(o), bits(o2)) and torch.equal(pos, pos2)
+
+
+@pytest.mark.parametrize("gate", ["softplus", "sigmoid"])
+@pytest.mark.parametrize("chunk,L", [(64, 200), (32, 37), (64, 64)])
+@pytest.mark.parametrize("dk,dv,dt", [(128, 128, "bf16"), (64, 64, "f32"), (64, 128, "bf16")])
+def test_prefill_chunked_prep_matches_oracle(dk, dv, dt, chunk, L, gate):
+    spec = spec_for(dk, dv, dt, gate=gate, tag=137)
+    B = 2
+    every = chunk
+    say(f"prefill_chunked_prep dk={dk} dv={dv} {dt} chunk={chunk} L={L} {gate}")
+    S0 = synth.initial_state(spec, B)
+    raw = synth.raw_token_inputs(spec, B, L)
+    d = _raw_dev(raw)
+    S = dev_tensor(S0)
+    pos = torch.tensor([5, 0], dtype=torch.int64, device="cuda")
+    n_ck = L // every
+    pool = kda.SlotPool(2 * n_ck, spec.H, dk, dv, "cuda")
+    slots = torch.arange(2 * n_ck, dtype=torch.int32, device="cuda").view(2, n_ck)
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    o = torch.full((B, L, spec.H, dv), float("nan"), device="cuda")
+    kda.prefill_chunked_prep(S, pos, d["q"], d["k"], d["v"], d["alpha_logit"], d["beta_logit"], o, gate=GATES[gate],
+                             chunk=chunk, ckpt_every=every, ckpt_slots=slots, pool=pool, dev_err=err)
+    assert kda.last_variant() == "prefill_chunked_prep"
+    S_ref, pos_ref, o_ref, ck = ko.prefill(S0, np.array([5, 0]), ko.prep(raw, GATES[gate]), spec.scale, every)
+    assert_parity(o.cpu().numpy(), o_ref, S.cpu().numpy(), S_ref, f"prefill_chunked_prep L={L} chunk={chunk}")
+    torch.cuda.synchronize()
+    assert pos.cpu().tolist() == pos_ref.tolist() and err.item() == 0
+    for m, (Sm, pm) in enumerate(ck):
+        for b in range(B):
+            slot = b * n_ck + m
+            assert state_err(pool.states[slot:slot + 1].cpu().numpy(), Sm[b:b + 1]) <= 1e-3
+            assert pool.pos[slot].item() == pm[b]
