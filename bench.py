@@ -537,6 +537,8 @@ def main():
     cpu = None if args.no_cpu else cpu_baseline(synth)
     bytes_per_launch = DECODE_BYTES * B_HEAD * H
     line = {
+        "device": {"name": props.name, "compute_units": props.multi_processor_count,
+                   "memory_bytes": props.total_memory},
         "metric": "KDA state-updates/s (tokens*heads/s) and % HBM roofline, B=1..64, 1 GPU",
         "value": head["updates_per_s"],
         "unit": "state-updates/s",

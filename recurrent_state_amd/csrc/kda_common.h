@@ -366,6 +366,38 @@ struct TokenIn {
 // matching kind.  Callers pick RAW from the log record before loading any
 // state, so each form runs as its own code path.
 template <int DK, int DV, typename TIn, int R, bool RAW>
+struct LogReplay {
+  const TIn* k;
+  const TIn* v;
+  const float* alpha;
+  const float* beta;
+  size_t tok0;
+  int H, row0, col0;
+  TokenIn<TIn, R, false> cur, nxt;
+  __device__ __forceinline__ void load(int t, TokenIn<TIn, R, false>& x) const {
+    const size_t tk = tok0 + (size_t)t * H;
+    x.load(k + tk * DK + row0, nullptr, alpha + tk * DK + row0, v + tk * DV + col0, beta + tk);
+  }
+  // Issues the loads of logged token 0 (present whenever a verify is pending),
+  // so they can be in flight before the count is known or the state loaded.
+  __device__ __forceinline__ void prime() { load(0, cur); }
+  // Applies logged tokens 0 .. n-1 (token 0 primed); the loads of token t + 1
+  // are issued before token t's update, so each token's memory latency hides
+  // behind the previous update.
+  __device__ __forceinline__ void run(float (&S)[R][4], int n, float gsign) {
+    for (int t = 0; t < n; ++t) {
+      if (t + 1 < n) load(t + 1, nxt);
+      float o[4];
+      if constexpr (RAW)
+        cur.update_prep(S, gsign, 0.f, o);
+      else
+        cur.update(S, 0.f, o);
+      cur = nxt;
+    }
+  }
+};
+
+template <int DK, int DV, typename TIn, int R, bool RAW>
 __device__ __forceinline__ void replay_log(float (&S)[R][4], const TIn* log_k, const TIn* log_v,
                                            const float* log_alpha, const float* log_beta, size_t tok0, int H,
                                            int n, int row0, int col0, float gsign) {

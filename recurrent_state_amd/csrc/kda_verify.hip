@@ -41,6 +41,8 @@
 
 #include <hip/hip_runtime.h>
 
+#include <type_traits>
+
 #include "kda_common.h"
 #include "kda_internal.h"
 
@@ -466,7 +468,10 @@ __device__ __forceinline__ void verify_group(const VerifyArgs<TIn>& a, const Str
 // COMMIT: first replay the accepted prefix of the pending verify (the commit
 // step, with the decode step's token loop), write the committed state and
 // position, then verify the new tokens from the state still in registers.
-template <int DK, int DV, typename TIn, bool MULTI, bool COMMIT, bool PREP>
+// PF (with COMMIT): the replay keeps the next logged token's loads in flight
+// (double-buffered, more registers): for small batches, where the round is
+// bound by the latency of one workgroup's serial replay, not by bandwidth.
+template <int DK, int DV, typename TIn, bool MULTI, bool COMMIT, bool PREP, bool PF>
 __global__ void __launch_bounds__(kWave * (DV / kSliceCols)) verify_chunk_kernel(VerifyArgs<TIn> a) {
   constexpr int R = DK / kRowGroups;
   __shared__ __align__(16) VerifyLds<DK> L;
@@ -508,6 +513,8 @@ __global__ void __launch_bounds__(kWave * (DV / kSliceCols)) verify_chunk_kernel
     }
   }
   if (COMMIT) {
+    LogReplay<DK, DV, TIn, R, PREP> rp{a.log_k, a.log_v, a.log_alpha, a.log_beta, tok0_log, a.H, row0, col0};
+    if (PF && a.T_pend > 0) rp.prime();  // logged token 0's loads go out ahead of the state tile
     load_state(S);
     if (a.T_pend > 0) {
       const int n = a.accepted[b];
@@ -515,8 +522,11 @@ __global__ void __launch_bounds__(kWave * (DV / kSliceCols)) verify_chunk_kernel
       if (n < 0 || n > min(a.T_pend, log_rows(rec))) {
         if (h == 0 && wave == 0 && lane == 0) atomicOr(a.dev_err, KDA_DEV_ERR_ACCEPTED);
       } else if (n > 0) {
-        replay_log<DK, DV, TIn, R, PREP>(S, a.log_k, a.log_v, a.log_alpha, a.log_beta, tok0_log, a.H, n, row0,
-                                         col0, a.pend_gate_sign);
+        if constexpr (PF)
+          rp.run(S, n, a.pend_gate_sign);
+        else
+          replay_log<DK, DV, TIn, R, PREP>(S, a.log_k, a.log_v, a.log_alpha, a.log_beta, tok0_log, a.H, n, row0,
+                                           col0, a.pend_gate_sign);
 #pragma unroll
         for (int r = 0; r < R; ++r) {
           const u32x4 w = {__float_as_uint(S[r][0]), __float_as_uint(S[r][1]), __float_as_uint(S[r][2]),
@@ -547,13 +557,26 @@ __global__ void __launch_bounds__(kWave * (DV / kSliceCols)) verify_chunk_kernel
   }
 }
 
+// Below this many (sequence, head) pairs the fused round prefetches its replay.
+constexpr int kLatencyPairs = 512;
+
 template <int DK, int DV, typename TIn, bool COMMIT, bool PREP>
 void launch_cfg(const VerifyArgs<TIn>& a, int32_t B, hipStream_t st) {
   const dim3 grid(B * a.H), block(kWave * (DV / kSliceCols));
-  if (a.T <= kGroup)
-    verify_chunk_kernel<DK, DV, TIn, false, COMMIT, PREP><<<grid, block, 0, st>>>(a);
-  else
-    verify_chunk_kernel<DK, DV, TIn, true, COMMIT, PREP><<<grid, block, 0, st>>>(a);
+  auto go = [&](auto pf) {
+    constexpr bool PF = decltype(pf)::value;
+    if (a.T <= kGroup)
+      verify_chunk_kernel<DK, DV, TIn, false, COMMIT, PREP, PF><<<grid, block, 0, st>>>(a);
+    else
+      verify_chunk_kernel<DK, DV, TIn, true, COMMIT, PREP, PF><<<grid, block, 0, st>>>(a);
+  };
+  if constexpr (COMMIT) {
+    if (B * a.H < kLatencyPairs) {
+      go(std::true_type{});
+      return;
+    }
+  }
+  go(std::false_type{});
 }
 
 template <typename TIn, bool COMMIT, bool PREP>

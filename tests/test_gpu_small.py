@@ -482,3 +482,37 @@ def test_workgroup_shapes_bit_identical():
         assert torch.equal(bits(Sc), bits(S)), f"commit({T}) != {T} decode steps at B={B}"
         res[B] = (bits(S[:2]).clone(), bits(o_dec[:2]).clone())
     assert torch.equal(res[2][0], res[Bbig][0]) and torch.equal(res[2][1], res[Bbig][1])
+
+
+@pytest.mark.parametrize("T1,T2", [(4, 4), (7, 7)])
+def test_commit_verify_large_batch_equals_separate_calls(T1, T2):
+    # Batches of 512 (sequence, head) pairs and more take the fused kernel
+    # without the replay prefetch that small batches use; both must equal
+    # commit followed by verify bit for bit.
+    spec = synth.ConfigSpec("cvlarge", 116, (17,), 32, 128, 128, "bf16", "softplus", "normal", 0)
+    B = 17
+    say(f"commit_verify large batch T1={T1} T2={T2}")
+    S0 = synth.initial_state(spec, B)
+    d = dev_inputs(synth.token_inputs(spec, B, T1 + T2))
+    r1 = {k_: v_[:, :T1].contiguous() for k_, v_ in d.items()}
+    r2 = {k_: v_[:, T1:].contiguous() for k_, v_ in d.items()}
+    acc = torch.tensor(np.random.default_rng(5).integers(0, T1 + 1, B), dtype=torch.int32, device="cuda")
+    outs = {}
+    for path in ("separate", "fused"):
+        S = dev_tensor(S0)
+        pos = torch.zeros(B, dtype=torch.int64, device="cuda")
+        log = kda.InputLog(S, T_max=8)
+        err = torch.zeros(1, dtype=torch.int32, device="cuda")
+        o1 = torch.empty((B, T1, spec.H, 128), device="cuda")
+        o2 = torch.empty((B, T2, spec.H, 128), device="cuda")
+        kda.verify(S, r1["q"], r1["k"], r1["v"], r1["alpha"], r1["beta"], o1, log)
+        if path == "separate":
+            kda.commit(S, pos, log, acc, err)
+            kda.verify(S, r2["q"], r2["k"], r2["v"], r2["alpha"], r2["beta"], o2, log)
+        else:
+            kda.commit_verify(S, pos, r2["q"], r2["k"], r2["v"], r2["alpha"], r2["beta"], o2, log, acc, err)
+        torch.cuda.synchronize()
+        assert err.item() == 0
+        outs[path] = (bits(S), bits(o2), pos.clone())
+    for x, y in zip(outs["separate"], outs["fused"]):
+        assert torch.equal(x, y)
