@@ -537,8 +537,6 @@ def main():
     cpu = None if args.no_cpu else cpu_baseline(synth)
     bytes_per_launch = DECODE_BYTES * B_HEAD * H
     line = {
-        "device": {"name": props.name, "compute_units": props.multi_processor_count,
-                   "memory_bytes": props.total_memory},
         "metric": "KDA state-updates/s (tokens*heads/s) and % HBM roofline, B=1..64, 1 GPU",
         "value": head["updates_per_s"],
         "unit": "state-updates/s",
@@ -555,7 +553,9 @@ def main():
         "config": {"workload": "batched decode, B=64, H=32, dk=dv=128, bf16 q/k/v, fp32 state; one step = one "
                                "token through 8 independent layer states (1 GiB)",
                    "B": B_HEAD, "H": H, "dk": DK, "dv": DV, "layers": L_LAYERS, "in_dtype": "bf16"},
-        "roofline": {"bound": "hbm", "kernel": "decode_kernel<128,128,bf16>",
+        "device": {"name": props.name, "compute_units": props.multi_processor_count,
+                   "memory_bytes": props.total_memory},
+        "roofline": {"bound": "hbm", "kernel": "decode_kernel<128,128,bf16,4,false,false>",
                      "achieved": head["achieved_GBs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": head["achieved_GBs"] / HBM_PEAK_GBS, "traffic": counted_traffic(),
                      "algorithmic_bytes_per_launch": bytes_per_launch, "launch_us": head["launch_us"]},
