@@ -414,6 +414,35 @@ def bench_snapshot_restore(torch, kda, synth, device, reps=20):
             "restore_hbm_frac": nbytes / (tr.ms * 1e-3 / reps) / 1e9 / HBM_PEAK_GBS}
 
 
+def bench_resume(torch, kda, synth, device, steps=128):
+    """The prefill workload's resume: restore the 8 sequences' mid-prompt
+    checkpoints from a 64-slot pool into the live states, then 128 decode
+    steps on fresh tokens (one layer, graph-replayed steps)."""
+    spec = synth.CONFIGS["prefill"]
+    B = spec.B[0]
+    pool = kda.SlotPool(8 * B, H, DK, DV, device)
+    pool.states.normal_(0.0, 0.02)
+    pool.pos.copy_(torch.arange(8 * B, device=device) * 1024)
+    S = torch.zeros((B, H, DK, DV), device=device)
+    pos = torch.zeros(B, dtype=torch.int64, device=device)
+    inp = decode_inputs(torch, synth, B, N_TOKENS_IN, device)
+    o = torch.empty((B, H, DV), dtype=torch.float32, device=device)
+    graphs = [capture(torch, [kda.DecodePlan(S, pos, inp["q"][t], inp["k"][t], inp["v"][t], inp["alpha"][t],
+                                             inp["beta"][t], o)]) for t in range(N_TOKENS_IN)]
+    seqs, slots = list(range(B)), [8 * b + 3 for b in range(B)]   # the checkpoint at token 4096
+    kda.restore(S, pos, seqs, slots, pool)
+    for s in range(8):
+        graphs[s % N_TOKENS_IN].replay()
+    with Timer(torch) as tr:
+        kda.restore(S, pos, seqs, slots, pool)
+    with Timer(torch) as td:
+        for s in range(steps):
+            graphs[s % N_TOKENS_IN].replay()
+    return {"B": B, "restore_us": tr.ms * 1e3, "decode_steps": steps, "decode_us_per_step": td.ms * 1e3 / steps,
+            "total_us": (tr.ms + td.ms) * 1e3,
+            "decode_hbm_frac": DECODE_BYTES * B * H / (td.ms * 1e-3 / steps) / 1e9 / HBM_PEAK_GBS}
+
+
 def bench_copy(torch, device, reps=20):
     n = 1 << 28  # 1 GiB of fp32
     a = torch.empty(n, dtype=torch.float32, device=device).fill_(1.0)
@@ -529,6 +558,8 @@ def main():
     if not args.quick and "slots" in picked:
         log("snapshot/restore")
         rows["snapshot_restore"] = bench_snapshot_restore(torch, kda, synth, device)
+        log("resume from a mid-prompt checkpoint")
+        rows["resume_b8"] = bench_resume(torch, kda, synth, device)
     if not args.quick and "prefill" in picked:
         log("prefill")
         for variant in ("chunked", "chunked_prep", "recurrent"):
