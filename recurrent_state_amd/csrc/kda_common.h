@@ -172,7 +172,13 @@ __device__ __forceinline__ float wave_sum(float x) {
   return pair_sum32(pair_sum16(x));
 }
 
-// Sum over aligned groups of N = 32 or 64 lanes (N = 64: wave_sum).
+// Sum over aligned groups of N = 32 or 64 lanes, every lane of a group
+// getting the same value.  Across 16-lane rows it exchanges through the LDS
+// crossbar (ds_swizzle for lane ^ 16, ds_bpermute for lane ^ 32) rather than
+// the inline-assembly swaps above: those are scheduling boundaries, and a
+// caller that needs many independent sums (one per token) wants them
+// interleaved.  Each stage adds the same two values on both partner lanes
+// (in either order; IEEE addition is commutative), so the group agrees.
 template <int N>
 __device__ __forceinline__ float lane_group_sum(float x) {
   static_assert(N == 32 || N == 64, "lane group");
@@ -180,8 +186,13 @@ __device__ __forceinline__ float lane_group_sum(float x) {
   x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x124, 0xf, 0xf, false));
   x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x122, 0xf, 0xf, false));
   x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x121, 0xf, 0xf, false));
-  x = pair_sum16(x);
-  return N == 64 ? pair_sum32(x) : x;
+  // ds_swizzle bit mode: and_mask 0x1f, or_mask 0, xor_mask 0x10 (lane ^ 16).
+  x += __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, x), 0x401f));
+  if (N == 64) {
+    const int lane = __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+    x += __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute((lane ^ 32) << 2, __builtin_bit_cast(int, x)));
+  }
+  return x;
 }
 
 // One token of the gated delta rule on a lane's R x 4 register tile:
@@ -240,7 +251,10 @@ __device__ __forceinline__ float sigmoid_f32(float x) { return __builtin_amdgcn_
 // 1 / |x| from the squared norm; a zero vector keeps norm factor 0, so it
 // stays zero.  IEEE square root and division: scaling the vector by 2^p
 // scales the factor by exactly 2^-p.
-__device__ __forceinline__ float inv_norm(float sq) { return sq > 0.f ? 1.f / sqrtf(sq) : 0.f; }
+__device__ __forceinline__ float inv_norm(float sq) {
+  const float r = 1.f / sqrtf(sq);  // computed unconditionally: a select, not a branch
+  return sq > 0.f ? r : 0.f;
+}
 
 // token_update from raw projections (the input preparation fused into the
 // step).  q and k arrive un-normalised, the decay as its logit x (per key

@@ -374,11 +374,20 @@ __global__ void __launch_bounds__(DV * 4) prefill_chunked_kernel(PrefillArgs<TIn
       k1[i] = pad ? 0.f : rk[i].hi();
       q0[i] = pad ? 0.f : rq[i].lo();
       q1[i] = pad ? 0.f : rq[i].hi();
-      if constexpr (PREP) {
-        // The CP lanes of token group tg (an aligned group of 32 or 64 lanes)
-        // hold all DK key channels of token tg TPG + i, two per lane.
-        const float rk_ = inv_norm(lane_group_sum<CP>(__builtin_fmaf(k0[i], k0[i], k1[i] * k1[i])));
-        const float rq_ = inv_norm(lane_group_sum<CP>(__builtin_fmaf(q0[i], q0[i], q1[i] * q1[i])));
+    }
+    if constexpr (PREP) {
+      // The CP lanes of token group tg (an aligned group of 32 or 64 lanes)
+      // hold all DK key channels of its tokens, two per lane.  The 2 TPG
+      // sums are independent, so they are formed together and interleave.
+      float sk[TPG], sq[TPG];
+#pragma unroll
+      for (int i = 0; i < TPG; ++i) {
+        sk[i] = lane_group_sum<CP>(__builtin_fmaf(k0[i], k0[i], k1[i] * k1[i]));
+        sq[i] = lane_group_sum<CP>(__builtin_fmaf(q0[i], q0[i], q1[i] * q1[i]));
+      }
+#pragma unroll
+      for (int i = 0; i < TPG; ++i) {
+        const float rk_ = inv_norm(sk[i]), rq_ = inv_norm(sq[i]);
         k0[i] *= rk_;
         k1[i] *= rk_;
         q0[i] *= rq_;
