@@ -172,6 +172,25 @@ __device__ __forceinline__ float wave_sum(float x) {
   return pair_sum32(pair_sum16(x));
 }
 
+// lane ^ 16 and lane ^ 32 partners through the LDS crossbar (no LDS memory).
+__device__ __forceinline__ float xor16_partner(float x) {
+  // ds_swizzle bit mode: and_mask 0x1f, or_mask 0, xor_mask 0x10.
+  return __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, x), 0x401f));
+}
+__device__ __forceinline__ float xor32_partner(float x) {
+  const int lane = __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+  return __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute((lane ^ 32) << 2, __builtin_bit_cast(int, x)));
+}
+
+// rowgroup_sum for callers with many independent sums: the same additions in
+// the same pairs (so bit-identical results), with the cross-row exchanges
+// through the crossbar so that the compiler can interleave the sums.
+__device__ __forceinline__ float rowgroup_sum_many(float x) {
+  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x128, 0xf, 0xf, false));
+  x += xor16_partner(x);
+  return x + xor32_partner(x);
+}
+
 // Sum over aligned groups of N = 32 or 64 lanes, every lane of a group
 // getting the same value.  Across 16-lane rows it exchanges through the LDS
 // crossbar (ds_swizzle for lane ^ 16, ds_bpermute for lane ^ 32) rather than
@@ -186,12 +205,8 @@ __device__ __forceinline__ float lane_group_sum(float x) {
   x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x124, 0xf, 0xf, false));
   x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x122, 0xf, 0xf, false));
   x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x121, 0xf, 0xf, false));
-  // ds_swizzle bit mode: and_mask 0x1f, or_mask 0, xor_mask 0x10 (lane ^ 16).
-  x += __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, x), 0x401f));
-  if (N == 64) {
-    const int lane = __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
-    x += __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute((lane ^ 32) << 2, __builtin_bit_cast(int, x)));
-  }
+  x += xor16_partner(x);
+  if (N == 64) x += xor32_partner(x);
   return x;
 }
 

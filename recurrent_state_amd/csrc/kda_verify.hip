@@ -274,7 +274,7 @@ __device__ __forceinline__ void verify_group(const VerifyArgs<TIn>& a, const Str
       }
     }
     if constexpr (PREP) {
-      kn[r] = inv_norm(wave_sum(k2));
+      kn[r] = inv_norm(lane_group_sum<64>(k2));
       bp[r] = sigmoid_f32(bt[r]);
     } else {
       kn[r] = 1.f;
@@ -304,7 +304,7 @@ __device__ __forceinline__ void verify_group(const VerifyArgs<TIn>& a, const Str
       float q2 = 0.f;
 #pragma unroll
       for (int c = 0; c < CPL; ++c) q2 = __builtin_fmaf(qt[c], qt[c], q2);
-      qnt = inv_norm(wave_sum(q2));
+      qnt = inv_norm(lane_group_sum<64>(q2));
     }
     kt.store(st.log_k, kvo_in, tt * st.sk_in);
     at.store(st.log_alpha, kvo_f32, tt * st.sk_f32);
@@ -343,8 +343,8 @@ __device__ __forceinline__ void verify_group(const VerifyArgs<TIn>& a, const Str
 #pragma unroll
     for (int s = 0; s < kGroup; ++s) {
       if (s <= t) {
-        const float ps = wave_sum(pP[s]);
-        const float as = s < t ? wave_sum(pA[s]) : 0.f;
+        const float ps = lane_group_sum<64>(pP[s]);
+        const float as = s < t ? lane_group_sum<64>(pA[s]) : 0.f;
         if (lane == 0) {
           L.P[t][s] = ps;
           L.A[t][s] = as;
@@ -406,8 +406,8 @@ __device__ __forceinline__ void verify_group(const VerifyArgs<TIn>& a, const Str
     if (t < G) {
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
-        x[t][c] = rowgroup_sum(x[t][c]);
-        y[t][c] = rowgroup_sum(y[t][c]);
+        x[t][c] = rowgroup_sum_many(x[t][c]);
+        y[t][c] = rowgroup_sum_many(y[t][c]);
       }
     }
   }
