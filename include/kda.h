@@ -102,6 +102,9 @@ typedef enum kda_dtype { KDA_BF16 = 0, KDA_F32 = 1 } kda_dtype;
 #define KDA_VARIANT_SLOT_COPY 15
 #define KDA_VARIANT_PREFILL_CHUNKED_PREP 16
 #define KDA_VARIANT_PREFILL_RECURRENT_PREP 17
+#define KDA_VARIANT_VERIFY_SLOTS 18
+#define KDA_VARIANT_COMMIT_SLOTS 19
+#define KDA_VARIANT_COMMIT_VERIFY_SLOTS 20
 
 /* Decay gate of kda_decode_step_prep: alpha = f(x) of the logit x. */
 #define KDA_GATE_EXP_NEG_SOFTPLUS 0 /* alpha = exp(-softplus(x)) = 1 / (1 + e^x) */
@@ -309,6 +312,27 @@ kda_status kda_commit_verify_prep(const kda_shape* shape, int32_t gate, int32_t 
 kda_status kda_decode_step_slots(const kda_shape* shape, const int32_t* slot_ids, const kda_slots* slots,
                                  const void* q, const void* k, const void* v, const float* alpha,
                                  const float* beta, float* o, int32_t* dev_err, void* stream);
+
+/*
+ * The speculative calls on states in a slot pool (as kda_decode_step_slots):
+ * sequence b's state is slots->states[slot_ids[b]] (read by the verify,
+ * updated by the commits) and its position slots->pos[slot_ids[b]] (advanced
+ * by the commits).  slot_ids is a DEVICE int32 [B] of distinct ids; an id out
+ * of range sets KDA_DEV_ERR_SLOT_ID and the sequence is skipped (its verify
+ * logs no row, so a later count above 0 for it is flagged too).  The log,
+ * inputs, outputs and counts are the batch's, as in kda_verify, kda_commit
+ * and kda_commit_verify; the arithmetic is theirs, so states and outputs are
+ * bit-identical.  dev_err must not be NULL.
+ */
+kda_status kda_verify_slots(const kda_shape* shape, int32_t T, const int32_t* slot_ids, const kda_slots* slots,
+                            const void* q, const void* k, const void* v, const float* alpha, const float* beta,
+                            float* o, kda_log* log, int32_t* dev_err, void* stream);
+kda_status kda_commit_slots(const kda_shape* shape, const int32_t* slot_ids, const kda_slots* slots, kda_log* log,
+                            const int32_t* accepted, int32_t* dev_err, void* stream);
+kda_status kda_commit_verify_slots(const kda_shape* shape, int32_t T, const int32_t* slot_ids, const kda_slots* slots,
+                                   const void* q, const void* k, const void* v, const float* alpha,
+                                   const float* beta, float* o, kda_log* log, const int32_t* accepted,
+                                   int32_t* dev_err, void* stream);
 
 /*
  * Slot-to-slot copy of whole states (all H heads) and positions:

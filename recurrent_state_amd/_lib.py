@@ -21,7 +21,8 @@ KDA_BF16, KDA_F32 = 0, 1
 VARIANTS = {0: "none", 1: "decode", 2: "verify", 3: "commit", 4: "snapshot", 5: "restore",
             6: "prefill_recurrent", 7: "prefill_chunked", 8: "commit_verify", 9: "verify_varlen",
             10: "commit_verify_varlen", 11: "decode_prep", 12: "verify_prep", 13: "commit_verify_prep",
-            14: "decode_slots", 15: "slot_copy", 16: "prefill_chunked_prep", 17: "prefill_recurrent_prep"}
+            14: "decode_slots", 15: "slot_copy", 16: "prefill_chunked_prep", 17: "prefill_recurrent_prep",
+            18: "verify_slots", 19: "commit_slots", 20: "commit_verify_slots"}
 GATE_EXP_NEG_SOFTPLUS, GATE_SIGMOID = 0, 1
 DEV_ERR_ACCEPTED, DEV_ERR_CKPT_SLOT, DEV_ERR_DRAFT_LEN, DEV_ERR_SLOT_ID = 1, 2, 4, 8
 
@@ -69,6 +70,11 @@ _SIGS = {
     "kda_decode_step_slots": (_I, [ctypes.POINTER(Shape), _P, ctypes.POINTER(_Slots), _P, _P, _P, _P, _P, _P, _P,
                                    _P]),
     "kda_slot_copy": (_I, [ctypes.POINTER(Shape), _P, _P, _I, ctypes.POINTER(_Slots), _P]),
+    "kda_verify_slots": (_I, [ctypes.POINTER(Shape), _I, _P, ctypes.POINTER(_Slots), _P, _P, _P, _P, _P, _P,
+                              ctypes.POINTER(_Log), _P, _P]),
+    "kda_commit_slots": (_I, [ctypes.POINTER(Shape), _P, ctypes.POINTER(_Slots), ctypes.POINTER(_Log), _P, _P, _P]),
+    "kda_commit_verify_slots": (_I, [ctypes.POINTER(Shape), _I, _P, ctypes.POINTER(_Slots), _P, _P, _P, _P, _P, _P,
+                                     ctypes.POINTER(_Log), _P, _P, _P]),
     "kda_snapshot": (_I, [ctypes.POINTER(Shape), _P, _P, _P, _P, _I, ctypes.POINTER(_Slots), _P]),
     "kda_restore": (_I, [ctypes.POINTER(Shape), _P, _P, _P, _P, _I, ctypes.POINTER(_Slots), _P]),
     "kda_prefill_chunked": (_I, [ctypes.POINTER(Shape), _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _I, _P,
@@ -357,6 +363,49 @@ class DecodeSlotsPlan:
 
     def __call__(self):
         _check(self._fn(*self._args, _stream()))
+
+
+def _slots_batch(slot_ids, pool: SlotPool, log: InputLog, dev_err):
+    B = slot_ids.shape[0]
+    _need(slot_ids, "slot_ids", (B,), torch.int32, pool.states.device)
+    _need(dev_err, "dev_err", (1,), torch.int32, pool.states.device)
+    batch = _Batch(B, pool)
+    if batch.shape != (log.shape.B, log.shape.H, log.shape.dk, log.shape.dv):
+        raise ValueError("log was sized for a different shape")
+    return batch
+
+
+def verify_slots(slot_ids, pool: SlotPool, q, k, v, alpha, beta, o, log: InputLog, dev_err, scale=None):
+    """verify on states in a slot pool (sequence b reads slot slot_ids[b]); log, inputs and o are the batch's."""
+    batch = _slots_batch(slot_ids, pool, log, dev_err)
+    T = q.shape[1]
+    _check_tokens(batch, T, q, k, v, alpha, beta, o)
+    sh = _shape(batch, q.dtype, scale)
+    _check(lib().kda_verify_slots(ctypes.byref(sh), T, _ptr(slot_ids), ctypes.byref(pool.c),
+                                  *(_ptr(x) for x in (q, k, v, alpha, beta, o)), ctypes.byref(log.c), _ptr(dev_err),
+                                  _stream()))
+
+
+def commit_slots(slot_ids, pool: SlotPool, log: InputLog, accepted, dev_err):
+    """commit onto states and positions in a slot pool (sequence b updates slot slot_ids[b])."""
+    batch = _slots_batch(slot_ids, pool, log, dev_err)
+    _need(accepted, "accepted", (batch.shape[0],), torch.int32, pool.states.device)
+    _check(lib().kda_commit_slots(ctypes.byref(log.shape), _ptr(slot_ids), ctypes.byref(pool.c), ctypes.byref(log.c),
+                                  _ptr(accepted), _ptr(dev_err), _stream()))
+
+
+def commit_verify_slots(slot_ids, pool: SlotPool, q, k, v, alpha, beta, o, log: InputLog, dev_err, accepted=None,
+                        scale=None):
+    """commit_verify on states and positions in a slot pool."""
+    batch = _slots_batch(slot_ids, pool, log, dev_err)
+    T = q.shape[1]
+    _check_tokens(batch, T, q, k, v, alpha, beta, o)
+    if accepted is not None:
+        _need(accepted, "accepted", (batch.shape[0],), torch.int32, pool.states.device)
+    sh = _shape(batch, q.dtype, scale)
+    _check(lib().kda_commit_verify_slots(ctypes.byref(sh), T, _ptr(slot_ids), ctypes.byref(pool.c),
+                                         *(_ptr(x) for x in (q, k, v, alpha, beta, o)), ctypes.byref(log.c),
+                                         _ptr(accepted) if accepted is not None else None, _ptr(dev_err), _stream()))
 
 
 def slot_copy(src_slots, dst_slots, pool: SlotPool):

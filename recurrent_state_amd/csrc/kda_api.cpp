@@ -192,9 +192,17 @@ namespace {
 bool valid_gate(int32_t gate) { return gate == KDA_GATE_EXP_NEG_SOFTPLUS || gate == KDA_GATE_SIGMOID; }
 
 // gate < 0: prepared inputs; otherwise raw projections and logits.
+kda_status check_slot_ids(const int32_t* slot_ids, int32_t* dev_err) {
+  if (!slot_ids || !dev_err) return KDA_ERR_NULL;
+  if (!aligned(slot_ids, 4) || !aligned(dev_err, 4)) return KDA_ERR_ALIGN;
+  return KDA_OK;
+}
+
+// slot_ids non-null: state (and pos) are a slot pool's arrays of n_slots.
 kda_status verify_impl(const kda_shape* shape, int32_t T, const int32_t* draft_len, const float* state, const void* q,
                        const void* k, const void* v, const float* alpha, const float* beta, float* o, kda_log* log,
-                       int32_t* dev_err, bool varlen, int32_t gate, void* stream) {
+                       int32_t* dev_err, bool varlen, int32_t gate, void* stream, const int32_t* slot_ids = nullptr,
+                       int32_t n_slots = 0) {
   kda_status r = check_shape(shape);
   if (r != KDA_OK) return r;
   if ((r = check_log(*shape, log)) != KDA_OK) return r;
@@ -207,9 +215,14 @@ kda_status verify_impl(const kda_shape* shape, int32_t T, const int32_t* draft_l
       if (!draft_len || !dev_err) return KDA_ERR_NULL;
       if (!aligned(draft_len, 4) || !aligned(dev_err, 4)) return KDA_ERR_ALIGN;
     }
+    if (n_slots > 0 && (r = check_slot_ids(slot_ids, dev_err)) != KDA_OK) return r;
     r = launched(kda::launch_verify(*shape, T, draft_len, state, kda::TokenInputs{q, k, v, alpha, beta}, o,
-                                    log_ptrs(*shape, log), dev_err, gate, static_cast<hipStream_t>(stream)),
-                 gate >= 0 ? KDA_VARIANT_VERIFY_PREP : varlen ? KDA_VARIANT_VERIFY_VARLEN : KDA_VARIANT_VERIFY);
+                                    log_ptrs(*shape, log), dev_err, gate, static_cast<hipStream_t>(stream), slot_ids,
+                                    n_slots),
+                 n_slots > 0 ? KDA_VARIANT_VERIFY_SLOTS
+                 : gate >= 0 ? KDA_VARIANT_VERIFY_PREP
+                 : varlen    ? KDA_VARIANT_VERIFY_VARLEN
+                             : KDA_VARIANT_VERIFY);
     if (r != KDA_OK) return r;
   }
   log->pending_T = T;
@@ -220,7 +233,8 @@ kda_status verify_impl(const kda_shape* shape, int32_t T, const int32_t* draft_l
 kda_status commit_verify_impl(const kda_shape* shape, int32_t T, const int32_t* draft_len, float* state,
                               int64_t* pos, const void* q, const void* k, const void* v, const float* alpha,
                               const float* beta, float* o, kda_log* log, const int32_t* accepted, int32_t* dev_err,
-                              bool varlen, int32_t gate, void* stream) {
+                              bool varlen, int32_t gate, void* stream, const int32_t* slot_ids = nullptr,
+                              int32_t n_slots = 0) {
   kda_status r = check_shape(shape);
   if (r != KDA_OK) return r;
   if ((r = check_log(*shape, log)) != KDA_OK) return r;
@@ -246,11 +260,15 @@ kda_status commit_verify_impl(const kda_shape* shape, int32_t T, const int32_t* 
       if (!dev_err) return KDA_ERR_NULL;
       if (!aligned(dev_err, 4)) return KDA_ERR_ALIGN;
     }
+    if (n_slots > 0 && (r = check_slot_ids(slot_ids, dev_err)) != KDA_OK) return r;
     r = launched(kda::launch_commit_verify(*shape, pend, T, draft_len, state, pos, accepted, dev_err,
                                            kda::TokenInputs{q, k, v, alpha, beta}, o, log_ptrs(*shape, log), gate,
-                                           log->pending_form - 1, static_cast<hipStream_t>(stream)),
-                 gate >= 0 ? KDA_VARIANT_COMMIT_VERIFY_PREP
-                           : varlen ? KDA_VARIANT_COMMIT_VERIFY_VARLEN : KDA_VARIANT_COMMIT_VERIFY);
+                                           log->pending_form - 1, static_cast<hipStream_t>(stream), slot_ids,
+                                           n_slots),
+                 n_slots > 0 ? KDA_VARIANT_COMMIT_VERIFY_SLOTS
+                 : gate >= 0 ? KDA_VARIANT_COMMIT_VERIFY_PREP
+                 : varlen    ? KDA_VARIANT_COMMIT_VERIFY_VARLEN
+                             : KDA_VARIANT_COMMIT_VERIFY);
     if (r != KDA_OK) return r;
   }
   log->pending_T = T;
@@ -278,8 +296,10 @@ kda_status kda_verify_varlen(const kda_shape* shape, int32_t T, const int32_t* d
   return verify_impl(shape, T, draft_len, state, q, k, v, alpha, beta, o, log, dev_err, true, -1, stream);
 }
 
-kda_status kda_commit(const kda_shape* shape, float* state, int64_t* pos, kda_log* log, const int32_t* accepted,
-                      int32_t* dev_err, void* stream) {
+namespace {
+
+kda_status commit_impl(const kda_shape* shape, float* state, int64_t* pos, kda_log* log, const int32_t* accepted,
+                       int32_t* dev_err, void* stream, const int32_t* slot_ids, int32_t n_slots) {
   kda_status r = check_shape(shape);
   if (r != KDA_OK) return r;
   if ((r = check_log(*shape, log)) != KDA_OK) return r;
@@ -288,13 +308,51 @@ kda_status kda_commit(const kda_shape* shape, float* state, int64_t* pos, kda_lo
     if ((r = check_ptrs({state})) != KDA_OK) return r;
     if (!pos || !accepted || !dev_err) return KDA_ERR_NULL;
     if (!aligned(pos, 8) || !aligned(accepted, 4) || !aligned(dev_err, 4)) return KDA_ERR_ALIGN;
+    if (n_slots > 0 && (r = check_slot_ids(slot_ids, dev_err)) != KDA_OK) return r;
     r = launched(kda::launch_commit(*shape, log->pending_T, state, pos, log_ptrs(*shape, log), accepted, dev_err,
-                                    log->pending_form, static_cast<hipStream_t>(stream)),
-                 KDA_VARIANT_COMMIT);
+                                    log->pending_form, static_cast<hipStream_t>(stream), slot_ids, n_slots),
+                 n_slots > 0 ? KDA_VARIANT_COMMIT_SLOTS : KDA_VARIANT_COMMIT);
     if (r != KDA_OK) return r;
   }
   log->pending_T = 0;
   return KDA_OK;
+}
+
+}  // namespace
+
+kda_status kda_commit(const kda_shape* shape, float* state, int64_t* pos, kda_log* log, const int32_t* accepted,
+                      int32_t* dev_err, void* stream) {
+  return commit_impl(shape, state, pos, log, accepted, dev_err, stream, nullptr, 0);
+}
+
+kda_status kda_verify_slots(const kda_shape* shape, int32_t T, const int32_t* slot_ids, const kda_slots* slots,
+                            const void* q, const void* k, const void* v, const float* alpha, const float* beta,
+                            float* o, kda_log* log, int32_t* dev_err, void* stream) {
+  kda_status r = check_slots(slots);
+  if (r != KDA_OK) return r;
+  if (slots->n_slots == 0 && shape && shape->B > 0) return KDA_ERR_SLOT;
+  return verify_impl(shape, T, nullptr, slots->states, q, k, v, alpha, beta, o, log, dev_err, false, -1, stream,
+                     slot_ids, slots->n_slots);
+}
+
+kda_status kda_commit_slots(const kda_shape* shape, const int32_t* slot_ids, const kda_slots* slots, kda_log* log,
+                            const int32_t* accepted, int32_t* dev_err, void* stream) {
+  kda_status r = check_slots(slots);
+  if (r != KDA_OK) return r;
+  if (slots->n_slots == 0 && shape && shape->B > 0) return KDA_ERR_SLOT;
+  return commit_impl(shape, slots->states, slots->pos, log, accepted, dev_err, stream, slot_ids, slots->n_slots);
+}
+
+kda_status kda_commit_verify_slots(const kda_shape* shape, int32_t T, const int32_t* slot_ids, const kda_slots* slots,
+                                   const void* q, const void* k, const void* v, const float* alpha,
+                                   const float* beta, float* o, kda_log* log, const int32_t* accepted,
+                                   int32_t* dev_err, void* stream) {
+  kda_status r = check_slots(slots);
+  if (r != KDA_OK) return r;
+  if (slots->n_slots == 0 && shape && shape->B > 0) return KDA_ERR_SLOT;
+  if (!dev_err) return KDA_ERR_NULL;
+  return commit_verify_impl(shape, T, nullptr, slots->states, slots->pos, q, k, v, alpha, beta, o, log, accepted,
+                            dev_err, false, -1, stream, slot_ids, slots->n_slots);
 }
 
 kda_status kda_commit_verify(const kda_shape* shape, int32_t T, float* state, int64_t* pos, const void* q,

@@ -58,8 +58,12 @@ hipError_t launch_decode(const kda_shape& s, float* state, int64_t* pos, TokenIn
 // KDA_DEV_ERR_DRAFT_LEN in *dev_err and counts as 0.
 // gate < 0: prepared inputs; otherwise raw projections and logits with that
 // KDA_GATE_* (prepared in the kernel, logged raw).
+// slot_ids (device [B], may be null) puts the states (and, for the commits,
+// the positions) in a slot pool of n_slots: sequence b uses slot slot_ids[b];
+// an id out of range sets KDA_DEV_ERR_SLOT_ID and the sequence is skipped.
 hipError_t launch_verify(const kda_shape& s, int32_t T, const int32_t* draft_len, const float* state, TokenInputs in,
-                         float* o, LogPtrs log, int32_t* dev_err, int32_t gate, hipStream_t st);
+                         float* o, LogPtrs log, int32_t* dev_err, int32_t gate, hipStream_t st,
+                         const int32_t* slot_ids = nullptr, int32_t n_slots = 0);
 // Decode from raw projections: q, k un-normalised, `alpha` / `beta` hold the
 // decay and beta logits; decay = sigmoid(gate_sign * logit).
 hipError_t launch_decode_prep(const kda_shape& s, float* state, int64_t* pos, TokenInputs raw, float* o,
@@ -71,14 +75,16 @@ hipError_t launch_decode_prep(const kda_shape& s, float* state, int64_t* pos, To
 hipError_t launch_decode_slots(const kda_shape& s, const int32_t* slot_ids, float* pool_states, int64_t* pool_pos,
                                int32_t n_slots, TokenInputs in, float* o, int32_t* dev_err, hipStream_t st);
 hipError_t launch_commit(const kda_shape& s, int32_t T, float* state, int64_t* pos, LogPtrs log,
-                         const int32_t* accepted, int32_t* dev_err, int32_t form, hipStream_t st);
+                         const int32_t* accepted, int32_t* dev_err, int32_t form, hipStream_t st,
+                         const int32_t* slot_ids = nullptr, int32_t n_slots = 0);
 // Commit of the pending T_pend logged tokens (T_pend = 0: none) followed by
 // the verify of T new tokens from the committed state, in one launch.
 // The pending log must be prepared when gate < 0 and raw when gate >= 0;
 // pend_gate is the gate of a raw pending log.
 hipError_t launch_commit_verify(const kda_shape& s, int32_t T_pend, int32_t T, const int32_t* draft_len, float* state,
                                 int64_t* pos, const int32_t* accepted, int32_t* dev_err, TokenInputs in, float* o,
-                                LogPtrs log, int32_t gate, int32_t pend_gate, hipStream_t st);
+                                LogPtrs log, int32_t gate, int32_t pend_gate, hipStream_t st,
+                                const int32_t* slot_ids = nullptr, int32_t n_slots = 0);
 // Prefills: gate < 0 prepared inputs, otherwise raw projections and logits.
 hipError_t launch_prefill_recurrent(const kda_shape& s, int32_t L, float* state, int64_t* pos,
                                     TokenInputs in, float* o, int32_t ckpt_every, const int32_t* ckpt_slots,

@@ -58,6 +58,8 @@ struct CommitArgs {
   int32_t T;     // tokens of the pending verify
   int32_t Tmax;  // token rows per sequence in the log
   float gate_sign;  // raw logs: decay = sigmoid(gate_sign * logit)
+  const int32_t* slot_ids;  // states and positions in a slot pool (null: dense [B])
+  int32_t n_slots;
 };
 
 template <typename TIn>
@@ -187,19 +189,27 @@ __global__ void KDA_OCCUPANCY __launch_bounds__((kWave * waves_per_group<DV, WPG
   typedef Place<DK, DV, WPG> P;
   constexpr int R = P::R;
   const P p(a.H);
+  int sb = p.b;  // index of the state and position this sequence uses
+  if (a.slot_ids) {
+    sb = a.slot_ids[p.b];
+    if (sb < 0 || sb >= a.n_slots) {
+      if (p.h == 0 && p.slice == 0 && p.lane == 0) atomicOr(a.dev_err, KDA_DEV_ERR_SLOT_ID);
+      return;
+    }
+  }
   const int n = a.accepted[p.b];
   if (n < 0 || n > min(a.T, log_rows(a.log_len[p.bh]))) {
     if (p.h == 0 && p.slice == 0 && p.lane == 0) atomicOr(a.dev_err, KDA_DEV_ERR_ACCEPTED);
     return;
   }
   if (n == 0) return;
-  float* sp = a.state + (size_t)p.bh * DK * DV + p.tile_off();
+  float* sp = a.state + ((size_t)sb * a.H + p.h) * DK * DV + p.tile_off();
   float S[R][4];
   load_tile<R, DV>(sp, S);
   replay_log<DK, DV, TIn, R, RAW>(S, a.log_k, a.log_v, a.log_alpha, a.log_beta, (size_t)p.b * a.Tmax * a.H + p.h,
                                   a.H, n, p.row0, p.col0, a.gate_sign);
   store_tile<R, DV>(sp, S);
-  if (p.h == 0 && p.slice == 0 && p.lane == 0) a.pos[p.b] += n;
+  if (p.h == 0 && p.slice == 0 && p.lane == 0) a.pos[sb] += n;
 }
 
 // PREP: raw projections and logits, prepared in every step (the decode step
@@ -320,14 +330,15 @@ hipError_t launch_decode_slots(const kda_shape& s, const int32_t* slot_ids, floa
 }
 
 hipError_t launch_commit(const kda_shape& s, int32_t T, float* state, int64_t* pos, LogPtrs log,
-                         const int32_t* accepted, int32_t* dev_err, int32_t form, hipStream_t st) {
+                         const int32_t* accepted, int32_t* dev_err, int32_t form, hipStream_t st,
+                         const int32_t* slot_ids, int32_t n_slots) {
   dispatch(s, [&](auto c) {
     typedef decltype(c) C;
     typedef typename C::TIn TIn;
     constexpr int DK = C::DK, DV = C::DV;
     const float gsign = form == kLogPrepared ? 0.f : (form - kLogRaw == KDA_GATE_SIGMOID ? 1.f : -1.f);
-    CommitArgs<TIn> a{state, pos, (const TIn*)log.k, (const TIn*)log.v, log.alpha, log.beta, accepted, dev_err,
-                      log.len, s.H, T, log.T_max, gsign};
+    CommitArgs<TIn> a{state, pos,   (const TIn*)log.k, (const TIn*)log.v, log.alpha, log.beta, accepted, dev_err,
+                      log.len, s.H, T,   log.T_max,        gsign,            slot_ids,  n_slots};
     auto go = [&](auto raw) {
       constexpr bool RAW = decltype(raw)::value;
       if (slice_waves<DV>(s) >= kWideWaves)

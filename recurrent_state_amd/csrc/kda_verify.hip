@@ -82,6 +82,10 @@ struct VerifyArgs {
   int32_t gate;
   float gate_sign;
   float pend_gate_sign;  // fused commit of a raw pending log (PREP): its decay sign
+  // States (and, with COMMIT, positions) in a slot pool: sequence b uses
+  // state[slot_ids[b]] and pos[slot_ids[b]]; null: the dense [B] arrays.
+  const int32_t* slot_ids;
+  int32_t n_slots;
 };
 
 // Per-group LDS.  Key-channel vectors are stored by row group with a padded
@@ -484,10 +488,19 @@ __global__ void __launch_bounds__(kWave * (DV / kSliceCols)) verify_chunk_kernel
   const size_t tok0 = (size_t)b * T * a.H + h;         // [B][T][H] row of input token 0
   const size_t tok0_log = (size_t)b * a.Tmax * a.H + h;  // [B][T_max][H] row of log token 0
   const Streams<TIn, DK, DV> st(a, tok0, tok0_log, T);
+  int sb = b;  // index of the state (and position) this sequence uses
+  if (a.slot_ids) {
+    sb = a.slot_ids[b];
+    if (sb < 0 || sb >= a.n_slots) {  // uniform over the workgroup: nothing is read or written
+      if (h == 0 && threadIdx.x == 0) atomicOr(a.dev_err, KDA_DEV_ERR_SLOT_ID);
+      if (threadIdx.x == 0) a.log_len[bh] = log_record(0, kLogPrepared);
+      return;
+    }
+  }
 
   // The lane's state tile, loaded once.
   float S[R][4];
-  const rsrc_t rs = make_rsrc(a.state + (size_t)bh * DK * DV, DK * DV * 4);
+  const rsrc_t rs = make_rsrc(a.state + ((size_t)sb * a.H + h) * DK * DV, DK * DV * 4);
   const int row0 = rg * R, col0 = wave * kSliceCols + cg * 4;
   const int svo = (row0 * DV + col0) * 4;
   auto load_state = [&](float (&St)[R][4]) {
@@ -533,7 +546,7 @@ __global__ void __launch_bounds__(kWave * (DV / kSliceCols)) verify_chunk_kernel
                            __float_as_uint(S[r][3])};
           __builtin_amdgcn_raw_buffer_store_b128(w, rs, svo, r * DV * 4, 0);
         }
-        if (h == 0 && wave == 0 && lane == 0) a.pos[b] += n;
+        if (h == 0 && wave == 0 && lane == 0) a.pos[sb] += n;
       }
       __syncthreads();  // every wave has read the pending log rows and count before the verify rewrites them
     }
@@ -591,11 +604,12 @@ void launch_shape(const kda_shape& s, const VerifyArgs<TIn>& a, hipStream_t st) 
 template <typename TIn, bool COMMIT>
 void launch_any(const kda_shape& s, int32_t T_pend, int32_t T, const int32_t* draft_len, float* state, int64_t* pos,
                 const int32_t* accepted, int32_t* dev_err, TokenInputs in, float* o, LogPtrs log, int32_t gate,
-                int32_t pend_gate, hipStream_t st) {
+                int32_t pend_gate, const int32_t* slot_ids, int32_t n_slots, hipStream_t st) {
   const VerifyArgs<TIn> a{state,   (const TIn*)in.q, (const TIn*)in.k, (const TIn*)in.v, in.alpha, in.beta, o,
                           (TIn*)log.k, (TIn*)log.v, log.alpha, log.beta, s.H, T, log.T_max, s.scale, pos, accepted,
                           dev_err, T_pend, draft_len, log.len, gate < 0 ? 0 : gate,
-                          gate == KDA_GATE_SIGMOID ? 1.f : -1.f, pend_gate == KDA_GATE_SIGMOID ? 1.f : -1.f};
+                          gate == KDA_GATE_SIGMOID ? 1.f : -1.f, pend_gate == KDA_GATE_SIGMOID ? 1.f : -1.f,
+                          slot_ids, n_slots};
   if (gate < 0)
     launch_shape<TIn, COMMIT, false>(s, a, st);
   else
@@ -605,23 +619,29 @@ void launch_any(const kda_shape& s, int32_t T_pend, int32_t T, const int32_t* dr
 }  // namespace
 
 hipError_t launch_verify(const kda_shape& s, int32_t T, const int32_t* draft_len, const float* state, TokenInputs in,
-                         float* o, LogPtrs log, int32_t* dev_err, int32_t gate, hipStream_t st) {
+                         float* o, LogPtrs log, int32_t* dev_err, int32_t gate, hipStream_t st,
+                         const int32_t* slot_ids, int32_t n_slots) {
   // The verify-only kernel never writes through `state`.
   float* sp = const_cast<float*>(state);
   if (s.in_dtype == KDA_BF16)
-    launch_any<bf16_t, false>(s, 0, T, draft_len, sp, nullptr, nullptr, dev_err, in, o, log, gate, -1, st);
+    launch_any<bf16_t, false>(s, 0, T, draft_len, sp, nullptr, nullptr, dev_err, in, o, log, gate, -1, slot_ids,
+                              n_slots, st);
   else
-    launch_any<float, false>(s, 0, T, draft_len, sp, nullptr, nullptr, dev_err, in, o, log, gate, -1, st);
+    launch_any<float, false>(s, 0, T, draft_len, sp, nullptr, nullptr, dev_err, in, o, log, gate, -1, slot_ids,
+                             n_slots, st);
   return hipGetLastError();
 }
 
 hipError_t launch_commit_verify(const kda_shape& s, int32_t T_pend, int32_t T, const int32_t* draft_len, float* state,
                                 int64_t* pos, const int32_t* accepted, int32_t* dev_err, TokenInputs in, float* o,
-                                LogPtrs log, int32_t gate, int32_t pend_gate, hipStream_t st) {
+                                LogPtrs log, int32_t gate, int32_t pend_gate, hipStream_t st,
+                                const int32_t* slot_ids, int32_t n_slots) {
   if (s.in_dtype == KDA_BF16)
-    launch_any<bf16_t, true>(s, T_pend, T, draft_len, state, pos, accepted, dev_err, in, o, log, gate, pend_gate, st);
+    launch_any<bf16_t, true>(s, T_pend, T, draft_len, state, pos, accepted, dev_err, in, o, log, gate, pend_gate,
+                             slot_ids, n_slots, st);
   else
-    launch_any<float, true>(s, T_pend, T, draft_len, state, pos, accepted, dev_err, in, o, log, gate, pend_gate, st);
+    launch_any<float, true>(s, T_pend, T, draft_len, state, pos, accepted, dev_err, in, o, log, gate, pend_gate,
+                            slot_ids, n_slots, st);
   return hipGetLastError();
 }
 

@@ -244,6 +244,22 @@ def test_slot_decode_and_copy_validation(k):
     assert cp(ids(), ids(), 0) == OK
     assert cp(ids(0), ids(1), -1) == SHAPE
     assert L.kda_slot_copy(ctypes.byref(s), None, None, 1, ctypes.byref(slots), None) == NULL
+    log = k._lib._Log(0x100000, k.log_bytes(s, 4), 4, 0, 0)
+    assert L.kda_verify_slots(ctypes.byref(s), 2, None, ctypes.byref(slots), GOOD, GOOD, GOOD, GOOD, GOOD, GOOD,
+                              ctypes.byref(log), GOOD, None) == NULL
+    assert L.kda_verify_slots(ctypes.byref(s), 2, GOOD, ctypes.byref(slots), GOOD, GOOD, GOOD, GOOD, GOOD, GOOD,
+                              ctypes.byref(log), None, None) == NULL
+    assert L.kda_verify_slots(ctypes.byref(s), 2, GOOD, ctypes.byref(k._lib._Slots(0x200000, 0x300000, 0)), GOOD,
+                              GOOD, GOOD, GOOD, GOOD, GOOD, ctypes.byref(log), GOOD, None) == SLOT
+    assert log.pending_T == 0
+    assert L.kda_commit_slots(ctypes.byref(s), GOOD, ctypes.byref(slots), ctypes.byref(log), GOOD, GOOD,
+                              None) == ORDER                      # nothing pending
+    pend = k._lib._Log(0x100000, k.log_bytes(s, 4), 4, 2, 0)
+    assert L.kda_commit_slots(ctypes.byref(s), P(0x10002), ctypes.byref(slots), ctypes.byref(pend), GOOD, GOOD,
+                              None) == ALIGN
+    assert L.kda_commit_verify_slots(ctypes.byref(s), 2, GOOD, ctypes.byref(slots), GOOD, GOOD, GOOD, GOOD, GOOD,
+                                     GOOD, ctypes.byref(pend), GOOD, None, None) == NULL
+    assert pend.pending_T == 2
 
 
 def test_snapshot_restore_validation(k):

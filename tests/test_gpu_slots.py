@@ -108,3 +108,73 @@ def test_slot_copy_forks_a_prefix():
     assert torch.equal(bits(pool.states[5]), bits(pool.states[2])) and pool.pos[5].item() == 23
     with pytest.raises(kda.KdaError):
         kda.slot_copy([1, 2], [2, 3], pool)    # slot 2 both read and written
+
+
+@pytest.mark.parametrize("T,B,fused", [(4, 4, False), (4, 4, True), (7, 3, True), (4, 20, True)])
+def test_speculative_rounds_on_slots_equal_dense(T, B, fused):
+    # Two rounds (verify + commit, or fused) on pool slots against the same
+    # sequences in a dense batch: states, positions and outputs bit for bit.
+    spec = synth.ConfigSpec("spslots", 153, (B,), 32 if B > 8 else 5, 128, 128, "bf16", "softplus", "normal", 0)
+    n_slots = 2 * B + 1
+    say(f"speculative on slots T={T} B={B} fused={fused}")
+    pool = _pool(spec, n_slots, 5)
+    ids = np.random.default_rng(6).permutation(n_slots)[:B].astype(np.int32)
+    slot_ids = torch.from_numpy(ids).cuda()
+    S = pool.states[slot_ids.long()].clone()
+    pos = pool.pos[slot_ids.long()].clone()
+    untouched = [i for i in range(n_slots) if i not in set(ids.tolist())]
+    keep = bits(pool.states[untouched]).clone()
+    d = {name: dev_tensor(x) for name, x in synth.token_inputs(spec, B, 2 * T).items()}
+    rounds = [{k_: v_[:, r * T:(r + 1) * T].contiguous() for k_, v_ in d.items()} for r in range(2)]
+    counts = [torch.tensor(np.random.default_rng(7 + r).integers(0, T + 1, B), dtype=torch.int32, device="cuda")
+              for r in range(2)]
+    err_s = torch.zeros(1, dtype=torch.int32, device="cuda")
+    err_d = torch.zeros(1, dtype=torch.int32, device="cuda")
+    log_s = kda.InputLog(S, T_max=8)
+    log_d = kda.InputLog(S, T_max=8)
+    for r in range(2):
+        x = rounds[r]
+        o_s = torch.empty((B, T, spec.H, 128), device="cuda")
+        o_d = torch.empty_like(o_s)
+        if fused:
+            acc = counts[r - 1] if r > 0 else None
+            kda.commit_verify_slots(slot_ids, pool, x["q"], x["k"], x["v"], x["alpha"], x["beta"], o_s, log_s,
+                                    err_s, accepted=acc)
+            assert kda.last_variant() == "commit_verify_slots"
+            kda.commit_verify(S, pos, x["q"], x["k"], x["v"], x["alpha"], x["beta"], o_d, log_d, acc,
+                              err_d if acc is not None else None)
+        else:
+            kda.verify_slots(slot_ids, pool, x["q"], x["k"], x["v"], x["alpha"], x["beta"], o_s, log_s, err_s)
+            assert kda.last_variant() == "verify_slots"
+            kda.verify(S, x["q"], x["k"], x["v"], x["alpha"], x["beta"], o_d, log_d)
+            kda.commit_slots(slot_ids, pool, log_s, counts[r], err_s)
+            assert kda.last_variant() == "commit_slots"
+            kda.commit(S, pos, log_d, counts[r], err_d)
+        assert torch.equal(bits(o_s), bits(o_d)), f"round {r} outputs"
+    torch.cuda.synchronize()
+    assert err_s.item() == 0 and err_d.item() == 0
+    assert torch.equal(bits(pool.states[slot_ids.long()]), bits(S))
+    assert torch.equal(pool.pos[slot_ids.long()], pos)
+    assert torch.equal(bits(pool.states[untouched]), keep)
+
+
+def test_verify_slots_out_of_range_id_logs_nothing():
+    spec = spec_for(128, 128, "bf16", tag=154)
+    B, T, n_slots = 3, 4, 5
+    pool = _pool(spec, n_slots, 8)
+    before = bits(pool.states).clone()
+    slot_ids = torch.tensor([1, 9, 3], dtype=torch.int32, device="cuda")
+    d = {name: dev_tensor(x) for name, x in synth.token_inputs(spec, B, T).items()}
+    log = kda.InputLog(torch.empty((B, spec.H, 128, 128), device="cuda"), T_max=T)
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    o = torch.full((B, T, spec.H, 128), SENTINEL, dtype=torch.int32, device="cuda").view(torch.float32)
+    kda.verify_slots(slot_ids, pool, d["q"], d["k"], d["v"], d["alpha"], d["beta"], o, log, err)
+    torch.cuda.synchronize()
+    assert err.item() == kda.DEV_ERR_SLOT_ID
+    assert (bits(o)[1] == SENTINEL).all() and not (bits(o)[0] == SENTINEL).any()
+    err.zero_()
+    kda.commit_slots(slot_ids, pool, log, torch.tensor([2, 1, 0], dtype=torch.int32, device="cuda"), err)
+    torch.cuda.synchronize()
+    assert err.item() == kda.DEV_ERR_SLOT_ID          # the bad id is flagged again and skipped
+    changed = [i for i in range(n_slots) if not torch.equal(bits(pool.states[i]), before[i])]
+    assert changed == [1]
