@@ -105,6 +105,7 @@ typedef enum kda_dtype { KDA_BF16 = 0, KDA_F32 = 1 } kda_dtype;
 #define KDA_VARIANT_VERIFY_SLOTS 18
 #define KDA_VARIANT_COMMIT_SLOTS 19
 #define KDA_VARIANT_COMMIT_VERIFY_SLOTS 20
+#define KDA_VARIANT_PREFILL_CHUNKED_SLOTS 21
 
 /* Decay gate of kda_decode_step_prep: alpha = f(x) of the logit x. */
 #define KDA_GATE_EXP_NEG_SOFTPLUS 0 /* alpha = exp(-softplus(x)) = 1 / (1 + e^x) */
@@ -396,6 +397,19 @@ kda_status kda_prefill_recurrent(const kda_shape* shape, int32_t L, float* state
                                  const float* beta, float* o, int32_t ckpt_every,
                                  const int32_t* ckpt_slots, const kda_slots* slots, int32_t* dev_err,
                                  void* stream);
+
+/*
+ * kda_prefill_chunked on states in the slot pool: sequence b starts from
+ * slot state_slots[b] (device int32 [B], distinct ids) and leaves its final
+ * state and position there, so a prompt can continue from a cached prefix
+ * without copies.  Checkpoints go to the same pool (ckpt_slots as above, none
+ * of them one of the state slots).  An id outside [0, n_slots) sets
+ * KDA_DEV_ERR_SLOT_ID and the sequence is skipped.  dev_err must not be NULL.
+ */
+kda_status kda_prefill_chunked_slots(const kda_shape* shape, int32_t L, int32_t chunk, const int32_t* state_slots,
+                                     const kda_slots* slots, const void* q, const void* k, const void* v,
+                                     const float* alpha, const float* beta, float* o, int32_t ckpt_every,
+                                     const int32_t* ckpt_slots, int32_t* dev_err, void* stream);
 
 /*
  * The two prefills from raw projections (q, k, alpha_logit, beta_logit as in

@@ -22,7 +22,7 @@ VARIANTS = {0: "none", 1: "decode", 2: "verify", 3: "commit", 4: "snapshot", 5: 
             6: "prefill_recurrent", 7: "prefill_chunked", 8: "commit_verify", 9: "verify_varlen",
             10: "commit_verify_varlen", 11: "decode_prep", 12: "verify_prep", 13: "commit_verify_prep",
             14: "decode_slots", 15: "slot_copy", 16: "prefill_chunked_prep", 17: "prefill_recurrent_prep",
-            18: "verify_slots", 19: "commit_slots", 20: "commit_verify_slots"}
+            18: "verify_slots", 19: "commit_slots", 20: "commit_verify_slots", 21: "prefill_chunked_slots"}
 GATE_EXP_NEG_SOFTPLUS, GATE_SIGMOID = 0, 1
 DEV_ERR_ACCEPTED, DEV_ERR_CKPT_SLOT, DEV_ERR_DRAFT_LEN, DEV_ERR_SLOT_ID = 1, 2, 4, 8
 
@@ -70,6 +70,8 @@ _SIGS = {
     "kda_decode_step_slots": (_I, [ctypes.POINTER(Shape), _P, ctypes.POINTER(_Slots), _P, _P, _P, _P, _P, _P, _P,
                                    _P]),
     "kda_slot_copy": (_I, [ctypes.POINTER(Shape), _P, _P, _I, ctypes.POINTER(_Slots), _P]),
+    "kda_prefill_chunked_slots": (_I, [ctypes.POINTER(Shape), _I, _I, _P, ctypes.POINTER(_Slots), _P, _P, _P, _P, _P,
+                                       _P, _I, _P, _P, _P]),
     "kda_verify_slots": (_I, [ctypes.POINTER(Shape), _I, _P, ctypes.POINTER(_Slots), _P, _P, _P, _P, _P, _P,
                               ctypes.POINTER(_Log), _P, _P]),
     "kda_commit_slots": (_I, [ctypes.POINTER(Shape), _P, ctypes.POINTER(_Slots), ctypes.POINTER(_Log), _P, _P, _P]),
@@ -406,6 +408,24 @@ def commit_verify_slots(slot_ids, pool: SlotPool, q, k, v, alpha, beta, o, log: 
     _check(lib().kda_commit_verify_slots(ctypes.byref(sh), T, _ptr(slot_ids), ctypes.byref(pool.c),
                                          *(_ptr(x) for x in (q, k, v, alpha, beta, o)), ctypes.byref(log.c),
                                          _ptr(accepted) if accepted is not None else None, _ptr(dev_err), _stream()))
+
+
+def prefill_chunked_slots(state_slots, pool: SlotPool, q, k, v, alpha, beta, o, dev_err, *, chunk=64, ckpt_every=0,
+                          ckpt_slots=None, scale=None):
+    """prefill_chunked on states in a slot pool: sequence b starts from and ends in slot state_slots[b]."""
+    B = state_slots.shape[0]
+    _need(state_slots, "state_slots", (B,), torch.int32, pool.states.device)
+    _need(dev_err, "dev_err", (1,), torch.int32, pool.states.device)
+    batch = _Batch(B, pool)
+    L = q.shape[1]
+    _check_tokens(batch, L, q, k, v, alpha, beta, o)
+    n_ckpt = L // ckpt_every if ckpt_every > 0 else 0
+    if n_ckpt > 0:
+        _need(ckpt_slots, "ckpt_slots", (B, n_ckpt), torch.int32, pool.states.device)
+    sh = _shape(batch, q.dtype, scale)
+    _check(lib().kda_prefill_chunked_slots(ctypes.byref(sh), L, chunk, _ptr(state_slots), ctypes.byref(pool.c),
+                                           *(_ptr(x) for x in (q, k, v, alpha, beta, o)), ckpt_every,
+                                           _ptr(ckpt_slots) if n_ckpt else None, _ptr(dev_err), _stream()))
 
 
 def slot_copy(src_slots, dst_slots, pool: SlotPool):

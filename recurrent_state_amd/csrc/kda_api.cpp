@@ -456,11 +456,19 @@ namespace {
 kda_status prefill_chunked_impl(const kda_shape* shape, int32_t L, int32_t chunk, float* state, int64_t* pos,
                                 const void* q, const void* k, const void* v, const float* alpha, const float* beta,
                                 float* o, int32_t ckpt_every, const int32_t* ckpt_slots, const kda_slots* slots,
-                                int32_t* dev_err, int32_t gate, void* stream) {
+                                int32_t* dev_err, int32_t gate, void* stream, const int32_t* state_slots = nullptr) {
   kda_status r = check_prefill(shape, L, chunk, state, pos, q, k, v, alpha, beta, o, ckpt_every, ckpt_slots, slots,
                                dev_err);
   if (r != KDA_OK || shape->B == 0) return r;
   const bool ck = ckpt_every > 0 && L >= ckpt_every;
+  if (state_slots) {  // the caller passed the pool's arrays as state and pos
+    if ((r = check_slot_ids(state_slots, dev_err)) != KDA_OK) return r;
+    return launched(kda::launch_prefill_chunked(*shape, L, chunk, state, pos, kda::TokenInputs{q, k, v, alpha, beta},
+                                                o, ck ? ckpt_every : 0, ck ? ckpt_slots : nullptr, slots->states,
+                                                slots->pos, slots->n_slots, dev_err, gate,
+                                                static_cast<hipStream_t>(stream), state_slots),
+                    KDA_VARIANT_PREFILL_CHUNKED_SLOTS);
+  }
   return launched(kda::launch_prefill_chunked(*shape, L, chunk, state, pos, kda::TokenInputs{q, k, v, alpha, beta},
                                               o, ck ? ckpt_every : 0, ck ? ckpt_slots : nullptr,
                                               ck ? slots->states : nullptr, ck ? slots->pos : nullptr,
@@ -500,6 +508,18 @@ kda_status kda_prefill_chunked(const kda_shape* shape, int32_t L, int32_t chunk,
                                int32_t* dev_err, void* stream) {
   return prefill_chunked_impl(shape, L, chunk, state, pos, q, k, v, alpha, beta, o, ckpt_every, ckpt_slots, slots,
                               dev_err, -1, stream);
+}
+
+kda_status kda_prefill_chunked_slots(const kda_shape* shape, int32_t L, int32_t chunk, const int32_t* state_slots,
+                                     const kda_slots* slots, const void* q, const void* k, const void* v,
+                                     const float* alpha, const float* beta, float* o, int32_t ckpt_every,
+                                     const int32_t* ckpt_slots, int32_t* dev_err, void* stream) {
+  kda_status r = check_slots(slots);
+  if (r != KDA_OK) return r;
+  if (slots->n_slots == 0 && shape && shape->B > 0) return KDA_ERR_SLOT;
+  if (!dev_err && shape && shape->B > 0) return KDA_ERR_NULL;
+  return prefill_chunked_impl(shape, L, chunk, slots->states, slots->pos, q, k, v, alpha, beta, o, ckpt_every,
+                              ckpt_slots, slots, dev_err, -1, stream, state_slots);
 }
 
 kda_status kda_prefill_chunked_prep(const kda_shape* shape, int32_t gate, int32_t L, int32_t chunk, float* state,

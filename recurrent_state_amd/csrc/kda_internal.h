@@ -86,14 +86,18 @@ hipError_t launch_commit_verify(const kda_shape& s, int32_t T_pend, int32_t T, c
                                 LogPtrs log, int32_t gate, int32_t pend_gate, hipStream_t st,
                                 const int32_t* slot_ids = nullptr, int32_t n_slots = 0);
 // Prefills: gate < 0 prepared inputs, otherwise raw projections and logits.
+// state_slots (device [B], may be null): the states and positions are the
+// slot pool's (slot_states, slot_pos, n_slots), sequence b using slot
+// state_slots[b]; state and pos must then be the pool's arrays too.
 hipError_t launch_prefill_recurrent(const kda_shape& s, int32_t L, float* state, int64_t* pos,
                                     TokenInputs in, float* o, int32_t ckpt_every, const int32_t* ckpt_slots,
                                     float* slot_states, int64_t* slot_pos, int32_t n_slots,
-                                    int32_t* dev_err, int32_t gate, hipStream_t st);
+                                    int32_t* dev_err, int32_t gate, hipStream_t st,
+                                    const int32_t* state_slots = nullptr);
 hipError_t launch_prefill_chunked(const kda_shape& s, int32_t L, int32_t chunk, float* state, int64_t* pos,
                                   TokenInputs in, float* o, int32_t ckpt_every, const int32_t* ckpt_slots,
                                   float* slot_states, int64_t* slot_pos, int32_t n_slots, int32_t* dev_err,
-                                  int32_t gate, hipStream_t st);
+                                  int32_t gate, hipStream_t st, const int32_t* state_slots = nullptr);
 
 // Copies whole per-sequence states (n_floats each) and positions for up to
 // kMaxPairs (src, dst) index pairs per launch.

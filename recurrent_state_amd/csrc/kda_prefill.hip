@@ -189,6 +189,9 @@ struct PrefillArgs {
   int32_t n_slots;
   float scale;
   float gate_sign;  // raw projections: decay = sigmoid(gate_sign * logit)
+  // Non-null: sequence b's state and position are slot state_slots[b] of the
+  // pool (slot_states / slot_pos, n_slots); a bad id skips the sequence.
+  const int32_t* state_slots;
 };
 
 // LDS layout of one workgroup (bytes).  Region R2 holds Kh during the A/P
@@ -283,8 +286,16 @@ __global__ void __launch_bounds__(DV * 4) prefill_chunked_kernel(PrefillArgs<TIn
 
   const int bh = blockIdx.x;
   const int b = bh / a.H, h = bh - b * a.H;
+  int sb = b;  // index of the state and position this sequence uses
+  if (a.state_slots) {
+    sb = a.state_slots[b];
+    if (sb < 0 || sb >= a.n_slots) {  // uniform over the workgroup
+      if (h == 0 && threadIdx.x == 0) atomicOr(a.dev_err, KDA_DEV_ERR_SLOT_ID);
+      return;
+    }
+  }
   const bool owner = h == 0 && threadIdx.x == 0;  // the one writer of positions
-  const int64_t pos0 = owner ? a.pos[b] : 0;
+  const int64_t pos0 = owner ? a.pos[sb] : 0;
   const int n_ckpt = a.ckpt_every > 0 ? a.L / a.ckpt_every : 0;
   const size_t tok0 = (size_t)b * a.L;  // first token row of this sequence
   const f32x4_t zero4 = {0.f, 0.f, 0.f, 0.f};
@@ -293,7 +304,7 @@ __global__ void __launch_bounds__(DV * 4) prefill_chunked_kernel(PrefillArgs<TIn
   // st[mt][r] = S[16 mt + 4 g + r][col], at byte tile_voff + (16 mt + r) DV 4.
   f32x4_t st[MT];
   const int tile_voff = ((4 * ((threadIdx.x & 63) >> 4)) * DV + 16 * (threadIdx.x >> 6) + (threadIdx.x & 15)) * 4;
-  const rsrc_t rs_state = make_rsrc(a.state + (size_t)bh * DK * DV, DK * DV * 4);
+  const rsrc_t rs_state = make_rsrc(a.state + ((size_t)sb * a.H + h) * DK * DV, DK * DV * 4);
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
@@ -660,16 +671,16 @@ __global__ void __launch_bounds__(DV * 4) prefill_chunked_kernel(PrefillArgs<TIn
   for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
     for (int r = 0; r < 4; ++r) st_f32(rs_state, st[mt][r], tile_voff, (16 * mt + r) * DV * 4);
-  if (owner) a.pos[b] = pos0 + a.L;
+  if (owner) a.pos[sb] = pos0 + a.L;
 }
 
 template <int DK, int DV, typename TIn>
 hipError_t launch_cfg(const kda_shape& s, int32_t L, int32_t chunk, float* state, int64_t* pos, TokenInputs in,
                       float* o, int32_t ckpt_every, const int32_t* ckpt_slots, float* slot_states, int64_t* slot_pos,
-                      int32_t n_slots, int32_t* dev_err, int32_t gate, hipStream_t st) {
+                      int32_t n_slots, int32_t* dev_err, int32_t gate, const int32_t* state_slots, hipStream_t st) {
   PrefillArgs<TIn> a{state,      pos,     (const TIn*)in.q, (const TIn*)in.k, (const TIn*)in.v, in.alpha, in.beta,
                      o,          ckpt_slots, slot_states,  slot_pos,         dev_err,          s.H,      L,
-                     ckpt_every, n_slots, s.scale,         gate == KDA_GATE_SIGMOID ? 1.f : -1.f};
+                     ckpt_every, n_slots, s.scale,         gate == KDA_GATE_SIGMOID ? 1.f : -1.f, state_slots};
   const dim3 grid((unsigned)((size_t)s.B * s.H));
   auto go = [&](auto prep) {
     constexpr bool PREP = decltype(prep)::value;
@@ -688,18 +699,19 @@ hipError_t launch_cfg(const kda_shape& s, int32_t L, int32_t chunk, float* state
 template <typename TIn>
 hipError_t launch_dtype(const kda_shape& s, int32_t L, int32_t chunk, float* state, int64_t* pos, TokenInputs in,
                         float* o, int32_t ckpt_every, const int32_t* ckpt_slots, float* slot_states, int64_t* slot_pos,
-                        int32_t n_slots, int32_t* dev_err, int32_t gate, hipStream_t st) {
+                        int32_t n_slots, int32_t* dev_err, int32_t gate, const int32_t* state_slots,
+                        hipStream_t st) {
   if (s.dk == 128 && s.dv == 128)
     return launch_cfg<128, 128, TIn>(s, L, chunk, state, pos, in, o, ckpt_every, ckpt_slots, slot_states, slot_pos,
-                                     n_slots, dev_err, gate, st);
+                                     n_slots, dev_err, gate, state_slots, st);
   if (s.dk == 128 && s.dv == 64)
     return launch_cfg<128, 64, TIn>(s, L, chunk, state, pos, in, o, ckpt_every, ckpt_slots, slot_states, slot_pos,
-                                    n_slots, dev_err, gate, st);
+                                    n_slots, dev_err, gate, state_slots, st);
   if (s.dk == 64 && s.dv == 128)
     return launch_cfg<64, 128, TIn>(s, L, chunk, state, pos, in, o, ckpt_every, ckpt_slots, slot_states, slot_pos,
-                                    n_slots, dev_err, gate, st);
+                                    n_slots, dev_err, gate, state_slots, st);
   return launch_cfg<64, 64, TIn>(s, L, chunk, state, pos, in, o, ckpt_every, ckpt_slots, slot_states, slot_pos,
-                                 n_slots, dev_err, gate, st);
+                                 n_slots, dev_err, gate, state_slots, st);
 }
 
 }  // namespace
@@ -707,13 +719,13 @@ hipError_t launch_dtype(const kda_shape& s, int32_t L, int32_t chunk, float* sta
 hipError_t launch_prefill_chunked(const kda_shape& s, int32_t L, int32_t chunk, float* state, int64_t* pos,
                                   TokenInputs in, float* o, int32_t ckpt_every, const int32_t* ckpt_slots,
                                   float* slot_states, int64_t* slot_pos, int32_t n_slots, int32_t* dev_err,
-                                  int32_t gate, hipStream_t st) {
+                                  int32_t gate, hipStream_t st, const int32_t* state_slots) {
   if (chunk != 32 && chunk != 64) return hipErrorInvalidValue;
   if (s.in_dtype == KDA_BF16)
     return launch_dtype<bf16_t>(s, L, chunk, state, pos, in, o, ckpt_every, ckpt_slots, slot_states, slot_pos,
-                                n_slots, dev_err, gate, st);
+                                n_slots, dev_err, gate, state_slots, st);
   return launch_dtype<float>(s, L, chunk, state, pos, in, o, ckpt_every, ckpt_slots, slot_states, slot_pos, n_slots,
-                             dev_err, gate, st);
+                             dev_err, gate, state_slots, st);
 }
 
 }  // namespace kda

@@ -82,6 +82,7 @@ struct PrefillArgs {
   int32_t n_slots;
   float scale;
   float gate_sign;  // raw projections: decay = sigmoid(gate_sign * logit)
+  const int32_t* state_slots;  // non-null: states and positions in the slot pool
 };
 
 // Waves per workgroup (WPG): the column slices of one (sequence, head) are
@@ -220,9 +221,17 @@ __global__ void KDA_OCCUPANCY __launch_bounds__(kWave) prefill_recurrent_kernel(
   constexpr int R = P::R;
   const P p(a.H);
   const bool owner = p.h == 0 && p.slice == 0 && p.lane == 0;  // the one writer of positions
-  const int64_t pos0 = owner ? a.pos[p.b] : 0;
+  int sb = p.b;  // index of the state and position this sequence uses
+  if (a.state_slots) {
+    sb = a.state_slots[p.b];
+    if (sb < 0 || sb >= a.n_slots) {
+      if (owner) atomicOr(a.dev_err, KDA_DEV_ERR_SLOT_ID);
+      return;
+    }
+  }
+  const int64_t pos0 = owner ? a.pos[sb] : 0;
   const int n_ckpt = a.ckpt_every > 0 ? a.L / a.ckpt_every : 0;
-  float* sp = a.state + (size_t)p.bh * DK * DV + p.tile_off();
+  float* sp = a.state + ((size_t)sb * a.H + p.h) * DK * DV + p.tile_off();
   float S[R][4];
   load_tile<R, DV>(sp, S);
   TokenIn<TIn, R, true> cur, nxt;
@@ -255,7 +264,7 @@ __global__ void KDA_OCCUPANCY __launch_bounds__(kWave) prefill_recurrent_kernel(
     tok = tn;
   }
   store_tile<R, DV>(sp, S);
-  if (owner) a.pos[p.b] = pos0 + a.L;
+  if (owner) a.pos[sb] = pos0 + a.L;
 }
 
 template <int DK, int DV, int WPG>
@@ -357,14 +366,14 @@ hipError_t launch_commit(const kda_shape& s, int32_t T, float* state, int64_t* p
 hipError_t launch_prefill_recurrent(const kda_shape& s, int32_t L, float* state, int64_t* pos, TokenInputs in,
                                     float* o, int32_t ckpt_every, const int32_t* ckpt_slots, float* slot_states,
                                     int64_t* slot_pos, int32_t n_slots, int32_t* dev_err, int32_t gate,
-                                    hipStream_t st) {
+                                    hipStream_t st, const int32_t* state_slots) {
   dispatch(s, [&](auto c) {
     typedef decltype(c) C;
     typedef typename C::TIn TIn;
     constexpr int DK = C::DK, DV = C::DV;
     PrefillArgs<TIn> a{state,    pos,     (const TIn*)in.q, (const TIn*)in.k, (const TIn*)in.v, in.alpha, in.beta,
                        o,        ckpt_slots, slot_states,  slot_pos,         dev_err,          s.H,      L,
-                       ckpt_every, n_slots, s.scale,       gate == KDA_GATE_SIGMOID ? 1.f : -1.f};
+                       ckpt_every, n_slots, s.scale,       gate == KDA_GATE_SIGMOID ? 1.f : -1.f, state_slots};
     if (gate < 0)
       prefill_recurrent_kernel<DK, DV, TIn, false><<<grid_of<DK, DV, 1>(s), kWave, 0, st>>>(a);
     else

@@ -260,6 +260,13 @@ def test_slot_decode_and_copy_validation(k):
     assert L.kda_commit_verify_slots(ctypes.byref(s), 2, GOOD, ctypes.byref(slots), GOOD, GOOD, GOOD, GOOD, GOOD,
                                      GOOD, ctypes.byref(pend), GOOD, None, None) == NULL
     assert pend.pending_T == 2
+    assert L.kda_prefill_chunked_slots(ctypes.byref(s), 64, 64, GOOD, ctypes.byref(slots), GOOD, GOOD, GOOD, GOOD,
+                                       GOOD, GOOD, 0, None, None, None) == NULL          # dev_err
+    assert L.kda_prefill_chunked_slots(ctypes.byref(s), 64, 64, P(0x10002), ctypes.byref(slots), GOOD, GOOD, GOOD,
+                                       GOOD, GOOD, GOOD, 0, None, GOOD, None) == ALIGN
+    assert L.kda_prefill_chunked_slots(ctypes.byref(s), 64, 64, GOOD,
+                                       ctypes.byref(k._lib._Slots(0x200000, 0x300000, 0)), GOOD, GOOD, GOOD, GOOD,
+                                       GOOD, GOOD, 0, None, GOOD, None) == SLOT
 
 
 def test_snapshot_restore_validation(k):

@@ -178,3 +178,37 @@ def test_verify_slots_out_of_range_id_logs_nothing():
     assert err.item() == kda.DEV_ERR_SLOT_ID          # the bad id is flagged again and skipped
     changed = [i for i in range(n_slots) if not torch.equal(bits(pool.states[i]), before[i])]
     assert changed == [1]
+
+
+@pytest.mark.parametrize("L,chunk", [(200, 64), (37, 32)])
+def test_prefill_chunked_on_slots_equals_dense(L, chunk):
+    spec = spec_for(128, 128, "bf16", tag=155)
+    B = 3
+    every = chunk
+    say(f"prefill on slots L={L} chunk={chunk}")
+    n_ck = L // every
+    n_slots = 2 * B + B * n_ck
+    pool = _pool(spec, n_slots, 9)
+    state_ids = torch.tensor([4, 0, 2], dtype=torch.int32, device="cuda")
+    ck_ids = (2 * B + torch.arange(B * n_ck, dtype=torch.int32, device="cuda")).view(B, n_ck)
+    S = pool.states[state_ids.long()].clone()
+    pos = pool.pos[state_ids.long()].clone()
+    dpool = kda.SlotPool(max(1, B * n_ck), spec.H, 128, 128, "cuda")
+    dck = torch.arange(B * n_ck, dtype=torch.int32, device="cuda").view(B, n_ck)
+    d = {name: dev_tensor(x) for name, x in synth.token_inputs(spec, B, L).items()}
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    o_s = torch.empty((B, L, spec.H, 128), device="cuda")
+    o_d = torch.empty_like(o_s)
+    kda.prefill_chunked_slots(state_ids, pool, d["q"], d["k"], d["v"], d["alpha"], d["beta"], o_s, err, chunk=chunk,
+                              ckpt_every=every, ckpt_slots=ck_ids)
+    assert kda.last_variant() == "prefill_chunked_slots"
+    kda.prefill_chunked(S, pos, d["q"], d["k"], d["v"], d["alpha"], d["beta"], o_d, chunk=chunk, ckpt_every=every,
+                        ckpt_slots=dck if n_ck else None, pool=dpool, dev_err=err)
+    torch.cuda.synchronize()
+    assert err.item() == 0
+    assert torch.equal(bits(o_s), bits(o_d))
+    assert torch.equal(bits(pool.states[state_ids.long()]), bits(S)) and torch.equal(pool.pos[state_ids.long()], pos)
+    for b in range(B):
+        for m in range(n_ck):
+            assert torch.equal(bits(pool.states[int(ck_ids[b, m])]), bits(dpool.states[int(dck[b, m])]))
+            assert pool.pos[int(ck_ids[b, m])].item() == dpool.pos[int(dck[b, m])].item()
