@@ -533,8 +533,8 @@ def main():
         rows["decode_slots_b64"] = bench_decode_slots(torch, kda, synth, B_HEAD, L_LAYERS, 100, 10, device)
         log("copy reference")
         rows["d2d_copy_1GiB"] = bench_copy(torch, device)
-        log("hot (cache-resident) decode B=64, one layer")
-        rows["decode_b64_one_layer_hot"] = bench_decode(torch, kda, synth, 64, 1, 400, 40, device)
+        log("decode B=64, one layer state (128 MiB)")
+        rows["decode_b64_one_layer"] = bench_decode(torch, kda, synth, 64, 1, 400, 40, device)
         sweep = []
         for B in (1, 2, 4, 8, 16, 32, 64):
             layers = max(L_LAYERS, (1 << 30) // (B * H * STATE_BYTES))
