@@ -584,7 +584,11 @@ __global__ void __launch_bounds__(DV * 4) prefill_chunked_kernel(PrefillArgs<TIn
         }
       }
     }
-    __syncthreads();
+    // No barrier here: the next loads and the X product below read only
+    // registers and the Kt/Qt planes, so the waves without a diagonal block
+    // run them while the others are still solving theirs (two waves share a
+    // SIMD, so one's MFMA work fills the other's latency-bound solve).  The
+    // barrier after the X product orders the M writes before their reads.
 
     if (c + 1 < n_chunks) issue_loads(c + 1, tid);
 
@@ -600,6 +604,7 @@ __global__ void __launch_bounds__(DV * 4) prefill_chunked_kernel(PrefillArgs<TIn
 #pragma unroll
       for (int mt = 0; mt < 2 * NB; ++mt) xs[mt] = mfma3(plane_op2(kq_hi, kq_lo, 16 * mt + l16, L::RS_Q, k0_), sop, xs[mt]);
     }
+    __syncthreads();  // the diagonal blocks of M are complete
     // 4c/4d: R = V - Kt S, then E = (I + A)^-1 Diag(beta) R by 16-token blocks:
     //   E_i = X_ii (beta_i R_i - sum_{j<i} A_ij E_j).
     // E is kept only as MFMA B operands eop[kb] (32-token k blocks); while
