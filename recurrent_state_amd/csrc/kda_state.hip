@@ -90,10 +90,11 @@ struct PrefillArgs {
 // one workgroup on one CU (all slices).  The waves never synchronise either
 // way.  Decode and commit pick WPG from the batch: one-wave workgroups start
 // faster when there are few of them; whole-state workgroups keep a state's
-// reads and writes on one CU, which measured 3.5 % faster at B = 64 and 2 %
-// at B = 16 (H = 32).
+// reads and writes on one CU.  With non-temporal state traffic the
+// whole-state shape measured faster from B = 8 on at H = 32 (1,024 slices:
+// 6.86 against 7.19 us per launch at B = 8, 49.6 against 52.2 us at B = 64).
 #ifndef KDA_WIDE_WAVES
-#define KDA_WIDE_WAVES 2048
+#define KDA_WIDE_WAVES 1024
 #endif
 constexpr size_t kWideWaves = KDA_WIDE_WAVES;  // total slices from which whole-state workgroups are used
 // The recurrent prefill loads token t+1's inputs while token t computes (1),

@@ -461,7 +461,7 @@ def test_workgroup_shapes_bit_identical():
     # sequence's results do not depend on the batch it ran in, and commit(a)
     # equals a decode steps in both shapes.
     spec = synth.ConfigSpec("wg", 117, (16,), 32, 128, 128, "bf16", "softplus", "normal", 0)
-    Bbig, T = 16, 3                      # 16 x 32 x 4 = 2,048 slices: whole-state workgroups
+    Bbig, T = 16, 3                      # 16 x 32 x 4 = 2,048 slices (>= 1,024): whole-state workgroups
     S0 = synth.initial_state(spec, Bbig)
     inp = synth.token_inputs(spec, Bbig, T)
     d = dev_inputs(inp)
