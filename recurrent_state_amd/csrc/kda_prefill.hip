@@ -5,14 +5,14 @@
 // rounding), chunk by chunk.  For a chunk of n <= CH tokens starting from
 // state S (rows = key channels, columns = value channels):
 //
-//   g_r  = sum_{s <= r} log alpha_s                 per key channel (log2 domain here)
-//   Kt   = k * 2^g,  Qt = q * 2^g,  Kh = k * 2^-g,  Kb = k * 2^(g_n - g)
+//   G_r  = prod_{s <= r} alpha_s                    per key channel (cumulative decay)
+//   Kt   = k * G,  Qt = q * G,  Kh = k / G,  Kb = k * G_n / G
 //   A    = strictly-lower(Diag(beta) Kt Kh^T)       (CH x CH)
 //   P    = lower-with-diagonal(Qt Kh^T)             (CH x CH)
 //   T    = (I + A)^-1 Diag(beta)
 //   E    = T (V - Kt S)                             (CH x dv)
 //   O    = scale (Qt S + P E)
-//   S'   = Diag(2^g_n) S + Kb^T E
+//   S'   = Diag(G_n) S + Kb^T E
 //
 // One workgroup owns one (sequence, head) for the whole prompt and walks
 // its chunks in order; wave w of the workgroup (dv / 16 waves) owns value
@@ -224,13 +224,13 @@ struct Smem {
   static constexpr int r2_b = 2 * CC_PLANE * 2 + DIAG * 4;
   static constexpr int off_r3 = off_r2 + (r2_a > r2_b ? r2_a : r2_b);
   static constexpr int total = off_r3 + 2 * CC_PLANE * 2;
-  // beta (CH floats) and 2^g_n (DK floats) live in the 16 unused bytes at
+  // beta (CH floats) and G_n (DK floats) live in the 16 unused bytes at
   // the end of each row of the Kb^T hi plane (4 floats per row).
-  static_assert(CH + DK <= 4 * DK && (RS_C - CH) * 2 == 16, "beta and 2^g_n must fit the Kb row padding");
-  // Token-group totals of the decay cumsum, only live between the two passes
+  static_assert(CH + DK <= 4 * DK && (RS_C - CH) * 2 == 16, "beta and G_n must fit the Kb row padding");
+  // Token-group decay products, only live between the two passes
   // of the preparation: they borrow the M region, which is written later.
   static constexpr int off_tot = off_r3;
-  static_assert(NG * DK * 4 <= 2 * CC_PLANE * 2, "cumsum scratch must fit the M region");
+  static_assert(NG * DK * 4 <= 2 * CC_PLANE * 2, "decay-product scratch must fit the M region");
   static_assert(total <= 163840, "LDS budget exceeded");
   static_assert(off_kb % 16 == 0 && r2_a % 16 == 0 && off_r3 % 16 == 0 && (RS_Q * 2) % 16 == 0 &&
                     (KQ_PLANE * 2) % 16 == 0 && (KB_PLANE * 2) % 16 == 0 && (KH_PLANE * 2) % 16 == 0 &&
@@ -274,7 +274,7 @@ __global__ void __launch_bounds__(DV * 4) prefill_chunked_kernel(PrefillArgs<TIn
   float* adiag = reinterpret_cast<float*>(smem + L::off_r2 + 2 * L::CC_PLANE * 2);
   bf16_t* m_hi = reinterpret_cast<bf16_t*>(smem + L::off_r3);
   bf16_t* m_lo = m_hi + L::CC_PLANE;
-  // beta_t at misc(t), 2^g_n of channel c at misc(CH + c): the Kb^T row padding.
+  // beta_t at misc(t), G_n of channel c at misc(CH + c): the Kb^T row padding.
   auto misc = [&](int v) -> float& {
     return *reinterpret_cast<float*>(smem + L::off_kb + (v >> 2) * (L::RS_C * 2) + CH * 2 + (v & 3) * 4);
   };
@@ -366,7 +366,7 @@ __global__ void __launch_bounds__(DV * 4) prefill_chunked_kernel(PrefillArgs<TIn
     const size_t row0 = (tok0 + t_base) * a.H + h;  // [B][L][H] row index of the chunk's first token
     const rsrc_t rs_o = make_rsrc(a.o + row0 * DV, ((n - 1) * rowv + DV) * 4);
 
-    // ---- Phase 1: decay cumsum and the decayed key/query planes ---------
+    // ---- Phase 1: cumulative decay and the decayed key/query planes -----
     const int cp = tid % CP, tg = tid / CP;
     const int c0 = 2 * cp;
     float al0[TPG], al1[TPG], k0[TPG], k1[TPG], q0[TPG], q1[TPG];
@@ -410,14 +410,16 @@ __global__ void __launch_bounds__(DV * 4) prefill_chunked_kernel(PrefillArgs<TIn
 #pragma unroll
       for (int r = 0; r < 4; ++r) vv[mt][r] = 16 * mt + 4 * g + r < n ? rv[mt][r].get() : 0.f;
     {
-      // Pass A: per-channel prefix sums of log2(alpha) within the token
-      // group; the group totals are combined through LDS.
+      // Pass A: per-channel running products of alpha within the token group
+      // (the cumulative decay itself: one multiply per token instead of a
+      // logarithm and two exponentials); the group totals are combined
+      // through LDS.
       float g0[TPG], g1[TPG];
-      float s0 = 0.f, s1 = 0.f;
+      float s0 = 1.f, s1 = 1.f;
 #pragma unroll
       for (int i = 0; i < TPG; ++i) {
-        s0 += __log2f(al0[i]);
-        s1 += __log2f(al1[i]);
+        s0 *= al0[i];
+        s1 *= al1[i];
         g0[i] = s0;
         g1[i] = s1;
       }
@@ -425,32 +427,31 @@ __global__ void __launch_bounds__(DV * 4) prefill_chunked_kernel(PrefillArgs<TIn
       stot[tg * DK + c0 + 1] = s1;
       if (cp < TPG) misc(tg * TPG + cp) = tg * TPG + cp < n ? (PREP ? sigmoid_f32(rb) : rb) : 0.f;  // padding: beta 0
       __syncthreads();
-      float off0 = 0.f, off1 = 0.f, gn0 = 0.f, gn1 = 0.f;
+      float off0 = 1.f, off1 = 1.f, gn0 = 1.f, gn1 = 1.f;
 #pragma unroll
       for (int j = 0; j < NG; ++j) {
         const float t0 = stot[j * DK + c0], t1 = stot[j * DK + c0 + 1];
         if (j < tg) {
-          off0 += t0;
-          off1 += t1;
+          off0 *= t0;
+          off1 *= t1;
         }
-        gn0 += t0;
-        gn1 += t1;
+        gn0 *= t0;
+        gn1 *= t1;
       }
       if (tg == 0) {
-        misc(CH + c0) = __builtin_amdgcn_exp2f(gn0);
-        misc(CH + c0 + 1) = __builtin_amdgcn_exp2f(gn1);
+        misc(CH + c0) = gn0;
+        misc(CH + c0 + 1) = gn1;
       }
       // Pass B: the decayed planes; Kb goes to transposed planes two tokens at a time.
-      // Kb = Kh 2^(g_n) (no third exponential per element).
-      const float egn0 = __builtin_amdgcn_exp2f(gn0), egn1 = __builtin_amdgcn_exp2f(gn1);
+      // Kb = Kh gamma_n (no third factor per element).
+      const float egn0 = gn0, egn1 = gn1;
       const int pc = kpos(c0);  // storage column of the channel pair (c0, c0 + 1)
       uint32_t kbh0 = 0, kbl0 = 0, kbh1 = 0, kbl1 = 0;
 #pragma unroll
       for (int i = 0; i < TPG; ++i) {
         const int tr = tg * TPG + i;
-        const float x0 = off0 + g0[i], x1 = off1 + g1[i];
-        const float e0 = __builtin_amdgcn_exp2f(x0), e1 = __builtin_amdgcn_exp2f(x1);
-        const float ie0 = __builtin_amdgcn_exp2f(-x0), ie1 = __builtin_amdgcn_exp2f(-x1);
+        const float e0 = off0 * g0[i], e1 = off1 * g1[i];  // gamma of token tr
+        const float ie0 = __builtin_amdgcn_rcpf(e0), ie1 = __builtin_amdgcn_rcpf(e1);
         uint32_t hi, lo;
         split2(k0[i] * e0, k1[i] * e1, hi, lo);  // Kt
         *reinterpret_cast<uint32_t*>(kq_hi + tr * L::RS_Q + pc) = hi;
@@ -642,7 +643,7 @@ __global__ void __launch_bounds__(DV * 4) prefill_chunked_kernel(PrefillArgs<TIn
         if (tr < n) st_f32(rs_o, a.scale * xs[NB + mt][r], (tr * rowv + col) * 4, 0);
       }
     }
-    // 4f: S = Diag(2^g_n) S + Kb^T E.
+    // 4f: S = Diag(G_n) S + Kb^T E.
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
       const float4 g4 = misc4(CH + 16 * mt + 4 * g);
