@@ -216,8 +216,9 @@ struct Streams {
 };
 
 // One group of G <= kGroup tokens starting at token t0, from the state tile S
-// (rows [R rg, R rg + R) of this lane, columns col0 .. col0 + 3).  MULTI:
-// advance S to the state after the group.  PREP: the inputs are raw
+// (rows [R rg, R rg + R) of this lane, columns col0 .. col0 + 3).  MULTI with
+// advance: advance S to the state after the group (not needed after the last
+// group, whose state is never written).  PREP: the inputs are raw
 // projections and logits; they are prepared here (unit q and k, decay and
 // beta from their logits, as the decode step from raw projections does) and
 // logged raw.
@@ -225,7 +226,7 @@ template <int DK, int DV, typename TIn, bool MULTI, bool PREP, typename LoadStat
 __device__ __forceinline__ void verify_group(const VerifyArgs<TIn>& a, const Streams<TIn, DK, DV>& st,
                                              VerifyLds<DK>& L, float (&S)[DK / kRowGroups][4], int t0, int G,
                                              size_t tok0, size_t tok0_log, int lane, int wave, bool first,
-                                             const LoadState& load_state) {
+                                             const LoadState& load_state, bool advance) {
   constexpr int NW = DV / kSliceCols;
   constexpr int R = DK / kRowGroups;
   constexpr int CPL = DK / kWave;  // key channels per lane in the preparation
@@ -325,7 +326,7 @@ __device__ __forceinline__ void verify_group(const VerifyArgs<TIn>& a, const Str
       const int ix = VerifyLds<DK>::at(ch0 + c);
       L.kap[t][ix] = kv * gam;
       L.rho[t][ix] = qv * gam;
-      if (MULTI) {
+      if (MULTI && advance) {
         float cof = kv;
 #pragma unroll
         for (int r = 1; r < kGroup; ++r)
@@ -356,7 +357,7 @@ __device__ __forceinline__ void verify_group(const VerifyArgs<TIn>& a, const Str
       }
     }
   }
-  if (MULTI && wave == 0) {
+  if (MULTI && advance && wave == 0) {
 #pragma unroll
     for (int c = 0; c < CPL; ++c) {
       float gam = av[0][c];
@@ -443,7 +444,7 @@ __device__ __forceinline__ void verify_group(const VerifyArgs<TIn>& a, const Str
   }
 
   // ---- 4. advance the in-register state --------------------------------
-  if (MULTI) {
+  if (MULTI && advance) {
 #pragma unroll
     for (int r4 = 0; r4 < R / 4; ++r4) {
       const float4 g4 = *reinterpret_cast<const float4*>(&L.gend[rg * RP + 4 * r4]);
@@ -557,16 +558,16 @@ __global__ void __launch_bounds__(kWave * (DV / kSliceCols)) verify_chunk_kernel
     if (MULTI) {
       for (int t0 = 0; t0 < Tv; t0 += kGroup)
         verify_group<DK, DV, TIn, true, PREP>(a, st, L, S, t0, min(kGroup, Tv - t0), tok0, tok0_log, lane, wave, t0 == 0,
-                                        no_load);
+                                              no_load, t0 + kGroup < Tv);
     } else {
-      verify_group<DK, DV, TIn, false, PREP>(a, st, L, S, 0, Tv, tok0, tok0_log, lane, wave, true, no_load);
+      verify_group<DK, DV, TIn, false, PREP>(a, st, L, S, 0, Tv, tok0, tok0_log, lane, wave, true, no_load, false);
     }
   } else if (MULTI) {
     for (int t0 = 0; t0 < Tv; t0 += kGroup)
       verify_group<DK, DV, TIn, true, PREP>(a, st, L, S, t0, min(kGroup, Tv - t0), tok0, tok0_log, lane, wave, t0 == 0,
-                                      load_state);
+                                            load_state, t0 + kGroup < Tv);
   } else {
-    verify_group<DK, DV, TIn, false, PREP>(a, st, L, S, 0, Tv, tok0, tok0_log, lane, wave, true, load_state);
+    verify_group<DK, DV, TIn, false, PREP>(a, st, L, S, 0, Tv, tok0, tok0_log, lane, wave, true, load_state, false);
   }
 }
 
