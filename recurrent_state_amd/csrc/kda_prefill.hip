@@ -145,13 +145,11 @@ struct Pair2<bf16_t> {
 };
 template <>
 struct Pair2<float> {
-  float a, b;
-  __device__ __forceinline__ void load(rsrc_t r, int voff) {
-    a = ld_f32(r, voff, 0);
-    b = ld_f32(r, voff + 4, 0);
-  }
-  __device__ __forceinline__ float lo() const { return a; }
-  __device__ __forceinline__ float hi() const { return b; }
+  typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+  u32x2 w;  // one 8-byte load (a vector result type keeps the load full width)
+  __device__ __forceinline__ void load(rsrc_t r, int voff) { w = __builtin_amdgcn_raw_buffer_load_b64(r, voff, 0, 0); }
+  __device__ __forceinline__ float lo() const { return __uint_as_float(w.x); }
+  __device__ __forceinline__ float hi() const { return __uint_as_float(w.y); }
 };
 // One input element as loaded.
 template <typename TIn>
