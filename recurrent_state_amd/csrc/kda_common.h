@@ -97,39 +97,60 @@ __device__ __forceinline__ float elem(const Raw<float, N>& r, int i) {
   return (i % 4) == 0 ? w.x : (i % 4) == 1 ? w.y : (i % 4) == 2 ? w.z : w.w;
 }
 
-// Four consecutive value entries (the lane's columns).
-template <typename TIn>
-struct Raw4;
+// The lane's NC consecutive value entries (NC = 4, or 2 in the small-batch
+// speculative kernels, whose waves own 16 value columns).
+template <typename TIn, int NC>
+struct RawV;
 template <>
-struct Raw4<bf16_t> {
+struct RawV<bf16_t, 4> {
   typedef uint2 vec;
   vec w;
 };
 template <>
-struct Raw4<float> {
+struct RawV<float, 4> {
   typedef float4 vec;
   vec w;
 };
+template <>
+struct RawV<bf16_t, 2> {
+  typedef uint32_t vec;
+  vec w;
+};
+template <>
+struct RawV<float, 2> {
+  typedef float2 vec;
+  vec w;
+};
+template <typename TIn>
+using Raw4 = RawV<TIn, 4>;
 
-template <typename TIn>
-__device__ __forceinline__ void load4(const TIn* p, Raw4<TIn>& r) {
-  r.w = *reinterpret_cast<const typename Raw4<TIn>::vec*>(p);
+template <typename TIn, int NC>
+__device__ __forceinline__ void load4(const TIn* p, RawV<TIn, NC>& r) {
+  r.w = *reinterpret_cast<const typename RawV<TIn, NC>::vec*>(p);
 }
-template <typename TIn>
-__device__ __forceinline__ void store4(TIn* p, const Raw4<TIn>& r) {
-  *reinterpret_cast<typename Raw4<TIn>::vec*>(p) = r.w;
+template <typename TIn, int NC>
+__device__ __forceinline__ void store4(TIn* p, const RawV<TIn, NC>& r) {
+  *reinterpret_cast<typename RawV<TIn, NC>::vec*>(p) = r.w;
 }
-__device__ __forceinline__ void widen4(const Raw4<bf16_t>& r, float (&x)[4]) {
+__device__ __forceinline__ void widen4(const RawV<bf16_t, 4>& r, float (&x)[4]) {
   x[0] = bf16_lo(r.w.x);
   x[1] = bf16_hi(r.w.x);
   x[2] = bf16_lo(r.w.y);
   x[3] = bf16_hi(r.w.y);
 }
-__device__ __forceinline__ void widen4(const Raw4<float>& r, float (&x)[4]) {
+__device__ __forceinline__ void widen4(const RawV<float, 4>& r, float (&x)[4]) {
   x[0] = r.w.x;
   x[1] = r.w.y;
   x[2] = r.w.z;
   x[3] = r.w.w;
+}
+__device__ __forceinline__ void widen4(const RawV<bf16_t, 2>& r, float (&x)[2]) {
+  x[0] = bf16_lo(r.w);
+  x[1] = bf16_hi(r.w);
+}
+__device__ __forceinline__ void widen4(const RawV<float, 2>& r, float (&x)[2]) {
+  x[0] = r.w.x;
+  x[1] = r.w.y;
 }
 
 // Cross-lane pair exchange on gfx950.  After the swap, a holds the value of
@@ -218,18 +239,19 @@ __device__ __forceinline__ float lane_group_sum(float x) {
 // live next to the state.  Decode, verify, commit and the recurrent prefill
 // all call this one function with the same lane mapping, so their states and
 // outputs agree bit for bit.
-template <int R, bool WITH_OUT, typename TIn>
-__device__ __forceinline__ void token_update(float (&S)[R][4], const Raw<TIn, R>& kraw, const Raw<float, R>& araw,
-                                             const Raw<TIn, R>& qraw, const float (&vc)[4], float beta,
-                                             float scale, float (&o)[4]) {
-  float u[4] = {0.f, 0.f, 0.f, 0.f};
-  float w[4] = {0.f, 0.f, 0.f, 0.f};
+template <int R, bool WITH_OUT, typename TIn, int NC>
+__device__ __forceinline__ void token_update(float (&S)[R][NC], const Raw<TIn, R>& kraw, const Raw<float, R>& araw,
+                                             const Raw<TIn, R>& qraw, const float (&vc)[NC], float beta,
+                                             float scale, float (&o)[NC]) {
+  float u[NC], w[NC];
+#pragma unroll
+  for (int c = 0; c < NC; ++c) u[c] = w[c] = 0.f;
   float kq = 0.f;
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     const float kr = elem(kraw, r), ar = elem(araw, r);
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
+    for (int c = 0; c < NC; ++c) {
       const float s1 = ar * S[r][c];
       S[r][c] = s1;
       u[c] = __builtin_fmaf(kr, s1, u[c]);
@@ -238,24 +260,24 @@ __device__ __forceinline__ void token_update(float (&S)[R][4], const Raw<TIn, R>
     if (WITH_OUT) kq = __builtin_fmaf(kr, elem(qraw, r), kq);
   }
 #pragma unroll
-  for (int c = 0; c < 4; ++c) u[c] = rowgroup_sum(u[c]);
+  for (int c = 0; c < NC; ++c) u[c] = rowgroup_sum(u[c]);
   if (WITH_OUT) {
 #pragma unroll
-    for (int c = 0; c < 4; ++c) w[c] = rowgroup_sum(w[c]);
+    for (int c = 0; c < NC; ++c) w[c] = rowgroup_sum(w[c]);
     kq = rowgroup_sum(kq);
   }
-  float e[4];
+  float e[NC];
 #pragma unroll
-  for (int c = 0; c < 4; ++c) e[c] = beta * (vc[c] - u[c]);
+  for (int c = 0; c < NC; ++c) e[c] = beta * (vc[c] - u[c]);
   if (WITH_OUT) {
 #pragma unroll
-    for (int c = 0; c < 4; ++c) o[c] = scale * __builtin_fmaf(e[c], kq, w[c]);
+    for (int c = 0; c < NC; ++c) o[c] = scale * __builtin_fmaf(e[c], kq, w[c]);
   }
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     const float kr = elem(kraw, r);
 #pragma unroll
-    for (int c = 0; c < 4; ++c) S[r][c] = __builtin_fmaf(kr, e[c], S[r][c]);
+    for (int c = 0; c < NC; ++c) S[r][c] = __builtin_fmaf(kr, e[c], S[r][c]);
   }
 }
 
@@ -283,20 +305,21 @@ __device__ __forceinline__ float inv_norm(float sq) {
 // vectors enter as factors: u = (S1^T k) / |k|, S = S1 + (k / |k|) e^T,
 // o = scale (S1^T q / |q| + e (k . q) / (|k| |q|)).  Without WITH_OUT (the
 // replay of logged tokens) q is not touched and the state is the same.
-template <int R, bool WITH_OUT, typename TIn>
-__device__ __forceinline__ void token_update_prep(float (&S)[R][4], const Raw<TIn, R>& kraw,
+template <int R, bool WITH_OUT, typename TIn, int NC>
+__device__ __forceinline__ void token_update_prep(float (&S)[R][NC], const Raw<TIn, R>& kraw,
                                                   const Raw<float, R>& xraw, const Raw<TIn, R>& qraw,
-                                                  const float (&vc)[4], float beta_logit, float gsign, float scale,
-                                                  float (&o)[4]) {
-  float u[4] = {0.f, 0.f, 0.f, 0.f};
-  float w[4] = {0.f, 0.f, 0.f, 0.f};
+                                                  const float (&vc)[NC], float beta_logit, float gsign, float scale,
+                                                  float (&o)[NC]) {
+  float u[NC], w[NC];
+#pragma unroll
+  for (int c = 0; c < NC; ++c) u[c] = w[c] = 0.f;
   float kq = 0.f, kk = 0.f, qq = 0.f;
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     const float kr = elem(kraw, r);
     const float ar = sigmoid_f32(gsign * elem(xraw, r));
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
+    for (int c = 0; c < NC; ++c) {
       const float s1 = ar * S[r][c];
       S[r][c] = s1;
       u[c] = __builtin_fmaf(kr, s1, u[c]);
@@ -310,7 +333,7 @@ __device__ __forceinline__ void token_update_prep(float (&S)[R][4], const Raw<TI
     }
   }
 #pragma unroll
-  for (int c = 0; c < 4; ++c) {
+  for (int c = 0; c < NC; ++c) {
     u[c] = rowgroup_sum(u[c]);
     if (WITH_OUT) w[c] = rowgroup_sum(w[c]);
   }
@@ -321,20 +344,20 @@ __device__ __forceinline__ void token_update_prep(float (&S)[R][4], const Raw<TI
   }
   const float rk = inv_norm(kk);
   const float beta = sigmoid_f32(beta_logit);
-  float e[4];
+  float e[NC];
 #pragma unroll
-  for (int c = 0; c < 4; ++c) e[c] = beta * (vc[c] - u[c] * rk);
+  for (int c = 0; c < NC; ++c) e[c] = beta * (vc[c] - u[c] * rk);
   if (WITH_OUT) {
     const float rq = inv_norm(qq);
     const float kqn = kq * rk * rq;
 #pragma unroll
-    for (int c = 0; c < 4; ++c) o[c] = scale * __builtin_fmaf(e[c], kqn, w[c] * rq);
+    for (int c = 0; c < NC; ++c) o[c] = scale * __builtin_fmaf(e[c], kqn, w[c] * rq);
   }
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     const float kn = elem(kraw, r) * rk;
 #pragma unroll
-    for (int c = 0; c < 4; ++c) S[r][c] = __builtin_fmaf(kn, e[c], S[r][c]);
+    for (int c = 0; c < NC; ++c) S[r][c] = __builtin_fmaf(kn, e[c], S[r][c]);
   }
 }
 
@@ -389,11 +412,11 @@ __device__ __forceinline__ void store_tile(float* p, const float (&S)[R][4]) {
 }
 
 // The per-token inputs one lane needs, as stored (raw) and widened.
-template <typename TIn, int R, bool WITH_Q>
+template <typename TIn, int R, bool WITH_Q, int NC = 4>
 struct TokenIn {
   Raw<TIn, R> k, q;
   Raw<float, R> a;
-  Raw4<TIn> v;
+  RawV<TIn, NC> v;
   float beta;
   __device__ __forceinline__ void load(const TIn* kp, const TIn* qp, const float* ap, const TIn* vp,
                                        const float* bp) {
@@ -403,14 +426,14 @@ struct TokenIn {
     load4(vp, v);
     beta = *bp;
   }
-  __device__ __forceinline__ void update(float (&S)[R][4], float scale, float (&o)[4]) const {
-    float vc[4];
+  __device__ __forceinline__ void update(float (&S)[R][NC], float scale, float (&o)[NC]) const {
+    float vc[NC];
     widen4(v, vc);
     token_update<R, WITH_Q>(S, k, a, q, vc, beta, scale, o);
   }
   // Raw projections: `a` holds the decay logits and `beta` the beta logit.
-  __device__ __forceinline__ void update_prep(float (&S)[R][4], float gsign, float scale, float (&o)[4]) const {
-    float vc[4];
+  __device__ __forceinline__ void update_prep(float (&S)[R][NC], float gsign, float scale, float (&o)[NC]) const {
+    float vc[NC];
     widen4(v, vc);
     token_update_prep<R, WITH_Q>(S, k, a, q, vc, beta, gsign, scale, o);
   }
@@ -425,7 +448,7 @@ struct TokenIn {
 // both call this, so their states are bit-identical to n decode steps of the
 // matching kind.  Callers pick RAW from the log record before loading any
 // state, so each form runs as its own code path.
-template <int DK, int DV, typename TIn, int R, bool RAW>
+template <int DK, int DV, typename TIn, int R, bool RAW, int NC = 4>
 struct LogReplay {
   const TIn* k;
   const TIn* v;
@@ -433,8 +456,8 @@ struct LogReplay {
   const float* beta;
   size_t tok0;
   int H, row0, col0;
-  TokenIn<TIn, R, false> cur, nxt;
-  __device__ __forceinline__ void load(int t, TokenIn<TIn, R, false>& x) const {
+  TokenIn<TIn, R, false, NC> cur, nxt;
+  __device__ __forceinline__ void load(int t, TokenIn<TIn, R, false, NC>& x) const {
     const size_t tk = tok0 + (size_t)t * H;
     x.load(k + tk * DK + row0, nullptr, alpha + tk * DK + row0, v + tk * DV + col0, beta + tk);
   }
@@ -444,10 +467,10 @@ struct LogReplay {
   // Applies logged tokens 0 .. n-1 (token 0 primed); the loads of token t + 1
   // are issued before token t's update, so each token's memory latency hides
   // behind the previous update.
-  __device__ __forceinline__ void run(float (&S)[R][4], int n, float gsign) {
+  __device__ __forceinline__ void run(float (&S)[R][NC], int n, float gsign) {
     for (int t = 0; t < n; ++t) {
       if (t + 1 < n) load(t + 1, nxt);
-      float o[4];
+      float o[NC];
       if constexpr (RAW)
         cur.update_prep(S, gsign, 0.f, o);
       else
@@ -457,15 +480,15 @@ struct LogReplay {
   }
 };
 
-template <int DK, int DV, typename TIn, int R, bool RAW>
-__device__ __forceinline__ void replay_log(float (&S)[R][4], const TIn* log_k, const TIn* log_v,
+template <int DK, int DV, typename TIn, int R, bool RAW, int NC>
+__device__ __forceinline__ void replay_log(float (&S)[R][NC], const TIn* log_k, const TIn* log_v,
                                            const float* log_alpha, const float* log_beta, size_t tok0, int H,
                                            int n, int row0, int col0, float gsign) {
-  TokenIn<TIn, R, false> cur;
+  TokenIn<TIn, R, false, NC> cur;
   for (int t = 0; t < n; ++t) {
     const size_t tk = tok0 + (size_t)t * H;
     cur.load(log_k + tk * DK + row0, nullptr, log_alpha + tk * DK + row0, log_v + tk * DV + col0, log_beta + tk);
-    float o[4];
+    float o[NC];
     if constexpr (RAW)
       cur.update_prep(S, gsign, 0.f, o);
     else

@@ -159,11 +159,12 @@ struct Chan<float, 2> {
   }
 };
 
-// Four consecutive value columns as stored.
-template <typename TIn>
-struct Val4;
+// NC consecutive value columns as stored (NC = 4, or 2 in the small-batch
+// kernels whose waves own 16 value columns).
+template <typename TIn, int NC>
+struct ValC;
 template <>
-struct Val4<bf16_t> {
+struct ValC<bf16_t, 4> {
   u32x2 w;
   __device__ __forceinline__ void load(rsrc_t r, int vo, int so) { w = __builtin_amdgcn_raw_buffer_load_b64(r, vo, so, 0); }
   __device__ __forceinline__ void store(rsrc_t r, int vo, int so) const {
@@ -177,7 +178,7 @@ struct Val4<bf16_t> {
   }
 };
 template <>
-struct Val4<float> {
+struct ValC<float, 4> {
   u32x4 w;
   __device__ __forceinline__ void load(rsrc_t r, int vo, int so) { w = __builtin_amdgcn_raw_buffer_load_b128(r, vo, so, 0); }
   __device__ __forceinline__ void store(rsrc_t r, int vo, int so) const {
@@ -190,6 +191,57 @@ struct Val4<float> {
     x[3] = __uint_as_float(w.w);
   }
 };
+template <>
+struct ValC<bf16_t, 2> {
+  uint32_t w;
+  __device__ __forceinline__ void load(rsrc_t r, int vo, int so) { w = __builtin_amdgcn_raw_buffer_load_b32(r, vo, so, 0); }
+  __device__ __forceinline__ void store(rsrc_t r, int vo, int so) const {
+    __builtin_amdgcn_raw_buffer_store_b32(w, r, vo, so, 0);
+  }
+  __device__ __forceinline__ void widen(float (&x)[2]) const {
+    x[0] = bf16_lo(w);
+    x[1] = bf16_hi(w);
+  }
+};
+template <>
+struct ValC<float, 2> {
+  u32x2 w;
+  __device__ __forceinline__ void load(rsrc_t r, int vo, int so) { w = __builtin_amdgcn_raw_buffer_load_b64(r, vo, so, 0); }
+  __device__ __forceinline__ void store(rsrc_t r, int vo, int so) const {
+    __builtin_amdgcn_raw_buffer_store_b64(w, r, vo, so, 0);
+  }
+  __device__ __forceinline__ void widen(float (&x)[2]) const {
+    x[0] = __uint_as_float(w.x);
+    x[1] = __uint_as_float(w.y);
+  }
+};
+
+// NC fp32 values as one 16- or 8-byte buffer store (AUX: cache-policy bits).
+template <int NC, int AUX>
+__device__ __forceinline__ void store_cols(const float (&x)[NC], rsrc_t r, int vo, int so) {
+  if constexpr (NC == 4) {
+    const u32x4 w = {__float_as_uint(x[0]), __float_as_uint(x[1]), __float_as_uint(x[2]), __float_as_uint(x[3])};
+    __builtin_amdgcn_raw_buffer_store_b128(w, r, vo, so, AUX);
+  } else {
+    const u32x2 w = {__float_as_uint(x[0]), __float_as_uint(x[1])};
+    __builtin_amdgcn_raw_buffer_store_b64(w, r, vo, so, AUX);
+  }
+}
+// NC fp32 values from one 16- or 8-byte buffer load (AUX: cache-policy bits).
+template <int NC, int AUX>
+__device__ __forceinline__ void load_cols(float (&x)[NC], rsrc_t r, int vo, int so) {
+  if constexpr (NC == 4) {
+    const u32x4 w = __builtin_amdgcn_raw_buffer_load_b128(r, vo, so, AUX);
+    x[0] = __uint_as_float(w.x);
+    x[1] = __uint_as_float(w.y);
+    x[2] = __uint_as_float(w.z);
+    x[3] = __uint_as_float(w.w);
+  } else {
+    const u32x2 w = __builtin_amdgcn_raw_buffer_load_b64(r, vo, so, AUX);
+    x[0] = __uint_as_float(w.x);
+    x[1] = __uint_as_float(w.y);
+  }
+}
 
 // Windows over one (sequence, head)'s T tokens: consecutive tokens are H
 // rows apart in every [B][T][H][d] tensor.
@@ -222,17 +274,18 @@ struct Streams {
 // projections and logits; they are prepared here (unit q and k, decay and
 // beta from their logits, as the decode step from raw projections does) and
 // logged raw.
-template <int DK, int DV, typename TIn, bool MULTI, bool PREP, typename LoadState>
+template <int DK, int DV, typename TIn, bool MULTI, bool PREP, int NC, typename LoadState>
 __device__ __forceinline__ void verify_group(const VerifyArgs<TIn>& a, const Streams<TIn, DK, DV>& st,
-                                             VerifyLds<DK>& L, float (&S)[DK / kRowGroups][4], int t0, int G,
+                                             VerifyLds<DK>& L, float (&S)[DK / kRowGroups][NC], int t0, int G,
                                              size_t tok0, size_t tok0_log, int lane, int wave, bool first,
                                              const LoadState& load_state, bool advance) {
-  constexpr int NW = DV / kSliceCols;
+  constexpr int NW = DV / (kRowGroups * NC);  // waves: each owns 8 NC value columns
+  constexpr int QW = (kGroup + NW - 1) / NW;    // preparation tokens per wave
   constexpr int R = DK / kRowGroups;
   constexpr int CPL = DK / kWave;  // key channels per lane in the preparation
   constexpr int RP = VerifyLds<DK>::RP;
   const int rg = lane >> 3, cg = lane & 7;
-  const int col0 = wave * kSliceCols + cg * 4;
+  const int col0 = wave * kRowGroups * NC + cg * NC;
   const int ch0 = lane * CPL;
   const int kvo_in = ch0 * (int)sizeof(TIn), kvo_f32 = ch0 * 4;
   const int vvo_in = col0 * (int)sizeof(TIn), vvo_f32 = col0 * 4;
@@ -242,8 +295,8 @@ __device__ __forceinline__ void verify_group(const VerifyArgs<TIn>& a, const Str
   // (r >= G) re-read the group's last token and are never used.
   Chan<float, CPL> al[kGroup];
   Chan<TIn, CPL> kk[kGroup];
-  Val4<TIn> vv[kGroup];
-  Chan<TIn, CPL> qq[kGroup / NW];  // q of this wave's tokens wave, wave + NW, ...
+  ValC<TIn, NC> vv[kGroup];
+  Chan<TIn, CPL> qq[QW];  // q of this wave's tokens wave, wave + NW, ...
   float bt[kGroup];
 #pragma unroll
   for (int r = 0; r < kGroup; ++r) {
@@ -254,7 +307,7 @@ __device__ __forceinline__ void verify_group(const VerifyArgs<TIn>& a, const Str
     bt[r] = a.beta[tok0 + (size_t)tr * a.H];
   }
 #pragma unroll
-  for (int j = 0; j < kGroup / NW; ++j) qq[j].load(st.q, kvo_in, (t0 + min(wave + j * NW, G - 1)) * st.sk_in);
+  for (int j = 0; j < QW; ++j) qq[j].load(st.q, kvo_in, (t0 + min(wave + j * NW, G - 1)) * st.sk_in);
   // The state tile goes last: loads retire in order, so the preparation
   // below waits only for the small input loads while the tile streams in,
   // and the projections consume its rows as they land.
@@ -288,7 +341,7 @@ __device__ __forceinline__ void verify_group(const VerifyArgs<TIn>& a, const Str
   }
   if (MULTI && !first) __syncthreads();  // the previous group's LDS reads are done
 #pragma unroll
-  for (int j = 0; j < kGroup / NW; ++j) {
+  for (int j = 0; j < QW; ++j) {
     const int t = wave + j * NW;
     if (t >= G) break;
     const int tt = t0 + t;
@@ -383,11 +436,11 @@ __device__ __forceinline__ void verify_group(const VerifyArgs<TIn>& a, const Str
   // ---- 2. projections x_t = S0^T kap_t, y_t = S0^T rho_t -----------------
   // Row blocks outermost: each block of four state rows is used by every
   // token of the group and is then dead (single-group case).
-  float x[kGroup][4], y[kGroup][4];
+  float x[kGroup][NC], y[kGroup][NC];
 #pragma unroll
   for (int t = 0; t < kGroup; ++t)
 #pragma unroll
-    for (int c = 0; c < 4; ++c) x[t][c] = y[t][c] = 0.f;
+    for (int c = 0; c < NC; ++c) x[t][c] = y[t][c] = 0.f;
 #pragma unroll
   for (int r4 = 0; r4 < R / 4; ++r4) {
 #pragma unroll
@@ -399,7 +452,7 @@ __device__ __forceinline__ void verify_group(const VerifyArgs<TIn>& a, const Str
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
-          for (int c = 0; c < 4; ++c) {
+          for (int c = 0; c < NC; ++c) {
             x[t][c] = __builtin_fmaf(kq[i], S[4 * r4 + i][c], x[t][c]);
             y[t][c] = __builtin_fmaf(rq[i], S[4 * r4 + i][c], y[t][c]);
           }
@@ -410,7 +463,7 @@ __device__ __forceinline__ void verify_group(const VerifyArgs<TIn>& a, const Str
   for (int t = 0; t < kGroup; ++t) {
     if (t < G) {
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
+      for (int c = 0; c < NC; ++c) {
         x[t][c] = rowgroup_sum_many(x[t][c]);
         y[t][c] = rowgroup_sum_many(y[t][c]);
       }
@@ -418,15 +471,15 @@ __device__ __forceinline__ void verify_group(const VerifyArgs<TIn>& a, const Str
   }
 
   // ---- 3. forward substitution and outputs, per column ------------------
-  float e[kGroup][4];
+  float e[kGroup][NC];
 #pragma unroll
   for (int t = 0; t < kGroup; ++t) {
     if (t < G) {
-      float vc[4];
+      float vc[NC];
       vv[t].widen(vc);
-      float o[4];
+      float o[NC];
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
+      for (int c = 0; c < NC; ++c) {
         float u = x[t][c];
 #pragma unroll
         for (int s = 0; s < t; ++s) u = __builtin_fmaf(L.A[t][s], e[s][c], u);
@@ -437,8 +490,7 @@ __device__ __forceinline__ void verify_group(const VerifyArgs<TIn>& a, const Str
         o[c] = a.scale * w;
       }
       if (rg == t) {
-        const u32x4 ov = {__float_as_uint(o[0]), __float_as_uint(o[1]), __float_as_uint(o[2]), __float_as_uint(o[3])};
-        __builtin_amdgcn_raw_buffer_store_b128(ov, st.o, vvo_f32, (t0 + t) * st.sv_f32, 0);
+        store_cols<NC, 0>(o, st.o, vvo_f32, (t0 + t) * st.sv_f32);
       }
     }
   }
@@ -452,7 +504,7 @@ __device__ __forceinline__ void verify_group(const VerifyArgs<TIn>& a, const Str
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int c = 0; c < 4; ++c) S[4 * r4 + i][c] *= gq[i];
+        for (int c = 0; c < NC; ++c) S[4 * r4 + i][c] *= gq[i];
 #pragma unroll
       for (int s = 0; s < kGroup; ++s) {
         if (s < G) {
@@ -461,7 +513,7 @@ __device__ __forceinline__ void verify_group(const VerifyArgs<TIn>& a, const Str
 #pragma unroll
           for (int i = 0; i < 4; ++i)
 #pragma unroll
-            for (int c = 0; c < 4; ++c) S[4 * r4 + i][c] = __builtin_fmaf(cq[i], e[s][c], S[4 * r4 + i][c]);
+            for (int c = 0; c < NC; ++c) S[4 * r4 + i][c] = __builtin_fmaf(cq[i], e[s][c], S[4 * r4 + i][c]);
         }
       }
     }
@@ -477,8 +529,12 @@ __device__ __forceinline__ void verify_group(const VerifyArgs<TIn>& a, const Str
 // (double-buffered, more registers): for small batches, where the round is
 // bound by the latency of one workgroup's serial replay, not by bandwidth.
 template <int DK, int DV, typename TIn, bool MULTI, bool COMMIT, bool PREP, bool PF>
-__global__ void __launch_bounds__(kWave * (DV / kSliceCols)) verify_chunk_kernel(VerifyArgs<TIn> a) {
+__global__ void __launch_bounds__(kWave * DV / (kRowGroups * (PF ? 2 : 4))) verify_chunk_kernel(VerifyArgs<TIn> a) {
   constexpr int R = DK / kRowGroups;
+  // Value columns per lane: small batches (PF) split a state over twice as
+  // many waves (16 columns each) to halve each wave's serial chain; the
+  // arithmetic of every column is the same either way.
+  constexpr int NC = PF ? 2 : 4;
   __shared__ __align__(16) VerifyLds<DK> L;
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -500,21 +556,15 @@ __global__ void __launch_bounds__(kWave * (DV / kSliceCols)) verify_chunk_kernel
   }
 
   // The lane's state tile, loaded once.
-  float S[R][4];
+  float S[R][NC];
   const rsrc_t rs = make_rsrc(a.state + ((size_t)sb * a.H + h) * DK * DV, DK * DV * 4);
-  const int row0 = rg * R, col0 = wave * kSliceCols + cg * 4;
+  const int row0 = rg * R, col0 = wave * kRowGroups * NC + cg * NC;
   const int svo = (row0 * DV + col0) * 4;
-  auto load_state = [&](float (&St)[R][4]) {
+  auto load_state = [&](float (&St)[R][NC]) {
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
-      const u32x4 w = __builtin_amdgcn_raw_buffer_load_b128(rs, svo, r * DV * 4, kStateLoadAux);
-      St[r][0] = __uint_as_float(w.x);
-      St[r][1] = __uint_as_float(w.y);
-      St[r][2] = __uint_as_float(w.z);
-      St[r][3] = __uint_as_float(w.w);
-    }
+    for (int r = 0; r < R; ++r) load_cols<NC, kStateLoadAux>(St[r], rs, svo, r * DV * 4);
   };
-  auto no_load = [](float (&)[R][4]) {};
+  auto no_load = [](float (&)[R][NC]) {};
   // Tokens this sequence verifies.
   int Tv = T;
   if (a.draft_len) {
@@ -527,7 +577,7 @@ __global__ void __launch_bounds__(kWave * (DV / kSliceCols)) verify_chunk_kernel
     }
   }
   if (COMMIT) {
-    LogReplay<DK, DV, TIn, R, PREP> rp{a.log_k, a.log_v, a.log_alpha, a.log_beta, tok0_log, a.H, row0, col0};
+    LogReplay<DK, DV, TIn, R, PREP, NC> rp{a.log_k, a.log_v, a.log_alpha, a.log_beta, tok0_log, a.H, row0, col0};
     if (PF && a.T_pend > 0) rp.prime();  // logged token 0's loads go out ahead of the state tile
     load_state(S);
     if (a.T_pend > 0) {
@@ -542,11 +592,7 @@ __global__ void __launch_bounds__(kWave * (DV / kSliceCols)) verify_chunk_kernel
           replay_log<DK, DV, TIn, R, PREP>(S, a.log_k, a.log_v, a.log_alpha, a.log_beta, tok0_log, a.H, n, row0,
                                            col0, a.pend_gate_sign);
 #pragma unroll
-        for (int r = 0; r < R; ++r) {
-          const u32x4 w = {__float_as_uint(S[r][0]), __float_as_uint(S[r][1]), __float_as_uint(S[r][2]),
-                           __float_as_uint(S[r][3])};
-          __builtin_amdgcn_raw_buffer_store_b128(w, rs, svo, r * DV * 4, kStateStoreAux);
-        }
+        for (int r = 0; r < R; ++r) store_cols<NC, kStateStoreAux>(S[r], rs, svo, r * DV * 4);
         if (h == 0 && wave == 0 && lane == 0) a.pos[sb] += n;
       }
       __syncthreads();  // every wave has read the pending log rows and count before the verify rewrites them
@@ -557,17 +603,17 @@ __global__ void __launch_bounds__(kWave * (DV / kSliceCols)) verify_chunk_kernel
   if (COMMIT) {
     if (MULTI) {
       for (int t0 = 0; t0 < Tv; t0 += kGroup)
-        verify_group<DK, DV, TIn, true, PREP>(a, st, L, S, t0, min(kGroup, Tv - t0), tok0, tok0_log, lane, wave, t0 == 0,
+        verify_group<DK, DV, TIn, true, PREP, NC>(a, st, L, S, t0, min(kGroup, Tv - t0), tok0, tok0_log, lane, wave, t0 == 0,
                                               no_load, t0 + kGroup < Tv);
     } else {
-      verify_group<DK, DV, TIn, false, PREP>(a, st, L, S, 0, Tv, tok0, tok0_log, lane, wave, true, no_load, false);
+      verify_group<DK, DV, TIn, false, PREP, NC>(a, st, L, S, 0, Tv, tok0, tok0_log, lane, wave, true, no_load, false);
     }
   } else if (MULTI) {
     for (int t0 = 0; t0 < Tv; t0 += kGroup)
-      verify_group<DK, DV, TIn, true, PREP>(a, st, L, S, t0, min(kGroup, Tv - t0), tok0, tok0_log, lane, wave, t0 == 0,
+      verify_group<DK, DV, TIn, true, PREP, NC>(a, st, L, S, t0, min(kGroup, Tv - t0), tok0, tok0_log, lane, wave, t0 == 0,
                                             load_state, t0 + kGroup < Tv);
   } else {
-    verify_group<DK, DV, TIn, false, PREP>(a, st, L, S, 0, Tv, tok0, tok0_log, lane, wave, true, load_state, false);
+    verify_group<DK, DV, TIn, false, PREP, NC>(a, st, L, S, 0, Tv, tok0, tok0_log, lane, wave, true, load_state, false);
   }
 }
 
@@ -576,9 +622,10 @@ constexpr int kLatencyPairs = 512;
 
 template <int DK, int DV, typename TIn, bool COMMIT, bool PREP>
 void launch_cfg(const VerifyArgs<TIn>& a, int32_t B, hipStream_t st) {
-  const dim3 grid(B * a.H), block(kWave * (DV / kSliceCols));
+  const dim3 grid(B * a.H);
   auto go = [&](auto pf) {
     constexpr bool PF = decltype(pf)::value;
+    const dim3 block(kWave * DV / (kRowGroups * (PF ? 2 : 4)));
     if (a.T <= kGroup)
       verify_chunk_kernel<DK, DV, TIn, false, COMMIT, PREP, PF><<<grid, block, 0, st>>>(a);
     else
