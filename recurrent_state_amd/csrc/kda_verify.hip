@@ -525,9 +525,10 @@ __device__ __forceinline__ void verify_group(const VerifyArgs<TIn>& a, const Str
 // COMMIT: first replay the accepted prefix of the pending verify (the commit
 // step, with the decode step's token loop), write the committed state and
 // position, then verify the new tokens from the state still in registers.
-// PF (with COMMIT): the replay keeps the next logged token's loads in flight
-// (double-buffered, more registers): for small batches, where the round is
-// bound by the latency of one workgroup's serial replay, not by bandwidth.
+// PF: small batches, where a launch is bound by the latency of one
+// workgroup's serial chain, not by bandwidth.  Each wave owns 16 value
+// columns instead of 32 (twice the waves per state), and with COMMIT the
+// replay keeps the next logged token's loads in flight (double-buffered).
 template <int DK, int DV, typename TIn, bool MULTI, bool COMMIT, bool PREP, bool PF>
 __global__ void __launch_bounds__(kWave * DV / (kRowGroups * (PF ? 2 : 4))) verify_chunk_kernel(VerifyArgs<TIn> a) {
   constexpr int R = DK / kRowGroups;
@@ -617,7 +618,9 @@ __global__ void __launch_bounds__(kWave * DV / (kRowGroups * (PF ? 2 : 4))) veri
   }
 }
 
-// Below this many (sequence, head) pairs the fused round prefetches its replay.
+// Below this many (sequence, head) pairs a launch is bound by each
+// workgroup's serial chain, not by bandwidth: verify (and the fused round)
+// run 16 value columns per wave, and the fused round prefetches its replay.
 constexpr int kLatencyPairs = 512;
 
 template <int DK, int DV, typename TIn, bool COMMIT, bool PREP>
@@ -631,11 +634,9 @@ void launch_cfg(const VerifyArgs<TIn>& a, int32_t B, hipStream_t st) {
     else
       verify_chunk_kernel<DK, DV, TIn, true, COMMIT, PREP, PF><<<grid, block, 0, st>>>(a);
   };
-  if constexpr (COMMIT) {
-    if (B * a.H < kLatencyPairs) {
-      go(std::true_type{});
-      return;
-    }
+  if (B * a.H < kLatencyPairs) {
+    go(std::true_type{});
+    return;
   }
   go(std::false_type{});
 }
