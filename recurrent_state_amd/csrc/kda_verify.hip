@@ -26,11 +26,13 @@
 // One workgroup per (sequence, head), dv / 32 waves; wave w owns value
 // columns [32 w, 32 w + 32) with the state lane mapping of the other state
 // kernels (lane = 8 rg + cg: rows [R rg, R rg + R), columns 4 cg .. 4 cg + 3).
-// Per group of up to four tokens:
+// Small batches use dv / 16 waves of 16 columns (columns 2 cg, 2 cg + 1 of
+// the wave's slice): each column's arithmetic is the same, with half the work
+// per wave.  Per group of up to four tokens:
 //   1. preparation (all waves): gamma_t k_t, gamma_t q_t, the update
 //      coefficients and the A / P entries into LDS; wave w takes the tokens
 //      t = w (mod waves) and lane l key channels [CPL l, CPL l + CPL);
-//   2. projections: each lane multiplies its R x 4 state tile into 2 G
+//   2. projections: each lane multiplies its R x NC state tile into 2 G
 //      accumulators per column, then sums over the 8 row groups in-wave
 //      (DPP row rotate, v_permlane16_swap, v_permlane32_swap);
 //   3. per column: forward substitution for e_t, then o_t;
