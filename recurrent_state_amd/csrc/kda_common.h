@@ -393,22 +393,54 @@ __device__ __forceinline__ void state_store4(float* p, float a, float b, float c
 #endif
 }
 
-template <int R, int DV>
-__device__ __forceinline__ void load_tile(const float* p, float (&S)[R][4]) {
+__device__ __forceinline__ float2 state_load2(const float* p) {
+#if KDA_STATE_NT & 2
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  const f32x2 x = __builtin_nontemporal_load(reinterpret_cast<const f32x2*>(p));
+  return make_float2(x.x, x.y);
+#else
+  return *reinterpret_cast<const float2*>(p);
+#endif
+}
+
+__device__ __forceinline__ void state_store2(float* p, float a, float b) {
+#if KDA_STATE_NT & 1
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  const f32x2 x = {a, b};
+  __builtin_nontemporal_store(x, reinterpret_cast<f32x2*>(p));
+#else
+  *reinterpret_cast<float2*>(p) = make_float2(a, b);
+#endif
+}
+
+// A lane's R x NC state tile (rows DV floats apart), NC = 4 or 2 columns.
+template <int R, int DV, int NC>
+__device__ __forceinline__ void load_tile(const float* p, float (&S)[R][NC]) {
 #pragma unroll
   for (int r = 0; r < R; ++r) {
-    const float4 x = state_load4(p + (size_t)r * DV);
-    S[r][0] = x.x;
-    S[r][1] = x.y;
-    S[r][2] = x.z;
-    S[r][3] = x.w;
+    if constexpr (NC == 4) {
+      const float4 x = state_load4(p + (size_t)r * DV);
+      S[r][0] = x.x;
+      S[r][1] = x.y;
+      S[r][2] = x.z;
+      S[r][3] = x.w;
+    } else {
+      const float2 x = state_load2(p + (size_t)r * DV);
+      S[r][0] = x.x;
+      S[r][1] = x.y;
+    }
   }
 }
 
-template <int R, int DV>
-__device__ __forceinline__ void store_tile(float* p, const float (&S)[R][4]) {
+template <int R, int DV, int NC>
+__device__ __forceinline__ void store_tile(float* p, const float (&S)[R][NC]) {
 #pragma unroll
-  for (int r = 0; r < R; ++r) state_store4(p + (size_t)r * DV, S[r][0], S[r][1], S[r][2], S[r][3]);
+  for (int r = 0; r < R; ++r) {
+    if constexpr (NC == 4)
+      state_store4(p + (size_t)r * DV, S[r][0], S[r][1], S[r][2], S[r][3]);
+    else
+      state_store2(p + (size_t)r * DV, S[r][0], S[r][1]);
+  }
 }
 
 // The per-token inputs one lane needs, as stored (raw) and widened.

@@ -97,6 +97,14 @@ struct PrefillArgs {
 #define KDA_WIDE_WAVES 1024
 #endif
 constexpr size_t kWideWaves = KDA_WIDE_WAVES;  // total slices from which whole-state workgroups are used
+// Below this many 32-column slices (B <= 3 at H = 32, dv = 128) decode runs
+// one-wave workgroups of 16 value columns: twice the waves per state, half
+// the serial work per wave, the same arithmetic per column (measured 3.33 ->
+// 2.95 us per launch at B = 1, 3.71 -> 3.53 at B = 2; at B = 4 it was slower).
+#ifndef KDA_NARROW_WAVES
+#define KDA_NARROW_WAVES 512
+#endif
+constexpr size_t kNarrowWaves = KDA_NARROW_WAVES;
 // The recurrent prefill loads token t+1's inputs while token t computes (1),
 // or loads each token's inputs when it starts (0: fewer live registers).
 #ifndef KDA_PREFETCH_NEXT
@@ -115,17 +123,19 @@ constexpr size_t kWideWaves = KDA_WIDE_WAVES;  // total slices from which whole-
 
 constexpr int kXcds = 8;  // accelerator complex dies on MI355X, each with its own L2
 
-template <int DV, int WPG>
+// Value columns per lane NC: 4 (waves of 32 columns) or, for the smallest
+// batches' decode, 2 (waves of 16 columns, twice the waves per state).
+template <int DV, int WPG, int NC = 4>
 constexpr int waves_per_group() {
-  return WPG < DV / kSliceCols ? WPG : DV / kSliceCols;
+  return WPG < DV / (kRowGroups * NC) ? WPG : DV / (kRowGroups * NC);
 }
 
 // Where a wave sits: its (sequence, head) index and its lane's rows/columns.
-template <int DK, int DV, int WPG_ = 1>
+template <int DK, int DV, int WPG_ = 1, int NC = 4>
 struct Place {
   static constexpr int R = DK / kRowGroups;
-  static constexpr int SLICES = DV / kSliceCols;
-  static constexpr int WPG = waves_per_group<DV, WPG_>();
+  static constexpr int SLICES = DV / (kRowGroups * NC);
+  static constexpr int WPG = waves_per_group<DV, WPG_, NC>();
   int bh, b, h, slice, rg, cg, row0, col0, lane;
   __device__ __forceinline__ Place(int H) {
     lane = threadIdx.x & (kWave - 1);
@@ -147,7 +157,7 @@ struct Place {
     rg = lane >> 3;
     cg = lane & 7;
     row0 = rg * R;
-    col0 = slice * kSliceCols + cg * 4;
+    col0 = slice * kRowGroups * NC + cg * NC;
   }
   // Offset of this lane's first state element inside a [dk][dv] state.
   __device__ __forceinline__ size_t tile_off() const { return (size_t)row0 * DV + col0; }
@@ -156,9 +166,9 @@ struct Place {
 // PREP: the inputs are raw projections and logits, prepared in the step
 // (token_update_prep).  SLOTS: the states and positions live in a slot pool,
 // addressed through slot_ids (an id out of range is flagged and skipped).
-template <int DK, int DV, typename TIn, int WPG, bool PREP, bool SLOTS>
-__global__ void KDA_OCCUPANCY __launch_bounds__((kWave * waves_per_group<DV, WPG>())) decode_kernel(StepArgs<TIn> a) {
-  typedef Place<DK, DV, WPG> P;
+template <int DK, int DV, typename TIn, int WPG, bool PREP, bool SLOTS, int NC = 4>
+__global__ void KDA_OCCUPANCY __launch_bounds__((kWave * waves_per_group<DV, WPG, NC>())) decode_kernel(StepArgs<TIn> a) {
+  typedef Place<DK, DV, WPG, NC> P;
   constexpr int R = P::R;
   const P p(a.H);
   int sb = p.b;  // index of the state (and position) this sequence uses
@@ -170,18 +180,23 @@ __global__ void KDA_OCCUPANCY __launch_bounds__((kWave * waves_per_group<DV, WPG
     }
   }
   float* sp = a.state + ((size_t)sb * a.H + p.h) * DK * DV + p.tile_off();
-  float S[R][4];
+  float S[R][NC];
   load_tile<R, DV>(sp, S);
-  TokenIn<TIn, R, true> in;
+  TokenIn<TIn, R, true, NC> in;
   in.load(a.k + (size_t)p.bh * DK + p.row0, a.q + (size_t)p.bh * DK + p.row0,
           a.alpha + (size_t)p.bh * DK + p.row0, a.v + (size_t)p.bh * DV + p.col0, a.beta + p.bh);
-  float o[4];
+  float o[NC];
   if constexpr (PREP)
     in.update_prep(S, a.gate_sign, a.scale, o);
   else
     in.update(S, a.scale, o);
   store_tile<R, DV>(sp, S);
-  if (p.rg == 0) *reinterpret_cast<float4*>(a.o + (size_t)p.bh * DV + p.col0) = make_float4(o[0], o[1], o[2], o[3]);
+  if (p.rg == 0) {
+    if constexpr (NC == 4)
+      *reinterpret_cast<float4*>(a.o + (size_t)p.bh * DV + p.col0) = make_float4(o[0], o[1], o[2], o[3]);
+    else
+      *reinterpret_cast<float2*>(a.o + (size_t)p.bh * DV + p.col0) = make_float2(o[0], o[1]);
+  }
   if (p.h == 0 && p.slice == 0 && p.lane == 0) a.pos[sb] += 1;
 }
 
@@ -268,9 +283,9 @@ __global__ void KDA_OCCUPANCY __launch_bounds__(kWave) prefill_recurrent_kernel(
   if (owner) a.pos[sb] = pos0 + a.L;
 }
 
-template <int DK, int DV, int WPG>
+template <int DK, int DV, int WPG, int NC = 4>
 dim3 grid_of(const kda_shape& s) {
-  return dim3((unsigned)((size_t)s.B * s.H * (DV / kSliceCols) / waves_per_group<DV, WPG>()));
+  return dim3((unsigned)((size_t)s.B * s.H * (DV / (kRowGroups * NC)) / waves_per_group<DV, WPG, NC>()));
 }
 
 // Total one-wave slices of a launch (one per 32 value columns of every state).
@@ -316,8 +331,10 @@ hipError_t launch_decode_any(const kda_shape& s, float* state, int64_t* pos, Tok
     if (slice_waves<DV>(s) >= kWideWaves)
       decode_kernel<DK, DV, TIn, 4, PREP, SLOTS>
           <<<grid_of<DK, DV, 4>(s), kWave * waves_per_group<DV, 4>(), 0, st>>>(a);
-    else
+    else if (slice_waves<DV>(s) >= kNarrowWaves)
       decode_kernel<DK, DV, TIn, 1, PREP, SLOTS><<<grid_of<DK, DV, 1>(s), kWave, 0, st>>>(a);
+    else
+      decode_kernel<DK, DV, TIn, 1, PREP, SLOTS, 2><<<grid_of<DK, DV, 1, 2>(s), kWave, 0, st>>>(a);
   });
   return hipGetLastError();
 }

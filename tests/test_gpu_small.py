@@ -457,9 +457,10 @@ def test_commit_verify_bad_count_and_nothing_pending():
 
 def test_workgroup_shapes_bit_identical():
     # Large batches run decode and commit with whole-state workgroups, small
-    # ones with one-wave workgroups; the lane arithmetic is the same, so a
-    # sequence's results do not depend on the batch it ran in, and commit(a)
-    # equals a decode steps in both shapes.
+    # ones with one-wave workgroups, and the smallest decode (B = 2 here) with
+    # one-wave workgroups of 16 value columns; the arithmetic of every column
+    # is the same, so a sequence's results do not depend on the batch it ran
+    # in, and commit(a) equals a decode steps in every shape.
     spec = synth.ConfigSpec("wg", 117, (16,), 32, 128, 128, "bf16", "softplus", "normal", 0)
     Bbig, T = 16, 3                      # 16 x 32 x 4 = 2,048 slices (>= 1,024): whole-state workgroups
     S0 = synth.initial_state(spec, Bbig)
