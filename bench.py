@@ -603,7 +603,7 @@ def main():
                    "steps_per_graph": STEPS_PER_GRAPH},
         "device": {"name": props.name, "compute_units": props.multi_processor_count,
                    "memory_bytes": props.total_memory},
-        "roofline": {"bound": "hbm", "kernel": "decode_kernel<128,128,bf16,4,false,false>",
+        "roofline": {"bound": "hbm", "kernel": "decode_kernel<128,128,bf16,4,false,false,4>",
                      "achieved": head["achieved_GBs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": head["achieved_GBs"] / HBM_PEAK_GBS, "traffic": counted_traffic(),
                      "algorithmic_bytes_per_launch": bytes_per_launch, "launch_us": head["launch_us"]},
