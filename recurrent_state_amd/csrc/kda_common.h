@@ -9,6 +9,9 @@
 // row index by the whole wave touches 8 full 128-byte lines (one per row
 // group).  Reductions over the key axis run inside the wave (xor over lane
 // bits 3..5), so waves never synchronise with each other and no LDS is used.
+// The smallest batches use 16-column slices instead (NC = 2 columns per
+// lane: col0 = 16 * slice + 2 * cg): the same rows per lane and the same
+// reduction tree, so every column's arithmetic is unchanged.
 #pragma once
 
 #include <hip/hip_runtime.h>
