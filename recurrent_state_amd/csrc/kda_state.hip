@@ -97,8 +97,8 @@ struct PrefillArgs {
 #define KDA_WIDE_WAVES 1024
 #endif
 constexpr size_t kWideWaves = KDA_WIDE_WAVES;  // total slices from which whole-state workgroups are used
-// Below this many 32-column slices (B <= 3 at H = 32, dv = 128) decode runs
-// one-wave workgroups of 16 value columns: twice the waves per state, half
+// Below this many 32-column slices (B <= 3 at H = 32, dv = 128) decode and
+// commit run one-wave workgroups of 16 value columns: twice the waves per state, half
 // the serial work per wave, the same arithmetic per column (measured 3.33 ->
 // 2.95 us per launch at B = 1, 3.71 -> 3.53 at B = 2; at B = 4 it was slower).
 #ifndef KDA_NARROW_WAVES
@@ -201,9 +201,9 @@ __global__ void KDA_OCCUPANCY __launch_bounds__((kWave * waves_per_group<DV, WPG
 }
 
 // RAW: the log holds raw projections and logits (decay sigmoid(gate_sign * x)).
-template <int DK, int DV, typename TIn, int WPG, bool RAW>
-__global__ void KDA_OCCUPANCY __launch_bounds__((kWave * waves_per_group<DV, WPG>())) commit_kernel(CommitArgs<TIn> a) {
-  typedef Place<DK, DV, WPG> P;
+template <int DK, int DV, typename TIn, int WPG, bool RAW, int NC = 4>
+__global__ void KDA_OCCUPANCY __launch_bounds__((kWave * waves_per_group<DV, WPG, NC>())) commit_kernel(CommitArgs<TIn> a) {
+  typedef Place<DK, DV, WPG, NC> P;
   constexpr int R = P::R;
   const P p(a.H);
   int sb = p.b;  // index of the state and position this sequence uses
@@ -221,7 +221,7 @@ __global__ void KDA_OCCUPANCY __launch_bounds__((kWave * waves_per_group<DV, WPG
   }
   if (n == 0) return;
   float* sp = a.state + ((size_t)sb * a.H + p.h) * DK * DV + p.tile_off();
-  float S[R][4];
+  float S[R][NC];
   load_tile<R, DV>(sp, S);
   replay_log<DK, DV, TIn, R, RAW>(S, a.log_k, a.log_v, a.log_alpha, a.log_beta, (size_t)p.b * a.Tmax * a.H + p.h,
                                   a.H, n, p.row0, p.col0, a.gate_sign);
@@ -370,8 +370,10 @@ hipError_t launch_commit(const kda_shape& s, int32_t T, float* state, int64_t* p
       constexpr bool RAW = decltype(raw)::value;
       if (slice_waves<DV>(s) >= kWideWaves)
         commit_kernel<DK, DV, TIn, 4, RAW><<<grid_of<DK, DV, 4>(s), kWave * waves_per_group<DV, 4>(), 0, st>>>(a);
-      else
+      else if (slice_waves<DV>(s) >= kNarrowWaves)
         commit_kernel<DK, DV, TIn, 1, RAW><<<grid_of<DK, DV, 1>(s), kWave, 0, st>>>(a);
+      else
+        commit_kernel<DK, DV, TIn, 1, RAW, 2><<<grid_of<DK, DV, 1, 2>(s), kWave, 0, st>>>(a);
     };
     if (form == kLogPrepared)
       go(std::false_type{});
