@@ -15,7 +15,12 @@ kernel's: algorithmic bytes per launch / measured average launch time.
 `cpu_baseline` times the fp64 oracle on a bounded sample of the headline
 workload on the host.
 
+Timing: every figure is the median of 5 samples of at least 200 ms each
+(HIP events on the launch stream); the headline's samples are whole blocks of
+the K steps asked for, and its first K-step block is reported beside them.
+
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--quick] [--no-cpu]
+                       [--rows decode,spec,slots,prefill] [--samples N] [--min-sample-ms M]
 """
 
 from __future__ import annotations
@@ -94,6 +99,29 @@ class Timer:
         self.ms = self.a.elapsed_time(self.b)
 
 
+MIN_SAMPLE_MS = 200.0   # each timed sample lasts at least this long
+N_SAMPLES = 5           # samples per figure; the median is reported
+
+
+def sampled(torch, run, unit, min_units=1):
+    """Median time per unit over N_SAMPLES samples of at least MIN_SAMPLE_MS.
+
+    run(n) enqueues n units of work back to back (no synchronisation); the
+    first call calibrates how many units one sample needs.  Returns
+    (median ms per unit, {"count", "units_per_sample", "unit", "ms_per_unit"}).
+    """
+    with Timer(torch) as tm:
+        run(min_units)
+    per = max(tm.ms / min_units, 1e-6)
+    n = max(min_units, int(np.ceil(MIN_SAMPLE_MS / per)))
+    ms = []
+    for _ in range(N_SAMPLES):
+        with Timer(torch) as tm:
+            run(n)
+        ms.append(tm.ms / n)
+    return float(np.median(ms)), {"count": N_SAMPLES, "units_per_sample": n, "unit": unit, "ms_per_unit": ms}
+
+
 def dev_tensor(torch, x, device):
     if x.dtype == np.uint16:
         return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).to(device).view(torch.bfloat16)
@@ -165,18 +193,24 @@ def bench_decode(torch, kda, synth, B, layers, steps, warmup, device, use_graph=
                 for p in plans[s % N_TOKENS_IN]:
                     p()
     run(warmup)
+    # The first timed block is exactly `steps` steps; the reported figure is
+    # the median of the samples, each a whole number of `steps`-step blocks.
     with Timer(torch) as tm:
         run(steps)
-    launches = steps * layers
-    launch_us = tm.ms * 1e3 / launches
+    first_ms = tm.ms / steps
+    step_ms, samples = sampled(torch, lambda n: [run(steps) for _ in range(n)], f"{steps} steps")
+    step_ms /= steps
+    samples["ms_per_step"] = [x / steps for x in samples.pop("ms_per_unit")]
+    launch_us = step_ms * 1e3 / layers
     bytes_per_launch = DECODE_BYTES * B * H
     return {
         "B": B, "layers": layers, "steps": steps, "graph": use_graph,
-        "steps_per_graph": STEPS_PER_GRAPH if use_graph else None, "ms_per_step": tm.ms / steps,
-        "launch_us": launch_us, "updates_per_s": B * H * launches / (tm.ms / 1e3),
+        "steps_per_graph": STEPS_PER_GRAPH if use_graph else None, "ms_per_step": step_ms,
+        "first_block_ms_per_step": first_ms,
+        "launch_us": launch_us, "updates_per_s": B * H * layers / (step_ms / 1e3),
         "achieved_GBs": bytes_per_launch / (launch_us * 1e-6) / 1e9,
         "hbm_frac": bytes_per_launch / (launch_us * 1e-6) / 1e9 / HBM_PEAK_GBS,
-        "state_bytes_total": layers * B * H * STATE_BYTES,
+        "state_bytes_total": layers * B * H * STATE_BYTES, "samples": samples,
     }
 
 
@@ -199,16 +233,18 @@ def bench_decode_slots(torch, kda, synth, B, layers, steps, warmup, device):
               for t in range(N_TOKENS_IN)]
     for s in range(warmup):
         graphs[s % N_TOKENS_IN].replay()
-    with Timer(torch) as tm:
-        for s in range(steps):
+
+    def run(n):
+        for s in range(n):
             graphs[s % N_TOKENS_IN].replay()
-    launches = steps * layers
-    launch_us = tm.ms * 1e3 / launches
+
+    step_ms, samples = sampled(torch, run, "step", steps)
+    launch_us = step_ms * 1e3 / layers
     bytes_per_launch = DECODE_BYTES * B * H
     assert err.item() == 0
-    return {"B": B, "layers": layers, "steps": steps, "launch_us": launch_us,
-            "updates_per_s": B * H * launches / (tm.ms / 1e3),
-            "hbm_frac": bytes_per_launch / (launch_us * 1e-6) / 1e9 / HBM_PEAK_GBS}
+    return {"B": B, "layers": layers, "launch_us": launch_us,
+            "updates_per_s": B * H * layers / (step_ms / 1e3),
+            "hbm_frac": bytes_per_launch / (launch_us * 1e-6) / 1e9 / HBM_PEAK_GBS, "samples": samples}
 
 
 def bench_verify_commit(torch, kda, synth, B, T, rounds, layers, device):
@@ -238,18 +274,35 @@ def bench_verify_commit(torch, kda, synth, B, T, rounds, layers, device):
     for r in range(rounds):          # warm-up pass
         vg[r].replay()
         cg[r].replay()
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * rounds + 1)]
+
+    def one_pass():
+        """All rounds once, with events between the verify and commit replays."""
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * rounds + 1)]
+        ev[0].record()
+        for r in range(rounds):
+            vg[r].replay()
+            ev[2 * r + 1].record()
+            cg[r].replay()
+            ev[2 * r + 2].record()
+        return ev
+
     torch.cuda.synchronize()
-    ev[0].record()
-    for r in range(rounds):
-        vg[r].replay()
-        ev[2 * r + 1].record()
-        cg[r].replay()
-        ev[2 * r + 2].record()
+    t0 = time.perf_counter()
+    one_pass()
     torch.cuda.synchronize()
-    ver_ms = sum(ev[2 * r].elapsed_time(ev[2 * r + 1]) for r in range(rounds))
-    com_ms = sum(ev[2 * r + 1].elapsed_time(ev[2 * r + 2]) for r in range(rounds))
-    tot_ms = ev[0].elapsed_time(ev[-1])
+    passes = max(1, int(np.ceil(MIN_SAMPLE_MS / 1e3 / (time.perf_counter() - t0))))
+    per_sample = []
+    for _ in range(N_SAMPLES):
+        evs = [one_pass() for _ in range(passes)]
+        torch.cuda.synchronize()
+        v = sum(ev[2 * r].elapsed_time(ev[2 * r + 1]) for ev in evs for r in range(rounds))
+        c = sum(ev[2 * r + 1].elapsed_time(ev[2 * r + 2]) for ev in evs for r in range(rounds))
+        t = sum(ev[0].elapsed_time(ev[-1]) for ev in evs)
+        per_sample.append((v / passes, c / passes, t / passes))
+    med = lambda i: float(np.median([x[i] for x in per_sample]))  # noqa: E731
+    ver_ms, com_ms, tot_ms = med(0), med(1), med(2)
+    samples = {"count": N_SAMPLES, "units_per_sample": passes, "unit": f"{rounds} rounds",
+               "ms_per_unit": [x[2] for x in per_sample]}
     n_launch = rounds * layers
     ver_bytes = B * H * (STATE_BYTES + T * (TOKEN_IN_BYTES + 128 * 4 + LOG_BYTES))
     com_bytes = float((int((acc_np > 0).sum()) * 2 * STATE_BYTES + int(acc_np.sum()) * LOG_BYTES) * H) * layers
@@ -262,6 +315,7 @@ def bench_verify_commit(torch, kda, synth, B, T, rounds, layers, device):
         "round_hbm_frac": (ver_bytes * n_launch + com_bytes) / (tot_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
         "verified_token_heads_per_s": B * H * n_launch * T / (tot_ms / 1e3),
         "committed_token_heads_per_s": float(acc_np.sum()) * H * layers / (tot_ms / 1e3),
+        "samples": samples,
     }
 
 
@@ -297,19 +351,23 @@ def bench_spec_fused(torch, kda, synth, B, T, rounds, layers, device, fixed_acce
                                       for S, lg in zip(states, logs)]))
     for g in graphs:
         g.replay()
-    with Timer(torch) as tm:
-        for g in graphs:
-            g.replay()
+
+    def run(n):
+        for _ in range(n):
+            for g in graphs:
+                g.replay()
+
+    pass_ms, samples = sampled(torch, run, f"{rounds} rounds")
     n_launch = rounds * layers
-    us = tm.ms * 1e3 / n_launch
+    us = pass_ms * 1e3 / n_launch
     a = acc_np[:rounds]
     per_bh = (STATE_BYTES + T * (TOKEN_IN_BYTES + 128 * 4 + LOG_BYTES)) * a.size
     per_bh += int((a > 0).sum()) * STATE_BYTES + int(a.sum()) * LOG_BYTES
     bytes_total = float(per_bh) * H * layers
     return {"B": B, "T": T, "rounds": rounds, "layers": layers, "mean_accepted": float(a.mean()),
-            "round_us": us, "hbm_frac": bytes_total / (tm.ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "round_us": us, "hbm_frac": bytes_total / (pass_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
             "verified_token_heads_per_s": B * H * T / (us * 1e-6),
-            "committed_token_heads_per_s": float(a.sum()) * H * layers / (tm.ms * 1e-3)}
+            "committed_token_heads_per_s": float(a.sum()) * H * layers / (pass_ms * 1e-3), "samples": samples}
 
 
 def bench_verify_only(torch, kda, synth, B, T, layers, reps, device):
@@ -327,18 +385,20 @@ def bench_verify_only(torch, kda, synth, B, T, layers, reps, device):
                         for S, lg in zip(states, logs)])
     for _ in range(3):
         g.replay()
-    with Timer(torch) as tm:
-        for _ in range(reps):
+
+    def run(n):
+        for _ in range(n):
             g.replay()
-    launches = reps * layers
-    us = tm.ms * 1e3 / launches
+
+    rep_ms, samples = sampled(torch, run, f"{layers} launches", reps)
+    us = rep_ms * 1e3 / layers
     ver_bytes = B * H * (STATE_BYTES + T * (TOKEN_IN_BYTES + 128 * 4 + LOG_BYTES))
     return {"B": B, "T": T, "layers": layers, "launch_us": us,
             "verified_token_heads_per_s": B * H * T / (us * 1e-6),
-            "hbm_frac": ver_bytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS}
+            "hbm_frac": ver_bytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, "samples": samples}
 
 
-def bench_prefill(torch, kda, synth, device, variant, reps=2):
+def bench_prefill(torch, kda, synth, device, variant):
     spec = synth.CONFIGS["prefill"]
     B, L = spec.B[0], spec.steps
     every = spec.extra["ckpt_every"]
@@ -364,21 +424,17 @@ def bench_prefill(torch, kda, synth, device, variant, reps=2):
     if variant != "recurrent":
         kw["chunk"] = spec.extra["chunk"]
 
-    def run():
-        S.copy_(S0)
-        fn(S, pos, d["q"], d["k"], d["v"], d["alpha"], d["beta"], o, **kw)
-
-    run()
-    best = None
-    for _ in range(reps):
-        S.copy_(S0)
-        with Timer(torch) as tm:
+    def run(n):  # back-to-back prompts continue from the state the last one left
+        for _ in range(n):
             fn(S, pos, d["q"], d["k"], d["v"], d["alpha"], d["beta"], o, **kw)
-        best = tm.ms if best is None else min(best, tm.ms)
+
+    run(1)
+    best, samples = sampled(torch, run, "prompt")
     th = B * L * H
     total_bytes = th * PREFILL_BYTES_PER_TOKEN_HEAD + B * H * STATE_BYTES * (2 + n_ck)
     row = {"variant": variant, "B": B, "L": L, "ms": best, "token_heads_per_s": th / (best / 1e3),
-           "hbm_frac": total_bytes / (best * 1e-3) / 1e9 / HBM_PEAK_GBS, "algorithmic_bytes": total_bytes}
+           "hbm_frac": total_bytes / (best * 1e-3) / 1e9 / HBM_PEAK_GBS, "algorithmic_bytes": total_bytes,
+           "samples": samples}
     if variant == "chunked":
         C = spec.extra["chunk"]
         chunks = B * H * (L // C)
@@ -418,16 +474,15 @@ def bench_snapshot_restore(torch, kda, synth, device, reps=20):
     pool = kda.SlotPool(n_slots, H, DK, DV, device)
     ids = list(range(B))
     kda.snapshot(S, pos, ids, ids, pool)
-    with Timer(torch) as ts:
-        for _ in range(reps):
-            kda.snapshot(S, pos, ids, ids, pool)
-    with Timer(torch) as tr:
-        for _ in range(reps):
-            kda.restore(S, pos, ids, ids, pool)
+    snap_ms, s_samples = sampled(torch, lambda n: [kda.snapshot(S, pos, ids, ids, pool) for _ in range(n)],
+                                 "snapshot", reps)
+    rest_ms, r_samples = sampled(torch, lambda n: [kda.restore(S, pos, ids, ids, pool) for _ in range(n)],
+                                 "restore", reps)
     nbytes = 2 * B * H * STATE_BYTES
-    return {"pairs": B, "snapshot_us": ts.ms * 1e3 / reps, "restore_us": tr.ms * 1e3 / reps,
-            "snapshot_hbm_frac": nbytes / (ts.ms * 1e-3 / reps) / 1e9 / HBM_PEAK_GBS,
-            "restore_hbm_frac": nbytes / (tr.ms * 1e-3 / reps) / 1e9 / HBM_PEAK_GBS}
+    return {"pairs": B, "snapshot_us": snap_ms * 1e3, "restore_us": rest_ms * 1e3,
+            "snapshot_hbm_frac": nbytes / (snap_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "restore_hbm_frac": nbytes / (rest_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "samples": {"snapshot": s_samples, "restore": r_samples}}
 
 
 def bench_resume(torch, kda, synth, device, steps=128):
@@ -449,14 +504,21 @@ def bench_resume(torch, kda, synth, device, steps=128):
     kda.restore(S, pos, seqs, slots, pool)
     for s in range(8):
         graphs[s % N_TOKENS_IN].replay()
-    with Timer(torch) as tr:
-        kda.restore(S, pos, seqs, slots, pool)
-    with Timer(torch) as td:
-        for s in range(steps):
-            graphs[s % N_TOKENS_IN].replay()
-    return {"B": B, "restore_us": tr.ms * 1e3, "decode_steps": steps, "decode_us_per_step": td.ms * 1e3 / steps,
-            "total_us": (tr.ms + td.ms) * 1e3,
-            "decode_hbm_frac": DECODE_BYTES * B * H / (td.ms * 1e-3 / steps) / 1e9 / HBM_PEAK_GBS}
+    rest_ms, r_samples = sampled(torch, lambda n: [kda.restore(S, pos, seqs, slots, pool) for _ in range(n)],
+                                 "restore of the 8 checkpoints")
+
+    def resume(n):  # n whole resumes: restore, then the decode steps
+        for _ in range(n):
+            kda.restore(S, pos, seqs, slots, pool)
+            for s in range(steps):
+                graphs[s % N_TOKENS_IN].replay()
+
+    tot_ms, samples = sampled(torch, resume, f"restore + {steps} decode steps")
+    dec_ms = (tot_ms - rest_ms) / steps
+    return {"B": B, "restore_us": rest_ms * 1e3, "decode_steps": steps, "decode_us_per_step": dec_ms * 1e3,
+            "total_us": tot_ms * 1e3,
+            "decode_hbm_frac": DECODE_BYTES * B * H / (dec_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "samples": {"restore": r_samples, "resume": samples}}
 
 
 def bench_copy(torch, device, reps=20):
@@ -464,39 +526,85 @@ def bench_copy(torch, device, reps=20):
     a = torch.empty(n, dtype=torch.float32, device=device).fill_(1.0)
     b = torch.empty_like(a)
     b.copy_(a)
-    with Timer(torch) as tm:
-        for _ in range(reps):
-            b.copy_(a)
-    return {"bytes_per_copy": 2 * 4 * n, "GBs": 2 * 4 * n * reps / (tm.ms * 1e-3) / 1e9}
+    ms, samples = sampled(torch, lambda k: [b.copy_(a) for _ in range(k)], "1 GiB copy", reps)
+    return {"bytes_per_copy": 2 * 4 * n, "GBs": 2 * 4 * n / (ms * 1e-3) / 1e9, "samples": samples}
 
 
-def cpu_baseline(synth, budget_s=12.0):
-    """The fp64 oracle (as it stands) on a bounded sample of the headline
-    workload: B = 64, H = 32 decode steps, on one host core."""
+_CPU = {}  # inputs shared with the forked oracle workers
+
+
+def _cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _oracle_worker(args):
+    """Decode steps of the fp64 oracle on sequences [b0, b1), one thread, until `budget_s` passes."""
+    b0, b1, budget_s = args
     from threadpoolctl import threadpool_limits
 
     from oracle import kda_oracle as ko
-    spec = synth.CONFIGS["batched_decode"]
-    B = B_HEAD
-    S0 = synth.initial_state(spec, B)
-    inp = synth.token_inputs(spec, B, N_TOKENS_IN)
-    S = ko.widen(S0)
+    inp, S = _CPU["inp"], ko.widen(_CPU["S0"][b0:b1])
     done = 0
     with threadpool_limits(limits=1):
         t0 = time.perf_counter()
         while True:
             t = done % N_TOKENS_IN
-            tok = [ko.widen(inp[n][:, t]) for n in ("q", "k", "v", "alpha", "beta")]
+            tok = [ko.widen(inp[n][b0:b1, t]) for n in ("q", "k", "v", "alpha", "beta")]
             S, _ = ko.step(S, *tok, SCALE)
             done += 1
             el = time.perf_counter() - t0
             if el >= budget_s:
                 break
-    return {"value": done * B * H / el, "unit": "state-updates/s", "cores": 1, "kind": "oracle",
-            "sample": f"{done} decode steps of B=64 x H=32 (dk=dv=128) in fp64, one core, {el:.1f} s"}
+    return done * (b1 - b0) * H, el
+
+
+def cpu_baseline(synth, budget_s=8.0):
+    """The fp64 oracle (as it stands) on bounded samples of the headline
+    workload, B = 64, H = 32 decode steps: split over the host's cores by
+    sequence (one single-threaded worker process per core, each stepping its
+    own sequences for `budget_s`), and on one core over all 64 sequences.
+    Runs before the GPU is initialised, so the workers fork from a process
+    that has not touched it."""
+    import multiprocessing as mp
+
+    spec = synth.CONFIGS["batched_decode"]
+    _CPU["S0"] = synth.initial_state(spec, B_HEAD)
+    _CPU["inp"] = synth.token_inputs(spec, B_HEAD, N_TOKENS_IN)
+    cores = max(1, min(len(os.sched_getaffinity(0)), 16, B_HEAD))
+    one, el1 = _oracle_worker((0, B_HEAD, budget_s))
+    per = B_HEAD // cores
+    parts = [(i * per, B_HEAD if i == cores - 1 else (i + 1) * per, budget_s) for i in range(cores)]
+    env = {k: os.environ.get(k) for k in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS")}
+    for k in env:
+        os.environ[k] = "1"
+    try:
+        with mp.get_context("fork").Pool(cores) as pool:
+            res = pool.map(_oracle_worker, parts)
+    finally:
+        for k, v in env.items():
+            if v is None:
+                os.environ.pop(k, None)
+            else:
+                os.environ[k] = v
+    updates = sum(u for u, _ in res)
+    wall = max(e for _, e in res)
+    return {"value": updates / wall, "unit": "state-updates/s", "cores": cores, "kind": "oracle",
+            "cpu_model": _cpu_model(), "one_core": {"value": one / el1, "unit": "state-updates/s", "seconds": el1},
+            "sample": f"fp64 oracle decode steps of the B=64 x H=32 (dk=dv=128) headline workload: {cores} "
+                      f"single-threaded worker processes, one per core, each stepping {per} or more of the 64 "
+                      f"sequences for {budget_s:.0f} s ({updates} state-updates); plus one core over all 64 "
+                      f"sequences for {el1:.1f} s"}
 
 
 def main():
+    global N_SAMPLES, MIN_SAMPLE_MS
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
@@ -505,9 +613,14 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--with-copy-ref", action="store_true",
                     help="also run one 256 MiB device copy (known bytes) to scale profiler byte counters")
+    ap.add_argument("--samples", type=int, default=5,
+                    help="timed samples per figure, median reported (profiling runs: 1)")
+    ap.add_argument("--min-sample-ms", type=float, default=200.0,
+                    help="minimum length of one sample (profiling runs: 0)")
     ap.add_argument("--rows", default="all",
                     help="comma-separated row groups after the headline: decode, spec, slots, prefill (default all)")
     args = ap.parse_args()
+    N_SAMPLES, MIN_SAMPLE_MS = max(1, args.samples), max(0.0, args.min_sample_ms)
     groups = {"decode", "spec", "slots", "prefill"}
     picked = groups if args.rows == "all" else set(args.rows.split(","))
     if not picked <= groups:
@@ -517,10 +630,17 @@ def main():
               "(sequences and heads shard with no exchange); run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
+    import synth
+
+    # The oracle's CPU baseline runs first: its worker processes fork from
+    # this process, which must not have initialised the GPU yet.
+    cpu = None if args.no_cpu else cpu_baseline(synth)
+    if cpu is not None:
+        log(f"cpu baseline: {cpu['value']:.0f} state-updates/s on {cpu['cores']} cores")
+
     import torch
 
     import recurrent_state_amd as kda
-    import synth
 
     kda.lib()  # fails loudly if libkda.so is missing
     device = torch.device("cuda:0")
@@ -581,7 +701,6 @@ def main():
         for variant in ("chunked", "chunked_prep", "recurrent"):
             rows[f"prefill_{variant}"] = bench_prefill(torch, kda, synth, device, variant)
 
-    cpu = None if args.no_cpu else cpu_baseline(synth)
     bytes_per_launch = DECODE_BYTES * B_HEAD * H
     line = {
         "metric": "KDA state-updates/s (tokens*heads/s) and % HBM roofline, B=1..64, 1 GPU",
@@ -591,6 +710,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": head["ms_per_step"],
+        "samples": head["samples"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,

@@ -20,7 +20,7 @@
  *   state   f32 [B][H][dk][dv]        updated in place
  *   q, k    in_dtype [B][T][H][dk]    (T = 1 for a decode step)
  *   v       in_dtype [B][T][H][dv]
- *   alpha   f32 [B][T][H][dk]         gates in (0, 1]
+ *   alpha   f32 [B][T][H][dk]         gates in [0, 1] (0 forgets the channel)
  *   beta    f32 [B][T][H]
  *   o       f32 [B][T][H][dv]         must not alias any input
  *   pos     i64 [B]                   token position of each sequence
@@ -376,6 +376,13 @@ kda_status kda_restore(const kda_shape* shape, float* state, int64_t* pos, const
  * pos[b] + (m + 1) * ckpt_every.  ckpt_slots is a DEVICE int32 array; an id
  * outside [0, slots->n_slots) sets KDA_DEV_ERR_CKPT_SLOT and that checkpoint
  * is skipped.  `dev_err` may be NULL only when ckpt_every == 0.
+ * Gates: every alpha in [0, 1] is handled exactly (up to rounding).  The
+ * chunk form divides by in-chunk decay products, so a chunk ends early, and
+ * the next one starts, where some key channel's product of alphas since the
+ * chunk's first token would fall below 2^-96; gates that decay that fast
+ * make the call slower (shorter chunks), never less accurate.
+ * L = 0 is a no-op: nothing is enqueued, the token pointers may be NULL, and
+ * state and pos are left as they are.
  * (Webinar summary: prompt processing that prefix caching avoids, and the
  * recurrent-state checkpoint at a token boundary.)
  */
@@ -389,7 +396,7 @@ kda_status kda_prefill_chunked(const kda_shape* shape, int32_t L, int32_t chunk,
  * The same prompt processing as kda_prefill_chunked, computed token by token
  * with the decode update while each (sequence, head) state stays in
  * registers for the whole prompt.  Arguments as for kda_prefill_chunked
- * without `chunk`; any ckpt_every > 0 is allowed.  It is the cross-check for
+ * without `chunk`; any ckpt_every > 0 is allowed (L = 0 is a no-op).  It is the cross-check for
  * the chunked form and the cheaper choice for very short prompts.
  */
 kda_status kda_prefill_recurrent(const kda_shape* shape, int32_t L, float* state, int64_t* pos,

@@ -9,6 +9,7 @@ from __future__ import annotations
 import os
 import subprocess
 import sys
+from concurrent.futures import ThreadPoolExecutor
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
@@ -40,11 +41,7 @@ def hipcc() -> str:
     return "hipcc"
 
 
-def build(verbose: bool = False, extra_flags=(), out: str = LIB) -> str:
-    """Compile every HIP/C++ source into libkda.so (or `out`); returns its path."""
-    tmp = out + ".tmp"
-    cmd = [hipcc(), *HIPCC_FLAGS, *extra_flags, "-I", os.path.join(ROOT, "include"), "-I", CSRC,
-           *[os.path.join(CSRC, s) for s in SOURCES], "-o", tmp]
+def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -52,6 +49,26 @@ def build(verbose: bool = False, extra_flags=(), out: str = LIB) -> str:
         raise RuntimeError(f"hipcc failed ({res.returncode}):\n{res.stderr[-8000:]}")
     if verbose and res.stderr.strip():
         print(res.stderr[-4000:], file=sys.stderr)
+
+
+def build(verbose: bool = False, extra_flags=(), out: str = LIB, jobs: int = 0) -> str:
+    """Compile every HIP/C++ source into libkda.so (or `out`); returns its path.
+
+    Each source is compiled to its own object (in parallel), then the objects
+    are linked; every object carries its own gfx950 code, so no device-side
+    linking is involved.
+    """
+    objdir = os.path.join(os.path.dirname(out), "_build")
+    os.makedirs(objdir, exist_ok=True)
+    flags = [f for f in HIPCC_FLAGS if f != "-shared"]
+    objs = [os.path.join(objdir, s + ".o") for s in SOURCES]
+    cmds = [[hipcc(), *flags, *extra_flags, "-I", os.path.join(ROOT, "include"), "-I", CSRC, "-c",
+             os.path.join(CSRC, s), "-o", o] for s, o in zip(SOURCES, objs)]
+    n = jobs or min(len(cmds), os.cpu_count() or 1, 16)
+    with ThreadPoolExecutor(max_workers=n) as ex:
+        list(ex.map(lambda c: _run(c, verbose), cmds))
+    tmp = out + ".tmp"
+    _run([hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp], verbose)
     os.replace(tmp, out)
     return out
 

@@ -459,7 +459,8 @@ kda_status prefill_chunked_impl(const kda_shape* shape, int32_t L, int32_t chunk
                                 int32_t* dev_err, int32_t gate, void* stream, const int32_t* state_slots = nullptr) {
   kda_status r = check_prefill(shape, L, chunk, state, pos, q, k, v, alpha, beta, o, ckpt_every, ckpt_slots, slots,
                                dev_err);
-  if (r != KDA_OK || shape->B == 0) return r;
+  // An empty prompt leaves every state and position as it is: nothing to launch.
+  if (r != KDA_OK || shape->B == 0 || L == 0) return r;
   const bool ck = ckpt_every > 0 && L >= ckpt_every;
   if (state_slots) {  // the caller passed the pool's arrays as state and pos
     if ((r = check_slot_ids(state_slots, dev_err)) != KDA_OK) return r;
@@ -486,6 +487,7 @@ kda_status prefill_recurrent_impl(const kda_shape* shape, int32_t L, float* stat
   kda_status r = check_prefill(shape, L, 32, state, pos, q, k, v, alpha, beta, o, 0, nullptr, nullptr, dev_err);
   if (r != KDA_OK || shape->B == 0) return r;
   if (ckpt_every < 0) return KDA_ERR_SHAPE;
+  if (L == 0) return KDA_OK;  // an empty prompt: nothing to launch
   const bool ck = ckpt_every > 0 && L >= ckpt_every;
   if (ck) {
     if (!ckpt_slots || !dev_err) return KDA_ERR_NULL;

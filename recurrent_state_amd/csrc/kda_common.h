@@ -376,74 +376,73 @@ __device__ __forceinline__ void token_update_prep(float (&S)[R][NC], const Raw<T
 // Cache-policy bits of a buffer instruction for state traffic (2 = nt).
 constexpr int kStateLoadAux = (KDA_STATE_NT & 2) ? 2 : 0;
 constexpr int kStateStoreAux = (KDA_STATE_NT & 1) ? 2 : 0;
-typedef float f32x4 __attribute__((ext_vector_type(4)));
+// Buffer-resource access: one SGPR base + range per tensor window, a 32-bit
+// lane offset in a VGPR and uniform offsets in SGPRs (or the instruction's
+// immediate), so no 64-bit address is kept per lane.  The hardware range
+// check covers the lane offset plus the immediate, not the SGPR offset, so
+// callers keep every access inside its window.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+constexpr int kRsrcWord3 = 0x00020000;  // raw 32-bit data format
 
-__device__ __forceinline__ float4 state_load4(const float* p) {
-#if KDA_STATE_NT & 2
-  const f32x4 x = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p));
-  return make_float4(x.x, x.y, x.z, x.w);
-#else
-  return *reinterpret_cast<const float4*>(p);
-#endif
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kRsrcWord3);
 }
 
-__device__ __forceinline__ void state_store4(float* p, float a, float b, float c, float d) {
-#if KDA_STATE_NT & 1
-  const f32x4 x = {a, b, c, d};
-  __builtin_nontemporal_store(x, reinterpret_cast<f32x4*>(p));
-#else
-  *reinterpret_cast<float4*>(p) = make_float4(a, b, c, d);
-#endif
+// NC fp32 values as one 16- or 8-byte buffer store (AUX: cache-policy bits).
+// The uniform offset `so` is folded into the lane offset and the SGPR offset
+// operand left zero: the compiler tracks the hazard of a VALU write to the
+// data registers of a wide store (more than 32 bits here, to be safe) only
+// when the store has no SGPR offset, and on gfx950 the hazard is real (such
+// stores were seen writing the register's next value).  Every buffer store
+// wider than 32 bits in this library is written this way.
+template <int NC, int AUX>
+__device__ __forceinline__ void store_cols(const float (&x)[NC], rsrc_t r, int vo, int so) {
+  if constexpr (NC == 4) {
+    const u32x4 w = {__float_as_uint(x[0]), __float_as_uint(x[1]), __float_as_uint(x[2]), __float_as_uint(x[3])};
+    __builtin_amdgcn_raw_buffer_store_b128(w, r, vo + so, 0, AUX);
+  } else {
+    const u32x2 w = {__float_as_uint(x[0]), __float_as_uint(x[1])};
+    __builtin_amdgcn_raw_buffer_store_b64(w, r, vo + so, 0, AUX);
+  }
 }
-
-__device__ __forceinline__ float2 state_load2(const float* p) {
-#if KDA_STATE_NT & 2
-  typedef float f32x2 __attribute__((ext_vector_type(2)));
-  const f32x2 x = __builtin_nontemporal_load(reinterpret_cast<const f32x2*>(p));
-  return make_float2(x.x, x.y);
-#else
-  return *reinterpret_cast<const float2*>(p);
-#endif
-}
-
-__device__ __forceinline__ void state_store2(float* p, float a, float b) {
-#if KDA_STATE_NT & 1
-  typedef float f32x2 __attribute__((ext_vector_type(2)));
-  const f32x2 x = {a, b};
-  __builtin_nontemporal_store(x, reinterpret_cast<f32x2*>(p));
-#else
-  *reinterpret_cast<float2*>(p) = make_float2(a, b);
-#endif
-}
-
-// A lane's R x NC state tile (rows DV floats apart), NC = 4 or 2 columns.
-template <int R, int DV, int NC>
-__device__ __forceinline__ void load_tile(const float* p, float (&S)[R][NC]) {
-#pragma unroll
-  for (int r = 0; r < R; ++r) {
-    if constexpr (NC == 4) {
-      const float4 x = state_load4(p + (size_t)r * DV);
-      S[r][0] = x.x;
-      S[r][1] = x.y;
-      S[r][2] = x.z;
-      S[r][3] = x.w;
-    } else {
-      const float2 x = state_load2(p + (size_t)r * DV);
-      S[r][0] = x.x;
-      S[r][1] = x.y;
-    }
+// NC fp32 values from one 16- or 8-byte buffer load (AUX: cache-policy bits).
+template <int NC, int AUX>
+__device__ __forceinline__ void load_cols(float (&x)[NC], rsrc_t r, int vo, int so) {
+  if constexpr (NC == 4) {
+    const u32x4 w = __builtin_amdgcn_raw_buffer_load_b128(r, vo, so, AUX);
+    x[0] = __uint_as_float(w.x);
+    x[1] = __uint_as_float(w.y);
+    x[2] = __uint_as_float(w.z);
+    x[3] = __uint_as_float(w.w);
+  } else {
+    const u32x2 w = __builtin_amdgcn_raw_buffer_load_b64(r, vo, so, AUX);
+    x[0] = __uint_as_float(w.x);
+    x[1] = __uint_as_float(w.y);
   }
 }
 
+// Window over one (sequence, head) state [dk][dv].
+template <int DK, int DV>
+__device__ __forceinline__ rsrc_t state_rsrc(const float* state_bh) {
+  return make_rsrc(state_bh, (uint32_t)(DK * DV * 4));
+}
+
+// A lane's R x NC state tile (rows DV floats apart, NC = 4 or 2 columns) in
+// the state window rs, starting at byte offset vo: R buffer accesses that
+// share one offset register (the rows are uniform offsets), with the
+// non-temporal hint of the state traffic.
 template <int R, int DV, int NC>
-__device__ __forceinline__ void store_tile(float* p, const float (&S)[R][NC]) {
+__device__ __forceinline__ void load_tile(rsrc_t rs, int vo, float (&S)[R][NC]) {
 #pragma unroll
-  for (int r = 0; r < R; ++r) {
-    if constexpr (NC == 4)
-      state_store4(p + (size_t)r * DV, S[r][0], S[r][1], S[r][2], S[r][3]);
-    else
-      state_store2(p + (size_t)r * DV, S[r][0], S[r][1]);
-  }
+  for (int r = 0; r < R; ++r) load_cols<NC, kStateLoadAux>(S[r], rs, vo, r * DV * 4);
+}
+
+template <int R, int DV, int NC>
+__device__ __forceinline__ void store_tile(rsrc_t rs, int vo, const float (&S)[R][NC]) {
+#pragma unroll
+  for (int r = 0; r < R; ++r) store_cols<NC, kStateStoreAux>(S[r], rs, vo, r * DV * 4);
 }
 
 // The per-token inputs one lane needs, as stored (raw) and widened.

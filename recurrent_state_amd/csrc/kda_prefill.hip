@@ -5,14 +5,24 @@
 // rounding), chunk by chunk.  For a chunk of n <= CH tokens starting from
 // state S (rows = key channels, columns = value channels):
 //
-//   G_r  = prod_{s <= r} alpha_s                    per key channel (cumulative decay)
-//   Kt   = k * G,  Qt = q * G,  Kh = k / G,  Kb = k * G_n / G
+//   S~   = Diag(alpha_0) S                          first token's decay, applied up front
+//   G_r  = prod_{1 <= s <= r} alpha_s               per key channel (G_0 = 1)
+//   Kt   = k * G,  Qt = q * G,  Kh = k / G,  Kb = k * G_{n-1} / G
 //   A    = strictly-lower(Diag(beta) Kt Kh^T)       (CH x CH)
 //   P    = lower-with-diagonal(Qt Kh^T)             (CH x CH)
 //   T    = (I + A)^-1 Diag(beta)
-//   E    = T (V - Kt S)                             (CH x dv)
-//   O    = scale (Qt S + P E)
-//   S'   = Diag(G_n) S + Kb^T E
+//   E    = T (V - Kt S~)                            (CH x dv)
+//   O    = scale (Qt S~ + P E)
+//   S'   = Diag(G_{n-1}) S~ + Kb^T E
+//
+// Kt Kh^T only ever forms the ratios G_r / G_i = prod_{i < s <= r} alpha_s
+// (<= 1), but Kh itself grows as 1 / G.  Leaving the first token's decay out
+// of G (it goes into S~) keeps a one-token chunk free of any division, and a
+// chunk is cut short where some channel's G would drop below kMinDecay
+// (2^-96): the chunk ends before that token and the next chunk starts there.
+// So every factor stays within fp32 range and every gate in [0, 1] is
+// handled exactly; gates that decay by less than 2^96 over a full chunk, in
+// every channel, never shorten a chunk.
 //
 // One workgroup owns one (sequence, head) for the whole prompt and walks
 // its chunks in order; wave w of the workgroup (dv / 16 waves) owns value
@@ -114,18 +124,12 @@ __device__ __forceinline__ Op plane_op2(const bf16_t* hi, const bf16_t* lo, int 
   return Op{plane_op(hi, row, rs, c0), plane_op(lo, row, rs, c0)};
 }
 
-// Buffer resources: the base address and byte range of a window live in
-// SGPRs, each lane supplies one VGPR offset, and per-access constants go in
-// the SGPR offset operand, so a 64-element register tile spread over many
-// rows costs one address VGPR.  The hardware range check covers only the
-// VGPR (+ instruction) offset, not the SGPR offset, so every access below is
-// kept inside its window by explicit guards; the window size is a backstop.
-typedef __amdgpu_buffer_rsrc_t rsrc_t;
-constexpr int kRsrcWord3 = 0x00020000;  // raw 32-bit data format
-
-__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kRsrcWord3);
-}
+// Global accesses go through buffer resources (make_rsrc): each lane
+// supplies one VGPR offset and per-access constants go in the SGPR offset
+// operand, so a 64-element register tile spread over many rows costs one
+// address VGPR.  The hardware range check does not cover the SGPR offset, so
+// every access below is kept inside its window by explicit guards; the window
+// size is a backstop.
 __device__ __forceinline__ float ld_f32(rsrc_t r, int voff, int soff) {
   return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0));
 }
@@ -222,9 +226,10 @@ struct Smem {
   static constexpr int r2_b = 2 * CC_PLANE * 2 + DIAG * 4;
   static constexpr int off_r3 = off_r2 + (r2_a > r2_b ? r2_a : r2_b);
   static constexpr int total = off_r3 + 2 * CC_PLANE * 2;
-  // beta (CH floats) and G_n (DK floats) live in the 16 unused bytes at
-  // the end of each row of the Kb^T hi plane (4 floats per row).
-  static_assert(CH + DK <= 4 * DK && (RS_C - CH) * 2 == 16, "beta and G_n must fit the Kb row padding");
+  // beta (CH floats), G_{n-1} and alpha_0 (DK floats each) and one int per
+  // wave live in the 16 unused bytes at the end of each row of the Kb^T hi
+  // plane (4 floats per row).
+  static_assert(CH + 2 * DK + NW <= 4 * DK && (RS_C - CH) * 2 == 16, "misc values must fit the Kb row padding");
   // Token-group decay products, only live between the two passes
   // of the preparation: they borrow the M region, which is written later.
   static constexpr int off_tot = off_r3;
@@ -246,6 +251,11 @@ __device__ __forceinline__ void tri_tile(int ii, int& mt, int& nt) {
 // preparation phase normalises q and k (one full-wave sum per token: a wave
 // holds every key channel of its tokens) and applies the gates, and the rest
 // of the chunk is the prepared kernel's.
+// Smallest in-chunk decay product G a chunk may hold in any key channel:
+// 1 / G then stays below 2^96, far inside the fp32 (and bf16) range, and the
+// hi/lo split of k G keeps its precision for all but negligible components.
+constexpr float kMinDecay = 0x1p-96f;
+
 template <int DK, int DV, int CH, typename TIn, bool PREP>
 __global__ void __launch_bounds__(DV * 4) prefill_chunked_kernel(PrefillArgs<TIn> a) {
   constexpr int NW = DV / 16;        // waves; wave w owns value columns [16 w, 16 w + 16)
@@ -308,8 +318,15 @@ __global__ void __launch_bounds__(DV * 4) prefill_chunked_kernel(PrefillArgs<TIn
 #pragma unroll
     for (int r = 0; r < 4; ++r) st[mt][r] = ld_f32(rs_state, tile_voff, (16 * mt + r) * DV * 4);
 
-  const int n_chunks = (a.L + CH - 1) / CH;
   const int rowk = a.H * DK, rowv = a.H * DV;  // elements between consecutive tokens
+  // Nominal length of the chunk starting at token t: CH tokens, fewer at the
+  // end of the prompt, and never past the next checkpoint boundary.
+  const int ck_end = n_ckpt * a.ckpt_every;  // last checkpointed token position
+  auto nominal = [&](int t) {
+    int m = min(CH, a.L - t);
+    if (t < ck_end) m = min(m, (t / a.ckpt_every + 1) * a.ckpt_every - t);
+    return m;
+  };
 
   // Every global input load of a chunk (alpha, k, q, beta and this wave's
   // value tile) is issued one chunk ahead, before the previous chunk's value
@@ -321,8 +338,7 @@ __global__ void __launch_bounds__(DV * 4) prefill_chunked_kernel(PrefillArgs<TIn
   Pair2<TIn> rk[TPG], rq[TPG];
   float rb;  // beta of token tg TPG + (cp mod TPG): one load per lane instead of TPG identical ones
   One<TIn> rv[NB][4];
-  auto issue_loads = [&](int cc, int tid_) {
-    const int t_b = cc * CH, nn = min(CH, a.L - t_b);
+  auto issue_loads = [&](int t_b, int nn, int tid_) {
     const size_t r0 = (tok0 + t_b) * a.H + h;
     const rsrc_t wk = make_rsrc(a.k + r0 * DK, ((nn - 1) * rowk + DK) * sizeof(TIn));
     const rsrc_t wq = make_rsrc(a.q + r0 * DK, ((nn - 1) * rowk + DK) * sizeof(TIn));
@@ -348,9 +364,10 @@ __global__ void __launch_bounds__(DV * 4) prefill_chunked_kernel(PrefillArgs<TIn
         rv[mt][r].load(wv, (rc * rowv + col_) * (int)sizeof(TIn));
       }
   };
-  issue_loads(0, threadIdx.x);
+  int n_next = a.L > 0 ? nominal(0) : 0;
+  if (a.L > 0) issue_loads(0, n_next, threadIdx.x);
 
-  for (int c = 0; c < n_chunks; ++c) {
+  for (int t_base = 0; t_base < a.L;) {
     // Lane coordinates are re-derived from an opaque copy of the thread id
     // in every chunk: otherwise the compiler hoists every LDS address of the
     // loop body out of the chunk loop and keeps them all live in registers.
@@ -359,8 +376,7 @@ __global__ void __launch_bounds__(DV * 4) prefill_chunked_kernel(PrefillArgs<TIn
     const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l16 = lane & 15, g = lane >> 4;
     const int col = 16 * wave + l16;  // this lane's value column in the accumulator layout
-    const int t_base = c * CH;
-    const int n = min(CH, a.L - t_base);  // valid tokens in this chunk; rows n.. are padding
+    int n = n_next;  // valid tokens in this chunk (cut short below if a decay is too strong); rows n.. are padding
     const size_t row0 = (tok0 + t_base) * a.H + h;  // [B][L][H] row index of the chunk's first token
     const rsrc_t rs_o = make_rsrc(a.o + row0 * DV, ((n - 1) * rowv + DV) * 4);
 
@@ -403,10 +419,13 @@ __global__ void __launch_bounds__(DV * 4) prefill_chunked_kernel(PrefillArgs<TIn
         q1[i] *= rq_;
       }
     }
-#pragma unroll
-    for (int mt = 0; mt < NB; ++mt)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) vv[mt][r] = 16 * mt + 4 * g + r < n ? rv[mt][r].get() : 0.f;
+    // Token 0's decay is applied to the state before the chunk's products
+    // (S~ = Diag(alpha_0) S), so it stays out of G.
+    if (tg == 0) {
+      misc(CH + DK + c0) = al0[0];
+      misc(CH + DK + c0 + 1) = al1[0];
+      al0[0] = al1[0] = 1.f;
+    }
     {
       // Pass A: per-channel running products of alpha within the token group
       // (the cumulative decay itself: one multiply per token instead of a
@@ -436,12 +455,51 @@ __global__ void __launch_bounds__(DV * 4) prefill_chunked_kernel(PrefillArgs<TIn
         gn0 *= t0;
         gn1 *= t1;
       }
-      if (tg == 0) {
+      // Every wave holds every key channel (CP lanes per token group), so each
+      // wave reaches the same verdict from the same group totals.  G is
+      // monotone in r, so the whole chunk is safe when G_{n-1} >= kMinDecay in
+      // every channel.
+      if (__any(gn0 < kMinDecay || gn1 < kMinDecay)) {
+        // Cut the chunk before the first token r whose G_r < kMinDecay in some
+        // channel (r >= 1: G_0 = 1).  Tokens from there on become padding and
+        // start the next chunk.
+        int f = n;
+#pragma unroll
+        for (int i = TPG - 1; i >= 0; --i) {
+          const int r = tg * TPG + i;
+          if (r < n && (off0 * g0[i] < kMinDecay || off1 * g1[i] < kMinDecay)) f = r;
+        }
+#pragma unroll
+        for (int m = 32; m >= 1; m >>= 1) f = min(f, __shfl_xor(f, m));
+        if (lane == 0) *reinterpret_cast<int*>(&misc(CH + 2 * DK + wave)) = f;
+        __syncthreads();
+#pragma unroll
+        for (int w = 0; w < NW; ++w) f = min(f, *reinterpret_cast<const int*>(&misc(CH + 2 * DK + w)));
+        n = f;
+        // The lanes holding token n - 1 publish G_{n-1} of their channels.
+#pragma unroll
+        for (int i = 0; i < TPG; ++i)
+          if (tg * TPG + i == n - 1) {
+            misc(CH + c0) = off0 * g0[i];
+            misc(CH + c0 + 1) = off1 * g1[i];
+          }
+        __syncthreads();
+        gn0 = misc(CH + c0);
+        gn1 = misc(CH + c0 + 1);
+#pragma unroll
+        for (int i = 0; i < TPG; ++i)
+          if (tg * TPG + i >= n) k0[i] = k1[i] = q0[i] = q1[i] = 0.f;
+        if (cp < TPG && tg * TPG + cp >= n) misc(tg * TPG + cp) = 0.f;
+      } else if (tg == 0) {
         misc(CH + c0) = gn0;
         misc(CH + c0 + 1) = gn1;
       }
+#pragma unroll
+      for (int mt = 0; mt < NB; ++mt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) vv[mt][r] = 16 * mt + 4 * g + r < n ? rv[mt][r].get() : 0.f;
       // Pass B: the decayed planes; Kb goes to transposed planes two tokens at a time.
-      // Kb = Kh gamma_n (no third factor per element).
+      // Kb = Kh G_{n-1} (no third factor per element).
       const float egn0 = gn0, egn1 = gn1;
       const int pc = kpos(c0);  // storage column of the channel pair (c0, c0 + 1)
       uint32_t kbh0 = 0, kbl0 = 0, kbh1 = 0, kbl1 = 0;
@@ -457,7 +515,8 @@ __global__ void __launch_bounds__(DV * 4) prefill_chunked_kernel(PrefillArgs<TIn
         split2(q0[i] * e0, q1[i] * e1, hi, lo);  // Qt
         *reinterpret_cast<uint32_t*>(kq_hi + (CH + tr) * L::RS_Q + pc) = hi;
         *reinterpret_cast<uint32_t*>(kq_lo + (CH + tr) * L::RS_Q + pc) = lo;
-        const float kh0 = k0[i] * ie0, kh1 = k1[i] * ie1;
+        // Padding rows: zero (their G may be below kMinDecay, even 0).
+        const float kh0 = tr < n ? k0[i] * ie0 : 0.f, kh1 = tr < n ? k1[i] * ie1 : 0.f;
         split2(kh0, kh1, hi, lo);  // Kh
         *reinterpret_cast<uint32_t*>(kh_hi + tr * L::RS_K + pc) = hi;
         *reinterpret_cast<uint32_t*>(kh_lo + tr * L::RS_K + pc) = lo;
@@ -589,10 +648,22 @@ __global__ void __launch_bounds__(DV * 4) prefill_chunked_kernel(PrefillArgs<TIn
     // SIMD, so one's MFMA work fills the other's latency-bound solve).  The
     // barrier after the X product orders the M writes before their reads.
 
-    if (c + 1 < n_chunks) issue_loads(c + 1, tid);
+    const int t_end = t_base + n;
+    if (t_end < a.L) {
+      n_next = nominal(t_end);
+      issue_loads(t_end, n_next, tid);
+    }
 
     // ---- Phase 4: value side for this wave's 16 columns ------------------
-    // 4b: X = [Kt; Qt] S, rows 0..CH-1 = Kt S, rows CH..2CH-1 = Qt S.
+    // 4a: S~ = Diag(alpha_0) S.
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      const float4 a4 = misc4(CH + DK + 16 * mt + 4 * g);
+      const float a0[4] = {a4.x, a4.y, a4.z, a4.w};
+#pragma unroll
+      for (int r = 0; r < 4; ++r) st[mt][r] *= a0[r];
+    }
+    // 4b: X = [Kt; Qt] S~, rows 0..CH-1 = Kt S~, rows CH..2CH-1 = Qt S~.
     f32x4_t xs[2 * NB];
 #pragma unroll
     for (int mt = 0; mt < 2 * NB; ++mt) xs[mt] = zero4;
@@ -641,7 +712,7 @@ __global__ void __launch_bounds__(DV * 4) prefill_chunked_kernel(PrefillArgs<TIn
         if (tr < n) st_f32(rs_o, a.scale * xs[NB + mt][r], (tr * rowv + col) * 4, 0);
       }
     }
-    // 4f: S = Diag(G_n) S + Kb^T E.
+    // 4f: S = Diag(G_{n-1}) S~ + Kb^T E.
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
       const float4 g4 = misc4(CH + 16 * mt + 4 * g);
@@ -652,9 +723,9 @@ __global__ void __launch_bounds__(DV * 4) prefill_chunked_kernel(PrefillArgs<TIn
       for (int kb = 0; kb < NB / 2; ++kb)
         st[mt] = mfma3(plane_op2(kb_hi, kb_lo, 16 * mt + l16, L::RS_C, 32 * kb + 4 * g), eop[kb], st[mt]);
     }
-    // Checkpoint at the end of this chunk when one is due.
-    const int t_end = t_base + n;
-    if (n_ckpt > 0 && n == CH && t_end % a.ckpt_every == 0) {
+    // Checkpoint at the end of this chunk when one is due (chunks never
+    // cross a checkpoint boundary).
+    if (t_end <= ck_end && t_end % a.ckpt_every == 0) {
       const int m = t_end / a.ckpt_every - 1;
       const int slot = a.ckpt_slots[(size_t)b * n_ckpt + m];
       if (slot >= 0 && slot < a.n_slots) {
@@ -669,6 +740,7 @@ __global__ void __launch_bounds__(DV * 4) prefill_chunked_kernel(PrefillArgs<TIn
       }
     }
     __syncthreads();  // the next chunk rewrites every LDS region
+    t_base = t_end;
   }
 
 #pragma unroll

@@ -179,9 +179,10 @@ __global__ void KDA_OCCUPANCY __launch_bounds__((kWave * waves_per_group<DV, WPG
       return;
     }
   }
-  float* sp = a.state + ((size_t)sb * a.H + p.h) * DK * DV + p.tile_off();
+  const rsrc_t rs = state_rsrc<DK, DV>(a.state + ((size_t)sb * a.H + p.h) * DK * DV);
+  const int vo = (int)p.tile_off() * 4;
   float S[R][NC];
-  load_tile<R, DV>(sp, S);
+  load_tile<R, DV>(rs, vo, S);
   TokenIn<TIn, R, true, NC> in;
   in.load(a.k + (size_t)p.bh * DK + p.row0, a.q + (size_t)p.bh * DK + p.row0,
           a.alpha + (size_t)p.bh * DK + p.row0, a.v + (size_t)p.bh * DV + p.col0, a.beta + p.bh);
@@ -190,7 +191,7 @@ __global__ void KDA_OCCUPANCY __launch_bounds__((kWave * waves_per_group<DV, WPG
     in.update_prep(S, a.gate_sign, a.scale, o);
   else
     in.update(S, a.scale, o);
-  store_tile<R, DV>(sp, S);
+  store_tile<R, DV>(rs, vo, S);
   if (p.rg == 0) {
     if constexpr (NC == 4)
       *reinterpret_cast<float4*>(a.o + (size_t)p.bh * DV + p.col0) = make_float4(o[0], o[1], o[2], o[3]);
@@ -220,12 +221,13 @@ __global__ void KDA_OCCUPANCY __launch_bounds__((kWave * waves_per_group<DV, WPG
     return;
   }
   if (n == 0) return;
-  float* sp = a.state + ((size_t)sb * a.H + p.h) * DK * DV + p.tile_off();
+  const rsrc_t rs = state_rsrc<DK, DV>(a.state + ((size_t)sb * a.H + p.h) * DK * DV);
+  const int vo = (int)p.tile_off() * 4;
   float S[R][NC];
-  load_tile<R, DV>(sp, S);
+  load_tile<R, DV>(rs, vo, S);
   replay_log<DK, DV, TIn, R, RAW>(S, a.log_k, a.log_v, a.log_alpha, a.log_beta, (size_t)p.b * a.Tmax * a.H + p.h,
                                   a.H, n, p.row0, p.col0, a.gate_sign);
-  store_tile<R, DV>(sp, S);
+  store_tile<R, DV>(rs, vo, S);
   if (p.h == 0 && p.slice == 0 && p.lane == 0) a.pos[sb] += n;
 }
 
@@ -247,9 +249,10 @@ __global__ void KDA_OCCUPANCY __launch_bounds__(kWave) prefill_recurrent_kernel(
   }
   const int64_t pos0 = owner ? a.pos[sb] : 0;
   const int n_ckpt = a.ckpt_every > 0 ? a.L / a.ckpt_every : 0;
-  float* sp = a.state + ((size_t)sb * a.H + p.h) * DK * DV + p.tile_off();
+  const rsrc_t rs = state_rsrc<DK, DV>(a.state + ((size_t)sb * a.H + p.h) * DK * DV);
+  const int vo = (int)p.tile_off() * 4;
   float S[R][4];
-  load_tile<R, DV>(sp, S);
+  load_tile<R, DV>(rs, vo, S);
   TokenIn<TIn, R, true> cur, nxt;
   size_t tok = (size_t)p.b * a.L * a.H + p.h;
   if (a.L > 0)
@@ -270,7 +273,7 @@ __global__ void KDA_OCCUPANCY __launch_bounds__(kWave) prefill_recurrent_kernel(
       const int m = (t + 1) / a.ckpt_every - 1;
       const int slot = a.ckpt_slots[(size_t)p.b * n_ckpt + m];
       if (slot >= 0 && slot < a.n_slots) {
-        store_tile<R, DV>(a.slot_states + ((size_t)slot * a.H + p.h) * DK * DV + p.tile_off(), S);
+        store_tile<R, DV>(state_rsrc<DK, DV>(a.slot_states + ((size_t)slot * a.H + p.h) * DK * DV), vo, S);
         if (owner) a.slot_pos[slot] = pos0 + t + 1;
       } else if (p.slice == 0 && p.lane == 0) {
         atomicOr(a.dev_err, KDA_DEV_ERR_CKPT_SLOT);
@@ -279,7 +282,7 @@ __global__ void KDA_OCCUPANCY __launch_bounds__(kWave) prefill_recurrent_kernel(
     cur = nxt;
     tok = tn;
   }
-  store_tile<R, DV>(sp, S);
+  store_tile<R, DV>(rs, vo, S);
   if (owner) a.pos[sb] = pos0 + a.L;
 }
 

@@ -107,18 +107,6 @@ struct VerifyLds {
   static __device__ __forceinline__ int at(int ch) { return (ch / R) * RP + ch % R; }
 };
 
-// Buffer-resource access: one SGPR base + range per tensor window, a 32-bit
-// lane offset in a VGPR and uniform offsets in SGPRs, so no 64-bit address
-// is kept per load.
-typedef __amdgpu_buffer_rsrc_t rsrc_t;
-typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-constexpr int kRsrcWord3 = 0x00020000;  // raw 32-bit data format
-
-__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kRsrcWord3);
-}
-
 // N consecutive key channels as stored (N = 1 or 2).
 template <typename TIn, int N>
 struct Chan;
@@ -157,7 +145,7 @@ struct Chan<float, 2> {
   __device__ __forceinline__ float operator[](int i) const { return __uint_as_float(i ? w.y : w.x); }
   __device__ __forceinline__ void load(rsrc_t r, int vo, int so) { w = __builtin_amdgcn_raw_buffer_load_b64(r, vo, so, 0); }
   __device__ __forceinline__ void store(rsrc_t r, int vo, int so) const {
-    __builtin_amdgcn_raw_buffer_store_b64(w, r, vo, so, 0);
+    __builtin_amdgcn_raw_buffer_store_b64(w, r, vo + so, 0, 0);  // SGPR offset zero: see store_cols
   }
 };
 
@@ -170,7 +158,7 @@ struct ValC<bf16_t, 4> {
   u32x2 w;
   __device__ __forceinline__ void load(rsrc_t r, int vo, int so) { w = __builtin_amdgcn_raw_buffer_load_b64(r, vo, so, 0); }
   __device__ __forceinline__ void store(rsrc_t r, int vo, int so) const {
-    __builtin_amdgcn_raw_buffer_store_b64(w, r, vo, so, 0);
+    __builtin_amdgcn_raw_buffer_store_b64(w, r, vo + so, 0, 0);  // SGPR offset zero: see store_cols
   }
   __device__ __forceinline__ void widen(float (&x)[4]) const {
     x[0] = bf16_lo(w.x);
@@ -184,7 +172,7 @@ struct ValC<float, 4> {
   u32x4 w;
   __device__ __forceinline__ void load(rsrc_t r, int vo, int so) { w = __builtin_amdgcn_raw_buffer_load_b128(r, vo, so, 0); }
   __device__ __forceinline__ void store(rsrc_t r, int vo, int so) const {
-    __builtin_amdgcn_raw_buffer_store_b128(w, r, vo, so, 0);
+    __builtin_amdgcn_raw_buffer_store_b128(w, r, vo + so, 0, 0);  // SGPR offset zero: see store_cols
   }
   __device__ __forceinline__ void widen(float (&x)[4]) const {
     x[0] = __uint_as_float(w.x);
@@ -210,40 +198,13 @@ struct ValC<float, 2> {
   u32x2 w;
   __device__ __forceinline__ void load(rsrc_t r, int vo, int so) { w = __builtin_amdgcn_raw_buffer_load_b64(r, vo, so, 0); }
   __device__ __forceinline__ void store(rsrc_t r, int vo, int so) const {
-    __builtin_amdgcn_raw_buffer_store_b64(w, r, vo, so, 0);
+    __builtin_amdgcn_raw_buffer_store_b64(w, r, vo + so, 0, 0);  // SGPR offset zero: see store_cols
   }
   __device__ __forceinline__ void widen(float (&x)[2]) const {
     x[0] = __uint_as_float(w.x);
     x[1] = __uint_as_float(w.y);
   }
 };
-
-// NC fp32 values as one 16- or 8-byte buffer store (AUX: cache-policy bits).
-template <int NC, int AUX>
-__device__ __forceinline__ void store_cols(const float (&x)[NC], rsrc_t r, int vo, int so) {
-  if constexpr (NC == 4) {
-    const u32x4 w = {__float_as_uint(x[0]), __float_as_uint(x[1]), __float_as_uint(x[2]), __float_as_uint(x[3])};
-    __builtin_amdgcn_raw_buffer_store_b128(w, r, vo, so, AUX);
-  } else {
-    const u32x2 w = {__float_as_uint(x[0]), __float_as_uint(x[1])};
-    __builtin_amdgcn_raw_buffer_store_b64(w, r, vo, so, AUX);
-  }
-}
-// NC fp32 values from one 16- or 8-byte buffer load (AUX: cache-policy bits).
-template <int NC, int AUX>
-__device__ __forceinline__ void load_cols(float (&x)[NC], rsrc_t r, int vo, int so) {
-  if constexpr (NC == 4) {
-    const u32x4 w = __builtin_amdgcn_raw_buffer_load_b128(r, vo, so, AUX);
-    x[0] = __uint_as_float(w.x);
-    x[1] = __uint_as_float(w.y);
-    x[2] = __uint_as_float(w.z);
-    x[3] = __uint_as_float(w.w);
-  } else {
-    const u32x2 w = __builtin_amdgcn_raw_buffer_load_b64(r, vo, so, AUX);
-    x[0] = __uint_as_float(w.x);
-    x[1] = __uint_as_float(w.y);
-  }
-}
 
 // Windows over one (sequence, head)'s T tokens: consecutive tokens are H
 // rows apart in every [B][T][H][d] tensor.

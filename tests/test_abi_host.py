@@ -4,7 +4,9 @@ anything.
 
 Every call here is built to fail host-side validation (or to be a pure size
 query), so no kernel is ever launched: the pointers passed are fake but never
-reach a device.  Safe with or without a GPU.
+reach a device.  Safe with or without a GPU.  The one exception, an empty
+prompt (which must return before any launch), runs only where no GPU is
+visible; tests/test_gpu_decay.py covers it on the GPU with real buffers.
 """
 
 from __future__ import annotations
@@ -310,6 +312,31 @@ def test_prefill_validation(k):
                None) == SHAPE
     assert rec(ctypes.byref(s), 8, GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, 4, None, None, None,
                None) == NULL
+
+
+def test_empty_prompt_returns_before_any_launch(k):
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("fake pointers: host-only check (the GPU suite tests empty prompts with real buffers)")
+    L = k.lib()
+    s = shape(k)
+    before = L.kda_last_variant()
+    # NULL token pointers are allowed when L = 0, and nothing is enqueued.
+    assert L.kda_prefill_chunked(ctypes.byref(s), 0, 64, GOOD, GOOD, None, None, None, None, None, None, 0, None,
+                                 None, None, None) == OK
+    assert L.kda_prefill_chunked_prep(ctypes.byref(s), 0, 0, 32, GOOD, GOOD, None, None, None, None, None, None, 0,
+                                      None, None, None, None) == OK
+    assert L.kda_prefill_recurrent(ctypes.byref(s), 0, GOOD, GOOD, None, None, None, None, None, None, 0, None, None,
+                                   None, None) == OK
+    assert L.kda_prefill_recurrent_prep(ctypes.byref(s), 1, 0, GOOD, GOOD, None, None, None, None, None, None, 0,
+                                        None, None, None, None) == OK
+    slots = k._lib._Slots(0x200000, 0x300000, 8)
+    assert L.kda_prefill_chunked_slots(ctypes.byref(s), 0, 64, GOOD, ctypes.byref(slots), None, None, None, None,
+                                       None, None, 0, None, GOOD, None) == OK
+    assert L.kda_last_variant() == before
+    # The state and position are still required.
+    assert L.kda_prefill_chunked(ctypes.byref(s), 0, 64, None, GOOD, None, None, None, None, None, None, 0, None,
+                                 None, None, None) == NULL
 
 
 def test_status_strings(k):

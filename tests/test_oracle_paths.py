@@ -169,3 +169,79 @@ def test_chunk_form_collapses_to_recurrence_at_chunk_one():
     S_new, O = chunk_form.chunk_step(S, q, k, v, a, b, 0.5)
     S_ref, o_ref = ko.step(S, q[0], k[0], v[0], a[0], b[0], 0.5)
     assert np.allclose(S_new, S_ref, atol=1e-14) and np.allclose(O[0], o_ref, atol=1e-14)
+
+
+# ---- strongly decaying gates: the guarded chunk form the prefill kernel runs ----
+
+def _gate_case(kind, L, dk, rng):
+    if kind == "sigmoid_m1":                      # sigmoid(N(-1, 1)): mean ~0.3, often below 0.1
+        return 1.0 / (1.0 + np.exp(-rng.normal(-1.0, 1.0, (L, dk))))
+    if kind == "const_0.05":
+        return np.full((L, dk), 0.05)
+    if kind == "zeros":                           # some channels shut at some tokens, the rest near 1
+        a = 1.0 / (1.0 + np.exp(-rng.normal(3.0, 1.0, (L, dk))))
+        a[rng.random((L, dk)) < 0.02] = 0.0
+        a[:, 3] = 0.0                             # one channel forgets every token
+        a[17] = 0.0                               # one token resets every channel
+        return a
+    if kind == "ones":
+        return np.ones((L, dk))
+    raise ValueError(kind)
+
+
+@pytest.mark.parametrize("chunk", [32, 64])
+@pytest.mark.parametrize("kind", ["sigmoid_m1", "const_0.05", "zeros", "ones"])
+def test_guarded_chunk_form_fp32_matches_oracle_for_any_gate(chunk, kind):
+    # The kernel's algebra in fp32 stays finite and within the parity bar for
+    # gates anywhere in [0, 1], including exact zeros; the oracle is the
+    # plain recurrence.
+    rng = np.random.default_rng(11)
+    L, dk, dv = 200, 16, 8
+    k = rng.standard_normal((L, dk))
+    k /= np.linalg.norm(k, axis=1, keepdims=True)
+    q = rng.standard_normal((L, dk))
+    q /= np.linalg.norm(q, axis=1, keepdims=True)
+    v = rng.standard_normal((L, dv))
+    beta = 1.0 / (1.0 + np.exp(-rng.standard_normal(L)))
+    alpha = _gate_case(kind, L, dk, rng).astype(np.float32).astype(np.float64)
+    S0 = rng.normal(0.0, 0.02, (dk, dv))
+    inp = {"q": q[None, :, None], "k": k[None, :, None], "v": v[None, :, None], "alpha": alpha[None, :, None],
+           "beta": beta[None, :, None]}
+    S_ref, o_ref = ko.decode(S0[None, None], inp, dk ** -0.5)
+    S, O, lengths = chunk_form.run_guarded(S0, q, k, v, alpha, beta, dk ** -0.5, chunk)
+    assert np.all(np.isfinite(O)) and np.all(np.isfinite(S))
+    rms = np.sqrt(np.mean(o_ref ** 2))
+    assert np.max(np.abs(O - o_ref[0, :, 0])) <= 2e-3 * rms
+    assert np.linalg.norm(S - S_ref[0, 0]) <= 1e-3 * np.linalg.norm(S_ref[0, 0])
+    assert sum(lengths) == L and min(lengths) >= 1
+    if kind == "ones":
+        assert lengths == [min(chunk, L - i) for i in range(0, L, chunk)], "no cut for gates that do not decay"
+
+
+def test_guarded_chunk_form_cuts_only_where_needed():
+    # Gates of the decode workloads (mean ~0.97) never cut a 64-token chunk;
+    # a constant 0.05 cuts before the product passes 2^-96 (0.05^22 > 2^-96 > 0.05^23).
+    spec = synth.CONFIGS["prefill"]
+    a = synth.token_inputs(spec, 1, 4096, heads=[0])["alpha"][0, :, 0].astype(np.float64)
+    r = np.random.default_rng(1)
+    z = np.zeros((4096, 128))
+    _, _, lengths = chunk_form.run_guarded(np.zeros((128, 2)), z, z, np.zeros((4096, 2)), a, np.zeros(4096), 1.0, 64)
+    assert set(lengths) == {64}
+    c = np.full((100, 4), 0.05)
+    _, _, lengths = chunk_form.run_guarded(np.zeros((4, 2)), r.random((100, 4)), r.random((100, 4)),
+                                           r.random((100, 2)), c, r.random(100), 1.0, 64)
+    assert lengths[:4] == [23, 23, 23, 23]
+
+
+def test_unguarded_chunk_algebra_breaks_for_strong_decay():
+    # The earlier algebra (k / prod alpha from the chunk start) overflows: alpha = 0.05
+    # over a 64-token chunk gives 1 / 0.05^63, beyond fp32, and alpha = 0 divides by zero.
+    rng = np.random.default_rng(12)
+    L, dk, dv = 64, 8, 4
+    k = rng.standard_normal((L, dk))
+    k /= np.linalg.norm(k, axis=1, keepdims=True)
+    args = (rng.normal(0, 0.02, (dk, dv)), k, k, rng.standard_normal((L, dv)))
+    _, O = chunk_form.run_inclusive(*args, np.full((L, dk), 0.05), np.full(L, 0.5), 0.5, 64)
+    assert not np.all(np.isfinite(O))
+    _, O, _ = chunk_form.run_guarded(*args, np.full((L, dk), 0.05), np.full(L, 0.5), 0.5, 64)
+    assert np.all(np.isfinite(O))
