@@ -36,7 +36,8 @@
 // accumulated in fp32 (the three-product bf16 scheme of Henry, Tang and
 // Heinecke, "Leveraging the bfloat16 Artificial Intelligence Datatype For
 // Higher-Precision Computations", ARITH 2019): about 2^-16 relative error
-// per product instead of bf16's 2^-9.  The triangular inverse is fp32 VALU.
+// per product instead of bf16's 2^-9.  The inverses of the 16 x 16 diagonal
+// blocks of I + A are fp32 VALU.
 //
 // Operand layouts (16x16x32 bf16, verified on gfx950): lane l holds
 //   A[m = l & 15][k = 8 (l >> 4) + e],  B[k = 8 (l >> 4) + e][n = l & 15],
@@ -221,8 +222,13 @@ struct Smem {
   static constexpr int off_kb = off_kq + 2 * KQ_PLANE * 2;
   static constexpr int off_r2 = off_kb + 2 * KB_PLANE * 2;
   static constexpr int r2_a = 2 * KH_PLANE * 2;
-  static constexpr int RS_D = 20;      // fp32 row stride of a diagonal block: 16-byte rows, conflict-free writes
-  static constexpr int DIAG = NB * 16 * RS_D;  // floats of the diagonal blocks
+  // Diagonal blocks of A, fp32 and transposed (column i of a block is a
+  // contiguous row of RS_D floats).  A block takes 16 RS_D + 4 floats: the
+  // 4-float skew puts the same column of the NB blocks in different banks,
+  // as the inverse reads them in one instruction.
+  static constexpr int RS_D = 20;
+  static constexpr int DSTRIDE = 16 * RS_D + 4;
+  static constexpr int DIAG = NB * DSTRIDE;  // floats of the diagonal blocks
   static constexpr int r2_b = 2 * CC_PLANE * 2 + DIAG * 4;
   static constexpr int off_r3 = off_r2 + (r2_a > r2_b ? r2_a : r2_b);
   static constexpr int total = off_r3 + 2 * CC_PLANE * 2;
@@ -541,7 +547,11 @@ __global__ void __launch_bounds__(DV * 4) prefill_chunked_kernel(PrefillArgs<TIn
 
     // ---- Phase 2: A = Diag(beta) Kt Kh^T and P = Qt Kh^T (lower tiles) ---
     // Tile list: index i < NA are A tiles (mt, nt), nt <= mt < NB; the next
-    // NA are P tiles (NB + mt, nt).  Waves take tiles round-robin.
+    // NA are P tiles (NB + mt, nt).  Waves take tiles round-robin.  Each tile
+    // is formed transposed (Kh as the A operand), so lane (g, l16) holds
+    // row 16 mt + l16, columns 16 nt + 4 g .. + 3 of the tile: four
+    // consecutive slots of a plane row, written hi and lo with one 8-byte
+    // store each.
     constexpr int NA = NB * (NB + 1) / 2;
     constexpr int MAXT = (2 * NA + NW - 1) / NW;
     constexpr bool EVEN = (2 * NA) % NW == 0;  // every wave has MAXT tiles
@@ -557,7 +567,7 @@ __global__ void __launch_bounds__(DV * 4) prefill_chunked_kernel(PrefillArgs<TIn
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) {
           const int k0_ = 32 * kb + 4 * g;
-          at[s_] = mfma3(plane_op2(kq_hi, kq_lo, row, L::RS_Q, k0_), plane_op2(kh_hi, kh_lo, 16 * nt + l16, L::RS_K, k0_),
+          at[s_] = mfma3(plane_op2(kh_hi, kh_lo, 16 * nt + l16, L::RS_K, k0_), plane_op2(kq_hi, kq_lo, row, L::RS_Q, k0_),
                          at[s_]);
         }
       }
@@ -569,30 +579,29 @@ __global__ void __launch_bounds__(DV * 4) prefill_chunked_kernel(PrefillArgs<TIn
       if (EVEN || i < 2 * NA) {
         int mt, nt;
         tri_tile(i < NA ? i : i - NA, mt, nt);
-        const int tc = 16 * nt + l16;
-        float4 b4 = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (i < NA) b4 = misc4(16 * mt + 4 * g);  // wave-uniform branch
-        const float bt4[4] = {b4.x, b4.y, b4.z, b4.w};
+        const int tr = 16 * mt + l16;  // row token of this lane
+        const int c0 = 16 * nt + 4 * g;  // its first column token
+        float v4[4];
+        if (i < NA) {  // wave-uniform branch
+          const float bta = misc(tr);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int tr = 16 * mt + 4 * g + r;
-          if (i < NA) {
-            const float bta = bt4[r];
-            const float av = tc < tr ? at[s_][r] * bta : 0.f;
-            if (mt == nt) {
-              adiag[(mt * 16 + 4 * g + r) * L::RS_D + l16] = av;
-            } else {
-              __bf16 lo;
-              const __bf16 hi = split_hi(av, lo);
-              m_hi[tr * L::RS_C + kpos(tc)] = __builtin_bit_cast(bf16_t, hi);
-              m_lo[tr * L::RS_C + kpos(tc)] = __builtin_bit_cast(bf16_t, lo);
-            }
-          } else {
-            __bf16 lo;
-            const __bf16 hi = split_hi(tc <= tr ? at[s_][r] : 0.f, lo);
-            p_hi[tr * L::RS_C + kpos(tc)] = __builtin_bit_cast(bf16_t, hi);
-            p_lo[tr * L::RS_C + kpos(tc)] = __builtin_bit_cast(bf16_t, lo);
-          }
+          for (int e = 0; e < 4; ++e) v4[e] = c0 + e < tr ? at[s_][e] * bta : 0.f;
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v4[e] = c0 + e <= tr ? at[s_][e] : 0.f;
+        }
+        if (i < NA && mt == nt) {
+          float* aj = adiag + mt * L::DSTRIDE;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) aj[(4 * g + e) * L::RS_D + l16] = v4[e];
+        } else {
+          uint32_t h0, l0, h1, l1;
+          split2(v4[0], v4[1], h0, l0);
+          split2(v4[2], v4[3], h1, l1);
+          bf16_t* dh = (i < NA ? m_hi : p_hi) + tr * L::RS_C + kpos(c0);
+          bf16_t* dl = (i < NA ? m_lo : p_lo) + tr * L::RS_C + kpos(c0);
+          *reinterpret_cast<uint2*>(dh) = make_uint2(h0, h1);
+          *reinterpret_cast<uint2*>(dl) = make_uint2(l0, l1);
         }
       }
     }
@@ -611,42 +620,41 @@ __global__ void __launch_bounds__(DV * 4) prefill_chunked_kernel(PrefillArgs<TIn
     __syncthreads();
 
     // ---- Phase 3: diagonal blocks X_jj = (I + A_jj)^-1 into M ------------
-    // Lane c < 16 of wave j solves column c of block j by forward
-    // substitution in fp32, then writes the block (1 on the diagonal, 0
-    // above) as hi/lo.
-    for (int j = wave; j < NB; j += NW) {
-      if (lane < 16) {
-        const int cc = lane;
-        float x[16];
+    // The last wave (it has the fewest A/P tiles) inverts every block at
+    // once: lane 16 j + c forms column c of block j by right-looking
+    // elimination in fp32 (x = e_c; for each i, column i of A_jj times x_i
+    // is subtracted from the rows below i), so the chain is one multiply-add
+    // per step; the columns are broadcast reads of the transposed copy.  The
+    // block goes to M (1 on the diagonal, 0 above) as hi/lo.
+    if (wave == NW - 1 && lane < 16 * NB) {
+      const int j = lane >> 4, cc = lane & 15;
+      const float* aj = adiag + j * L::DSTRIDE;
+      float x[16];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          // Row r of the block, read four entries at a time (same address on
-          // every lane: a broadcast).
-          float acc = 0.f;
+      for (int r = 0; r < 16; ++r) x[r] = r == cc ? 1.f : 0.f;
 #pragma unroll
-          for (int i4 = 0; i4 < (r + 3) / 4; ++i4) {
-            const float4 a4 = *reinterpret_cast<const float4*>(&adiag[(j * 16 + r) * L::RS_D + 4 * i4]);
-            const float av[4] = {a4.x, a4.y, a4.z, a4.w};
+      for (int i = 0; i < 15; ++i) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-              if (4 * i4 + i < r) acc = __builtin_fmaf(av[i], x[4 * i4 + i], acc);
-          }
-          x[r] = r == cc ? 1.f : (r < cc ? 0.f : -acc);
+        for (int q = (i + 1) / 4; q < 4; ++q) {
+          const float4 c4 = *reinterpret_cast<const float4*>(aj + i * L::RS_D + 4 * q);
+          const float cv[4] = {c4.x, c4.y, c4.z, c4.w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (4 * q + e > i) x[4 * q + e] = __builtin_fmaf(-cv[e], x[i], x[4 * q + e]);
         }
+      }
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          __bf16 lo;
-          const __bf16 hi = split_hi(x[r], lo);
-          m_hi[(16 * j + r) * L::RS_C + kpos(16 * j + cc)] = __builtin_bit_cast(bf16_t, hi);
-          m_lo[(16 * j + r) * L::RS_C + kpos(16 * j + cc)] = __builtin_bit_cast(bf16_t, lo);
-        }
+      for (int r = 0; r < 16; ++r) {
+        __bf16 lo;
+        const __bf16 hi = split_hi(x[r], lo);
+        m_hi[(16 * j + r) * L::RS_C + kpos(16 * j + cc)] = __builtin_bit_cast(bf16_t, hi);
+        m_lo[(16 * j + r) * L::RS_C + kpos(16 * j + cc)] = __builtin_bit_cast(bf16_t, lo);
       }
     }
     // No barrier here: the next loads and the X product below read only
-    // registers and the Kt/Qt planes, so the waves without a diagonal block
-    // run them while the others are still solving theirs (two waves share a
-    // SIMD, so one's MFMA work fills the other's latency-bound solve).  The
-    // barrier after the X product orders the M writes before their reads.
+    // registers and the Kt/Qt planes, so the other waves run them while the
+    // last one inverts the blocks.  The barrier after the X product orders
+    // the M writes before their reads.
 
     const int t_end = t_base + n;
     if (t_end < a.L) {
