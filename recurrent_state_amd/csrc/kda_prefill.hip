@@ -257,14 +257,28 @@ __device__ __forceinline__ void tri_tile(int ii, int& mt, int& nt) {
 // preparation phase normalises q and k (one full-wave sum per token: a wave
 // holds every key channel of its tokens) and applies the gates, and the rest
 // of the chunk is the prepared kernel's.
+// 16-column tiles of the state per wave.  A wave reads each LDS operand of
+// its value-side products once and applies it to all of its tiles.  Two
+// tiles per wave (four waves at dv = 128) halve the LDS reads per matrix
+// instruction but measured much slower (2.40 against 1.82 ms at B = 8,
+// L = 8192): the chunk's chain is bound by latency, which eight waves hide
+// better than four, not by LDS bandwidth.  One tile per wave is the default.
+#ifndef KDA_PREFILL_CT
+#define KDA_PREFILL_CT 1
+#endif
+// dv = 64 keeps one tile per wave: with two its two waves would each prepare
+// twice the tokens, beyond the register file.
+constexpr int prefill_ct(int DV) { return DV >= 128 ? KDA_PREFILL_CT : 1; }
+
 // Smallest in-chunk decay product G a chunk may hold in any key channel:
 // 1 / G then stays below 2^96, far inside the fp32 (and bf16) range, and the
 // hi/lo split of k G keeps its precision for all but negligible components.
 constexpr float kMinDecay = 0x1p-96f;
 
 template <int DK, int DV, int CH, typename TIn, bool PREP>
-__global__ void __launch_bounds__(DV * 4) prefill_chunked_kernel(PrefillArgs<TIn> a) {
-  constexpr int NW = DV / 16;        // waves; wave w owns value columns [16 w, 16 w + 16)
+__global__ void __launch_bounds__(DV * 4 / prefill_ct(DV)) prefill_chunked_kernel(PrefillArgs<TIn> a) {
+  constexpr int CT = prefill_ct(DV);  // 16-column state tiles per wave
+  constexpr int NW = DV / (16 * CT);  // waves; wave w owns value columns [16 CT w, 16 CT (w + 1))
   constexpr int NT = 64 * NW;        // threads
   constexpr int NB = CH / 16;        // 16-token blocks
   constexpr int KB = DK / 32;        // 32-channel k blocks
@@ -315,14 +329,17 @@ __global__ void __launch_bounds__(DV * 4) prefill_chunked_kernel(PrefillArgs<TIn
   const f32x4_t zero4 = {0.f, 0.f, 0.f, 0.f};
 
   // State columns of this wave in the accumulator layout:
-  // st[mt][r] = S[16 mt + 4 g + r][col], at byte tile_voff + (16 mt + r) DV 4.
-  f32x4_t st[MT];
-  const int tile_voff = ((4 * ((threadIdx.x & 63) >> 4)) * DV + 16 * (threadIdx.x >> 6) + (threadIdx.x & 15)) * 4;
+  // st[ct][mt][r] = S[16 mt + 4 g + r][16 CT wave + 16 ct + l16], at byte
+  // tile_voff + (16 mt + r) DV 4 + 64 ct.
+  f32x4_t st[CT][MT];
+  const int tile_voff = ((4 * ((threadIdx.x & 63) >> 4)) * DV + 16 * CT * (threadIdx.x >> 6) + (threadIdx.x & 15)) * 4;
   const rsrc_t rs_state = make_rsrc(a.state + ((size_t)sb * a.H + h) * DK * DV, DK * DV * 4);
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt)
+  for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) st[mt][r] = ld_f32(rs_state, tile_voff, (16 * mt + r) * DV * 4);
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) st[ct][mt][r] = ld_f32(rs_state, tile_voff, (16 * mt + r) * DV * 4 + 64 * ct);
 
   const int rowk = a.H * DK, rowv = a.H * DV;  // elements between consecutive tokens
   // Nominal length of the chunk starting at token t: CH tokens, fewer at the
@@ -343,7 +360,7 @@ __global__ void __launch_bounds__(DV * 4) prefill_chunked_kernel(PrefillArgs<TIn
   Pair2<float> ra[TPG];
   Pair2<TIn> rk[TPG], rq[TPG];
   float rb;  // beta of token tg TPG + (cp mod TPG): one load per lane instead of TPG identical ones
-  One<TIn> rv[NB][4];
+  One<TIn> rv[CT][NB][4];
   auto issue_loads = [&](int t_b, int nn, int tid_) {
     const size_t r0 = (tok0 + t_b) * a.H + h;
     const rsrc_t wk = make_rsrc(a.k + r0 * DK, ((nn - 1) * rowk + DK) * sizeof(TIn));
@@ -352,7 +369,7 @@ __global__ void __launch_bounds__(DV * 4) prefill_chunked_kernel(PrefillArgs<TIn
     const rsrc_t wb = make_rsrc(a.beta + r0, ((nn - 1) * a.H + 1) * 4);
     const rsrc_t wv = make_rsrc(a.v + r0 * DV, ((nn - 1) * rowv + DV) * sizeof(TIn));
     const int cp_ = tid_ % CP, tg_ = tid_ / CP;
-    const int g_ = (tid_ & 63) >> 4, col_ = 16 * (tid_ >> 6) + (tid_ & 15);
+    const int g_ = (tid_ & 63) >> 4, col_ = 16 * CT * (tid_ >> 6) + (tid_ & 15);
 #pragma unroll
     for (int i = 0; i < TPG; ++i) {
       const int rc = min(tg_ * TPG + i, nn - 1);
@@ -363,12 +380,14 @@ __global__ void __launch_bounds__(DV * 4) prefill_chunked_kernel(PrefillArgs<TIn
     }
     rb = ld_f32(wb, min(tg_ * TPG + cp_ % TPG, nn - 1) * a.H * 4, 0);
 #pragma unroll
-    for (int mt = 0; mt < NB; ++mt)
+    for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int rc = min(16 * mt + 4 * g_ + r, nn - 1);
-        rv[mt][r].load(wv, (rc * rowv + col_) * (int)sizeof(TIn));
-      }
+      for (int mt = 0; mt < NB; ++mt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int rc = min(16 * mt + 4 * g_ + r, nn - 1);
+          rv[ct][mt][r].load(wv, (rc * rowv + col_ + 16 * ct) * (int)sizeof(TIn));
+        }
   };
   int n_next = a.L > 0 ? nominal(0) : 0;
   if (a.L > 0) issue_loads(0, n_next, threadIdx.x);
@@ -381,7 +400,7 @@ __global__ void __launch_bounds__(DV * 4) prefill_chunked_kernel(PrefillArgs<TIn
     asm volatile("" : "+v"(tid));
     const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l16 = lane & 15, g = lane >> 4;
-    const int col = 16 * wave + l16;  // this lane's value column in the accumulator layout
+    const int col = 16 * CT * wave + l16;  // this lane's value column in its first tile
     int n = n_next;  // valid tokens in this chunk (cut short below if a decay is too strong); rows n.. are padding
     const size_t row0 = (tok0 + t_base) * a.H + h;  // [B][L][H] row index of the chunk's first token
     const rsrc_t rs_o = make_rsrc(a.o + row0 * DV, ((n - 1) * rowv + DV) * 4);
@@ -390,7 +409,7 @@ __global__ void __launch_bounds__(DV * 4) prefill_chunked_kernel(PrefillArgs<TIn
     const int cp = tid % CP, tg = tid / CP;
     const int c0 = 2 * cp;
     float al0[TPG], al1[TPG], k0[TPG], k1[TPG], q0[TPG], q1[TPG];
-    float vv[NB][4];
+    float vv[CT][NB][4];
 #pragma unroll
     for (int i = 0; i < TPG; ++i) {
       const bool pad = tg * TPG + i >= n;
@@ -501,9 +520,11 @@ __global__ void __launch_bounds__(DV * 4) prefill_chunked_kernel(PrefillArgs<TIn
         misc(CH + c0 + 1) = gn1;
       }
 #pragma unroll
-      for (int mt = 0; mt < NB; ++mt)
+      for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) vv[mt][r] = 16 * mt + 4 * g + r < n ? rv[mt][r].get() : 0.f;
+        for (int mt = 0; mt < NB; ++mt)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) vv[ct][mt][r] = 16 * mt + 4 * g + r < n ? rv[ct][mt][r].get() : 0.f;
       // Pass B: the decayed planes; Kb goes to transposed planes two tokens at a time.
       // Kb = Kh G_{n-1} (no third factor per element).
       const float egn0 = gn0, egn1 = gn1;
@@ -662,63 +683,90 @@ __global__ void __launch_bounds__(DV * 4) prefill_chunked_kernel(PrefillArgs<TIn
       issue_loads(t_end, n_next, tid);
     }
 
-    // ---- Phase 4: value side for this wave's 16 columns ------------------
+    // ---- Phase 4: value side for this wave's CT tiles of 16 columns ------
+    // Every LDS operand below is read once and used for all CT tiles.
     // 4a: S~ = Diag(alpha_0) S.
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
       const float4 a4 = misc4(CH + DK + 16 * mt + 4 * g);
       const float a0[4] = {a4.x, a4.y, a4.z, a4.w};
 #pragma unroll
-      for (int r = 0; r < 4; ++r) st[mt][r] *= a0[r];
+      for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) st[ct][mt][r] *= a0[r];
     }
     // 4b: X = [Kt; Qt] S~, rows 0..CH-1 = Kt S~, rows CH..2CH-1 = Qt S~.
-    f32x4_t xs[2 * NB];
+    f32x4_t xs[CT][2 * NB];
 #pragma unroll
-    for (int mt = 0; mt < 2 * NB; ++mt) xs[mt] = zero4;
+    for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+      for (int mt = 0; mt < 2 * NB; ++mt) xs[ct][mt] = zero4;
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
-      const Op sop = op_from_tiles(st[2 * kb], st[2 * kb + 1]);
+      Op sop[CT];
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct) sop[ct] = op_from_tiles(st[ct][2 * kb], st[ct][2 * kb + 1]);
       const int k0_ = 32 * kb + 4 * g;
 #pragma unroll
-      for (int mt = 0; mt < 2 * NB; ++mt) xs[mt] = mfma3(plane_op2(kq_hi, kq_lo, 16 * mt + l16, L::RS_Q, k0_), sop, xs[mt]);
+      for (int mt = 0; mt < 2 * NB; ++mt) {
+        const Op kop = plane_op2(kq_hi, kq_lo, 16 * mt + l16, L::RS_Q, k0_);
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) xs[ct][mt] = mfma3(kop, sop[ct], xs[ct][mt]);
+      }
     }
     __syncthreads();  // the diagonal blocks of M are complete
-    // 4c/4d: R = V - Kt S, then E = (I + A)^-1 Diag(beta) R by 16-token blocks:
+    // 4c/4d: R = V - Kt S~, then E = (I + A)^-1 Diag(beta) R by 16-token blocks:
     //   E_i = X_ii (beta_i R_i - sum_{j<i} A_ij E_j).
-    // E is kept only as MFMA B operands eop[kb] (32-token k blocks); while
-    // block 2 kb + 1 is pending, eop[kb] holds E_{2kb} and zeros.  The sum
+    // E is kept only as MFMA B operands eop[ct][kb] (32-token k blocks); while
+    // block 2 kb + 1 is pending, eop[ct][kb] holds E_{2kb} and zeros.  The sum
     // runs over whole k blocks of M: the zero half adds nothing.
-    Op eop[NB / 2];
+    Op eop[CT][NB / 2];
 #pragma unroll
     for (int i = 0; i < NB; ++i) {
-      f32x4_t z;
+      f32x4_t z[CT];
       const float4 b4 = misc4(16 * i + 4 * g);
       const float bt4[4] = {b4.x, b4.y, b4.z, b4.w};
 #pragma unroll
-      for (int r = 0; r < 4; ++r) z[r] = bt4[r] * (vv[i][r] - xs[i][r]);
-      if (i > 0) {
-        f32x4_t cs = zero4;
+      for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
-        for (int kb = 0; kb <= (i - 1) / 2; ++kb)
-          cs = mfma3(plane_op2(m_hi, m_lo, 16 * i + l16, L::RS_C, 32 * kb + 4 * g), eop[kb], cs);
-        z -= cs;
+        for (int r = 0; r < 4; ++r) z[ct][r] = bt4[r] * (vv[ct][i][r] - xs[ct][i][r]);
+      if (i > 0) {
+        f32x4_t cs[CT];
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) cs[ct] = zero4;
+#pragma unroll
+        for (int kb = 0; kb <= (i - 1) / 2; ++kb) {
+          const Op mop = plane_op2(m_hi, m_lo, 16 * i + l16, L::RS_C, 32 * kb + 4 * g);
+#pragma unroll
+          for (int ct = 0; ct < CT; ++ct) cs[ct] = mfma3(mop, eop[ct][kb], cs[ct]);
+        }
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) z[ct] -= cs[ct];
       }
       const Op ax = plane_op2(m_hi, m_lo, 16 * i + l16, L::RS_C, 32 * (i / 2) + 4 * g);
-      const f32x4_t e = mfma3(ax, (i & 1) ? op_from_tiles(zero4, z) : op_from_tiles(z, zero4), zero4);
-      xs[i] = e;  // R_i is dead: keep E_i until its k block is complete
-      eop[i / 2] = (i & 1) ? op_from_tiles(xs[i - 1], e) : op_from_tiles(e, zero4);
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct) {
+        const f32x4_t e = mfma3(ax, (i & 1) ? op_from_tiles(zero4, z[ct]) : op_from_tiles(z[ct], zero4), zero4);
+        xs[ct][i] = e;  // R_i is dead: keep E_i until its k block is complete
+        eop[ct][i / 2] = (i & 1) ? op_from_tiles(xs[ct][i - 1], e) : op_from_tiles(e, zero4);
+      }
     }
-    // 4e: O = scale (Qt S + P E), stored for the valid tokens.
+    // 4e: O = scale (Qt S~ + P E), stored for the valid tokens.
 #pragma unroll
     for (int mt = 0; mt < NB; ++mt) {
 #pragma unroll
-      for (int kb = 0; kb <= mt / 2; ++kb)
-        xs[NB + mt] = mfma3(plane_op2(p_hi, p_lo, 16 * mt + l16, L::RS_C, 32 * kb + 4 * g), eop[kb], xs[NB + mt]);
+      for (int kb = 0; kb <= mt / 2; ++kb) {
+        const Op pop = plane_op2(p_hi, p_lo, 16 * mt + l16, L::RS_C, 32 * kb + 4 * g);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int tr = 16 * mt + 4 * g + r;
-        if (tr < n) st_f32(rs_o, a.scale * xs[NB + mt][r], (tr * rowv + col) * 4, 0);
+        for (int ct = 0; ct < CT; ++ct) xs[ct][NB + mt] = mfma3(pop, eop[ct][kb], xs[ct][NB + mt]);
       }
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int tr = 16 * mt + 4 * g + r;
+          if (tr < n) st_f32(rs_o, a.scale * xs[ct][NB + mt][r], (tr * rowv + col + 16 * ct) * 4, 0);
+        }
     }
     // 4f: S = Diag(G_{n-1}) S~ + Kb^T E.
 #pragma unroll
@@ -726,10 +774,15 @@ __global__ void __launch_bounds__(DV * 4) prefill_chunked_kernel(PrefillArgs<TIn
       const float4 g4 = misc4(CH + 16 * mt + 4 * g);
       const float gn4[4] = {g4.x, g4.y, g4.z, g4.w};
 #pragma unroll
-      for (int r = 0; r < 4; ++r) st[mt][r] *= gn4[r];
+      for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
-      for (int kb = 0; kb < NB / 2; ++kb)
-        st[mt] = mfma3(plane_op2(kb_hi, kb_lo, 16 * mt + l16, L::RS_C, 32 * kb + 4 * g), eop[kb], st[mt]);
+        for (int r = 0; r < 4; ++r) st[ct][mt][r] *= gn4[r];
+#pragma unroll
+      for (int kb = 0; kb < NB / 2; ++kb) {
+        const Op bop = plane_op2(kb_hi, kb_lo, 16 * mt + l16, L::RS_C, 32 * kb + 4 * g);
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) st[ct][mt] = mfma3(bop, eop[ct][kb], st[ct][mt]);
+      }
     }
     // Checkpoint at the end of this chunk when one is due (chunks never
     // cross a checkpoint boundary).
@@ -739,9 +792,11 @@ __global__ void __launch_bounds__(DV * 4) prefill_chunked_kernel(PrefillArgs<TIn
       if (slot >= 0 && slot < a.n_slots) {
         const rsrc_t rs_slot = make_rsrc(a.slot_states + ((size_t)slot * a.H + h) * DK * DV, DK * DV * 4);
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
+        for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
-          for (int r = 0; r < 4; ++r) st_f32(rs_slot, st[mt][r], tile_voff, (16 * mt + r) * DV * 4);
+          for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) st_f32(rs_slot, st[ct][mt][r], tile_voff, (16 * mt + r) * DV * 4 + 64 * ct);
         if (owner) a.slot_pos[slot] = pos0 + t_end;
       } else if (tid == 0) {
         atomicOr(a.dev_err, KDA_DEV_ERR_CKPT_SLOT);
@@ -752,9 +807,11 @@ __global__ void __launch_bounds__(DV * 4) prefill_chunked_kernel(PrefillArgs<TIn
   }
 
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt)
+  for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) st_f32(rs_state, st[mt][r], tile_voff, (16 * mt + r) * DV * 4);
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) st_f32(rs_state, st[ct][mt][r], tile_voff, (16 * mt + r) * DV * 4 + 64 * ct);
   if (owner) a.pos[sb] = pos0 + a.L;
 }
 
@@ -769,9 +826,9 @@ hipError_t launch_cfg(const kda_shape& s, int32_t L, int32_t chunk, float* state
   auto go = [&](auto prep) {
     constexpr bool PREP = decltype(prep)::value;
     if (chunk == 64)
-      prefill_chunked_kernel<DK, DV, 64, TIn, PREP><<<grid, 4 * DV, 0, st>>>(a);
+      prefill_chunked_kernel<DK, DV, 64, TIn, PREP><<<grid, 4 * DV / prefill_ct(DV), 0, st>>>(a);
     else
-      prefill_chunked_kernel<DK, DV, 32, TIn, PREP><<<grid, 4 * DV, 0, st>>>(a);
+      prefill_chunked_kernel<DK, DV, 32, TIn, PREP><<<grid, 4 * DV / prefill_ct(DV), 0, st>>>(a);
   };
   if (gate < 0)
     go(std::false_type{});
