@@ -82,6 +82,7 @@ typedef enum kda_dtype { KDA_BF16 = 0, KDA_F32 = 1 } kda_dtype;
 #define KDA_DEV_ERR_CKPT_SLOT 2 /* a checkpoint slot id was outside [0, n_slots) */
 #define KDA_DEV_ERR_DRAFT_LEN 4 /* a per-sequence draft length was outside [0, T] */
 #define KDA_DEV_ERR_SLOT_ID 8   /* a device-side state slot id was outside [0, n_slots) */
+#define KDA_DEV_ERR_MIXED 16    /* kda_mixed_step: roles or token ranges inconsistent with the launch */
 
 /* Kernel variants reported by kda_last_variant(). */
 #define KDA_VARIANT_NONE 0
@@ -106,6 +107,13 @@ typedef enum kda_dtype { KDA_BF16 = 0, KDA_F32 = 1 } kda_dtype;
 #define KDA_VARIANT_COMMIT_SLOTS 19
 #define KDA_VARIANT_COMMIT_VERIFY_SLOTS 20
 #define KDA_VARIANT_PREFILL_CHUNKED_SLOTS 21
+#define KDA_VARIANT_MIXED 22
+
+/* What a sequence does in a kda_mixed_step. */
+#define KDA_ROLE_IDLE 0    /* nothing this step */
+#define KDA_ROLE_DECODE 1  /* one token, as kda_decode_step */
+#define KDA_ROLE_SPEC 2    /* commit of its accepted drafts, then a verify of new ones */
+#define KDA_ROLE_PREFILL 3 /* a segment of its prompt, as kda_prefill_chunked */
 
 /* Decay gate of kda_decode_step_prep: alpha = f(x) of the logit x. */
 #define KDA_GATE_EXP_NEG_SOFTPLUS 0 /* alpha = exp(-softplus(x)) = 1 / (1 + e^x) */
@@ -435,6 +443,53 @@ kda_status kda_prefill_recurrent_prep(const kda_shape* shape, int32_t gate, int3
                                       const float* beta_logit, float* o, int32_t ckpt_every,
                                       const int32_t* ckpt_slots, const kda_slots* slots, int32_t* dev_err,
                                       void* stream);
+
+/*
+ * One serving step over a mixed batch, in one launch: each sequence b of
+ * the batch (shape->B of them) decodes, speculates or processes a prompt
+ * segment, as roles[b] says ("Hyper-optimizing Kimi K3 in vLLM", Part 2,
+ * section 4: pure decode and mixed workloads are measured apart; "What's
+ * Next": prefill and mixed batches).
+ *   roles      device int32 [B], KDA_ROLE_*; exactly n_decode, n_spec and
+ *              n_prefill of them DECODE, SPEC and PREFILL (host counts: the
+ *              grid is sized from them).
+ *   tok_start  device int32 [B + 1]: sequence b's tokens are rows
+ *              tok_start[b] .. tok_start[b + 1] - 1 of the packed inputs
+ *              q, k, v, alpha (in_dtype / f32 [n_tokens][H][d]) and beta
+ *              (f32 [n_tokens][H]); its outputs go to the same rows of o
+ *              (f32 [n_tokens][H][dv]).  DECODE takes exactly 1 token, SPEC
+ *              0 .. log->T_max drafts, PREFILL any number (0: nothing).
+ *   state/pos  the states and positions: dense [B] when slot_ids is NULL,
+ *              otherwise a slot pool of n_slots entries that sequence b
+ *              reaches through slot_ids[b] (device int32 [B], distinct ids).
+ *   log        the speculative log, sized for this B (NULL allowed when
+ *              n_spec == 0 and nothing is pending).  Rows are indexed by
+ *              batch position, so a speculating sequence keeps its position
+ *              from one step to the next.  SPEC sequences first commit
+ *              accepted[b] rows of the pending verify (device int32 [B],
+ *              read when log->pending_T > 0; the pending verify must have
+ *              logged prepared inputs), then verify and log their drafts.
+ *              Every other role must have accepted[b] == 0; after the step
+ *              the log holds this step's drafts only (pending_T = T_max when
+ *              n_spec > 0, else 0).
+ * Prepared inputs only (unit q, k; gates and beta as for kda_decode_step).
+ * The arithmetic of each role is that of kda_decode_step, kda_commit_verify
+ * and kda_prefill_chunked with chunk 64, so states and outputs are bit-
+ * identical to those calls (no checkpoints are taken).  Device-side checks
+ * set bits in *dev_err (device int32, required) and skip the sequence:
+ * KDA_DEV_ERR_MIXED for role counts that differ from roles[], an unknown
+ * role or a token range outside [0, n_tokens] or wrong for its role;
+ * KDA_DEV_ERR_SLOT_ID; KDA_DEV_ERR_ACCEPTED for a count out of range or one
+ * given to a sequence that does not speculate.  Host-side failures:
+ * KDA_ERR_SHAPE (counts negative or summing above B, n_tokens too large),
+ * KDA_ERR_NULL, KDA_ERR_ALIGN, KDA_ERR_ORDER (a pending verify of raw
+ * projections).
+ */
+kda_status kda_mixed_step(const kda_shape* shape, const int32_t* roles, const int32_t* tok_start, int32_t n_tokens,
+                          int32_t n_decode, int32_t n_spec, int32_t n_prefill, float* state, int64_t* pos,
+                          const int32_t* slot_ids, int32_t n_slots, const void* q, const void* k, const void* v,
+                          const float* alpha, const float* beta, float* o, kda_log* log, const int32_t* accepted,
+                          int32_t* dev_err, void* stream);
 
 /* Human-readable name of a status code (static string). */
 const char* kda_status_str(kda_status status);

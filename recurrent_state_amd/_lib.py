@@ -22,9 +22,11 @@ VARIANTS = {0: "none", 1: "decode", 2: "verify", 3: "commit", 4: "snapshot", 5: 
             6: "prefill_recurrent", 7: "prefill_chunked", 8: "commit_verify", 9: "verify_varlen",
             10: "commit_verify_varlen", 11: "decode_prep", 12: "verify_prep", 13: "commit_verify_prep",
             14: "decode_slots", 15: "slot_copy", 16: "prefill_chunked_prep", 17: "prefill_recurrent_prep",
-            18: "verify_slots", 19: "commit_slots", 20: "commit_verify_slots", 21: "prefill_chunked_slots"}
+            18: "verify_slots", 19: "commit_slots", 20: "commit_verify_slots", 21: "prefill_chunked_slots",
+            22: "mixed"}
 GATE_EXP_NEG_SOFTPLUS, GATE_SIGMOID = 0, 1
-DEV_ERR_ACCEPTED, DEV_ERR_CKPT_SLOT, DEV_ERR_DRAFT_LEN, DEV_ERR_SLOT_ID = 1, 2, 4, 8
+DEV_ERR_ACCEPTED, DEV_ERR_CKPT_SLOT, DEV_ERR_DRAFT_LEN, DEV_ERR_SLOT_ID, DEV_ERR_MIXED = 1, 2, 4, 8, 16
+ROLE_IDLE, ROLE_DECODE, ROLE_SPEC, ROLE_PREFILL = 0, 1, 2, 3
 
 
 class KdaError(RuntimeError):
@@ -87,6 +89,8 @@ _SIGS = {
                                       ctypes.POINTER(_Slots), _P, _P]),
     "kda_prefill_recurrent_prep": (_I, [ctypes.POINTER(Shape), _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _I, _P,
                                         ctypes.POINTER(_Slots), _P, _P]),
+    "kda_mixed_step": (_I, [ctypes.POINTER(Shape), _P, _P, _I, _I, _I, _I, _P, _P, _P, _I, _P, _P, _P, _P, _P, _P,
+                            ctypes.POINTER(_Log), _P, _P, _P]),
     "kda_status_str": (ctypes.c_char_p, [_I]),
     "kda_last_variant": (_I, []),
     "kda_abi_version": (_I, []),
@@ -426,6 +430,50 @@ def prefill_chunked_slots(state_slots, pool: SlotPool, q, k, v, alpha, beta, o, 
     _check(lib().kda_prefill_chunked_slots(ctypes.byref(sh), L, chunk, _ptr(state_slots), ctypes.byref(pool.c),
                                            *(_ptr(x) for x in (q, k, v, alpha, beta, o)), ckpt_every,
                                            _ptr(ckpt_slots) if n_ckpt else None, _ptr(dev_err), _stream()))
+
+
+def mixed_step(state, pos, roles, tok_start, counts, q, k, v, alpha, beta, o, dev_err, *, log: InputLog = None,
+               accepted=None, slot_ids=None, scale=None):
+    """One serving step over a mixed batch in one launch (kda_mixed_step).
+
+    roles (device int32 [B], ROLE_*) and tok_start (device int32 [B + 1])
+    describe the batch; counts = (n_decode, n_spec, n_prefill) are the host's
+    role counts.  Tokens are packed: q, k [N][H][dk], v [N][H][dv], alpha
+    [N][H][dk], beta [N][H], o [N][H][dv].  state / pos are the dense [B]
+    states, or a slot pool's arrays when slot_ids (device int32 [B]) is given.
+    """
+    B = roles.shape[0]
+    dev = state.device
+    _need(roles, "roles", (B,), torch.int32, dev)
+    _need(tok_start, "tok_start", (B + 1,), torch.int32, dev)
+    _need(dev_err, "dev_err", (1,), torch.int32, dev)
+    n_slots, H, dk, dv = state.shape
+    _need(state, "state", (n_slots, H, dk, dv), torch.float32, dev)
+    _need(pos, "pos", (n_slots,), torch.int64, dev)
+    if slot_ids is None:
+        if n_slots != B:
+            raise ValueError("without slot_ids, state holds one entry per sequence")
+    else:
+        _need(slot_ids, "slot_ids", (B,), torch.int32, dev)
+    N = q.shape[0]
+    _need(q, "q", (N, H, dk), q.dtype, dev)
+    _need(k, "k", (N, H, dk), q.dtype, dev)
+    _need(v, "v", (N, H, dv), q.dtype, dev)
+    _need(alpha, "alpha", (N, H, dk), torch.float32, dev)
+    _need(beta, "beta", (N, H), torch.float32, dev)
+    _need(o, "o", (N, H, dv), torch.float32, dev)
+    if accepted is not None:
+        _need(accepted, "accepted", (B,), torch.int32, dev)
+    sh = _shape(torch.empty((B, H, dk, dv), device="meta"), q.dtype, scale)
+    if log is not None and (B, H, dk, dv, sh.in_dtype) != (log.shape.B, log.shape.H, log.shape.dk, log.shape.dv,
+                                                           log.shape.in_dtype):
+        raise ValueError("log was sized for a different shape")
+    n_dec, n_spec, n_pf = (int(c) for c in counts)
+    _check(lib().kda_mixed_step(ctypes.byref(sh), _ptr(roles), _ptr(tok_start), N, n_dec, n_spec, n_pf, _ptr(state),
+                                _ptr(pos), _ptr(slot_ids), n_slots if slot_ids is not None else 0,
+                                *(_ptr(x) for x in (q, k, v, alpha, beta, o)),
+                                ctypes.byref(log.c) if log is not None else None, _ptr(accepted), _ptr(dev_err),
+                                _stream()))
 
 
 def slot_copy(src_slots, dst_slots, pool: SlotPool):

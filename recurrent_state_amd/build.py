@@ -16,7 +16,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libkda.so")
 
-SOURCES = ["kda_api.cpp", "kda_state.hip", "kda_verify.hip", "kda_slots.hip", "kda_prefill.hip"]
+SOURCES = ["kda_api.cpp", "kda_state.hip", "kda_verify.hip", "kda_slots.hip", "kda_prefill.hip", "kda_mixed.hip"]
 
 # -ffp-contract=off: every fused multiply-add in the kernels is written out,
 #   so decode and commit round identically.

@@ -552,6 +552,51 @@ kda_status kda_prefill_recurrent_prep(const kda_shape* shape, int32_t gate, int3
                                 slots, dev_err, gate, stream);
 }
 
+kda_status kda_mixed_step(const kda_shape* shape, const int32_t* roles, const int32_t* tok_start, int32_t n_tokens,
+                          int32_t n_decode, int32_t n_spec, int32_t n_prefill, float* state, int64_t* pos,
+                          const int32_t* slot_ids, int32_t n_slots, const void* q, const void* k, const void* v,
+                          const float* alpha, const float* beta, float* o, kda_log* log, const int32_t* accepted,
+                          int32_t* dev_err, void* stream) {
+  kda_status r = check_shape(shape);
+  if (r != KDA_OK) return r;
+  if (n_tokens < 0 || n_decode < 0 || n_spec < 0 || n_prefill < 0) return KDA_ERR_SHAPE;
+  if ((int64_t)n_decode + n_spec + n_prefill > shape->B) return KDA_ERR_SHAPE;
+  if (slot_ids && n_slots < 1) return KDA_ERR_SHAPE;
+  int32_t pend = 0;
+  if (log) {
+    if ((r = check_log(*shape, log)) != KDA_OK) return r;
+    pend = log->pending_T;
+    if (pend < 0 || pend > log->T_max) return KDA_ERR_ORDER;
+    if (pend > 0 && log->pending_form != 0) return KDA_ERR_ORDER;  // one replay form: prepared
+  } else if (n_spec > 0) {
+    return KDA_ERR_NULL;
+  }
+  if (shape->B > 0) {
+    if (!roles || !tok_start || !dev_err || !pos) return KDA_ERR_NULL;
+    if (!aligned(roles, 4) || !aligned(tok_start, 4) || !aligned(dev_err, 4) || !aligned(pos, 8))
+      return KDA_ERR_ALIGN;
+    if ((r = check_ptrs({state})) != KDA_OK) return r;
+    if (n_tokens > 0 && (r = check_tokens(q, k, v, alpha, beta, o)) != KDA_OK) return r;
+    if (pend > 0) {
+      if (!accepted) return KDA_ERR_NULL;
+      if (!aligned(accepted, 4)) return KDA_ERR_ALIGN;
+    }
+    if (slot_ids && !aligned(slot_ids, 4)) return KDA_ERR_ALIGN;
+    const kda::LogPtrs lp = log ? log_ptrs(*shape, log) : kda::LogPtrs{};
+    const kda::MixedBatch m{roles, tok_start, n_tokens, n_decode, n_spec, n_prefill};
+    r = launched(kda::launch_mixed(*shape, m, state, pos, slot_ids, slot_ids ? n_slots : shape->B,
+                                   kda::TokenInputs{q, k, v, alpha, beta}, o, log ? &lp : nullptr, pend, accepted,
+                                   dev_err, static_cast<hipStream_t>(stream)),
+                 KDA_VARIANT_MIXED);
+    if (r != KDA_OK) return r;
+  }
+  if (log) {
+    log->pending_T = n_spec > 0 ? log->T_max : 0;
+    log->pending_form = 0;
+  }
+  return KDA_OK;
+}
+
 const char* kda_status_str(kda_status status) {
   switch (status) {
     case KDA_OK: return "ok";

@@ -99,6 +99,19 @@ hipError_t launch_prefill_chunked(const kda_shape& s, int32_t L, int32_t chunk, 
                                   float* slot_states, int64_t* slot_pos, int32_t n_slots, int32_t* dev_err,
                                   int32_t gate, hipStream_t st, const int32_t* state_slots = nullptr);
 
+// A mixed batch (kda_mixed_step): device roles [B] and token offsets
+// [B + 1] into the packed token rows, with the host's role counts.
+struct MixedBatch {
+  const int32_t* roles;
+  const int32_t* tok_start;
+  int32_t n_tokens, n_decode, n_spec, n_prefill;
+};
+// log may be null (no speculating sequence, nothing pending); T_pend is the
+// pending verify's row count (0: none, accepted unused).
+hipError_t launch_mixed(const kda_shape& s, const MixedBatch& m, float* state, int64_t* pos, const int32_t* slot_ids,
+                        int32_t n_slots, TokenInputs in, float* o, const LogPtrs* log, int32_t T_pend,
+                        const int32_t* accepted, int32_t* dev_err, hipStream_t st);
+
 // Copies whole per-sequence states (n_floats each) and positions for up to
 // kMaxPairs (src, dst) index pairs per launch.
 constexpr int kMaxPairs = 64;

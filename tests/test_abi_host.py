@@ -339,6 +339,43 @@ def test_empty_prompt_returns_before_any_launch(k):
                                  None, None, None) == NULL
 
 
+def test_mixed_step_validation(k):
+    L = k.lib()
+    s = shape(k, B=4)
+    need = k.log_bytes(s, 4)
+
+    def mx(counts=(1, 1, 1), n_tok=8, lg=None, roles=GOOD, ts=GOOD, err=GOOD, pos=GOOD, st=GOOD, acc=GOOD,
+           slot_ids=None, n_slots=0, q=GOOD, sh=s):
+        return L.kda_mixed_step(ctypes.byref(sh), roles, ts, n_tok, *counts, st, pos, slot_ids, n_slots, q, GOOD,
+                                GOOD, GOOD, GOOD, GOOD, ctypes.byref(lg) if lg is not None else None, acc, err, None)
+
+    log = k._lib._Log(0x100000, need, 4, 0)
+    assert mx(lg=None) == NULL                                   # a speculating sequence needs a log
+    assert mx(counts=(-1, 0, 0)) == SHAPE
+    assert mx(counts=(2, 2, 1), lg=log) == SHAPE                 # 5 roles for 4 sequences
+    assert mx(n_tok=-1, lg=log) == SHAPE
+    assert mx(lg=log, roles=None) == NULL
+    assert mx(lg=log, ts=None) == NULL
+    assert mx(lg=log, err=None) == NULL
+    assert mx(lg=log, pos=P(0x10004)) == ALIGN
+    assert mx(lg=log, roles=P(0x10002)) == ALIGN
+    assert mx(lg=log, q=None) == NULL                            # tokens present: token pointers required
+    assert mx(lg=log, slot_ids=GOOD, n_slots=0) == SHAPE
+    assert mx(lg=k._lib._Log(0x100000, need - 256, 4, 0)) == SHAPE
+    raw = k._lib._Log(0x100000, need, 4, 3, 1)                   # a pending verify of raw projections
+    assert mx(lg=raw) == ORDER and raw.pending_T == 3
+    pend = k._lib._Log(0x100000, need, 4, 3, 0)
+    assert mx(lg=pend, acc=None) == NULL                         # pending rows: counts needed
+    assert pend.pending_T == 3, "a rejected call must not touch the pending count"
+    # An empty batch enqueues nothing and leaves nothing pending.
+    empty = shape(k, B=0)
+    lg0 = k._lib._Log(0x100000, k.log_bytes(empty, 4) or 256, 4, 3, 0)
+    before = L.kda_last_variant()
+    assert mx(counts=(0, 0, 0), n_tok=0, lg=lg0, roles=None, ts=None, err=None, pos=None, st=None, acc=None,
+              q=None, sh=empty) == OK
+    assert lg0.pending_T == 0 and L.kda_last_variant() == before
+
+
 def test_status_strings(k):
     L = k.lib()
     names = [L.kda_status_str(i).decode() for i in range(8)]
