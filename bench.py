@@ -9,8 +9,10 @@ so every launch streams its state from HBM as a multi-layer model would.
 
 `rows` reports the other parts of the path, each against its own roofline:
 the decode batch sweep B = 1..64, speculative verify (T = 4) and commit,
-snapshot/restore, the prompt prefill with checkpoints (B = 8, L = 8192), and a
-measured device-to-device copy for reference.  `roofline` is the decode
+snapshot/restore, the prompt prefill with checkpoints (B = 8, L = 8192), mixed
+batches (decode, speculative rounds and prompt segments in one launch, against
+the standalone kernels one after another), and a measured device-to-device
+copy for reference.  `roofline` is the decode
 kernel's: algorithmic bytes per launch / measured average launch time.
 `cpu_baseline` times the fp64 oracle on a bounded sample of the headline
 workload on the host.
@@ -20,7 +22,7 @@ Timing: every figure is the median of 5 samples of at least 200 ms each
 the K steps asked for, and its first K-step block is reported beside them.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--quick] [--no-cpu]
-                       [--rows decode,spec,slots,prefill] [--samples N] [--min-sample-ms M]
+                       [--rows decode,spec,slots,prefill,mixed] [--samples N] [--min-sample-ms M]
 """
 
 from __future__ import annotations
@@ -467,6 +469,110 @@ def prefill_flops_per_chunk(C, K, V):
     return alg, mfmas * 16384
 
 
+def bench_mixed(torch, kda, synth, device, n_dec, n_spec, pf_lens, T=4, accept=2, layers=8):
+    """A serving step over a mixed batch, one step = every layer's state
+    (slot pools of B = n_dec + n_spec + len(pf_lens) sequences, one per layer):
+    n_dec sequences decode a token, n_spec run a speculative round (commit of
+    `accept` drafts, verify of T new ones) and each prompt segment of pf_lens
+    is processed.  Timed two ways on the same inputs, each captured in one
+    graph per step: the one-launch mixed step per layer, and the standalone
+    kernels (fused commit + verify, decode, one chunked prefill per segment
+    length) launched one after another per layer."""
+    spec = synth.CONFIGS["spec_verify"]
+    roles = ["pf"] * len(pf_lens) + ["spec"] * n_spec + ["dec"] * n_dec
+    lens = list(pf_lens) + [T] * n_spec + [1] * n_dec
+    B = len(roles)
+    code = {"dec": kda.ROLE_DECODE, "spec": kda.ROLE_SPEC, "pf": kda.ROLE_PREFILL}
+    start = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    N = int(start[-1])
+    inp = synth.token_inputs(spec, 1, N, phase=11)
+    packed = {k: dev_tensor(torch, v[0], device) for k, v in inp.items()}          # [N][H][d]
+    o = torch.empty((N, H, DV), dtype=torch.float32, device=device)
+    roles_dev = torch.tensor([code[r] for r in roles], dtype=torch.int32, device=device)
+    start_dev = torch.from_numpy(start).to(device)
+    slot_ids = torch.arange(B, dtype=torch.int32, device=device)
+    S0 = dev_tensor(torch, synth.initial_state(spec, 1), device)
+    err = torch.zeros(1, dtype=torch.int32, device=device)
+    acc = torch.tensor([accept if r == "spec" else 0 for r in roles], dtype=torch.int32, device=device)
+
+    def pools():
+        out = []
+        for _ in range(layers):
+            p = kda.SlotPool(B, H, DK, DV, device)
+            p.states.copy_(S0.expand(B, -1, -1, -1))
+            p.pos.zero_()
+            out.append(p)
+        return out
+
+    # One launch per layer.
+    pool_m = pools()
+    logs_m = [kda.InputLog(p.states, T) for p in pool_m]
+    counts = (n_dec, n_spec, len(pf_lens))
+
+    def mixed_layer(p, lg):
+        return lambda: kda.mixed_step(p.states, p.pos, roles_dev, start_dev, counts, packed["q"], packed["k"],
+                                      packed["v"], packed["alpha"], packed["beta"], o, err, log=lg, accepted=acc,
+                                      slot_ids=slot_ids)
+
+    for p, lg in zip(pool_m, logs_m):   # a first step leaves drafts pending
+        mixed_layer(p, lg)()
+    g_mixed = capture(torch, [mixed_layer(p, lg) for p, lg in zip(pool_m, logs_m)])
+
+    # The standalone kernels per layer: sub-batches by role, inputs copied into
+    # their dense layouts once.
+    pool_s = pools()
+    spec_ids = slot_ids[len(pf_lens):len(pf_lens) + n_spec].contiguous()
+    dec_ids = slot_ids[len(pf_lens) + n_spec:].contiguous()
+    rows = lambda b: slice(int(start[b]), int(start[b + 1]))  # noqa: E731
+    sp = {k: torch.stack([v[rows(len(pf_lens) + i)] for i in range(n_spec)]).contiguous() for k, v in packed.items()}
+    dc = {k: torch.stack([v[rows(len(pf_lens) + n_spec + i)] for i in range(n_dec)]).contiguous()
+          for k, v in packed.items()}
+    by_len = {}
+    for i, n in enumerate(pf_lens):
+        by_len.setdefault(n, []).append(i)
+    pf = {n: ({k: torch.stack([v[rows(i)] for i in ix]).contiguous() for k, v in packed.items()},
+              slot_ids[ix].contiguous(), torch.empty((len(ix), n, H, DV), dtype=torch.float32, device=device))
+          for n, ix in by_len.items()}
+    o_sp = torch.empty((n_spec, T, H, DV), dtype=torch.float32, device=device)
+    o_dc = torch.empty((n_dec, 1, H, DV), dtype=torch.float32, device=device)
+    logs_s = [kda.InputLog(p.states[:n_spec], T) for p in pool_s]
+    acc_s = torch.full((n_spec,), accept, dtype=torch.int32, device=device)
+
+    def separate_layer(p, lg):
+        def f():
+            kda.commit_verify_slots(spec_ids, p, sp["q"], sp["k"], sp["v"], sp["alpha"], sp["beta"], o_sp, lg, err,
+                                    accepted=acc_s)
+            kda.decode_step_slots(dec_ids, p, dc["q"], dc["k"], dc["v"], dc["alpha"], dc["beta"], o_dc, err)
+            for n, (d, ids, o_pf) in pf.items():
+                kda.prefill_chunked_slots(ids, p, d["q"], d["k"], d["v"], d["alpha"], d["beta"], o_pf, err, chunk=64)
+        return f
+
+    for p, lg in zip(pool_s, logs_s):
+        kda.verify_slots(spec_ids, p, sp["q"], sp["k"], sp["v"], sp["alpha"], sp["beta"], o_sp, lg, err)
+    g_sep = capture(torch, [separate_layer(p, lg) for p, lg in zip(pool_s, logs_s)])
+
+    def runner(g):
+        def run(n):
+            for _ in range(n):
+                g.replay()
+        return run
+
+    for g in (g_mixed, g_sep):
+        g.replay()
+    ms_m, samp_m = sampled(torch, runner(g_mixed), f"step of {layers} layers")
+    ms_s, samp_s = sampled(torch, runner(g_sep), f"step of {layers} layers")
+    torch.cuda.synchronize()
+    if err.item() != 0:
+        raise RuntimeError(f"mixed bench: device error flags {err.item()}")
+    per_layer = (n_dec * DECODE_BYTES
+                 + n_spec * (2 * STATE_BYTES + T * (TOKEN_IN_BYTES + 128 * 4 + LOG_BYTES) + accept * LOG_BYTES)
+                 + sum(2 * STATE_BYTES + n * PREFILL_BYTES_PER_TOKEN_HEAD for n in pf_lens)) * H
+    return {"B": B, "decode": n_dec, "spec": n_spec, "T": T, "accepted": accept, "prompt_segments": list(pf_lens),
+            "layers": layers, "mixed_us_per_layer": ms_m * 1e3 / layers, "separate_us_per_layer": ms_s * 1e3 / layers,
+            "speedup": ms_s / ms_m, "mixed_hbm_frac": per_layer * layers / (ms_m * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "algorithmic_bytes_per_layer": per_layer, "samples_mixed": samp_m, "samples_separate": samp_s}
+
+
 def bench_snapshot_restore(torch, kda, synth, device, reps=20):
     B, n_slots = 64, 64
     S = torch.randn((B, H, DK, DV), device=device)
@@ -618,10 +724,11 @@ def main():
     ap.add_argument("--min-sample-ms", type=float, default=200.0,
                     help="minimum length of one sample (profiling runs: 0)")
     ap.add_argument("--rows", default="all",
-                    help="comma-separated row groups after the headline: decode, spec, slots, prefill (default all)")
+                    help="comma-separated row groups after the headline: decode, spec, slots, prefill, mixed "
+                         "(default all)")
     args = ap.parse_args()
     N_SAMPLES, MIN_SAMPLE_MS = max(1, args.samples), max(0.0, args.min_sample_ms)
-    groups = {"decode", "spec", "slots", "prefill"}
+    groups = {"decode", "spec", "slots", "prefill", "mixed"}
     picked = groups if args.rows == "all" else set(args.rows.split(","))
     if not picked <= groups:
         ap.error(f"--rows: unknown group(s) {sorted(picked - groups)}")
@@ -700,6 +807,11 @@ def main():
         log("prefill")
         for variant in ("chunked", "chunked_prep", "recurrent"):
             rows[f"prefill_{variant}"] = bench_prefill(torch, kda, synth, device, variant)
+    if not args.quick and "mixed" in picked:
+        log("mixed batches: one launch against the standalone kernels")
+        rows["mixed_b64_pf200"] = bench_mixed(torch, kda, synth, device, 55, 8, [200])
+        rows["mixed_b64_pf4x512"] = bench_mixed(torch, kda, synth, device, 52, 8, [512] * 4)
+        rows["mixed_b16_pf200"] = bench_mixed(torch, kda, synth, device, 11, 4, [200], layers=16)
 
     bytes_per_launch = DECODE_BYTES * B_HEAD * H
     line = {
