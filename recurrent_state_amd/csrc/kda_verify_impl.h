@@ -528,23 +528,28 @@ __device__ __forceinline__ void verify_seq(const VerifyArgs<TIn>& a, VerifyLds<D
     LogReplay<DK, DV, TIn, R, PREP, NC> rp{a.log_k, a.log_v, a.log_alpha, a.log_beta, tok0_log, a.H, row0, col0};
     if (PF && a.T_pend > 0) rp.prime();  // logged token 0's loads go out ahead of the state tile
     load_state(S);
+    // The replay runs with a count of 0 when nothing is to be committed, so
+    // the tile has one definition after it (a replay under a branch keeps a
+    // second copy of the 64-register tile live for the path that skips it).
+    int n = 0;
     if (a.T_pend > 0) {
-      const int n = a.accepted[b];
-      const int rec = a.log_len[bh];
-      if (n < 0 || n > min(a.T_pend, log_rows(rec))) {
+      n = a.accepted[b];
+      if (n < 0 || n > min(a.T_pend, log_rows(a.log_len[bh]))) {
         if (h == 0 && wave == 0 && lane == 0) atomicOr(a.dev_err, KDA_DEV_ERR_ACCEPTED);
-      } else if (n > 0) {
-        if constexpr (PF)
-          rp.run(S, n, a.pend_gate_sign);
-        else
-          replay_log<DK, DV, TIn, R, PREP>(S, a.log_k, a.log_v, a.log_alpha, a.log_beta, tok0_log, a.H, n, row0,
-                                           col0, a.pend_gate_sign);
-#pragma unroll
-        for (int r = 0; r < R; ++r) store_cols<NC, kStateStoreAux>(S[r], rs, svo, r * DV * 4);
-        if (h == 0 && wave == 0 && lane == 0) a.pos[sb] += n;
+        n = 0;
       }
-      __syncthreads();  // every wave has read the pending log rows and count before the verify rewrites them
     }
+    if constexpr (PF)
+      rp.run(S, n, a.pend_gate_sign);
+    else
+      replay_log<DK, DV, TIn, R, PREP>(S, a.log_k, a.log_v, a.log_alpha, a.log_beta, tok0_log, a.H, n, row0, col0,
+                                       a.pend_gate_sign);
+    if (n > 0) {
+#pragma unroll
+      for (int r = 0; r < R; ++r) store_cols<NC, kStateStoreAux>(S[r], rs, svo, r * DV * 4);
+      if (h == 0 && wave == 0 && lane == 0) a.pos[sb] += n;
+    }
+    if (a.T_pend > 0) __syncthreads();  // every wave has read the pending log rows and count before the verify rewrites them
   }
   if (threadIdx.x == 0) a.log_len[bh] = log_record(Tv, PREP ? kLogRaw + a.gate : kLogPrepared);
   if (Tv == 0) return;
