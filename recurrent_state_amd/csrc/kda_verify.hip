@@ -47,7 +47,13 @@ __global__ void __launch_bounds__(kWave * DV / (kRowGroups * (PF ? 2 : 4))) veri
 // Below this many (sequence, head) pairs a launch is bound by each
 // workgroup's serial chain, not by bandwidth: verify (and the fused round)
 // run 16 value columns per wave, and the fused round prefetches its replay.
-constexpr int kLatencyPairs = 512;
+// At and above it the 32-column shape wins (16-column waves up to 4,096
+// pairs measured: verify at B = 64 37.6 against 30.5 us, the fused round at
+// B = 16 22.0 against 17.6 us; H = 32).
+#ifndef KDA_LATENCY_PAIRS
+#define KDA_LATENCY_PAIRS 512
+#endif
+constexpr int kLatencyPairs = KDA_LATENCY_PAIRS;
 
 template <int DK, int DV, typename TIn, bool COMMIT, bool PREP>
 void launch_cfg(const VerifyArgs<TIn>& a, int32_t B, hipStream_t st) {
