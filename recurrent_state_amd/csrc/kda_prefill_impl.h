@@ -497,7 +497,7 @@ __device__ __forceinline__ void prefill_seq(const PrefillArgs<TIn>& a, char* sme
         __syncthreads();
 #pragma unroll
         for (int w = 0; w < NW; ++w) f = min(f, *reinterpret_cast<const int*>(&misc(CH + 2 * DK + w)));
-        n = f;
+        n = __builtin_amdgcn_readfirstlane(f);  // equal in every lane
         // The lanes holding token n - 1 publish G_{n-1} of their channels.
 #pragma unroll
         for (int i = 0; i < TPG; ++i)
@@ -674,7 +674,11 @@ __device__ __forceinline__ void prefill_seq(const PrefillArgs<TIn>& a, char* sme
     // last one inverts the blocks.  The barrier after the X product orders
     // the M writes before their reads.
 
-    const int t_end = t_base + n;
+    // The chunk's end, taken after the possible cut above (whose branch the
+    // compiler cannot prove uniform): readfirstlane keeps it, the next
+    // chunk's length and every buffer resource formed from them in scalar
+    // registers.
+    const int t_end = __builtin_amdgcn_readfirstlane(t_base + n);
     if (t_end < n_tok) {
       n_next = nominal(t_end);
       issue_loads(t_end, n_next, tid);

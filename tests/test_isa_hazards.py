@@ -7,6 +7,14 @@ and on gfx950 that assumption was seen to fail (a decode step's state row
 picked up the next value of its register).  Every wide buffer store in the
 library therefore folds its uniform offset into the lane offset and passes a
 zero SGPR offset; this test keeps it that way.
+
+A buffer resource built from a value the compiler cannot prove wave-uniform
+(one read from LDS, or merged after a branch it takes to be divergent) is held
+in vector registers, and every access through it becomes a loop over the
+distinct resources in the wave: readfirstlane, compare, exec mask, access.
+Such loops once sat around every input load and output store of the chunked
+prefill's chunk loop (1.83 against 1.58 ms without them); the second test
+finds none in any kernel.
 """
 
 from __future__ import annotations
@@ -23,6 +31,9 @@ from recurrent_state_amd import build as b
 
 WIDE_STORE_SGPR_OFFSET = re.compile(r"buffer_store_dwordx[234]\s+v\[[0-9:]+\],\s*v[0-9]+,\s*s\[[0-9:]+\],\s*s[0-9]+")
 WIDE_STORE = re.compile(r"buffer_store_dwordx[234]\b")
+# readfirstlane into a resource, then an access under a per-resource exec mask.
+RESOURCE_LOOP = re.compile(r"v_readfirstlane_b32[^\n]*\n(?:[^\n]*\n){0,10}?\s*s_and_saveexec_b64[^\n]*\n\s*buffer_(?:load|store)")
+HAVE_HIPCC = os.path.exists(b.hipcc()) or shutil.which(b.hipcc())
 
 
 def _asm(src, out):
@@ -34,14 +45,45 @@ def _asm(src, out):
         return f.read()
 
 
-@pytest.mark.skipif(not (os.path.exists(b.hipcc()) or shutil.which(b.hipcc())), reason="hipcc not available")
-def test_no_wide_buffer_store_takes_an_sgpr_offset(tmp_path):
+@pytest.fixture(scope="module")
+def asm(tmp_path_factory):
+    if not HAVE_HIPCC:
+        pytest.skip("hipcc not available")
+    d = tmp_path_factory.mktemp("asm")
     srcs = [s for s in b.SOURCES if s.endswith(".hip")]
     with ThreadPoolExecutor(max_workers=len(srcs)) as ex:
-        asm = dict(zip(srcs, ex.map(lambda s: _asm(s, str(tmp_path / (s + ".s"))), srcs)))
+        return dict(zip(srcs, ex.map(lambda s: _asm(s, str(d / (s + ".s"))), srcs)))
+
+
+def test_no_wide_buffer_store_takes_an_sgpr_offset(asm):
     total = 0
     for src, text in asm.items():
         bad = WIDE_STORE_SGPR_OFFSET.findall(text)
         assert not bad, f"{src}: {len(bad)} wide buffer stores with an SGPR offset, e.g. {bad[0]}"
         total += len(WIDE_STORE.findall(text))
     assert total > 0, "the pattern must see the library's wide stores"
+
+
+def test_no_buffer_access_loops_over_resources(asm):
+    for src, text in asm.items():
+        bad = RESOURCE_LOOP.findall(text)
+        assert not bad, f"{src}: {len(bad)} buffer accesses through a resource held in vector registers"
+
+
+def test_resource_loop_pattern_matches_its_shape():
+    # The shape the compiler emits for a divergent resource (taken from an
+    # earlier build of the chunked prefill), so the pattern above is live.
+    sample = """	v_readfirstlane_b32 s8, v50
+	v_readfirstlane_b32 s9, v51
+	v_readfirstlane_b32 s10, v52
+	v_readfirstlane_b32 s11, v53
+	v_cmp_eq_u64_e64 s[2:3], s[8:9], v[50:51]
+	s_nop 0
+	v_cmp_eq_u64_e64 s[4:5], s[10:11], v[52:53]
+	s_and_b64 s[2:3], s[2:3], s[4:5]
+	s_and_saveexec_b64 s[2:3], s[2:3]
+	buffer_load_dwordx2 v[64:65], v41, s[8:11], 0 offen
+	s_xor_b64 exec, exec, s[2:3]
+	s_cbranch_execnz .LBB0_117
+"""
+    assert len(RESOURCE_LOOP.findall(sample)) == 1
