@@ -13,7 +13,8 @@
 //                       prefill of kda_prefill_impl.h (chunk 64);
 //   [P H, (P + S) H)    one (speculating sequence, head) each: the fused
 //                       commit + verify of kda_verify_impl.h with 16 value
-//                       columns per wave;
+//                       columns per wave, its first group's preparation
+//                       ahead of the replay;
 //   the rest            decode items ((sequence, head) pairs), taken by
 //                       groups of dv / 32 waves (32 value columns per wave,
 //                       the decode kernel's lane mapping), several items per
@@ -284,7 +285,7 @@ __global__ void __launch_bounds__(4 * DV) mixed_kernel(MixedArgs<TIn> a) {
       if (s.ok && s.n > 0) prefill_seq<DK, DV, kMixedChunk, TIn, false>(a.pf, smem, s.b, h, s.sb, (size_t)s.s0, s.n);
       return;
     }
-    verify_seq<DK, DV, TIn, true, true, false, true>(a.vf, *reinterpret_cast<VerifyLds<DK>*>(smem), s.b, h, s.sb,
+    verify_seq<DK, DV, TIn, true, true, false, true, true>(a.vf, *reinterpret_cast<VerifyLds<DK>*>(smem), s.b, h, s.sb,
                                                      (size_t)s.s0 * H + h, (size_t)s.b * a.vf.Tmax * H + h,
                                                      max(s.n, 1), s.n);
     return;

@@ -14,7 +14,9 @@
 namespace kda {
 namespace {
 
-template <int DK, int DV, typename TIn, bool MULTI, bool COMMIT, bool PREP, bool PF>
+// EARLY (fused round only): the first verify group's preparation runs ahead
+// of the replay (verify_seq).
+template <int DK, int DV, typename TIn, bool MULTI, bool COMMIT, bool PREP, bool PF, bool EARLY>
 __global__ void __launch_bounds__(kWave * DV / (kRowGroups * (PF ? 2 : 4))) verify_chunk_kernel(VerifyArgs<TIn> a) {
   __shared__ __align__(16) VerifyLds<DK> L;
   const int bh = blockIdx.x;
@@ -40,7 +42,7 @@ __global__ void __launch_bounds__(kWave * DV / (kRowGroups * (PF ? 2 : 4))) veri
       Tv = d;
     }
   }
-  verify_seq<DK, DV, TIn, MULTI, COMMIT, PREP, PF>(a, L, b, h, sb, (size_t)b * T * a.H + h,
+  verify_seq<DK, DV, TIn, MULTI, COMMIT, PREP, PF, EARLY>(a, L, b, h, sb, (size_t)b * T * a.H + h,
                                                    (size_t)b * a.Tmax * a.H + h, T, Tv);
 }
 
@@ -54,23 +56,39 @@ __global__ void __launch_bounds__(kWave * DV / (kRowGroups * (PF ? 2 : 4))) veri
 #define KDA_LATENCY_PAIRS 512
 #endif
 constexpr int kLatencyPairs = KDA_LATENCY_PAIRS;
+// The fused round runs its first verify group's preparation ahead of the
+// replay when the whole launch fits at two waves per SIMD (256 CUs x 4 SIMDs
+// x 2): the registers that work holds through the replay then cost no
+// occupancy, and the preparation's loads and LDS work leave the chain.
+#ifndef KDA_EARLY_WAVES
+#define KDA_EARLY_WAVES (2 * 4 * 256)
+#endif
+constexpr int kEarlyWaves = KDA_EARLY_WAVES;
 
 template <int DK, int DV, typename TIn, bool COMMIT, bool PREP>
 void launch_cfg(const VerifyArgs<TIn>& a, int32_t B, hipStream_t st) {
   const dim3 grid(B * a.H);
-  auto go = [&](auto pf) {
-    constexpr bool PF = decltype(pf)::value;
+  const bool pf_shape = B * a.H < kLatencyPairs;
+  const bool early = COMMIT && (int64_t)B * a.H * (DV / (kRowGroups * (pf_shape ? 2 : 4))) <= kEarlyWaves;
+  auto go = [&](auto pf, auto ea) {
+    constexpr bool PF = decltype(pf)::value, EA = decltype(ea)::value;
     const dim3 block(kWave * DV / (kRowGroups * (PF ? 2 : 4)));
     if (a.T <= kGroup)
-      verify_chunk_kernel<DK, DV, TIn, false, COMMIT, PREP, PF><<<grid, block, 0, st>>>(a);
+      verify_chunk_kernel<DK, DV, TIn, false, COMMIT, PREP, PF, EA><<<grid, block, 0, st>>>(a);
     else
-      verify_chunk_kernel<DK, DV, TIn, true, COMMIT, PREP, PF><<<grid, block, 0, st>>>(a);
+      verify_chunk_kernel<DK, DV, TIn, true, COMMIT, PREP, PF, EA><<<grid, block, 0, st>>>(a);
   };
-  if (B * a.H < kLatencyPairs) {
-    go(std::true_type{});
+  auto go_ea = [&](auto pf) {
+    if (COMMIT && early)
+      go(pf, std::true_type{});
+    else
+      go(pf, std::false_type{});
+  };
+  if (pf_shape) {
+    go_ea(std::true_type{});
     return;
   }
-  go(std::false_type{});
+  go_ea(std::false_type{});
 }
 
 template <typename TIn, bool COMMIT, bool PREP>

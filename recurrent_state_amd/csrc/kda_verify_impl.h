@@ -232,6 +232,11 @@ struct Streams {
   }
 };
 
+// A no-op for verify_group's `before_barrier` hook.
+struct NoHook {
+  __device__ __forceinline__ void operator()() const {}
+};
+
 // One group of G <= kGroup tokens starting at token t0, from the state tile S
 // (rows [R rg, R rg + R) of this lane, columns col0 .. col0 + 3).  MULTI with
 // advance: advance S to the state after the group (not needed after the last
@@ -239,11 +244,17 @@ struct Streams {
 // projections and logits; they are prepared here (unit q and k, decay and
 // beta from their logits, as the decode step from raw projections does) and
 // logged raw.
-template <int DK, int DV, typename TIn, bool MULTI, bool PREP, int NC, typename LoadState>
+// EARLY: before_barrier() runs between the group's preparation and the
+// barrier that ends it, and the group's log rows are written after that
+// barrier (the fused round replays the pending rows there, from the same
+// log, while the preparation's loads and LDS work are in flight).
+template <int DK, int DV, typename TIn, bool MULTI, bool PREP, int NC, bool EARLY = false, typename LoadState,
+          typename Hook = NoHook>
 __device__ __forceinline__ void verify_group(const VerifyArgs<TIn>& a, const Streams<TIn, DK, DV>& st,
                                              VerifyLds<DK>& L, float (&S)[DK / kRowGroups][NC], int t0, int G,
                                              size_t tok0, size_t tok0_log, int lane, int wave, bool first,
-                                             const LoadState& load_state, bool advance) {
+                                             const LoadState& load_state, bool advance,
+                                             const Hook& before_barrier = Hook()) {
   constexpr int NW = DV / (kRowGroups * NC);  // waves: each owns 8 NC value columns
   constexpr int QW = (kGroup + NW - 1) / NW;    // preparation tokens per wave
   constexpr int R = DK / kRowGroups;
@@ -305,6 +316,9 @@ __device__ __forceinline__ void verify_group(const VerifyArgs<TIn>& a, const Str
     }
   }
   if (MULTI && !first) __syncthreads();  // the previous group's LDS reads are done
+  // This wave's tokens' k and alpha as stored, kept for a deferred log write.
+  Chan<TIn, CPL> kt_log[EARLY ? QW : 1];
+  Chan<float, CPL> at_log[EARLY ? QW : 1];
 #pragma unroll
   for (int j = 0; j < QW; ++j) {
     const int t = wave + j * NW;
@@ -329,8 +343,13 @@ __device__ __forceinline__ void verify_group(const VerifyArgs<TIn>& a, const Str
       for (int c = 0; c < CPL; ++c) q2 = __builtin_fmaf(qt[c], qt[c], q2);
       qnt = inv_norm(lane_group_sum<64>(q2));
     }
-    kt.store(st.log_k, kvo_in, tt * st.sk_in);
-    at.store(st.log_alpha, kvo_f32, tt * st.sk_f32);
+    if constexpr (EARLY) {
+      kt_log[j] = kt;
+      at_log[j] = at;
+    } else {
+      kt.store(st.log_k, kvo_in, tt * st.sk_in);
+      at.store(st.log_alpha, kvo_f32, tt * st.sk_f32);
+    }
     float pA[kGroup], pP[kGroup];
 #pragma unroll
     for (int s = 0; s < kGroup; ++s) pA[s] = pP[s] = 0.f;
@@ -385,7 +404,22 @@ __device__ __forceinline__ void verify_group(const VerifyArgs<TIn>& a, const Str
       L.gend[VerifyLds<DK>::at(ch0 + c)] = gam;
     }
   }
+  if constexpr (EARLY) {
+    before_barrier();
+    __syncthreads();  // every wave has replayed the pending rows: the log can be rewritten
+#pragma unroll
+    for (int j = 0; j < QW; ++j) {
+      const int t = wave + j * NW;
+      if (t < G) {
+        kt_log[j].store(st.log_k, kvo_in, (t0 + t) * st.sk_in);
+        at_log[j].store(st.log_alpha, kvo_f32, (t0 + t) * st.sk_f32);
+      }
+    }
+  }
   // Log of v (this wave's columns; row group r writes token r) and beta.
+  // (Written out here, not in a helper taking the arrays by reference: the
+  // compiler would move such an array to LDS and wait for its loads before
+  // issuing the state tile's.)
 #pragma unroll
   for (int r = 0; r < kGroup; ++r)
     if (r < G && rg == r) vv[r].store(st.log_v, vvo_in, (t0 + r) * st.sv_in);
@@ -396,7 +430,7 @@ __device__ __forceinline__ void verify_group(const VerifyArgs<TIn>& a, const Str
       if (lane == r) bl = bt[r];
     a.log_beta[tok0_log + (size_t)(t0 + lane) * a.H] = bl;
   }
-  __syncthreads();
+  if constexpr (!EARLY) __syncthreads();
 
   // ---- 2. projections x_t = S0^T kap_t, y_t = S0^T rho_t -----------------
   // Row blocks outermost: each block of four state rows is used by every
@@ -500,7 +534,7 @@ __device__ __forceinline__ void verify_group(const VerifyArgs<TIn>& a, const Str
 // of the log; the state and position are entry sb; bh = b H + h indexes
 // the log's records.  With COMMIT the accepted prefix of the pending verify
 // is replayed first; then the Tv tokens are verified and logged.
-template <int DK, int DV, typename TIn, bool MULTI, bool COMMIT, bool PREP, bool PF>
+template <int DK, int DV, typename TIn, bool MULTI, bool COMMIT, bool PREP, bool PF, bool EARLY = false>
 __device__ __forceinline__ void verify_seq(const VerifyArgs<TIn>& a, VerifyLds<DK>& L, int b, int h, int sb,
                                            size_t tok0, size_t tok0_log, int T_span, int Tv) {
   constexpr int R = DK / kRowGroups;
@@ -539,16 +573,32 @@ __device__ __forceinline__ void verify_seq(const VerifyArgs<TIn>& a, VerifyLds<D
         n = 0;
       }
     }
-    if constexpr (PF)
-      rp.run(S, n, a.pend_gate_sign);
-    else
-      replay_log<DK, DV, TIn, R, PREP>(S, a.log_k, a.log_v, a.log_alpha, a.log_beta, tok0_log, a.H, n, row0, col0,
-                                       a.pend_gate_sign);
-    if (n > 0) {
+    auto commit = [&]() {
+      if constexpr (PF)
+        rp.run(S, n, a.pend_gate_sign);
+      else
+        replay_log<DK, DV, TIn, R, PREP>(S, a.log_k, a.log_v, a.log_alpha, a.log_beta, tok0_log, a.H, n, row0, col0,
+                                         a.pend_gate_sign);
+      if (n > 0) {
 #pragma unroll
-      for (int r = 0; r < R; ++r) store_cols<NC, kStateStoreAux>(S[r], rs, svo, r * DV * 4);
-      if (h == 0 && wave == 0 && lane == 0) a.pos[sb] += n;
+        for (int r = 0; r < R; ++r) store_cols<NC, kStateStoreAux>(S[r], rs, svo, r * DV * 4);
+        if (h == 0 && wave == 0 && lane == 0) a.pos[sb] += n;
+      }
+    };
+    if (EARLY && Tv > 0) {
+      // The first group's preparation (its input loads and LDS work) goes
+      // ahead of the replay; the group's barrier then orders every wave's
+      // reads of the pending rows and count before the group rewrites them.
+      verify_group<DK, DV, TIn, MULTI, PREP, NC, true>(a, st, L, S, 0, min(kGroup, Tv), tok0, tok0_log, lane, wave,
+                                                      true, no_load, MULTI && kGroup < Tv, commit);
+      if (threadIdx.x == 0) a.log_len[bh] = log_record(Tv, PREP ? kLogRaw + a.gate : kLogPrepared);
+      if constexpr (MULTI)
+        for (int t0 = kGroup; t0 < Tv; t0 += kGroup)
+          verify_group<DK, DV, TIn, true, PREP, NC>(a, st, L, S, t0, min(kGroup, Tv - t0), tok0, tok0_log, lane, wave,
+                                                    false, no_load, t0 + kGroup < Tv);
+      return;
     }
+    commit();
     if (a.T_pend > 0) __syncthreads();  // every wave has read the pending log rows and count before the verify rewrites them
   }
   if (threadIdx.x == 0) a.log_len[bh] = log_record(Tv, PREP ? kLogRaw + a.gate : kLogPrepared);

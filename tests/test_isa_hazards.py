@@ -15,6 +15,12 @@ distinct resources in the wave: readfirstlane, compare, exec mask, access.
 Such loops once sat around every input load and output store of the chunked
 prefill's chunk loop (1.83 against 1.58 ms without them); the second test
 finds none in any kernel.
+
+A private array whose address escapes (say, into a lambda that captures it
+by reference) can be moved by the compiler into LDS; the verify kernels once
+waited for such an array's loads before issuing their state tile (verify at
+B = 64 30.5 against 39.5 us).  The third test holds every verify kernel to
+exactly the LDS it declares.
 """
 
 from __future__ import annotations
@@ -87,3 +93,22 @@ def test_resource_loop_pattern_matches_its_shape():
 	s_cbranch_execnz .LBB0_117
 """
     assert len(RESOURCE_LOOP.findall(sample)) == 1
+
+
+# Declared LDS of a verify workgroup (VerifyLds<DK>): three token vectors and
+# the group-end decay of 8 row groups x (R + 4) floats each, plus two 4 x 4
+# float blocks.
+def _verify_lds(dk):
+    r = dk // 8
+    vec = 8 * (r + 4)
+    return 4 * (3 * 4 * vec + vec + 2 * 16)
+
+
+def test_verify_kernels_use_only_their_declared_lds(asm):
+    text = asm["kda_verify.hip"]
+    found = re.findall(r"\.amdhsa_kernel (_ZN3kda12_GLOBAL__N_119verify_chunk_kernelILi(\d+)\S*)\n(.*?)\.end_amdhsa_kernel",
+                       text, flags=re.S)
+    assert len(found) >= 32
+    for name, dk, body in found:
+        lds = int(re.search(r"\.amdhsa_group_segment_fixed_size (\d+)", body).group(1))
+        assert lds == _verify_lds(int(dk)), f"{name}: {lds} bytes of LDS, {_verify_lds(int(dk))} declared"
