@@ -397,7 +397,6 @@ __device__ __forceinline__ void prefill_seq(const PrefillArgs<TIn>& a, char* sme
     asm volatile("" : "+v"(tid));
     const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l16 = lane & 15, g = lane >> 4;
-    const int col = 16 * CT * wave + l16;  // this lane's value column in its first tile
     int n = n_next;  // valid tokens in this chunk (cut short below if a decay is too strong); rows n.. are padding
     const size_t row0 = (tok0 + t_base) * a.H + h;  // [B][L][H] row index of the chunk's first token
     const rsrc_t rs_o = make_rsrc(a.o + row0 * DV, ((n - 1) * rowv + DV) * 4);
@@ -696,12 +695,17 @@ __device__ __forceinline__ void prefill_seq(const PrefillArgs<TIn>& a, char* sme
 #pragma unroll
         for (int r = 0; r < 4; ++r) st[ct][mt][r] *= a0[r];
     }
-    // 4b: X = [Kt; Qt] S~, rows 0..CH-1 = Kt S~, rows CH..2CH-1 = Qt S~.
-    f32x4_t xs[CT][2 * NB];
+    // 4b: X = Kt S~ in the accumulator layout (lane: tokens 16 mt + 4 g + r,
+    // column l16), and Qt S~ transposed into ot: with the state as the first
+    // operand and the Qt plane as the second, lane (g, l16) holds columns
+    // 4 g .. 4 g + 3 of token 16 mt + l16 (an accumulator tile is a valid
+    // operand of either side, transposed), so the outputs leave as one
+    // 16-byte store per token block instead of four 4-byte ones.
+    f32x4_t xs[CT][NB], ot[CT][NB];
 #pragma unroll
     for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
-      for (int mt = 0; mt < 2 * NB; ++mt) xs[ct][mt] = zero4;
+      for (int mt = 0; mt < NB; ++mt) xs[ct][mt] = ot[ct][mt] = zero4;
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
       Op sop[CT];
@@ -709,10 +713,16 @@ __device__ __forceinline__ void prefill_seq(const PrefillArgs<TIn>& a, char* sme
       for (int ct = 0; ct < CT; ++ct) sop[ct] = op_from_tiles(st[ct][2 * kb], st[ct][2 * kb + 1]);
       const int k0_ = 32 * kb + 4 * g;
 #pragma unroll
-      for (int mt = 0; mt < 2 * NB; ++mt) {
+      for (int mt = 0; mt < NB; ++mt) {
         const Op kop = plane_op2(kq_hi, kq_lo, 16 * mt + l16, L::RS_Q, k0_);
 #pragma unroll
         for (int ct = 0; ct < CT; ++ct) xs[ct][mt] = mfma3(kop, sop[ct], xs[ct][mt]);
+      }
+#pragma unroll
+      for (int mt = 0; mt < NB; ++mt) {
+        const Op qop = plane_op2(kq_hi, kq_lo, CH + 16 * mt + l16, L::RS_Q, k0_);
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) ot[ct][mt] = mfma3(sop[ct], qop, ot[ct][mt]);
       }
     }
     __syncthreads();  // the diagonal blocks of M are complete
@@ -752,22 +762,28 @@ __device__ __forceinline__ void prefill_seq(const PrefillArgs<TIn>& a, char* sme
         eop[ct][i / 2] = (i & 1) ? op_from_tiles(xs[ct][i - 1], e) : op_from_tiles(e, zero4);
       }
     }
-    // 4e: O = scale (Qt S~ + P E), stored for the valid tokens.
+    // 4e: O = scale (Qt S~ + P E), transposed like ot: (P E)^T = E^T P^T
+    // takes E's operand as the first factor and the P plane rows as the
+    // second.  Padding tokens (n..CH-1) need no test: their offsets start at
+    // or past the end of rs_o's range, so the buffer unit drops those stores
+    // (a per-lane branch here costs the kernel its registers).  The lane's
+    // offset is laundered so that one register serves every token block.
+    int ovo = (l16 * rowv + 16 * CT * wave + 4 * g) * 4;
+    asm volatile("" : "+v"(ovo));
 #pragma unroll
     for (int mt = 0; mt < NB; ++mt) {
 #pragma unroll
       for (int kb = 0; kb <= mt / 2; ++kb) {
         const Op pop = plane_op2(p_hi, p_lo, 16 * mt + l16, L::RS_C, 32 * kb + 4 * g);
 #pragma unroll
-        for (int ct = 0; ct < CT; ++ct) xs[ct][NB + mt] = mfma3(pop, eop[ct][kb], xs[ct][NB + mt]);
+        for (int ct = 0; ct < CT; ++ct) ot[ct][mt] = mfma3(eop[ct][kb], pop, ot[ct][mt]);
       }
 #pragma unroll
-      for (int ct = 0; ct < CT; ++ct)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int tr = 16 * mt + 4 * g + r;
-          if (tr < n) st_f32(rs_o, a.scale * xs[ct][NB + mt][r], (tr * rowv + col + 16 * ct) * 4, 0);
-        }
+      for (int ct = 0; ct < CT; ++ct) {
+        const float o4[4] = {a.scale * ot[ct][mt][0], a.scale * ot[ct][mt][1], a.scale * ot[ct][mt][2],
+                             a.scale * ot[ct][mt][3]};
+        store_cols<4, 0>(o4, rs_o, ovo, (16 * mt * rowv + 16 * ct) * 4);
+      }
     }
     // 4f: S = Diag(G_{n-1}) S~ + Kb^T E.
 #pragma unroll
