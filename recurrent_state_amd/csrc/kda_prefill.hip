@@ -1,7 +1,9 @@
-// Chunked prompt processing on MFMA: the kernel over a batch of prompts of
-// one length (one workgroup per (sequence, head)) and its launchers.  The
-// chunk algebra and the workgroup's code are in kda_prefill_impl.h, which the
-// mixed-batch kernel shares.
+// Chunked prompt processing on MFMA: the kernels over a batch of prompts of
+// one length (one workgroup per (sequence, head)) and their launchers.  The
+// chunk algebra and the single-role workgroup's code are in
+// kda_prefill_impl.h, which the mixed-batch kernel shares; at chunk 64 and
+// dk = dv = 128 the prepared inputs run on the bit-identical form with
+// separate key and value waves (kda_prefill_ws.h).
 
 #include <hip/hip_runtime.h>
 
@@ -10,6 +12,12 @@
 #include "kda_common.h"
 #include "kda_internal.h"
 #include "kda_prefill_impl.h"
+#include "kda_prefill_ws.h"
+
+// 0 keeps every shape on the single-role kernel.
+#ifndef KDA_PREFILL_WS
+#define KDA_PREFILL_WS 1
+#endif
 
 namespace kda {
 namespace {
@@ -30,6 +38,23 @@ __global__ void __launch_bounds__(DV * 4 / prefill_ct(DV)) prefill_chunked_kerne
   prefill_seq<DK, DV, CH, TIn, PREP>(a, smem, b, h, sb, (size_t)b * a.L, a.L);
 }
 
+// One workgroup of dv / 16 value waves and ws_key_waves(dk) key waves per (sequence, head).
+template <int DK, int DV, int CH, typename TIn>
+__global__ void __launch_bounds__(64 * (DV / 16 + ws_key_waves(DK))) prefill_ws_kernel(PrefillArgs<TIn> a) {
+  __shared__ __align__(16) char smem[SmemWs<DK, CH>::total];
+  const int bh = blockIdx.x;
+  const int b = bh / a.H, h = bh - b * a.H;
+  int sb = b;
+  if (a.state_slots) {
+    sb = a.state_slots[b];
+    if (sb < 0 || sb >= a.n_slots) {  // uniform over the workgroup
+      if (h == 0 && threadIdx.x == 0) atomicOr(a.dev_err, KDA_DEV_ERR_SLOT_ID);
+      return;
+    }
+  }
+  prefill_seq_ws<DK, DV, CH, TIn>(a, smem, b, h, sb, (size_t)b * a.L, a.L);
+}
+
 template <int DK, int DV, typename TIn>
 hipError_t launch_cfg(const kda_shape& s, int32_t L, int32_t chunk, float* state, int64_t* pos, TokenInputs in,
                       float* o, int32_t ckpt_every, const int32_t* ckpt_slots, float* slot_states, int64_t* slot_pos,
@@ -40,6 +65,12 @@ hipError_t launch_cfg(const kda_shape& s, int32_t L, int32_t chunk, float* state
   const dim3 grid((unsigned)((size_t)s.B * s.H));
   auto go = [&](auto prep) {
     constexpr bool PREP = decltype(prep)::value;
+    if constexpr (KDA_PREFILL_WS && !PREP && DK == 128 && DV == 128) {
+      if (chunk == 64) {
+        prefill_ws_kernel<DK, DV, 64, TIn><<<grid, 64 * (DV / 16 + ws_key_waves(DK)), 0, st>>>(a);
+        return;
+      }
+    }
     if (chunk == 64)
       prefill_chunked_kernel<DK, DV, 64, TIn, PREP><<<grid, 4 * DV / prefill_ct(DV), 0, st>>>(a);
     else

@@ -83,12 +83,21 @@ __device__ __forceinline__ f32x4_t mfma3(const Op& a, const Op& b, f32x4_t c) {
 
 __device__ __forceinline__ uint32_t bf16_bits(__bf16 h) { return (uint32_t)__builtin_bit_cast(uint16_t, h); }
 
-// fp32 pair -> packed hi and lo bf16 pairs (round to nearest even both times).
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
+typedef __attribute__((ext_vector_type(2))) float f32x2_t;
+
+// Two fp32 values -> one packed bf16 pair (a in the low half), rounded to
+// nearest even by one packed conversion instruction.
+__device__ __forceinline__ uint32_t cvt2(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){a, b}, bf16x2_t));
+}
+
+// fp32 pair -> packed hi and lo bf16 pairs (round to nearest even both times):
+// hi = bf16(x), lo = bf16(x - hi).  Written with packed conversions (two per
+// pair); converting each value on its own costs twice the instructions.
 __device__ __forceinline__ void split2(float a, float b, uint32_t& hi, uint32_t& lo) {
-  const __bf16 ha = (__bf16)a, hb = (__bf16)b;
-  const __bf16 la = (__bf16)(a - (float)ha), lb = (__bf16)(b - (float)hb);
-  hi = bf16_bits(ha) | (bf16_bits(hb) << 16);
-  lo = bf16_bits(la) | (bf16_bits(lb) << 16);
+  hi = cvt2(a, b);
+  lo = cvt2(a - __uint_as_float(hi << 16), b - __uint_as_float(hi & 0xffff0000u));
 }
 
 __device__ __forceinline__ __bf16 split_hi(float x, __bf16& lo) {
@@ -99,16 +108,13 @@ __device__ __forceinline__ __bf16 split_hi(float x, __bf16& lo) {
 
 // B operand from two stacked D tiles (rows 0..15 and 16..31 of a k block).
 __device__ __forceinline__ Op op_from_tiles(const f32x4_t& t0, const f32x4_t& t1) {
-  Op o;
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    __bf16 l0, l1;
-    o.hi[e] = split_hi(t0[e], l0);
-    o.hi[4 + e] = split_hi(t1[e], l1);
-    o.lo[e] = l0;
-    o.lo[4 + e] = l1;
-  }
-  return o;
+  uint32_t h0, h1, h2, h3, l0, l1, l2, l3;
+  split2(t0[0], t0[1], h0, l0);
+  split2(t0[2], t0[3], h1, l1);
+  split2(t1[0], t1[1], h2, l2);
+  split2(t1[2], t1[3], h3, l3);
+  const u32x4_t h = {h0, h1, h2, h3}, l = {l0, l1, l2, l3};
+  return Op{__builtin_bit_cast(bf16x8_t, h), __builtin_bit_cast(bf16x8_t, l)};
 }
 
 // Storage position of column c in a plane row: inside each 32-wide k block,
