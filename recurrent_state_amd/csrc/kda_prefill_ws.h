@@ -8,34 +8,37 @@
 // is who does the work and when.  The key-side products of a chunk (the
 // cumulative decays, the Kt / Qt / Kh / Kb^T planes, the A and P tiles and
 // the inverses of the diagonal blocks of I + A) do not depend on the state.
-// Four key waves (each owning 32 key channels) build them for chunk c while
-// the value waves (one per 16 state columns, holding the state in
-// registers) finish chunk c - 1, so each SIMD runs one key wave (vector
-// arithmetic and LDS writes) beside two value waves (mostly matrix work).
+// Eight key waves (each owning 16 key channels) build them for chunk c
+// while eight value waves (one per 16 state columns, holding the state in
+// registers) finish chunk c - 1; each SIMD runs two of each, the key waves'
+// vector arithmetic and LDS writes beside the value waves' matrix work.
+// The split keeps both roles within 128 registers (four waves per SIMD)
+// without spills.
 //
 // One period of the loop handles the key side of chunk c and the value
 // side of chunk c - 1; it has four workgroup barriers, and each role does
 // the following between them (the LDS region each step reads or writes is
-// named after the step):
+// named after the step; the default build does all of Kt S~ and (Qt S~)^T
+// in I3 and gives every tile to the key waves):
 //
 //   interval  value waves                          key waves
 //   I1        E and outputs of c - 1 (M, P, beta)  cumulative decay of c, cut vote, alpha_0
 //   I2        state update of c - 1 (Kb^T, G),     chunk length; Kt / Qt planes; Kh into
-//             checkpoint, value loads of c         the P / M region
+//             checkpoint                           the P / M region
 //   I3        S~ = Diag(alpha_0) S; Kt S~, Qt S~   Kb^T, beta, G; A and P tiles (Kh,
-//             (Kt / Qt), first k blocks; one P     Kt / Qt); one diagonal block each, inverted
-//             tile (Kh, Qt)
-//   I4        Kt S~, Qt S~, last k block; its P    A and P tiles into M and P; inverses into M
-//             tile into P
+//             (Kt / Qt); value loads of c          Kt / Qt); one diagonal block each
+//                                                  (key waves 0..3), inverted
+//   I4        (optionally: last k blocks of the    A and P tiles into M and P; inverses into M
+//             products, a P tile)
 //
 // Each region is written only after the barrier that ends its last read of
-// the previous chunk: Kt / Qt (read in I3) are rewritten in I2 of the next
-// period; the P / M region (read in I1) takes Kh in I2 and P / M in I4,
-// after the A / P products have read Kh (I3); Kb^T and its row padding
-// (read in I2) are rewritten in I3.  Each key wave forms and inverts one
-// diagonal block of A in its own part of the fp32 diagonal region, so that
-// needs no barrier.  Both roles run the same number of periods, from values
-// both read from LDS, so their barriers pair up.
+// the previous chunk: Kt / Qt (read in I3 and I4) are rewritten in I2 of
+// the next period; the P / M region (read in I1) takes Kh in I2 and P / M in
+// I4, after the A / P products have read Kh (I3); Kb^T and its row padding
+// (read in I2) are rewritten in I3.  Each of key waves 0..3 forms and
+// inverts one diagonal block of A in its own part of the fp32 diagonal
+// region, so that needs no barrier.  Both roles run the same number of
+// periods, from values both read from LDS, so their barriers pair up.
 
 #pragma once
 
@@ -44,7 +47,7 @@
 // k blocks of the value waves' Kt S~ and (Qt S~)^T products done in I3; the
 // rest run in I4, beside the key waves' write-back.
 #ifndef KDA_PREFILL_WS_XS
-#define KDA_PREFILL_WS_XS 2
+#define KDA_PREFILL_WS_XS 4
 #endif
 
 namespace kda {
@@ -81,15 +84,23 @@ struct SmemWs {
                 "16-byte aligned planes");
 };
 
-// Key waves per workgroup (each owns dk / ws_key_waves key channels).
-constexpr int ws_key_waves(int DK) { return DK / 32; }
+// P tiles formed by each value wave (1), or none (0: the key waves form all).
+#ifndef KDA_PREFILL_WS_VALUE_TILES
+#define KDA_PREFILL_WS_VALUE_TILES 0
+#endif
+// Key channels per key wave.
+#ifndef KDA_PREFILL_WS_KEY_CHANNELS
+#define KDA_PREFILL_WS_KEY_CHANNELS 16
+#endif
+// Key waves per workgroup.
+constexpr int ws_key_waves(int DK) { return DK / KDA_PREFILL_WS_KEY_CHANNELS; }
 
 // Tiles of A and P (chunk 64): entries 0..5 are A's strictly lower blocks
 // (mt, nt), nt < mt; entries 6..15 the P blocks (mt, nt), nt <= mt, in
-// tri_tile order; entries 16..19 A's diagonal blocks.  Value wave v takes
-// entry 16 - NV + v (after its own products, where it has time to spare);
-// key wave kw takes diagonal block 16 + kw and entries kw, kw + NK, ...
-// below 16 - NV.
+// tri_tile order; entries 16..19 A's diagonal blocks.  With value-wave
+// tiles, value wave v takes entry 16 - NV + v; key wave kw takes diagonal
+// block kw (entry 16 + kw) if kw < 4, and entries kw, kw + NK, ... below the
+// value waves' entries.
 __device__ __forceinline__ void ws_tile(int i, bool& is_a, int& mt, int& nt) {
   if (i >= 16) {
     is_a = true;
@@ -123,6 +134,8 @@ __device__ __forceinline__ void prefill_seq_ws(const PrefillArgs<TIn>& a, char* 
   constexpr int SGL = TPL / TPG;  // sub-groups per key lane
   static_assert(TPL % TPG == 0 && 64 % PPW == 0 && NK >= 2, "key-wave mapping");
   typedef SmemWs<DK, CH> L;
+  constexpr int VT = KDA_PREFILL_WS_VALUE_TILES;  // P tiles per value wave (0 or 1)
+  static_assert(VT == 0 || VT == 1, "value-wave tiles");
 
   bf16_t* kq_hi = reinterpret_cast<bf16_t*>(smem + L::off_kq);
   bf16_t* kq_lo = kq_hi + L::KQ_PLANE;
@@ -288,7 +301,7 @@ __device__ __forceinline__ void prefill_seq_ws(const PrefillArgs<TIn>& a, char* 
         x_blocks(0, XS, l16, g);
         // This wave's tile of P.
         pt_v = zero4;
-        {
+        if (VT) {
           bool is_a;
           int mt, nt;
           ws_tile(16 - NV + wave, is_a, mt, nt);
@@ -318,8 +331,8 @@ __device__ __forceinline__ void prefill_seq_ws(const PrefillArgs<TIn>& a, char* 
       }
       __syncthreads();  // B3
       // ---- I4: the rest of Kt S~ and (Qt S~)^T; this wave's tile of P into the P planes ----
-      if (have) {
-        x_blocks(XS, KB, l16, g);
+      if (have) x_blocks(XS, KB, l16, g);
+      if (have && VT) {
         bool is_a;
         int mt, nt;
         ws_tile(16 - NV + wave, is_a, mt, nt);
@@ -525,9 +538,10 @@ __device__ __forceinline__ void prefill_seq_ws(const PrefillArgs<TIn>& a, char* 
       __syncthreads();  // B2
 
       // ---- I3: Kb^T, beta, G; next loads; A and P tiles; diagonal blocks ----
-      constexpr int KT = 16 - NV;  // tiles of the key waves other than the diagonal blocks
+      constexpr int KT = 16 - NV * VT;  // tiles of the key waves other than the diagonal blocks
       static_assert(NV <= 10, "value waves take P tiles only");
-      static_assert(NK == NB, "one diagonal block per key wave");
+      static_assert(NK >= NB, "at most one diagonal block per key wave");
+      const bool has_diag = kw < NB;
       constexpr int MAXT = 1 + (KT + NK - 1) / NK;  // slots per key wave
       f32x4_t at[MAXT];
       float xinv[16];
@@ -559,7 +573,7 @@ __device__ __forceinline__ void prefill_seq_ws(const PrefillArgs<TIn>& a, char* 
         for (int s = 0; s < MAXT; ++s) {
           const int i = s == 0 ? 16 + kw : kw + NK * (s - 1);
           at[s] = zero4;
-          if (s == 0 || i < KT) {
+          if (s == 0 ? has_diag : i < KT) {
             bool is_a;
             int mt, nt;
             ws_tile(i, is_a, mt, nt);
@@ -572,28 +586,30 @@ __device__ __forceinline__ void prefill_seq_ws(const PrefillArgs<TIn>& a, char* 
             }
           }
         }
-        // Diagonal block kw of A (fp32, transposed, into this wave's own part
-        // of the diagonal region) and its inverse: lane cc (every group of 16
-        // lanes does the same) forms column cc by right-looking elimination.
-        {
-          const float bta = __shfl(beta_l, 16 * kw + l16);  // beta of this lane's row token
-          float* aj = adiag + kw * L::DSTRIDE;
+        if (has_diag) {
+          // Diagonal block kw of A (fp32, transposed, into this wave's own part
+          // of the diagonal region) and its inverse: lane cc (every group of 16
+          // lanes does the same) forms column cc by right-looking elimination.
+          {
+            const float bta = __shfl(beta_l, 16 * kw + l16);  // beta of this lane's row token
+            float* aj = adiag + kw * L::DSTRIDE;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) aj[(4 * g + e) * L::RS_D + l16] = 4 * g + e < l16 ? at[0][e] * bta : 0.f;
-        }
-        const int cc = lane & 15;
-        const float* aj = adiag + kw * L::DSTRIDE;
+            for (int e = 0; e < 4; ++e) aj[(4 * g + e) * L::RS_D + l16] = 4 * g + e < l16 ? at[0][e] * bta : 0.f;
+          }
+          const int cc = lane & 15;
+          const float* aj = adiag + kw * L::DSTRIDE;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) xinv[r] = r == cc ? 1.f : 0.f;
+          for (int r = 0; r < 16; ++r) xinv[r] = r == cc ? 1.f : 0.f;
 #pragma unroll
-        for (int i = 0; i < 15; ++i) {
+          for (int i = 0; i < 15; ++i) {
 #pragma unroll
-          for (int q = (i + 1) / 4; q < 4; ++q) {
-            const float4 c4 = *reinterpret_cast<const float4*>(aj + i * L::RS_D + 4 * q);
-            const float cv[4] = {c4.x, c4.y, c4.z, c4.w};
+            for (int q = (i + 1) / 4; q < 4; ++q) {
+              const float4 c4 = *reinterpret_cast<const float4*>(aj + i * L::RS_D + 4 * q);
+              const float cv[4] = {c4.x, c4.y, c4.z, c4.w};
 #pragma unroll
-            for (int e = 0; e < 4; ++e)
-              if (4 * q + e > i) xinv[4 * q + e] = __builtin_fmaf(-cv[e], xinv[i], xinv[4 * q + e]);
+              for (int e = 0; e < 4; ++e)
+                if (4 * q + e > i) xinv[4 * q + e] = __builtin_fmaf(-cv[e], xinv[i], xinv[4 * q + e]);
+            }
           }
         }
       }
@@ -644,7 +660,7 @@ __device__ __forceinline__ void prefill_seq_ws(const PrefillArgs<TIn>& a, char* 
         // of it (lane cc column cc); group q writes rows 4 q .. 4 q + 3.
         const int cc = lane & 15, q = lane >> 4;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
+        for (int e = 0; e < 4 && kw < NB; ++e) {
           float x = xinv[e];
 #pragma unroll
           for (int qq = 1; qq < 4; ++qq)
