@@ -59,8 +59,10 @@ namespace {
 template <int DK, int CH>
 struct SmemWs {
   static constexpr int RS_Q = DK + 16;  // Kt / Qt planes (conflict-free stride, as in Smem)
-  static constexpr int RS_K = DK + 8;   // Kh planes
-  static constexpr int RS_C = CH + 8;   // token-indexed planes (Kb^T, M, P)
+  // Every plane takes the conflict-free row stride (8 mod 16 dwords); the
+  // single-role kernel's layout has room for it only in the Kt / Qt planes.
+  static constexpr int RS_K = DK + 16;  // Kh planes
+  static constexpr int RS_C = CH + 16;  // token-indexed planes (Kb^T, M, P)
   static constexpr int NB = CH / 16;
   static constexpr int KQ_PLANE = 2 * CH * RS_Q;
   static constexpr int KH_PLANE = CH * RS_K;
@@ -77,7 +79,7 @@ struct SmemWs {
   static constexpr int total = off_diag + NB * DSTRIDE * 4;
   // Slots of the misc values (floats; the votes are ints).
   static constexpr int M_BETA = 0, M_GN = CH, M_A0 = CH + DK, M_VOTE = CH + 2 * DK;
-  static_assert(M_VOTE + DK / 32 <= 4 * DK && (RS_C - CH) * 2 == 16, "misc values must fit the Kb^T row padding");
+  static_assert(M_VOTE + DK / 32 <= 4 * DK && (RS_C - CH) * 2 >= 16, "misc values must fit the Kb^T row padding");
   static_assert(total <= 163840, "LDS budget exceeded");
   static_assert(off_kb % 16 == 0 && off_r2 % 16 == 0 && off_diag % 16 == 0 && (KQ_PLANE * 2) % 16 == 0 &&
                     (KB_PLANE * 2) % 16 == 0 && (KH_PLANE * 2) % 16 == 0 && (CC_PLANE * 2) % 16 == 0,
