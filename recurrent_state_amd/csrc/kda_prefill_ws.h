@@ -218,10 +218,17 @@ __device__ __forceinline__ void prefill_seq_ws(const PrefillArgs<TIn>& a, char* 
       // ---- I1: E and the outputs of the previous chunk ----
       if (prev) {
         float vv[NB][4];
+        if (n_prev == CH) {  // no padding rows
 #pragma unroll
-        for (int mt = 0; mt < NB; ++mt)
+          for (int mt = 0; mt < NB; ++mt)
 #pragma unroll
-          for (int r = 0; r < 4; ++r) vv[mt][r] = 16 * mt + 4 * g + r < n_prev ? rv[mt][r].get() : 0.f;
+            for (int r = 0; r < 4; ++r) vv[mt][r] = rv[mt][r].get();
+        } else {
+#pragma unroll
+          for (int mt = 0; mt < NB; ++mt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) vv[mt][r] = 16 * mt + 4 * g + r < n_prev ? rv[mt][r].get() : 0.f;
+        }
 #pragma unroll
         for (int i = 0; i < NB; ++i) {
           const float4 b4 = misc4(L::M_BETA + 16 * i + 4 * g);
@@ -515,27 +522,35 @@ __device__ __forceinline__ void prefill_seq_ws(const PrefillArgs<TIn>& a, char* 
           gn1 = __shfl(e1, src);
         }
         const int pc = kpos(c0);
+        // A full chunk has no padding rows: its copy of the loop drops the tests.
+        auto planes = [&](auto full) {
+          constexpr bool FULL = decltype(full)::value;
 #pragma unroll
-        for (int i = 0; i < TPL; ++i) {
-          const int tr = TPL * j + i;
-          const bool valid = tr < n;
-          const float k0 = valid ? rk[i].lo() : 0.f, k1 = valid ? rk[i].hi() : 0.f;
-          const float q0 = valid ? rq[i].lo() : 0.f, q1 = valid ? rq[i].hi() : 0.f;
-          const float e0 = off0[i / TPG] * g0[i], e1 = off1[i / TPG] * g1[i];  // G of token tr
-          const float ie0 = __builtin_amdgcn_rcpf(e0), ie1 = __builtin_amdgcn_rcpf(e1);
-          uint32_t hi, lo;
-          split2(k0 * e0, k1 * e1, hi, lo);  // Kt
-          *reinterpret_cast<uint32_t*>(kq_hi + tr * L::RS_Q + pc) = hi;
-          *reinterpret_cast<uint32_t*>(kq_lo + tr * L::RS_Q + pc) = lo;
-          split2(q0 * e0, q1 * e1, hi, lo);  // Qt
-          *reinterpret_cast<uint32_t*>(kq_hi + (CH + tr) * L::RS_Q + pc) = hi;
-          *reinterpret_cast<uint32_t*>(kq_lo + (CH + tr) * L::RS_Q + pc) = lo;
-          kh0[i] = valid ? k0 * ie0 : 0.f;  // padding rows: zero (their G may be 0)
-          kh1[i] = valid ? k1 * ie1 : 0.f;
-          split2(kh0[i], kh1[i], hi, lo);  // Kh
-          *reinterpret_cast<uint32_t*>(kh_hi + tr * L::RS_K + pc) = hi;
-          *reinterpret_cast<uint32_t*>(kh_lo + tr * L::RS_K + pc) = lo;
-        }
+          for (int i = 0; i < TPL; ++i) {
+            const int tr = TPL * j + i;
+            const bool valid = FULL || tr < n;
+            const float k0 = valid ? rk[i].lo() : 0.f, k1 = valid ? rk[i].hi() : 0.f;
+            const float q0 = valid ? rq[i].lo() : 0.f, q1 = valid ? rq[i].hi() : 0.f;
+            const float e0 = off0[i / TPG] * g0[i], e1 = off1[i / TPG] * g1[i];  // G of token tr
+            const float ie0 = __builtin_amdgcn_rcpf(e0), ie1 = __builtin_amdgcn_rcpf(e1);
+            uint32_t hi, lo;
+            split2(k0 * e0, k1 * e1, hi, lo);  // Kt
+            *reinterpret_cast<uint32_t*>(kq_hi + tr * L::RS_Q + pc) = hi;
+            *reinterpret_cast<uint32_t*>(kq_lo + tr * L::RS_Q + pc) = lo;
+            split2(q0 * e0, q1 * e1, hi, lo);  // Qt
+            *reinterpret_cast<uint32_t*>(kq_hi + (CH + tr) * L::RS_Q + pc) = hi;
+            *reinterpret_cast<uint32_t*>(kq_lo + (CH + tr) * L::RS_Q + pc) = lo;
+            kh0[i] = valid ? k0 * ie0 : 0.f;  // padding rows: zero (their G may be 0)
+            kh1[i] = valid ? k1 * ie1 : 0.f;
+            split2(kh0[i], kh1[i], hi, lo);  // Kh
+            *reinterpret_cast<uint32_t*>(kh_hi + tr * L::RS_K + pc) = hi;
+            *reinterpret_cast<uint32_t*>(kh_lo + tr * L::RS_K + pc) = lo;
+          }
+        };
+        if (n == CH)
+          planes(std::true_type{});
+        else
+          planes(std::false_type{});
       }
       __syncthreads();  // B2
 
