@@ -117,6 +117,20 @@ __device__ __forceinline__ Op op_from_tiles(const f32x4_t& t0, const f32x4_t& t1
   return Op{__builtin_bit_cast(bf16x8_t, h), __builtin_bit_cast(bf16x8_t, l)};
 }
 
+// op_from_tiles(t0, t1) from op_from_tiles(t0, zero): the t0 half (words
+// 0 and 1 of each part) is taken as it is, only t1 is split.
+__device__ __forceinline__ Op op_with_upper(const Op& lower, const f32x4_t& t1) {
+  u32x4_t h = __builtin_bit_cast(u32x4_t, lower.hi), l = __builtin_bit_cast(u32x4_t, lower.lo);
+  uint32_t h2, h3, l2, l3;
+  split2(t1[0], t1[1], h2, l2);
+  split2(t1[2], t1[3], h3, l3);
+  h[2] = h2;
+  h[3] = h3;
+  l[2] = l2;
+  l[3] = l3;
+  return Op{__builtin_bit_cast(bf16x8_t, h), __builtin_bit_cast(bf16x8_t, l)};
+}
+
 // Storage position of column c in a plane row: inside each 32-wide k block,
 // slot e of lane group g (logical column pi(g, e)) sits at 8 g + e.
 __device__ __forceinline__ int kpos(int c) { return (c & ~31) + 8 * ((c & 15) >> 2) + 4 * ((c & 31) >> 4) + (c & 3); }
@@ -765,7 +779,7 @@ __device__ __forceinline__ void prefill_seq(const PrefillArgs<TIn>& a, char* sme
       for (int ct = 0; ct < CT; ++ct) {
         const f32x4_t e = mfma3(ax, (i & 1) ? op_from_tiles(zero4, z[ct]) : op_from_tiles(z[ct], zero4), zero4);
         xs[ct][i] = e;  // R_i is dead: keep E_i until its k block is complete
-        eop[ct][i / 2] = (i & 1) ? op_from_tiles(xs[ct][i - 1], e) : op_from_tiles(e, zero4);
+        eop[ct][i / 2] = (i & 1) ? op_with_upper(eop[ct][i / 2], e) : op_from_tiles(e, zero4);
       }
     }
     // 4e: O = scale (Qt S~ + P E), transposed like ot: (P E)^T = E^T P^T
