@@ -188,3 +188,56 @@ def test_commit_verify_varlen_graph_replays_match_eager():
         S_ref, o_ref, pos_ref = ref[r - 1]
         assert torch.equal(bits(SB), S_ref) and torch.equal(bits(oB), o_ref) and torch.equal(posB, pos_ref), r
     assert errA.item() == 0 and errB.item() == 0
+
+
+def test_prefill_graph_replays_match_eager():
+    # The chunk-64 prompt at dk = dv = 128 (the wave-specialised kernel: 1,024
+    # threads and 157 KiB of LDS per workgroup) and the chunk-32 one (the
+    # single-role kernel) in one graph, with checkpoints; each replay starts
+    # from the same state, restored eagerly before it.
+    B, L, every = 2, 130, 64
+    say("graph: chunked prefill, chunk 64 and 32")
+    S0 = dev_tensor(synth.initial_state(SPEC, B))
+    d = {k: dev_tensor(v) for k, v in synth.token_inputs(SPEC, B, L).items()}
+    n_ck = L // every
+    ck = torch.arange(B * n_ck, dtype=torch.int32, device="cuda").view(B, n_ck)
+    pos0 = torch.tensor([7, 0], dtype=torch.int64, device="cuda")
+
+    def fresh():
+        return ([S0.clone(), S0.clone()], [pos0.clone(), pos0.clone()],
+                [kda.SlotPool(B * n_ck, SPEC.H, 128, 128, "cuda") for _ in range(2)],
+                [torch.empty((B, L, SPEC.H, 128), device="cuda") for _ in range(2)],
+                torch.zeros(1, dtype=torch.int32, device="cuda"))
+
+    def run(S, pos, pools, outs, err):
+        for i, chunk in enumerate((64, 32)):
+            kda.prefill_chunked(S[i], pos[i], d["q"], d["k"], d["v"], d["alpha"], d["beta"], outs[i], chunk=chunk,
+                                ckpt_every=every, ckpt_slots=ck, pool=pools[i], dev_err=err)
+
+    Se, pe, poolse, oe, erre = fresh()
+    run(Se, pe, poolse, oe, erre)
+    torch.cuda.synchronize()
+    assert erre.item() == 0
+    Sg, pg, poolsg, og, errg = fresh()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        run(Sg, pg, poolsg, og, errg)
+    torch.cuda.synchronize()
+    assert torch.equal(pg[0], pos0), "capture must not run the kernels"
+    for rep in range(3):
+        for i in range(2):
+            Sg[i].copy_(S0)
+            pg[i].copy_(pos0)
+            og[i].fill_(float("nan"))
+            poolsg[i].states.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        junk = torch.randn(1000, device="cuda").cumsum(0)  # unrelated eager work between replays
+        torch.cuda.synchronize()
+        assert junk.numel() == 1000 and errg.item() == 0
+        for i in range(2):
+            assert torch.equal(bits(Sg[i]), bits(Se[i])), f"replay {rep} state (chunk {(64, 32)[i]})"
+            assert torch.equal(bits(og[i]), bits(oe[i])), f"replay {rep} outputs (chunk {(64, 32)[i]})"
+            assert torch.equal(pg[i], pe[i])
+            assert torch.equal(bits(poolsg[i].states), bits(poolse[i].states)), f"replay {rep} checkpoints"
+            assert torch.equal(poolsg[i].pos, poolse[i].pos)
