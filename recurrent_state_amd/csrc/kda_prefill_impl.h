@@ -497,7 +497,7 @@ __device__ __forceinline__ void prefill_seq(const PrefillArgs<TIn>& a, char* sme
         gn1 *= t1;
       }
       // Every wave holds every key channel (CP lanes per token group), so each
-      // wave reaches the same verdict from the same group totals.  G is
+      // wave reaches the same decision from the same group totals.  G is
       // monotone in r, so the whole chunk is safe when G_{n-1} >= kMinDecay in
       // every channel.
       if (__any(gn0 < kMinDecay || gn1 < kMinDecay)) {
