@@ -49,6 +49,12 @@
 #ifndef KDA_PREFILL_WS_XS
 #define KDA_PREFILL_WS_XS 4
 #endif
+// Key waves request a chunk's inputs one period ahead (1) or in its own period
+// (0).  Only for bf16 inputs: fp32 keys and queries take twice the registers
+// and the prefetched form then spills.
+#ifndef KDA_PREFILL_WS_PREFETCH
+#define KDA_PREFILL_WS_PREFETCH 1
+#endif
 
 namespace kda {
 namespace {
@@ -381,20 +387,29 @@ __device__ __forceinline__ void prefill_seq_ws(const PrefillArgs<TIn>& a, char* 
       if (t < ck_end) m = min(m, (t / a.ckpt_every + 1) * a.ckpt_every - t);
       return m;
     };
-    // A chunk's inputs are loaded in its own period, the decays at its start
-    // and the keys and queries once the decays are consumed: the key waves'
-    // part of I1 is short, so both waits hide behind the value waves' solve,
-    // and no input register is live across the loop.
+    // With bf16 inputs a chunk's inputs are requested one period ahead: its
+    // decays and betas in I2 of the chunk before (once that chunk's length is
+    // voted and its decays are consumed), its keys and queries after that
+    // chunk's plane pass, into registers that are free from then on.  The
+    // loads are issued on every path, empty past the last chunk, so the
+    // compiler's wait counts let each wait cover only the loads it needs
+    // (with the requests under a branch, the waits after the join also
+    // covered the requests just issued).  Otherwise the decays are requested
+    // at the start of the chunk's own I1 and the keys and queries once the
+    // decays are consumed.
     // Padding rows lie past the end of the window, where the buffer unit
     // returns zero (their values are replaced anyway).  Each load's lane
     // offset is the previous one plus a row, passed through an opaque copy
     // so that the compiler keeps one offset register instead of sixteen.
+    constexpr bool kWsPrefetch = KDA_PREFILL_WS_PREFETCH && sizeof(TIn) == 2;
     Pair2<float> ra[TPL];
     Pair2<TIn> rk[TPL], rq[TPL];
-    float rb = 0.f;  // beta of token `lane`
-    auto issue_alpha = [&](int t_b, int nn, int lane_) {
+    float rb = 0.f;       // beta of token `lane`
+    float rb_next = 0.f;  // the same for the next chunk (requested a period ahead)
+    auto issue_alpha = [&](int t_b, int nn, int lane_, float& rb_dst) {
       const size_t r0 = (tok0 + t_b) * a.H + h;
-      const rsrc_t wa = make_rsrc(a.alpha + r0 * DK, ((nn - 1) * rowk + DK) * 4);
+      // nn = 0 (past the last chunk): an empty window, every load returns 0.
+      const rsrc_t wa = make_rsrc(a.alpha + r0 * DK, nn > 0 ? ((nn - 1) * rowk + DK) * 4 : 0);
       int vo = (TPL * (lane_ / PPW) * rowk + CPW * kw + 2 * (lane_ % PPW)) * 4;
 #pragma unroll
       for (int i = 0; i < TPL; ++i) {
@@ -403,14 +418,15 @@ __device__ __forceinline__ void prefill_seq_ws(const PrefillArgs<TIn>& a, char* 
         vo += rowk * 4;
       }
       {
-        const rsrc_t wb = make_rsrc(a.beta + r0, ((nn - 1) * a.H + 1) * 4);
-        rb = ld_f32(wb, min(lane_, nn - 1) * a.H * 4, 0);
+        const rsrc_t wb = make_rsrc(a.beta + r0, nn > 0 ? ((nn - 1) * a.H + 1) * 4 : 0);
+        rb_dst = ld_f32(wb, min(lane_, nn - 1) * a.H * 4, 0);
       }
     };
     auto issue_kq = [&](int t_b, int nn, int lane_) {
       const size_t r0 = (tok0 + t_b) * a.H + h;
-      const rsrc_t wk = make_rsrc(a.k + r0 * DK, ((nn - 1) * rowk + DK) * sizeof(TIn));
-      const rsrc_t wq = make_rsrc(a.q + r0 * DK, ((nn - 1) * rowk + DK) * sizeof(TIn));
+      const uint32_t bytes = nn > 0 ? ((nn - 1) * rowk + DK) * sizeof(TIn) : 0;
+      const rsrc_t wk = make_rsrc(a.k + r0 * DK, bytes);
+      const rsrc_t wq = make_rsrc(a.q + r0 * DK, bytes);
       int vo = (TPL * (lane_ / PPW) * rowk + CPW * kw + 2 * (lane_ % PPW)) * (int)sizeof(TIn);
 #pragma unroll
       for (int i = 0; i < TPL; ++i) {
@@ -422,6 +438,10 @@ __device__ __forceinline__ void prefill_seq_ws(const PrefillArgs<TIn>& a, char* 
     };
     int t_k = 0;
     int n_nom = n_tok > 0 ? nominal(0) : 0;  // nominal length of the chunk at t_k
+    if (kWsPrefetch && n_tok > 0) {
+      issue_alpha(0, n_nom, threadIdx.x & 63, rb_next);
+      issue_kq(0, n_nom, threadIdx.x & 63);
+    }
     while (t_k < n_tok) {
       int tid = threadIdx.x;
       asm volatile("" : "+v"(tid));
@@ -433,7 +453,10 @@ __device__ __forceinline__ void prefill_seq_ws(const PrefillArgs<TIn>& a, char* 
       float off0[SGL], off1[SGL];      // decay before each of the lane's sub-groups
       float gn0 = 1.f, gn1 = 1.f;      // G_{n-1} of the two channels
       {
-        issue_alpha(t_k, n_nom, lane);
+        if constexpr (kWsPrefetch)
+          rb = rb_next;
+        else
+          issue_alpha(t_k, n_nom, lane, rb);
         float al0[TPL], al1[TPL];
 #pragma unroll
         for (int i = 0; i < TPL; ++i) {
@@ -499,7 +522,7 @@ __device__ __forceinline__ void prefill_seq_ws(const PrefillArgs<TIn>& a, char* 
           for (int m = 32; m >= 1; m >>= 1) f = min(f, __shfl_xor(f, m));
         }
         if (lane == 0) vote(kw) = f;
-        issue_kq(t_k, n_nom, lane);
+        if constexpr (!kWsPrefetch) issue_kq(t_k, n_nom, lane);
       }
       __syncthreads();  // B1
 
@@ -521,6 +544,14 @@ __device__ __forceinline__ void prefill_seq_ws(const PrefillArgs<TIn>& a, char* 
           gn0 = __shfl(e0, src);
           gn1 = __shfl(e1, src);
         }
+        // The next chunk starts where this one ends: its decays and betas go
+        // out now (ra is free once the decay pass has run), its keys and
+        // queries after the plane pass below.  Past the last chunk the
+        // windows are empty: the loads are issued anyway (they return 0 and
+        // read nothing), so that the wait counts are the same on every path.
+        const int t_next = t_k + n;
+        const int n_next = t_next < n_tok ? nominal(t_next) : 0;
+        if (kWsPrefetch) issue_alpha(t_next, n_next, lane, rb_next);
         const int pc = kpos(c0);
         // A full chunk has no padding rows: its copy of the loop drops the tests.
         auto planes = [&](auto full) {
@@ -551,6 +582,7 @@ __device__ __forceinline__ void prefill_seq_ws(const PrefillArgs<TIn>& a, char* 
           planes(std::true_type{});
         else
           planes(std::false_type{});
+        if (kWsPrefetch) issue_kq(t_next, n_next, lane);
       }
       __syncthreads();  // B2
 
