@@ -3,7 +3,8 @@
 // chunk algebra and the single-role workgroup's code are in
 // kda_prefill_impl.h, which the mixed-batch kernel shares; at chunk 64 and
 // dk = dv = 128 the prepared inputs run on the bit-identical form with
-// separate key and value waves (kda_prefill_ws.h).
+// separate key and value waves (kda_prefill_ws.h), and so do bf16 raw
+// projections.
 
 #include <hip/hip_runtime.h>
 
@@ -17,6 +18,10 @@
 // 0 keeps every shape on the single-role kernel.
 #ifndef KDA_PREFILL_WS
 #define KDA_PREFILL_WS 1
+#endif
+// 0 keeps raw projections on the single-role kernel.
+#ifndef KDA_PREFILL_WS_PREP
+#define KDA_PREFILL_WS_PREP 1
 #endif
 
 namespace kda {
@@ -39,7 +44,7 @@ __global__ void __launch_bounds__(DV * 4 / prefill_ct(DV)) prefill_chunked_kerne
 }
 
 // One workgroup of dv / 16 value waves and ws_key_waves(dk) key waves per (sequence, head).
-template <int DK, int DV, int CH, typename TIn>
+template <int DK, int DV, int CH, typename TIn, bool PREP>
 __global__ void __launch_bounds__(64 * (DV / 16 + ws_key_waves(DK))) prefill_ws_kernel(PrefillArgs<TIn> a) {
   __shared__ __align__(16) char smem[SmemWs<DK, CH>::total];
   const int bh = blockIdx.x;
@@ -52,7 +57,7 @@ __global__ void __launch_bounds__(64 * (DV / 16 + ws_key_waves(DK))) prefill_ws_
       return;
     }
   }
-  prefill_seq_ws<DK, DV, CH, TIn>(a, smem, b, h, sb, (size_t)b * a.L, a.L);
+  prefill_seq_ws<DK, DV, CH, TIn, PREP>(a, smem, b, h, sb, (size_t)b * a.L, a.L);
 }
 
 template <int DK, int DV, typename TIn>
@@ -65,9 +70,12 @@ hipError_t launch_cfg(const kda_shape& s, int32_t L, int32_t chunk, float* state
   const dim3 grid((unsigned)((size_t)s.B * s.H));
   auto go = [&](auto prep) {
     constexpr bool PREP = decltype(prep)::value;
-    if constexpr (KDA_PREFILL_WS && !PREP && DK == 128 && DV == 128) {
+    // Raw projections run on it for bf16 inputs (the form that requests a
+    // chunk's inputs a period ahead); fp32 raw projections keep the
+    // single-role kernel.
+    if constexpr (KDA_PREFILL_WS && DK == 128 && DV == 128 && (!PREP || (KDA_PREFILL_WS_PREP && sizeof(TIn) == 2))) {
       if (chunk == 64) {
-        prefill_ws_kernel<DK, DV, 64, TIn><<<grid, 64 * (DV / 16 + ws_key_waves(DK)), 0, st>>>(a);
+        prefill_ws_kernel<DK, DV, 64, TIn, PREP><<<grid, 64 * (DV / 16 + ws_key_waves(DK)), 0, st>>>(a);
         return;
       }
     }

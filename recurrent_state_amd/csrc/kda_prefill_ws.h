@@ -4,7 +4,11 @@
 // The chunk algebra is the one of kda_prefill_impl.h, operation for
 // operation: every product, split and sum below is formed from the same
 // operands in the same order, so this kernel's outputs, states and
-// checkpoints are bit-identical to the single-role kernel's.  What changes
+// checkpoints are bit-identical to the single-role kernel's.  (Raw
+// projections, bf16 inputs only, are prepared by the key waves: each sums
+// its 16 channels' part of a token's squared norms and the eight parts are
+// added after the first barrier, an order the single-role kernel's full-wave
+// sums do not share, so that form agrees with it to rounding.)  What changes
 // is who does the work and when.  The key-side products of a chunk (the
 // cumulative decays, the Kt / Qt / Kh / Kb^T planes, the A and P tiles and
 // the inverses of the diagonal blocks of I + A) do not depend on the state.
@@ -123,9 +127,40 @@ __device__ __forceinline__ void ws_tile(int i, bool& is_a, int& mt, int& nt) {
   }
 }
 
+// Sum over aligned groups of 8 lanes, every lane of a group getting it:
+// partners lane ^ 1 and lane ^ 2 (quad permutes), then the other quad of the
+// group (half-row mirror).
+__device__ __forceinline__ float lane8_sum(float x) {
+  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0xb1, 0xf, 0xf, false));
+  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x4e, 0xf, 0xf, false));
+  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x141, 0xf, 0xf, false));
+  return x;
+}
+
+// Lane i of each aligned group of 8 lanes, to every lane of the group
+// (ds_swizzle bit mode: source lane (lane & 0x18) | i of each 32-lane half).
+// i must fold to a constant.
+__device__ __forceinline__ float lane8_bcast(float x, int i) {
+  const int v = __builtin_bit_cast(int, x);
+  int r;
+  switch (i & 7) {
+    case 0: r = __builtin_amdgcn_ds_swizzle(v, 0x18 | (0 << 5)); break;
+    case 1: r = __builtin_amdgcn_ds_swizzle(v, 0x18 | (1 << 5)); break;
+    case 2: r = __builtin_amdgcn_ds_swizzle(v, 0x18 | (2 << 5)); break;
+    case 3: r = __builtin_amdgcn_ds_swizzle(v, 0x18 | (3 << 5)); break;
+    case 4: r = __builtin_amdgcn_ds_swizzle(v, 0x18 | (4 << 5)); break;
+    case 5: r = __builtin_amdgcn_ds_swizzle(v, 0x18 | (5 << 5)); break;
+    case 6: r = __builtin_amdgcn_ds_swizzle(v, 0x18 | (6 << 5)); break;
+    default: r = __builtin_amdgcn_ds_swizzle(v, 0x18 | (7 << 5)); break;
+  }
+  return __builtin_bit_cast(float, r);
+}
+
 // The whole prompt of one (sequence, head), run by one workgroup of
 // 64 (dv / 16 + ws_key_waves(dk)) lanes; arguments as for prefill_seq.
-template <int DK, int DV, int CH, typename TIn>
+// PREP (bf16 inputs only): raw projections and logits, prepared by the key
+// waves (see the key role).
+template <int DK, int DV, int CH, typename TIn, bool PREP = false>
 __device__ __forceinline__ void prefill_seq_ws(const PrefillArgs<TIn>& a, char* smem, int b, int h, int sb,
                                                size_t tok0, int n_tok) {
   static_assert(DK == 128 && CH == 64 && DV % 16 == 0, "shape");
@@ -163,6 +198,11 @@ __device__ __forceinline__ void prefill_seq_ws(const PrefillArgs<TIn>& a, char* 
     return *reinterpret_cast<const float4*>(smem + L::off_kb + (v >> 2) * (L::RS_C * 2) + CH * 2);
   };
   auto vote = [&](int kw) -> int& { return *reinterpret_cast<int*>(&misc(L::M_VOTE + kw)); };
+  // The key waves' parts of a token's squared norm (raw projections): one
+  // float per key wave in the row padding of the Kt (row t: k of token t) or
+  // Qt (row CH + t: q) hi plane, which no product reads.
+  static_assert((L::RS_Q - DK) * 2 >= NK * 4 && (L::RS_Q * 2) % 16 == 0 && (DK * 2) % 16 == 0, "norm parts");
+  auto norm_part = [&](int row) -> float* { return reinterpret_cast<float*>(kq_hi + row * L::RS_Q + DK); };
   // The chunk length agreed after the votes (every wave reads the same four).
   auto voted_length = [&]() {
     int n = vote(0);
@@ -401,7 +441,14 @@ __device__ __forceinline__ void prefill_seq_ws(const PrefillArgs<TIn>& a, char* 
     // returns zero (their values are replaced anyway).  Each load's lane
     // offset is the previous one plus a row, passed through an opaque copy
     // so that the compiler keeps one offset register instead of sixteen.
-    constexpr bool kWsPrefetch = KDA_PREFILL_WS_PREFETCH && sizeof(TIn) == 2;
+    // kPfKQ: keys and queries a period ahead; kPfA: decays and betas too.
+    // Raw projections need a chunk's keys and queries at the start of its I1
+    // (their norms), so they run only with kPfKQ; their decays are requested
+    // at the start of I1, where the norm parts are formed while they arrive
+    // (held from I2 on, they pushed the key role past 128 registers).
+    constexpr bool kPfKQ = KDA_PREFILL_WS_PREFETCH && sizeof(TIn) == 2;
+    constexpr bool kPfA = kPfKQ && !PREP;
+    static_assert(!PREP || (kPfKQ && NK == 8 && PPW == TPL), "raw projections on the key waves");
     Pair2<float> ra[TPL];
     Pair2<TIn> rk[TPL], rq[TPL];
     float rb = 0.f;       // beta of token `lane`
@@ -438,10 +485,8 @@ __device__ __forceinline__ void prefill_seq_ws(const PrefillArgs<TIn>& a, char* 
     };
     int t_k = 0;
     int n_nom = n_tok > 0 ? nominal(0) : 0;  // nominal length of the chunk at t_k
-    if (kWsPrefetch && n_tok > 0) {
-      issue_alpha(0, n_nom, threadIdx.x & 63, rb_next);
-      issue_kq(0, n_nom, threadIdx.x & 63);
-    }
+    if (kPfA && n_tok > 0) issue_alpha(0, n_nom, threadIdx.x & 63, rb_next);
+    if (kPfKQ && n_tok > 0) issue_kq(0, n_nom, threadIdx.x & 63);
     while (t_k < n_tok) {
       int tid = threadIdx.x;
       asm volatile("" : "+v"(tid));
@@ -453,7 +498,7 @@ __device__ __forceinline__ void prefill_seq_ws(const PrefillArgs<TIn>& a, char* 
       float off0[SGL], off1[SGL];      // decay before each of the lane's sub-groups
       float gn0 = 1.f, gn1 = 1.f;      // G_{n-1} of the two channels
       {
-        if constexpr (kWsPrefetch)
+        if constexpr (kPfA)
           rb = rb_next;
         else
           issue_alpha(t_k, n_nom, lane, rb);
@@ -461,8 +506,35 @@ __device__ __forceinline__ void prefill_seq_ws(const PrefillArgs<TIn>& a, char* 
 #pragma unroll
         for (int i = 0; i < TPL; ++i) {
           const bool pad = TPL * j + i >= n_nom;
-          al0[i] = pad ? 1.f : ra[i].lo();  // padding tokens do not decay
-          al1[i] = pad ? 1.f : ra[i].hi();
+          float x0 = ra[i].lo(), x1 = ra[i].hi();
+          if constexpr (PREP) {
+            x0 = sigmoid_f32(a.gate_sign * x0);
+            x1 = sigmoid_f32(a.gate_sign * x1);
+          }
+          al0[i] = pad ? 1.f : x0;  // padding tokens do not decay
+          al1[i] = pad ? 1.f : x1;
+        }
+        if constexpr (PREP) {
+          // This wave's part (its 16 key channels) of the squared norms of
+          // each token's k and q; lane p of token group j writes token
+          // TPL j + p's into the row padding of the Kt / Qt hi planes, and
+          // every wave sums the eight parts after the barrier.
+          float sk[TPL], sq[TPL];
+#pragma unroll
+          for (int i = 0; i < TPL; ++i) {
+            const float k0 = rk[i].lo(), k1 = rk[i].hi(), q0 = rq[i].lo(), q1 = rq[i].hi();
+            sk[i] = lane8_sum(__builtin_fmaf(k0, k0, k1 * k1));
+            sq[i] = lane8_sum(__builtin_fmaf(q0, q0, q1 * q1));
+          }
+          float mk = sk[0], mq = sq[0];
+#pragma unroll
+          for (int i = 1; i < TPL; ++i)
+            if (p_ == i) {
+              mk = sk[i];
+              mq = sq[i];
+            }
+          norm_part(TPL * j + p_)[kw] = mk;
+          norm_part(CH + TPL * j + p_)[kw] = mq;
         }
         // Token 0's decay goes into S~ = Diag(alpha_0) S, not into G.
         if (j == 0) {
@@ -522,7 +594,7 @@ __device__ __forceinline__ void prefill_seq_ws(const PrefillArgs<TIn>& a, char* 
           for (int m = 32; m >= 1; m >>= 1) f = min(f, __shfl_xor(f, m));
         }
         if (lane == 0) vote(kw) = f;
-        if constexpr (!kWsPrefetch) issue_kq(t_k, n_nom, lane);
+        if constexpr (!kPfKQ) issue_kq(t_k, n_nom, lane);
       }
       __syncthreads();  // B1
 
@@ -551,7 +623,19 @@ __device__ __forceinline__ void prefill_seq_ws(const PrefillArgs<TIn>& a, char* 
         // read nothing), so that the wait counts are the same on every path.
         const int t_next = t_k + n;
         const int n_next = t_next < n_tok ? nominal(t_next) : 0;
-        if (kWsPrefetch) issue_alpha(t_next, n_next, lane, rb_next);
+        // Lane p forms 1 / |k| and 1 / |q| of token TPL j + p from the eight
+        // waves' parts (PREP); the plane pass takes each token's pair from the
+        // lane that holds it, as it reaches the token.
+        float ik = 0.f, iq = 0.f;
+        if constexpr (PREP) {
+          const float4 a0 = *reinterpret_cast<const float4*>(norm_part(TPL * j + p_));
+          const float4 a1 = *reinterpret_cast<const float4*>(norm_part(TPL * j + p_) + 4);
+          const float4 b0 = *reinterpret_cast<const float4*>(norm_part(CH + TPL * j + p_));
+          const float4 b1 = *reinterpret_cast<const float4*>(norm_part(CH + TPL * j + p_) + 4);
+          ik = inv_norm(((a0.x + a0.y) + (a0.z + a0.w)) + ((a1.x + a1.y) + (a1.z + a1.w)));
+          iq = inv_norm(((b0.x + b0.y) + (b0.z + b0.w)) + ((b1.x + b1.y) + (b1.z + b1.w)));
+        }
+        if (kPfA) issue_alpha(t_next, n_next, lane, rb_next);
         const int pc = kpos(c0);
         // A full chunk has no padding rows: its copy of the loop drops the tests.
         auto planes = [&](auto full) {
@@ -560,8 +644,15 @@ __device__ __forceinline__ void prefill_seq_ws(const PrefillArgs<TIn>& a, char* 
           for (int i = 0; i < TPL; ++i) {
             const int tr = TPL * j + i;
             const bool valid = FULL || tr < n;
-            const float k0 = valid ? rk[i].lo() : 0.f, k1 = valid ? rk[i].hi() : 0.f;
-            const float q0 = valid ? rq[i].lo() : 0.f, q1 = valid ? rq[i].hi() : 0.f;
+            float k0 = valid ? rk[i].lo() : 0.f, k1 = valid ? rk[i].hi() : 0.f;
+            float q0 = valid ? rq[i].lo() : 0.f, q1 = valid ? rq[i].hi() : 0.f;
+            if constexpr (PREP) {
+              const float nk = lane8_bcast(ik, i), nq = lane8_bcast(iq, i);  // from lane p = i of the group
+              k0 *= nk;
+              k1 *= nk;
+              q0 *= nq;
+              q1 *= nq;
+            }
             const float e0 = off0[i / TPG] * g0[i], e1 = off1[i / TPG] * g1[i];  // G of token tr
             const float ie0 = __builtin_amdgcn_rcpf(e0), ie1 = __builtin_amdgcn_rcpf(e1);
             uint32_t hi, lo;
@@ -582,7 +673,7 @@ __device__ __forceinline__ void prefill_seq_ws(const PrefillArgs<TIn>& a, char* 
           planes(std::true_type{});
         else
           planes(std::false_type{});
-        if (kWsPrefetch) issue_kq(t_next, n_next, lane);
+        if (kPfKQ) issue_kq(t_next, n_next, lane);
       }
       __syncthreads();  // B2
 
@@ -611,7 +702,7 @@ __device__ __forceinline__ void prefill_seq_ws(const PrefillArgs<TIn>& a, char* 
           misc(L::M_GN + c0) = gn0;
           misc(L::M_GN + c0 + 1) = gn1;
         }
-        const float beta_l = lane < n ? rb : 0.f;  // beta of token `lane` (padding: 0)
+        const float beta_l = lane < n ? (PREP ? sigmoid_f32(rb) : rb) : 0.f;  // beta of token `lane` (padding: 0)
         if (kw == 0) misc(L::M_BETA + lane) = beta_l;
 
         // Slot 0 of key wave kw is diagonal block kw of A, the other slots

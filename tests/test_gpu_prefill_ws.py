@@ -102,3 +102,65 @@ def test_chunk64_prefill_bad_checkpoint_slot_flags_and_skips_it():
     # The slot the bad id replaced is untouched: zero state, position still -1.
     untouched = int(bad[0] * n_ck + bad[1])
     assert torch.count_nonzero(pool.states[untouched]).item() == 0 and pool.pos[untouched].item() == -1
+
+
+GATES = {"softplus": kda.GATE_EXP_NEG_SOFTPLUS, "sigmoid": kda.GATE_SIGMOID}
+
+
+def raw_dev(raw):
+    return {name: dev_tensor(np.ascontiguousarray(x)) for name, x in raw.items()}
+
+
+def run_prefill_raw(spec, B, L, every, gate, scale_qk=1.0):
+    """prefill_chunked_prep at chunk 64 (raw projections: the key waves form the
+    norms and the gates); returns the device results and the host inputs."""
+    S0 = synth.initial_state(spec, B)
+    raw = synth.raw_token_inputs(spec, B, L)
+    d = raw_dev(raw)
+    if scale_qk != 1.0:
+        d["q"] = (d["q"].view(torch.bfloat16) * scale_qk).view(d["q"].dtype)
+        d["k"] = (d["k"].view(torch.bfloat16) * scale_qk).view(d["k"].dtype)
+    S = dev_tensor(S0)
+    pos = torch.tensor([3 * b for b in range(B)], dtype=torch.int64, device="cuda")
+    n_ck = L // every if every else 0
+    pool = kda.SlotPool(max(1, B * n_ck), spec.H, 128, 128, "cuda")
+    slots = torch.arange(B * n_ck, dtype=torch.int32, device="cuda").view(B, n_ck) if n_ck else None
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    o = torch.full((B, L, spec.H, 128), float("nan"), dtype=torch.float32, device="cuda")
+    kda.prefill_chunked_prep(S, pos, d["q"], d["k"], d["v"], d["alpha_logit"], d["beta_logit"], o, gate=GATES[gate],
+                             chunk=64, ckpt_every=every, ckpt_slots=slots, pool=pool, dev_err=err)
+    torch.cuda.synchronize()
+    assert kda.last_variant() == "prefill_chunked_prep"
+    return S0, raw, S, pos, o, err, pool, n_ck
+
+
+@pytest.mark.parametrize("gate", ["softplus", "sigmoid"])
+@pytest.mark.parametrize("L,every", [(300, 128), (129, 64), (65, 0), (1, 0)])
+def test_chunk64_prefill_raw_projections_uneven_chunks_match_oracle(L, every, gate):
+    spec = synth.ConfigSpec("ws128raw", 213, (3,), 4, 128, 128, "bf16", gate, "normal", 0)
+    B = 3
+    say(f"chunk-64 prefill from raw projections dk=dv=128 bf16 L={L} ckpt_every={every} {gate}")
+    S0, raw, S, pos, o, err, pool, n_ck = run_prefill_raw(spec, B, L, every, gate)
+    assert err.item() == 0
+    S_ref, pos_ref, o_ref, ck = ko.prefill(S0, np.array([3 * b for b in range(B)]), ko.prep(raw, GATES[gate]),
+                                           spec.scale, every)
+    assert_parity(o.cpu().numpy(), o_ref, S.cpu().numpy(), S_ref, f"raw L={L} every={every} {gate}")
+    assert pos.cpu().tolist() == pos_ref.tolist()
+    assert len(ck) == n_ck
+    for m, (Sm, pm) in enumerate(ck):
+        for b in range(B):
+            se = state_err(pool.states[b * n_ck + m:b * n_ck + m + 1].cpu().numpy(), Sm[b:b + 1])
+            assert se <= 1e-3, f"checkpoint {m} of sequence {b}: {se:.3e}"
+            assert pool.pos[b * n_ck + m].item() == pm[b]
+
+
+def test_chunk64_prefill_raw_projections_power_of_two_scaling_is_exact():
+    # The norms are sums of squares, an IEEE square root and a division:
+    # scaling every q and k by 2 scales each by exactly 2, and the unit
+    # vectors, so every output and state bit, stay the same.
+    spec = synth.ConfigSpec("ws128raw", 214, (2,), 4, 128, 128, "bf16", "softplus", "normal", 0)
+    say("chunk-64 prefill from raw projections: q, k scaled by 2")
+    _, _, S1, _, o1, _, _, _ = run_prefill_raw(spec, 2, 150, 0, "softplus")
+    _, _, S2, _, o2, _, _, _ = run_prefill_raw(spec, 2, 150, 0, "softplus", scale_qk=2.0)
+    assert torch.equal(o1.view(torch.int32), o2.view(torch.int32))
+    assert torch.equal(S1.view(torch.int32), S2.view(torch.int32))
