@@ -164,3 +164,44 @@ def test_chunk64_prefill_raw_projections_power_of_two_scaling_is_exact():
     _, _, S2, _, o2, _, _, _ = run_prefill_raw(spec, 2, 150, 0, "softplus", scale_qk=2.0)
     assert torch.equal(o1.view(torch.int32), o2.view(torch.int32))
     assert torch.equal(S1.view(torch.int32), S2.view(torch.int32))
+
+
+@pytest.mark.parametrize("raw", [False, True])
+@pytest.mark.parametrize("L,every", [(200, 64), (1, 0)])
+def test_chunk64_prefill_dv64_matches_oracle(L, every, raw):
+    # dk = 128, dv = 64: four value waves beside the eight key waves.
+    spec = synth.ConfigSpec("ws64", 215, (2,), 4, 128, 64, "bf16", "softplus", "normal", 0)
+    B = 2
+    say(f"chunk-64 prefill dk=128 dv=64 bf16 L={L} ckpt_every={every} raw={raw}")
+    S0 = synth.initial_state(spec, B)
+    pos0 = np.array([4, 0])
+    pos = torch.from_numpy(pos0.astype(np.int64)).cuda()
+    S = dev_tensor(S0)
+    n_ck = L // every if every else 0
+    pool = kda.SlotPool(max(1, B * n_ck), spec.H, 128, 64, "cuda")
+    slots = torch.arange(B * n_ck, dtype=torch.int32, device="cuda").view(B, n_ck) if n_ck else None
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    o = torch.full((B, L, spec.H, 64), float("nan"), dtype=torch.float32, device="cuda")
+    if raw:
+        host = synth.raw_token_inputs(spec, B, L)
+        d = raw_dev(host)
+        kda.prefill_chunked_prep(S, pos, d["q"], d["k"], d["v"], d["alpha_logit"], d["beta_logit"], o,
+                                 gate=GATES["softplus"], chunk=64, ckpt_every=every, ckpt_slots=slots, pool=pool,
+                                 dev_err=err)
+        ref_inp = ko.prep(host, GATES["softplus"])
+    else:
+        host = synth.token_inputs(spec, B, L)
+        d = dev_inputs(host)
+        kda.prefill_chunked(S, pos, d["q"], d["k"], d["v"], d["alpha"], d["beta"], o, chunk=64, ckpt_every=every,
+                            ckpt_slots=slots, pool=pool, dev_err=err)
+        ref_inp = host
+    torch.cuda.synchronize()
+    assert err.item() == 0
+    S_ref, pos_ref, o_ref, ck = ko.prefill(S0, pos0, ref_inp, spec.scale, every)
+    assert_parity(o.cpu().numpy(), o_ref, S.cpu().numpy(), S_ref, f"dv=64 L={L} raw={raw}")
+    assert pos.cpu().tolist() == pos_ref.tolist()
+    for m, (Sm, pm) in enumerate(ck):
+        for b in range(B):
+            se = state_err(pool.states[b * n_ck + m:b * n_ck + m + 1].cpu().numpy(), Sm[b:b + 1])
+            assert se <= 1e-3, f"checkpoint {m} of sequence {b}: {se:.3e}"
+            assert pool.pos[b * n_ck + m].item() == pm[b]
