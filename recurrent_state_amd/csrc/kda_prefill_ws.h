@@ -1,5 +1,6 @@
 // Chunked prompt processing with the key side and the value side of each
-// chunk on different waves (dk = 128, chunk 64).
+// chunk on different waves (chunk 64; dk and dv 64 or 128).  The comments
+// below count the waves of dk = dv = 128: eight of each role.
 //
 // The chunk algebra is the one of kda_prefill_impl.h, operation for
 // operation: every product, split and sum below is formed from the same
@@ -89,7 +90,7 @@ struct SmemWs {
   static constexpr int total = off_diag + NB * DSTRIDE * 4;
   // Slots of the misc values (floats; the votes are ints).
   static constexpr int M_BETA = 0, M_GN = CH, M_A0 = CH + DK, M_VOTE = CH + 2 * DK;
-  static_assert(M_VOTE + DK / 32 <= 4 * DK && (RS_C - CH) * 2 >= 16, "misc values must fit the Kb^T row padding");
+  static_assert(M_VOTE + DK / 8 <= 4 * DK && (RS_C - CH) * 2 >= 16, "misc values must fit the Kb^T row padding");
   static_assert(total <= 163840, "LDS budget exceeded");
   static_assert(off_kb % 16 == 0 && off_r2 % 16 == 0 && off_diag % 16 == 0 && (KQ_PLANE * 2) % 16 == 0 &&
                     (KB_PLANE * 2) % 16 == 0 && (KH_PLANE * 2) % 16 == 0 && (CC_PLANE * 2) % 16 == 0,
@@ -163,7 +164,7 @@ __device__ __forceinline__ float lane8_bcast(float x, int i) {
 template <int DK, int DV, int CH, typename TIn, bool PREP = false>
 __device__ __forceinline__ void prefill_seq_ws(const PrefillArgs<TIn>& a, char* smem, int b, int h, int sb,
                                                size_t tok0, int n_tok) {
-  static_assert(DK == 128 && CH == 64 && DV % 16 == 0, "shape");
+  static_assert((DK == 128 || DK == 64) && CH == 64 && DV % 16 == 0, "shape");
   constexpr int NV = DV / 16;   // value waves: wave v owns value columns [16 v, 16 v + 16)
   constexpr int NK = ws_key_waves(DK);  // key waves: key wave kw owns channels [CPW kw, CPW kw + CPW)
   constexpr int CPW = DK / NK;         // key channels per key wave
