@@ -449,7 +449,7 @@ __device__ __forceinline__ void prefill_seq_ws(const PrefillArgs<TIn>& a, char* 
     // (held from I2 on, they pushed the key role past 128 registers).
     constexpr bool kPfKQ = KDA_PREFILL_WS_PREFETCH && sizeof(TIn) == 2;
     constexpr bool kPfA = kPfKQ && !PREP;
-    static_assert(!PREP || (kPfKQ && NK == 8 && PPW == TPL), "raw projections on the key waves");
+    static_assert(!PREP || (kPfKQ && (NK == 8 || NK == 4) && PPW == TPL), "raw projections on the key waves");
     Pair2<float> ra[TPL];
     Pair2<TIn> rk[TPL], rq[TPL];
     float rb = 0.f;       // beta of token `lane`
@@ -624,17 +624,22 @@ __device__ __forceinline__ void prefill_seq_ws(const PrefillArgs<TIn>& a, char* 
         // read nothing), so that the wait counts are the same on every path.
         const int t_next = t_k + n;
         const int n_next = t_next < n_tok ? nominal(t_next) : 0;
-        // Lane p forms 1 / |k| and 1 / |q| of token TPL j + p from the eight
+        // Lane p forms 1 / |k| and 1 / |q| of token TPL j + p from the key
         // waves' parts (PREP); the plane pass takes each token's pair from the
         // lane that holds it, as it reaches the token.
         float ik = 0.f, iq = 0.f;
         if constexpr (PREP) {
           const float4 a0 = *reinterpret_cast<const float4*>(norm_part(TPL * j + p_));
-          const float4 a1 = *reinterpret_cast<const float4*>(norm_part(TPL * j + p_) + 4);
           const float4 b0 = *reinterpret_cast<const float4*>(norm_part(CH + TPL * j + p_));
-          const float4 b1 = *reinterpret_cast<const float4*>(norm_part(CH + TPL * j + p_) + 4);
-          ik = inv_norm(((a0.x + a0.y) + (a0.z + a0.w)) + ((a1.x + a1.y) + (a1.z + a1.w)));
-          iq = inv_norm(((b0.x + b0.y) + (b0.z + b0.w)) + ((b1.x + b1.y) + (b1.z + b1.w)));
+          float sk = (a0.x + a0.y) + (a0.z + a0.w), sq = (b0.x + b0.y) + (b0.z + b0.w);
+          if constexpr (NK == 8) {
+            const float4 a1 = *reinterpret_cast<const float4*>(norm_part(TPL * j + p_) + 4);
+            const float4 b1 = *reinterpret_cast<const float4*>(norm_part(CH + TPL * j + p_) + 4);
+            sk += (a1.x + a1.y) + (a1.z + a1.w);
+            sq += (b1.x + b1.y) + (b1.z + b1.w);
+          }
+          ik = inv_norm(sk);
+          iq = inv_norm(sq);
         }
         if (kPfA) issue_alpha(t_next, n_next, lane, rb_next);
         const int pc = kpos(c0);

@@ -168,17 +168,18 @@ def test_chunk64_prefill_raw_projections_power_of_two_scaling_is_exact():
 
 @pytest.mark.parametrize("raw", [False, True])
 @pytest.mark.parametrize("L,every", [(200, 64), (1, 0)])
-def test_chunk64_prefill_dv64_matches_oracle(L, every, raw):
-    # dk = 128, dv = 64: four value waves beside the eight key waves.
-    spec = synth.ConfigSpec("ws64", 215, (2,), 4, 128, 64, "bf16", "softplus", "normal", 0)
+@pytest.mark.parametrize("dk", [128, 64])
+def test_chunk64_prefill_dv64_matches_oracle(dk, L, every, raw):
+    # dv = 64: four value waves beside the dk / 16 key waves.
+    spec = synth.ConfigSpec("ws64", 215, (2,), 4, dk, 64, "bf16", "softplus", "normal", 0)
     B = 2
-    say(f"chunk-64 prefill dk=128 dv=64 bf16 L={L} ckpt_every={every} raw={raw}")
+    say(f"chunk-64 prefill dk={dk} dv=64 bf16 L={L} ckpt_every={every} raw={raw}")
     S0 = synth.initial_state(spec, B)
     pos0 = np.array([4, 0])
     pos = torch.from_numpy(pos0.astype(np.int64)).cuda()
     S = dev_tensor(S0)
     n_ck = L // every if every else 0
-    pool = kda.SlotPool(max(1, B * n_ck), spec.H, 128, 64, "cuda")
+    pool = kda.SlotPool(max(1, B * n_ck), spec.H, dk, 64, "cuda")
     slots = torch.arange(B * n_ck, dtype=torch.int32, device="cuda").view(B, n_ck) if n_ck else None
     err = torch.zeros(1, dtype=torch.int32, device="cuda")
     o = torch.full((B, L, spec.H, 64), float("nan"), dtype=torch.float32, device="cuda")
