@@ -7,8 +7,8 @@
 // operands in the same order, so this kernel's outputs, states and
 // checkpoints are bit-identical to the single-role kernel's.  (Raw
 // projections, bf16 inputs only, are prepared by the key waves: each sums
-// its 16 channels' part of a token's squared norms and the eight parts are
-// added after the first barrier, an order the single-role kernel's full-wave
+// its 16 channels' part of a token's squared norms and the key waves' parts
+// are added after the first barrier, an order the single-role kernel's full-wave
 // sums do not share, so that form agrees with it to rounding.)  What changes
 // is who does the work and when.  The key-side products of a chunk (the
 // cumulative decays, the Kt / Qt / Kh / Kb^T planes, the A and P tiles and
