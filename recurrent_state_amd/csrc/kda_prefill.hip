@@ -3,7 +3,7 @@
 // chunk algebra and the single-role workgroup's code are in
 // kda_prefill_impl.h, which the mixed-batch kernel shares; at chunk 64 the
 // prepared inputs run on the bit-identical form with separate key and value
-// waves (kda_prefill_ws.h), and so do bf16 raw projections.
+// waves (kda_prefill_ws.h), and so do raw projections.
 
 #include <hip/hip_runtime.h>
 
@@ -69,11 +69,10 @@ hipError_t launch_cfg(const kda_shape& s, int32_t L, int32_t chunk, float* state
   const dim3 grid((unsigned)((size_t)s.B * s.H));
   auto go = [&](auto prep) {
     constexpr bool PREP = decltype(prep)::value;
-    // Raw projections run on it for bf16 inputs (the form that requests a
-    // chunk's inputs a period ahead); fp32 raw projections keep the
-    // single-role kernel.
+    // Raw projections run on it too (their keys and queries requested a
+    // period ahead); chunk 32 keeps the single-role kernel.
     if constexpr (KDA_PREFILL_WS && (DV == 128 || DV == 64) &&
-                  (DK == 128 || DK == 64) && (!PREP || (KDA_PREFILL_WS_PREP && sizeof(TIn) == 2))) {
+                  (DK == 128 || DK == 64) && (!PREP || KDA_PREFILL_WS_PREP)) {
       if (chunk == 64) {
         prefill_ws_kernel<DK, DV, 64, TIn, PREP><<<grid, 64 * (DV / 16 + ws_key_waves(DK)), 0, st>>>(a);
         return;

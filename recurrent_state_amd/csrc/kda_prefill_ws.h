@@ -6,7 +6,7 @@
 // operation: every product, split and sum below is formed from the same
 // operands in the same order, so this kernel's outputs, states and
 // checkpoints are bit-identical to the single-role kernel's.  (Raw
-// projections, bf16 inputs only, are prepared by the key waves: each sums
+// projections are prepared by the key waves: each sums
 // its 16 channels' part of a token's squared norms and the key waves' parts
 // are added after the first barrier, an order the single-role kernel's full-wave
 // sums do not share, so that form agrees with it to rounding.)  What changes
@@ -55,8 +55,9 @@
 #define KDA_PREFILL_WS_XS 4
 #endif
 // Key waves request a chunk's inputs one period ahead (1) or in its own period
-// (0).  Only for bf16 inputs: fp32 keys and queries take twice the registers
-// and the prefetched form then spills.
+// (0).  Prepared fp32 inputs keep the in-period form: their keys and queries
+// take twice the registers and, with the decays also held, it spills.  Raw
+// projections (which hold only keys and queries ahead) use it at both widths.
 #ifndef KDA_PREFILL_WS_PREFETCH
 #define KDA_PREFILL_WS_PREFETCH 1
 #endif
@@ -159,7 +160,7 @@ __device__ __forceinline__ float lane8_bcast(float x, int i) {
 
 // The whole prompt of one (sequence, head), run by one workgroup of
 // 64 (dv / 16 + ws_key_waves(dk)) lanes; arguments as for prefill_seq.
-// PREP (bf16 inputs only): raw projections and logits, prepared by the key
+// PREP: raw projections and logits, prepared by the key
 // waves (see the key role).
 template <int DK, int DV, int CH, typename TIn, bool PREP = false>
 __device__ __forceinline__ void prefill_seq_ws(const PrefillArgs<TIn>& a, char* smem, int b, int h, int sb,
@@ -446,8 +447,9 @@ __device__ __forceinline__ void prefill_seq_ws(const PrefillArgs<TIn>& a, char* 
     // Raw projections need a chunk's keys and queries at the start of its I1
     // (their norms), so they run only with kPfKQ; their decays are requested
     // at the start of I1, where the norm parts are formed while they arrive
-    // (held from I2 on, they pushed the key role past 128 registers).
-    constexpr bool kPfKQ = KDA_PREFILL_WS_PREFETCH && sizeof(TIn) == 2;
+    // (held from I2 on, they pushed the key role past 128 registers).  With
+    // prepared fp32 inputs neither is requested ahead (that form spilled).
+    constexpr bool kPfKQ = KDA_PREFILL_WS_PREFETCH && (sizeof(TIn) == 2 || PREP);
     constexpr bool kPfA = kPfKQ && !PREP;
     static_assert(!PREP || (kPfKQ && (NK == 8 || NK == 4) && PPW == TPL), "raw projections on the key waves");
     Pair2<float> ra[TPL];

@@ -206,3 +206,21 @@ def test_chunk64_prefill_dv64_matches_oracle(dk, L, every, raw):
             se = state_err(pool.states[b * n_ck + m:b * n_ck + m + 1].cpu().numpy(), Sm[b:b + 1])
             assert se <= 1e-3, f"checkpoint {m} of sequence {b}: {se:.3e}"
             assert pool.pos[b * n_ck + m].item() == pm[b]
+
+
+@pytest.mark.parametrize("L,every", [(129, 64), (1, 0)])
+def test_chunk64_prefill_raw_projections_f32_match_oracle(L, every):
+    # fp32 raw projections: keys and queries a period ahead as for bf16.
+    spec = synth.ConfigSpec("ws128rawf", 216, (2,), 4, 128, 128, "f32", "sigmoid", "normal", 0)
+    B = 2
+    say(f"chunk-64 prefill from fp32 raw projections dk=dv=128 L={L} ckpt_every={every}")
+    S0, raw, S, pos, o, err, pool, n_ck = run_prefill_raw(spec, B, L, every, "sigmoid")
+    assert err.item() == 0
+    S_ref, pos_ref, o_ref, ck = ko.prefill(S0, np.array([3 * b for b in range(B)]), ko.prep(raw, GATES["sigmoid"]),
+                                           spec.scale, every)
+    assert_parity(o.cpu().numpy(), o_ref, S.cpu().numpy(), S_ref, f"f32 raw L={L} every={every}")
+    assert pos.cpu().tolist() == pos_ref.tolist()
+    for m, (Sm, pm) in enumerate(ck):
+        for b in range(B):
+            se = state_err(pool.states[b * n_ck + m:b * n_ck + m + 1].cpu().numpy(), Sm[b:b + 1])
+            assert se <= 1e-3, f"checkpoint {m} of sequence {b}: {se:.3e}"
