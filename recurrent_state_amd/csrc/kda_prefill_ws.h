@@ -55,9 +55,9 @@
 #define KDA_PREFILL_WS_XS 4
 #endif
 // Key waves request a chunk's inputs one period ahead (1) or in its own period
-// (0).  Prepared fp32 inputs keep the in-period form: their keys and queries
-// take twice the registers and, with the decays also held, it spills.  Raw
-// projections (which hold only keys and queries ahead) use it at both widths.
+// (0).  The decays and betas go ahead only for prepared bf16 inputs: fp32 keys
+// and queries take twice the registers, and raw projections need their
+// keys and queries early; both hold only those ahead.
 #ifndef KDA_PREFILL_WS_PREFETCH
 #define KDA_PREFILL_WS_PREFETCH 1
 #endif
@@ -447,10 +447,11 @@ __device__ __forceinline__ void prefill_seq_ws(const PrefillArgs<TIn>& a, char* 
     // Raw projections need a chunk's keys and queries at the start of its I1
     // (their norms), so they run only with kPfKQ; their decays are requested
     // at the start of I1, where the norm parts are formed while they arrive
-    // (held from I2 on, they pushed the key role past 128 registers).  With
-    // prepared fp32 inputs neither is requested ahead (that form spilled).
-    constexpr bool kPfKQ = KDA_PREFILL_WS_PREFETCH && (sizeof(TIn) == 2 || PREP);
-    constexpr bool kPfA = kPfKQ && !PREP;
+    // (held from I2 on, they pushed the key role past 128 registers).  Prepared
+    // fp32 inputs do the same: their keys and queries take twice the
+    // registers, and with the decays also held ahead that form spilled.
+    constexpr bool kPfKQ = KDA_PREFILL_WS_PREFETCH;
+    constexpr bool kPfA = kPfKQ && !PREP && sizeof(TIn) == 2;
     static_assert(!PREP || (kPfKQ && (NK == 8 || NK == 4) && PPW == TPL), "raw projections on the key waves");
     Pair2<float> ra[TPL];
     Pair2<TIn> rk[TPL], rq[TPL];
