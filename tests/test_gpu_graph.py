@@ -241,3 +241,50 @@ def test_prefill_graph_replays_match_eager():
             assert torch.equal(pg[i], pe[i])
             assert torch.equal(bits(poolsg[i].states), bits(poolse[i].states)), f"replay {rep} checkpoints"
             assert torch.equal(poolsg[i].pos, poolse[i].pos)
+
+
+def test_prefill_raw_projections_graph_replays_match_eager():
+    # The chunk-64 prompt from raw projections (the key waves form the norms
+    # and gates, exchanging norm parts through LDS), with checkpoints.
+    B, L, every = 2, 130, 64
+    say("graph: chunked prefill from raw projections, chunk 64")
+    S0 = dev_tensor(synth.initial_state(SPEC, B))
+    d = {k: dev_tensor(v) for k, v in synth.raw_token_inputs(SPEC, B, L).items()}
+    n_ck = L // every
+    ck = torch.arange(B * n_ck, dtype=torch.int32, device="cuda").view(B, n_ck)
+    pos0 = torch.tensor([2, 9], dtype=torch.int64, device="cuda")
+
+    def fresh():
+        return (S0.clone(), pos0.clone(), kda.SlotPool(B * n_ck, SPEC.H, 128, 128, "cuda"),
+                torch.empty((B, L, SPEC.H, 128), device="cuda"), torch.zeros(1, dtype=torch.int32, device="cuda"))
+
+    def run(S, pos, pool, o, err):
+        kda.prefill_chunked_prep(S, pos, d["q"], d["k"], d["v"], d["alpha_logit"], d["beta_logit"], o,
+                                 gate=kda.GATE_SIGMOID, chunk=64, ckpt_every=every, ckpt_slots=ck, pool=pool,
+                                 dev_err=err)
+
+    Se, pe, poole, oe, erre = fresh()
+    run(Se, pe, poole, oe, erre)
+    torch.cuda.synchronize()
+    assert erre.item() == 0
+    Sg, pg, poolg, og, errg = fresh()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        run(Sg, pg, poolg, og, errg)
+    torch.cuda.synchronize()
+    assert torch.equal(pg, pos0), "capture must not run the kernels"
+    for rep in range(3):
+        Sg.copy_(S0)
+        pg.copy_(pos0)
+        og.fill_(float("nan"))
+        poolg.states.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        junk = torch.randn(1000, device="cuda").cumsum(0)  # unrelated eager work between replays
+        torch.cuda.synchronize()
+        assert junk.numel() == 1000 and errg.item() == 0
+        assert torch.equal(bits(Sg), bits(Se)), f"replay {rep} state"
+        assert torch.equal(bits(og), bits(oe)), f"replay {rep} outputs"
+        assert torch.equal(pg, pe)
+        assert torch.equal(bits(poolg.states), bits(poole.states)), f"replay {rep} checkpoints"
+        assert torch.equal(poolg.pos, poole.pos)
